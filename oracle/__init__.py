@@ -1,0 +1,256 @@
+"""CPU oracle for the speculative-decoding verify step.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package.  The product library
+(``rejection_sampling_verify_05_amd``) never imports, links or calls it, and the
+two share no code: the arithmetic lives in ``oracle.c`` (plain C, fp64 for
+probabilities and race scores), and this module only marshals NumPy arrays into
+it through ctypes.
+
+What each function follows on the pages is documented in ``oracle.h`` /
+``oracle.c``.  Pins (worked examples, identities, known-answer vectors,
+chi-square tests of the output law) live in ``tests/test_oracle_*.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_SO = os.path.join(_HERE, "liborc.so")
+
+RACE_CHUNK = 1024
+TAG_ACCEPT, TAG_CHUNK, TAG_TOKEN = 0, 1, 2
+F32, BF16 = 0, 1
+ERR_CU, ERR_TEMPERATURE, ERR_PENALTY, ERR_ROW, ERR_SLOT, ERR_OFFSET = 1, 2, 4, 8, 16, 32
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liborc.so with gcc (no FMA contraction)."""
+    if force or not os.path.exists(_SO):
+        tmp = _SO + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+               "-fno-fast-math", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _SO)
+    return _SO
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_SO):
+            build()
+        L = ctypes.CDLL(_SO)
+        P = ctypes.c_void_p
+        i32, i64, u32, u64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_uint64
+        f32, f64 = ctypes.c_float, ctypes.c_double
+        L.orc_philox4x32_10.argtypes = [P, P, P]
+        L.orc_philox4x32_10.restype = None
+        L.orc_word.argtypes = [u64, u32, u32, u32, u32]
+        L.orc_word.restype = u32
+        L.orc_uniform_accept.argtypes = [u32]
+        L.orc_uniform_accept.restype = f64
+        L.orc_uniform_race.argtypes = [u32]
+        L.orc_uniform_race.restype = f64
+        L.orc_exp_noise.argtypes = [u64, u32, u32, u32, u32]
+        L.orc_exp_noise.restype = f64
+        L.orc_bf16_to_f32.argtypes = [ctypes.c_uint16]
+        L.orc_bf16_to_f32.restype = f32
+        L.orc_repetition_penalty.argtypes = [P, P, i32, f32]
+        L.orc_repetition_penalty.restype = None
+        L.orc_kth_largest.argtypes = [P, i32, i32]
+        L.orc_kth_largest.restype = f32
+        L.orc_top_k_mask.argtypes = [P, i32, i32]
+        L.orc_top_k_mask.restype = None
+        L.orc_argmax.argtypes = [P, i32]
+        L.orc_argmax.restype = i32
+        L.orc_softmax.argtypes = [P, i32, f64, P]
+        L.orc_softmax.restype = ctypes.c_int
+        L.orc_race.argtypes = [P, i32, i32, u64, u32, u32, P]
+        L.orc_race.restype = i32
+        L.orc_prepare_request.argtypes = [P, ctypes.c_int, i64, i32, i32, f32, i32, P, P, P, P]
+        L.orc_prepare_request.restype = ctypes.c_int
+        L.orc_decide_request.argtypes = [P, P, i32, i32, f32, P, P, i64, u32, u64, u32, i32,
+                                         P, P, P, P]
+        L.orc_decide_request.restype = f64
+        L.orc_verify_batch.argtypes = [P, ctypes.c_int, i64, i32, i32, P, i64, P, P, i32, i32,
+                                       P, P, P, P, P, i32, u64, u64, i32, P, i32, P, P, P, P]
+        L.orc_verify_batch.restype = u32
+        L.orc_post_update.argtypes = [P, P, P, i32, P, P, i32, i32, i32, P, P, P]
+        L.orc_post_update.restype = u32
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+# ---- random stream ---------------------------------------------------------
+def philox4x32_10(ctr, key) -> np.ndarray:
+    c = np.asarray(ctr, dtype=np.uint32)
+    k = np.asarray(key, dtype=np.uint32)
+    out = np.zeros(4, dtype=np.uint32)
+    lib().orc_philox4x32_10(_ptr(c), _ptr(k), _ptr(out))
+    return out
+
+
+def word(seed: int, offset: int, g: int, tag: int, idx: int) -> int:
+    return int(lib().orc_word(seed, offset, g, tag, idx))
+
+
+def uniform_accept(w: int) -> float:
+    return float(lib().orc_uniform_accept(w))
+
+
+def uniform_race(w: int) -> float:
+    return float(lib().orc_uniform_race(w))
+
+
+def exp_noise(seed: int, offset: int, g: int, tag: int, idx: int) -> float:
+    return float(lib().orc_exp_noise(seed, offset, g, tag, idx))
+
+
+# ---- logit processing ------------------------------------------------------
+def bf16_to_f32(bits) -> np.ndarray:
+    b = np.asarray(bits, dtype=np.uint16).ravel()
+    return np.array([lib().orc_bf16_to_f32(int(v)) for v in b], dtype=np.float32)
+
+
+def repetition_penalty(z, counts, theta: float) -> np.ndarray:
+    zz = _c(z, np.float32).copy()
+    cc = _c(counts, np.int32)
+    lib().orc_repetition_penalty(_ptr(zz), _ptr(cc), zz.size, theta)
+    return zz
+
+
+def kth_largest(z, k: int) -> float:
+    zz = _c(z, np.float32)
+    return float(lib().orc_kth_largest(_ptr(zz), zz.size, k))
+
+
+def top_k_mask(z, k: int) -> np.ndarray:
+    zz = _c(z, np.float32).copy()
+    lib().orc_top_k_mask(_ptr(zz), zz.size, k)
+    return zz
+
+
+def argmax(z) -> int:
+    zz = _c(z, np.float32)
+    return int(lib().orc_argmax(_ptr(zz), zz.size))
+
+
+def softmax(z, T: float) -> np.ndarray:
+    zz = _c(z, np.float32)
+    p = np.zeros(zz.size, dtype=np.float64)
+    err = lib().orc_softmax(_ptr(zz), zz.size, float(T), _ptr(p))
+    if err:
+        raise ValueError("row has no finite maximum")
+    return p
+
+
+def race(w, C: int, seed: int, offset: int, g: int):
+    ww = _c(w, np.float64)
+    m = ctypes.c_double(0.0)
+    x = lib().orc_race(_ptr(ww), ww.size, C, seed, offset, g, ctypes.byref(m))
+    return int(x), float(m.value)
+
+
+# ---- one request -----------------------------------------------------------
+def prepare_request(rows, T: float, top_k: int = 0, theta=None, counts=None):
+    """rows: [K+1, V] float32, or uint16 bf16 bits.  Returns (P [K+1,V] f64, amax, err)."""
+    dtype = BF16 if rows.dtype == np.uint16 else F32
+    rr = np.ascontiguousarray(rows)
+    n, V = rr.shape
+    P = np.zeros((n, V), dtype=np.float64)
+    amax = np.zeros(n, dtype=np.int32)
+    th = None if theta is None else np.array([theta], dtype=np.float32)
+    cc = _c(counts, np.int32)
+    err = lib().orc_prepare_request(_ptr(rr), dtype, V, n - 1, V, float(T), int(top_k),
+                                    _ptr(th), _ptr(cc), _ptr(P), _ptr(amax))
+    return P, amax, int(err)
+
+
+def decide_request(P, amax, T: float, draft_ids, draft_probs=None, g0: int = 0, seed: int = 0,
+                   offset: int = 0, C: int = RACE_CHUNK):
+    """Returns (tokens list, num_sampled, num_rejected, margin, p_draft)."""
+    n, V = P.shape
+    K = n - 1
+    PP = np.ascontiguousarray(P, dtype=np.float64)
+    am = _c(amax, np.int32)
+    d = _c(np.asarray(draft_ids).reshape(-1), np.int32) if K > 0 else np.zeros(1, np.int32)
+    q = _c(draft_probs, np.float32)
+    tokens = np.full(K + 1, -1, dtype=np.int32)
+    ns = ctypes.c_int32(0)
+    nr = ctypes.c_int32(0)
+    pd = np.zeros(max(K, 1), dtype=np.float32)
+    mg = lib().orc_decide_request(_ptr(PP), _ptr(am), K, V, float(T), _ptr(d), _ptr(q),
+                                  V if q is None else q.shape[-1], g0, seed, offset, C,
+                                  _ptr(tokens), ctypes.byref(ns), ctypes.byref(nr), _ptr(pd))
+    return tokens[: ns.value].tolist(), ns.value, nr.value, float(mg), pd[:K]
+
+
+# ---- whole call ------------------------------------------------------------
+def verify_batch(logits, cu, draft_ids, temperature, draft_probs=None, top_k=None,
+                 rep_penalty=None, idx_mapping=None, counts=None, seed: int = 0,
+                 offset: int = 0, max_k=None, out_stride=None, C: int = RACE_CHUNK):
+    """Whole verify call on host arrays.  logits: [R, V] float32 or uint16 (bf16
+    bits).  Returns a dict with tokens [B, out_stride], num_sampled, num_rejected,
+    margin [B], p_draft [D] and the error mask."""
+    lg = np.ascontiguousarray(logits)
+    dtype = BF16 if lg.dtype == np.uint16 else F32
+    R, V = lg.shape
+    cu = _c(cu, np.int32)
+    B = cu.size - 1
+    D = R - B
+    if max_k is None:
+        max_k = int(np.max(np.diff(cu))) if B > 0 else 0
+    if out_stride is None:
+        out_stride = max_k + 1
+    d = _c(draft_ids, np.int32) if D > 0 else np.zeros(1, np.int32)
+    q = _c(draft_probs, np.float32)
+    T = _c(temperature, np.float32)
+    tk = _c(top_k, np.int32)
+    rp = _c(rep_penalty, np.float32)
+    im = _c(idx_mapping, np.int32)
+    cc = _c(counts, np.int32)
+    S = 0 if cc is None else cc.shape[0]
+    tokens = np.full((B, out_stride), -1, dtype=np.int32)
+    ns = np.zeros(B, dtype=np.int32)
+    nr = np.zeros(B, dtype=np.int32)
+    mg = np.zeros(B, dtype=np.float64)
+    pd = np.zeros(max(D, 1), dtype=np.float32)
+    err = lib().orc_verify_batch(_ptr(lg), dtype, V, R, V, _ptr(q), V, _ptr(d), _ptr(cu), B,
+                                 int(max_k), _ptr(T), _ptr(tk), _ptr(rp), _ptr(im), _ptr(cc), S,
+                                 seed, offset, C, _ptr(tokens), out_stride, _ptr(ns), _ptr(nr),
+                                 _ptr(mg), _ptr(pd))
+    return dict(tokens=tokens, num_sampled=ns, num_rejected=nr, margin=mg, p_draft=pd[:D],
+                err=int(err))
+
+
+def post_update(idx_mapping, query_len, tokens, num_sampled, num_rejected, last_sampled,
+                counts, num_computed):
+    """In-place post_update on host arrays (int32).  Returns the error mask."""
+    im = _c(idx_mapping, np.int32)
+    ql = _c(query_len, np.int32)
+    tk = _c(tokens, np.int32)
+    ns = _c(num_sampled, np.int32)
+    nr = _c(num_rejected, np.int32)
+    for a in (last_sampled, counts, num_computed):
+        assert a.dtype == np.int32 and a.flags.c_contiguous
+    B = im.size
+    S, V = counts.shape
+    return int(lib().orc_post_update(_ptr(im), _ptr(ql), _ptr(tk), tk.shape[1], _ptr(ns),
+                                     _ptr(nr), B, V, S, _ptr(last_sampled), _ptr(counts),
+                                     _ptr(num_computed)))

@@ -1,0 +1,447 @@
+/*
+ * oracle.c -- CPU reference for the speculative-decoding verify step.
+ *
+ * TEST INFRASTRUCTURE ONLY (see oracle.h): used by the tests, the smoke check
+ * and the benchmark's CPU-baseline leg, never by the product path.
+ *
+ * Build: gcc -O2 -std=c11 -fPIC -shared -ffp-contract=off -fno-fast-math
+ * (no FMA contraction, so every fp32 operation on logits rounds once, as IEEE
+ * round-to-nearest-even; probabilities and race scores are fp64).
+ *
+ * Citations name the page and its section; "page 2" is "vLLM 投机解码（Eagle / MTP）
+ * 实现与运行流程", "page 1" is "【vllm】DeepSeekMTP、eagle", "page 3" is
+ * "speculative decoding in vLLM" (section 七, verification), "page 4" is the
+ * Mini-SGLang walk-through (sampler conventions).
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------ */
+/* Philox4x32-10, from Salmon et al., SC'11.  Each round multiplies counter    */
+/* words 0 and 2 by the two round multipliers, swaps the halves of the 64-bit  */
+/* products across lanes and xors in the other two counter words and the key; */
+/* the key is advanced by the two Weyl constants between rounds.               */
+/* ------------------------------------------------------------------------ */
+#define PHILOX_MUL_A 0xD2511F53u
+#define PHILOX_MUL_B 0xCD9E8D57u
+#define PHILOX_WEYL_A 0x9E3779B9u
+#define PHILOX_WEYL_B 0xBB67AE85u
+
+void orc_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+  uint32_t x0 = ctr[0], x1 = ctr[1], x2 = ctr[2], x3 = ctr[3];
+  uint32_t k0 = key[0], k1 = key[1];
+  for (int round = 0; round < 10; ++round) {
+    uint64_t prod_a = (uint64_t)PHILOX_MUL_A * (uint64_t)x0;
+    uint64_t prod_b = (uint64_t)PHILOX_MUL_B * (uint64_t)x2;
+    uint32_t hi_a = (uint32_t)(prod_a >> 32), lo_a = (uint32_t)prod_a;
+    uint32_t hi_b = (uint32_t)(prod_b >> 32), lo_b = (uint32_t)prod_b;
+    uint32_t y0 = hi_b ^ x1 ^ k0;
+    uint32_t y1 = lo_b;
+    uint32_t y2 = hi_a ^ x3 ^ k1;
+    uint32_t y3 = lo_a;
+    x0 = y0;
+    x1 = y1;
+    x2 = y2;
+    x3 = y3;
+    k0 += PHILOX_WEYL_A;
+    k1 += PHILOX_WEYL_B;
+  }
+  out[0] = x0;
+  out[1] = x1;
+  out[2] = x2;
+  out[3] = x3;
+}
+
+/* Counter layout: (idx >> 2, target row g, tag, call offset); word idx & 3.
+ * Key: the two 32-bit halves of the 64-bit seed. */
+uint32_t orc_word(uint64_t seed, uint32_t offset, uint32_t g, uint32_t tag, uint32_t idx) {
+  uint32_t ctr[4] = {idx >> 2, g, tag, offset};
+  uint32_t key[2] = {(uint32_t)(seed & 0xffffffffu), (uint32_t)(seed >> 32)};
+  uint32_t out[4];
+  orc_philox4x32_10(ctr, key, out);
+  return out[idx & 3u];
+}
+
+/* Accept uniform on the 2^-24 grid, excluding 0: a draft with p = 0 is never
+ * accepted, and u = 1 accepts only when p >= q. */
+double orc_uniform_accept(uint32_t w) { return ldexp((double)((w >> 8) + 1u), -24); }
+
+/* Race uniform on the 2^-24 grid, excluding 1 (E = -ln U is then never 0). */
+double orc_uniform_race(uint32_t w) { return ldexp((double)(w >> 8), -24); }
+
+/* Exp(1) noise E = -ln U; U = 0 gives E = +inf (a score of 0 that never wins
+ * against a positive score). */
+double orc_exp_noise(uint64_t seed, uint32_t offset, uint32_t g, uint32_t tag, uint32_t idx) {
+  double u = orc_uniform_race(orc_word(seed, offset, g, tag, idx));
+  if (u == 0.0) return INFINITY;
+  return -log(u);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Logit processing                                                          */
+/* ------------------------------------------------------------------------ */
+
+/* bf16 is the upper half of an IEEE binary32. */
+float orc_bf16_to_f32(uint16_t bits) {
+  uint32_t u = (uint32_t)bits << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return f;
+}
+
+/* Multiplicative repetition penalty on every token seen in the output so far
+ * (page 1, penalties section: applied to logits before sampling, from the
+ * per-request output_bin_counts histogram).  A positive logit is divided by
+ * theta, a non-positive one multiplied by theta, both in fp32. */
+void orc_repetition_penalty(float *z, const int32_t *counts, int32_t V, float theta) {
+  for (int32_t x = 0; x < V; ++x) {
+    if (counts[x] > 0) {
+      if (z[x] > 0.0f)
+        z[x] = z[x] / theta;
+      else
+        z[x] = z[x] * theta;
+    }
+  }
+}
+
+static int cmp_float_desc(const void *a, const void *b) {
+  float fa = *(const float *)a, fb = *(const float *)b;
+  return (fa < fb) - (fa > fb);
+}
+
+/* k-th largest value of z counting duplicates (1 <= k <= V), via a sort. */
+float orc_kth_largest(const float *z, int32_t V, int32_t k) {
+  float *tmp = (float *)malloc(sizeof(float) * (size_t)V);
+  memcpy(tmp, z, sizeof(float) * (size_t)V);
+  qsort(tmp, (size_t)V, sizeof(float), cmp_float_desc);
+  float tau = tmp[k - 1];
+  free(tmp);
+  return tau;
+}
+
+/* Top-k (page 4: top_k < 1 means the whole vocabulary): every logit below the
+ * k-th largest is removed; ties with the k-th largest are all kept. */
+void orc_top_k_mask(float *z, int32_t V, int32_t k) {
+  if (k < 1 || k >= V) return;
+  float tau = orc_kth_largest(z, V, k);
+  for (int32_t x = 0; x < V; ++x)
+    if (z[x] < tau) z[x] = -INFINITY;
+}
+
+/* First index of the maximum (lowest index wins ties). */
+int32_t orc_argmax(const float *z, int32_t V) {
+  int32_t best = 0;
+  for (int32_t x = 1; x < V; ++x)
+    if (z[x] > z[best]) best = x;
+  return best;
+}
+
+/* Temperature-scaled softmax in fp64 (page 2, 8.2). */
+int orc_softmax(const float *z, int32_t V, double T, double *p) {
+  double m = -INFINITY;
+  for (int32_t x = 0; x < V; ++x) {
+    double t = (double)z[x] / T;
+    if (t > m) m = t;
+  }
+  if (!isfinite(m)) return ORC_ERR_ROW;
+  double s = 0.0;
+  for (int32_t x = 0; x < V; ++x) {
+    p[x] = exp((double)z[x] / T - m);
+    s += p[x];
+  }
+  for (int32_t x = 0; x < V; ++x) p[x] /= s;
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Exponential race.  argmax_x w_x / E_x with E_x ~ Exp(1) i.i.d. picks x with  */
+/* probability w_x / sum(w) (page 2, NO_DRAFT_PROBS Q&A: no normalisation is   */
+/* needed before the argmax).  Two levels: first a chunk c with weight M_c =   */
+/* sum of w over the chunk, raced with one Exp(1) per chunk, then a token      */
+/* inside the winning chunk raced with one Exp(1) per token; the product of    */
+/* the two laws is (M_c / sum M)(w_x / M_c) = w_x / sum(w).  Ties go to the    */
+/* lowest index.  C >= V reduces to the one-level race over all tokens.        */
+/* ------------------------------------------------------------------------ */
+static void keep_top2(double score, int32_t idx, double *b1, int32_t *i1, double *b2) {
+  if (*i1 < 0 || score > *b1) {
+    if (*i1 >= 0) *b2 = *b1;
+    *b1 = score;
+    *i1 = idx;
+  } else if (score > *b2) {
+    *b2 = score;
+  }
+}
+
+static double level_margin(double b1, double b2, int have_second) {
+  if (!have_second) return 1.0;
+  if (!(b1 > 0.0)) return 0.0;
+  return 1.0 - b2 / b1;
+}
+
+int32_t orc_race(const double *w, int32_t V, int32_t C, uint64_t seed, uint32_t offset,
+                 uint32_t g, double *margin) {
+  int32_t nchunks = (V + C - 1) / C;
+  double b1 = 0.0, b2 = -1.0;
+  int32_t c_best = -1, ncand = 0;
+  for (int32_t c = 0; c < nchunks; ++c) {
+    int32_t lo = c * C, hi = lo + C < V ? lo + C : V;
+    double M = 0.0;
+    for (int32_t x = lo; x < hi; ++x) M += w[x];
+    if (!(M > 0.0)) continue;
+    double score = M / orc_exp_noise(seed, offset, g, ORC_TAG_CHUNK, (uint32_t)c);
+    keep_top2(score, c, &b1, &c_best, &b2);
+    ++ncand;
+  }
+  if (c_best < 0) {
+    if (margin) *margin = 1.0;
+    return -1;
+  }
+  double m1 = level_margin(b1, b2, ncand > 1);
+
+  double t1 = 0.0, t2 = -1.0;
+  int32_t x_best = -1, tcand = 0;
+  int32_t lo = c_best * C, hi = lo + C < V ? lo + C : V;
+  for (int32_t x = lo; x < hi; ++x) {
+    if (!(w[x] > 0.0)) continue;
+    double score = w[x] / orc_exp_noise(seed, offset, g, ORC_TAG_TOKEN, (uint32_t)x);
+    keep_top2(score, x, &t1, &x_best, &t2);
+    ++tcand;
+  }
+  double m2 = level_margin(t1, t2, tcand > 1);
+  if (margin) *margin = m1 < m2 ? m1 : m2;
+  return x_best;
+}
+
+/* ------------------------------------------------------------------------ */
+/* One request                                                               */
+/* ------------------------------------------------------------------------ */
+static void load_row(const void *rows, int dtype, int64_t stride, int32_t i, int32_t V, float *z) {
+  if (dtype == ORC_BF16) {
+    const uint16_t *r = (const uint16_t *)rows + (int64_t)i * stride;
+    for (int32_t x = 0; x < V; ++x) z[x] = orc_bf16_to_f32(r[x]);
+  } else {
+    const float *r = (const float *)rows + (int64_t)i * stride;
+    memcpy(z, r, sizeof(float) * (size_t)V);
+  }
+}
+
+/* Order of processing (page 2, 8.2): logits processors (the repetition penalty)
+ * -> sampling constraints (top-k) -> temperature and softmax.  Temperature 0
+ * selects the greedy rule, which needs only the argmax of the processed logits. */
+int orc_prepare_request(const void *rows, int dtype, int64_t stride, int32_t K, int32_t V,
+                        float T, int32_t top_k, const float *theta, const int32_t *counts,
+                        double *P, int32_t *amax) {
+  if (!(T >= 0.0f) || !isfinite(T)) return ORC_ERR_TEMPERATURE;
+  if (theta && !(isfinite(*theta) && *theta > 0.0f)) return ORC_ERR_PENALTY;
+  int err = 0;
+  float *z = (float *)malloc(sizeof(float) * (size_t)V);
+  for (int32_t i = 0; i <= K; ++i) {
+    load_row(rows, dtype, stride, i, V, z);
+    if (theta && counts && *theta != 1.0f) orc_repetition_penalty(z, counts, V, *theta);
+    orc_top_k_mask(z, V, top_k);
+    amax[i] = orc_argmax(z, V);
+    double *p = P + (int64_t)i * V;
+    if (!isfinite(z[amax[i]])) {
+      err |= ORC_ERR_ROW;
+      continue;
+    }
+    if (T == 0.0f) {
+      for (int32_t x = 0; x < V; ++x) p[x] = 0.0;
+      p[amax[i]] = 1.0;
+    } else {
+      err |= orc_softmax(z, V, (double)T, p);
+    }
+  }
+  free(z);
+  return err;
+}
+
+double orc_decide_request(const double *P, const int32_t *amax, int32_t K, int32_t V, float T,
+                          const int32_t *draft_ids, const float *draft_probs, int64_t dstride,
+                          uint32_t g0, uint64_t seed, uint32_t offset, int32_t C,
+                          int32_t *tokens, int32_t *num_sampled, int32_t *num_rejected,
+                          float *p_draft) {
+  double margin = INFINITY;
+
+  if (T == 0.0f) {
+    /* Greedy (page 2, 8.3): output the target argmax at each position, stop
+     * after the first position whose draft differs; bonus argmax if none did. */
+    for (int32_t i = 0; i < K; ++i)
+      if (p_draft) p_draft[i] = -1.0f;
+    for (int32_t i = 0; i < K; ++i) {
+      tokens[i] = amax[i];
+      if (draft_ids[i] != amax[i]) {
+        *num_sampled = i + 1;
+        *num_rejected = K - i;
+        return margin;
+      }
+    }
+    tokens[K] = amax[K];
+    *num_sampled = K + 1;
+    *num_rejected = 0;
+    return margin;
+  }
+
+  /* Target probability of every draft (page 2, 8.3: target_prob at the draft). */
+  if (p_draft)
+    for (int32_t i = 0; i < K; ++i) {
+      int32_t d = draft_ids[i];
+      p_draft[i] = (d >= 0 && d < V) ? (float)P[(int64_t)i * V + d] : 0.0f;
+    }
+
+  /* Accept loop (page 2, 8.3 and the Q&A on min(1, p/q)): draft i is accepted
+   * when it is a valid id, q(d) > 0 and p(d) >= u * q(d); q = 1 without draft
+   * probabilities (NO_DRAFT_PROBS Q&A).  The first reject ends the loop. */
+  int32_t j = K;
+  for (int32_t i = 0; i < K; ++i) {
+    int32_t d = draft_ids[i];
+    int valid = d >= 0 && d < V;
+    double q = 1.0;
+    if (draft_probs) q = valid ? (double)draft_probs[(int64_t)i * dstride + d] : 0.0;
+    double u = orc_uniform_accept(orc_word(seed, offset, g0 + (uint32_t)i, ORC_TAG_ACCEPT, 0));
+    if (!valid || !(q > 0.0)) {
+      j = i;
+      break;
+    }
+    double p = P[(int64_t)i * V + d];
+    double uq = u * q;
+    double mg = fabs(p - uq) / (p > uq ? p : uq);
+    if (mg < margin) margin = mg;
+    if (!(p >= uq)) {
+      j = i;
+      break;
+    }
+  }
+  for (int32_t i = 0; i < j; ++i) tokens[i] = draft_ids[i];
+
+  /* The sampled row: recovered token at the reject, else the bonus row
+   * (page 2, Q&A on the bonus token: only when every draft was accepted). */
+  double *w = (double *)malloc(sizeof(double) * (size_t)V);
+  const double *pj = P + (int64_t)j * V;
+  if (j < K) {
+    int32_t d = draft_ids[j];
+    double total = 0.0;
+    if (draft_probs) {
+      /* Residual max(0, p - q), unnormalised (page 2, residual Q&A; page 3, 7.0). */
+      const float *qj = draft_probs + (int64_t)j * dstride;
+      for (int32_t x = 0; x < V; ++x) {
+        double r = pj[x] - (double)qj[x];
+        w[x] = r > 0.0 ? r : 0.0;
+        total += w[x];
+      }
+    } else {
+      /* q is the point mass at d: the residual is p with d removed. */
+      for (int32_t x = 0; x < V; ++x) w[x] = pj[x];
+      if (d >= 0 && d < V) w[d] = 0.0;
+      for (int32_t x = 0; x < V; ++x) total += w[x];
+    }
+    /* A reject with no residual mass can only come from rounding; race over p. */
+    if (!(total > 0.0))
+      for (int32_t x = 0; x < V; ++x) w[x] = pj[x];
+  } else {
+    for (int32_t x = 0; x < V; ++x) w[x] = pj[x];
+  }
+  double mg = 1.0;
+  tokens[j] = orc_race(w, V, C, seed, offset, g0 + (uint32_t)j, &mg);
+  if (mg < margin) margin = mg;
+  free(w);
+  *num_sampled = j + 1;
+  *num_rejected = K - j;
+  return margin;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Whole call                                                                */
+/* ------------------------------------------------------------------------ */
+uint32_t orc_verify_batch(const void *logits, int dtype, int64_t stride, int32_t num_rows,
+                          int32_t V, const float *draft_probs, int64_t dstride,
+                          const int32_t *draft_ids, const int32_t *cu, int32_t B,
+                          int32_t max_k, const float *temperature, const int32_t *top_k,
+                          const float *rep_penalty, const int32_t *idx_mapping,
+                          const int32_t *counts, int32_t num_slots, uint64_t seed,
+                          uint64_t offset, int32_t C, int32_t *out_tokens, int32_t out_stride,
+                          int32_t *num_sampled, int32_t *num_rejected, double *margin,
+                          float *p_draft) {
+  uint32_t err = 0;
+  int32_t D = num_rows - B;
+  for (int32_t r = 0; r < B; ++r) {
+    for (int32_t t = 0; t < out_stride; ++t) out_tokens[(int64_t)r * out_stride + t] = -1;
+    num_sampled[r] = 0;
+    num_rejected[r] = 0;
+    if (margin) margin[r] = INFINITY;
+  }
+  if (offset >> 32) return ORC_ERR_OFFSET;
+
+  /* cu_num_draft: prefix sums of the per-request draft counts (page 1, the
+   * rejection_sample inputs), so request r owns target rows cu[r]+r .. cu[r+1]+r,
+   * the last of which is its bonus row. */
+  int cu_ok = cu[0] == 0 && cu[B] == D;
+  for (int32_t r = 0; r < B && cu_ok; ++r)
+    if (cu[r + 1] < cu[r] || cu[r + 1] - cu[r] > max_k || cu[r + 1] - cu[r] + 1 > out_stride)
+      cu_ok = 0;
+  if (!cu_ok) return ORC_ERR_CU;
+
+  for (int32_t r = 0; r < B; ++r) {
+    int32_t K = cu[r + 1] - cu[r];
+    int32_t g0 = cu[r] + r;
+    float T = temperature[r];
+    int32_t k = top_k ? top_k[r] : 0;
+    const float *theta = rep_penalty ? &rep_penalty[r] : NULL;
+    const int32_t *counts_row = NULL;
+    if (theta && isfinite(*theta) && *theta > 0.0f && *theta != 1.0f) {
+      int32_t slot = idx_mapping[r];
+      if (slot < 0 || slot >= num_slots) {
+        err |= ORC_ERR_SLOT;
+        continue;
+      }
+      counts_row = counts + (int64_t)slot * V;
+    }
+    double *P = (double *)malloc(sizeof(double) * (size_t)(K + 1) * (size_t)V);
+    int32_t *amax = (int32_t *)malloc(sizeof(int32_t) * (size_t)(K + 1));
+    const void *rows = dtype == ORC_BF16 ? (const void *)((const uint16_t *)logits + (int64_t)g0 * stride)
+                                         : (const void *)((const float *)logits + (int64_t)g0 * stride);
+    int e = orc_prepare_request(rows, dtype, stride, K, V, T, k, theta, counts_row, P, amax);
+    if (e) {
+      err |= (uint32_t)e;
+    } else {
+      const float *q = draft_probs ? draft_probs + (int64_t)cu[r] * dstride : NULL;
+      double mg = orc_decide_request(P, amax, K, V, T, draft_ids + cu[r], q, dstride, (uint32_t)g0,
+                                     seed, (uint32_t)offset, C, out_tokens + (int64_t)r * out_stride,
+                                     &num_sampled[r], &num_rejected[r],
+                                     p_draft ? p_draft + cu[r] : NULL);
+      if (margin) margin[r] = mg;
+    }
+    free(P);
+    free(amax);
+  }
+  return err;
+}
+
+/* post_update (page 1, _post_update_kernel): for each request, add its sampled
+ * tokens to the slot's histogram, record the last sampled token, and advance
+ * num_computed_tokens by query_len - num_rejected. */
+uint32_t orc_post_update(const int32_t *idx_mapping, const int32_t *query_len,
+                         const int32_t *tokens, int32_t tokens_stride,
+                         const int32_t *num_sampled, const int32_t *num_rejected, int32_t B,
+                         int32_t V, int32_t num_slots, int32_t *last_sampled, int32_t *counts,
+                         int32_t *num_computed) {
+  uint32_t err = 0;
+  for (int32_t r = 0; r < B; ++r) {
+    int32_t n = num_sampled[r];
+    if (n <= 0) continue;
+    int32_t s = idx_mapping[r];
+    if (s < 0 || s >= num_slots) {
+      err |= ORC_ERR_SLOT;
+      continue;
+    }
+    const int32_t *tok = tokens + (int64_t)r * tokens_stride;
+    for (int32_t i = 0; i < n; ++i)
+      if (tok[i] >= 0 && tok[i] < V) counts[(int64_t)s * V + tok[i]] += 1;
+    last_sampled[s] = tok[n - 1];
+    num_computed[s] += query_len[r] - num_rejected[r];
+  }
+  return err;
+}
