@@ -1,0 +1,196 @@
+/*
+ * specverify.h -- C ABI of the MI355X (gfx950) speculative-decoding verify step.
+ *
+ * One call of spec_verify_run verifies a batch of B requests.  Request r
+ * proposed K_r draft tokens; the target model produced K_r + 1 logit rows for
+ * it (one per draft position plus the extra "bonus" row), packed request after
+ * request into target_logits [R, V] with R = sum_r (K_r + 1).  Request r owns
+ * rows cu[r] + r ... cu[r+1] + r, where cu = cu_num_draft is the prefix sum of
+ * the K_r (the layout of the target logits and the cu_num_logits prefix sums
+ * in "【vllm】DeepSeekMTP、eagle", sample() walk-through; bonus rows are the last
+ * row of each request as in "vLLM 投机解码（Eagle / MTP）实现与运行流程", 8.2).
+ *
+ * For each request the library computes, on the device:
+ *   1. processed logits z: repetition penalty (optional), then top-k (optional)
+ *      (8.2 of the second page: processors, constraints, then softmax);
+ *   2. p = softmax(z / T) per row (T = temperature[r]); T == 0 selects the
+ *      greedy rule of 8.3 (argmax of z, lowest index on ties);
+ *   3. for i = 0..K_r-1: accept draft d_i iff it is a valid id, q_i(d_i) > 0
+ *      and p_i(d_i) >= u_i * q_i(d_i) (q = 1 without draft probabilities),
+ *      u_i a Philox uniform on ((0,1]; 8.3, stochastic branch, and the
+ *      residual-distribution Q&A of the same page); stop at the first reject j;
+ *   4. after a reject: the recovered token from max(0, p_j - q_j), or, with no
+ *      draft probabilities, from p_j with d_j removed (NO_DRAFT_PROBS Q&A);
+ *      if every draft passed: the bonus token from row K_r (bonus Q&A);
+ *      sampling is a two-level exponential race argmax(w / E), E ~ Exp(1),
+ *      over chunks of SV_RACE_CHUNK tokens and then over the winning chunk's
+ *      tokens (its law is exactly w / sum w);
+ *   5. outputs: out_tokens[r][0..num_sampled) = accepted drafts then the
+ *      recovered or bonus token, -1 after; num_sampled = accepted + 1;
+ *      num_rejected = K_r - accepted.
+ * spec_post_update then applies the per-request bookkeeping of the first page's
+ * postprocess walk-through: last_sampled, output_bin_counts and
+ * num_computed_tokens += query_len - num_rejected.
+ *
+ * Random stream: Philox4x32-10 (Salmon et al., SC'11), key = (seed lo, seed
+ * hi), counter = (idx >> 2, target row g, tag, offset), word idx & 3; tag 0 is
+ * the accept uniform of row g (idx 0), tag 1 the chunk race (idx = chunk), tag
+ * 2 the token race (idx = token).  Accept uniform ((w >> 8) + 1) * 2^-24, race
+ * uniform (w >> 8) * 2^-24 with E = -ln U.  Results are a pure function of
+ * (inputs, seed, offset): the same call replays bit for bit.
+ *
+ * Conventions for every entry point:
+ *   - pointers in argument structs are DEVICE pointers unless stated; the
+ *     caller owns them and they must stay valid until the stream reaches the
+ *     work enqueued by the call;
+ *   - calls are stream-ordered and asynchronous; nothing synchronises the host
+ *     except spec_verify_read_error;
+ *   - a context is used by one stream at a time (not re-entrant);
+ *   - host-side checks (pointers, sizes, capacities, dtype) run before any
+ *     launch and return SV_EINVAL / SV_ECAPACITY / SV_EDTYPE with nothing
+ *     enqueued; a failed launch returns SV_EHIP;
+ *   - device-side checks set bits in the context's error word (read with
+ *     spec_verify_read_error).  A request whose temperature, penalty, slot or
+ *     rows are invalid gets num_sampled = num_rejected = 0 and a row of -1; an
+ *     invalid cu_num_draft leaves that call's outputs unspecified.  Every
+ *     memory access stays inside the buffers described here in all cases.
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SV_RACE_CHUNK 1024        /* tokens per chunk of the two-level race        */
+#define SV_MAX_DRAFTS 64          /* largest max_k a context accepts               */
+#define SV_TOPK_CANDIDATES 1024   /* top-k rows with more kept tokens use the dense path */
+
+typedef struct sv_ctx sv_ctx; /* opaque; owns the device scratch */
+
+/* Return codes. */
+enum {
+  SV_OK = 0,
+  SV_EINVAL = -1,    /* bad pointer, size or scalar                       */
+  SV_ECAPACITY = -2, /* exceeds the capacities given to spec_verify_create */
+  SV_EDTYPE = -3,    /* unknown logits dtype                               */
+  SV_EHIP = -4,      /* a HIP runtime call or kernel launch failed         */
+  SV_EINPUT = -5     /* device-side input check failed (see error bits)    */
+};
+
+/* Logits element types. */
+enum { SV_F32 = 0, SV_BF16 = 1 };
+
+/* Bits of the device error word. */
+enum {
+  SV_ERR_CU = 1u << 0,          /* cu_num_draft is not a valid prefix sum for this call */
+  SV_ERR_TEMPERATURE = 1u << 1, /* temperature < 0, NaN or infinite                      */
+  SV_ERR_PENALTY = 1u << 2,     /* repetition penalty <= 0, NaN or infinite              */
+  SV_ERR_ROW = 1u << 3,         /* a processed logit row has no finite maximum           */
+  SV_ERR_SLOT = 1u << 4         /* idx_mapping outside [0, num_slots)                    */
+};
+
+/* spec_verify_create flags. */
+enum {
+  SV_CREATE_TOPK = 1u << 0 /* reserve top-k candidate storage (needed for top_k != NULL) */
+};
+
+/*
+ * Create a context sized for calls with at most max_rows target rows,
+ * max_reqs requests, max_k drafts per request (<= SV_MAX_DRAFTS) and a
+ * vocabulary of at most max_vocab tokens.  Allocates device scratch on the
+ * current device (chunk tables of ceil(max_vocab / SV_RACE_CHUNK) entries per
+ * row, per-request counters; with SV_CREATE_TOPK also SV_TOPK_CANDIDATES
+ * candidates per row).  *out receives the context.  Errors: SV_EINVAL (NULL
+ * out, non-positive size), SV_ECAPACITY (max_k > SV_MAX_DRAFTS), SV_EHIP.
+ */
+int spec_verify_create(sv_ctx **out, int32_t max_rows, int32_t max_reqs, int32_t max_k,
+                       int32_t max_vocab, uint32_t flags);
+
+/* Free a context (synchronises the device first).  NULL is ignored. */
+void spec_verify_destroy(sv_ctx *ctx);
+
+typedef struct sv_verify_args {
+  const void *target_logits;        /* [num_rows, logits_row_stride], dtype logits_dtype    */
+  const float *draft_probs;         /* [D, draft_row_stride] fp32, or NULL: no-draft-probs  */
+                                    /* mode (q is the point mass at the draft), D = R - B   */
+  const int32_t *draft_ids;         /* [D]; ids outside [0, V) are simply rejected         */
+  const int32_t *cu_num_draft;      /* [num_reqs + 1]; cu[0] = 0, nondecreasing,            */
+                                    /* cu[B] = D, K_r <= out_stride - 1                     */
+  const float *temperature;         /* [num_reqs]; 0 = greedy, > 0 sampled                  */
+  const int32_t *top_k;             /* [num_reqs] or NULL; k < 1 or k >= V disables         */
+  const float *rep_penalty;         /* [num_reqs] or NULL; 1 = none                         */
+  const int32_t *idx_mapping;       /* [num_reqs] batch row -> state slot (with rep_penalty) */
+  const int32_t *output_bin_counts; /* [num_slots, vocab_size] (read here, with rep_penalty) */
+  int32_t *out_tokens;              /* [num_reqs, out_stride], -1 padded                    */
+  int32_t *out_num_sampled;         /* [num_reqs]                                           */
+  int32_t *out_num_rejected;        /* [num_reqs]                                           */
+  float *dbg_p_draft;               /* [D] p_i(d_i) (-1 for greedy requests) or NULL        */
+  float *dbg_probs;                 /* [num_rows, vocab_size] processed probabilities or   */
+                                    /* NULL; slow, for parity checks only                   */
+  int64_t logits_row_stride;        /* elements between rows, >= vocab_size                */
+  int64_t draft_row_stride;         /* elements between draft rows, >= vocab_size           */
+  uint64_t seed;                    /* Philox key                                           */
+  uint64_t offset;                  /* per-call step, must be < 2^32                        */
+  int32_t logits_dtype;             /* SV_F32 or SV_BF16                                    */
+  int32_t num_rows;                 /* R = cu[B] + B                                        */
+  int32_t num_reqs;                 /* B                                                    */
+  int32_t vocab_size;               /* V <= max_vocab                                       */
+  int32_t out_stride;               /* row length of out_tokens, <= max_k + 1               */
+  int32_t num_slots;                /* rows of output_bin_counts (0 without rep_penalty)    */
+} sv_verify_args;
+
+/*
+ * Enqueue one verify step on `stream` (see the top of this file).  Reads the
+ * target logits once per row in a streaming pass; in draft-probs mode it also
+ * reads the full draft row of each rejected request.  Errors: SV_EINVAL,
+ * SV_ECAPACITY, SV_EDTYPE, SV_EHIP (nothing enqueued on the first three).
+ */
+int spec_verify_run(sv_ctx *ctx, const sv_verify_args *args, hipStream_t stream);
+
+typedef struct sv_post_update_args {
+  const int32_t *idx_mapping;   /* [num_reqs] batch row -> state slot                     */
+  const int32_t *query_len;     /* [num_reqs] tokens scheduled for the request this step  */
+  const int32_t *tokens;        /* [num_reqs, tokens_stride] out_tokens of the verify step */
+  const int32_t *num_sampled;   /* [num_reqs]                                             */
+  const int32_t *num_rejected;  /* [num_reqs]                                             */
+  int32_t *last_sampled;        /* [num_slots] in/out                                     */
+  int32_t *output_bin_counts;   /* [num_slots, vocab_size] in/out                         */
+  int32_t *num_computed_tokens; /* [num_slots] in/out                                     */
+  int32_t num_reqs;
+  int32_t tokens_stride;
+  int32_t vocab_size;
+  int32_t num_slots;
+} sv_post_update_args;
+
+/*
+ * post_update ("【vllm】DeepSeekMTP、eagle", postprocess / _post_update_kernel):
+ * for every request with num_sampled > 0 and slot s = idx_mapping[r]:
+ * output_bin_counts[s][t] += 1 for each sampled token t in [0, V) (a token
+ * sampled twice counts twice), last_sampled[s] = the last sampled token,
+ * num_computed_tokens[s] += query_len[r] - num_rejected[r].  Slots outside
+ * [0, num_slots) are skipped and raise SV_ERR_SLOT.  Two requests of one call
+ * must not share a slot (counts stay exact, last_sampled is then either one).
+ * Errors: SV_EINVAL, SV_EHIP.
+ */
+int spec_post_update(sv_ctx *ctx, const sv_post_update_args *args, hipStream_t stream);
+
+/* Static string for a return code. */
+const char *spec_verify_strerror(int status);
+
+/*
+ * Synchronise `stream`, copy the device error word into *host_flags (a host
+ * pointer) and clear it.  Returns SV_OK when no bit was set, SV_EINPUT when
+ * some were, SV_EINVAL / SV_EHIP on failure.  For tests and debugging: it
+ * blocks the host.
+ */
+int spec_verify_read_error(sv_ctx *ctx, uint32_t *host_flags, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPECVERIFY_H */

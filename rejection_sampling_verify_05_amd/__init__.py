@@ -1,0 +1,288 @@
+"""Python binding of the MI355X speculative-decoding verify library.
+
+The library is the C ABI declared in ``include/specverify.h`` and built into
+``libspecverify.so`` (HIP, gfx950) next to this file.  This module only
+marshals arguments: torch tensors supply device pointers and the stream, and
+every step of the verify path runs in the library's kernels.  There is no
+fallback: if the shared library is missing or fails to load, every entry
+point raises.
+
+Entry points (same names as the C ABI):
+    spec_verify_create, spec_verify_destroy, spec_verify_run,
+    spec_post_update, spec_verify_strerror, spec_verify_read_error
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "SV_OK", "SV_EINVAL", "SV_ECAPACITY", "SV_EDTYPE", "SV_EHIP", "SV_EINPUT",
+    "SV_F32", "SV_BF16", "SV_CREATE_TOPK", "SV_RACE_CHUNK", "SV_MAX_DRAFTS",
+    "SV_ERR_CU", "SV_ERR_TEMPERATURE", "SV_ERR_PENALTY", "SV_ERR_ROW", "SV_ERR_SLOT",
+    "SpecVerifyError", "VerifyArgs", "PostUpdateArgs", "lib", "library_path",
+    "spec_verify_create", "spec_verify_destroy", "spec_verify_run", "spec_post_update",
+    "spec_verify_strerror", "spec_verify_read_error",
+]
+
+SV_OK, SV_EINVAL, SV_ECAPACITY, SV_EDTYPE, SV_EHIP, SV_EINPUT = 0, -1, -2, -3, -4, -5
+SV_F32, SV_BF16 = 0, 1
+SV_CREATE_TOPK = 1
+SV_RACE_CHUNK = 1024
+SV_MAX_DRAFTS = 64
+SV_TOPK_CANDIDATES = 1024
+SV_ERR_CU, SV_ERR_TEMPERATURE, SV_ERR_PENALTY, SV_ERR_ROW, SV_ERR_SLOT = 1, 2, 4, 8, 16
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SO = os.path.join(_HERE, "libspecverify.so")
+
+
+def library_path() -> str:
+    return _SO
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {spec_verify_strerror(status)} ({status})")
+
+
+class VerifyArgs(ctypes.Structure):
+    """Mirror of ``sv_verify_args``."""
+    _fields_ = [
+        ("target_logits", ctypes.c_void_p),
+        ("draft_probs", ctypes.c_void_p),
+        ("draft_ids", ctypes.c_void_p),
+        ("cu_num_draft", ctypes.c_void_p),
+        ("temperature", ctypes.c_void_p),
+        ("top_k", ctypes.c_void_p),
+        ("rep_penalty", ctypes.c_void_p),
+        ("idx_mapping", ctypes.c_void_p),
+        ("output_bin_counts", ctypes.c_void_p),
+        ("out_tokens", ctypes.c_void_p),
+        ("out_num_sampled", ctypes.c_void_p),
+        ("out_num_rejected", ctypes.c_void_p),
+        ("dbg_p_draft", ctypes.c_void_p),
+        ("dbg_probs", ctypes.c_void_p),
+        ("logits_row_stride", ctypes.c_int64),
+        ("draft_row_stride", ctypes.c_int64),
+        ("seed", ctypes.c_uint64),
+        ("offset", ctypes.c_uint64),
+        ("logits_dtype", ctypes.c_int32),
+        ("num_rows", ctypes.c_int32),
+        ("num_reqs", ctypes.c_int32),
+        ("vocab_size", ctypes.c_int32),
+        ("out_stride", ctypes.c_int32),
+        ("num_slots", ctypes.c_int32),
+    ]
+
+
+class PostUpdateArgs(ctypes.Structure):
+    """Mirror of ``sv_post_update_args``."""
+    _fields_ = [
+        ("idx_mapping", ctypes.c_void_p),
+        ("query_len", ctypes.c_void_p),
+        ("tokens", ctypes.c_void_p),
+        ("num_sampled", ctypes.c_void_p),
+        ("num_rejected", ctypes.c_void_p),
+        ("last_sampled", ctypes.c_void_p),
+        ("output_bin_counts", ctypes.c_void_p),
+        ("num_computed_tokens", ctypes.c_void_p),
+        ("num_reqs", ctypes.c_int32),
+        ("tokens_stride", ctypes.c_int32),
+        ("vocab_size", ctypes.c_int32),
+        ("num_slots", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libspecverify.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_SO):
+            raise ImportError(f"{_SO} is missing: build it with __graft_entry__.build() "
+                              "(python -c 'import __graft_entry__ as g; g.build()')")
+        L = ctypes.CDLL(_SO)
+        P = ctypes.c_void_p
+        L.spec_verify_create.argtypes = [ctypes.POINTER(P), ctypes.c_int32, ctypes.c_int32,
+                                         ctypes.c_int32, ctypes.c_int32, ctypes.c_uint32]
+        L.spec_verify_create.restype = ctypes.c_int
+        L.spec_verify_destroy.argtypes = [P]
+        L.spec_verify_destroy.restype = None
+        L.spec_verify_run.argtypes = [P, ctypes.POINTER(VerifyArgs), P]
+        L.spec_verify_run.restype = ctypes.c_int
+        L.spec_post_update.argtypes = [P, ctypes.POINTER(PostUpdateArgs), P]
+        L.spec_post_update.restype = ctypes.c_int
+        L.spec_verify_strerror.argtypes = [ctypes.c_int]
+        L.spec_verify_strerror.restype = ctypes.c_char_p
+        L.spec_verify_read_error.argtypes = [P, ctypes.POINTER(ctypes.c_uint32), P]
+        L.spec_verify_read_error.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+# ---------------------------------------------------------------------------
+# Marshalling helpers
+# ---------------------------------------------------------------------------
+def _stream_handle(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dev(t, dtype, name, ndim=None, contiguous=True):
+    import torch
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+# ---------------------------------------------------------------------------
+# Entry points
+# ---------------------------------------------------------------------------
+def spec_verify_strerror(status: int) -> str:
+    return lib().spec_verify_strerror(int(status)).decode()
+
+
+def spec_verify_create(max_rows: int, max_reqs: int, max_k: int, max_vocab: int,
+                       flags: int = 0) -> ctypes.c_void_p:
+    ctx = ctypes.c_void_p()
+    st = lib().spec_verify_create(ctypes.byref(ctx), max_rows, max_reqs, max_k, max_vocab, flags)
+    if st != SV_OK:
+        raise SpecVerifyError(st, "spec_verify_create")
+    return ctx
+
+
+def spec_verify_destroy(ctx) -> None:
+    lib().spec_verify_destroy(ctx)
+
+
+def make_verify_args(target_logits, draft_ids, cu_num_draft, temperature, out_tokens,
+                     out_num_sampled, out_num_rejected, *, draft_probs=None, top_k=None,
+                     rep_penalty=None, idx_mapping=None, output_bin_counts=None, seed=0,
+                     offset=0, dbg_p_draft=None, dbg_probs=None) -> VerifyArgs:
+    """Fill an sv_verify_args from torch tensors (no copies, no compute)."""
+    import torch
+    if target_logits.dim() != 2 or not target_logits.is_cuda or target_logits.stride(1) != 1:
+        raise ValueError("target_logits must be a 2-D CUDA tensor with unit column stride")
+    if target_logits.dtype == torch.float32:
+        dt = SV_F32
+    elif target_logits.dtype == torch.bfloat16:
+        dt = SV_BF16
+    else:
+        raise TypeError("target_logits must be float32 or bfloat16")
+    R, V = target_logits.shape
+    _dev(draft_ids, torch.int32, "draft_ids", 1)
+    _dev(cu_num_draft, torch.int32, "cu_num_draft", 1)
+    _dev(temperature, torch.float32, "temperature", 1)
+    _dev(out_tokens, torch.int32, "out_tokens", 2)
+    _dev(out_num_sampled, torch.int32, "out_num_sampled", 1)
+    _dev(out_num_rejected, torch.int32, "out_num_rejected", 1)
+    if draft_probs is not None:
+        _dev(draft_probs, torch.float32, "draft_probs", 2, contiguous=False)
+        if draft_probs.stride(1) != 1:
+            raise ValueError("draft_probs must have unit column stride")
+    _dev(top_k, torch.int32, "top_k", 1)
+    _dev(rep_penalty, torch.float32, "rep_penalty", 1)
+    _dev(idx_mapping, torch.int32, "idx_mapping", 1)
+    _dev(output_bin_counts, torch.int32, "output_bin_counts", 2)
+    _dev(dbg_p_draft, torch.float32, "dbg_p_draft", 1)
+    _dev(dbg_probs, torch.float32, "dbg_probs", 2)
+    B = cu_num_draft.numel() - 1
+    a = VerifyArgs()
+    a.target_logits = target_logits.data_ptr()
+    a.draft_probs = None if draft_probs is None else draft_probs.data_ptr()
+    a.draft_ids = draft_ids.data_ptr() if draft_ids.numel() else None
+    a.cu_num_draft = cu_num_draft.data_ptr()
+    a.temperature = temperature.data_ptr()
+    a.top_k = None if top_k is None else top_k.data_ptr()
+    a.rep_penalty = None if rep_penalty is None else rep_penalty.data_ptr()
+    a.idx_mapping = None if idx_mapping is None else idx_mapping.data_ptr()
+    a.output_bin_counts = None if output_bin_counts is None else output_bin_counts.data_ptr()
+    a.out_tokens = out_tokens.data_ptr()
+    a.out_num_sampled = out_num_sampled.data_ptr()
+    a.out_num_rejected = out_num_rejected.data_ptr()
+    a.dbg_p_draft = None if dbg_p_draft is None else dbg_p_draft.data_ptr()
+    a.dbg_probs = None if dbg_probs is None else dbg_probs.data_ptr()
+    a.logits_row_stride = target_logits.stride(0)
+    a.draft_row_stride = 0 if draft_probs is None else draft_probs.stride(0)
+    a.seed = int(seed)
+    a.offset = int(offset)
+    a.logits_dtype = dt
+    a.num_rows = R
+    a.num_reqs = B
+    a.vocab_size = V
+    a.out_stride = out_tokens.shape[1]
+    a.num_slots = 0 if output_bin_counts is None else output_bin_counts.shape[0]
+    return a
+
+
+def spec_verify_run(ctx, *args, stream=None, **kwargs) -> None:
+    """spec_verify_run(ctx, target_logits, draft_ids, cu_num_draft, temperature,
+    out_tokens, out_num_sampled, out_num_rejected, *, draft_probs=None, top_k=None,
+    rep_penalty=None, idx_mapping=None, output_bin_counts=None, seed=0, offset=0,
+    dbg_p_draft=None, dbg_probs=None, stream=None), or spec_verify_run(ctx, VerifyArgs)."""
+    a = args[0] if len(args) == 1 and isinstance(args[0], VerifyArgs) else make_verify_args(*args, **kwargs)
+    st = lib().spec_verify_run(ctx, ctypes.byref(a), _stream_handle(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "spec_verify_run")
+
+
+def make_post_update_args(idx_mapping, query_len, tokens, num_sampled, num_rejected,
+                          last_sampled, output_bin_counts, num_computed_tokens) -> PostUpdateArgs:
+    import torch
+    for t, n, d in [(idx_mapping, "idx_mapping", 1), (query_len, "query_len", 1),
+                    (tokens, "tokens", 2), (num_sampled, "num_sampled", 1),
+                    (num_rejected, "num_rejected", 1), (last_sampled, "last_sampled", 1),
+                    (output_bin_counts, "output_bin_counts", 2),
+                    (num_computed_tokens, "num_computed_tokens", 1)]:
+        _dev(t, torch.int32, n, d)
+    a = PostUpdateArgs()
+    a.idx_mapping = idx_mapping.data_ptr()
+    a.query_len = query_len.data_ptr()
+    a.tokens = tokens.data_ptr()
+    a.num_sampled = num_sampled.data_ptr()
+    a.num_rejected = num_rejected.data_ptr()
+    a.last_sampled = last_sampled.data_ptr()
+    a.output_bin_counts = output_bin_counts.data_ptr()
+    a.num_computed_tokens = num_computed_tokens.data_ptr()
+    a.num_reqs = idx_mapping.numel()
+    a.tokens_stride = tokens.shape[1]
+    a.vocab_size = output_bin_counts.shape[1]
+    a.num_slots = output_bin_counts.shape[0]
+    return a
+
+
+def spec_post_update(ctx, *args, stream=None) -> None:
+    """spec_post_update(ctx, idx_mapping, query_len, tokens, num_sampled, num_rejected,
+    last_sampled, output_bin_counts, num_computed_tokens, stream=None), or with a
+    PostUpdateArgs."""
+    a = args[0] if len(args) == 1 and isinstance(args[0], PostUpdateArgs) else make_post_update_args(*args)
+    st = lib().spec_post_update(ctx, ctypes.byref(a), _stream_handle(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "spec_post_update")
+
+
+def spec_verify_read_error(ctx, stream=None) -> int:
+    """Synchronise the stream and return (and clear) the device error bits."""
+    flags = ctypes.c_uint32(0)
+    st = lib().spec_verify_read_error(ctx, ctypes.byref(flags), _stream_handle(stream))
+    if st not in (SV_OK, SV_EINPUT):
+        raise SpecVerifyError(st, "spec_verify_read_error")
+    return int(flags.value)

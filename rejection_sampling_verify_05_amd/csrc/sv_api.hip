@@ -1,0 +1,226 @@
+// sv_api.hip -- C ABI of the verify library (declared in include/specverify.h):
+// context and scratch ownership, host-side argument checks, launch sequencing.
+#include <stdint.h>
+#include <string.h>
+
+#include <new>
+
+#include <hip/hip_runtime.h>
+
+#include "specverify.h"
+#include "sv_internal.h"
+
+struct sv_ctx {
+  int device;
+  int32_t max_rows, max_reqs, max_k, max_vocab;
+  uint32_t flags;
+  int32_t nc_stride;
+  uint32_t epoch;
+  float2 *chunk_tab;
+  float4 *row_info;
+  unsigned long long *req_ctr;
+  unsigned long long *res_ctr;
+  int4 *res_req;
+  float *res_tab;
+  float *cand_val;
+  int32_t *cand_idx;
+  int32_t *cand_n;
+  float *cand_tau;
+  unsigned int *err;
+};
+
+namespace {
+
+void free_ctx(sv_ctx *c) {
+  void *ptrs[] = {c->chunk_tab, c->row_info, c->req_ctr, c->res_ctr, c->res_req, c->res_tab,
+                  c->cand_val,  c->cand_idx, c->cand_n,  c->cand_tau, c->err};
+  for (void *p : ptrs)
+    if (p) (void)hipFree(p);
+  delete c;
+}
+
+template <class T>
+bool dev_alloc(T **p, size_t count) {
+  *p = nullptr;
+  if (count == 0) count = 1;
+  return hipMalloc(reinterpret_cast<void **>(p), sizeof(T) * count) == hipSuccess;
+}
+
+}  // namespace
+
+extern "C" int spec_verify_create(sv_ctx **out, int32_t max_rows, int32_t max_reqs, int32_t max_k,
+                                  int32_t max_vocab, uint32_t flags) {
+  if (!out) return SV_EINVAL;
+  *out = nullptr;
+  if (max_rows <= 0 || max_reqs <= 0 || max_k < 0 || max_vocab <= 0) return SV_EINVAL;
+  if (max_k > SV_MAX_DRAFTS || max_rows > (1 << 30) / 2) return SV_ECAPACITY;
+  if ((flags & ~(uint32_t)SV_CREATE_TOPK) != 0) return SV_EINVAL;
+  sv_ctx *c = new (std::nothrow) sv_ctx();
+  if (!c) return SV_EHIP;
+  if (hipGetDevice(&c->device) != hipSuccess) {
+    delete c;
+    return SV_EHIP;
+  }
+  c->max_rows = max_rows;
+  c->max_reqs = max_reqs;
+  c->max_k = max_k;
+  c->max_vocab = max_vocab;
+  c->flags = flags;
+  c->nc_stride = (max_vocab + sv::kChunk - 1) / sv::kChunk;
+  c->epoch = 0;
+  const size_t rows = (size_t)max_rows, reqs = (size_t)max_reqs, ncs = (size_t)c->nc_stride;
+  bool ok = dev_alloc(&c->chunk_tab, rows * ncs) && dev_alloc(&c->row_info, rows) &&
+            dev_alloc(&c->req_ctr, reqs) && dev_alloc(&c->res_ctr, reqs) && dev_alloc(&c->res_req, reqs) &&
+            dev_alloc(&c->res_tab, reqs * ncs) && dev_alloc(&c->err, 1);
+  if (ok && (flags & SV_CREATE_TOPK))
+    ok = dev_alloc(&c->cand_val, rows * sv::kCandCap) && dev_alloc(&c->cand_idx, rows * sv::kCandCap) &&
+         dev_alloc(&c->cand_n, rows) && dev_alloc(&c->cand_tau, rows);
+  if (ok)
+    ok = hipMemset(c->req_ctr, 0, reqs * sizeof(unsigned long long)) == hipSuccess &&
+         hipMemset(c->res_ctr, 0, reqs * sizeof(unsigned long long)) == hipSuccess &&
+         hipMemset(c->res_req, 0, reqs * sizeof(int4)) == hipSuccess &&
+         hipMemset(c->err, 0, sizeof(unsigned int)) == hipSuccess && hipDeviceSynchronize() == hipSuccess;
+  if (!ok) {
+    free_ctx(c);
+    return SV_EHIP;
+  }
+  *out = c;
+  return SV_OK;
+}
+
+extern "C" void spec_verify_destroy(sv_ctx *ctx) {
+  if (!ctx) return;
+  (void)hipDeviceSynchronize();
+  free_ctx(ctx);
+}
+
+extern "C" int spec_verify_run(sv_ctx *ctx, const sv_verify_args *a, hipStream_t stream) {
+  if (!ctx || !a) return SV_EINVAL;
+  if (a->logits_dtype != SV_F32 && a->logits_dtype != SV_BF16) return SV_EDTYPE;
+  if (a->num_reqs < 0 || a->vocab_size <= 0 || a->num_rows < a->num_reqs) return SV_EINVAL;
+  if (a->num_reqs == 0) return SV_OK;
+  if (a->num_rows > ctx->max_rows || a->num_reqs > ctx->max_reqs || a->vocab_size > ctx->max_vocab)
+    return SV_ECAPACITY;
+  if (a->out_stride < 1) return SV_EINVAL;
+  if (a->out_stride > ctx->max_k + 1) return SV_ECAPACITY;
+  const int32_t D = a->num_rows - a->num_reqs;
+  if (!a->target_logits || !a->cu_num_draft || !a->temperature || !a->out_tokens || !a->out_num_sampled ||
+      !a->out_num_rejected)
+    return SV_EINVAL;
+  if (D > 0 && !a->draft_ids) return SV_EINVAL;
+  if (a->logits_row_stride < a->vocab_size) return SV_EINVAL;
+  if (a->draft_probs && a->draft_row_stride < a->vocab_size) return SV_EINVAL;
+  if (a->offset >> 32) return SV_EINVAL;
+  if (a->rep_penalty && (!a->idx_mapping || !a->output_bin_counts || a->num_slots < 1)) return SV_EINVAL;
+  if (a->top_k && !(ctx->flags & SV_CREATE_TOPK)) return SV_ECAPACITY;
+
+  sv::Params p;
+  memset(&p, 0, sizeof p);
+  p.logits = a->target_logits;
+  p.draft_probs = a->draft_probs;
+  p.draft_ids = a->draft_ids;
+  p.cu = a->cu_num_draft;
+  p.temperature = a->temperature;
+  p.top_k = a->top_k;
+  p.rep_penalty = a->rep_penalty;
+  p.idx_mapping = a->idx_mapping;
+  p.counts = a->output_bin_counts;
+  p.out_tokens = a->out_tokens;
+  p.out_ns = a->out_num_sampled;
+  p.out_nr = a->out_num_rejected;
+  p.dbg_p_draft = a->dbg_p_draft;
+  p.dbg_probs = a->dbg_probs;
+  p.chunk_tab = ctx->chunk_tab;
+  p.row_info = ctx->row_info;
+  p.req_ctr = ctx->req_ctr;
+  p.res_ctr = ctx->res_ctr;
+  p.res_req = ctx->res_req;
+  p.res_tab = ctx->res_tab;
+  p.cand_val = ctx->cand_val;
+  p.cand_idx = ctx->cand_idx;
+  p.cand_n = ctx->cand_n;
+  p.cand_tau = ctx->cand_tau;
+  p.err = ctx->err;
+  p.lstride = a->logits_row_stride;
+  p.dstride = a->draft_probs ? a->draft_row_stride : 0;
+  p.dtype = a->logits_dtype;
+  p.R = a->num_rows;
+  p.B = a->num_reqs;
+  p.D = D;
+  p.V = a->vocab_size;
+  p.NC = (a->vocab_size + sv::kChunk - 1) / sv::kChunk;
+  p.nc_stride = ctx->nc_stride;
+  p.cps = sv::kWaves * sv::kStatsCPW;
+  p.nseg = (p.NC + p.cps - 1) / p.cps;
+  p.out_stride = a->out_stride;
+  p.num_slots = a->rep_penalty ? a->num_slots : 0;
+  const int esize = a->logits_dtype == SV_BF16 ? 2 : 4;
+  p.vec_ok = ((uintptr_t)a->target_logits % 16 == 0) && ((a->logits_row_stride * esize) % 16 == 0);
+  p.has_topk = a->top_k ? 1 : 0;
+  p.seed_lo = (uint32_t)(a->seed & 0xFFFFFFFFu);
+  p.seed_hi = (uint32_t)(a->seed >> 32);
+  p.offset = (uint32_t)a->offset;
+  ctx->epoch = ctx->epoch == 0xFFFFFFFFu ? 1u : ctx->epoch + 1u;
+  p.epoch = ctx->epoch;
+
+  if ((int64_t)p.R * p.nseg > 0x7FFFFFFF) return SV_ECAPACITY;
+
+  if (p.has_topk && sv::launch_topk(p, stream) != hipSuccess) return SV_EHIP;
+  if (sv::launch_stats(p, stream) != hipSuccess) return SV_EHIP;
+  if (p.draft_probs && sv::launch_resid(p, stream) != hipSuccess) return SV_EHIP;
+  if (p.dbg_probs && sv::launch_dbg_probs(p, stream) != hipSuccess) return SV_EHIP;
+  return SV_OK;
+}
+
+extern "C" int spec_post_update(sv_ctx *ctx, const sv_post_update_args *a, hipStream_t stream) {
+  if (!ctx || !a) return SV_EINVAL;
+  if (a->num_reqs < 0 || a->tokens_stride < 1 || a->vocab_size <= 0 || a->num_slots < 1) return SV_EINVAL;
+  if (a->num_reqs == 0) return SV_OK;
+  if (!a->idx_mapping || !a->query_len || !a->tokens || !a->num_sampled || !a->num_rejected ||
+      !a->last_sampled || !a->output_bin_counts || !a->num_computed_tokens)
+    return SV_EINVAL;
+  sv::PostParams p;
+  p.idx_mapping = a->idx_mapping;
+  p.query_len = a->query_len;
+  p.tokens = a->tokens;
+  p.num_sampled = a->num_sampled;
+  p.num_rejected = a->num_rejected;
+  p.last_sampled = a->last_sampled;
+  p.counts = a->output_bin_counts;
+  p.num_computed = a->num_computed_tokens;
+  p.B = a->num_reqs;
+  p.tokens_stride = a->tokens_stride;
+  p.V = a->vocab_size;
+  p.num_slots = a->num_slots;
+  p.err = ctx->err;
+  return sv::launch_post_update(p, stream) == hipSuccess ? SV_OK : SV_EHIP;
+}
+
+extern "C" const char *spec_verify_strerror(int status) {
+  switch (status) {
+    case SV_OK:
+      return "ok";
+    case SV_EINVAL:
+      return "invalid argument";
+    case SV_ECAPACITY:
+      return "exceeds context capacity";
+    case SV_EDTYPE:
+      return "unsupported logits dtype";
+    case SV_EHIP:
+      return "HIP runtime error";
+    case SV_EINPUT:
+      return "device-side input check failed";
+    default:
+      return "unknown status";
+  }
+}
+
+extern "C" int spec_verify_read_error(sv_ctx *ctx, uint32_t *host_flags, hipStream_t stream) {
+  if (!ctx || !host_flags) return SV_EINVAL;
+  unsigned int h = 0;
+  if (hipStreamSynchronize(stream) != hipSuccess) return SV_EHIP;
+  if (hipMemcpy(&h, ctx->err, sizeof h, hipMemcpyDeviceToHost) != hipSuccess) return SV_EHIP;
+  if (hipMemset(ctx->err, 0, sizeof h) != hipSuccess) return SV_EHIP;
+  *host_flags = h;
+  return h ? SV_EINPUT : SV_OK;
+}

@@ -1,0 +1,204 @@
+// sv_device.h -- gfx950 device helpers for the verify kernels: the Philox
+// counter stream, wave64 reductions built on DPP row operations, block
+// reductions through LDS, and logit-row access.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "sv_internal.h"
+
+namespace sv {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two 32x32
+// multiplies whose high halves are xored with the other counter words and the
+// round key; the key advances by the golden-ratio Weyl increments.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint4 philox10(uint4 ctr, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int round = 0; round < 10; ++round) {
+    const uint32_t m0 = 0xD2511F53u, m1 = 0xCD9E8D57u;
+    uint32_t hi0 = __umulhi(m0, ctr.x), lo0 = m0 * ctr.x;
+    uint32_t hi1 = __umulhi(m1, ctr.z), lo1 = m1 * ctr.z;
+    ctr = make_uint4(hi1 ^ ctr.y ^ k0, lo1, hi0 ^ ctr.w ^ k1, lo0);
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return ctr;
+}
+
+enum : uint32_t { kTagAccept = 0, kTagChunk = 1, kTagToken = 2 };
+
+// Four consecutive words idx = 4*blk .. 4*blk+3 of stream (g, tag).
+__device__ __forceinline__ uint4 rng_block(const Params &p, uint32_t blk, uint32_t g, uint32_t tag) {
+  return philox10(make_uint4(blk, g, tag, p.offset), p.seed_lo, p.seed_hi);
+}
+
+__device__ __forceinline__ uint32_t pick(uint4 w, int k) {
+  return k == 0 ? w.x : k == 1 ? w.y : k == 2 ? w.z : w.w;
+}
+
+// Accept uniform ((w>>8)+1) 2^-24 in (0,1]; exact in fp64.
+__device__ __forceinline__ double u_accept(uint32_t w) { return (double)((w >> 8) + 1u) * 0x1p-24; }
+
+// Exp(1) noise from the race uniform (w>>8) 2^-24 in [0,1); U = 0 -> +inf.
+__device__ __forceinline__ double exp_noise(uint32_t w) {
+  uint32_t k = w >> 8;
+  if (k == 0) return __builtin_huge_val();
+  return -log((double)k * 0x1p-24);
+}
+
+// ---------------------------------------------------------------------------
+// wave64 reductions.  Within a 16-lane row: quad_perm swaps and the two
+// mirrors leave the row total in every lane; the four row totals are then
+// combined through readlane (uniform result).
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+constexpr int kQuad1032 = 0xB1, kQuad2301 = 0x4E, kHalfMirror = 0x141, kMirror = 0x140;
+
+__device__ __forceinline__ float rd(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_f<kQuad1032>(v));
+  v = fmaxf(v, dpp_f<kQuad2301>(v));
+  v = fmaxf(v, dpp_f<kHalfMirror>(v));
+  v = fmaxf(v, dpp_f<kMirror>(v));
+  return fmaxf(fmaxf(rd(v, 0), rd(v, 16)), fmaxf(rd(v, 32), rd(v, 48)));
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_f<kQuad1032>(v);
+  v += dpp_f<kQuad2301>(v);
+  v += dpp_f<kHalfMirror>(v);
+  v += dpp_f<kMirror>(v);
+  return (rd(v, 0) + rd(v, 16)) + (rd(v, 32) + rd(v, 48));
+}
+
+__device__ __forceinline__ int wave_min_i(int v) {
+  v = min(v, dpp_i<kQuad1032>(v));
+  v = min(v, dpp_i<kQuad2301>(v));
+  v = min(v, dpp_i<kHalfMirror>(v));
+  v = min(v, dpp_i<kMirror>(v));
+  return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+             min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+
+// (score, index) arg-max with the lowest index winning ties; non-candidates
+// carry score -1 (real scores are >= 0).
+struct ArgMax {
+  double s;
+  int i;
+};
+__device__ __forceinline__ bool better(ArgMax a, ArgMax b) { return a.s > b.s || (a.s == b.s && a.i < b.i); }
+
+__device__ __forceinline__ ArgMax wave_argmax(ArgMax a) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    ArgMax o{__shfl_xor(a.s, off), __shfl_xor(a.i, off)};
+    if (better(o, a)) a = o;
+  }
+  return a;
+}
+
+// Block-wide (256 threads) reductions; every thread gets the result.
+struct BlockScratch {
+  double s[kWaves];
+  int i[kWaves];
+  float f[kWaves];
+};
+
+__device__ __forceinline__ ArgMax block_argmax(ArgMax a, BlockScratch &sh) {
+  a = wave_argmax(a);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) {
+    sh.s[w] = a.s;
+    sh.i[w] = a.i;
+  }
+  __syncthreads();
+  ArgMax b{sh.s[0], sh.i[0]};
+#pragma unroll
+  for (int k = 1; k < kWaves; ++k) {
+    ArgMax o{sh.s[k], sh.i[k]};
+    if (better(o, b)) b = o;
+  }
+  return b;
+}
+
+__device__ __forceinline__ float block_sum(float v, BlockScratch &sh) {
+  v = wave_sum(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh.f[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float t = 0.f;
+#pragma unroll
+  for (int k = 0; k < kWaves; ++k) t += sh.f[k];
+  return t;
+}
+
+__device__ __forceinline__ float block_max(float v, BlockScratch &sh) {
+  v = wave_max(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh.f[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float t = sh.f[0];
+#pragma unroll
+  for (int k = 1; k < kWaves; ++k) t = fmaxf(t, sh.f[k]);
+  return t;
+}
+
+// ---------------------------------------------------------------------------
+// Logit access
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+__device__ __forceinline__ float load_logit(const Params &p, int64_t row, int x) {
+  if (p.dtype == 1) {
+    const uint16_t *b = static_cast<const uint16_t *>(p.logits);
+    return bf16_bits_to_f32(b[row * p.lstride + x]);
+  }
+  return static_cast<const float *>(p.logits)[row * p.lstride + x];
+}
+
+// Per-request logit processing (penalty, then the top-k threshold).
+struct Proc {
+  const int32_t *counts; // counts row or nullptr (no penalty)
+  float theta;
+  float tau;             // -inf: no threshold
+};
+
+__device__ __forceinline__ float apply_proc(float z, int x, const Proc &pr) {
+  if (pr.counts != nullptr && pr.counts[x] > 0) z = z > 0.0f ? z / pr.theta : z * pr.theta;
+  return z < pr.tau ? -__builtin_inff() : z;
+}
+
+// Largest r in [0, B) with cu[r] + r <= g (cu nondecreasing => cu[r] + r
+// strictly increasing).  With a corrupt cu it still returns some r in range.
+__device__ __forceinline__ int find_request(const int32_t *__restrict__ cu, int B, int g) {
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] + mid <= g)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ void raise_err(const Params &p, unsigned bits) { atomicOr(p.err, bits); }
+
+}  // namespace sv

@@ -1,0 +1,87 @@
+// sv_internal.h -- launch parameters shared by the host API and the gfx950
+// kernels of the verify step.  Not part of the public ABI.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "specverify.h"
+
+namespace sv {
+
+constexpr int kChunk = 1024;      // tokens per race chunk (SV_RACE_CHUNK)
+constexpr int kThreads = 256;     // threads per workgroup (4 wave64)
+constexpr int kWaves = kThreads / 64;
+constexpr int kMaxDrafts = 64;    // SV_MAX_DRAFTS: one lane per draft position
+constexpr int kCandCap = 1024;    // SV_TOPK_CANDIDATES
+constexpr int kStatsCPW = 2;      // chunks per wave in the stats pass (cps = kWaves * kStatsCPW)
+
+// Per-row candidate state written by the top-k pass.
+constexpr int kRowDense = -2;     // no top-k on this row: dense stats
+constexpr int kRowThreshold = -1; // top-k kept too many tokens: dense stats with z < tau masked
+
+// Request-level modes.
+enum : int { kModeSample = 0, kModeGreedy = 1, kModeInvalid = 2 };
+
+struct Params {
+  // inputs
+  const void *logits;
+  const float *draft_probs;
+  const int32_t *draft_ids;
+  const int32_t *cu;
+  const float *temperature;
+  const int32_t *top_k;
+  const float *rep_penalty;
+  const int32_t *idx_mapping;
+  const int32_t *counts;
+  // outputs
+  int32_t *out_tokens;
+  int32_t *out_ns;
+  int32_t *out_nr;
+  float *dbg_p_draft;
+  float *dbg_probs;
+  // scratch
+  float2 *chunk_tab;           // [max_rows, nc_stride]: (m_c, s_c) or (m_c, argmax_c)
+  float4 *row_info;            // [max_rows]: (m, s, argmax bits, state bits)
+  unsigned long long *req_ctr; // [max_reqs] arrivals (epoch << 32 | count)
+  unsigned long long *res_ctr; // [max_reqs]
+  int4 *res_req;               // [max_reqs]: (row g*, position j, draft d_j, epoch)
+  float *res_tab;              // [max_reqs, nc_stride] residual chunk masses
+  float *cand_val;             // [max_rows, kCandCap]
+  int32_t *cand_idx;           // [max_rows, kCandCap]
+  int32_t *cand_n;             // [max_rows]
+  float *cand_tau;             // [max_rows]
+  unsigned int *err;           // device error word
+  // sizes and scalars
+  int64_t lstride;
+  int64_t dstride;
+  int32_t dtype;
+  int32_t R, B, D, V;
+  int32_t NC;        // ceil(V / kChunk)
+  int32_t nc_stride; // chunk-table row length (>= NC)
+  int32_t cps;       // chunks per stats workgroup
+  int32_t nseg;      // stats workgroups per row
+  int32_t out_stride;
+  int32_t num_slots;
+  int32_t vec_ok;    // rows and base 16-byte aligned: vector loads allowed
+  int32_t has_topk;
+  uint32_t seed_lo, seed_hi, offset;
+  uint32_t epoch;
+};
+
+struct PostParams {
+  const int32_t *idx_mapping, *query_len, *tokens, *num_sampled, *num_rejected;
+  int32_t *last_sampled, *counts, *num_computed;
+  int32_t B, tokens_stride, V, num_slots;
+  unsigned int *err;
+};
+
+// Launchers (sv_kernels.hip).  Return the hipError_t of the last launch.
+hipError_t launch_topk(const Params &p, hipStream_t s);
+hipError_t launch_stats(const Params &p, hipStream_t s);
+hipError_t launch_resid(const Params &p, hipStream_t s);
+hipError_t launch_dbg_probs(const Params &p, hipStream_t s);
+hipError_t launch_post_update(const PostParams &p, hipStream_t s);
+
+}  // namespace sv

@@ -1,0 +1,151 @@
+"""Helpers shared by the GPU parity tests, the smoke check and the bench's CPU
+leg: run one verify step through the C ABI, run the oracle on the same inputs,
+and compare under the acceptance rule.
+
+Acceptance rule (per request):
+  * greedy requests, num_sampled, num_rejected and tokens: bit-exact, except
+    requests whose oracle decision margin is below MARGIN (relative), which
+    are counted and reported instead;
+  * p(d) of every draft and the processed probabilities: within PROB_ATOL.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+import rejection_sampling_verify_05_amd as sv
+
+MARGIN = 1e-5
+PROB_ATOL = 1e-6
+
+
+class Ctx:
+    """A library context sized for one workload (destroyed on close)."""
+
+    def __init__(self, max_rows, max_reqs, max_k, max_vocab, topk=False):
+        self.h = sv.spec_verify_create(max_rows, max_reqs, max_k, max_vocab,
+                                       sv.SV_CREATE_TOPK if topk else 0)
+
+    def close(self):
+        if self.h is not None:
+            sv.spec_verify_destroy(self.h)
+            self.h = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *a):
+        self.close()
+
+
+def ctx_for(inp, extra_rows=0):
+    w = inp["workload"]
+    return Ctx(inp["R"] + extra_rows, inp["B"], max(int(inp["K"].max().item()) if inp["B"] else 0, 1),
+               inp["V"], topk=inp["top_k"] is not None)
+
+
+def run_gpu(ctx: Ctx, inp: dict, seed=0, offset=0, dbg_probs=False, out_stride=None,
+            stream=None):
+    """One spec_verify_run; returns host numpy outputs."""
+    B, D, V = inp["B"], inp["D"], inp["V"]
+    dev = inp["logits"].device
+    if out_stride is None:
+        out_stride = int(inp["K"].max().item()) + 1 if B else 1
+    out = torch.full((B, out_stride), -7, dtype=torch.int32, device=dev)
+    ns = torch.full((B,), -7, dtype=torch.int32, device=dev)
+    nr = torch.full((B,), -7, dtype=torch.int32, device=dev)
+    pd = torch.full((max(D, 1),), -7.0, dtype=torch.float32, device=dev)
+    probs = torch.full((inp["R"], V), -7.0, dtype=torch.float32, device=dev) if dbg_probs else None
+    sv.spec_verify_run(ctx.h, inp["logits"], inp["draft_ids"], inp["cu"], inp["temperature"],
+                       out, ns, nr, draft_probs=inp["draft_probs"], top_k=inp["top_k"],
+                       rep_penalty=inp["rep_penalty"], idx_mapping=inp["idx_mapping"],
+                       output_bin_counts=inp["counts"] if inp["rep_penalty"] is not None else None,
+                       seed=seed, offset=offset, dbg_p_draft=pd if D else None, dbg_probs=probs,
+                       stream=stream)
+    err = sv.spec_verify_read_error(ctx.h, stream)
+    res = dict(tokens=out.cpu().numpy(), num_sampled=ns.cpu().numpy(),
+               num_rejected=nr.cpu().numpy(), p_draft=pd[:D].cpu().numpy(), err=err)
+    if probs is not None:
+        res["probs"] = probs.cpu().numpy()
+    return res
+
+
+class OracleRequest:
+    """Oracle state of one request: processed probabilities are computed once,
+    decisions can then be replayed for many (seed, offset)."""
+
+    def __init__(self, inp: dict, r: int, host: dict | None = None):
+        cu = inp["cu"].cpu().numpy() if host is None else host["cu"]
+        self.r = r
+        self.c0, self.c1 = int(cu[r]), int(cu[r + 1])
+        self.K = self.c1 - self.c0
+        self.g0 = self.c0 + r
+        rows = slice(self.g0, self.g0 + self.K + 1)
+        lg = inp["logits"][rows]
+        if lg.dtype == torch.bfloat16:
+            self.rows = lg.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        else:
+            self.rows = lg.contiguous().cpu().numpy()
+        self.T = float(inp["temperature"][r].item())
+        self.top_k = int(inp["top_k"][r].item()) if inp["top_k"] is not None else 0
+        self.theta = None
+        counts = None
+        if inp["rep_penalty"] is not None:
+            self.theta = float(inp["rep_penalty"][r].item())
+            slot = int(inp["idx_mapping"][r].item())
+            counts = inp["counts"][slot].cpu().numpy()
+        self.d = inp["draft_ids"][self.c0:self.c1].cpu().numpy()
+        self.q = None
+        if inp["draft_probs"] is not None and self.K:
+            self.q = inp["draft_probs"][self.c0:self.c1].float().cpu().numpy()
+        self.P, self.amax, self.err = oracle.prepare_request(self.rows, self.T, self.top_k,
+                                                            self.theta, counts)
+
+    def decide(self, seed=0, offset=0, C=oracle.RACE_CHUNK):
+        return oracle.decide_request(self.P, self.amax, self.T, self.d, self.q, self.g0, seed,
+                                     offset, C)
+
+
+def compare_request(g: dict, r: int, o_tokens, o_ns, o_nr, o_margin, out_stride):
+    """Returns 'ok', 'margin' or a mismatch description."""
+    want = list(o_tokens) + [-1] * (out_stride - len(o_tokens))
+    got = g["tokens"][r].tolist()
+    same = got == want and g["num_sampled"][r] == o_ns and g["num_rejected"][r] == o_nr
+    if same:
+        return "ok"
+    if o_margin < MARGIN:
+        return "margin"
+    return (f"request {r}: gpu tokens {got} ns {g['num_sampled'][r]} nr {g['num_rejected'][r]}; "
+            f"oracle {want} ns {o_ns} nr {o_nr} margin {o_margin:.3g}")
+
+
+def check_requests(g: dict, inp: dict, requests, seed=0, offset=0, probs=False):
+    """Compare the GPU outputs of `requests` with the oracle; returns (n_margin,
+    mismatches list).  Also checks p(d) and (optionally) processed probs."""
+    out_stride = g["tokens"].shape[1]
+    bad, n_margin = [], 0
+    for r in requests:
+        o = OracleRequest(inp, r)
+        assert o.err == 0, f"oracle rejected request {r}: {o.err}"
+        toks, ns, nr, mg, pd = o.decide(seed, offset)
+        res = compare_request(g, r, toks, ns, nr, mg, out_stride)
+        if res == "margin":
+            n_margin += 1
+        elif res != "ok":
+            bad.append(res)
+        if o.K and o.T > 0:
+            gp = g["p_draft"][o.c0:o.c1]
+            err = np.max(np.abs(gp.astype(np.float64) - pd.astype(np.float64)))
+            # the oracle's p_draft is fp32-rounded; compare against its fp64 value
+            P = o.P
+            exact = np.array([P[i, d] if 0 <= d < P.shape[1] else 0.0 for i, d in enumerate(o.d)])
+            err = np.max(np.abs(gp.astype(np.float64) - exact))
+            if err > PROB_ATOL:
+                bad.append(f"request {r}: p(d) error {err:.3g}")
+        if probs and "probs" in g:
+            gp = g["probs"][o.g0:o.g0 + o.K + 1].astype(np.float64)
+            err = np.max(np.abs(gp - o.P))
+            if err > PROB_ATOL:
+                bad.append(f"request {r}: probability error {err:.3g}")
+    return n_margin, bad

@@ -1,0 +1,120 @@
+"""The C-ABI library loads, exports every entry point include/specverify.h
+declares, its argument structs match the header's layout, and host-side
+argument checks fail before touching the GPU (no compute calls here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import rejection_sampling_verify_05_amd as sv
+from rejection_sampling_verify_05_amd import build as libbuild
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "specverify.h")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built():
+    if not os.path.exists(libbuild.OUTPUT):
+        libbuild.build_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(spec_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert names == sorted(["spec_post_update", "spec_verify_create", "spec_verify_destroy",
+                            "spec_verify_read_error", "spec_verify_run", "spec_verify_strerror"])
+    L = ctypes.CDLL(sv.library_path())
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", sv.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (spec_\w+)", out))
+    assert set(names) <= exported
+
+
+def test_struct_layout_matches_header(tmp_path):
+    src = tmp_path / "layout.c"
+    src.write_text(r'''
+#include <stddef.h>
+#include <stdio.h>
+#include "specverify.h"
+#define F(s, m) printf(#s "." #m " %zu %zu\n", offsetof(s, m), sizeof(((s*)0)->m));
+int main(void) {
+  printf("sv_verify_args %zu\n", sizeof(sv_verify_args));
+  printf("sv_post_update_args %zu\n", sizeof(sv_post_update_args));
+  F(sv_verify_args, target_logits) F(sv_verify_args, dbg_probs) F(sv_verify_args, logits_row_stride)
+  F(sv_verify_args, seed) F(sv_verify_args, offset) F(sv_verify_args, logits_dtype)
+  F(sv_verify_args, num_rows) F(sv_verify_args, num_slots)
+  F(sv_post_update_args, num_computed_tokens) F(sv_post_update_args, num_reqs)
+  F(sv_post_update_args, num_slots)
+  return 0;
+}
+''')
+    exe = tmp_path / "layout"
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", f"-I{ROOT}/include", f"-I{rocm}/include",
+                    str(src), "-o", str(exe)], check=True)
+    lines = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split("\n")
+    got = {}
+    for ln in lines:
+        if not ln:
+            continue
+        parts = ln.split()
+        got[parts[0]] = tuple(int(x) for x in parts[1:])
+    assert got["sv_verify_args"] == (ctypes.sizeof(sv.VerifyArgs),)
+    assert got["sv_post_update_args"] == (ctypes.sizeof(sv.PostUpdateArgs),)
+    for key, val in got.items():
+        if "." not in key:
+            continue
+        struct, field = key.split(".")
+        cls = sv.VerifyArgs if struct == "sv_verify_args" else sv.PostUpdateArgs
+        f = getattr(cls, field)
+        assert (f.offset, f.size) == val, key
+
+
+def test_strerror_and_host_checks_without_gpu():
+    L = sv.lib()
+    assert sv.spec_verify_strerror(0) == "ok"
+    assert sv.spec_verify_strerror(-5) == "device-side input check failed"
+    assert sv.spec_verify_strerror(42) == "unknown status"
+    # argument checks that run before any HIP call
+    ctx = ctypes.c_void_p()
+    assert L.spec_verify_create(None, 1, 1, 1, 1, 0) == sv.SV_EINVAL
+    assert L.spec_verify_create(ctypes.byref(ctx), 0, 1, 1, 1, 0) == sv.SV_EINVAL
+    assert L.spec_verify_create(ctypes.byref(ctx), 1, 1, 65, 1, 0) == sv.SV_ECAPACITY
+    assert L.spec_verify_create(ctypes.byref(ctx), 1, 1, 1, 1, 0x80) == sv.SV_EINVAL
+    a = sv.VerifyArgs()
+    assert L.spec_verify_run(None, ctypes.byref(a), None) == sv.SV_EINVAL
+    fake = ctypes.c_void_p(1)  # never dereferenced: checks fail first
+    a.logits_dtype = 7
+    assert L.spec_verify_run(fake, ctypes.byref(a), None) == sv.SV_EDTYPE
+    a.logits_dtype = sv.SV_BF16
+    a.num_reqs = -1
+    assert L.spec_verify_run(fake, ctypes.byref(a), None) == sv.SV_EINVAL
+    pa = sv.PostUpdateArgs()
+    assert L.spec_post_update(None, ctypes.byref(pa), None) == sv.SV_EINVAL
+    assert L.spec_post_update(fake, None, None) == sv.SV_EINVAL
+    pa.num_reqs = 1
+    pa.tokens_stride = 0
+    assert L.spec_post_update(fake, ctypes.byref(pa), None) == sv.SV_EINVAL
+    assert L.spec_verify_read_error(None, None, None) == sv.SV_EINVAL
+    L.spec_verify_destroy(None)
+
+
+def test_product_package_has_no_oracle_or_cpu_fallback():
+    # The product path never imports the oracle and has no CPU fallback.
+    pkg = os.path.join(ROOT, "rejection_sampling_verify_05_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, fn), encoding="utf-8").read()
+                assert "import oracle" not in text and "from oracle" not in text, fn
+                assert "oracle.h" not in text, fn
