@@ -1,0 +1,204 @@
+#!/usr/bin/env python3
+"""Benchmark of the speculative-decoding verify step on one MI355X.
+
+One step = spec_verify_run + spec_post_update over one batch of the headline
+workload (B=256 requests, K_r uniform in {0..3}, V=128256, bf16 target logits
+N(0, 3^2), no draft probabilities).  Inputs are resident in HBM before the
+timed region; the step rotates over several distinct input copies (more than
+1 GB in total) so that the 256 MB Infinity Cache cannot serve the logits.
+
+Prints one JSON line: verified logit rows/s over the timed steps, the stats
+kernel's achieved algorithmic HBM bandwidth against the 8 TB/s peak (timed
+with HIP events on the launch stream), and the CPU oracle's rate on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="3", help="workload id (1, 2, 3, 3k3, 4, 5)")
+    ap.add_argument("--copies", type=int, default=0, help="input copies to rotate (0: >= 1 GB)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(inp, out_stride) -> int:
+    """Bytes the method must move in one spec_verify_run: every target row once,
+    each draft id (and q(d) plus the rejected requests' draft rows in draft-probs
+    mode: counted by the caller), cu, temperatures and the outputs."""
+    esize = inp["logits"].element_size()
+    B, R, D, V = inp["B"], inp["R"], inp["D"], inp["V"]
+    b = R * V * esize + D * 4 + (B + 1) * 4 + B * 4 + B * (out_stride + 2) * 4
+    if inp["draft_probs"] is not None:
+        b += D * 4
+    if inp["top_k"] is not None:
+        b += B * 4
+    if inp["rep_penalty"] is not None:
+        b += B * (V * 4 + 8)
+    return b
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+              "the verify step shards by request with no exchange, so run one process per GPU.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import workloads as wl
+    from rejection_sampling_verify_05_amd import build as libbuild
+    if not os.path.exists(libbuild.OUTPUT):
+        libbuild.build_library()
+    import rejection_sampling_verify_05_amd as sv
+
+    torch.cuda.set_device(0)
+    w = wl.CONFIGS[args.workload]
+    first = wl.make_inputs(w, "cuda", salt=0)
+    per_copy = first["logits"].numel() * first["logits"].element_size()
+    ncopies = args.copies or max(4, -(-(1 << 30) // per_copy))
+    copies = [first] + [wl.make_inputs(w, "cuda", salt=i) for i in range(1, ncopies)]
+    out_stride = w.K + 1
+    max_rows = max(c["R"] for c in copies)
+    ctx = sv.spec_verify_create(max_rows, w.B, w.K, w.V, sv.SV_CREATE_TOPK if w.top_k else 0)
+
+    stream = torch.cuda.current_stream()
+    S = first["num_slots"]
+    last = torch.zeros(S, dtype=torch.int32, device="cuda")
+    ncomp = torch.zeros(S, dtype=torch.int32, device="cuda")
+    counts = first["counts"].clone()
+    outs = []
+    for c in copies:
+        o = dict(tokens=torch.empty((w.B, out_stride), dtype=torch.int32, device="cuda"),
+                 ns=torch.empty(w.B, dtype=torch.int32, device="cuda"),
+                 nr=torch.empty(w.B, dtype=torch.int32, device="cuda"))
+        o["vargs"] = sv.make_verify_args(
+            c["logits"], c["draft_ids"], c["cu"], c["temperature"], o["tokens"], o["ns"], o["nr"],
+            draft_probs=c["draft_probs"], top_k=c["top_k"], rep_penalty=c["rep_penalty"],
+            idx_mapping=c["idx_mapping"], output_bin_counts=c["counts"] if c["rep_penalty"] is not None else None,
+            seed=1234, offset=0)
+        o["pargs"] = sv.make_post_update_args(c["idx_mapping"], c["query_len"], o["tokens"], o["ns"],
+                                              o["nr"], last, counts, ncomp)
+        outs.append(o)
+
+    def step(i):
+        o = outs[i % ncopies]
+        o["vargs"].offset = i
+        sv.spec_verify_run(ctx, o["vargs"], stream=stream)
+        sv.spec_post_update(ctx, o["pargs"], stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    assert sv.spec_verify_read_error(ctx) == 0
+
+    # timed region: one event pair around each verify call (stats kernel) and
+    # one around the whole loop
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    rows = 0
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for k in range(args.steps):
+        i = args.warmup + k
+        o = outs[i % ncopies]
+        o["vargs"].offset = i
+        ev[k][0].record(stream)
+        sv.spec_verify_run(ctx, o["vargs"], stream=stream)
+        ev[k][1].record(stream)
+        sv.spec_post_update(ctx, o["pargs"], stream=stream)
+        rows += copies[i % ncopies]["R"]
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t0.elapsed_time(t1)
+    verify_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    assert sv.spec_verify_read_error(ctx) == 0
+
+    # algorithmic bytes of the dominant kernel per launch, averaged over the copies used
+    bytes_per = np.mean([algorithmic_bytes(copies[(args.warmup + k) % ncopies], out_stride)
+                         for k in range(args.steps)])
+    rows_per = rows / args.steps
+    kern_s = float(np.mean(verify_ms)) * 1e-3
+    achieved = bytes_per / kern_s / 1e9
+    value = rows / (total_ms * 1e-3)
+
+    # CPU baseline: the oracle on a bounded sample of the same workload
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        h = wl.to_numpy(first)
+        dp = None if first["draft_probs"] is None else first["draft_probs"].cpu().numpy()
+        t_start = time.perf_counter()
+        n_calls, cpu_rows = 0, 0
+        while True:
+            oracle.verify_batch(h["logits"], h["cu"], h["draft_ids"], h["temperature"], draft_probs=dp,
+                                top_k=h["top_k"], rep_penalty=h["rep_penalty"], idx_mapping=h["idx_mapping"],
+                                counts=None if first["rep_penalty"] is None else first["counts"].cpu().numpy(),
+                                seed=1234, offset=n_calls)
+            n_calls += 1
+            cpu_rows += first["R"]
+            if time.perf_counter() - t_start >= args.cpu_seconds:
+                break
+        cpu_s = time.perf_counter() - t_start
+        cpu = {"value": cpu_rows / cpu_s, "unit": "rows/s", "cores": 1, "kind": "oracle",
+               "sample": f"{n_calls} full batch(es) of workload {w.cid} ({first['R']} rows each, "
+                         f"offsets 0..{n_calls - 1}), single-threaded C oracle, {cpu_s:.1f} s"}
+
+    sv.spec_verify_destroy(ctx)
+    line = {
+        "metric": "verified logit rows/sec + achieved HBM GB/s (B=256, K=3, V=128256)",
+        "value": round(value, 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == torch.bfloat16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: B={w.B}, K_r {'~U{0..%d}' % w.K if w.ragged else '=%d' % w.K}, "
+                               f"V={w.V}, {'bf16' if w.dtype == torch.bfloat16 else 'fp32'} logits, "
+                               f"{'draft probs' if w.draft_probs else 'draft ids only'}",
+                   "global_batch": w.B, "rows_per_step": round(rows_per, 1), "input_copies": ncopies,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "stats_kernel (spec_verify_run)",
+                     "kernel_us": {"mean": round(float(np.mean(verify_ms)) * 1e3, 2),
+                                   "p10": round(float(np.percentile(verify_ms, 10)) * 1e3, 2),
+                                   "p50": round(float(np.median(verify_ms)) * 1e3, 2),
+                                   "p90": round(float(np.percentile(verify_ms, 90)) * 1e3, 2)},
+                     "bytes_per_launch": int(bytes_per)},
+        "cpu_baseline": cpu,
+        "wall_s": round(wall, 3),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

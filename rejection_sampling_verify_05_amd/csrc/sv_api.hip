@@ -16,10 +16,9 @@ struct sv_ctx {
   uint32_t flags;
   int32_t nc_stride;
   uint32_t epoch;
+  int32_t resident[2][2];  // resident stats workgroups: [dtype][fast pass]
   float2 *chunk_tab;
   float4 *row_info;
-  unsigned long long *req_ctr;
-  unsigned long long *res_ctr;
   int4 *res_req;
   float *res_tab;
   float *cand_val;
@@ -32,7 +31,7 @@ struct sv_ctx {
 namespace {
 
 void free_ctx(sv_ctx *c) {
-  void *ptrs[] = {c->chunk_tab, c->row_info, c->req_ctr, c->res_ctr, c->res_req, c->res_tab,
+  void *ptrs[] = {c->chunk_tab, c->row_info, c->res_req, c->res_tab,
                   c->cand_val,  c->cand_idx, c->cand_n,  c->cand_tau, c->err};
   for (void *p : ptrs)
     if (p) (void)hipFree(p);
@@ -70,20 +69,22 @@ extern "C" int spec_verify_create(sv_ctx **out, int32_t max_rows, int32_t max_re
   c->epoch = 0;
   const size_t rows = (size_t)max_rows, reqs = (size_t)max_reqs, ncs = (size_t)c->nc_stride;
   bool ok = dev_alloc(&c->chunk_tab, rows * ncs) && dev_alloc(&c->row_info, rows) &&
-            dev_alloc(&c->req_ctr, reqs) && dev_alloc(&c->res_ctr, reqs) && dev_alloc(&c->res_req, reqs) &&
+            dev_alloc(&c->res_req, reqs) &&
             dev_alloc(&c->res_tab, reqs * ncs) && dev_alloc(&c->err, 1);
   if (ok && (flags & SV_CREATE_TOPK))
     ok = dev_alloc(&c->cand_val, rows * sv::kCandCap) && dev_alloc(&c->cand_idx, rows * sv::kCandCap) &&
          dev_alloc(&c->cand_n, rows) && dev_alloc(&c->cand_tau, rows);
   if (ok)
-    ok = hipMemset(c->req_ctr, 0, reqs * sizeof(unsigned long long)) == hipSuccess &&
-         hipMemset(c->res_ctr, 0, reqs * sizeof(unsigned long long)) == hipSuccess &&
-         hipMemset(c->res_req, 0, reqs * sizeof(int4)) == hipSuccess &&
+    ok = hipMemset(c->res_req, 0, reqs * sizeof(int4)) == hipSuccess &&
          hipMemset(c->err, 0, sizeof(unsigned int)) == hipSuccess && hipDeviceSynchronize() == hipSuccess;
+  int ncu = 0;
+  if (ok) ok = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, c->device) == hipSuccess;
   if (!ok) {
     free_ctx(c);
     return SV_EHIP;
   }
+  for (int dt = 0; dt < 2; ++dt)
+    for (int f = 0; f < 2; ++f) c->resident[dt][f] = ncu * sv::stats_blocks_per_cu(dt, f != 0);
   *out = c;
   return SV_OK;
 }
@@ -132,8 +133,6 @@ extern "C" int spec_verify_run(sv_ctx *ctx, const sv_verify_args *a, hipStream_t
   p.dbg_probs = a->dbg_probs;
   p.chunk_tab = ctx->chunk_tab;
   p.row_info = ctx->row_info;
-  p.req_ctr = ctx->req_ctr;
-  p.res_ctr = ctx->res_ctr;
   p.res_req = ctx->res_req;
   p.res_tab = ctx->res_tab;
   p.cand_val = ctx->cand_val;
@@ -150,8 +149,23 @@ extern "C" int spec_verify_run(sv_ctx *ctx, const sv_verify_args *a, hipStream_t
   p.V = a->vocab_size;
   p.NC = (a->vocab_size + sv::kChunk - 1) / sv::kChunk;
   p.nc_stride = ctx->nc_stride;
-  p.cps = sv::kWaves * sv::kStatsCPW;
+  p.cps = sv::kResidCPS;
   p.nseg = (p.NC + p.cps - 1) / p.cps;
+  {
+    // Fast pass: aligned rows whose length is whole 16-byte vectors, no penalty,
+    // no top-k.  Grid: every resident workgroup, but enough workgroups that a
+    // slice of the R * NC chunks spans at most kSliceRows rows.
+    const int esize_ = a->logits_dtype == SV_BF16 ? 2 : 4;
+    const bool aligned = ((uintptr_t)a->target_logits % 16 == 0) && ((a->logits_row_stride * esize_) % 16 == 0);
+    p.fast = aligned && a->vocab_size % (16 / esize_) == 0 && !a->rep_penalty && !a->top_k;
+    const int64_t chunks = (int64_t)a->num_rows * p.NC;
+    if (chunks > 0x7FFFFFFF) return SV_ECAPACITY;
+    const int64_t per = (int64_t)(sv::kSliceRows - 1) * p.NC + 1;  // longest slice allowed
+    int64_t grid = ctx->resident[a->logits_dtype][p.fast ? 1 : 0];
+    if (grid * per < chunks) grid = (chunks + per - 1) / per;
+    if (grid > chunks) grid = chunks;
+    p.stats_grid = (int32_t)grid;
+  }
   p.out_stride = a->out_stride;
   p.num_slots = a->rep_penalty ? a->num_slots : 0;
   const int esize = a->logits_dtype == SV_BF16 ? 2 : 4;
@@ -163,10 +177,11 @@ extern "C" int spec_verify_run(sv_ctx *ctx, const sv_verify_args *a, hipStream_t
   ctx->epoch = ctx->epoch == 0xFFFFFFFFu ? 1u : ctx->epoch + 1u;
   p.epoch = ctx->epoch;
 
-  if ((int64_t)p.R * p.nseg > 0x7FFFFFFF) return SV_ECAPACITY;
+  if ((int64_t)p.B * p.nseg > 0x7FFFFFFF) return SV_ECAPACITY;
 
   if (p.has_topk && sv::launch_topk(p, stream) != hipSuccess) return SV_EHIP;
   if (sv::launch_stats(p, stream) != hipSuccess) return SV_EHIP;
+  if (sv::launch_epilogue(p, stream) != hipSuccess) return SV_EHIP;
   if (p.draft_probs && sv::launch_resid(p, stream) != hipSuccess) return SV_EHIP;
   if (p.dbg_probs && sv::launch_dbg_probs(p, stream) != hipSuccess) return SV_EHIP;
   return SV_OK;

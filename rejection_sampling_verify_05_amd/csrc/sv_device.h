@@ -45,11 +45,16 @@ __device__ __forceinline__ uint32_t pick(uint4 w, int k) {
 // Accept uniform ((w>>8)+1) 2^-24 in (0,1]; exact in fp64.
 __device__ __forceinline__ double u_accept(uint32_t w) { return (double)((w >> 8) + 1u) * 0x1p-24; }
 
-// Exp(1) noise from the race uniform (w>>8) 2^-24 in [0,1); U = 0 -> +inf.
-__device__ __forceinline__ double exp_noise(uint32_t w) {
-  uint32_t k = w >> 8;
-  if (k == 0) return __builtin_huge_val();
-  return -log((double)k * 0x1p-24);
+// Exp(1) noise E = -ln U from the race uniform U = (w>>8) 2^-24 in [0,1);
+// U = 0 gives +inf.  For U >= 1/2, E = -log1p(-(1 - U)) with 1 - U exact, so
+// small E (the likely race winners) keep full relative precision; for
+// U < 1/2, |ln U| >= ln 2 and logf is well conditioned.  Both library
+// functions are accurate to about one ulp.
+__device__ __forceinline__ float exp_noise(uint32_t w) {
+  const uint32_t k = w >> 8;
+  if (k == 0) return __builtin_inff();
+  if (k >= (1u << 23)) return -log1pf(-(float)((1u << 24) - k) * 0x1p-24f);
+  return -logf((float)k * 0x1p-24f);
 }
 
 // ---------------------------------------------------------------------------
@@ -99,23 +104,59 @@ __device__ __forceinline__ int wave_min_i(int v) {
 // (score, index) arg-max with the lowest index winning ties; non-candidates
 // carry score -1 (real scores are >= 0).
 struct ArgMax {
-  double s;
+  float s;
   int i;
 };
 __device__ __forceinline__ bool better(ArgMax a, ArgMax b) { return a.s > b.s || (a.s == b.s && a.i < b.i); }
 
-__device__ __forceinline__ ArgMax wave_argmax(ArgMax a) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    ArgMax o{__shfl_xor(a.s, off), __shfl_xor(a.i, off)};
-    if (better(o, a)) a = o;
-  }
-  return a;
+template <int CTRL>
+__device__ __forceinline__ ArgMax argmax_dpp(ArgMax a) {
+  ArgMax o{dpp_f<CTRL>(a.s), dpp_i<CTRL>(a.i)};
+  return better(o, a) ? o : a;
 }
+// Wave-wide arg-max with DPP row steps; uniform result.
+__device__ __forceinline__ ArgMax wave_argmax(ArgMax a) {
+  a = argmax_dpp<kQuad1032>(a);
+  a = argmax_dpp<kQuad2301>(a);
+  a = argmax_dpp<kHalfMirror>(a);
+  a = argmax_dpp<kMirror>(a);
+  ArgMax b{rd(a.s, 0), __builtin_amdgcn_readlane(a.i, 0)};
+#pragma unroll
+  for (int row = 16; row < 64; row += 16) {
+    ArgMax o{rd(a.s, row), __builtin_amdgcn_readlane(a.i, row)};
+    if (better(o, b)) b = o;
+  }
+  return b;
+}
+
+// ---------------------------------------------------------------------------
+// Publication between workgroups of one launch.  Entries are written with
+// agent-scope stores (written through to the device-coherent level, not held
+// in one XCD's L2), the writer waits for its stores to be acknowledged, and
+// only then bumps an agent-scope counter; the reader observes the counter and
+// then reads the entries with agent-scope loads.  No L2 write-back or
+// invalidate of unrelated lines is needed.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void publish_f2(float2 *addr, float2 v) {
+  __hip_atomic_store(reinterpret_cast<unsigned long long *>(addr), __builtin_bit_cast(unsigned long long, v),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 fetch_f2(const float2 *addr) {
+  return __builtin_bit_cast(float2, __hip_atomic_load(reinterpret_cast<const unsigned long long *>(addr),
+                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ void publish_f(float *addr, float v) {
+  __hip_atomic_store(addr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float fetch_f(const float *addr) {
+  return __hip_atomic_load(addr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until every memory operation this wave issued has completed.
+__device__ __forceinline__ void wait_memory() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Block-wide (256 threads) reductions; every thread gets the result.
 struct BlockScratch {
-  double s[kWaves];
+  float s[kWaves];
   int i[kWaves];
   float f[kWaves];
 };

@@ -15,7 +15,7 @@ constexpr int kThreads = 256;     // threads per workgroup (4 wave64)
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxDrafts = 64;    // SV_MAX_DRAFTS: one lane per draft position
 constexpr int kCandCap = 1024;    // SV_TOPK_CANDIDATES
-constexpr int kStatsCPW = 2;      // chunks per wave in the stats pass (cps = kWaves * kStatsCPW)
+constexpr int kResidCPS = 8;      // chunks per residual-pass workgroup
 
 // Per-row candidate state written by the top-k pass.
 constexpr int kRowDense = -2;     // no top-k on this row: dense stats
@@ -44,8 +44,6 @@ struct Params {
   // scratch
   float2 *chunk_tab;           // [max_rows, nc_stride]: (m_c, s_c) or (m_c, argmax_c)
   float4 *row_info;            // [max_rows]: (m, s, argmax bits, state bits)
-  unsigned long long *req_ctr; // [max_reqs] arrivals (epoch << 32 | count)
-  unsigned long long *res_ctr; // [max_reqs]
   int4 *res_req;               // [max_reqs]: (row g*, position j, draft d_j, epoch)
   float *res_tab;              // [max_reqs, nc_stride] residual chunk masses
   float *cand_val;             // [max_rows, kCandCap]
@@ -60,8 +58,10 @@ struct Params {
   int32_t R, B, D, V;
   int32_t NC;        // ceil(V / kChunk)
   int32_t nc_stride; // chunk-table row length (>= NC)
-  int32_t cps;       // chunks per stats workgroup
-  int32_t nseg;      // stats workgroups per row
+  int32_t cps;       // chunks per residual-pass workgroup
+  int32_t nseg;      // residual-pass workgroups per row
+  int32_t stats_grid; // stats workgroups (persistent grid; slices span <= kRowCache rows)
+  int32_t fast;       // use the fast streaming pass
   int32_t out_stride;
   int32_t num_slots;
   int32_t vec_ok;    // rows and base 16-byte aligned: vector loads allowed
@@ -80,8 +80,12 @@ struct PostParams {
 // Launchers (sv_kernels.hip).  Return the hipError_t of the last launch.
 hipError_t launch_topk(const Params &p, hipStream_t s);
 hipError_t launch_stats(const Params &p, hipStream_t s);
+hipError_t launch_epilogue(const Params &p, hipStream_t s);
 hipError_t launch_resid(const Params &p, hipStream_t s);
 hipError_t launch_dbg_probs(const Params &p, hipStream_t s);
 hipError_t launch_post_update(const PostParams &p, hipStream_t s);
+// Resident stats workgroups per CU (occupancy query).
+int stats_blocks_per_cu(int dtype, bool fast);
+constexpr int kSliceRows = 4;  // rows a stats slice may span (kRowCache)
 
 }  // namespace sv

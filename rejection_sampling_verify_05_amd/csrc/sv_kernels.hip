@@ -4,16 +4,16 @@
 //   topk_kernel   (only with top_k)      one workgroup per target row: exact
 //                 k-th largest processed logit tau and, when at most
 //                 kCandCap tokens reach tau, the kept tokens sorted by id.
-//   stats_kernel  the streaming pass.  Workgroup (row g, segment) reads
-//                 cps chunks of kChunk logits of row g once, and stores per
-//                 chunk (max, sum exp2(a (z - max))) -- or (max, argmax) for
-//                 greedy rows -- in the chunk table.  The last workgroup to
-//                 finish a request (per-request arrival counter) runs the
-//                 request epilogue: row softmax statistics from the chunk
-//                 table, the accept tests, the first reject, and the
-//                 bonus / recovered race.
-//   resid_kernel  (draft-probs mode) residual max(0, p - q) chunk masses of
-//                 each rejected request's row, then the race.
+//   stats_kernel  the streaming pass.  A persistent grid reads every chunk of
+//   (or the       kChunk logits once, each workgroup a balanced contiguous
+//   fast variant) slice, and stores per chunk (max, sum exp2(a (z - max))) --
+//                 or (max, argmax) for greedy rows -- in the chunk table.
+//   epilogue_kernel  one workgroup per request: row softmax statistics from
+//                 the chunk table, the accept tests, the first reject, and
+//                 the bonus / recovered race.
+//   resid_kernel, resid_race_kernel  (draft-probs mode) residual
+//                 max(0, p - q) chunk masses of each rejected request's row,
+//                 then the race.
 //   dbg_kernel    (optional) writes the processed probabilities.
 //
 // The method follows "vLLM 投机解码（Eagle / MTP）实现与运行流程" section 八
@@ -45,9 +45,10 @@ struct Req {
   Proc proc;         // penalty part (tau set per row)
 };
 
-__device__ Req load_req(const Params &p, int r) {
+// Fills a Req from the request's cu entries and temperature, plus the optional
+// penalty settings (one more round trip, only when a penalty is given).
+__device__ __forceinline__ Req make_req(const Params &p, int r, int c0, int c1, float T) {
   Req q;
-  const int c0 = p.cu[r], c1 = p.cu[r + 1];
   q.r = r;
   q.c0 = c0;
   q.K = c1 - c0;
@@ -57,7 +58,6 @@ __device__ Req load_req(const Params &p, int r) {
   q.proc.counts = nullptr;
   q.proc.theta = 1.0f;
   q.proc.tau = kNegInf;
-  const float T = p.temperature[r];
   q.a = 0.0f;
   if (!(T >= 0.0f) || !__builtin_isfinite(T)) {
     q.mode = kModeInvalid;
@@ -85,6 +85,61 @@ __device__ Req load_req(const Params &p, int r) {
     }
   }
   return q;
+}
+
+__device__ __forceinline__ Req load_req(const Params &p, int r) { return make_req(p, r, p.cu[r], p.cu[r + 1], p.temperature[r]); }
+
+// Request owning target row g: the r with f(r) = cu[r] + r <= g < f(r + 1),
+// f strictly increasing.  One wide load of a 64-request window around the
+// linear guess g B / R (one round trip when the K_r are not far from uniform);
+// otherwise a wave-parallel 64-ary search, one wide load per level.  The load
+// that finds r also fetches cu[r+1] and the temperature.  Every lane of the
+// wave must call it; the result is uniform.
+__device__ __forceinline__ Req lookup_req(const Params &p, int g) {
+  const int lane = threadIdx.x & 63;
+  {
+    int base = (int)((int64_t)g * p.B / p.R) - 32;
+    base = max(0, min(base, p.B - 64));
+    const int idx = base + lane;
+    const bool in = idx < p.B;
+    const int c = in ? p.cu[idx] : 0x7FFFFFFF;
+    const int cn = in ? p.cu[idx + 1] : 0;
+    const float T = in ? p.temperature[idx] : 0.0f;
+    const int last_lane = min(63, p.B - 1 - base);
+    const bool lo_ok = __builtin_amdgcn_readlane(c, 0) + base <= g;
+    const bool hi_ok = __builtin_amdgcn_readlane(cn, last_lane) + base + last_lane + 1 > g;
+    if (lo_ok && hi_ok) {
+      const unsigned long long m = __ballot(in && c + idx <= g);
+      const int last = m ? 63 - __clzll((long long)m) : 0;
+      return make_req(p, base + last, __builtin_amdgcn_readlane(c, last), __builtin_amdgcn_readlane(cn, last),
+                      __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, T), last)));
+    }
+  }
+  int stride = 1;
+  while (stride * 64 < p.B) stride *= 64;
+  int base = 0;
+  for (;;) {
+    const int idx = base + lane * stride;
+    const bool in = idx < p.B;
+    int c = 0, cn = 0;
+    float T = 0.0f;
+    if (in) {
+      c = p.cu[idx];
+      if (stride == 1) {
+        cn = p.cu[idx + 1];
+        T = p.temperature[idx];
+      }
+    }
+    const unsigned long long m = __ballot(in && c + idx <= g);
+    const int last = m ? 63 - __clzll((long long)m) : 0;
+    if (stride == 1) {
+      const int r = base + last;
+      return make_req(p, r, __builtin_amdgcn_readlane(c, last), __builtin_amdgcn_readlane(cn, last),
+                      __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, T), last)));
+    }
+    base += last * stride;
+    stride /= 64;
+  }
 }
 
 __device__ __forceinline__ int row_state(const Params &p, int g) { return p.has_topk ? p.cand_n[g] : kRowDense; }
@@ -124,134 +179,88 @@ struct Layout<0> {
 };
 
 // ---------------------------------------------------------------------------
-// Arrival protocol.  A counter holds (epoch << 32 | arrivals).  Each
-// workgroup first raises the counter to (epoch << 32) -- a no-op once this
-// call has started counting, a reset if it holds an older call's count --
-// then adds one after its results are visible device-wide.  The last arrival
-// resets the count so that replays with the same epoch also start from zero.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ void arrive_begin(unsigned long long *ctr, uint32_t epoch) {
-  if (threadIdx.x == 0)
-    __hip_atomic_fetch_max(ctr, (unsigned long long)epoch << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Returns true (in every thread) if this workgroup is the last of `target`.
-__device__ __forceinline__ bool arrive_end(unsigned long long *ctr, uint32_t epoch, unsigned target, int *sh_flag) {
-  __threadfence();  // release this workgroup's table entries
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    unsigned long long old =
-        __hip_atomic_fetch_add(ctr, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const bool last = (old >> 32) == epoch && (unsigned)(old & 0xFFFFFFFFu) + 1u == target;
-    if (last) {
-      __threadfence();  // acquire the other workgroups' entries
-      __hip_atomic_store(ctr, (unsigned long long)epoch << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    *sh_flag = last ? 1 : 0;
-  }
-  __syncthreads();
-  return *sh_flag != 0;
-}
-
-// ---------------------------------------------------------------------------
 // Races.  RACE(w, g): chunk c* = argmax_c M_c / E(g, 1, c) over chunks with
 // M_c > 0, then token x* = argmax_{x in c*} w_x / E(g, 2, x) over w_x > 0.
 // Scores are compared in fp64; ties go to the lowest index.
 // ---------------------------------------------------------------------------
+constexpr int kTabCache = 2048;  // chunk-table entries the epilogue keeps in LDS
+
 struct EpiShared {
   BlockScratch red;
   float m[kMaxDrafts + 1];
   float s[kMaxDrafts + 1];
+  float tau[kMaxDrafts + 1];
+  float zd[kMaxDrafts + 1];
+  float qd[kMaxDrafts + 1];
+  float sx[kMaxDrafts + 1];
   int amax[kMaxDrafts + 1];
   int state[kMaxDrafts + 1];
-  float tau[kMaxDrafts + 1];
+  int d[kMaxDrafts + 1];
   int j;
   int bad;
   int flag;
-  float cw[kCandCap];  // compact rows: candidate weights
-  int ci[kCandCap];    // compact rows: candidate token ids
+  union {
+    float2 tab[kTabCache];  // dense rows: chunk tables of the request's rows
+    struct {
+      float cw[kCandCap];   // compact rows: candidate weights
+      int ci[kCandCap];     // compact rows: candidate token ids
+    } cand;
+  } u;
 };
 
-// Chunk race with weights from a functor W(c) (fp32, >= 0).
+// Block-level chunk race (all threads call it); thread t takes chunks t,
+// t + 256, ...; W(c) >= 0.  Returns -1 if no chunk has positive weight.
 template <class WF>
-__device__ int chunk_race(const Params &p, uint32_t g, int NC, WF W, BlockScratch &red) {
-  ArgMax best{-1.0, 0x7FFFFFFF};
-  for (int base = 0; base < NC; base += 4 * kThreads) {
-    const int c0 = base + 4 * (int)threadIdx.x;
-    if (c0 < NC) {
-      const uint4 w4 = rng_block(p, (uint32_t)c0 >> 2, g, kTagChunk);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int c = c0 + k;
-        if (c < NC) {
-          const float Wc = W(c);
-          if (Wc > 0.0f) {
-            ArgMax o{(double)Wc / exp_noise(pick(w4, k)), c};
-            if (better(o, best)) best = o;
-          }
-        }
-      }
+__device__ __forceinline__ int block_chunk_race(const Params &p, uint32_t g, int NC, WF W, BlockScratch &red) {
+  ArgMax best{-1.0f, 0x7FFFFFFF};
+  for (int c = threadIdx.x; c < NC; c += kThreads) {
+    const float Wc = W(c);
+    if (Wc > 0.0f) {
+      const uint4 w4 = rng_block(p, (uint32_t)c >> 2, g, kTagChunk);
+      ArgMax o{Wc / exp_noise(pick(w4, c & 3)), c};
+      if (better(o, best)) best = o;
     }
   }
   const ArgMax b = block_argmax(best, red);
-  return b.s < 0.0 ? -1 : b.i;
+  return b.s < 0.0f ? -1 : b.i;
 }
 
-// Token race inside chunk c (0 <= c < NC) with weights from a functor w(x)
-// (x < V).  Returns -1 if no token of the chunk has positive weight.
-template <class TF>
-__device__ int token_race(const Params &p, uint32_t g, int c, TF w, BlockScratch &red) {
-  ArgMax best{-1.0, 0x7FFFFFFF};
-  const int x0 = c * kChunk + 4 * (int)threadIdx.x;
-  const uint4 w4 = rng_block(p, (uint32_t)x0 >> 2, g, kTagToken);
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int x = x0 + k;
-    if (x < p.V) {
-      const float wx = w(x);
-      if (wx > 0.0f) {
-        ArgMax o{(double)wx / exp_noise(pick(w4, k)), x};
-        if (better(o, best)) best = o;
-      }
-    }
-  }
-  const ArgMax b = block_argmax(best, red);
-  return b.s < 0.0 ? -1 : b.i;
-}
-
-// Race over a compact candidate list (token ids ascending in sh.ci, weights in
-// sh.cw, n entries).  Same law and random words as the dense race: chunk
-// masses are the sums over the candidates of each chunk.
-__device__ int compact_race(const Params &p, uint32_t g, int n, EpiShared &sh) {
+// Race over a compact candidate list (token ids ascending in sh.u.cand.ci,
+// weights in sh.u.cand.cw, n entries); all threads call it.  Same law and
+// random words as the dense race: chunk masses are the sums over the
+// candidates of each chunk.
+__device__ __forceinline__ int compact_race(const Params &p, uint32_t g, int n, EpiShared &sh) {
   __syncthreads();
-  ArgMax best{-1.0, 0x7FFFFFFF};
+  const float *cw = sh.u.cand.cw;
+  const int *ci = sh.u.cand.ci;
+  ArgMax best{-1.0f, 0x7FFFFFFF};
   for (int i = threadIdx.x; i < n; i += kThreads) {
-    const int c = sh.ci[i] / kChunk;
-    if (i > 0 && sh.ci[i - 1] / kChunk == c) continue;  // not the first candidate of its chunk
+    const int c = ci[i] / kChunk;
+    if (i > 0 && ci[i - 1] / kChunk == c) continue;  // not the first candidate of its chunk
     float M = 0.0f;
-    for (int t = i; t < n && sh.ci[t] / kChunk == c; ++t) M += sh.cw[t];
+    for (int t = i; t < n && ci[t] / kChunk == c; ++t) M += cw[t];
     if (M > 0.0f) {
       const uint4 w4 = rng_block(p, (uint32_t)c >> 2, g, kTagChunk);
-      ArgMax o{(double)M / exp_noise(pick(w4, c & 3)), c};
+      ArgMax o{M / exp_noise(pick(w4, c & 3)), c};
       if (better(o, best)) best = o;
     }
   }
   const ArgMax cb = block_argmax(best, sh.red);
-  if (cb.s < 0.0) return -1;
+  if (cb.s < 0.0f) return -1;
   const int cstar = cb.i;
-  ArgMax tb{-1.0, 0x7FFFFFFF};
+  ArgMax tb{-1.0f, 0x7FFFFFFF};
   for (int i = threadIdx.x; i < n; i += kThreads) {
-    const int x = sh.ci[i];
-    if (x / kChunk != cstar || !(sh.cw[i] > 0.0f)) continue;
+    const int x = ci[i];
+    if (x / kChunk != cstar || !(cw[i] > 0.0f)) continue;
     const uint4 w4 = rng_block(p, (uint32_t)x >> 2, g, kTagToken);
-    ArgMax o{(double)sh.cw[i] / exp_noise(pick(w4, x & 3)), x};
+    ArgMax o{cw[i] / exp_noise(pick(w4, x & 3)), x};
     if (better(o, tb)) tb = o;
   }
   const ArgMax b = block_argmax(tb, sh.red);
-  return b.s < 0.0 ? -1 : b.i;
+  return b.s < 0.0f ? -1 : b.i;
 }
 
-__device__ void write_empty(const Params &p, int r) {
+__device__ __forceinline__ void write_empty(const Params &p, int r) {
   for (int t = threadIdx.x; t < p.out_stride; t += kThreads) p.out_tokens[(int64_t)r * p.out_stride + t] = -1;
   if (threadIdx.x == 0) {
     p.out_ns[r] = 0;
@@ -260,11 +269,16 @@ __device__ void write_empty(const Params &p, int r) {
 }
 
 // ---------------------------------------------------------------------------
-// Request epilogue (run by the last stats workgroup of request q.r).
+// Request epilogue: one workgroup per request, after the streaming pass.
+//
+// Round trips: the request's cu entries and temperature; the chunk tables and
+// the draft ids; the logits of each draft token's chunk (z_d, q(d) and the
+// chunk mass without d); the logits of the winning chunk.  Everything else is
+// arithmetic on those values and on the Philox stream.
 // ---------------------------------------------------------------------------
-__device__ void request_epilogue(const Params &p, const Req &q, EpiShared &sh) {
+__device__ __forceinline__ void request_epilogue(const Params &p, const Req &q, EpiShared &sh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int K = q.K, r = q.r;
+  const int K = q.K, r = q.r, nrow = K + 1;
 
   if (!q.cu_ok || p.cu[0] != 0 || p.cu[p.B] != p.D) {
     if (tid == 0) raise_err(p, SV_ERR_CU);
@@ -278,10 +292,71 @@ __device__ void request_epilogue(const Params &p, const Req &q, EpiShared &sh) {
   }
   const bool greedy = q.mode == kModeGreedy;
 
-  // Row statistics: one wave per row.
-  for (int i = wave; i <= K; i += kWaves) {
+  // Row states (top-k pass results) and draft ids.
+  for (int i = tid; i < nrow; i += kThreads) {
     const int g = q.g0 + i;
     const int st = row_state(p, g);
+    sh.state[i] = st;
+    sh.tau[i] = (st == kRowDense) ? kNegInf : p.cand_tau[g];
+    if (i < K) sh.d[i] = p.draft_ids[q.c0 + i];
+  }
+  const bool cached = nrow * p.NC <= kTabCache;
+  if (cached) {
+    for (int t = tid; t < nrow * p.NC; t += kThreads) {
+      const int i = t / p.NC, c = t - i * p.NC;
+      sh.u.tab[t] = p.chunk_tab[(int64_t)(q.g0 + i) * p.nc_stride + c];
+    }
+  }
+  __syncthreads();
+  // Draft records (stochastic dense rows): the processed z_d, q(d) and the sum
+  // of exp2(a (z - m_c)) over d's chunk without d, in the chunk entry's
+  // scale; one wave per draft row, 16 tokens per lane.
+  if (!greedy) {
+    for (int i = wave; i < K; i += kWaves) {
+      const int d = sh.d[i];
+      if (sh.state[i] >= 0 || d < 0 || d >= p.V) continue;
+      const int g = q.g0 + i, c = d / kChunk;
+      Proc pr = q.proc;
+      pr.tau = sh.tau[i];
+      float z[kChunk / 64];
+#pragma unroll
+      for (int t = 0; t < kChunk / 64; ++t) z[t] = load_logit(p, g, min(c * kChunk + t * 64 + lane, p.V - 1));
+      const float qd = p.draft_probs ? p.draft_probs[(int64_t)(q.c0 + i) * p.dstride + d] : 1.0f;
+      float mx = kNegInf;
+#pragma unroll
+      for (int t = 0; t < kChunk / 64; ++t) {
+        const int x = c * kChunk + t * 64 + lane;
+        z[t] = x < p.V ? apply_proc(z[t], x, pr) : kNegInf;
+        mx = fmaxf(mx, z[t]);
+      }
+      const float mc = wave_max(mx);
+      float sx = 0.0f, zl = kNegInf;
+      const float a = q.a;
+      const float hi = a * mc, lo = __builtin_fmaf(a, mc, -hi);
+#pragma unroll
+      for (int t = 0; t < kChunk / 64; ++t) {
+        if (c * kChunk + t * 64 + lane == d)
+          zl = z[t];
+        else if (mc > kNegInf)
+          sx += exp2_acc(__builtin_fmaf(z[t], a, -hi));
+      }
+      sx = mc > kNegInf ? wave_sum(sx) * exp2_acc(-lo) : 0.0f;
+      const float zd = wave_max(zl);
+      if (lane == 0) {
+        sh.zd[i] = zd;
+        sh.qd[i] = qd;
+        sh.sx[i] = sx;
+      }
+    }
+  }
+  auto entry = [&](int i, int c) -> float2 {
+    return cached ? sh.u.tab[i * p.NC + c] : p.chunk_tab[(int64_t)(q.g0 + i) * p.nc_stride + c];
+  };
+
+  // Row statistics: one wave per row.
+  for (int i = wave; i < nrow; i += kWaves) {
+    const int g = q.g0 + i;
+    const int st = sh.state[i];
     float m, s = 0.0f;
     int am = 0x7FFFFFFF;
     if (st >= 0) {
@@ -293,21 +368,32 @@ __device__ void request_epilogue(const Params &p, const Req &q, EpiShared &sh) {
       for (int t = lane; t < st; t += 64) ls += exp2_acc(q.a * (cv[t] - m));
       s = wave_sum(ls);
     } else {
-      const float2 *tab = p.chunk_tab + (int64_t)g * p.nc_stride;
       float lm = kNegInf;
-      for (int c = lane; c < p.NC; c += 64) lm = fmaxf(lm, tab[c].x);
+      for (int c = lane; c < p.NC; c += 64) lm = fmaxf(lm, entry(i, c).x);
       m = wave_max(lm);
       if (greedy) {
+        // Lowest chunk holding the row maximum, then its lowest token equal to
+        // the maximum (the streaming pass keeps only chunk maxima for greedy rows).
+        int lc = 0x7FFFFFFF;
+        for (int c = lane; c < p.NC; c += 64)
+          if (entry(i, c).x == m) lc = min(lc, c);
+        lc = wave_min_i(lc);
+        Proc pr = q.proc;
+        pr.tau = sh.tau[i];
+        float zz[kChunk / 64];
+#pragma unroll
+        for (int t = 0; t < kChunk / 64; ++t) zz[t] = load_logit(p, g, min(lc * kChunk + t * 64 + lane, p.V - 1));
         int li = 0x7FFFFFFF;
-        for (int c = lane; c < p.NC; c += 64) {
-          const float2 e = tab[c];
-          if (e.x == m) li = min(li, __float_as_int(e.y));
+#pragma unroll
+        for (int t = kChunk / 64 - 1; t >= 0; --t) {
+          const int x = lc * kChunk + t * 64 + lane;
+          if (x < p.V && apply_proc(zz[t], x, pr) == m) li = x;
         }
         am = wave_min_i(li);
       } else if (m > kNegInf) {
         float ls = 0.0f;
         for (int c = lane; c < p.NC; c += 64) {
-          const float2 e = tab[c];
+          const float2 e = entry(i, c);
           if (e.x > kNegInf) ls += e.y * exp2_acc(q.a * (e.x - m));
         }
         s = wave_sum(ls);
@@ -317,15 +403,13 @@ __device__ void request_epilogue(const Params &p, const Req &q, EpiShared &sh) {
       sh.m[i] = m;
       sh.s[i] = s;
       sh.amax[i] = am;
-      sh.state[i] = st;
-      sh.tau[i] = (st == kRowDense) ? kNegInf : p.cand_tau[g];
       p.row_info[g] = make_float4(m, s, __int_as_float(am), __int_as_float(st));
     }
   }
   __syncthreads();
   if (tid == 0) {
     int bad = 0;
-    for (int i = 0; i <= K; ++i) bad |= !__builtin_isfinite(sh.m[i]);
+    for (int i = 0; i < nrow; ++i) bad |= !__builtin_isfinite(sh.m[i]);
     sh.bad = bad;
   }
   __syncthreads();
@@ -339,7 +423,7 @@ __device__ void request_epilogue(const Params &p, const Req &q, EpiShared &sh) {
   if (wave == 0) {
     bool rej = false;
     if (lane < K) {
-      const int d = p.draft_ids[q.c0 + lane];
+      const int d = sh.d[lane];
       const int g = q.g0 + lane;
       if (greedy) {
         rej = d != sh.amax[lane];
@@ -347,14 +431,22 @@ __device__ void request_epilogue(const Params &p, const Req &q, EpiShared &sh) {
       } else {
         const bool valid = d >= 0 && d < p.V;
         float pd = 0.0f;
-        if (valid) {
-          Proc pr = q.proc;
-          pr.tau = sh.tau[lane];
-          const float z = apply_proc(load_logit(p, g, d), d, pr);
-          pd = exp2_acc(q.a * (z - sh.m[lane])) / sh.s[lane];
-        }
         double qd = 1.0;
-        if (p.draft_probs) qd = valid ? (double)p.draft_probs[(int64_t)(q.c0 + lane) * p.dstride + d] : 0.0;
+        if (valid) {
+          float z;
+          if (sh.state[lane] >= 0) {  // compact row: not streamed, read z_d and q_d here
+            Proc pr = q.proc;
+            pr.tau = sh.tau[lane];
+            z = apply_proc(load_logit(p, g, d), d, pr);
+            if (p.draft_probs) qd = (double)p.draft_probs[(int64_t)(q.c0 + lane) * p.dstride + d];
+          } else {
+            z = sh.zd[lane];
+            if (p.draft_probs) qd = (double)sh.qd[lane];
+          }
+          pd = exp2_acc(q.a * (z - sh.m[lane])) / sh.s[lane];
+        } else if (p.draft_probs) {
+          qd = 0.0;
+        }
         const double u = u_accept(rng_block(p, 0, (uint32_t)g, kTagAccept).x);
         rej = !(valid && qd > 0.0 && (double)pd >= u * qd);
         if (p.dbg_p_draft) p.dbg_p_draft[q.c0 + lane] = pd;
@@ -368,15 +460,14 @@ __device__ void request_epilogue(const Params &p, const Req &q, EpiShared &sh) {
 
   // Accepted prefix, padding and counts.
   for (int t = tid; t < p.out_stride; t += kThreads) {
-    int v = -1;
-    if (t < j) v = p.draft_ids[q.c0 + t];
+    const int v = t < j ? sh.d[t] : -1;
     if (t != j) p.out_tokens[(int64_t)r * p.out_stride + t] = v;
   }
   if (tid == 0) {
     p.out_ns[r] = j + 1;
     p.out_nr[r] = K - j;
   }
-  int64_t out_j = (int64_t)r * p.out_stride + j;
+  const int64_t out_j = (int64_t)r * p.out_stride + j;
 
   if (greedy) {
     if (tid == 0) p.out_tokens[out_j] = sh.amax[j];
@@ -385,21 +476,23 @@ __device__ void request_epilogue(const Params &p, const Req &q, EpiShared &sh) {
 
   const int gs = q.g0 + j;
   const bool rejected = j < K;
-  const int dj = rejected ? p.draft_ids[q.c0 + j] : -1;
+  const int dj = rejected ? sh.d[j] : -1;
   const float m = sh.m[j], s = sh.s[j];
   Proc pr = q.proc;
   pr.tau = sh.tau[j];
   const int st = sh.state[j];
+  const float a = q.a;
 
   if (st >= 0) {
     // Compact top-k row: the race runs over the kept tokens only.
+    __syncthreads();  // the LDS chunk-table cache is reused for the candidates
     const float *cv = p.cand_val + (int64_t)gs * kCandCap;
     const int32_t *cix = p.cand_idx + (int64_t)gs * kCandCap;
     const float *qrow = (rejected && p.draft_probs) ? p.draft_probs + (int64_t)(q.c0 + j) * p.dstride : nullptr;
     float part = 0.0f;
     for (int t = tid; t < st; t += kThreads) {
       const int x = cix[t];
-      const float pxv = exp2_acc(q.a * (cv[t] - m)) / s;
+      const float pxv = exp2_acc(a * (cv[t] - m)) / s;
       float w = pxv;
       if (rejected) {
         if (qrow)
@@ -407,13 +500,13 @@ __device__ void request_epilogue(const Params &p, const Req &q, EpiShared &sh) {
         else if (x == dj)
           w = 0.0f;
       }
-      sh.ci[t] = x;
-      sh.cw[t] = w;
+      sh.u.cand.ci[t] = x;
+      sh.u.cand.cw[t] = w;
       part += w;
     }
     const float total = block_sum(part, sh.red);
     if (!(total > 0.0f)) {  // residual empty by rounding: race over p
-      for (int t = tid; t < st; t += kThreads) sh.cw[t] = exp2_acc(q.a * (cv[t] - m)) / s;
+      for (int t = tid; t < st; t += kThreads) sh.u.cand.cw[t] = exp2_acc(a * (cv[t] - m)) / s;
     }
     const int x = compact_race(p, (uint32_t)gs, st, sh);
     if (tid == 0) p.out_tokens[out_j] = x;
@@ -427,155 +520,377 @@ __device__ void request_epilogue(const Params &p, const Req &q, EpiShared &sh) {
   }
 
   // Dense race over p_j (bonus row, or the rejected row with d_j removed).
-  // Chunk weights come from the chunk table, W_c = s_c exp2(a (m_c - m)); the
-  // token weights inside a chunk use the streaming pass's own per-element
-  // formula exp2(fma(z, a, -hi_c)) (a common factor per chunk cancels in the
-  // token race), so a chunk with positive weight always has a token with one.
-  const float2 *tab = p.chunk_tab + (int64_t)gs * p.nc_stride;
-  const float a = q.a;
+  // Chunk weights come from the chunk table, W_c = s_c exp2(a (m_c - m)), with
+  // the chunk of d_j replaced by its sum without d_j; wave 0 runs the chunk
+  // race.  Token weights inside the winning chunk use the streaming pass's
+  // per-element formula exp2(fma(z, a, -a m_c)) (a common factor per chunk
+  // cancels in the token race), so a chunk with positive weight always has a
+  // token with one; the 4 waves run the token race, 4 tokens per thread.
   bool excl = rejected && dj >= 0 && dj < p.V;
   const int cd = excl ? dj / kChunk : -1;
-  float Wd = 0.0f;
-  if (excl) {
-    const float2 e = tab[cd];
-    const float hi = a * e.x, lo = __builtin_fmaf(a, e.x, -hi);
-    float part = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int x = cd * kChunk + 4 * tid + k;
-      if (x < p.V && x != dj) part += exp2_acc(__builtin_fmaf(apply_proc(load_logit(p, gs, x), x, pr), a, -hi));
-    }
-    Wd = e.x > kNegInf ? block_sum(part, sh.red) * exp2_acc(-lo) * exp2_acc(a * (e.x - m)) : 0.0f;
-  }
+  const float sxj = excl ? sh.sx[j] : 0.0f;
   auto chunk_w = [&](int c) -> float {
-    if (excl && c == cd) return Wd;
-    const float2 e = tab[c];
-    return e.x > kNegInf ? e.y * exp2_acc(a * (e.x - m)) : 0.0f;
+    const float2 e = entry(j, c);
+    if (!(e.x > kNegInf)) return 0.0f;
+    return ((excl && c == cd) ? sxj : e.y) * exp2_acc(a * (e.x - m));
   };
-  int cstar = chunk_race(p, (uint32_t)gs, p.NC, chunk_w, sh.red);
+  int cstar = block_chunk_race(p, (uint32_t)gs, p.NC, chunk_w, sh.red);
   if (cstar < 0 && excl) {  // nothing left once d_j is removed (rounding): race over p_j
     excl = false;
-    cstar = chunk_race(p, (uint32_t)gs, p.NC, chunk_w, sh.red);
+    cstar = block_chunk_race(p, (uint32_t)gs, p.NC, chunk_w, sh.red);
   }
   int x = -1;
   if (cstar >= 0) {
-    const float hi = a * tab[cstar].x;
-    x = token_race(
-        p, (uint32_t)gs, cstar,
-        [&](int xx) -> float {
-          if (excl && xx == dj) return 0.0f;
-          return exp2_acc(__builtin_fmaf(apply_proc(load_logit(p, gs, xx), xx, pr), a, -hi));
-        },
-        sh.red);
+    const float hi = a * entry(j, cstar).x;
+    const int x0 = cstar * kChunk + 4 * tid;
+    float z[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) z[k] = load_logit(p, gs, min(x0 + k, p.V - 1));  // all loads first
+    const uint4 w4 = rng_block(p, (uint32_t)x0 >> 2, (uint32_t)gs, kTagToken);
+    ArgMax best{-1.0f, 0x7FFFFFFF};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int xx = x0 + k;
+      if (xx < p.V && !(excl && xx == dj)) {
+        const float wx = exp2_acc(__builtin_fmaf(apply_proc(z[k], xx, pr), a, -hi));
+        if (wx > 0.0f) {
+          ArgMax o{wx / exp_noise(pick(w4, k)), xx};
+          if (better(o, best)) best = o;
+        }
+      }
+    }
+    const ArgMax bb = block_argmax(best, sh.red);
+    x = bb.s < 0.0f ? -1 : bb.i;
   }
   if (tid == 0) p.out_tokens[out_j] = x;
 }
 
 // ---------------------------------------------------------------------------
 // Streaming statistics pass.
+//
+// Persistent and balanced: the grid is the resident workgroup count, and
+// workgroup w owns the contiguous slice [w N / G, (w+1) N / G) of the N = R NC
+// chunks, row-major.  Its waves take every 4th chunk of the slice through a
+// three-deep load pipeline and write each chunk's (max, scaled mass) entry to
+// the chunk table.  Nothing here depends on the draft tokens: the request
+// epilogue kernel, launched next on the same stream, reads the tables.
 // ---------------------------------------------------------------------------
-template <int DT, int CPW>
+struct RowInfo {
+  int g, r, i, c0, K, g0, mode, st;  // mode kModeInvalid: row skipped
+  float a, theta, tau;
+  const int32_t *counts;
+};
+constexpr int kRowCache = kSliceRows;  // rows of a slice looked up before streaming
+
+__device__ __forceinline__ RowInfo row_info_of(const Params &p, const Req &q, int g) {
+  RowInfo ri;
+  ri.g = g;
+  ri.r = q.r;
+  ri.i = g - q.g0;
+  ri.c0 = q.c0;
+  ri.K = q.K;
+  ri.g0 = q.g0;
+  const bool ok = q.cu_ok && ri.i >= 0 && ri.i <= q.K && q.mode != kModeInvalid;
+  ri.mode = ok ? q.mode : kModeInvalid;
+  ri.st = ok ? row_state(p, g) : kRowDense;
+  ri.a = q.a;
+  ri.theta = q.proc.theta;
+  ri.counts = q.proc.counts;
+  ri.tau = (ok && ri.st == kRowThreshold) ? p.cand_tau[g] : kNegInf;
+  return ri;
+}
+
+template <int DT>
+__device__ __forceinline__ void issue_chunk(const Params &p, int64_t f, int64_t end, u32x4 (&v)[Layout<DT>::kVec]) {
+  using L = Layout<DT>;
+  if (f >= end || !p.vec_ok) return;
+  const int64_t g = f / p.NC;
+  const int c = (int)(f - g * p.NC);
+  if ((c + 1) * kChunk > p.V) return;
+  const int lane = threadIdx.x & 63;
+  const u32x4 *src = reinterpret_cast<const u32x4 *>(static_cast<const char *>(p.logits) +
+                                                    (g * p.lstride + (int64_t)c * kChunk) * L::kBytes);
+#pragma unroll
+  for (int h = 0; h < L::kVec; ++h) v[h] = __builtin_nontemporal_load(&src[h * 64 + lane]);
+}
+
+// Statistics of chunk c of row ri.g into the chunk table: (max, sum of
+// exp2(a (z - max))).  Greedy rows carry a = 0 and only their maxima are used.
+template <int DT>
+__device__ __forceinline__ void chunk_stats(const Params &p, const RowInfo &ri, int c, const u32x4 (&v)[Layout<DT>::kVec]) {
+  using L = Layout<DT>;
+  const int lane = threadIdx.x & 63;
+  const int g = ri.g;
+  Proc pr;
+  pr.counts = ri.counts;
+  pr.theta = ri.theta;
+  pr.tau = ri.tau;
+  float z[16];
+  if (p.vec_ok && (c + 1) * kChunk <= p.V) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) z[e] = L::elem(v, e);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int x = c * kChunk + L::local(e, lane);
+      z[e] = x < p.V ? load_logit(p, g, x) : kNegInf;
+    }
+  }
+  if (pr.counts != nullptr || pr.tau > kNegInf) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int x = c * kChunk + L::local(e, lane);
+      if (x < p.V) z[e] = apply_proc(z[e], x, pr);
+    }
+  }
+  float mx = z[0];
+#pragma unroll
+  for (int e = 1; e < 16; ++e) mx = fmaxf(mx, z[e]);
+  const float mc = wave_max(mx);
+  // exp2(a (z - mc)) = exp2(fma(z, a, -hi)) * exp2(-lo), a * mc = hi + lo exactly.
+  const float a = ri.a;
+  const float hi = a * mc;
+  const float lo = __builtin_fmaf(a, mc, -hi);
+  float sa = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) sa += exp2_acc(__builtin_fmaf(z[e], a, -hi));
+  const float2 entry = make_float2(mc, mc > kNegInf ? wave_sum(sa) * exp2_acc(-lo) : 0.0f);
+  if (lane == 0) p.chunk_tab[(int64_t)g * p.nc_stride + c] = entry;
+}
+
+// Flattened chunk ff of a slice: row lookup (cached) and statistics.
+template <int DT>
+__device__ __forceinline__ void process_chunk(const Params &p, int64_t ff, const u32x4 (&v)[Layout<DT>::kVec],
+                                              RowInfo &cur, const RowInfo *rows, int g_first) {
+  const int g = (int)(ff / p.NC);
+  const int c = (int)(ff - (int64_t)g * p.NC);
+  if (g != cur.g) cur = (g - g_first < kRowCache) ? rows[g - g_first] : row_info_of(p, lookup_req(p, g), g);
+  if (cur.mode != kModeInvalid && cur.st < 0) chunk_stats<DT>(p, cur, c, v);
+}
+
+// Row state read back from LDS is the same in every lane: keep it in SGPRs.
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ float uni(float v) { return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v))); }
+__device__ __forceinline__ RowInfo uniform_row(const RowInfo &x) {
+  RowInfo y;
+  y.g = uni(x.g);
+  y.r = uni(x.r);
+  y.i = uni(x.i);
+  y.c0 = uni(x.c0);
+  y.K = uni(x.K);
+  y.g0 = uni(x.g0);
+  y.mode = uni(x.mode);
+  y.st = uni(x.st);
+  y.a = uni(x.a);
+  y.theta = uni(x.theta);
+  y.tau = uni(x.tau);
+  const uintptr_t c = (uintptr_t)x.counts;
+  y.counts = (const int32_t *)(((uintptr_t)(uint32_t)uni((int)(uint32_t)c)) | ((uintptr_t)(uint32_t)uni((int)(uint32_t)(c >> 32)) << 32));
+  return y;
+}
+
+struct StatsShared {
+  RowInfo rows[kRowCache];
+};
+
+template <int DT>
 __global__ __launch_bounds__(kThreads) void stats_kernel(Params p) {
   using L = Layout<DT>;
   constexpr int NV = L::kVec;
-  __shared__ EpiShared sh;
-
+  __shared__ StatsShared sh;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int g = blockIdx.x / p.nseg;
-  const int seg = blockIdx.x - g * p.nseg;
-  const int cbase = seg * p.cps + wave;
+  const int64_t N = (int64_t)p.R * p.NC;
+  const int64_t start = (int64_t)blockIdx.x * N / gridDim.x;
+  const int64_t end = (int64_t)(blockIdx.x + 1) * N / gridDim.x;
+  if (start >= end) return;
+  const int g_first = (int)(start / p.NC), g_last = (int)((end - 1) / p.NC);
+  const int nrows = g_last - g_first + 1;
 
-  // Issue this wave's streaming loads before anything else.
-  const char *rowp = static_cast<const char *>(p.logits) + (int64_t)g * p.lstride * L::kBytes;
-  u32x4 raw[CPW][NV];
-#pragma unroll
-  for (int k = 0; k < CPW; ++k) {
-    const int c = cbase + kWaves * k;
-    if (p.vec_ok && c < p.NC && (c + 1) * kChunk <= p.V) {
-      const u32x4 *v = reinterpret_cast<const u32x4 *>(rowp + (int64_t)c * kChunk * L::kBytes);
-#pragma unroll
-      for (int h = 0; h < NV; ++h) raw[k][h] = __builtin_nontemporal_load(&v[h * 64 + lane]);
-    }
+  // Three chunks in flight per wave before anything else.
+  u32x4 A[NV], Bv[NV], Cv[NV];
+  int64_t f = start + wave;
+  issue_chunk<DT>(p, f, end, A);
+  issue_chunk<DT>(p, f + kWaves, end, Bv);
+  issue_chunk<DT>(p, f + 2 * kWaves, end, Cv);
+
+  // Request lookups for the first rows of the slice (overlapping the loads).
+  if (wave < min(nrows, kRowCache)) {
+    const int g = g_first + wave;
+    const RowInfo ri = row_info_of(p, lookup_req(p, g), g);
+    if (lane == 0) sh.rows[wave] = ri;
+  }
+  __syncthreads();
+
+  RowInfo cur;
+  cur.g = -1;
+  for (; f < end; f += 3 * kWaves) {
+    process_chunk<DT>(p, f, A, cur, sh.rows, g_first);
+    issue_chunk<DT>(p, f + 3 * kWaves, end, A);
+    if (f + kWaves >= end) break;
+    process_chunk<DT>(p, f + kWaves, Bv, cur, sh.rows, g_first);
+    issue_chunk<DT>(p, f + 4 * kWaves, end, Bv);
+    if (f + 2 * kWaves >= end) break;
+    process_chunk<DT>(p, f + 2 * kWaves, Cv, cur, sh.rows, g_first);
+    issue_chunk<DT>(p, f + 5 * kWaves, end, Cv);
   }
 
-  const int r = find_request(p.cu, p.B, g);
-  arrive_begin(p.req_ctr + r, p.epoch);
-  const Req q = load_req(p, r);
-  const bool row_ok = q.cu_ok && g >= q.g0 && g <= q.g0 + q.K && q.mode != kModeInvalid;
-  const int st = row_state(p, g);
-
-  if (row_ok && st < 0) {
-    Proc pr = q.proc;
-    if (st == kRowThreshold) pr.tau = p.cand_tau[g];
-    const bool plain = pr.counts == nullptr && !(pr.tau > kNegInf);
-    const bool greedy = q.mode == kModeGreedy;
-    const float a = q.a;
-    float2 *tab = p.chunk_tab + (int64_t)g * p.nc_stride;
-#pragma unroll
-    for (int k = 0; k < CPW; ++k) {
-      const int c = cbase + kWaves * k;
-      if (c >= p.NC) break;
-      float z[16];
-      if (p.vec_ok && (c + 1) * kChunk <= p.V) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) z[e] = L::elem(raw[k], e);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int x = c * kChunk + L::local(e, lane);
-          z[e] = x < p.V ? load_logit(p, g, x) : kNegInf;
-        }
-      }
-      if (!plain) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int x = c * kChunk + L::local(e, lane);
-          if (x < p.V) z[e] = apply_proc(z[e], x, pr);
-        }
-      }
-      float mx = z[0];
-#pragma unroll
-      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, z[e]);
-      const float mc = wave_max(mx);
-      float2 entry;
-      if (greedy) {
-        int li = 0x7FFFFFFF;
-#pragma unroll
-        for (int e = 15; e >= 0; --e)
-          if (z[e] == mc) li = L::local(e, lane);
-        entry = make_float2(mc, __int_as_float(c * kChunk + wave_min_i(li)));
-      } else if (mc > kNegInf) {
-        // exp2(a (z - mc)) = exp2(fma(z, a, -hi)) * exp2(-lo), a * mc = hi + lo exactly.
-        const float hi = a * mc;
-        const float lo = __builtin_fmaf(a, mc, -hi);
-        float sacc = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) sacc += exp2_acc(__builtin_fmaf(z[e], a, -hi));
-        entry = make_float2(mc, wave_sum(sacc) * exp2_acc(-lo));
-      } else {
-        entry = make_float2(kNegInf, 0.0f);
-      }
-      if (lane == 0) tab[c] = entry;
-    }
-  }
-
-  if (!arrive_end(p.req_ctr + r, p.epoch, (unsigned)((q.cu_ok ? q.K + 1 : 1) * p.nseg), &sh.flag)) return;
-  request_epilogue(p, q, sh);
 }
 
 // ---------------------------------------------------------------------------
-// Residual pass (draft-probs mode, dense rows): chunk masses of
-// w = max(0, p_j - q_j) for each rejected request, then the race.
+// Fast streaming pass: aligned rows, V a multiple of the vector width, no
+// penalty and no top-k (the common case, and the no-draft-probs workload).
+// Same slices and tables as stats_kernel, with a loop the compiler
+// can pipeline exactly: every wave issues one unconditional set of 16-byte
+// loads per chunk (lanes past the row end read the row's first vector and are
+// masked), tracks (row, chunk) in 32-bit, and keeps three chunks in flight.
+// ---------------------------------------------------------------------------
+template <int DT>
+__device__ __forceinline__ void fast_load(const Params &p, int g, int c, u32x4 (&v)[Layout<DT>::kVec]) {
+  using L = Layout<DT>;
+  constexpr int kTok = 16 / L::kBytes;  // tokens per 16-byte vector
+  const int lane = threadIdx.x & 63;
+  // Uniform row base plus a 32-bit per-lane byte offset (SGPR-base addressing).
+  const char *row = static_cast<const char *>(p.logits) + (int64_t)g * p.lstride * L::kBytes;
+#pragma unroll
+  for (int h = 0; h < L::kVec; ++h) {
+    const int x = c * kChunk + L::local(h * kTok, lane);  // first token of this lane's vector h
+    const uint32_t off = x + kTok <= p.V ? (uint32_t)x * L::kBytes : 0u;
+    v[h] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(row + off));
+  }
+}
+
+__device__ __forceinline__ void advance_chunk(int &g, int &c, int by, int NC) {
+  c += by;
+  while (c >= NC) {
+    c -= NC;
+    ++g;
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ void fast_chunk(const Params &p, const RowInfo &ri, int c, const u32x4 (&v)[Layout<DT>::kVec]) {
+  using L = Layout<DT>;
+  const int lane = threadIdx.x & 63;
+  float z[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) z[e] = L::elem(v, e);
+  if ((c + 1) * kChunk > p.V) {  // row tail: tokens past V do not exist
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      if (c * kChunk + L::local(e, lane) >= p.V) z[e] = kNegInf;
+  }
+  float mx = z[0];
+#pragma unroll
+  for (int e = 1; e < 16; ++e) mx = fmaxf(mx, z[e]);
+  const float mc = wave_max(mx);
+  // exp2(a (z - mc)) = exp2(fma(z, a, -hi)) * exp2(-lo), a * mc = hi + lo
+  // exactly; greedy rows carry a = 0 and only their maxima are used.
+  const float a = ri.a;
+  const float hi = a * mc;
+  const float lo = __builtin_fmaf(a, mc, -hi);
+  float sa = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) sa += exp2_acc(__builtin_fmaf(z[e], a, -hi));
+  const float2 entry = make_float2(mc, mc > kNegInf ? wave_sum(sa) * exp2_acc(-lo) : 0.0f);
+  if (lane == 0 && ri.mode != kModeInvalid) p.chunk_tab[(int64_t)ri.g * p.nc_stride + c] = entry;
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void stats_fast_kernel(Params p) {
+  using L = Layout<DT>;
+  constexpr int NV = L::kVec;
+  __shared__ StatsShared sh;
+  const int wave = uni((int)(threadIdx.x >> 6));
+  const int N = p.R * p.NC;
+  const int start = (int)((int64_t)blockIdx.x * N / gridDim.x);
+  const int end = (int)((int64_t)(blockIdx.x + 1) * N / gridDim.x);
+  if (start >= end) return;
+  const int g_first = start / p.NC, g_last = (end - 1) / p.NC;
+  const int nrows = g_last - g_first + 1;
+  const int len = end - start;
+  const int n = wave < len ? (len - wave + kWaves - 1) / kWaves : 0;
+
+  int ga = (start + wave) / p.NC, ca = start + wave - ga * p.NC;
+  int gb = ga, cb = ca, gc = ga, cc = ca;
+  advance_chunk(gb, cb, kWaves, p.NC);
+  advance_chunk(gc, cc, 2 * kWaves, p.NC);
+  // The first three loads are unconditional (a wave with fewer chunks reads
+  // the slice's first chunk instead), so that every path into the loop has the
+  // same loads in flight and the waits stay three chunks deep.
+  u32x4 A[NV], Bv[NV], Cv[NV];
+  fast_load<DT>(p, n > 0 ? ga : g_first, n > 0 ? ca : 0, A);
+  fast_load<DT>(p, n > 1 ? gb : g_first, n > 1 ? cb : 0, Bv);
+  fast_load<DT>(p, n > 2 ? gc : g_first, n > 2 ? cc : 0, Cv);
+
+  // Request lookups for the slice's rows (overlapping the loads); q(d) is
+  // fetched here too so that the loop issues no dependent loads.
+  if (wave < nrows) {
+    const int g = g_first + wave;
+    const RowInfo ri = row_info_of(p, lookup_req(p, g), g);
+    if ((threadIdx.x & 63) == 0) sh.rows[wave] = ri;
+  }
+  __syncthreads();
+
+  RowInfo cur = uniform_row(sh.rows[ga - g_first]);
+  int k = 0;
+  for (; k + 5 < n; k += 3) {
+    if (ga != cur.g) cur = uniform_row(sh.rows[ga - g_first]);
+    fast_chunk<DT>(p, cur, ca, A);
+    advance_chunk(ga, ca, 3 * kWaves, p.NC);
+    fast_load<DT>(p, ga, ca, A);
+    if (gb != cur.g) cur = uniform_row(sh.rows[gb - g_first]);
+    fast_chunk<DT>(p, cur, cb, Bv);
+    advance_chunk(gb, cb, 3 * kWaves, p.NC);
+    fast_load<DT>(p, gb, cb, Bv);
+    if (gc != cur.g) cur = uniform_row(sh.rows[gc - g_first]);
+    fast_chunk<DT>(p, cur, cc, Cv);
+    advance_chunk(gc, cc, 3 * kWaves, p.NC);
+    fast_load<DT>(p, gc, cc, Cv);
+  }
+  // Drain: at most 5 chunks left, loads only while in range.
+#pragma unroll
+  for (int t = 0; t < 6; ++t) {
+    if (k + t >= n) break;
+    if (t % 3 == 0) {
+      if (ga != cur.g) cur = uniform_row(sh.rows[ga - g_first]);
+      fast_chunk<DT>(p, cur, ca, A);
+      if (k + t + 3 < n) {
+        advance_chunk(ga, ca, 3 * kWaves, p.NC);
+        fast_load<DT>(p, ga, ca, A);
+      }
+    } else if (t % 3 == 1) {
+      if (gb != cur.g) cur = uniform_row(sh.rows[gb - g_first]);
+      fast_chunk<DT>(p, cur, cb, Bv);
+      if (k + t + 3 < n) {
+        advance_chunk(gb, cb, 3 * kWaves, p.NC);
+        fast_load<DT>(p, gb, cb, Bv);
+      }
+    } else {
+      if (gc != cur.g) cur = uniform_row(sh.rows[gc - g_first]);
+      fast_chunk<DT>(p, cur, cc, Cv);
+      if (k + t + 3 < n) {
+        advance_chunk(gc, cc, 3 * kWaves, p.NC);
+        fast_load<DT>(p, gc, cc, Cv);
+      }
+    }
+  }
+
+}
+
+// ---------------------------------------------------------------------------
+// Residual pass (draft-probs mode, dense rows).  resid_kernel: chunk masses of
+// w = max(0, p_j - q_j) for each rejected request (one workgroup per segment
+// of cps chunks); resid_race_kernel: the race over them (one workgroup per
+// request).  A request is active when its res_req entry carries this call's
+// epoch.
 // ---------------------------------------------------------------------------
 template <int DT>
 __global__ __launch_bounds__(kThreads) void resid_kernel(Params p) {
-  __shared__ EpiShared sh;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = blockIdx.x / p.nseg;
   const int seg = blockIdx.x - r * p.nseg;
   const int4 rq = p.res_req[r];
   if (rq.w != (int)p.epoch) return;
-  arrive_begin(p.res_ctr + r, p.epoch);
   const Req q = load_req(p, r);
   const int gs = rq.x, j = rq.y;
   const float4 ri = p.row_info[gs];
@@ -584,7 +899,6 @@ __global__ __launch_bounds__(kThreads) void resid_kernel(Params p) {
   if (__float_as_int(ri.w) == kRowThreshold) pr.tau = p.cand_tau[gs];
   const float *qrow = p.draft_probs + (int64_t)(q.c0 + j) * p.dstride;
   float *rt = p.res_tab + (int64_t)r * p.nc_stride;
-
   for (int c = seg * p.cps + wave; c < min(p.NC, (seg + 1) * p.cps); c += kWaves) {
     float acc = 0.0f;
     for (int t = lane; t < kChunk; t += 64) {
@@ -597,31 +911,65 @@ __global__ __launch_bounds__(kThreads) void resid_kernel(Params p) {
     const float Wc = wave_sum(acc);
     if (lane == 0) rt[c] = Wc;
   }
+}
 
-  if (!arrive_end(p.res_ctr + r, p.epoch, (unsigned)p.nseg, &sh.flag)) return;
-
+__global__ __launch_bounds__(kThreads) void resid_race_kernel(Params p) {
+  __shared__ BlockScratch red;
+  const int r = blockIdx.x;
+  const int4 rq = p.res_req[r];
+  if (rq.w != (int)p.epoch) return;
+  const Req q = load_req(p, r);
+  const int gs = rq.x, j = rq.y;
+  const float4 ri = p.row_info[gs];
+  const float m = ri.x, inv_s = 1.0f / ri.y, a = q.a;
+  Proc pr = q.proc;
+  if (__float_as_int(ri.w) == kRowThreshold) pr.tau = p.cand_tau[gs];
+  const float *qrow = p.draft_probs + (int64_t)(q.c0 + j) * p.dstride;
+  const float *rt = p.res_tab + (int64_t)r * p.nc_stride;
+  // An empty residual (rounding) falls back to racing over p_j.
   float part = 0.0f;
   for (int c = threadIdx.x; c < p.NC; c += kThreads) part += rt[c];
-  const bool fallback = !(block_sum(part, sh.red) > 0.0f);
+  const bool fallback = !(block_sum(part, red) > 0.0f);
   const float2 *tab = p.chunk_tab + (int64_t)gs * p.nc_stride;
-  const int cstar = chunk_race(
-      p, (uint32_t)gs, p.NC,
-      [&](int c) -> float {
-        if (!fallback) return rt[c];
-        const float2 e = tab[c];
-        return e.x > kNegInf ? e.y * exp2_acc(a * (e.x - m)) : 0.0f;
-      },
-      sh.red);
+  const int cstar = block_chunk_race(p, (uint32_t)gs, p.NC, [&](int c) -> float {
+    if (!fallback) return rt[c];
+    const float2 e = tab[c];
+    return e.x > kNegInf ? e.y * exp2_acc(a * (e.x - m)) : 0.0f;
+  }, red);
   int x = -1;
-  if (cstar >= 0)
-    x = token_race(
-        p, (uint32_t)gs, cstar,
-        [&](int xx) -> float {
-          const float px = exp2_acc(a * (apply_proc(load_logit(p, gs, xx), xx, pr) - m)) * inv_s;
-          return fallback ? px : fmaxf(px - qrow[xx], 0.0f);
-        },
-        sh.red);
+  if (cstar >= 0) {
+    const int x0 = cstar * kChunk + 4 * (int)threadIdx.x;
+    float z[4], qx[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {  // all loads first
+      const int xc = min(x0 + k, p.V - 1);
+      z[k] = load_logit(p, gs, xc);
+      qx[k] = qrow[xc];
+    }
+    const uint4 w4 = rng_block(p, (uint32_t)x0 >> 2, (uint32_t)gs, kTagToken);
+    ArgMax best{-1.0f, 0x7FFFFFFF};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int xx = x0 + k;
+      if (xx < p.V) {
+        const float px = exp2_acc(a * (apply_proc(z[k], xx, pr) - m)) * inv_s;
+        const float wx = fallback ? px : fmaxf(px - qx[k], 0.0f);
+        if (wx > 0.0f) {
+          ArgMax o{wx / exp_noise(pick(w4, k)), xx};
+          if (better(o, best)) best = o;
+        }
+      }
+    }
+    const ArgMax bb = block_argmax(best, red);
+    x = bb.s < 0.0f ? -1 : bb.i;
+  }
   if (threadIdx.x == 0) p.out_tokens[(int64_t)r * p.out_stride + j] = x;
+}
+
+// Request epilogue kernel: one workgroup per request, after the stats pass.
+__global__ __launch_bounds__(kThreads) void epilogue_kernel(Params p) {
+  __shared__ EpiShared sh;
+  request_epilogue(p, load_req(p, blockIdx.x), sh);
 }
 
 // ---------------------------------------------------------------------------
@@ -892,11 +1240,29 @@ hipError_t launch_topk(const Params &p, hipStream_t s) {
 }
 
 hipError_t launch_stats(const Params &p, hipStream_t s) {
-  const dim3 grid((unsigned)(p.R * p.nseg));
-  if (p.dtype == 1)
-    stats_kernel<1, kStatsCPW><<<grid, dim3(kThreads), 0, s>>>(p);
+  const dim3 grid((unsigned)p.stats_grid);
+  if (p.fast)
+    p.dtype == 1 ? stats_fast_kernel<1><<<grid, dim3(kThreads), 0, s>>>(p)
+                 : stats_fast_kernel<0><<<grid, dim3(kThreads), 0, s>>>(p);
   else
-    stats_kernel<0, kStatsCPW><<<grid, dim3(kThreads), 0, s>>>(p);
+    p.dtype == 1 ? stats_kernel<1><<<grid, dim3(kThreads), 0, s>>>(p) : stats_kernel<0><<<grid, dim3(kThreads), 0, s>>>(p);
+  return hipGetLastError();
+}
+
+int stats_blocks_per_cu(int dtype, bool fast) {
+  int n = 0;
+  hipError_t e;
+  if (fast)
+    e = dtype == 1 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, stats_fast_kernel<1>, kThreads, 0)
+                   : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, stats_fast_kernel<0>, kThreads, 0);
+  else
+    e = dtype == 1 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, stats_kernel<1>, kThreads, 0)
+                   : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, stats_kernel<0>, kThreads, 0);
+  return e == hipSuccess && n > 0 ? n : 1;
+}
+
+hipError_t launch_epilogue(const Params &p, hipStream_t s) {
+  epilogue_kernel<<<dim3((unsigned)p.B), dim3(kThreads), 0, s>>>(p);
   return hipGetLastError();
 }
 
@@ -906,6 +1272,8 @@ hipError_t launch_resid(const Params &p, hipStream_t s) {
     resid_kernel<1><<<grid, dim3(kThreads), 0, s>>>(p);
   else
     resid_kernel<0><<<grid, dim3(kThreads), 0, s>>>(p);
+  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  resid_race_kernel<<<dim3((unsigned)p.B), dim3(kThreads), 0, s>>>(p);
   return hipGetLastError();
 }
 
