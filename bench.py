@@ -7,10 +7,12 @@ N(0, 3^2), no draft probabilities).  Inputs are resident in HBM before the
 timed region; the step rotates over several distinct input copies (more than
 1 GB in total) so that the 256 MB Infinity Cache cannot serve the logits.
 
-Prints one JSON line: verified logit rows/s over the timed steps, the stats
-kernel's achieved algorithmic HBM bandwidth against the 8 TB/s peak (timed
-with HIP events on the launch stream), and the CPU oracle's rate on a bounded
-sample of the same workload.
+Prints one JSON line: verified logit rows/s over the timed steps; the
+streaming statistics kernel's achieved algorithmic HBM bandwidth against the
+8 TB/s peak (its duration from dispatch-stamped HIP events on the launch
+stream, over a second, instrumented pass of the same steps); the whole verify
+call's and the epilogue kernel's durations; and the CPU oracle's rate on a
+bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -24,6 +26,34 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak
+# FETCH_SIZE / WRITE_SIZE counter record of the streaming kernel on this workload
+COUNTERS = os.path.join(ROOT, "profiles", "stats_fast_kernel_bf16_B256_V128256_counters.md")
+KERNEL_SOURCES = ["rejection_sampling_verify_05_amd/csrc/sv_kernels.hip", "rejection_sampling_verify_05_amd/csrc/sv_device.h",
+                  "rejection_sampling_verify_05_amd/csrc/sv_internal.h", "rejection_sampling_verify_05_amd/build.py"]
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic_per_row():
+    """HBM bytes per target row measured by the counter runs, or None when the
+    record is missing or was taken on different kernel sources."""
+    if not os.path.exists(COUNTERS):
+        return None
+    rec = {}
+    for line in open(COUNTERS):
+        if line.startswith("- ") and ": " in line:
+            k, v = line[2:].split(": ", 1)
+            rec[k.strip("` ")] = v.strip().strip("`")
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return float(rec["hbm_bytes_per_target_row"])
 
 
 def parse():
@@ -35,23 +65,10 @@ def parse():
     ap.add_argument("--copies", type=int, default=0, help="input copies to rotate (0: >= 1 GB)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="before warmup, run torch's copy kernel on 256 MiB three times (a known-size "
+                         "reference for the FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
-
-
-def algorithmic_bytes(inp, out_stride) -> int:
-    """Bytes the method must move in one spec_verify_run: every target row once,
-    each draft id (and q(d) plus the rejected requests' draft rows in draft-probs
-    mode: counted by the caller), cu, temperatures and the outputs."""
-    esize = inp["logits"].element_size()
-    B, R, D, V = inp["B"], inp["R"], inp["D"], inp["V"]
-    b = R * V * esize + D * 4 + (B + 1) * 4 + B * 4 + B * (out_stride + 2) * 4
-    if inp["draft_probs"] is not None:
-        b += D * 4
-    if inp["top_k"] is not None:
-        b += B * 4
-    if inp["rep_penalty"] is not None:
-        b += B * (V * 4 + 8)
-    return b
 
 
 def main():
@@ -106,15 +123,22 @@ def main():
         sv.spec_verify_run(ctx, o["vargs"], stream=stream)
         sv.spec_post_update(ctx, o["pargs"], stream=stream)
 
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     assert sv.spec_verify_read_error(ctx) == 0
 
-    # timed region: one event pair around each verify call (stats kernel) and
-    # one around the whole loop
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+    # Timed region: K steps between two synchronisations, nothing else on the
+    # stream.  `value` and ms_per_step come from it.
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     rows = 0
@@ -123,27 +147,53 @@ def main():
     t0.record(stream)
     for k in range(args.steps):
         i = args.warmup + k
+        step(i)
+        rows += copies[i % ncopies]["R"]
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t0.elapsed_time(t1)
+    assert sv.spec_verify_read_error(ctx) == 0
+
+    # The same K steps again, instrumented: the library launches its streaming
+    # and epilogue kernels with start/stop HIP events stamped by the dispatch
+    # on the launch stream (spec_verify_profile_*), and torch events on the
+    # same stream bracket each whole verify call.  The events add gaps between
+    # launches, which is why `value` comes from the clean pass above.
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    sv.spec_verify_profile_start(ctx, args.steps)
+    torch.cuda.synchronize()
+    for k in range(args.steps):
+        i = args.warmup + k
         o = outs[i % ncopies]
         o["vargs"].offset = i
         ev[k][0].record(stream)
         sv.spec_verify_run(ctx, o["vargs"], stream=stream)
         ev[k][1].record(stream)
         sv.spec_post_update(ctx, o["pargs"], stream=stream)
-        rows += copies[i % ncopies]["R"]
-    t1.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_ms = t0.elapsed_time(t1)
     verify_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    stream_ms, epi_ms = sv.spec_verify_profile_read(ctx, args.steps)
+    stream_ms, epi_ms = np.array(stream_ms), np.array(epi_ms)
+    assert len(stream_ms) == args.steps
     assert sv.spec_verify_read_error(ctx) == 0
 
-    # algorithmic bytes of the dominant kernel per launch, averaged over the copies used
-    bytes_per = np.mean([algorithmic_bytes(copies[(args.warmup + k) % ncopies], out_stride)
-                         for k in range(args.steps)])
+    # Dominant kernel: the streaming statistics pass.  Its algorithmic bytes
+    # are one read of every target row, R V s (s = 2 for bf16, 4 for fp32).
+    esize = first["logits"].element_size()
+    bytes_per = float(np.mean([copies[(args.warmup + k) % ncopies]["R"] * w.V * esize
+                               for k in range(args.steps)]))
     rows_per = rows / args.steps
-    kern_s = float(np.mean(verify_ms)) * 1e-3
-    achieved = bytes_per / kern_s / 1e9
+    achieved = bytes_per / (float(np.mean(stream_ms)) * 1e-3) / 1e9
+    per_row = recorded_traffic_per_row() if w.cid == "3" else None
+    traffic = None if per_row is None else int(per_row * float(np.mean(
+        [copies[(args.warmup + k) % ncopies]["R"] for k in range(args.steps)])))
     value = rows / (total_ms * 1e-3)
+
+    def pct(a):
+        return {"mean": round(float(np.mean(a)) * 1e3, 2), "p10": round(float(np.percentile(a, 10)) * 1e3, 2),
+                "p50": round(float(np.median(a)) * 1e3, 2), "p90": round(float(np.percentile(a, 90)) * 1e3, 2)}
 
     # CPU baseline: the oracle on a bounded sample of the same workload
     cpu = None
@@ -187,13 +237,12 @@ def main():
                    "global_batch": w.B, "rows_per_step": round(rows_per, 1), "input_copies": ncopies,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "stats_kernel (spec_verify_run)",
-                     "kernel_us": {"mean": round(float(np.mean(verify_ms)) * 1e3, 2),
-                                   "p10": round(float(np.percentile(verify_ms, 10)) * 1e3, 2),
-                                   "p50": round(float(np.median(verify_ms)) * 1e3, 2),
-                                   "p90": round(float(np.percentile(verify_ms, 90)) * 1e3, 2)},
-                     "bytes_per_launch": int(bytes_per)},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "stats_fast_kernel (streaming softmax statistics)",
+                     "kernel_us": pct(stream_ms), "bytes_per_launch": int(bytes_per),
+                     "bytes_rule": f"R*V*{esize} (each target row read once)"},
+        "verify_call_us": pct(verify_ms),
+        "epilogue_kernel_us": pct(epi_ms),
         "cpu_baseline": cpu,
         "wall_s": round(wall, 3),
     }

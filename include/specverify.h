@@ -190,6 +190,23 @@ const char *spec_verify_strerror(int status);
  */
 int spec_verify_read_error(sv_ctx *ctx, uint32_t *host_flags, hipStream_t stream);
 
+/*
+ * Measurement.  spec_verify_profile_start makes the next `max_calls` calls of
+ * spec_verify_run launch the streaming statistics kernel and the request
+ * epilogue kernel with start/stop HIP events that the launch stamps at the
+ * kernel's own start and end on the call's stream (hipExtLaunchKernel), so an
+ * interval is that kernel's execution time.  The events are created here,
+ * owned by the context, destroyed with it or by the next start.
+ * spec_verify_profile_read waits for those events, writes the per-call
+ * durations in milliseconds to the host arrays stream_ms[] and epilogue_ms[]
+ * (each with room for max_calls entries; either may be NULL), stores the
+ * number of recorded calls in *n_calls and stops recording.  Returns SV_OK,
+ * SV_EINVAL (null context, max_calls < 1 or > 65536, nothing started) or
+ * SV_EHIP.
+ */
+int spec_verify_profile_start(sv_ctx *ctx, int32_t max_calls);
+int spec_verify_profile_read(sv_ctx *ctx, float *stream_ms, float *epilogue_ms, int32_t *n_calls);
+
 #ifdef __cplusplus
 }
 #endif

@@ -120,6 +120,10 @@ def lib() -> ctypes.CDLL:
         L.spec_verify_strerror.restype = ctypes.c_char_p
         L.spec_verify_read_error.argtypes = [P, ctypes.POINTER(ctypes.c_uint32), P]
         L.spec_verify_read_error.restype = ctypes.c_int
+        L.spec_verify_profile_start.argtypes = [P, ctypes.c_int32]
+        L.spec_verify_profile_start.restype = ctypes.c_int
+        L.spec_verify_profile_read.argtypes = [P, P, P, ctypes.POINTER(ctypes.c_int32)]
+        L.spec_verify_profile_read.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -286,3 +290,24 @@ def spec_verify_read_error(ctx, stream=None) -> int:
     if st not in (SV_OK, SV_EINPUT):
         raise SpecVerifyError(st, "spec_verify_read_error")
     return int(flags.value)
+
+
+def spec_verify_profile_start(ctx, max_calls: int) -> None:
+    """Record HIP events around the streaming and epilogue kernels of the next
+    max_calls spec_verify_run calls (on their own stream)."""
+    st = lib().spec_verify_profile_start(ctx, int(max_calls))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "spec_verify_profile_start")
+
+
+def spec_verify_profile_read(ctx, max_calls: int):
+    """Wait for the recorded events; return (stream_ms, epilogue_ms) lists of
+    per-call kernel durations in milliseconds, and stop recording."""
+    a = (ctypes.c_float * max_calls)()
+    b = (ctypes.c_float * max_calls)()
+    n = ctypes.c_int32(0)
+    st = lib().spec_verify_profile_read(ctx, ctypes.cast(a, ctypes.c_void_p), ctypes.cast(b, ctypes.c_void_p),
+                                        ctypes.byref(n))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "spec_verify_profile_read")
+    return list(a[:n.value]), list(b[:n.value])

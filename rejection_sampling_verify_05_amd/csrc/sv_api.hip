@@ -26,11 +26,24 @@ struct sv_ctx {
   int32_t *cand_n;
   float *cand_tau;
   unsigned int *err;
+  hipEvent_t *ev;   // measurement: 4 events per recorded call
+  int32_t ev_cap, ev_n;
 };
 
 namespace {
 
+void free_events(sv_ctx *c) {
+  if (c->ev) {
+    for (int32_t i = 0; i < 4 * c->ev_cap; ++i)
+      if (c->ev[i]) (void)hipEventDestroy(c->ev[i]);
+    delete[] c->ev;
+  }
+  c->ev = nullptr;
+  c->ev_cap = c->ev_n = 0;
+}
+
 void free_ctx(sv_ctx *c) {
+  free_events(c);
   void *ptrs[] = {c->chunk_tab, c->row_info, c->res_req, c->res_tab,
                   c->cand_val,  c->cand_idx, c->cand_n,  c->cand_tau, c->err};
   for (void *p : ptrs)
@@ -179,9 +192,10 @@ extern "C" int spec_verify_run(sv_ctx *ctx, const sv_verify_args *a, hipStream_t
 
   if ((int64_t)p.B * p.nseg > 0x7FFFFFFF) return SV_ECAPACITY;
 
+  hipEvent_t *ev = (ctx->ev && ctx->ev_n < ctx->ev_cap) ? ctx->ev + 4 * ctx->ev_n++ : nullptr;
   if (p.has_topk && sv::launch_topk(p, stream) != hipSuccess) return SV_EHIP;
-  if (sv::launch_stats(p, stream) != hipSuccess) return SV_EHIP;
-  if (sv::launch_epilogue(p, stream) != hipSuccess) return SV_EHIP;
+  if (sv::launch_stats(p, stream, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr) != hipSuccess) return SV_EHIP;
+  if (sv::launch_epilogue(p, stream, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr) != hipSuccess) return SV_EHIP;
   if (p.draft_probs && sv::launch_resid(p, stream) != hipSuccess) return SV_EHIP;
   if (p.dbg_probs && sv::launch_dbg_probs(p, stream) != hipSuccess) return SV_EHIP;
   return SV_OK;
@@ -238,4 +252,39 @@ extern "C" int spec_verify_read_error(sv_ctx *ctx, uint32_t *host_flags, hipStre
   if (hipMemset(ctx->err, 0, sizeof h) != hipSuccess) return SV_EHIP;
   *host_flags = h;
   return h ? SV_EINPUT : SV_OK;
+}
+
+extern "C" int spec_verify_profile_start(sv_ctx *ctx, int32_t max_calls) {
+  if (!ctx || max_calls < 1 || max_calls > 65536) return SV_EINVAL;
+  free_events(ctx);
+  ctx->ev = new (std::nothrow) hipEvent_t[4 * (size_t)max_calls]();
+  if (!ctx->ev) return SV_EHIP;
+  ctx->ev_cap = max_calls;
+  for (int32_t i = 0; i < 4 * max_calls; ++i)
+    if (hipEventCreate(&ctx->ev[i]) != hipSuccess) {
+      free_events(ctx);
+      return SV_EHIP;
+    }
+  return SV_OK;
+}
+
+extern "C" int spec_verify_profile_read(sv_ctx *ctx, float *stream_ms, float *epilogue_ms, int32_t *n_calls) {
+  if (!ctx || !n_calls || !ctx->ev) return SV_EINVAL;
+  const int32_t n = ctx->ev_n;
+  int st = SV_OK;
+  for (int32_t i = 0; i < n && st == SV_OK; ++i) {
+    hipEvent_t *e = ctx->ev + 4 * i;
+    if (hipEventSynchronize(e[3]) != hipSuccess) {
+      st = SV_EHIP;
+      break;
+    }
+    float a = 0.0f, b = 0.0f;
+    if (hipEventElapsedTime(&a, e[0], e[1]) != hipSuccess || hipEventElapsedTime(&b, e[2], e[3]) != hipSuccess)
+      st = SV_EHIP;
+    if (stream_ms) stream_ms[i] = a;
+    if (epilogue_ms) epilogue_ms[i] = b;
+  }
+  *n_calls = st == SV_OK ? n : 0;
+  free_events(ctx);
+  return st;
 }

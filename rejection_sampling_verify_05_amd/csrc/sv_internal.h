@@ -79,8 +79,9 @@ struct PostParams {
 
 // Launchers (sv_kernels.hip).  Return the hipError_t of the last launch.
 hipError_t launch_topk(const Params &p, hipStream_t s);
-hipError_t launch_stats(const Params &p, hipStream_t s);
-hipError_t launch_epilogue(const Params &p, hipStream_t s);
+// t0, t1: optional events stamped at the kernel's start and end (may be null).
+hipError_t launch_stats(const Params &p, hipStream_t s, hipEvent_t t0, hipEvent_t t1);
+hipError_t launch_epilogue(const Params &p, hipStream_t s, hipEvent_t t0, hipEvent_t t1);
 hipError_t launch_resid(const Params &p, hipStream_t s);
 hipError_t launch_dbg_probs(const Params &p, hipStream_t s);
 hipError_t launch_post_update(const PostParams &p, hipStream_t s);

@@ -1239,14 +1239,21 @@ hipError_t launch_topk(const Params &p, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_stats(const Params &p, hipStream_t s) {
+// Launch with optional timing events: hipExtLaunchKernel stamps them from the
+// dispatch packet itself, so their interval is the kernel's execution time.
+hipError_t launch_timed(const void *fn, dim3 grid, const Params &p, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+  Params arg = p;
+  void *args[] = {&arg};
+  return hipExtLaunchKernel(fn, grid, dim3(kThreads), args, 0, s, t0, t1, 0);
+}
+
+hipError_t launch_stats(const Params &p, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
   const dim3 grid((unsigned)p.stats_grid);
-  if (p.fast)
-    p.dtype == 1 ? stats_fast_kernel<1><<<grid, dim3(kThreads), 0, s>>>(p)
-                 : stats_fast_kernel<0><<<grid, dim3(kThreads), 0, s>>>(p);
-  else
-    p.dtype == 1 ? stats_kernel<1><<<grid, dim3(kThreads), 0, s>>>(p) : stats_kernel<0><<<grid, dim3(kThreads), 0, s>>>(p);
-  return hipGetLastError();
+  const void *fn = p.fast ? (p.dtype == 1 ? reinterpret_cast<const void *>(&stats_fast_kernel<1>)
+                                          : reinterpret_cast<const void *>(&stats_fast_kernel<0>))
+                          : (p.dtype == 1 ? reinterpret_cast<const void *>(&stats_kernel<1>)
+                                          : reinterpret_cast<const void *>(&stats_kernel<0>));
+  return launch_timed(fn, grid, p, s, t0, t1);
 }
 
 int stats_blocks_per_cu(int dtype, bool fast) {
@@ -1261,9 +1268,8 @@ int stats_blocks_per_cu(int dtype, bool fast) {
   return e == hipSuccess && n > 0 ? n : 1;
 }
 
-hipError_t launch_epilogue(const Params &p, hipStream_t s) {
-  epilogue_kernel<<<dim3((unsigned)p.B), dim3(kThreads), 0, s>>>(p);
-  return hipGetLastError();
+hipError_t launch_epilogue(const Params &p, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+  return launch_timed(reinterpret_cast<const void *>(&epilogue_kernel), dim3((unsigned)p.B), p, s, t0, t1);
 }
 
 hipError_t launch_resid(const Params &p, hipStream_t s) {

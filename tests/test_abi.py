@@ -30,6 +30,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     names = declared_functions()
     assert names == sorted(["spec_post_update", "spec_verify_create", "spec_verify_destroy",
+                            "spec_verify_profile_read", "spec_verify_profile_start",
                             "spec_verify_read_error", "spec_verify_run", "spec_verify_strerror"])
     L = ctypes.CDLL(sv.library_path())
     for n in names:
@@ -106,6 +107,10 @@ def test_strerror_and_host_checks_without_gpu():
     pa.tokens_stride = 0
     assert L.spec_post_update(fake, ctypes.byref(pa), None) == sv.SV_EINVAL
     assert L.spec_verify_read_error(None, None, None) == sv.SV_EINVAL
+    assert L.spec_verify_profile_start(None, 4) == sv.SV_EINVAL
+    assert L.spec_verify_profile_start(fake, 0) == sv.SV_EINVAL
+    n = ctypes.c_int32(7)
+    assert L.spec_verify_profile_read(None, None, None, ctypes.byref(n)) == sv.SV_EINVAL
     L.spec_verify_destroy(None)
 
 
