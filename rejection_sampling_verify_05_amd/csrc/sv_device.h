@@ -46,15 +46,37 @@ __device__ __forceinline__ uint32_t pick(uint4 w, int k) {
 __device__ __forceinline__ double u_accept(uint32_t w) { return (double)((w >> 8) + 1u) * 0x1p-24; }
 
 // Exp(1) noise E = -ln U from the race uniform U = (w>>8) 2^-24 in [0,1);
-// U = 0 gives +inf.  For U >= 1/2, E = -log1p(-(1 - U)) with 1 - U exact, so
-// small E (the likely race winners) keep full relative precision; for
-// U < 1/2, |ln U| >= ln 2 and logf is well conditioned.  Both library
-// functions are accurate to about one ulp.
+// U = 0 gives +inf.  Short straight-line code (it runs once per raced chunk
+// and token, in unrolled loops):
+//  - U < 1/2: E = -ln2 log2(U) with the hardware log2 (U is exact in fp32 and
+//    |log2 U| >= 1, so about one ulp relative);
+//  - U >= 1/2: with v = 1 - U (exact) and y = v / (2 - v) <= 1/3,
+//    E = -ln(1 - v) = ln((1 + y)/(1 - y)) = 2 (y + y^3/3 + ... + y^15/15),
+//    so small E (the likely race winners) keep full relative precision.
+// The relative error is below 4e-7 over the whole grid; race scores are
+// compared in fp32, so decisions can differ from exact arithmetic only where
+// two scores are within a few 1e-7 of each other.
 __device__ __forceinline__ float exp_noise(uint32_t w) {
   const uint32_t k = w >> 8;
-  if (k == 0) return __builtin_inff();
-  if (k >= (1u << 23)) return -log1pf(-(float)((1u << 24) - k) * 0x1p-24f);
-  return -logf((float)k * 0x1p-24f);
+  const float lg = -0.69314718055994531f * __builtin_amdgcn_logf((float)k * 0x1p-24f);
+  const float v = (float)((1u << 24) - k) * 0x1p-24f;
+  const float y = v * __builtin_amdgcn_rcpf(2.0f - v);
+  const float y2 = y * y;
+  float t = 1.0f / 15.0f;
+  t = __builtin_fmaf(t, y2, 1.0f / 13.0f);
+  t = __builtin_fmaf(t, y2, 1.0f / 11.0f);
+  t = __builtin_fmaf(t, y2, 1.0f / 9.0f);
+  t = __builtin_fmaf(t, y2, 1.0f / 7.0f);
+  t = __builtin_fmaf(t, y2, 1.0f / 5.0f);
+  t = __builtin_fmaf(t, y2, 1.0f / 3.0f);
+  t = __builtin_fmaf(t, y2, 1.0f);
+  const float E = k < (1u << 23) ? lg : 2.0f * y * t;  // both computed: no divergent branch
+  return k == 0 ? __builtin_inff() : E;
+}
+
+// Race score w / E for the word w of a race position (0 when U = 0).
+__device__ __forceinline__ float race_score(float weight, uint32_t w) {
+  return weight * __builtin_amdgcn_rcpf(exp_noise(w));
 }
 
 // ---------------------------------------------------------------------------

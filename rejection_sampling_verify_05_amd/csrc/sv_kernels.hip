@@ -181,7 +181,7 @@ struct Layout<0> {
 // ---------------------------------------------------------------------------
 // Races.  RACE(w, g): chunk c* = argmax_c M_c / E(g, 1, c) over chunks with
 // M_c > 0, then token x* = argmax_{x in c*} w_x / E(g, 2, x) over w_x > 0.
-// Scores are compared in fp64; ties go to the lowest index.
+// Scores are fp32 (race_score); ties go to the lowest index.
 // ---------------------------------------------------------------------------
 constexpr int kTabCache = 2048;  // chunk-table entries the epilogue keeps in LDS
 
@@ -199,6 +199,11 @@ struct EpiShared {
   int j;
   int bad;
   int flag;
+  float zc[kWaves][kChunk];  // speculative chunks of rows 0..3 (raw logits, token order)
+  float zx[kWaves][kChunk];  // the draft tokens' chunks of rows 0..3
+  float w1s[kWaves];         // best chunk other than the draft token's: score
+  int w1c[kWaves];           //   and index (-1: none)
+  int cd[kWaves];            // the draft token's chunk when excluded, else -1
   union {
     float2 tab[kTabCache];  // dense rows: chunk tables of the request's rows
     struct {
@@ -217,7 +222,7 @@ __device__ __forceinline__ int block_chunk_race(const Params &p, uint32_t g, int
     const float Wc = W(c);
     if (Wc > 0.0f) {
       const uint4 w4 = rng_block(p, (uint32_t)c >> 2, g, kTagChunk);
-      ArgMax o{Wc / exp_noise(pick(w4, c & 3)), c};
+      ArgMax o{race_score(Wc, pick(w4, c & 3)), c};
       if (better(o, best)) best = o;
     }
   }
@@ -241,7 +246,7 @@ __device__ __forceinline__ int compact_race(const Params &p, uint32_t g, int n, 
     for (int t = i; t < n && ci[t] / kChunk == c; ++t) M += cw[t];
     if (M > 0.0f) {
       const uint4 w4 = rng_block(p, (uint32_t)c >> 2, g, kTagChunk);
-      ArgMax o{M / exp_noise(pick(w4, c & 3)), c};
+      ArgMax o{race_score(M, pick(w4, c & 3)), c};
       if (better(o, best)) best = o;
     }
   }
@@ -253,7 +258,7 @@ __device__ __forceinline__ int compact_race(const Params &p, uint32_t g, int n, 
     const int x = ci[i];
     if (x / kChunk != cstar || !(cw[i] > 0.0f)) continue;
     const uint4 w4 = rng_block(p, (uint32_t)x >> 2, g, kTagToken);
-    ArgMax o{cw[i] / exp_noise(pick(w4, x & 3)), x};
+    ArgMax o{race_score(cw[i], pick(w4, x & 3)), x};
     if (better(o, tb)) tb = o;
   }
   const ArgMax b = block_argmax(tb, sh.red);
@@ -271,11 +276,231 @@ __device__ __forceinline__ void write_empty(const Params &p, int r) {
 // ---------------------------------------------------------------------------
 // Request epilogue: one workgroup per request, after the streaming pass.
 //
-// Round trips: the request's cu entries and temperature; the chunk tables and
-// the draft ids; the logits of each draft token's chunk (z_d, q(d) and the
-// chunk mass without d); the logits of the winning chunk.  Everything else is
-// arithmetic on those values and on the Philox stream.
+// Round trips: (1) the request's cu entries and temperature; (2) the chunk
+// tables and the draft ids; (3) for each of the first four rows, speculatively,
+// the logits of the chunks its race could need: the chunk that wins the race
+// among the chunks without the draft token, and the draft token's own chunk
+// (z_d, and the chunk mass without d), plus single loads of z_d and q(d) for the
+// other rows.  The speculative chunks go to LDS; the accept tests then pick
+// the row j to sample and the whole workgroup finishes its race from LDS.  A
+// rejected row past the fourth, or a bonus row past the fourth, takes one more
+// round trip; compact (top-k) rows race over their candidate lists.
 // ---------------------------------------------------------------------------
+
+// Chunk c of row g, 16 tokens per lane: lane l holds c C + 256 t + 4 l + k for
+// t, k < 4 (one Philox block per 4 tokens); positions past V read token V - 1.
+__device__ __forceinline__ int c16_tok(int c, int e, int lane) { return c * kChunk + (e >> 2) * 256 + 4 * lane + (e & 3); }
+// The dtype test stays outside the loads so that all 16 issue back to back.
+__device__ __forceinline__ void load_chunk16(const Params &p, int g, int c, float (&z)[16]) {
+  const int lane = threadIdx.x & 63;
+  if (p.dtype == 1) {
+    const uint16_t *row = static_cast<const uint16_t *>(p.logits) + (int64_t)g * p.lstride;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) z[e] = bf16_bits_to_f32(row[min(c16_tok(c, e, lane), p.V - 1)]);
+  } else {
+    const float *row = static_cast<const float *>(p.logits) + (int64_t)g * p.lstride;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) z[e] = row[min(c16_tok(c, e, lane), p.V - 1)];
+  }
+}
+
+// Wave-level chunk race of row g over its chunk table (W_c = s_c exp2(a (m_c - m))),
+// chunk `skip` left out.  Lane l draws the words of chunks 4l..4l+3.
+template <class EF>
+__device__ __forceinline__ ArgMax wave_chunk_race(const Params &p, int g, EF ent, float a, float m, int skip) {
+  const int lane = threadIdx.x & 63;
+  ArgMax best{-1.0f, 0x7FFFFFFF};
+  for (int c0 = 4 * lane; c0 < p.NC; c0 += 256) {
+    const uint4 w4 = rng_block(p, (uint32_t)c0 >> 2, (uint32_t)g, kTagChunk);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int c = c0 + k;
+      if (c < p.NC && c != skip) {
+        const float2 e = ent(c);
+        if (e.x > kNegInf) {
+          const float Wc = e.y * exp2_acc(a * (e.x - m));
+          if (Wc > 0.0f) {
+            ArgMax o{Wc / exp_noise(pick(w4, k)), c};
+            if (better(o, best)) best = o;
+          }
+        }
+      }
+    }
+  }
+  return wave_argmax(best);
+}
+
+// Token race over chunk c of row g whose raw logits are in LDS (zs, token
+// order): weights exp2(fma(z', a, -hi)) on the processed z' (hi = a m_c; a
+// factor common to the chunk cancels), token `skip` left out.  Thread t takes
+// tokens 4t..4t+3 (one Philox block).  All threads call it; -1 if no token has
+// weight.
+__device__ __forceinline__ int block_token_race(const Params &p, int g, int c, const float *zs, const Proc &pr,
+                                                float a, float hi, int skip, BlockScratch &red) {
+  const int t4 = 4 * threadIdx.x;
+  const int x0 = c * kChunk + t4;
+  const uint4 w4 = rng_block(p, (uint32_t)x0 >> 2, (uint32_t)g, kTagToken);
+  const float4 z4 = *reinterpret_cast<const float4 *>(zs + t4);
+  const float zz[4] = {z4.x, z4.y, z4.z, z4.w};
+  ArgMax best{-1.0f, 0x7FFFFFFF};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int x = x0 + k;
+    const bool ok = x < p.V && x != skip;
+    const float wx = ok ? exp2_acc(__builtin_fmaf(apply_proc(zz[k], min(x, p.V - 1), pr), a, -hi)) : 0.0f;
+    const ArgMax o{race_score(wx, pick(w4, k)), x};
+    if (wx > 0.0f && better(o, best)) best = o;
+  }
+  const ArgMax b = block_argmax(best, red);
+  return b.s < 0.0f ? -1 : b.i;
+}
+
+// Lowest token of chunk c (held in z) whose processed logit equals m; INT_MAX if none.
+__device__ __forceinline__ int wave_first_equal(const Params &p, int c, const float (&z)[16], const Proc &pr, float m) {
+  const int lane = threadIdx.x & 63;
+  int li = 0x7FFFFFFF;
+#pragma unroll
+  for (int e = 15; e >= 0; --e) {
+    const int x = c16_tok(c, e, lane);
+    if (x < p.V && apply_proc(z[e], x, pr) == m) li = x;
+  }
+  return wave_min_i(li);
+}
+
+// Speculative state of one row while its wave waits for the loads.
+struct RowSpec {
+  float zc[16];   // logits of chunk c1 (stochastic) or of the lowest max chunk (greedy)
+  float zx[16];   // logits of the draft token's chunk cd
+  ArgMax w1;      // best chunk other than cd: (score, c1); c1 = -1 if none
+  int cd;         // draft token's chunk when it is excluded, else -1
+};
+
+// Row statistics of row i from its chunk table (dense) or candidates (compact):
+// maximum m and Σ exp2(a (z - m)); greedy dense rows also get the lowest
+// chunk holding the maximum.  One wave; results uniform.
+template <class EF>
+__device__ __forceinline__ void row_stats(const Params &p, const Req &q, int g, int st, bool greedy, EF ent,
+                                          float &m, float &s, int &lc) {
+  const int lane = threadIdx.x & 63;
+  s = 0.0f;
+  lc = 0x7FFFFFFF;
+  if (st >= 0) {
+    const float *cv = p.cand_val + (int64_t)g * kCandCap;
+    float lm = kNegInf;
+    for (int t = lane; t < st; t += 64) lm = fmaxf(lm, cv[t]);
+    m = wave_max(lm);
+    float ls = 0.0f;
+    for (int t = lane; t < st; t += 64) ls += exp2_acc(q.a * (cv[t] - m));
+    s = wave_sum(ls);
+    return;
+  }
+  float lm = kNegInf;
+  for (int c = lane; c < p.NC; c += 64) lm = fmaxf(lm, ent(c).x);
+  m = wave_max(lm);
+  if (greedy) {
+    int l = 0x7FFFFFFF;
+    for (int c = lane; c < p.NC; c += 64)
+      if (ent(c).x == m) l = min(l, c);
+    lc = wave_min_i(l);
+  } else if (m > kNegInf) {
+    float ls = 0.0f;
+    for (int c = lane; c < p.NC; c += 64) {
+      const float2 e = ent(c);
+      if (e.x > kNegInf) ls += e.y * exp2_acc(q.a * (e.x - m));
+    }
+    s = wave_sum(ls);
+  }
+}
+
+// Speculative part for dense stochastic row i (no-draft-probs rows and bonus
+// rows): the chunk race without the draft token's chunk, then the loads of
+// the winning chunk and of the draft token's chunk.
+template <class EF>
+__device__ __forceinline__ void spec_issue(const Params &p, const Req &q, int i, int d, float m, EF ent, RowSpec &rs) {
+  const int g = q.g0 + i;
+  const bool excl = i < q.K && !p.draft_probs && d >= 0 && d < p.V;
+  rs.cd = excl ? d / kChunk : -1;
+  rs.w1 = wave_chunk_race(p, g, ent, q.a, m, rs.cd);
+  const int c1 = rs.w1.s < 0.0f ? -1 : rs.w1.i;
+  if (c1 >= 0) load_chunk16(p, g, c1, rs.zc);
+  if (excl) load_chunk16(p, g, rs.cd, rs.zx);
+}
+
+// After the loads of spec_issue: z_d and the mass of d's chunk without d, in
+// the chunk entry's scale (exp2(fma(z, a, -hi)) exp2(-lo), a m_c = hi + lo).
+__device__ __forceinline__ void spec_draft_record(const Params &p, const Req &q, int d, const Proc &pr,
+                                                  const RowSpec &rs, float &zd, float &sx) {
+  const int lane = threadIdx.x & 63;
+  float z[16];
+  float mx = kNegInf, zl = kNegInf;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int x = c16_tok(rs.cd, e, lane);
+    z[e] = x < p.V ? apply_proc(rs.zx[e], x, pr) : kNegInf;
+    mx = fmaxf(mx, z[e]);
+    if (x == d) zl = z[e];
+  }
+  const float mc = wave_max(mx);
+  const float a = q.a, hi = a * mc, lo = __builtin_fmaf(a, mc, -hi);
+  float acc = 0.0f;
+  if (mc > kNegInf) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      if (c16_tok(rs.cd, e, lane) != d) acc += exp2_acc(__builtin_fmaf(z[e], a, -hi));
+  }
+  sx = mc > kNegInf ? wave_sum(acc) * exp2_acc(-lo) : 0.0f;
+  zd = wave_max(zl);
+}
+
+// Moves a wave's speculative chunks and race state for row i to LDS slot `slot`.
+__device__ __forceinline__ void spec_publish(const RowSpec &rs, int slot, EpiShared &sh) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    *reinterpret_cast<float4 *>(&sh.zc[slot][t * 256 + 4 * lane]) =
+        make_float4(rs.zc[4 * t], rs.zc[4 * t + 1], rs.zc[4 * t + 2], rs.zc[4 * t + 3]);
+    *reinterpret_cast<float4 *>(&sh.zx[slot][t * 256 + 4 * lane]) =
+        make_float4(rs.zx[4 * t], rs.zx[4 * t + 1], rs.zx[4 * t + 2], rs.zx[4 * t + 3]);
+  }
+  if (lane == 0) {
+    sh.w1s[slot] = rs.w1.s;
+    sh.w1c[slot] = rs.w1.i;
+    sh.cd[slot] = rs.cd;
+  }
+}
+
+// Final race of row j from LDS slot `slot` (all threads): the chunk of d
+// competes with its mass without d (sx); if nothing is left without d, the race
+// is over p_j.
+template <class EF>
+__device__ __forceinline__ int spec_finish(const Params &p, const Req &q, int j, int dj, float m, float sx,
+                                           const Proc &pr, EF ent, int slot, EpiShared &sh) {
+  const int gs = q.g0 + j;
+  const float a = q.a;
+  ArgMax win{sh.w1s[slot], sh.w1c[slot]};
+  const int cd = sh.cd[slot];
+  bool excl = cd >= 0;
+  if (excl) {
+    const float2 e = ent(cd);
+    const uint32_t wd = pick(rng_block(p, (uint32_t)cd >> 2, (uint32_t)gs, kTagChunk), cd & 3);
+    const float Wd = e.x > kNegInf ? sx * exp2_acc(a * (e.x - m)) : 0.0f;
+    if (Wd > 0.0f) {
+      ArgMax o{race_score(Wd, wd), cd};
+      if (better(o, win)) win = o;
+    }
+    if (win.s < 0.0f) {  // nothing left once d_j is removed (rounding): race over p_j
+      excl = false;
+      const float Wf = e.x > kNegInf ? e.y * exp2_acc(a * (e.x - m)) : 0.0f;
+      if (Wf > 0.0f) win = ArgMax{race_score(Wf, wd), cd};
+    }
+  }
+  if (win.s < 0.0f) return -1;
+  const int cstar = win.i;
+  const float hi = a * ent(cstar).x;
+  const float *zs = cstar == cd ? sh.zx[slot] : sh.zc[slot];
+  return block_token_race(p, gs, cstar, zs, pr, a, hi, (excl && cstar == cd) ? dj : -1, sh.red);
+}
+
 __device__ __forceinline__ void request_epilogue(const Params &p, const Req &q, EpiShared &sh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K = q.K, r = q.r, nrow = K + 1;
@@ -292,13 +517,13 @@ __device__ __forceinline__ void request_epilogue(const Params &p, const Req &q, 
   }
   const bool greedy = q.mode == kModeGreedy;
 
-  // Row states (top-k pass results) and draft ids.
+  // Row states (top-k pass results), draft ids and the chunk tables.
   for (int i = tid; i < nrow; i += kThreads) {
     const int g = q.g0 + i;
     const int st = row_state(p, g);
     sh.state[i] = st;
     sh.tau[i] = (st == kRowDense) ? kNegInf : p.cand_tau[g];
-    if (i < K) sh.d[i] = p.draft_ids[q.c0 + i];
+    sh.d[i] = i < K ? p.draft_ids[q.c0 + i] : -1;
   }
   const bool cached = nrow * p.NC <= kTabCache;
   if (cached) {
@@ -308,101 +533,51 @@ __device__ __forceinline__ void request_epilogue(const Params &p, const Req &q, 
     }
   }
   __syncthreads();
-  // Draft records (stochastic dense rows): the processed z_d, q(d) and the sum
-  // of exp2(a (z - m_c)) over d's chunk without d, in the chunk entry's
-  // scale; one wave per draft row, 16 tokens per lane.
-  if (!greedy) {
-    for (int i = wave; i < K; i += kWaves) {
-      const int d = sh.d[i];
-      if (sh.state[i] >= 0 || d < 0 || d >= p.V) continue;
-      const int g = q.g0 + i, c = d / kChunk;
-      Proc pr = q.proc;
-      pr.tau = sh.tau[i];
-      float z[kChunk / 64];
-#pragma unroll
-      for (int t = 0; t < kChunk / 64; ++t) z[t] = load_logit(p, g, min(c * kChunk + t * 64 + lane, p.V - 1));
-      const float qd = p.draft_probs ? p.draft_probs[(int64_t)(q.c0 + i) * p.dstride + d] : 1.0f;
-      float mx = kNegInf;
-#pragma unroll
-      for (int t = 0; t < kChunk / 64; ++t) {
-        const int x = c * kChunk + t * 64 + lane;
-        z[t] = x < p.V ? apply_proc(z[t], x, pr) : kNegInf;
-        mx = fmaxf(mx, z[t]);
-      }
-      const float mc = wave_max(mx);
-      float sx = 0.0f, zl = kNegInf;
-      const float a = q.a;
-      const float hi = a * mc, lo = __builtin_fmaf(a, mc, -hi);
-#pragma unroll
-      for (int t = 0; t < kChunk / 64; ++t) {
-        if (c * kChunk + t * 64 + lane == d)
-          zl = z[t];
-        else if (mc > kNegInf)
-          sx += exp2_acc(__builtin_fmaf(z[t], a, -hi));
-      }
-      sx = mc > kNegInf ? wave_sum(sx) * exp2_acc(-lo) : 0.0f;
-      const float zd = wave_max(zl);
-      if (lane == 0) {
-        sh.zd[i] = zd;
-        sh.qd[i] = qd;
-        sh.sx[i] = sx;
-      }
-    }
-  }
   auto entry = [&](int i, int c) -> float2 {
     return cached ? sh.u.tab[i * p.NC + c] : p.chunk_tab[(int64_t)(q.g0 + i) * p.nc_stride + c];
   };
 
-  // Row statistics: one wave per row.
+  // Each wave takes rows wave, wave + 4, ...  Its first row gets the
+  // speculative loads; the others only what the accept tests need.
+  RowSpec rs;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) rs.zc[e] = rs.zx[e] = 0.0f;
+  rs.cd = -1;
+  rs.w1 = ArgMax{-1.0f, 0x7FFFFFFF};
   for (int i = wave; i < nrow; i += kWaves) {
     const int g = q.g0 + i;
     const int st = sh.state[i];
-    float m, s = 0.0f;
+    const int d = sh.d[i];
+    auto ent = [&](int c) { return entry(i, c); };
+    float m, s;
+    int lc;
+    row_stats(p, q, g, st, greedy, ent, m, s, lc);
+    Proc pr = q.proc;
+    pr.tau = sh.tau[i];
     int am = 0x7FFFFFFF;
-    if (st >= 0) {
-      const float *cv = p.cand_val + (int64_t)g * kCandCap;
-      float lm = kNegInf;
-      for (int t = lane; t < st; t += 64) lm = fmaxf(lm, cv[t]);
-      m = wave_max(lm);
-      float ls = 0.0f;
-      for (int t = lane; t < st; t += 64) ls += exp2_acc(q.a * (cv[t] - m));
-      s = wave_sum(ls);
-    } else {
-      float lm = kNegInf;
-      for (int c = lane; c < p.NC; c += 64) lm = fmaxf(lm, entry(i, c).x);
-      m = wave_max(lm);
-      if (greedy) {
-        // Lowest chunk holding the row maximum, then its lowest token equal to
-        // the maximum (the streaming pass keeps only chunk maxima for greedy rows).
-        int lc = 0x7FFFFFFF;
-        for (int c = lane; c < p.NC; c += 64)
-          if (entry(i, c).x == m) lc = min(lc, c);
-        lc = wave_min_i(lc);
-        Proc pr = q.proc;
-        pr.tau = sh.tau[i];
-        float zz[kChunk / 64];
-#pragma unroll
-        for (int t = 0; t < kChunk / 64; ++t) zz[t] = load_logit(p, g, min(lc * kChunk + t * 64 + lane, p.V - 1));
-        int li = 0x7FFFFFFF;
-#pragma unroll
-        for (int t = kChunk / 64 - 1; t >= 0; --t) {
-          const int x = lc * kChunk + t * 64 + lane;
-          if (x < p.V && apply_proc(zz[t], x, pr) == m) li = x;
-        }
-        am = wave_min_i(li);
-      } else if (m > kNegInf) {
-        float ls = 0.0f;
-        for (int c = lane; c < p.NC; c += 64) {
-          const float2 e = entry(i, c);
-          if (e.x > kNegInf) ls += e.y * exp2_acc(q.a * (e.x - m));
-        }
-        s = wave_sum(ls);
+    float zd = kNegInf, qd = 1.0f, sx = 0.0f;
+    const bool valid_d = i < K && d >= 0 && d < p.V;
+    if (st < 0 && greedy) {
+      if (lc < p.NC) {
+        load_chunk16(p, g, lc, rs.zc);
+        am = wave_first_equal(p, lc, rs.zc, pr, m);
       }
+    } else if (st < 0 && i == wave && (!p.draft_probs || i == K)) {
+      spec_issue(p, q, i, d, m, ent, rs);
+      if (rs.cd >= 0) spec_draft_record(p, q, d, pr, rs, zd, sx);
+      spec_publish(rs, i, sh);
+    } else if (valid_d) {
+      // single loads: z_d (and q(d)) for the accept test
+      zd = apply_proc(load_logit(p, g, d), d, pr);
+      if (p.draft_probs) qd = p.draft_probs[(int64_t)(q.c0 + i) * p.dstride + d];
     }
     if (lane == 0) {
       sh.m[i] = m;
       sh.s[i] = s;
       sh.amax[i] = am;
+      sh.zd[i] = zd;
+      sh.qd[i] = qd;
+      sh.sx[i] = sx;
       p.row_info[g] = make_float4(m, s, __int_as_float(am), __int_as_float(st));
     }
   }
@@ -411,12 +586,6 @@ __device__ __forceinline__ void request_epilogue(const Params &p, const Req &q, 
     int bad = 0;
     for (int i = 0; i < nrow; ++i) bad |= !__builtin_isfinite(sh.m[i]);
     sh.bad = bad;
-  }
-  __syncthreads();
-  if (sh.bad) {
-    if (tid == 0) raise_err(p, SV_ERR_ROW);
-    write_empty(p, r);
-    return;
   }
 
   // Accept tests: lane i of wave 0 takes draft position i.
@@ -431,21 +600,10 @@ __device__ __forceinline__ void request_epilogue(const Params &p, const Req &q, 
       } else {
         const bool valid = d >= 0 && d < p.V;
         float pd = 0.0f;
-        double qd = 1.0;
+        double qd = p.draft_probs ? 0.0 : 1.0;
         if (valid) {
-          float z;
-          if (sh.state[lane] >= 0) {  // compact row: not streamed, read z_d and q_d here
-            Proc pr = q.proc;
-            pr.tau = sh.tau[lane];
-            z = apply_proc(load_logit(p, g, d), d, pr);
-            if (p.draft_probs) qd = (double)p.draft_probs[(int64_t)(q.c0 + lane) * p.dstride + d];
-          } else {
-            z = sh.zd[lane];
-            if (p.draft_probs) qd = (double)sh.qd[lane];
-          }
-          pd = exp2_acc(q.a * (z - sh.m[lane])) / sh.s[lane];
-        } else if (p.draft_probs) {
-          qd = 0.0;
+          pd = exp2_acc(q.a * (sh.zd[lane] - sh.m[lane])) / sh.s[lane];
+          if (p.draft_probs) qd = (double)sh.qd[lane];
         }
         const double u = u_accept(rng_block(p, 0, (uint32_t)g, kTagAccept).x);
         rej = !(valid && qd > 0.0 && (double)pd >= u * qd);
@@ -456,6 +614,11 @@ __device__ __forceinline__ void request_epilogue(const Params &p, const Req &q, 
     if (lane == 0) sh.j = mask ? (__ffsll((long long)mask) - 1) : K;
   }
   __syncthreads();
+  if (sh.bad) {
+    if (tid == 0) raise_err(p, SV_ERR_ROW);
+    write_empty(p, r);
+    return;
+  }
   const int j = sh.j;
 
   // Accepted prefix, padding and counts.
@@ -520,48 +683,23 @@ __device__ __forceinline__ void request_epilogue(const Params &p, const Req &q, 
   }
 
   // Dense race over p_j (bonus row, or the rejected row with d_j removed).
-  // Chunk weights come from the chunk table, W_c = s_c exp2(a (m_c - m)), with
-  // the chunk of d_j replaced by its sum without d_j; wave 0 runs the chunk
-  // race.  Token weights inside the winning chunk use the streaming pass's
-  // per-element formula exp2(fma(z, a, -a m_c)) (a common factor per chunk
-  // cancels in the token race), so a chunk with positive weight always has a
-  // token with one; the 4 waves run the token race, 4 tokens per thread.
-  bool excl = rejected && dj >= 0 && dj < p.V;
-  const int cd = excl ? dj / kChunk : -1;
-  const float sxj = excl ? sh.sx[j] : 0.0f;
-  auto chunk_w = [&](int c) -> float {
-    const float2 e = entry(j, c);
-    if (!(e.x > kNegInf)) return 0.0f;
-    return ((excl && c == cd) ? sxj : e.y) * exp2_acc(a * (e.x - m));
-  };
-  int cstar = block_chunk_race(p, (uint32_t)gs, p.NC, chunk_w, sh.red);
-  if (cstar < 0 && excl) {  // nothing left once d_j is removed (rounding): race over p_j
-    excl = false;
-    cstar = block_chunk_race(p, (uint32_t)gs, p.NC, chunk_w, sh.red);
-  }
-  int x = -1;
-  if (cstar >= 0) {
-    const float hi = a * entry(j, cstar).x;
-    const int x0 = cstar * kChunk + 4 * tid;
-    float z[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) z[k] = load_logit(p, gs, min(x0 + k, p.V - 1));  // all loads first
-    const uint4 w4 = rng_block(p, (uint32_t)x0 >> 2, (uint32_t)gs, kTagToken);
-    ArgMax best{-1.0f, 0x7FFFFFFF};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int xx = x0 + k;
-      if (xx < p.V && !(excl && xx == dj)) {
-        const float wx = exp2_acc(__builtin_fmaf(apply_proc(z[k], xx, pr), a, -hi));
-        if (wx > 0.0f) {
-          ArgMax o{wx / exp_noise(pick(w4, k)), xx};
-          if (better(o, best)) best = o;
-        }
-      }
+  auto entj = [&](int c) { return entry(j, c); };
+  int slot = j;
+  float sxj = sh.sx[j];
+  if (j >= kWaves) {  // no speculative state for this row: same steps, loads now
+    if (wave == 0) {
+      spec_issue(p, q, j, dj, m, entj, rs);
+      float zd = kNegInf;
+      sxj = 0.0f;
+      if (rs.cd >= 0) spec_draft_record(p, q, dj, pr, rs, zd, sxj);
+      spec_publish(rs, 0, sh);
+      if (lane == 0) sh.sx[j] = sxj;
     }
-    const ArgMax bb = block_argmax(best, sh.red);
-    x = bb.s < 0.0f ? -1 : bb.i;
+    __syncthreads();
+    slot = 0;
+    sxj = sh.sx[j];
   }
+  const int x = spec_finish(p, q, j, dj, m, sxj, pr, entj, slot, sh);
   if (tid == 0) p.out_tokens[out_j] = x;
 }
 
@@ -955,7 +1093,7 @@ __global__ __launch_bounds__(kThreads) void resid_race_kernel(Params p) {
         const float px = exp2_acc(a * (apply_proc(z[k], xx, pr) - m)) * inv_s;
         const float wx = fallback ? px : fmaxf(px - qx[k], 0.0f);
         if (wx > 0.0f) {
-          ArgMax o{wx / exp_noise(pick(w4, k)), xx};
+          ArgMax o{race_score(wx, pick(w4, k)), xx};
           if (better(o, best)) best = o;
         }
       }
