@@ -1344,24 +1344,31 @@ __global__ __launch_bounds__(kThreads) void dbg_kernel(Params p) {
 // ---------------------------------------------------------------------------
 // post_update ("【vllm】DeepSeekMTP、eagle", _post_update_kernel walk-through).
 // ---------------------------------------------------------------------------
+// One thread per (request, output slot): every load is issued at once (indices
+// clamped into range), the histogram updates are fire-and-forget atomics, and
+// the thread holding the last sampled token also writes last_sampled and
+// advances num_computed.
 __global__ __launch_bounds__(kThreads) void post_update_kernel(PostParams p) {
-  const int r = blockIdx.x * kThreads + threadIdx.x;
-  if (r >= p.B) return;
-  int n = p.num_sampled[r];
-  if (n <= 0) return;
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t total = (int64_t)p.B * p.tokens_stride;
+  if (i >= total) return;
+  const int r = (int)(i / p.tokens_stride), t = (int)(i - (int64_t)r * p.tokens_stride);
+  const int n = p.num_sampled[r];
   const int s = p.idx_mapping[r];
+  const int tok = p.tokens[i];
+  const int ql = p.query_len[r];
+  const int nr = p.num_rejected[r];
+  const int nn = min(n, p.tokens_stride);
+  if (nn <= 0 || t >= nn) return;
   if (s < 0 || s >= p.num_slots) {
-    atomicOr(p.err, SV_ERR_SLOT);
+    if (t == 0) atomicOr(p.err, SV_ERR_SLOT);
     return;
   }
-  n = min(n, p.tokens_stride);
-  const int32_t *tok = p.tokens + (int64_t)r * p.tokens_stride;
-  for (int i = 0; i < n; ++i) {
-    const int t = tok[i];
-    if (t >= 0 && t < p.V) atomicAdd(&p.counts[(int64_t)s * p.V + t], 1);
+  if (tok >= 0 && tok < p.V) atomicAdd(&p.counts[(int64_t)s * p.V + tok], 1);
+  if (t == nn - 1) {
+    p.last_sampled[s] = tok;
+    atomicAdd(&p.num_computed[s], ql - nr);
   }
-  p.last_sampled[s] = tok[n - 1];
-  atomicAdd(&p.num_computed[s], p.query_len[r] - p.num_rejected[r]);
 }
 
 }  // namespace
@@ -1428,7 +1435,8 @@ hipError_t launch_dbg_probs(const Params &p, hipStream_t s) {
 }
 
 hipError_t launch_post_update(const PostParams &p, hipStream_t s) {
-  post_update_kernel<<<dim3((unsigned)((p.B + kThreads - 1) / kThreads)), dim3(kThreads), 0, s>>>(p);
+  const int64_t total = (int64_t)p.B * p.tokens_stride;
+  post_update_kernel<<<dim3((unsigned)((total + kThreads - 1) / kThreads)), dim3(kThreads), 0, s>>>(p);
   return hipGetLastError();
 }
 

@@ -1,0 +1,97 @@
+"""post_update through the C ABI against the oracle's post_update (bit-exact):
+last_sampled, the output-token histogram and num_computed, on verify outputs
+of the workloads and on hand-made edge cases (skipped requests, tokens outside
+the vocabulary, slots out of range, two updates in a row)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import rejection_sampling_verify_05_amd as sv
+import workloads as wl
+from harness import ctx_for, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def gpu_post_update(ctx, idx, ql, toks, ns, nr, last, counts, ncomp):
+    """Runs spec_post_update on device copies; returns host (last, counts, ncomp, err)."""
+    d = {k: torch.from_numpy(np.ascontiguousarray(v)).to(DEV) for k, v in
+         dict(idx=idx, ql=ql, toks=toks, ns=ns, nr=nr, last=last, counts=counts, ncomp=ncomp).items()}
+    sv.spec_post_update(ctx.h, d["idx"], d["ql"], d["toks"], d["ns"], d["nr"], d["last"], d["counts"], d["ncomp"])
+    err = sv.spec_verify_read_error(ctx.h)
+    return d["last"].cpu().numpy(), d["counts"].cpu().numpy(), d["ncomp"].cpu().numpy(), err
+
+
+def oracle_post_update(idx, ql, toks, ns, nr, last, counts, ncomp):
+    last, counts, ncomp = last.copy(), counts.copy(), ncomp.copy()
+    err = oracle.post_update(idx, ql, toks, ns, nr, last, counts, ncomp)
+    return last, counts, ncomp, err
+
+
+@pytest.mark.parametrize("cid", ["1", "2", "3"])
+def test_post_update_on_verify_outputs(cid):
+    w = wl.CONFIGS[cid]
+    inp = wl.make_inputs(w, DEV)
+    say(f"config {cid}: B={inp['B']} V={inp['V']}")
+    with ctx_for(inp) as ctx:
+        g = run_gpu(ctx, inp, seed=3, offset=5)
+        assert g["err"] == 0
+        S, V = inp["num_slots"], inp["V"]
+        rng = np.random.default_rng(7)
+        last = rng.integers(-1, V, S).astype(np.int32)
+        ncomp = rng.integers(0, 1000, S).astype(np.int32)
+        counts = inp["counts"].cpu().numpy().copy()
+        counts[rng.integers(0, S, 64), rng.integers(0, V, 64)] += 3
+        idx = inp["idx_mapping"].cpu().numpy()
+        ql = inp["query_len"].cpu().numpy()
+        args = (idx, ql, g["tokens"], g["num_sampled"], g["num_rejected"], last, counts, ncomp)
+        got = gpu_post_update(ctx, *args)
+        want = oracle_post_update(*args)
+    assert got[3] == 0 and want[3] == 0
+    assert np.array_equal(got[0], want[0])
+    assert np.array_equal(got[2], want[2])
+    assert np.array_equal(got[1], want[1])
+
+
+def test_post_update_edge_cases_and_repeats():
+    B, V, S, stride = 9, 50, 12, 4
+    rng = np.random.default_rng(11)
+    idx = rng.permutation(S)[:B].astype(np.int32)
+    ql = rng.integers(1, 5, B).astype(np.int32)
+    ns = np.array([1, 4, 0, 2, 3, 4, 1, 2, 3], np.int32)           # request 2 sampled nothing
+    nr = np.maximum(ql - ns, 0).astype(np.int32)
+    toks = rng.integers(0, V, (B, stride)).astype(np.int32)
+    toks[1, 1] = -1                                                   # outside the vocabulary: not counted
+    toks[4, 0] = V + 3
+    toks[toks < -1] = -1
+    for r in range(B):
+        toks[r, ns[r]:] = -1
+    last = np.full(S, -5, np.int32)
+    counts = rng.integers(0, 3, (S, V)).astype(np.int32)
+    ncomp = np.zeros(S, np.int32)
+    inp = wl.make_inputs(wl.CONFIGS["1"], DEV)
+    with ctx_for(inp) as ctx:
+        state_g = (last, counts, ncomp)
+        state_o = (last, counts, ncomp)
+        for rep in range(2):  # two updates in a row accumulate
+            g = gpu_post_update(ctx, idx, ql, toks, ns, nr, *state_g)
+            o = oracle_post_update(idx, ql, toks, ns, nr, *state_o)
+            assert g[3] == 0 and o[3] == 0
+            for a, b in zip(g[:3], o[:3]):
+                assert np.array_equal(a, b), f"repeat {rep}"
+            state_g, state_o = g[:3], o[:3]
+        # a slot outside [0, S): that request is skipped and the error bit is set
+        bad = idx.copy()
+        bad[3] = S + 2
+        g = gpu_post_update(ctx, bad, ql, toks, ns, nr, *state_g)
+        o = oracle_post_update(bad, ql, toks, ns, nr, *state_o)
+        assert g[3] == sv.SV_ERR_SLOT and o[3] != 0
+        for a, b in zip(g[:3], o[:3]):
+            assert np.array_equal(a, b)
