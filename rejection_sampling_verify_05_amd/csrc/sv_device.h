@@ -81,47 +81,59 @@ __device__ __forceinline__ float race_score(float weight, uint32_t w) {
 
 // ---------------------------------------------------------------------------
 // wave64 reductions.  Within a 16-lane row: quad_perm swaps and the two
-// mirrors leave the row total in every lane; the four row totals are then
-// combined through readlane (uniform result).
+// mirrors leave the row total in every lane; row_bcast:15 then folds rows 0
+// and 2 into rows 1 and 3, row_bcast:31 folds row 1 into row 3, and lane 63
+// holds the wave total (read out once: uniform result).  Maxima are taken on
+// order-preserving integer keys of the floats, so each step is one integer
+// max with its DPP operand (a float max would first canonicalise it).
 // ---------------------------------------------------------------------------
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ float dpp_f(float v, float old = 0.0f) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old), __builtin_bit_cast(int, v),
+                                                               CTRL, ROWS, 0xF, false));
 }
-template <int CTRL>
-__device__ __forceinline__ int dpp_i(int v) {
-  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ int dpp_i(int v, int old = 0) {
+  return __builtin_amdgcn_update_dpp(old, v, CTRL, ROWS, 0xF, false);
 }
 constexpr int kQuad1032 = 0xB1, kQuad2301 = 0x4E, kHalfMirror = 0x141, kMirror = 0x140;
+constexpr int kBcast15 = 0x142, kBcast31 = 0x143;
 
 __device__ __forceinline__ float rd(float v, int lane) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-  v = fmaxf(v, dpp_f<kQuad1032>(v));
-  v = fmaxf(v, dpp_f<kQuad2301>(v));
-  v = fmaxf(v, dpp_f<kHalfMirror>(v));
-  v = fmaxf(v, dpp_f<kMirror>(v));
-  return fmaxf(fmaxf(rd(v, 0), rd(v, 16)), fmaxf(rd(v, 32), rd(v, 48)));
+// Order-preserving map float -> int32 (its own inverse): negative floats get
+// their magnitude bits flipped.
+__device__ __forceinline__ int fkey(float f) {
+  const int b = __builtin_bit_cast(int, f);
+  return b ^ ((b >> 31) & 0x7FFFFFFF);
 }
+__device__ __forceinline__ float fkey_inv(int k) { return __builtin_bit_cast(float, k ^ ((k >> 31) & 0x7FFFFFFF)); }
+
+__device__ __forceinline__ int wave_max_i(int v) {
+  v = max(v, dpp_i<kQuad1032>(v));
+  v = max(v, dpp_i<kQuad2301>(v));
+  v = max(v, dpp_i<kHalfMirror>(v));
+  v = max(v, dpp_i<kMirror>(v));
+  v = max(v, dpp_i<kBcast15, 0xA>(v, (int)0x80000000));
+  v = max(v, dpp_i<kBcast31, 0xC>(v, (int)0x80000000));
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
+__device__ __forceinline__ float wave_max(float v) { return fkey_inv(wave_max_i(fkey(v))); }
 
 __device__ __forceinline__ float wave_sum(float v) {
   v += dpp_f<kQuad1032>(v);
   v += dpp_f<kQuad2301>(v);
   v += dpp_f<kHalfMirror>(v);
   v += dpp_f<kMirror>(v);
-  return (rd(v, 0) + rd(v, 16)) + (rd(v, 32) + rd(v, 48));
+  v += dpp_f<kBcast15, 0xA>(v);
+  v += dpp_f<kBcast31, 0xC>(v);
+  return rd(v, 63);
 }
 
-__device__ __forceinline__ int wave_min_i(int v) {
-  v = min(v, dpp_i<kQuad1032>(v));
-  v = min(v, dpp_i<kQuad2301>(v));
-  v = min(v, dpp_i<kHalfMirror>(v));
-  v = min(v, dpp_i<kMirror>(v));
-  return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
-             min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
-}
+__device__ __forceinline__ int wave_min_i(int v) { return -wave_max_i(-v); }
 
 // (score, index) arg-max with the lowest index winning ties; non-candidates
 // carry score -1 (real scores are >= 0).
@@ -131,24 +143,21 @@ struct ArgMax {
 };
 __device__ __forceinline__ bool better(ArgMax a, ArgMax b) { return a.s > b.s || (a.s == b.s && a.i < b.i); }
 
-template <int CTRL>
+template <int CTRL, int ROWS = 0xF>
 __device__ __forceinline__ ArgMax argmax_dpp(ArgMax a) {
-  ArgMax o{dpp_f<CTRL>(a.s), dpp_i<CTRL>(a.i)};
+  // rows outside ROWS read back their own pair (the DPP "old" operand)
+  ArgMax o{dpp_f<CTRL, ROWS>(a.s, a.s), dpp_i<CTRL, ROWS>(a.i, a.i)};
   return better(o, a) ? o : a;
 }
-// Wave-wide arg-max with DPP row steps; uniform result.
+// Wave-wide arg-max with the same DPP steps as the reductions; uniform result.
 __device__ __forceinline__ ArgMax wave_argmax(ArgMax a) {
   a = argmax_dpp<kQuad1032>(a);
   a = argmax_dpp<kQuad2301>(a);
   a = argmax_dpp<kHalfMirror>(a);
   a = argmax_dpp<kMirror>(a);
-  ArgMax b{rd(a.s, 0), __builtin_amdgcn_readlane(a.i, 0)};
-#pragma unroll
-  for (int row = 16; row < 64; row += 16) {
-    ArgMax o{rd(a.s, row), __builtin_amdgcn_readlane(a.i, row)};
-    if (better(o, b)) b = o;
-  }
-  return b;
+  a = argmax_dpp<kBcast15, 0xA>(a);
+  a = argmax_dpp<kBcast31, 0xC>(a);
+  return ArgMax{rd(a.s, 63), __builtin_amdgcn_readlane(a.i, 63)};
 }
 
 // ---------------------------------------------------------------------------
