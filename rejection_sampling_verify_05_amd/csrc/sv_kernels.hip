@@ -844,32 +844,44 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(Params p) {
   const int g_first = (int)(start / p.NC), g_last = (int)((end - 1) / p.NC);
   const int nrows = g_last - g_first + 1;
 
-  // Three chunks in flight per wave before anything else.
-  u32x4 A[NV], Bv[NV], Cv[NV];
-  int64_t f = start + wave;
-  issue_chunk<DT>(p, f, end, A);
-  issue_chunk<DT>(p, f + kWaves, end, Bv);
-  issue_chunk<DT>(p, f + 2 * kWaves, end, Cv);
-
-  // Request lookups for the first rows of the slice (overlapping the loads).
+  // Request lookups for the slice's rows first: rows that are not streamed
+  // (invalid requests, compact top-k rows raced over their candidate lists)
+  // issue no loads at all.
   if (wave < min(nrows, kRowCache)) {
     const int g = g_first + wave;
     const RowInfo ri = row_info_of(p, lookup_req(p, g), g);
     if (lane == 0) sh.rows[wave] = ri;
   }
   __syncthreads();
+  auto streamed = [&](int64_t ff) {
+    if (ff >= end) return false;
+    const int gi = (int)(ff / p.NC) - g_first;
+    return gi >= kRowCache || (sh.rows[gi].mode != kModeInvalid && sh.rows[gi].st < 0);
+  };
+  {
+    bool any = false;
+    for (int i = 0; i < min(nrows, kRowCache); ++i) any |= sh.rows[i].mode != kModeInvalid && sh.rows[i].st < 0;
+    if (!any && nrows <= kRowCache) return;
+  }
+
+  // Three chunks in flight per wave.
+  u32x4 A[NV], Bv[NV], Cv[NV];
+  int64_t f = start + wave;
+  issue_chunk<DT>(p, f, streamed(f) ? end : f, A);
+  issue_chunk<DT>(p, f + kWaves, streamed(f + kWaves) ? end : f, Bv);
+  issue_chunk<DT>(p, f + 2 * kWaves, streamed(f + 2 * kWaves) ? end : f, Cv);
 
   RowInfo cur;
   cur.g = -1;
   for (; f < end; f += 3 * kWaves) {
     process_chunk<DT>(p, f, A, cur, sh.rows, g_first);
-    issue_chunk<DT>(p, f + 3 * kWaves, end, A);
+    issue_chunk<DT>(p, f + 3 * kWaves, streamed(f + 3 * kWaves) ? end : f, A);
     if (f + kWaves >= end) break;
     process_chunk<DT>(p, f + kWaves, Bv, cur, sh.rows, g_first);
-    issue_chunk<DT>(p, f + 4 * kWaves, end, Bv);
+    issue_chunk<DT>(p, f + 4 * kWaves, streamed(f + 4 * kWaves) ? end : f, Bv);
     if (f + 2 * kWaves >= end) break;
     process_chunk<DT>(p, f + 2 * kWaves, Cv, cur, sh.rows, g_first);
-    issue_chunk<DT>(p, f + 5 * kWaves, end, Cv);
+    issue_chunk<DT>(p, f + 5 * kWaves, streamed(f + 5 * kWaves) ? end : f, Cv);
   }
 
 }
@@ -1114,39 +1126,97 @@ __global__ __launch_bounds__(kThreads) void epilogue_kernel(Params p) {
 // Top-k pass: one workgroup per row.
 // ---------------------------------------------------------------------------
 constexpr int kBuf = 2048;   // LDS candidate buffer
-constexpr int kTile = 1024;  // tokens appended per step at most
 
 struct TopkShared {
   float bv[kBuf];
   int bi[kBuf];
   unsigned hist[256];
   int n;
+  int tile_n[2];  // passers of the current super-tile (by parity: one is reset while the other counts)
   int sel, want;
   float theta;
 };
 
+// Super-tile of the top-k filter: thread t holds kTopkPer tokens, as
+// kTopkPer / VW vectors of VW tokens (VW = 4 fp32, 8 bf16) at
+// base + (v kThreads + t) VW + w.
+constexpr int kTopkPer = 16;
+constexpr int kTopkTile = kTopkPer * kThreads;
+template <int DT>
+__device__ __forceinline__ int topk_tok(int base, int e) {
+  constexpr int VW = DT == 1 ? 8 : 4;
+  return base + ((e / VW) * kThreads + (int)threadIdx.x) * VW + (e % VW);
+}
+template <int DT, int NPER = kTopkPer>
+__device__ __forceinline__ void load_topk_tile(const Params &p, int g, int base, float (&z)[NPER]) {
+  constexpr int VW = DT == 1 ? 8 : 4;
+  static_assert(NPER % VW == 0, "whole vectors per thread");
+  if (p.vec_ok) {
+    const char *row = static_cast<const char *>(p.logits) + (int64_t)g * p.lstride * (DT == 1 ? 2 : 4);
+#pragma unroll
+    for (int v = 0; v < NPER / VW; ++v) {
+      const int x0 = topk_tok<DT>(base, v * VW);
+      const int xs = x0 + VW <= p.V ? x0 : 0;  // a vector past the row end reads the row start (masked)
+      const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(row + (int64_t)xs * (DT == 1 ? 2 : 4)));
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int i = 0; i < VW; ++i) {
+        float val;
+        if (DT == 1)
+          val = (i & 1) ? __uint_as_float(ww[i >> 1] & 0xFFFF0000u) : __uint_as_float(ww[i >> 1] << 16);
+        else
+          val = __uint_as_float(ww[i]);
+        z[v * VW + i] = x0 + VW <= p.V ? val : (x0 + i < p.V ? load_logit(p, g, x0 + i) : kNegInf);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < NPER; ++e) {
+      const int x = topk_tok<DT>(base, e);
+      z[e] = x < p.V ? load_logit(p, g, x) : kNegInf;
+    }
+  }
+}
+
 // Order-preserving map float -> uint32 (larger float, larger key).
-__device__ __forceinline__ uint32_t fkey(float f) {
+__device__ __forceinline__ uint32_t ukey(float f) {
   const uint32_t u = __float_as_uint(f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
-__device__ __forceinline__ float fval(uint32_t k) { return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k); }
+__device__ __forceinline__ float ukey_val(uint32_t k) { return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k); }
 
 // One MSD radix digit: among keys matching (prefix, mask), find the digit at
 // `shift` holding the want-th largest; updates prefix/mask/want (uniform).
-__device__ void radix_digit(TopkShared &sh, int shift, uint32_t &prefix, uint32_t &mask, int &want) {
-  if (threadIdx.x == 0) {
-    int acc = 0, sel = 0;
-    for (int b = 255; b >= 0; --b) {
-      const int h = (int)sh.hist[b];
-      if (acc + h >= want) {
-        sel = b;
-        break;
-      }
-      acc += h;
+__device__ __forceinline__ void radix_digit(TopkShared &sh, int shift, uint32_t &prefix, uint32_t &mask, int &want) {
+  // Wave 0 finds the digit: lane l holds bins 255-4l .. 252-4l (descending),
+  // an inclusive prefix sum over lanes gives the count of larger digits.
+  if (threadIdx.x < 64) {
+    const int l = threadIdx.x;
+    const int h0 = (int)sh.hist[255 - 4 * l], h1 = (int)sh.hist[254 - 4 * l];
+    const int h2 = (int)sh.hist[253 - 4 * l], h3 = (int)sh.hist[252 - 4 * l];
+    const int own = h0 + h1 + h2 + h3;
+    int incl = own;  // inclusive scan over lanes (Hillis-Steele with shuffles)
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(incl, d, 64);
+      if (l >= d) incl += o;
     }
-    sh.sel = sel;
-    sh.want = want - acc;
+    const int before = incl - own;  // count in bins above this lane's four
+    const bool here = before < want && incl >= want;
+    if (here) {
+      int acc = before, b = 255 - 4 * l;
+      const int hh[4] = {h0, h1, h2, h3};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (acc + hh[i] >= want) {
+          b = 255 - 4 * l - i;
+          break;
+        }
+        acc += hh[i];
+      }
+      sh.sel = b;
+      sh.want = want - acc;
+    }
   }
   __syncthreads();
   prefix |= (uint32_t)sh.sel << shift;
@@ -1155,46 +1225,124 @@ __device__ void radix_digit(TopkShared &sh, int shift, uint32_t &prefix, uint32_
   __syncthreads();
 }
 
+// Pipelined form of the super-tile load for aligned rows: the raw 16-byte
+// vectors are issued unconditionally (a vector not wholly inside [0, vfull)
+// reads the row start) and decoded later; tokens in [vfull, V) are handled
+// apart, after the loop.
+template <int DT>
+struct TopkRaw {
+  static constexpr int VW = DT == 1 ? 8 : 4;
+  u32x4 v[kTopkPer / VW];
+};
+template <int DT>
+__device__ __forceinline__ void topk_issue(const Params &p, int g, int base, int vfull, TopkRaw<DT> &r) {
+  constexpr int VW = TopkRaw<DT>::VW;
+  const char *row = static_cast<const char *>(p.logits) + (int64_t)g * p.lstride * (DT == 1 ? 2 : 4);
+#pragma unroll
+  for (int v = 0; v < kTopkPer / VW; ++v) {
+    const int x0 = topk_tok<DT>(base, v * VW);
+    const uint32_t off = x0 + VW <= vfull ? (uint32_t)x0 * (DT == 1 ? 2u : 4u) : 0u;
+    r.v[v] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(row + off));
+  }
+}
+template <int DT>
+__device__ __forceinline__ void topk_decode(int base, int vfull, const TopkRaw<DT> &r, float (&z)[kTopkPer]) {
+  constexpr int VW = TopkRaw<DT>::VW;
+#pragma unroll
+  for (int v = 0; v < kTopkPer / VW; ++v) {
+    const int x0 = topk_tok<DT>(base, v * VW);
+    const uint32_t ww[4] = {r.v[v].x, r.v[v].y, r.v[v].z, r.v[v].w};
+#pragma unroll
+    for (int i = 0; i < VW; ++i) {
+      const float val = DT == 1 ? ((i & 1) ? __uint_as_float(ww[i >> 1] & 0xFFFF0000u) : __uint_as_float(ww[i >> 1] << 16))
+                                : __uint_as_float(ww[i]);
+      z[v * VW + i] = x0 + VW <= vfull ? val : kNegInf;
+    }
+  }
+}
+
+// Repetition penalty on a whole super-tile held in z (raw logits): the counts
+// of all its tokens are loaded together (one round trip per 8).
+template <int DT, int NPER = kTopkPer>
+__device__ __forceinline__ void penalize_tile(const Params &p, const Proc &pr, int base, float (&z)[NPER]) {
+#pragma unroll
+  for (int e0 = 0; e0 < NPER; e0 += 8) {
+    int c[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) c[e] = pr.counts[min(topk_tok<DT>(base, e0 + e), p.V - 1)];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int x = topk_tok<DT>(base, e0 + e);
+      if (x < p.V && c[e] > 0) z[e0 + e] = z[e0 + e] > 0.0f ? z[e0 + e] / pr.theta : z[e0 + e] * pr.theta;
+    }
+  }
+}
+
+// Candidates appended with their raw logit (penalty still to apply) carry
+// index | kUnresolved.  Applies the penalty to every such entry.
+constexpr int kUnresolved = (int)0x80000000;
+__device__ __forceinline__ void resolve_buffer(TopkShared &sh, int n, const Proc &pr) {
+  for (int e = threadIdx.x; e < n; e += kThreads) {
+    const int xi = sh.bi[e];
+    if (xi & kUnresolved) {
+      const int x = xi & 0x7FFFFFFF;
+      float z = sh.bv[e];
+      if (pr.counts[x] > 0) z = z > 0.0f ? z / pr.theta : z * pr.theta;
+      sh.bv[e] = z;
+      sh.bi[e] = x;
+    }
+  }
+  __syncthreads();
+}
+
 // k-th largest value among sh.bv[0..n) (1 <= k <= n).
-__device__ float buffer_kth(TopkShared &sh, int n, int k) {
+__device__ __forceinline__ float buffer_kth(TopkShared &sh, int n, int k) {
   uint32_t prefix = 0, mask = 0;
   int want = k;
   for (int shift = 24; shift >= 0; shift -= 8) {
     sh.hist[threadIdx.x] = 0;
     __syncthreads();
     for (int e = threadIdx.x; e < n; e += kThreads) {
-      const uint32_t key = fkey(sh.bv[e]);
+      const uint32_t key = ukey(sh.bv[e]);
       if ((key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & 0xFFu], 1u);
     }
     __syncthreads();
     radix_digit(sh, shift, prefix, mask, want);
   }
-  return fval(prefix);
+  return ukey_val(prefix);
 }
 
-// Keep the buffer entries >= t (order not preserved).
-__device__ void buffer_keep(TopkShared &sh, int n, float t) {
+// In-place compaction of the candidate buffer: keeps entry e < n when
+// keep(value, index) holds, and sets sh.n.  Each thread reads its entries into
+// registers (fixed slots, no dynamic indexing), then appends the kept ones.
+template <class KEEP>
+__device__ __forceinline__ void buffer_compact(TopkShared &sh, int n, KEEP keep) {
   float kv[kBuf / kThreads];
   int ki[kBuf / kThreads];
-  int nk = 0;
+  bool kk[kBuf / kThreads];
 #pragma unroll
   for (int m = 0; m < kBuf / kThreads; ++m) {
     const int e = threadIdx.x + m * kThreads;
-    if (e < n && sh.bv[e] >= t) {
-      kv[nk] = sh.bv[e];
-      ki[nk] = sh.bi[e];
-      ++nk;
-    }
+    kv[m] = e < n ? sh.bv[e] : 0.0f;
+    ki[m] = e < n ? sh.bi[e] : -1;
+    kk[m] = e < n && keep(kv[m], ki[m]);
   }
   __syncthreads();
   if (threadIdx.x == 0) sh.n = 0;
   __syncthreads();
-  for (int m = 0; m < nk; ++m) {
-    const int pos = atomicAdd(&sh.n, 1);
-    sh.bv[pos] = kv[m];
-    sh.bi[pos] = ki[m];
+#pragma unroll
+  for (int m = 0; m < kBuf / kThreads; ++m) {
+    if (kk[m]) {
+      const int pos = atomicAdd(&sh.n, 1);
+      sh.bv[pos] = kv[m];
+      sh.bi[pos] = ki[m];
+    }
   }
   __syncthreads();
+}
+// Keep the buffer entries >= t (order not preserved).
+__device__ __forceinline__ void buffer_keep(TopkShared &sh, int n, float t) {
+  buffer_compact(sh, n, [t](float v, int) { return v >= t; });
 }
 
 template <int DT>
@@ -1217,38 +1365,150 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(Params p) {
   if (threadIdx.x == 0) {
     sh.n = 0;
     sh.theta = kNegInf;
+    sh.tile_n[0] = sh.tile_n[1] = 0;
   }
   __syncthreads();
+  // Streaming filter in super-tiles of kTopkTile tokens, kTopkPer per thread
+  // (vector loads, all in flight together).  A token passes when its processed
+  // logit is >= the running threshold theta (a lower bound of tau_k: the k-th
+  // largest of a subset of the row).  With a penalty theta_r >= 1 the penalty
+  // never raises a logit, so later super-tiles test the raw logit and the counts
+  // of the few passers are read only when a selection needs them.  Two barriers
+  // per super-tile: one to count the passers (compacting the candidate buffer
+  // first if they would not fit), one after they are appended.
+  const bool pen = pr.counts != nullptr;
+  const bool raw_first = !pen || pr.theta >= 1.0f;
   bool overflow = k > kCandCap;
+  constexpr int kFirstPer = kBuf / kThreads;  // the first kBuf tokens are all kept
   if (!overflow) {
-    for (int base = 0; base < p.V; base += kTile) {
-      const float th = sh.theta;
+    float z[kFirstPer];
+    load_topk_tile<DT, kFirstPer>(p, g, 0, z);
+    if (pen) penalize_tile<DT, kFirstPer>(p, pr, 0, z);
 #pragma unroll
-      for (int t = 0; t < kTile / kThreads; ++t) {
-        const int x = base + t * kThreads + (int)threadIdx.x;
-        if (x < p.V) {
-          const float z = apply_proc(load_logit(p, g, x), x, pr);
-          if (z >= th && z > kNegInf) {
-            const int pos = atomicAdd(&sh.n, 1);
-            sh.bv[pos] = z;
-            sh.bi[pos] = x;
-          }
+    for (int e = 0; e < kFirstPer; ++e) {
+      const int x = topk_tok<DT>(0, e);
+      sh.bv[threadIdx.x * kFirstPer + e] = z[e];
+      sh.bi[threadIdx.x * kFirstPer + e] = x < p.V && z[e] > kNegInf ? x : -1;
+    }
+    __syncthreads();
+    // compact the finite entries, then theta = their k-th largest
+    buffer_compact(sh, kBuf, [](float, int x) { return x >= 0; });
+    const int n = sh.n;
+    if (n >= k) {
+      const float t = buffer_kth(sh, n, k);
+      buffer_keep(sh, n, t);
+      if (threadIdx.x == 0) sh.theta = t;
+    }
+    __syncthreads();
+  }
+  // One super-tile: filter z (raw logits) against theta, count the passers,
+  // make room if needed, append them.  All threads call it (barriers inside).
+  auto tile_step = [&](int base, int par, float (&z)[kTopkPer]) {
+    // sh.n and sh.theta last changed before the previous super-tile's final
+    // barrier: every thread reads the same values here.
+    const int n0 = sh.n;
+    const float th = sh.theta;
+    if (!raw_first) penalize_tile<DT>(p, pr, base, z);  // a penalty < 1 can raise logits: test processed ones
+    int npass = 0;
+#pragma unroll
+    for (int e = 0; e < kTopkPer; ++e) {
+      const int x = topk_tok<DT>(base, e);
+      z[e] = (x < p.V && z[e] >= th && z[e] > kNegInf) ? z[e] : kNegInf;
+      npass += z[e] > kNegInf ? 1 : 0;
+    }
+    if (npass) atomicAdd(&sh.tile_n[par], npass);
+    __syncthreads();
+    if (threadIdx.x == 0) sh.tile_n[par ^ 1] = 0;  // read last in the previous super-tile
+    if (n0 + sh.tile_n[par] > kBuf) {
+      // Not enough room: theta becomes the k-th largest kept candidate
+      // (penalties applied first); this super-tile's passers are re-tested.
+      if (n0 < k) {
+        overflow = true;  // fewer than k finite logits so far and a full tile: exact radix select below
+      } else {
+        if (pen) resolve_buffer(sh, n0, pr);
+        const float t = buffer_kth(sh, n0, k);
+        buffer_keep(sh, n0, t);
+        if (threadIdx.x == 0) {
+          sh.theta = t;
+          sh.tile_n[par] = 0;
         }
+        __syncthreads();
+        npass = 0;
+#pragma unroll
+        for (int e = 0; e < kTopkPer; ++e) {
+          if (!(z[e] >= t)) z[e] = kNegInf;
+          npass += z[e] > kNegInf ? 1 : 0;
+        }
+        if (npass) atomicAdd(&sh.tile_n[par], npass);
+        __syncthreads();
+        const bool full = sh.n + sh.tile_n[par] > kBuf;  // ties at theta: exact radix select below
+        __syncthreads();  // every thread has read the counts before anyone appends
+        overflow = full;
       }
-      __syncthreads();
-      const int n = sh.n;
-      if (n > kBuf - kTile) {
+    }
+    if (overflow) return;
+    const int flag = raw_first && pen ? kUnresolved : 0;  // raw logits: penalty applied at the next selection
+#pragma unroll
+    for (int e = 0; e < kTopkPer; ++e) {
+      if (z[e] > kNegInf) {
+        const int pos = atomicAdd(&sh.n, 1);
+        sh.bv[pos] = z[e];
+        sh.bi[pos] = topk_tok<DT>(base, e) | flag;
+      }
+    }
+    __syncthreads();
+  };
+  if (p.vec_ok) {
+    // Two super-tiles in flight: the next one's loads are issued before this
+    // one is filtered.
+    constexpr int VW = TopkRaw<DT>::VW;
+    const int vfull = p.V - p.V % VW;
+    TopkRaw<DT> ra, rb;
+    int base = kBuf, par = 0;
+    topk_issue<DT>(p, g, base, vfull, ra);
+    topk_issue<DT>(p, g, base + kTopkTile, vfull, rb);
+    while (base < vfull && !overflow) {
+      float z[kTopkPer];
+      topk_decode<DT>(base, vfull, ra, z);
+      topk_issue<DT>(p, g, base + 2 * kTopkTile, vfull, ra);
+      tile_step(base, par, z);
+      base += kTopkTile;
+      par ^= 1;
+      if (base >= vfull || overflow) break;
+      topk_decode<DT>(base, vfull, rb, z);
+      topk_issue<DT>(p, g, base + 2 * kTopkTile, vfull, rb);
+      tile_step(base, par, z);
+      base += kTopkTile;
+      par ^= 1;
+    }
+    if (!overflow && vfull < p.V) {  // the last V % VW tokens, penalty applied at once
+      if (sh.n > kBuf - VW) {  // make room (n >= k here: k <= kCandCap < kBuf - VW)
+        const int n = sh.n;
+        if (pen) resolve_buffer(sh, n, pr);
         const float t = buffer_kth(sh, n, k);
         buffer_keep(sh, n, t);
         if (threadIdx.x == 0) sh.theta = t;
         __syncthreads();
-        if (sh.n > kBuf - kTile) {
-          overflow = true;
-          break;
+      }
+      const int x = vfull + (int)threadIdx.x;
+      if (x < p.V) {
+        const float z = apply_proc(load_logit(p, g, x), x, pr);
+        if (z >= sh.theta && z > kNegInf) {
+          const int pos = atomicAdd(&sh.n, 1);
+          sh.bv[pos] = z;
+          sh.bi[pos] = x;
         }
       }
+      __syncthreads();
+    }
+  } else {
+    for (int base = kBuf, par = 0; base < p.V && !overflow; base += kTopkTile, par ^= 1) {
+      float z[kTopkPer];
+      load_topk_tile<DT>(p, g, base, z);
+      tile_step(base, par, z);
     }
   }
+  if (pen && !overflow) resolve_buffer(sh, sh.n, pr);
 
   float tau;
   int ncand = -1;
@@ -1269,13 +1529,13 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(Params p) {
       sh.hist[threadIdx.x] = 0;
       __syncthreads();
       for (int x = threadIdx.x; x < p.V; x += kThreads) {
-        const uint32_t key = fkey(apply_proc(load_logit(p, g, x), x, pr));
+        const uint32_t key = ukey(apply_proc(load_logit(p, g, x), x, pr));
         if ((key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & 0xFFu], 1u);
       }
       __syncthreads();
       radix_digit(sh, shift, prefix, mask, want);
     }
-    tau = fval(prefix);
+    tau = ukey_val(prefix);
   }
 
   if (ncand < 0 || ncand > kCandCap) {
@@ -1286,30 +1546,14 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(Params p) {
     return;
   }
 
-  // Sort the kept tokens by id (bitonic over kCandCap slots, padding = INT_MAX).
-  for (int e = ncand + (int)threadIdx.x; e < kCandCap; e += kThreads) sh.bi[e] = 0x7FFFFFFF;
-  __syncthreads();
-  for (int size = 2; size <= kCandCap; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int pi = threadIdx.x; pi < kCandCap / 2; pi += kThreads) {
-        const int i = 2 * stride * (pi / stride) + (pi % stride);
-        const int jj = i + stride;
-        const bool up = (i & size) == 0;
-        const int a = sh.bi[i], b = sh.bi[jj];
-        if ((a > b) == up) {
-          sh.bi[i] = b;
-          sh.bi[jj] = a;
-          const float fa = sh.bv[i];
-          sh.bv[i] = sh.bv[jj];
-          sh.bv[jj] = fa;
-        }
-      }
-      __syncthreads();
-    }
-  }
+  // Write the kept tokens in increasing id order: each one's position is the
+  // number of kept tokens with a smaller id (ids are distinct).
   for (int e = threadIdx.x; e < ncand; e += kThreads) {
-    p.cand_val[(int64_t)g * kCandCap + e] = sh.bv[e];
-    p.cand_idx[(int64_t)g * kCandCap + e] = sh.bi[e];
+    const int id = sh.bi[e];
+    int rank = 0;
+    for (int t = 0; t < ncand; ++t) rank += sh.bi[t] < id ? 1 : 0;
+    p.cand_val[(int64_t)g * kCandCap + rank] = sh.bv[e];
+    p.cand_idx[(int64_t)g * kCandCap + rank] = id;
   }
   if (threadIdx.x == 0) {
     p.cand_n[g] = ncand;
