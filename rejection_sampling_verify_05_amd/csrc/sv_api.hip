@@ -17,10 +17,13 @@ struct sv_ctx {
   int32_t nc_stride;
   uint32_t epoch;
   int32_t resident[2][2];  // resident stats workgroups: [dtype][fast pass]
+  int32_t ncu;             // compute units
   float2 *chunk_tab;
   float4 *row_info;
   int4 *res_req;
   float *res_tab;
+  int *res_list;
+  bool res_dirty;  // a call listed residual requests but did not reach the residual race
   float *cand_val;
   int32_t *cand_idx;
   int32_t *cand_n;
@@ -44,8 +47,8 @@ void free_events(sv_ctx *c) {
 
 void free_ctx(sv_ctx *c) {
   free_events(c);
-  void *ptrs[] = {c->chunk_tab, c->row_info, c->res_req, c->res_tab,
-                  c->cand_val,  c->cand_idx, c->cand_n,  c->cand_tau, c->err};
+  void *ptrs[] = {c->chunk_tab, c->row_info, c->res_req,  c->res_tab, c->res_list,
+                  c->cand_val,  c->cand_idx, c->cand_n,   c->cand_tau, c->err};
   for (void *p : ptrs)
     if (p) (void)hipFree(p);
   delete c;
@@ -83,12 +86,13 @@ extern "C" int spec_verify_create(sv_ctx **out, int32_t max_rows, int32_t max_re
   const size_t rows = (size_t)max_rows, reqs = (size_t)max_reqs, ncs = (size_t)c->nc_stride;
   bool ok = dev_alloc(&c->chunk_tab, rows * ncs) && dev_alloc(&c->row_info, rows) &&
             dev_alloc(&c->res_req, reqs) &&
-            dev_alloc(&c->res_tab, reqs * ncs) && dev_alloc(&c->err, 1);
+            dev_alloc(&c->res_tab, reqs * ncs) && dev_alloc(&c->res_list, reqs + 1) && dev_alloc(&c->err, 1);
   if (ok && (flags & SV_CREATE_TOPK))
     ok = dev_alloc(&c->cand_val, rows * sv::kCandCap) && dev_alloc(&c->cand_idx, rows * sv::kCandCap) &&
          dev_alloc(&c->cand_n, rows) && dev_alloc(&c->cand_tau, rows);
   if (ok)
     ok = hipMemset(c->res_req, 0, reqs * sizeof(int4)) == hipSuccess &&
+         hipMemset(c->res_list, 0, sizeof(int)) == hipSuccess &&
          hipMemset(c->err, 0, sizeof(unsigned int)) == hipSuccess && hipDeviceSynchronize() == hipSuccess;
   int ncu = 0;
   if (ok) ok = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, c->device) == hipSuccess;
@@ -98,6 +102,7 @@ extern "C" int spec_verify_create(sv_ctx **out, int32_t max_rows, int32_t max_re
   }
   for (int dt = 0; dt < 2; ++dt)
     for (int f = 0; f < 2; ++f) c->resident[dt][f] = ncu * sv::stats_blocks_per_cu(dt, f != 0);
+  c->ncu = ncu > 0 ? ncu : 1;
   *out = c;
   return SV_OK;
 }
@@ -148,6 +153,7 @@ extern "C" int spec_verify_run(sv_ctx *ctx, const sv_verify_args *a, hipStream_t
   p.row_info = ctx->row_info;
   p.res_req = ctx->res_req;
   p.res_tab = ctx->res_tab;
+  p.res_list = ctx->res_list;
   p.cand_val = ctx->cand_val;
   p.cand_idx = ctx->cand_idx;
   p.cand_n = ctx->cand_n;
@@ -164,6 +170,11 @@ extern "C" int spec_verify_run(sv_ctx *ctx, const sv_verify_args *a, hipStream_t
   p.nc_stride = ctx->nc_stride;
   p.cps = sv::kResidCPS;
   p.nseg = (p.NC + p.cps - 1) / p.cps;
+  {
+    const int64_t items = (int64_t)a->num_reqs * p.nseg;  // upper bound of (request, segment) items
+    const int64_t cap = (int64_t)ctx->ncu * 8;
+    p.resid_grid = (int32_t)(items < cap ? items : cap);
+  }
   {
     // Fast pass: aligned rows whose length is whole 16-byte vectors, no penalty,
     // no top-k.  Grid: every resident workgroup, but enough workgroups that a
@@ -193,10 +204,18 @@ extern "C" int spec_verify_run(sv_ctx *ctx, const sv_verify_args *a, hipStream_t
   if ((int64_t)p.B * p.nseg > 0x7FFFFFFF) return SV_ECAPACITY;
 
   hipEvent_t *ev = (ctx->ev && ctx->ev_n < ctx->ev_cap) ? ctx->ev + 4 * ctx->ev_n++ : nullptr;
+  if (ctx->res_dirty) {
+    if (sv::launch_zero_count(ctx->res_list, stream) != hipSuccess) return SV_EHIP;
+    ctx->res_dirty = false;
+  }
   if (p.has_topk && sv::launch_topk(p, stream) != hipSuccess) return SV_EHIP;
+  ctx->res_dirty = p.draft_probs != nullptr;  // until the residual race has zeroed the count
   if (sv::launch_stats(p, stream, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr) != hipSuccess) return SV_EHIP;
   if (sv::launch_epilogue(p, stream, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr) != hipSuccess) return SV_EHIP;
-  if (p.draft_probs && sv::launch_resid(p, stream) != hipSuccess) return SV_EHIP;
+  if (p.draft_probs) {
+    if (sv::launch_resid(p, stream) != hipSuccess) return SV_EHIP;
+    ctx->res_dirty = false;
+  }
   if (p.dbg_probs && sv::launch_dbg_probs(p, stream) != hipSuccess) return SV_EHIP;
   return SV_OK;
 }

@@ -46,6 +46,8 @@ struct Params {
   float4 *row_info;            // [max_rows]: (m, s, argmax bits, state bits)
   int4 *res_req;               // [max_reqs]: (row g*, position j, draft d_j, epoch)
   float *res_tab;              // [max_reqs, nc_stride] residual chunk masses
+  int *res_list;               // [max_reqs + 1]: count of rejected draft-probs requests, then their ids (count zero between calls)
+  int32_t resid_grid;          // persistent residual-pass workgroups
   float *cand_val;             // [max_rows, kCandCap]
   int32_t *cand_idx;           // [max_rows, kCandCap]
   int32_t *cand_n;             // [max_rows]
@@ -83,6 +85,8 @@ hipError_t launch_topk(const Params &p, hipStream_t s);
 hipError_t launch_stats(const Params &p, hipStream_t s, hipEvent_t t0, hipEvent_t t1);
 hipError_t launch_epilogue(const Params &p, hipStream_t s, hipEvent_t t0, hipEvent_t t1);
 hipError_t launch_resid(const Params &p, hipStream_t s);
+// Zeroes the residual-request count (after a call that stopped before the residual race).
+hipError_t launch_zero_count(int *count, hipStream_t s);
 hipError_t launch_dbg_probs(const Params &p, hipStream_t s);
 hipError_t launch_post_update(const PostParams &p, hipStream_t s);
 // Resident stats workgroups per CU (occupancy query).

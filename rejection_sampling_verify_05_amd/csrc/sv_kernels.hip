@@ -204,6 +204,7 @@ struct EpiShared {
   float w1s[kWaves];         // best chunk other than the draft token's: score
   int w1c[kWaves];           //   and index (-1: none)
   int cd[kWaves];            // the draft token's chunk when excluded, else -1
+  float rcd[kWaves];         // 1/E of that chunk in the chunk race
   union {
     float2 tab[kTabCache];  // dense rows: chunk tables of the request's rows
     struct {
@@ -290,10 +291,37 @@ __device__ __forceinline__ void write_empty(const Params &p, int r) {
 // Chunk c of row g, 16 tokens per lane: lane l holds c C + 256 t + 4 l + k for
 // t, k < 4 (one Philox block per 4 tokens); positions past V read token V - 1.
 __device__ __forceinline__ int c16_tok(int c, int e, int lane) { return c * kChunk + (e >> 2) * 256 + 4 * lane + (e & 3); }
-// The dtype test stays outside the loads so that all 16 issue back to back.
+// The dtype and alignment tests stay outside the loads so that they issue back
+// to back: with aligned rows and V a multiple of 4, one 8-byte (bf16) or
+// 16-byte (fp32) load per group of 4 tokens (a group at or past V reads group
+// 0 and is masked later); otherwise 16 scalar loads.
 __device__ __forceinline__ void load_chunk16(const Params &p, int g, int c, float (&z)[16]) {
   const int lane = threadIdx.x & 63;
-  if (p.dtype == 1) {
+  if (p.vec_ok && (p.V & 3) == 0) {
+    if (p.dtype == 1) {
+      const uint2 *row = reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.logits) + (int64_t)g * p.lstride);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int x0 = c16_tok(c, 4 * t, lane);
+        const uint2 w = row[x0 < p.V ? x0 >> 2 : 0];
+        z[4 * t] = __uint_as_float(w.x << 16);
+        z[4 * t + 1] = __uint_as_float(w.x & 0xFFFF0000u);
+        z[4 * t + 2] = __uint_as_float(w.y << 16);
+        z[4 * t + 3] = __uint_as_float(w.y & 0xFFFF0000u);
+      }
+    } else {
+      const float4 *row = reinterpret_cast<const float4 *>(static_cast<const float *>(p.logits) + (int64_t)g * p.lstride);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int x0 = c16_tok(c, 4 * t, lane);
+        const float4 w = row[x0 < p.V ? x0 >> 2 : 0];
+        z[4 * t] = w.x;
+        z[4 * t + 1] = w.y;
+        z[4 * t + 2] = w.z;
+        z[4 * t + 3] = w.w;
+      }
+    }
+  } else if (p.dtype == 1) {
     const uint16_t *row = static_cast<const uint16_t *>(p.logits) + (int64_t)g * p.lstride;
 #pragma unroll
     for (int e = 0; e < 16; ++e) z[e] = bf16_bits_to_f32(row[min(c16_tok(c, e, lane), p.V - 1)]);
@@ -306,27 +334,54 @@ __device__ __forceinline__ void load_chunk16(const Params &p, int g, int c, floa
 
 // Wave-level chunk race of row g over its chunk table (W_c = s_c exp2(a (m_c - m))),
 // chunk `skip` left out.  Lane l draws the words of chunks 4l..4l+3.
+// 1/E of the chunk race for a wave's first 256 chunks of row g: lane l holds
+// chunks 4l..4l+3 (one Philox block).  Depends only on the row, so it can be
+// computed while the chunk tables are still in flight.
+struct ChunkNoise {
+  float r[4];
+};
+__device__ __forceinline__ ChunkNoise chunk_noise(const Params &p, int g) {
+  const int lane = threadIdx.x & 63;
+  const uint4 w4 = rng_block(p, (uint32_t)lane, (uint32_t)g, kTagChunk);
+  ChunkNoise n;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) n.r[k] = __builtin_amdgcn_rcpf(exp_noise(pick(w4, k)));
+  return n;
+}
+
+// Wave-level chunk race of row g over its chunk table (W_c = s_c exp2(a (m_c - m))),
+// chunk `skip` left out; scores W_c / E_c = W_c * (1/E_c), with 1/E from cn for
+// the first 256 chunks.  *rskip receives 1/E of chunk skip (if skip >= 0).
 template <class EF>
-__device__ __forceinline__ ArgMax wave_chunk_race(const Params &p, int g, EF ent, float a, float m, int skip) {
+__device__ __forceinline__ ArgMax wave_chunk_race(const Params &p, int g, EF ent, float a, float m, int skip,
+                                                  const ChunkNoise &cn, float *rskip) {
   const int lane = threadIdx.x & 63;
   ArgMax best{-1.0f, 0x7FFFFFFF};
+  float rs = 0.0f;
   for (int c0 = 4 * lane; c0 < p.NC; c0 += 256) {
-    const uint4 w4 = rng_block(p, (uint32_t)c0 >> 2, (uint32_t)g, kTagChunk);
+    ChunkNoise n = cn;
+    if (c0 >= 256) {  // chunks past the first 256: drawn here
+      const uint4 w4 = rng_block(p, (uint32_t)c0 >> 2, (uint32_t)g, kTagChunk);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) n.r[k] = __builtin_amdgcn_rcpf(exp_noise(pick(w4, k)));
+    }
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int c = c0 + k;
+      if (c == skip) rs = n.r[k];
       if (c < p.NC && c != skip) {
         const float2 e = ent(c);
         if (e.x > kNegInf) {
           const float Wc = e.y * exp2_acc(a * (e.x - m));
           if (Wc > 0.0f) {
-            ArgMax o{Wc / exp_noise(pick(w4, k)), c};
+            ArgMax o{Wc * n.r[k], c};
             if (better(o, best)) best = o;
           }
         }
       }
     }
   }
+  if (skip >= 0) *rskip = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rs), (skip >> 2) & 63));
   return wave_argmax(best);
 }
 
@@ -373,6 +428,7 @@ struct RowSpec {
   float zx[16];   // logits of the draft token's chunk cd
   ArgMax w1;      // best chunk other than cd: (score, c1); c1 = -1 if none
   int cd;         // draft token's chunk when it is excluded, else -1
+  float rcd;      // 1/E of chunk cd in the chunk race
 };
 
 // Row statistics of row i from its chunk table (dense) or candidates (compact):
@@ -416,11 +472,13 @@ __device__ __forceinline__ void row_stats(const Params &p, const Req &q, int g, 
 // rows): the chunk race without the draft token's chunk, then the loads of
 // the winning chunk and of the draft token's chunk.
 template <class EF>
-__device__ __forceinline__ void spec_issue(const Params &p, const Req &q, int i, int d, float m, EF ent, RowSpec &rs) {
+__device__ __forceinline__ void spec_issue(const Params &p, const Req &q, int i, int d, float m, EF ent, RowSpec &rs,
+                                           const ChunkNoise &cn) {
   const int g = q.g0 + i;
   const bool excl = i < q.K && !p.draft_probs && d >= 0 && d < p.V;
   rs.cd = excl ? d / kChunk : -1;
-  rs.w1 = wave_chunk_race(p, g, ent, q.a, m, rs.cd);
+  rs.rcd = 0.0f;
+  rs.w1 = wave_chunk_race(p, g, ent, q.a, m, rs.cd, cn, &rs.rcd);
   const int c1 = rs.w1.s < 0.0f ? -1 : rs.w1.i;
   if (c1 >= 0) load_chunk16(p, g, c1, rs.zc);
   if (excl) load_chunk16(p, g, rs.cd, rs.zx);
@@ -466,6 +524,7 @@ __device__ __forceinline__ void spec_publish(const RowSpec &rs, int slot, EpiSha
     sh.w1s[slot] = rs.w1.s;
     sh.w1c[slot] = rs.w1.i;
     sh.cd[slot] = rs.cd;
+    sh.rcd[slot] = rs.rcd;
   }
 }
 
@@ -482,16 +541,16 @@ __device__ __forceinline__ int spec_finish(const Params &p, const Req &q, int j,
   bool excl = cd >= 0;
   if (excl) {
     const float2 e = ent(cd);
-    const uint32_t wd = pick(rng_block(p, (uint32_t)cd >> 2, (uint32_t)gs, kTagChunk), cd & 3);
+    const float rd = sh.rcd[slot];  // 1/E of chunk cd, drawn by the chunk race
     const float Wd = e.x > kNegInf ? sx * exp2_acc(a * (e.x - m)) : 0.0f;
     if (Wd > 0.0f) {
-      ArgMax o{race_score(Wd, wd), cd};
+      ArgMax o{Wd * rd, cd};
       if (better(o, win)) win = o;
     }
     if (win.s < 0.0f) {  // nothing left once d_j is removed (rounding): race over p_j
       excl = false;
       const float Wf = e.x > kNegInf ? e.y * exp2_acc(a * (e.x - m)) : 0.0f;
-      if (Wf > 0.0f) win = ArgMax{race_score(Wf, wd), cd};
+      if (Wf > 0.0f) win = ArgMax{Wf * rd, cd};
     }
   }
   if (win.s < 0.0f) return -1;
@@ -499,6 +558,15 @@ __device__ __forceinline__ int spec_finish(const Params &p, const Req &q, int j,
   const float hi = a * ent(cstar).x;
   const float *zs = cstar == cd ? sh.zx[slot] : sh.zc[slot];
   return block_token_race(p, gs, cstar, zs, pr, a, hi, (excl && cstar == cd) ? dj : -1, sh.red);
+}
+
+// Speculative rows: with at most four rows, row w for wave w; with more, rows
+// 0, 1, 2 and the bonus row (the likeliest to be sampled after row 0 when the
+// acceptance rate is high).  spec_slot: the wave (LDS slot) of row i, or -1.
+__device__ __forceinline__ int spec_row(int w, int nrow) { return nrow <= kWaves || w < kWaves - 1 ? w : nrow - 1; }
+__device__ __forceinline__ int spec_slot(int i, int nrow) {
+  if (nrow <= kWaves) return i;
+  return i < kWaves - 1 ? i : (i == nrow - 1 ? kWaves - 1 : -1);
 }
 
 __device__ __forceinline__ void request_epilogue(const Params &p, const Req &q, EpiShared &sh) {
@@ -526,10 +594,24 @@ __device__ __forceinline__ void request_epilogue(const Params &p, const Req &q, 
     sh.d[i] = i < K ? p.draft_ids[q.c0 + i] : -1;
   }
   const bool cached = nrow * p.NC <= kTabCache;
-  if (cached) {
-    for (int t = tid; t < nrow * p.NC; t += kThreads) {
+  float2 tv[kTabCache / kThreads];
+  if (cached) {  // all table loads issued first
+#pragma unroll
+    for (int m = 0; m < kTabCache / kThreads; ++m) {
+      const int t = tid + m * kThreads;
       const int i = t / p.NC, c = t - i * p.NC;
-      sh.u.tab[t] = p.chunk_tab[(int64_t)(q.g0 + i) * p.nc_stride + c];
+      tv[m] = t < nrow * p.NC ? p.chunk_tab[(int64_t)(q.g0 + i) * p.nc_stride + c] : make_float2(0.0f, 0.0f);
+    }
+  }
+  // While the tables are in flight: the chunk-race noise of this wave's
+  // speculative row (it depends only on the row).
+  const int srow = spec_row(wave, nrow);
+  const ChunkNoise cn = chunk_noise(p, q.g0 + min(srow, nrow - 1));
+  if (cached) {
+#pragma unroll
+    for (int m = 0; m < kTabCache / kThreads; ++m) {
+      const int t = tid + m * kThreads;
+      if (t < nrow * p.NC) sh.u.tab[t] = tv[m];
     }
   }
   __syncthreads();
@@ -537,14 +619,26 @@ __device__ __forceinline__ void request_epilogue(const Params &p, const Req &q, 
     return cached ? sh.u.tab[i * p.NC + c] : p.chunk_tab[(int64_t)(q.g0 + i) * p.nc_stride + c];
   };
 
-  // Each wave takes rows wave, wave + 4, ...  Its first row gets the
-  // speculative loads; the others only what the accept tests need.
+  // Wave w first takes its speculative row spec_row(w) -- rows 0..3, or with
+  // more than four rows 0, 1, 2 and the bonus row K -- with the speculative
+  // loads; then, round robin, the rows nobody speculates on, with only what
+  // the accept tests need.
   RowSpec rs;
 #pragma unroll
   for (int e = 0; e < 16; ++e) rs.zc[e] = rs.zx[e] = 0.0f;
   rs.cd = -1;
   rs.w1 = ArgMax{-1.0f, 0x7FFFFFFF};
-  for (int i = wave; i < nrow; i += kWaves) {
+  for (int i = srow, phase = 0;;) {
+    bool spec = phase == 0;
+    if (spec && i >= nrow) {  // no speculative row for this wave
+      phase = 1;
+      i = wave;
+      continue;
+    }
+    if (!spec) {
+      while (i < nrow && spec_slot(i, nrow) >= 0) i += kWaves;
+      if (i >= nrow) break;
+    }
     const int g = q.g0 + i;
     const int st = sh.state[i];
     const int d = sh.d[i];
@@ -562,10 +656,10 @@ __device__ __forceinline__ void request_epilogue(const Params &p, const Req &q, 
         load_chunk16(p, g, lc, rs.zc);
         am = wave_first_equal(p, lc, rs.zc, pr, m);
       }
-    } else if (st < 0 && i == wave && (!p.draft_probs || i == K)) {
-      spec_issue(p, q, i, d, m, ent, rs);
+    } else if (st < 0 && spec && (!p.draft_probs || i == K)) {
+      spec_issue(p, q, i, d, m, ent, rs, cn);
       if (rs.cd >= 0) spec_draft_record(p, q, d, pr, rs, zd, sx);
-      spec_publish(rs, i, sh);
+      spec_publish(rs, wave, sh);
     } else if (valid_d) {
       // single loads: z_d (and q(d)) for the accept test
       zd = apply_proc(load_logit(p, g, d), d, pr);
@@ -579,6 +673,12 @@ __device__ __forceinline__ void request_epilogue(const Params &p, const Req &q, 
       sh.qd[i] = qd;
       sh.sx[i] = sx;
       p.row_info[g] = make_float4(m, s, __int_as_float(am), __int_as_float(st));
+    }
+    if (spec) {
+      phase = 1;
+      i = wave;
+    } else {
+      i += kWaves;
     }
   }
   __syncthreads();
@@ -678,17 +778,20 @@ __device__ __forceinline__ void request_epilogue(const Params &p, const Req &q, 
 
   if (rejected && p.draft_probs) {
     // Dense residual: handed to resid_kernel (needs the full draft row).
-    if (tid == 0) p.res_req[r] = make_int4(gs, j, dj, (int)p.epoch);
+    if (tid == 0) {
+      p.res_req[r] = make_int4(gs, j, dj, (int)p.epoch);
+      p.res_list[1 + atomicAdd(p.res_list, 1)] = r;  // at most one entry per request: fits in max_reqs
+    }
     return;
   }
 
   // Dense race over p_j (bonus row, or the rejected row with d_j removed).
   auto entj = [&](int c) { return entry(j, c); };
-  int slot = j;
+  int slot = spec_slot(j, nrow);
   float sxj = sh.sx[j];
-  if (j >= kWaves) {  // no speculative state for this row: same steps, loads now
+  if (slot < 0) {  // no speculative state for this row: same steps, loads now
     if (wave == 0) {
-      spec_issue(p, q, j, dj, m, entj, rs);
+      spec_issue(p, q, j, dj, m, entj, rs, chunk_noise(p, q.g0 + j));
       float zd = kNegInf;
       sxj = 0.0f;
       if (rs.cd >= 0) spec_draft_record(p, q, dj, pr, rs, zd, sxj);
@@ -1028,44 +1131,55 @@ __global__ __launch_bounds__(kThreads) void stats_fast_kernel(Params p) {
 }
 
 // ---------------------------------------------------------------------------
-// Residual pass (draft-probs mode, dense rows).  resid_kernel: chunk masses of
-// w = max(0, p_j - q_j) for each rejected request (one workgroup per segment
-// of cps chunks); resid_race_kernel: the race over them (one workgroup per
-// request).  A request is active when its res_req entry carries this call's
-// epoch.
+// Residual pass (draft-probs mode, dense rows).  The epilogue lists each
+// rejected request (res_list: a count, then request ids) and records its row in
+// res_req with this call's epoch.  resid_kernel: chunk masses of
+// w = max(0, p_j - q_j), persistent over (listed request, segment of cps chunks)
+// items; resid_race_kernel: the race over them (one workgroup per request,
+// active when its res_req entry carries this call's epoch).
 // ---------------------------------------------------------------------------
 template <int DT>
 __global__ __launch_bounds__(kThreads) void resid_kernel(Params p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int r = blockIdx.x / p.nseg;
-  const int seg = blockIdx.x - r * p.nseg;
-  const int4 rq = p.res_req[r];
-  if (rq.w != (int)p.epoch) return;
-  const Req q = load_req(p, r);
-  const int gs = rq.x, j = rq.y;
-  const float4 ri = p.row_info[gs];
-  const float m = ri.x, inv_s = 1.0f / ri.y, a = q.a;
-  Proc pr = q.proc;
-  if (__float_as_int(ri.w) == kRowThreshold) pr.tau = p.cand_tau[gs];
-  const float *qrow = p.draft_probs + (int64_t)(q.c0 + j) * p.dstride;
-  float *rt = p.res_tab + (int64_t)r * p.nc_stride;
-  for (int c = seg * p.cps + wave; c < min(p.NC, (seg + 1) * p.cps); c += kWaves) {
-    float acc = 0.0f;
-    for (int t = lane; t < kChunk; t += 64) {
-      const int x = c * kChunk + t;
-      if (x < p.V) {
-        const float px = exp2_acc(a * (apply_proc(load_logit(p, gs, x), x, pr) - m)) * inv_s;
-        acc += fmaxf(px - qrow[x], 0.0f);
+  const int nact = p.res_list[0];
+  // persistent: work item w = (active request w / nseg, segment w % nseg)
+  for (int w = blockIdx.x; w < nact * p.nseg; w += gridDim.x) {
+    const int r = p.res_list[1 + w / p.nseg];
+    const int seg = w % p.nseg;
+    const int4 rq = p.res_req[r];
+    const Req q = load_req(p, r);
+    const int gs = rq.x, j = rq.y;
+    const float4 ri = p.row_info[gs];
+    const float m = ri.x, inv_s = 1.0f / ri.y, a = q.a;
+    Proc pr = q.proc;
+    if (__float_as_int(ri.w) == kRowThreshold) pr.tau = p.cand_tau[gs];
+    const float *qrow = p.draft_probs + (int64_t)(q.c0 + j) * p.dstride;
+    float *rt = p.res_tab + (int64_t)r * p.nc_stride;
+    for (int c = seg * p.cps + wave; c < min(p.NC, (seg + 1) * p.cps); c += kWaves) {
+      // 16 tokens per lane, all loads issued before any use
+      float z[16], qx[16];
+      load_chunk16(p, gs, c, z);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) qx[e] = qrow[min(c16_tok(c, e, lane), p.V - 1)];
+      float acc = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int x = c16_tok(c, e, lane);
+        if (x < p.V) {
+          const float px = exp2_acc(a * (apply_proc(z[e], x, pr) - m)) * inv_s;
+          acc += fmaxf(px - qx[e], 0.0f);
+        }
       }
+      const float Wc = wave_sum(acc);
+      if (lane == 0) rt[c] = Wc;
     }
-    const float Wc = wave_sum(acc);
-    if (lane == 0) rt[c] = Wc;
   }
 }
 
 __global__ __launch_bounds__(kThreads) void resid_race_kernel(Params p) {
   __shared__ BlockScratch red;
   const int r = blockIdx.x;
+  if (r == 0 && threadIdx.x == 0) p.res_list[0] = 0;  // the residual pass has read it: zero for the next call
   const int4 rq = p.res_req[r];
   if (rq.w != (int)p.epoch) return;
   const Req q = load_req(p, r);
@@ -1661,8 +1775,15 @@ hipError_t launch_epilogue(const Params &p, hipStream_t s, hipEvent_t t0, hipEve
   return launch_timed(reinterpret_cast<const void *>(&epilogue_kernel), dim3((unsigned)p.B), p, s, t0, t1);
 }
 
+__global__ void zero_count_kernel(int *count) { *count = 0; }
+
+hipError_t launch_zero_count(int *count, hipStream_t s) {
+  zero_count_kernel<<<dim3(1), dim3(1), 0, s>>>(count);
+  return hipGetLastError();
+}
+
 hipError_t launch_resid(const Params &p, hipStream_t s) {
-  const dim3 grid((unsigned)(p.B * p.nseg));
+  const dim3 grid((unsigned)p.resid_grid);
   if (p.dtype == 1)
     resid_kernel<1><<<grid, dim3(kThreads), 0, s>>>(p);
   else
