@@ -195,8 +195,10 @@ int spec_verify_read_error(sv_ctx *ctx, uint32_t *host_flags, hipStream_t stream
  * spec_verify_run launch the streaming statistics kernel and the request
  * epilogue kernel with start/stop HIP events that the launch stamps at the
  * kernel's own start and end on the call's stream (hipExtLaunchKernel), so an
- * interval is that kernel's execution time.  The events are created here,
- * owned by the context, destroyed with it or by the next start.
+ * interval is that kernel's execution time.  The events are created here
+ * (timing only: no system-scope fence, so they add no cache writeback to the
+ * kernels they bracket), owned by the context, destroyed with it or by the
+ * next start.
  * spec_verify_profile_read waits for those events, writes the per-call
  * durations in milliseconds to the host arrays stream_ms[] and epilogue_ms[]
  * (each with room for max_calls entries; either may be NULL), stores the

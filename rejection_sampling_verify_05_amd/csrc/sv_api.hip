@@ -279,8 +279,10 @@ extern "C" int spec_verify_profile_start(sv_ctx *ctx, int32_t max_calls) {
   ctx->ev = new (std::nothrow) hipEvent_t[4 * (size_t)max_calls]();
   if (!ctx->ev) return SV_EHIP;
   ctx->ev_cap = max_calls;
+  // Timing-only events: without the system-scope fence, recording them adds no
+  // cache writeback or invalidation to the kernels they bracket.
   for (int32_t i = 0; i < 4 * max_calls; ++i)
-    if (hipEventCreate(&ctx->ev[i]) != hipSuccess) {
+    if (hipEventCreateWithFlags(&ctx->ev[i], hipEventDisableSystemFence) != hipSuccess) {
       free_events(ctx);
       return SV_EHIP;
     }

@@ -42,7 +42,7 @@ struct Params {
   float *dbg_p_draft;
   float *dbg_probs;
   // scratch
-  float2 *chunk_tab;           // [max_rows, nc_stride]: (m_c, s_c) or (m_c, argmax_c)
+  float2 *chunk_tab;           // [max_rows, nc_stride]: (r_c, s_c)
   float4 *row_info;            // [max_rows]: (m, s, argmax bits, state bits)
   int4 *res_req;               // [max_reqs]: (row g*, position j, draft d_j, epoch)
   float *res_tab;              // [max_reqs, nc_stride] residual chunk masses

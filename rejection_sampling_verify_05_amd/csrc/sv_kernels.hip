@@ -332,7 +332,7 @@ __device__ __forceinline__ void load_chunk16(const Params &p, int g, int c, floa
   }
 }
 
-// Wave-level chunk race of row g over its chunk table (W_c = s_c exp2(a (m_c - m))),
+// Wave-level chunk race of row g over its chunk table (W_c = s_c exp2(a (r_c - m))),
 // chunk `skip` left out.  Lane l draws the words of chunks 4l..4l+3.
 // 1/E of the chunk race for a wave's first 256 chunks of row g: lane l holds
 // chunks 4l..4l+3 (one Philox block).  Depends only on the row, so it can be
@@ -349,7 +349,7 @@ __device__ __forceinline__ ChunkNoise chunk_noise(const Params &p, int g) {
   return n;
 }
 
-// Wave-level chunk race of row g over its chunk table (W_c = s_c exp2(a (m_c - m))),
+// Wave-level chunk race of row g over its chunk table (W_c = s_c exp2(a (r_c - m))),
 // chunk `skip` left out; scores W_c / E_c = W_c * (1/E_c), with 1/E from cn for
 // the first 256 chunks.  *rskip receives 1/E of chunk skip (if skip >= 0).
 template <class EF>
@@ -386,7 +386,7 @@ __device__ __forceinline__ ArgMax wave_chunk_race(const Params &p, int g, EF ent
 }
 
 // Token race over chunk c of row g whose raw logits are in LDS (zs, token
-// order): weights exp2(fma(z', a, -hi)) on the processed z' (hi = a m_c; a
+// order): weights exp2(fma(z', a, -hi)) on the processed z' (hi = a r_c; a
 // factor common to the chunk cancels), token `skip` left out.  Thread t takes
 // tokens 4t..4t+3 (one Philox block).  All threads call it; -1 if no token has
 // weight.
@@ -432,7 +432,8 @@ struct RowSpec {
 };
 
 // Row statistics of row i from its chunk table (dense) or candidates (compact):
-// maximum m and Σ exp2(a (z - m)); greedy dense rows also get the lowest
+// scale m (the largest chunk reference r_c; the row maximum for greedy rows and
+// compact rows) and Σ exp2(a (z - m)); greedy dense rows also get the lowest
 // chunk holding the maximum.  One wave; results uniform.
 template <class EF>
 __device__ __forceinline__ void row_stats(const Params &p, const Req &q, int g, int st, bool greedy, EF ent,
@@ -485,28 +486,23 @@ __device__ __forceinline__ void spec_issue(const Params &p, const Req &q, int i,
 }
 
 // After the loads of spec_issue: z_d and the mass of d's chunk without d, in
-// the chunk entry's scale (exp2(fma(z, a, -hi)) exp2(-lo), a m_c = hi + lo).
+// the scale of that chunk's table entry r = ent(c_d).x:
+// exp2(fma(z, a, -hi)) exp2(-lo) with a r = hi + lo.
 __device__ __forceinline__ void spec_draft_record(const Params &p, const Req &q, int d, const Proc &pr,
-                                                  const RowSpec &rs, float &zd, float &sx) {
+                                                  const RowSpec &rs, float ref, float &zd, float &sx) {
   const int lane = threadIdx.x & 63;
-  float z[16];
-  float mx = kNegInf, zl = kNegInf;
+  const float a = q.a, hi = a * ref, lo = __builtin_fmaf(a, ref, -hi);
+  float acc = 0.0f, zl = kNegInf;
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
     const int x = c16_tok(rs.cd, e, lane);
-    z[e] = x < p.V ? apply_proc(rs.zx[e], x, pr) : kNegInf;
-    mx = fmaxf(mx, z[e]);
-    if (x == d) zl = z[e];
+    const float z = x < p.V ? apply_proc(rs.zx[e], x, pr) : kNegInf;
+    if (x == d)
+      zl = z;
+    else
+      acc += exp2_acc(__builtin_fmaf(z, a, -hi));
   }
-  const float mc = wave_max(mx);
-  const float a = q.a, hi = a * mc, lo = __builtin_fmaf(a, mc, -hi);
-  float acc = 0.0f;
-  if (mc > kNegInf) {
-#pragma unroll
-    for (int e = 0; e < 16; ++e)
-      if (c16_tok(rs.cd, e, lane) != d) acc += exp2_acc(__builtin_fmaf(z[e], a, -hi));
-  }
-  sx = mc > kNegInf ? wave_sum(acc) * exp2_acc(-lo) : 0.0f;
+  sx = ref > kNegInf ? wave_sum(acc) * exp2_acc(-lo) : 0.0f;
   zd = wave_max(zl);
 }
 
@@ -658,7 +654,7 @@ __device__ __forceinline__ void request_epilogue(const Params &p, const Req &q, 
       }
     } else if (st < 0 && spec && (!p.draft_probs || i == K)) {
       spec_issue(p, q, i, d, m, ent, rs, cn);
-      if (rs.cd >= 0) spec_draft_record(p, q, d, pr, rs, zd, sx);
+      if (rs.cd >= 0) spec_draft_record(p, q, d, pr, rs, ent(rs.cd).x, zd, sx);
       spec_publish(rs, wave, sh);
     } else if (valid_d) {
       // single loads: z_d (and q(d)) for the accept test
@@ -794,7 +790,7 @@ __device__ __forceinline__ void request_epilogue(const Params &p, const Req &q, 
       spec_issue(p, q, j, dj, m, entj, rs, chunk_noise(p, q.g0 + j));
       float zd = kNegInf;
       sxj = 0.0f;
-      if (rs.cd >= 0) spec_draft_record(p, q, dj, pr, rs, zd, sxj);
+      if (rs.cd >= 0) spec_draft_record(p, q, dj, pr, rs, entj(rs.cd).x, zd, sxj);
       spec_publish(rs, 0, sh);
       if (lane == 0) sh.sx[j] = sxj;
     }
@@ -822,6 +818,7 @@ struct RowInfo {
   const int32_t *counts;
 };
 constexpr int kRowCache = kSliceRows;  // rows of a slice looked up before streaming
+constexpr int kFastDepth = 3;  // chunks in flight per wave in the fast pass (2, 4, 5: slower)
 
 __device__ __forceinline__ RowInfo row_info_of(const Params &p, const Req &q, int g) {
   RowInfo ri;
@@ -1020,8 +1017,18 @@ __device__ __forceinline__ void advance_chunk(int &g, int &c, int by, int NC) {
   }
 }
 
+// Table entry of one chunk: (r, sum over its tokens of exp2(a (z - r))).  For
+// a sampled row the reference r is the exact maximum of the first chunk of
+// the row that this wave streamed (`ref`); later chunks then need only the
+// sum, unless it reaches 2^20, in which case their exact maximum is taken and
+// becomes the reference.  With m = max over the row's entries of r,
+// a (z - m) <= 20 for every token, so every later use stays finite, and the
+// exponent of each term is rounded with an absolute error of at most
+// 20 * 2^-24.  Greedy rows (a = 0) always take the exact maximum: their
+// argmax search needs it.
 template <int DT>
-__device__ __forceinline__ void fast_chunk(const Params &p, const RowInfo &ri, int c, const u32x4 (&v)[Layout<DT>::kVec]) {
+__device__ __forceinline__ void fast_chunk(const Params &p, const RowInfo &ri, int c,
+                                           const u32x4 (&v)[Layout<DT>::kVec], float &ref) {
   using L = Layout<DT>;
   const int lane = threadIdx.x & 63;
   float z[16];
@@ -1032,19 +1039,31 @@ __device__ __forceinline__ void fast_chunk(const Params &p, const RowInfo &ri, i
     for (int e = 0; e < 16; ++e)
       if (c * kChunk + L::local(e, lane) >= p.V) z[e] = kNegInf;
   }
-  float mx = z[0];
-#pragma unroll
-  for (int e = 1; e < 16; ++e) mx = fmaxf(mx, z[e]);
-  const float mc = wave_max(mx);
-  // exp2(a (z - mc)) = exp2(fma(z, a, -hi)) * exp2(-lo), a * mc = hi + lo
-  // exactly; greedy rows carry a = 0 and only their maxima are used.
   const float a = ri.a;
-  const float hi = a * mc;
-  const float lo = __builtin_fmaf(a, mc, -hi);
-  float sa = 0.0f;
+  float2 entry;
+  bool done = false;
+  if (ref > kNegInf) {
+    // exp2(a (z - r)) = exp2(fma(z, a, -hi)) * exp2(-lo), a * r = hi + lo exactly
+    const float hi = a * ref, lo = __builtin_fmaf(a, ref, -hi);
+    float sa = 0.0f;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) sa += exp2_acc(__builtin_fmaf(z[e], a, -hi));
-  const float2 entry = make_float2(mc, mc > kNegInf ? wave_sum(sa) * exp2_acc(-lo) : 0.0f);
+    for (int e = 0; e < 16; ++e) sa += exp2_acc(__builtin_fmaf(z[e], a, -hi));
+    const float sr = wave_sum(sa);
+    entry = make_float2(ref, sr * exp2_acc(-lo));
+    done = sr < 0x1p20f;
+  }
+  if (!done) {
+    float mx = z[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, z[e]);
+    const float mc = wave_max(mx);
+    const float hi = a * mc, lo = __builtin_fmaf(a, mc, -hi);
+    float sa = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sa += exp2_acc(__builtin_fmaf(z[e], a, -hi));
+    entry = make_float2(mc, mc > kNegInf ? wave_sum(sa) * exp2_acc(-lo) : 0.0f);
+    if (a > 0.0f) ref = mc;
+  }
   if (lane == 0 && ri.mode != kModeInvalid) p.chunk_tab[(int64_t)ri.g * p.nc_stride + c] = entry;
 }
 
@@ -1052,6 +1071,7 @@ template <int DT>
 __global__ __launch_bounds__(kThreads) void stats_fast_kernel(Params p) {
   using L = Layout<DT>;
   constexpr int NV = L::kVec;
+  constexpr int D = kFastDepth;  // chunks in flight per wave
   __shared__ StatsShared sh;
   const int wave = uni((int)(threadIdx.x >> 6));
   const int N = p.R * p.NC;
@@ -1063,20 +1083,23 @@ __global__ __launch_bounds__(kThreads) void stats_fast_kernel(Params p) {
   const int len = end - start;
   const int n = wave < len ? (len - wave + kWaves - 1) / kWaves : 0;
 
-  int ga = (start + wave) / p.NC, ca = start + wave - ga * p.NC;
-  int gb = ga, cb = ca, gc = ga, cc = ca;
-  advance_chunk(gb, cb, kWaves, p.NC);
-  advance_chunk(gc, cc, 2 * kWaves, p.NC);
-  // The first three loads are unconditional (a wave with fewer chunks reads
-  // the slice's first chunk instead), so that every path into the loop has the
-  // same loads in flight and the waits stay three chunks deep.
-  u32x4 A[NV], Bv[NV], Cv[NV];
-  fast_load<DT>(p, n > 0 ? ga : g_first, n > 0 ? ca : 0, A);
-  fast_load<DT>(p, n > 1 ? gb : g_first, n > 1 ? cb : 0, Bv);
-  fast_load<DT>(p, n > 2 ? gc : g_first, n > 2 ? cc : 0, Cv);
+  // The first D loads are unconditional (a wave with fewer chunks reads the
+  // slice's first chunk instead), so that every path into the loop has the
+  // same loads in flight and the waits stay D chunks deep.
+  u32x4 buf[D][NV];
+  int gs[D], cs[D];
+  gs[0] = (start + wave) / p.NC;
+  cs[0] = start + wave - gs[0] * p.NC;
+#pragma unroll
+  for (int s = 1; s < D; ++s) {
+    gs[s] = gs[s - 1];
+    cs[s] = cs[s - 1];
+    advance_chunk(gs[s], cs[s], kWaves, p.NC);
+  }
+#pragma unroll
+  for (int s = 0; s < D; ++s) fast_load<DT>(p, n > s ? gs[s] : g_first, n > s ? cs[s] : 0, buf[s]);
 
-  // Request lookups for the slice's rows (overlapping the loads); q(d) is
-  // fetched here too so that the loop issues no dependent loads.
+  // Request lookups for the slice's rows (overlapping the loads).
   if (wave < nrows) {
     const int g = g_first + wave;
     const RowInfo ri = row_info_of(p, lookup_req(p, g), g);
@@ -1084,50 +1107,35 @@ __global__ __launch_bounds__(kThreads) void stats_fast_kernel(Params p) {
   }
   __syncthreads();
 
-  RowInfo cur = uniform_row(sh.rows[ga - g_first]);
+  RowInfo cur = uniform_row(sh.rows[gs[0] - g_first]);
+  float ref = kNegInf;  // this wave's reference for row cur.g (uniform)
+  auto chunk = [&](int s) {
+    if (gs[s] != cur.g) {
+      cur = uniform_row(sh.rows[gs[s] - g_first]);
+      ref = kNegInf;
+    }
+    fast_chunk<DT>(p, cur, cs[s], buf[s], ref);
+  };
   int k = 0;
-  for (; k + 5 < n; k += 3) {
-    if (ga != cur.g) cur = uniform_row(sh.rows[ga - g_first]);
-    fast_chunk<DT>(p, cur, ca, A);
-    advance_chunk(ga, ca, 3 * kWaves, p.NC);
-    fast_load<DT>(p, ga, ca, A);
-    if (gb != cur.g) cur = uniform_row(sh.rows[gb - g_first]);
-    fast_chunk<DT>(p, cur, cb, Bv);
-    advance_chunk(gb, cb, 3 * kWaves, p.NC);
-    fast_load<DT>(p, gb, cb, Bv);
-    if (gc != cur.g) cur = uniform_row(sh.rows[gc - g_first]);
-    fast_chunk<DT>(p, cur, cc, Cv);
-    advance_chunk(gc, cc, 3 * kWaves, p.NC);
-    fast_load<DT>(p, gc, cc, Cv);
-  }
-  // Drain: at most 5 chunks left, loads only while in range.
+  for (; k + 2 * D - 1 < n; k += D) {
 #pragma unroll
-  for (int t = 0; t < 6; ++t) {
-    if (k + t >= n) break;
-    if (t % 3 == 0) {
-      if (ga != cur.g) cur = uniform_row(sh.rows[ga - g_first]);
-      fast_chunk<DT>(p, cur, ca, A);
-      if (k + t + 3 < n) {
-        advance_chunk(ga, ca, 3 * kWaves, p.NC);
-        fast_load<DT>(p, ga, ca, A);
-      }
-    } else if (t % 3 == 1) {
-      if (gb != cur.g) cur = uniform_row(sh.rows[gb - g_first]);
-      fast_chunk<DT>(p, cur, cb, Bv);
-      if (k + t + 3 < n) {
-        advance_chunk(gb, cb, 3 * kWaves, p.NC);
-        fast_load<DT>(p, gb, cb, Bv);
-      }
-    } else {
-      if (gc != cur.g) cur = uniform_row(sh.rows[gc - g_first]);
-      fast_chunk<DT>(p, cur, cc, Cv);
-      if (k + t + 3 < n) {
-        advance_chunk(gc, cc, 3 * kWaves, p.NC);
-        fast_load<DT>(p, gc, cc, Cv);
-      }
+    for (int s = 0; s < D; ++s) {
+      chunk(s);
+      advance_chunk(gs[s], cs[s], D * kWaves, p.NC);
+      fast_load<DT>(p, gs[s], cs[s], buf[s]);
     }
   }
-
+  // Drain: at most 2D - 1 chunks left, loads only while in range.
+#pragma unroll
+  for (int t = 0; t < 2 * D; ++t) {
+    if (k + t >= n) break;
+    const int s = t % D;
+    chunk(s);
+    if (k + t + D < n) {
+      advance_chunk(gs[s], cs[s], D * kWaves, p.NC);
+      fast_load<DT>(p, gs[s], cs[s], buf[s]);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------

@@ -185,3 +185,34 @@ def test_strided_logits_rows():
         g = run_gpu(ctx, inp)
     n_margin, bad = check_requests(g, inp, range(8))
     assert not bad, "\n".join(bad)
+
+
+@pytest.mark.parametrize("draft_probs", [False, True])
+def test_chunk_scale_ramps(draft_probs):
+    # Rows whose chunks differ in mass by far more than 2^20: logits ramp up or
+    # down by 6 per 1024-token chunk, plus one row with a single spiked chunk.
+    # bf16 with V a multiple of 8 takes the fast streaming pass, which then
+    # meets chunks far above and far below the first chunk it saw in a row.
+    w = wl.CONFIGS["3"].with_(B=8, V=40000 + 8, ragged=False, K=2)
+    if draft_probs:
+        w = wl.CONFIGS["1"].with_(B=8, K=2, V=40000 + 8, dtype=torch.bfloat16)
+    inp = wl.make_inputs(w, DEV)
+    R, V = inp["R"], inp["V"]
+    chunk = torch.arange(V, device=DEV) // 1024
+    lg = inp["logits"].float()
+    for r in range(R):
+        kind = r % 3
+        if kind == 0:
+            lg[r] += 6.0 * chunk
+        elif kind == 1:
+            lg[r] -= 6.0 * chunk
+        else:
+            lg[r, (chunk == 17 + r % 5)] += 60.0
+    inp["logits"] = lg.to(inp["logits"].dtype)
+    with ctx_for(inp) as ctx:
+        for seed, off in [(0, 0), (99, 5)]:
+            g = run_gpu(ctx, inp, seed=seed, offset=off, dbg_probs=True)
+            assert g["err"] == 0
+            n_margin, bad = check_requests(g, inp, range(inp["B"]), seed, off, probs=True)
+            say(f"ramps draft_probs={draft_probs} seed {seed}: margin {n_margin}, mismatches {len(bad)}")
+            assert not bad, "\n".join(bad[:10])
