@@ -27,8 +27,19 @@ RACE_CHUNK = 1024
 TAG_ACCEPT, TAG_CHUNK, TAG_TOKEN = 0, 1, 2
 F32, BF16 = 0, 1
 ERR_CU, ERR_TEMPERATURE, ERR_PENALTY, ERR_ROW, ERR_SLOT, ERR_OFFSET = 1, 2, 4, 8, 16, 32
+ERR_TOP_P = 64
 
 _lib = None
+
+
+class _ReqOpts(ctypes.Structure):
+    _fields_ = [("top_k", ctypes.c_int32), ("theta", ctypes.c_void_p), ("freq", ctypes.c_float),
+                ("pres", ctypes.c_float), ("top_p", ctypes.c_float), ("top_p_shift", ctypes.c_double)]
+
+
+class _BatchOpts(ctypes.Structure):
+    _fields_ = [("freq", ctypes.c_void_p), ("pres", ctypes.c_void_p), ("top_p", ctypes.c_void_p),
+                ("synthetic_rates", ctypes.c_void_p)]
 
 
 def build(force: bool = True) -> str:
@@ -83,6 +94,20 @@ def lib():
         L.orc_verify_batch.argtypes = [P, ctypes.c_int, i64, i32, i32, P, i64, P, P, i32, i32,
                                        P, P, P, P, P, i32, u64, u64, i32, P, i32, P, P, P, P]
         L.orc_verify_batch.restype = u32
+        L.orc_frequency_presence_penalty.argtypes = [P, P, i32, f32, f32]
+        L.orc_frequency_presence_penalty.restype = None
+        L.orc_top_p_keep.argtypes = [P, i32, f64, f64, P, P]
+        L.orc_top_p_keep.restype = i32
+        L.orc_synthetic_rates.argtypes = [f64, i32, P]
+        L.orc_synthetic_rates.restype = ctypes.c_int
+        L.orc_prepare_request_ex.argtypes = [P, ctypes.c_int, i64, i32, i32, f32, P, P, P, P, P]
+        L.orc_prepare_request_ex.restype = ctypes.c_int
+        L.orc_decide_request_ex.argtypes = [P, P, i32, i32, f32, P, P, i64, u32, u64, u32, i32, P,
+                                            P, P, P, P]
+        L.orc_decide_request_ex.restype = f64
+        L.orc_verify_batch_ex.argtypes = [P, ctypes.c_int, i64, i32, i32, P, i64, P, P, i32, i32,
+                                          P, P, P, P, P, i32, u64, u64, i32, P, P, i32, P, P, P, P]
+        L.orc_verify_batch_ex.restype = u32
         L.orc_post_update.argtypes = [P, P, P, i32, P, P, i32, i32, i32, P, P, P]
         L.orc_post_update.restype = u32
         _lib = L
@@ -146,6 +171,29 @@ def top_k_mask(z, k: int) -> np.ndarray:
     return zz
 
 
+def frequency_presence_penalty(z, counts, freq: float, pres: float) -> np.ndarray:
+    zz = _c(z, np.float32).copy()
+    cc = _c(counts, np.int32)
+    lib().orc_frequency_presence_penalty(_ptr(zz), _ptr(cc), zz.size, freq, pres)
+    return zz
+
+
+def top_p_keep(p, top_p: float, shift: float = 0.0):
+    """Returns (keep bool array, margin, number kept) of the nucleus set of p."""
+    pp = _c(p, np.float64)
+    keep = np.zeros(pp.size, dtype=np.uint8)
+    m = ctypes.c_double(0.0)
+    n = lib().orc_top_p_keep(_ptr(pp), pp.size, float(top_p), float(shift), _ptr(keep), ctypes.byref(m))
+    return keep.astype(bool), float(m.value), int(n)
+
+
+def synthetic_rates(L: float, K: int) -> np.ndarray:
+    r = np.zeros(max(K, 1), dtype=np.float32)
+    if lib().orc_synthetic_rates(float(L), int(K), _ptr(r)) != 0:
+        raise ValueError("mean acceptance length outside [1, K + 1]")
+    return r[:K]
+
+
 def argmax(z) -> int:
     zz = _c(z, np.float32)
     return int(lib().orc_argmax(_ptr(zz), zz.size))
@@ -168,22 +216,34 @@ def race(w, C: int, seed: int, offset: int, g: int):
 
 
 # ---- one request -----------------------------------------------------------
-def prepare_request(rows, T: float, top_k: int = 0, theta=None, counts=None):
-    """rows: [K+1, V] float32, or uint16 bf16 bits.  Returns (P [K+1,V] f64, amax, err)."""
+def prepare_request_ex(rows, T: float, top_k: int = 0, theta=None, counts=None, freq: float = 0.0,
+                       pres: float = 0.0, top_p: float = 1.0, top_p_shift: float = 0.0):
+    """rows: [K+1, V] float32, or uint16 bf16 bits.  Returns (P [K+1,V] f64, amax,
+    err, top-p margin per row)."""
     dtype = BF16 if rows.dtype == np.uint16 else F32
     rr = np.ascontiguousarray(rows)
     n, V = rr.shape
     P = np.zeros((n, V), dtype=np.float64)
     amax = np.zeros(n, dtype=np.int32)
+    tm = np.zeros(n, dtype=np.float64)
     th = None if theta is None else np.array([theta], dtype=np.float32)
     cc = _c(counts, np.int32)
-    err = lib().orc_prepare_request(_ptr(rr), dtype, V, n - 1, V, float(T), int(top_k),
-                                    _ptr(th), _ptr(cc), _ptr(P), _ptr(amax))
-    return P, amax, int(err)
+    o = _ReqOpts(int(top_k), None if th is None else th.ctypes.data, float(freq), float(pres),
+                 float(top_p), float(top_p_shift))
+    err = lib().orc_prepare_request_ex(_ptr(rr), dtype, V, n - 1, V, float(T), ctypes.byref(o),
+                                       _ptr(cc), _ptr(P), _ptr(amax), _ptr(tm))
+    return P, amax, int(err), tm
+
+
+def prepare_request(rows, T: float, top_k: int = 0, theta=None, counts=None, **kw):
+    """rows: [K+1, V] float32, or uint16 bf16 bits.  Returns (P [K+1,V] f64, amax, err).
+    Keyword settings as prepare_request_ex (freq, pres, top_p, top_p_shift)."""
+    P, amax, err, _ = prepare_request_ex(rows, T, top_k, theta, counts, **kw)
+    return P, amax, err
 
 
 def decide_request(P, amax, T: float, draft_ids, draft_probs=None, g0: int = 0, seed: int = 0,
-                   offset: int = 0, C: int = RACE_CHUNK):
+                   offset: int = 0, C: int = RACE_CHUNK, synthetic_rates=None):
     """Returns (tokens list, num_sampled, num_rejected, margin, p_draft)."""
     n, V = P.shape
     K = n - 1
@@ -191,20 +251,24 @@ def decide_request(P, amax, T: float, draft_ids, draft_probs=None, g0: int = 0, 
     am = _c(amax, np.int32)
     d = _c(np.asarray(draft_ids).reshape(-1), np.int32) if K > 0 else np.zeros(1, np.int32)
     q = _c(draft_probs, np.float32)
+    sr = None if synthetic_rates is None else np.ascontiguousarray(synthetic_rates, np.float32)
+    if sr is not None:
+        assert sr.size >= K
     tokens = np.full(K + 1, -1, dtype=np.int32)
     ns = ctypes.c_int32(0)
     nr = ctypes.c_int32(0)
     pd = np.zeros(max(K, 1), dtype=np.float32)
-    mg = lib().orc_decide_request(_ptr(PP), _ptr(am), K, V, float(T), _ptr(d), _ptr(q),
-                                  V if q is None else q.shape[-1], g0, seed, offset, C,
-                                  _ptr(tokens), ctypes.byref(ns), ctypes.byref(nr), _ptr(pd))
+    mg = lib().orc_decide_request_ex(_ptr(PP), _ptr(am), K, V, float(T), _ptr(d), _ptr(q),
+                                     V if q is None else q.shape[-1], g0, seed, offset, C, _ptr(sr),
+                                     _ptr(tokens), ctypes.byref(ns), ctypes.byref(nr), _ptr(pd))
     return tokens[: ns.value].tolist(), ns.value, nr.value, float(mg), pd[:K]
 
 
 # ---- whole call ------------------------------------------------------------
 def verify_batch(logits, cu, draft_ids, temperature, draft_probs=None, top_k=None,
                  rep_penalty=None, idx_mapping=None, counts=None, seed: int = 0,
-                 offset: int = 0, max_k=None, out_stride=None, C: int = RACE_CHUNK):
+                 offset: int = 0, max_k=None, out_stride=None, C: int = RACE_CHUNK,
+                 freq=None, pres=None, top_p=None, synthetic_rates=None):
     """Whole verify call on host arrays.  logits: [R, V] float32 or uint16 (bf16
     bits).  Returns a dict with tokens [B, out_stride], num_sampled, num_rejected,
     margin [B], p_draft [D] and the error mask."""
@@ -231,10 +295,16 @@ def verify_batch(logits, cu, draft_ids, temperature, draft_probs=None, top_k=Non
     nr = np.zeros(B, dtype=np.int32)
     mg = np.zeros(B, dtype=np.float64)
     pd = np.zeros(max(D, 1), dtype=np.float32)
-    err = lib().orc_verify_batch(_ptr(lg), dtype, V, R, V, _ptr(q), V, _ptr(d), _ptr(cu), B,
-                                 int(max_k), _ptr(T), _ptr(tk), _ptr(rp), _ptr(im), _ptr(cc), S,
-                                 seed, offset, C, _ptr(tokens), out_stride, _ptr(ns), _ptr(nr),
-                                 _ptr(mg), _ptr(pd))
+    fq, pr, tp = _c(freq, np.float32), _c(pres, np.float32), _c(top_p, np.float32)
+    sr = None
+    if synthetic_rates is not None:
+        sr = np.zeros(max(int(max_k), 1), np.float32)
+        sr[: len(synthetic_rates)] = synthetic_rates
+    x = _BatchOpts(*(None if a is None else a.ctypes.data for a in (fq, pr, tp, sr)))
+    err = lib().orc_verify_batch_ex(_ptr(lg), dtype, V, R, V, _ptr(q), V, _ptr(d), _ptr(cu), B,
+                                    int(max_k), _ptr(T), _ptr(tk), _ptr(rp), _ptr(im), _ptr(cc), S,
+                                    seed, offset, C, ctypes.byref(x), _ptr(tokens), out_stride,
+                                    _ptr(ns), _ptr(nr), _ptr(mg), _ptr(pd))
     return dict(tokens=tokens, num_sampled=ns, num_rejected=nr, margin=mg, p_draft=pd[:D],
                 err=int(err))
 

@@ -139,6 +139,74 @@ int32_t orc_argmax(const float *z, int32_t V) {
   return best;
 }
 
+/* Frequency and presence penalties from the output histogram.  The frequency
+ * form is the walk-through of page 1 (penalties section: with penalty 0.5 a
+ * token seen once loses 0.5, seen twice loses 1.0): z -= freq * count, the
+ * product rounded to fp32 first.  The presence penalty subtracts a constant
+ * from every token seen at least once (a reading: the pages name no formula). */
+void orc_frequency_presence_penalty(float *z, const int32_t *counts, int32_t V, float freq,
+                                    float pres) {
+  for (int32_t x = 0; x < V; ++x) {
+    if (counts[x] > 0) {
+      float t = freq * (float)counts[x];
+      z[x] = z[x] - t;
+      z[x] = z[x] - pres;
+    }
+  }
+}
+
+static const double *g_sort_p; /* qsort context: probabilities, descending */
+static int cmp_idx_p_desc(const void *a, const void *b) {
+  int32_t ia = *(const int32_t *)a, ib = *(const int32_t *)b;
+  double pa = g_sort_p[ia], pb = g_sort_p[ib];
+  if (pa != pb) return pa < pb ? 1 : -1;
+  return (ia > ib) - (ia < ib);
+}
+
+/* Nucleus set: walk the distinct probability values from the largest down,
+ * carrying the mass of everything strictly above; a value is kept while that
+ * mass is below top_p (+ shift).  Ties share one decision. */
+int32_t orc_top_p_keep(const double *p, int32_t V, double top_p, double shift, uint8_t *keep,
+                       double *margin) {
+  int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * (size_t)V);
+  for (int32_t x = 0; x < V; ++x) idx[x] = x;
+  g_sort_p = p;
+  qsort(idx, (size_t)V, sizeof(int32_t), cmp_idx_p_desc);
+  double above = 0.0, mg = INFINITY;
+  int32_t n = 0;
+  for (int32_t i = 0; i < V;) {
+    int32_t j = i;
+    while (j < V && p[idx[j]] == p[idx[i]]) ++j;
+    int kept = p[idx[i]] > 0.0 && (i == 0 || above < top_p + shift); /* the top value always stays */
+    if (p[idx[i]] > 0.0 && fabs(above - top_p) < mg) mg = fabs(above - top_p);
+    for (int32_t t = i; t < j; ++t) {
+      keep[idx[t]] = (uint8_t)kept;
+      n += kept;
+    }
+    for (int32_t t = i; t < j; ++t) above += p[idx[t]];
+    i = j;
+  }
+  free(idx);
+  if (margin) *margin = mg;
+  return n;
+}
+
+/* Synthetic acceptance (page 3, 7.2): a target mean acceptance length L in
+ * [1, K + 1] becomes the minimum-variance per-position rates.  The number of
+ * accepted drafts N has mean L - 1; its variance is smallest when N takes only
+ * the two integers around L - 1, which gives unconditional rates P(N >= i) of
+ * 1 up to floor(L - 1), then the fractional part, then 0. */
+int orc_synthetic_rates(double L, int32_t K, float *rates) {
+  if (!(L >= 1.0) || !(L <= (double)K + 1.0)) return -1;
+  double n0 = floor(L - 1.0);
+  double f = (L - 1.0) - n0;
+  for (int32_t i = 1; i <= K; ++i) {
+    double a = (double)i <= n0 ? 1.0 : ((double)i == n0 + 1.0 ? f : 0.0);
+    rates[i - 1] = (float)a;
+  }
+  return 0;
+}
+
 /* Temperature-scaled softmax in fp64 (page 2, 8.2). */
 int orc_softmax(const float *z, int32_t V, double T, double *p) {
   double m = -INFINITY;
@@ -228,20 +296,33 @@ static void load_row(const void *rows, int dtype, int64_t stride, int32_t i, int
   }
 }
 
-/* Order of processing (page 2, 8.2): logits processors (the repetition penalty)
- * -> sampling constraints (top-k) -> temperature and softmax.  Temperature 0
- * selects the greedy rule, which needs only the argmax of the processed logits. */
-int orc_prepare_request(const void *rows, int dtype, int64_t stride, int32_t K, int32_t V,
-                        float T, int32_t top_k, const float *theta, const int32_t *counts,
-                        double *P, int32_t *amax) {
+/* Order of processing (page 2, 8.2): logits processors (the repetition,
+ * frequency and presence penalties) -> sampling constraints (top-k) ->
+ * temperature and softmax -> top-p on the probabilities (page 4: top-p is
+ * clamped to [1e-6, 1], 1 meaning no restriction), renormalised over the kept
+ * tokens.  Temperature 0 selects the greedy rule, which needs only the argmax
+ * of the processed logits (top-p never removes the argmax). */
+int orc_prepare_request_ex(const void *rows, int dtype, int64_t stride, int32_t K, int32_t V,
+                           float T, const orc_req_opts *o, const int32_t *counts, double *P,
+                           int32_t *amax, double *topp_margin) {
+  orc_req_opts none = {0, NULL, 0.0f, 0.0f, 1.0f, 0.0};
+  if (!o) o = &none;
+  for (int32_t i = 0; i <= K && topp_margin; ++i) topp_margin[i] = INFINITY;
   if (!(T >= 0.0f) || !isfinite(T)) return ORC_ERR_TEMPERATURE;
-  if (theta && !(isfinite(*theta) && *theta > 0.0f)) return ORC_ERR_PENALTY;
+  if (o->theta && !(isfinite(*o->theta) && *o->theta > 0.0f)) return ORC_ERR_PENALTY;
+  if (!isfinite(o->freq) || !isfinite(o->pres)) return ORC_ERR_PENALTY;
+  if (isnan(o->top_p)) return ORC_ERR_TOP_P;
+  const float top_p = o->top_p < 1e-6f ? 1e-6f : o->top_p;
+  const int use_top_p = top_p < 1.0f && T > 0.0f;
   int err = 0;
   float *z = (float *)malloc(sizeof(float) * (size_t)V);
+  uint8_t *keep = use_top_p ? (uint8_t *)malloc((size_t)V) : NULL;
   for (int32_t i = 0; i <= K; ++i) {
     load_row(rows, dtype, stride, i, V, z);
-    if (theta && counts && *theta != 1.0f) orc_repetition_penalty(z, counts, V, *theta);
-    orc_top_k_mask(z, V, top_k);
+    if (o->theta && counts && *o->theta != 1.0f) orc_repetition_penalty(z, counts, V, *o->theta);
+    if (counts && (o->freq != 0.0f || o->pres != 0.0f))
+      orc_frequency_presence_penalty(z, counts, V, o->freq, o->pres);
+    orc_top_k_mask(z, V, o->top_k);
     amax[i] = orc_argmax(z, V);
     double *p = P + (int64_t)i * V;
     if (!isfinite(z[amax[i]])) {
@@ -251,29 +332,67 @@ int orc_prepare_request(const void *rows, int dtype, int64_t stride, int32_t K, 
     if (T == 0.0f) {
       for (int32_t x = 0; x < V; ++x) p[x] = 0.0;
       p[amax[i]] = 1.0;
-    } else {
-      err |= orc_softmax(z, V, (double)T, p);
+      continue;
+    }
+    err |= orc_softmax(z, V, (double)T, p);
+    if (use_top_p) {
+      double mg = INFINITY;
+      orc_top_p_keep(p, V, (double)top_p, o->top_p_shift, keep, &mg);
+      if (topp_margin) topp_margin[i] = mg;
+      double s = 0.0;
+      for (int32_t x = 0; x < V; ++x)
+        if (keep[x]) s += p[x];
+      for (int32_t x = 0; x < V; ++x) p[x] = keep[x] ? p[x] / s : 0.0;
     }
   }
+  free(keep);
   free(z);
   return err;
 }
 
-double orc_decide_request(const double *P, const int32_t *amax, int32_t K, int32_t V, float T,
-                          const int32_t *draft_ids, const float *draft_probs, int64_t dstride,
-                          uint32_t g0, uint64_t seed, uint32_t offset, int32_t C,
-                          int32_t *tokens, int32_t *num_sampled, int32_t *num_rejected,
-                          float *p_draft) {
+int orc_prepare_request(const void *rows, int dtype, int64_t stride, int32_t K, int32_t V,
+                        float T, int32_t top_k, const float *theta, const int32_t *counts,
+                        double *P, int32_t *amax) {
+  orc_req_opts o = {top_k, theta, 0.0f, 0.0f, 1.0f, 0.0};
+  return orc_prepare_request_ex(rows, dtype, stride, K, V, T, &o, counts, P, amax, NULL);
+}
+
+/* Synthetic accept test of draft position i (0-based): unconditional rates a
+ * of positions 1..K, a_0 = 1; accept iff u * a_i <= a_{i+1}, i.e. with the
+ * conditional probability a_{i+1} / a_i, so that position i + 1 is reached and
+ * accepted with probability a_{i+1} (page 3, 7.2).  The product of two fp32
+ * values is exact in fp64. */
+static int synthetic_accept(const float *a, int32_t i, double u) {
+  double prev = i == 0 ? 1.0 : (double)a[i - 1];
+  return u * prev <= (double)a[i];
+}
+
+double orc_decide_request_ex(const double *P, const int32_t *amax, int32_t K, int32_t V, float T,
+                             const int32_t *draft_ids, const float *draft_probs, int64_t dstride,
+                             uint32_t g0, uint64_t seed, uint32_t offset, int32_t C,
+                             const float *syn_rates, int32_t *tokens, int32_t *num_sampled,
+                             int32_t *num_rejected, float *p_draft) {
   double margin = INFINITY;
 
   if (T == 0.0f) {
     /* Greedy (page 2, 8.3): output the target argmax at each position, stop
-     * after the first position whose draft differs; bonus argmax if none did. */
+     * after the first position whose draft differs; bonus argmax if none did.
+     * In synthetic mode the rate test replaces the comparison and accepted
+     * positions output the draft itself. */
     for (int32_t i = 0; i < K; ++i)
       if (p_draft) p_draft[i] = -1.0f;
     for (int32_t i = 0; i < K; ++i) {
-      tokens[i] = amax[i];
-      if (draft_ids[i] != amax[i]) {
+      int acc;
+      if (syn_rates) {
+        int32_t d = draft_ids[i];
+        double u = orc_uniform_accept(orc_word(seed, offset, g0 + (uint32_t)i, ORC_TAG_ACCEPT, 0));
+        acc = d >= 0 && d < V && synthetic_accept(syn_rates, i, u);
+        tokens[i] = acc ? d : amax[i];
+      } else {
+        acc = draft_ids[i] == amax[i];
+        tokens[i] = amax[i];
+      }
+      if (!acc) {
         *num_sampled = i + 1;
         *num_rejected = K - i;
         return margin;
@@ -294,14 +413,22 @@ double orc_decide_request(const double *P, const int32_t *amax, int32_t K, int32
 
   /* Accept loop (page 2, 8.3 and the Q&A on min(1, p/q)): draft i is accepted
    * when it is a valid id, q(d) > 0 and p(d) >= u * q(d); q = 1 without draft
-   * probabilities (NO_DRAFT_PROBS Q&A).  The first reject ends the loop. */
+   * probabilities (NO_DRAFT_PROBS Q&A).  Synthetic mode: the rate test.  The
+   * first reject ends the loop. */
   int32_t j = K;
   for (int32_t i = 0; i < K; ++i) {
     int32_t d = draft_ids[i];
     int valid = d >= 0 && d < V;
+    double u = orc_uniform_accept(orc_word(seed, offset, g0 + (uint32_t)i, ORC_TAG_ACCEPT, 0));
+    if (syn_rates) {
+      if (!valid || !synthetic_accept(syn_rates, i, u)) {
+        j = i;
+        break;
+      }
+      continue;
+    }
     double q = 1.0;
     if (draft_probs) q = valid ? (double)draft_probs[(int64_t)i * dstride + d] : 0.0;
-    double u = orc_uniform_accept(orc_word(seed, offset, g0 + (uint32_t)i, ORC_TAG_ACCEPT, 0));
     if (!valid || !(q > 0.0)) {
       j = i;
       break;
@@ -353,20 +480,32 @@ double orc_decide_request(const double *P, const int32_t *amax, int32_t K, int32
   return margin;
 }
 
+
+double orc_decide_request(const double *P, const int32_t *amax, int32_t K, int32_t V, float T,
+                          const int32_t *draft_ids, const float *draft_probs, int64_t dstride,
+                          uint32_t g0, uint64_t seed, uint32_t offset, int32_t C,
+                          int32_t *tokens, int32_t *num_sampled, int32_t *num_rejected,
+                          float *p_draft) {
+  return orc_decide_request_ex(P, amax, K, V, T, draft_ids, draft_probs, dstride, g0, seed, offset,
+                               C, NULL, tokens, num_sampled, num_rejected, p_draft);
+}
+
 /* ------------------------------------------------------------------------ */
 /* Whole call                                                                */
 /* ------------------------------------------------------------------------ */
-uint32_t orc_verify_batch(const void *logits, int dtype, int64_t stride, int32_t num_rows,
-                          int32_t V, const float *draft_probs, int64_t dstride,
-                          const int32_t *draft_ids, const int32_t *cu, int32_t B,
-                          int32_t max_k, const float *temperature, const int32_t *top_k,
-                          const float *rep_penalty, const int32_t *idx_mapping,
-                          const int32_t *counts, int32_t num_slots, uint64_t seed,
-                          uint64_t offset, int32_t C, int32_t *out_tokens, int32_t out_stride,
-                          int32_t *num_sampled, int32_t *num_rejected, double *margin,
-                          float *p_draft) {
+uint32_t orc_verify_batch_ex(const void *logits, int dtype, int64_t stride, int32_t num_rows,
+                             int32_t V, const float *draft_probs, int64_t dstride,
+                             const int32_t *draft_ids, const int32_t *cu, int32_t B,
+                             int32_t max_k, const float *temperature, const int32_t *top_k,
+                             const float *rep_penalty, const int32_t *idx_mapping,
+                             const int32_t *counts, int32_t num_slots, uint64_t seed,
+                             uint64_t offset, int32_t C, const orc_batch_opts *x,
+                             int32_t *out_tokens, int32_t out_stride, int32_t *num_sampled,
+                             int32_t *num_rejected, double *margin, float *p_draft) {
   uint32_t err = 0;
   int32_t D = num_rows - B;
+  orc_batch_opts none = {NULL, NULL, NULL, NULL};
+  if (!x) x = &none;
   for (int32_t r = 0; r < B; ++r) {
     for (int32_t t = 0; t < out_stride; ++t) out_tokens[(int64_t)r * out_stride + t] = -1;
     num_sampled[r] = 0;
@@ -388,10 +527,14 @@ uint32_t orc_verify_batch(const void *logits, int dtype, int64_t stride, int32_t
     int32_t K = cu[r + 1] - cu[r];
     int32_t g0 = cu[r] + r;
     float T = temperature[r];
-    int32_t k = top_k ? top_k[r] : 0;
-    const float *theta = rep_penalty ? &rep_penalty[r] : NULL;
+    orc_req_opts o = {top_k ? top_k[r] : 0, rep_penalty ? &rep_penalty[r] : NULL,
+                      x->freq ? x->freq[r] : 0.0f, x->pres ? x->pres[r] : 0.0f,
+                      x->top_p ? x->top_p[r] : 1.0f, 0.0};
+    /* A valid penalty other than the identity reads the request's histogram row. */
+    int needs_counts = (o.theta && isfinite(*o.theta) && *o.theta > 0.0f && *o.theta != 1.0f) ||
+                       (isfinite(o.freq) && o.freq != 0.0f) || (isfinite(o.pres) && o.pres != 0.0f);
     const int32_t *counts_row = NULL;
-    if (theta && isfinite(*theta) && *theta > 0.0f && *theta != 1.0f) {
+    if (needs_counts) {
       int32_t slot = idx_mapping[r];
       if (slot < 0 || slot >= num_slots) {
         err |= ORC_ERR_SLOT;
@@ -403,21 +546,36 @@ uint32_t orc_verify_batch(const void *logits, int dtype, int64_t stride, int32_t
     int32_t *amax = (int32_t *)malloc(sizeof(int32_t) * (size_t)(K + 1));
     const void *rows = dtype == ORC_BF16 ? (const void *)((const uint16_t *)logits + (int64_t)g0 * stride)
                                          : (const void *)((const float *)logits + (int64_t)g0 * stride);
-    int e = orc_prepare_request(rows, dtype, stride, K, V, T, k, theta, counts_row, P, amax);
+    int e = orc_prepare_request_ex(rows, dtype, stride, K, V, T, &o, counts_row, P, amax, NULL);
     if (e) {
       err |= (uint32_t)e;
     } else {
       const float *q = draft_probs ? draft_probs + (int64_t)cu[r] * dstride : NULL;
-      double mg = orc_decide_request(P, amax, K, V, T, draft_ids + cu[r], q, dstride, (uint32_t)g0,
-                                     seed, (uint32_t)offset, C, out_tokens + (int64_t)r * out_stride,
-                                     &num_sampled[r], &num_rejected[r],
-                                     p_draft ? p_draft + cu[r] : NULL);
+      double mg = orc_decide_request_ex(P, amax, K, V, T, draft_ids + cu[r], q, dstride,
+                                        (uint32_t)g0, seed, (uint32_t)offset, C, x->synthetic_rates,
+                                        out_tokens + (int64_t)r * out_stride, &num_sampled[r],
+                                        &num_rejected[r], p_draft ? p_draft + cu[r] : NULL);
       if (margin) margin[r] = mg;
     }
     free(P);
     free(amax);
   }
   return err;
+}
+
+uint32_t orc_verify_batch(const void *logits, int dtype, int64_t stride, int32_t num_rows,
+                          int32_t V, const float *draft_probs, int64_t dstride,
+                          const int32_t *draft_ids, const int32_t *cu, int32_t B,
+                          int32_t max_k, const float *temperature, const int32_t *top_k,
+                          const float *rep_penalty, const int32_t *idx_mapping,
+                          const int32_t *counts, int32_t num_slots, uint64_t seed,
+                          uint64_t offset, int32_t C, int32_t *out_tokens, int32_t out_stride,
+                          int32_t *num_sampled, int32_t *num_rejected, double *margin,
+                          float *p_draft) {
+  return orc_verify_batch_ex(logits, dtype, stride, num_rows, V, draft_probs, dstride, draft_ids,
+                             cu, B, max_k, temperature, top_k, rep_penalty, idx_mapping, counts,
+                             num_slots, seed, offset, C, NULL, out_tokens, out_stride, num_sampled,
+                             num_rejected, margin, p_draft);
 }
 
 /* post_update (page 1, _post_update_kernel): for each request, add its sampled

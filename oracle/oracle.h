@@ -24,6 +24,14 @@
  *  - post_update: last sampled token, output-token histogram, and
  *      num_computed += query_len - num_rejected ("【vllm】DeepSeekMTP、eagle",
  *      postprocess / _post_update_kernel walk-through);
+ *  - optional settings: the frequency penalty of the first page's penalties
+ *      walk-through (logit -= penalty * count), a presence penalty (a constant
+ *      for every token seen; a reading), top-p on the probabilities (clamped to
+ *      [1e-6, 1] as in the Mini-SGLang walk-through's sampler conventions; the
+ *      kept set is every token whose strictly more probable tokens hold less
+ *      than top_p of the mass), and synthetic acceptance with per-position
+ *      unconditional rates or a mean acceptance length ("speculative decoding
+ *      in vLLM", 7.2);
  *  - sampling by an exponential race argmax(w / E), E ~ Exp(1)
  *      (Q&A on NO_DRAFT_PROBS: the recovered-token kernel draws Exp(1) noise and
  *      takes argmax(prob / q)); here run as a two-level race (chunk, then token)
@@ -49,10 +57,33 @@ enum {
   ORC_ERR_ROW = 1u << 3,         /* a processed row has no finite maximum          */
   ORC_ERR_SLOT = 1u << 4,        /* idx_mapping outside [0, num_slots)             */
   ORC_ERR_OFFSET = 1u << 5,      /* offset does not fit in 32 bits                 */
+  ORC_ERR_TOP_P = 1u << 6,       /* top_p is NaN                                  */
 };
 
 enum { ORC_TAG_ACCEPT = 0, ORC_TAG_CHUNK = 1, ORC_TAG_TOKEN = 2 };
 enum { ORC_F32 = 0, ORC_BF16 = 1 };
+
+/* Optional per-request settings beyond temperature.  Processing order of the
+ * logits: repetition penalty, frequency penalty, presence penalty, top-k, then
+ * temperature and softmax, then top-p on the probabilities. */
+typedef struct orc_req_opts {
+  int32_t top_k;      /* < 1 or >= V: off                                        */
+  const float *theta; /* repetition penalty, or NULL (1: off)                    */
+  float freq;         /* frequency penalty: z -= freq * count (0: off)           */
+  float pres;         /* presence penalty: z -= pres where count > 0 (0: off)    */
+  float top_p;        /* nucleus mass, clamped to [1e-6, 1]; 1: off; NaN: error  */
+  double top_p_shift; /* keep iff mass above < top_p + shift; 0 for the method,  */
+                      /* other values only to bracket rounding in tests          */
+} orc_req_opts;
+
+/* Batch-level optional settings for orc_verify_batch_ex (NULL arrays: off). */
+typedef struct orc_batch_opts {
+  const float *freq;            /* [B] frequency penalties or NULL             */
+  const float *pres;            /* [B] presence penalties or NULL              */
+  const float *top_p;           /* [B] nucleus masses or NULL                  */
+  const float *synthetic_rates; /* [max_k] unconditional acceptance rates of   */
+                                /* draft positions 1..max_k, or NULL           */
+} orc_batch_opts;
 
 /* ---- random stream ----------------------------------------------------- */
 void orc_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]);
@@ -68,6 +99,18 @@ void orc_repetition_penalty(float *z, const int32_t *counts, int32_t V, float th
 float orc_kth_largest(const float *z, int32_t V, int32_t k);
 void orc_top_k_mask(float *z, int32_t V, int32_t k);
 int32_t orc_argmax(const float *z, int32_t V);
+void orc_frequency_presence_penalty(float *z, const int32_t *counts, int32_t V, float freq,
+                                    float pres);
+/* Nucleus (top-p) set of the probabilities p[0..V): keep[x] = 1 iff the mass of
+ * the tokens strictly more probable than x is below top_p + shift (ties at the
+ * boundary are all kept).  *margin receives the smallest |mass above - top_p|
+ * over the distinct probability values.  Returns the number of kept tokens. */
+int32_t orc_top_p_keep(const double *p, int32_t V, double top_p, double shift, uint8_t *keep,
+                       double *margin);
+/* Minimum-variance unconditional acceptance rates for a target mean acceptance
+ * length L in [1, K + 1] (accepted drafts + 1): rates[i] for position i + 1.
+ * Returns 0, or -1 when L is out of range or not finite. */
+int orc_synthetic_rates(double L, int32_t K, float *rates);
 /* p = softmax(z / T) in fp64; returns 0, or ORC_ERR_ROW if max(z) is not finite. */
 int orc_softmax(const float *z, int32_t V, double T, double *p);
 
@@ -89,6 +132,13 @@ int orc_prepare_request(const void *rows, int dtype, int64_t stride, int32_t K, 
                         float T, int32_t top_k, const float *theta, const int32_t *counts,
                         double *P, int32_t *amax);
 
+/* orc_prepare_request with the settings of orc_req_opts (o may be NULL).
+ * topp_margin [K+1] (or NULL) receives each row's top-p margin (+inf when
+ * top-p is off or the row is greedy). */
+int orc_prepare_request_ex(const void *rows, int dtype, int64_t stride, int32_t K, int32_t V,
+                           float T, const orc_req_opts *o, const int32_t *counts, double *P,
+                           int32_t *amax, double *topp_margin);
+
 /* Accept/reject decisions and the recovered / bonus token for one request whose
  * rows were prepared by orc_prepare_request.  draft_probs: [K, V] fp32 rows with
  * stride dstride, or NULL for the no-draft-probs mode.  g0: global index of the
@@ -100,6 +150,17 @@ double orc_decide_request(const double *P, const int32_t *amax, int32_t K, int32
                           uint32_t g0, uint64_t seed, uint32_t offset, int32_t C,
                           int32_t *tokens, int32_t *num_sampled, int32_t *num_rejected,
                           float *p_draft);
+
+/* orc_decide_request with synthetic acceptance: when syn_rates (K unconditional
+ * rates of positions 1..K, non-increasing, in [0, 1]) is not NULL, draft i is
+ * accepted iff it is a valid id and u_i * a_i <= a_{i+1} (a_0 = 1, exact in
+ * fp64), in place of the probability test or the greedy comparison; the
+ * recovered and bonus tokens are unchanged. */
+double orc_decide_request_ex(const double *P, const int32_t *amax, int32_t K, int32_t V, float T,
+                             const int32_t *draft_ids, const float *draft_probs, int64_t dstride,
+                             uint32_t g0, uint64_t seed, uint32_t offset, int32_t C,
+                             const float *syn_rates, int32_t *tokens, int32_t *num_sampled,
+                             int32_t *num_rejected, float *p_draft);
 
 /* ---- whole call -------------------------------------------------------- */
 /* Mirrors the library's verify entry point with host arrays.  out_tokens is
@@ -115,6 +176,18 @@ uint32_t orc_verify_batch(const void *logits, int dtype, int64_t stride, int32_t
                           uint64_t offset, int32_t C, int32_t *out_tokens, int32_t out_stride,
                           int32_t *num_sampled, int32_t *num_rejected, double *margin,
                           float *p_draft);
+
+/* orc_verify_batch with the optional settings of orc_batch_opts (x may be NULL;
+ * a request with a frequency or presence penalty needs its histogram slot). */
+uint32_t orc_verify_batch_ex(const void *logits, int dtype, int64_t stride, int32_t num_rows,
+                             int32_t V, const float *draft_probs, int64_t dstride,
+                             const int32_t *draft_ids, const int32_t *cu, int32_t B,
+                             int32_t max_k, const float *temperature, const int32_t *top_k,
+                             const float *rep_penalty, const int32_t *idx_mapping,
+                             const int32_t *counts, int32_t num_slots, uint64_t seed,
+                             uint64_t offset, int32_t C, const orc_batch_opts *x,
+                             int32_t *out_tokens, int32_t out_stride, int32_t *num_sampled,
+                             int32_t *num_rejected, double *margin, float *p_draft);
 
 /* post_update on host arrays (batch order).  Requests with num_sampled <= 0 or a
  * slot outside [0, num_slots) are skipped; returns ORC_ERR_SLOT if any slot was
