@@ -11,14 +11,23 @@
  * row of each request as in "vLLM 投机解码（Eagle / MTP）实现与运行流程", 8.2).
  *
  * For each request the library computes, on the device:
- *   1. processed logits z: repetition penalty (optional), then top-k (optional)
- *      (8.2 of the second page: processors, constraints, then softmax);
+ *   1. processed logits z: repetition penalty, frequency penalty, presence
+ *      penalty (each optional), then top-k (optional) (8.2 of the second page:
+ *      processors, constraints, then softmax; the frequency penalty is the
+ *      first page's penalties walk-through, z -= penalty * count);
  *   2. p = softmax(z / T) per row (T = temperature[r]); T == 0 selects the
- *      greedy rule of 8.3 (argmax of z, lowest index on ties);
+ *      greedy rule of 8.3 (argmax of z, lowest index on ties); then top-p
+ *      (optional; clamped to [1e-6, 1] as in the Mini-SGLang sampler
+ *      conventions): a token stays iff the tokens strictly more probable than
+ *      it hold less than top_p of the mass, and p is renormalised over them;
  *   3. for i = 0..K_r-1: accept draft d_i iff it is a valid id, q_i(d_i) > 0
  *      and p_i(d_i) >= u_i * q_i(d_i) (q = 1 without draft probabilities),
  *      u_i a Philox uniform on ((0,1]; 8.3, stochastic branch, and the
- *      residual-distribution Q&A of the same page); stop at the first reject j;
+ *      residual-distribution Q&A of the same page); stop at the first reject j.
+ *      Synthetic acceptance ("speculative decoding in vLLM", 7.2) replaces this
+ *      test by u_i * a_i <= a_{i+1} (fp64) for unconditional per-position
+ *      rates a (a_0 = 1), so position i + 1 is accepted with probability
+ *      a_{i+1}; everything else is unchanged;
  *   4. after a reject: the recovered token from max(0, p_j - q_j), or, with no
  *      draft probabilities, from p_j with d_j removed (NO_DRAFT_PROBS Q&A);
  *      if every draft passed: the bonus token from row K_r (bonus Q&A);
@@ -91,7 +100,8 @@ enum {
   SV_ERR_TEMPERATURE = 1u << 1, /* temperature < 0, NaN or infinite                      */
   SV_ERR_PENALTY = 1u << 2,     /* repetition penalty <= 0, NaN or infinite              */
   SV_ERR_ROW = 1u << 3,         /* a processed logit row has no finite maximum           */
-  SV_ERR_SLOT = 1u << 4         /* idx_mapping outside [0, num_slots)                    */
+  SV_ERR_SLOT = 1u << 4,        /* idx_mapping outside [0, num_slots)                    */
+  SV_ERR_TOP_P = 1u << 6        /* top_p is NaN                                          */
 };
 
 /* spec_verify_create flags. */
@@ -124,8 +134,8 @@ typedef struct sv_verify_args {
   const float *temperature;         /* [num_reqs]; 0 = greedy, > 0 sampled                  */
   const int32_t *top_k;             /* [num_reqs] or NULL; k < 1 or k >= V disables         */
   const float *rep_penalty;         /* [num_reqs] or NULL; 1 = none                         */
-  const int32_t *idx_mapping;       /* [num_reqs] batch row -> state slot (with rep_penalty) */
-  const int32_t *output_bin_counts; /* [num_slots, vocab_size] (read here, with rep_penalty) */
+  const int32_t *idx_mapping;       /* [num_reqs] batch row -> state slot (with a penalty)  */
+  const int32_t *output_bin_counts; /* [num_slots, vocab_size] (read here, with a penalty)  */
   int32_t *out_tokens;              /* [num_reqs, out_stride], -1 padded                    */
   int32_t *out_num_sampled;         /* [num_reqs]                                           */
   int32_t *out_num_rejected;        /* [num_reqs]                                           */
@@ -141,14 +151,25 @@ typedef struct sv_verify_args {
   int32_t num_reqs;                 /* B                                                    */
   int32_t vocab_size;               /* V <= max_vocab                                       */
   int32_t out_stride;               /* row length of out_tokens, <= max_k + 1               */
-  int32_t num_slots;                /* rows of output_bin_counts (0 without rep_penalty)    */
+  int32_t num_slots;                /* rows of output_bin_counts (0 without a penalty)      */
+  const float *frequency_penalty;   /* [num_reqs] or NULL; z -= f * count, 0 = none          */
+  const float *presence_penalty;    /* [num_reqs] or NULL; z -= f where count > 0, 0 = none  */
+  const float *top_p;               /* [num_reqs] or NULL; clamped to [1e-6, 1], 1 = none    */
+  const float *synthetic_rates;     /* HOST pointer [out_stride - 1] or NULL: synthetic      */
+                                    /* acceptance with these unconditional rates of draft   */
+                                    /* positions 1.., each in [0, 1], non-increasing        */
 } sv_verify_args;
 
 /*
  * Enqueue one verify step on `stream` (see the top of this file).  Reads the
  * target logits once per row in a streaming pass; in draft-probs mode it also
- * reads the full draft row of each rejected request.  Errors: SV_EINVAL,
- * SV_ECAPACITY, SV_EDTYPE, SV_EHIP (nothing enqueued on the first three).
+ * reads the full draft row of each rejected request.  With top_p, rows that
+ * have no top-k candidate list are read again: two (bf16 without penalties) or
+ * four more passes find the nucleus threshold, and one more recomputes their
+ * statistics under it.  A penalty array other than NULL needs idx_mapping,
+ * output_bin_counts and num_slots >= 1.  Errors: SV_EINVAL (also synthetic
+ * rates outside [0, 1], not finite or increasing), SV_ECAPACITY, SV_EDTYPE,
+ * SV_EHIP (nothing enqueued on the first three).
  */
 int spec_verify_run(sv_ctx *ctx, const sv_verify_args *args, hipStream_t stream);
 
@@ -178,6 +199,16 @@ typedef struct sv_post_update_args {
  * Errors: SV_EINVAL, SV_EHIP.
  */
 int spec_post_update(sv_ctx *ctx, const sv_post_update_args *args, hipStream_t stream);
+
+/*
+ * Host helper for synthetic acceptance ("speculative decoding in vLLM", 7.2):
+ * the minimum-variance unconditional rates for a mean acceptance length L in
+ * [1, k + 1] (accepted drafts + 1).  The accepted count then takes only the two
+ * integers around L - 1: rates[i] (position i + 1) is 1 up to floor(L - 1),
+ * then the fractional part, then 0.  rates is a HOST array of k floats.
+ * Returns SV_OK, or SV_EINVAL (L out of range or not finite, k < 0, NULL).
+ */
+int spec_verify_synthetic_rates(float mean_length, int32_t k, float *rates);
 
 /* Static string for a return code. */
 const char *spec_verify_strerror(int status);

@@ -9,7 +9,8 @@ point raises.
 
 Entry points (same names as the C ABI):
     spec_verify_create, spec_verify_destroy, spec_verify_run,
-    spec_post_update, spec_verify_strerror, spec_verify_read_error
+    spec_post_update, spec_verify_strerror, spec_verify_read_error,
+    spec_verify_synthetic_rates, spec_verify_profile_start, spec_verify_profile_read
 """
 from __future__ import annotations
 
@@ -19,10 +20,10 @@ import os
 __all__ = [
     "SV_OK", "SV_EINVAL", "SV_ECAPACITY", "SV_EDTYPE", "SV_EHIP", "SV_EINPUT",
     "SV_F32", "SV_BF16", "SV_CREATE_TOPK", "SV_RACE_CHUNK", "SV_MAX_DRAFTS",
-    "SV_ERR_CU", "SV_ERR_TEMPERATURE", "SV_ERR_PENALTY", "SV_ERR_ROW", "SV_ERR_SLOT",
+    "SV_ERR_CU", "SV_ERR_TEMPERATURE", "SV_ERR_PENALTY", "SV_ERR_ROW", "SV_ERR_SLOT", "SV_ERR_TOP_P",
     "SpecVerifyError", "VerifyArgs", "PostUpdateArgs", "lib", "library_path",
     "spec_verify_create", "spec_verify_destroy", "spec_verify_run", "spec_post_update",
-    "spec_verify_strerror", "spec_verify_read_error",
+    "spec_verify_strerror", "spec_verify_read_error", "spec_verify_synthetic_rates",
 ]
 
 SV_OK, SV_EINVAL, SV_ECAPACITY, SV_EDTYPE, SV_EHIP, SV_EINPUT = 0, -1, -2, -3, -4, -5
@@ -32,6 +33,7 @@ SV_RACE_CHUNK = 1024
 SV_MAX_DRAFTS = 64
 SV_TOPK_CANDIDATES = 1024
 SV_ERR_CU, SV_ERR_TEMPERATURE, SV_ERR_PENALTY, SV_ERR_ROW, SV_ERR_SLOT = 1, 2, 4, 8, 16
+SV_ERR_TOP_P = 64
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SO = os.path.join(_HERE, "libspecverify.so")
@@ -74,6 +76,10 @@ class VerifyArgs(ctypes.Structure):
         ("vocab_size", ctypes.c_int32),
         ("out_stride", ctypes.c_int32),
         ("num_slots", ctypes.c_int32),
+        ("frequency_penalty", ctypes.c_void_p),
+        ("presence_penalty", ctypes.c_void_p),
+        ("top_p", ctypes.c_void_p),
+        ("synthetic_rates", ctypes.c_void_p),  # host pointer
     ]
 
 
@@ -120,6 +126,8 @@ def lib() -> ctypes.CDLL:
         L.spec_verify_strerror.restype = ctypes.c_char_p
         L.spec_verify_read_error.argtypes = [P, ctypes.POINTER(ctypes.c_uint32), P]
         L.spec_verify_read_error.restype = ctypes.c_int
+        L.spec_verify_synthetic_rates.argtypes = [ctypes.c_float, ctypes.c_int32, P]
+        L.spec_verify_synthetic_rates.restype = ctypes.c_int
         L.spec_verify_profile_start.argtypes = [P, ctypes.c_int32]
         L.spec_verify_profile_start.restype = ctypes.c_int
         L.spec_verify_profile_read.argtypes = [P, P, P, ctypes.POINTER(ctypes.c_int32)]
@@ -180,7 +188,8 @@ def spec_verify_destroy(ctx) -> None:
 def make_verify_args(target_logits, draft_ids, cu_num_draft, temperature, out_tokens,
                      out_num_sampled, out_num_rejected, *, draft_probs=None, top_k=None,
                      rep_penalty=None, idx_mapping=None, output_bin_counts=None, seed=0,
-                     offset=0, dbg_p_draft=None, dbg_probs=None) -> VerifyArgs:
+                     offset=0, dbg_p_draft=None, dbg_probs=None, frequency_penalty=None,
+                     presence_penalty=None, top_p=None, synthetic_rates=None) -> VerifyArgs:
     """Fill an sv_verify_args from torch tensors (no copies, no compute)."""
     import torch
     if target_logits.dim() != 2 or not target_logits.is_cuda or target_logits.stride(1) != 1:
@@ -204,6 +213,9 @@ def make_verify_args(target_logits, draft_ids, cu_num_draft, temperature, out_to
             raise ValueError("draft_probs must have unit column stride")
     _dev(top_k, torch.int32, "top_k", 1)
     _dev(rep_penalty, torch.float32, "rep_penalty", 1)
+    _dev(frequency_penalty, torch.float32, "frequency_penalty", 1)
+    _dev(presence_penalty, torch.float32, "presence_penalty", 1)
+    _dev(top_p, torch.float32, "top_p", 1)
     _dev(idx_mapping, torch.int32, "idx_mapping", 1)
     _dev(output_bin_counts, torch.int32, "output_bin_counts", 2)
     _dev(dbg_p_draft, torch.float32, "dbg_p_draft", 1)
@@ -234,6 +246,15 @@ def make_verify_args(target_logits, draft_ids, cu_num_draft, temperature, out_to
     a.vocab_size = V
     a.out_stride = out_tokens.shape[1]
     a.num_slots = 0 if output_bin_counts is None else output_bin_counts.shape[0]
+    a.frequency_penalty = None if frequency_penalty is None else frequency_penalty.data_ptr()
+    a.presence_penalty = None if presence_penalty is None else presence_penalty.data_ptr()
+    a.top_p = None if top_p is None else top_p.data_ptr()
+    if synthetic_rates is not None:
+        # host array: copied by the library during the call
+        vals = [float(v) for v in synthetic_rates]
+        buf = (ctypes.c_float * max(len(vals), 1))(*vals)
+        a._synthetic_buf = buf
+        a.synthetic_rates = ctypes.cast(buf, ctypes.c_void_p).value
     return a
 
 
@@ -241,7 +262,9 @@ def spec_verify_run(ctx, *args, stream=None, **kwargs) -> None:
     """spec_verify_run(ctx, target_logits, draft_ids, cu_num_draft, temperature,
     out_tokens, out_num_sampled, out_num_rejected, *, draft_probs=None, top_k=None,
     rep_penalty=None, idx_mapping=None, output_bin_counts=None, seed=0, offset=0,
-    dbg_p_draft=None, dbg_probs=None, stream=None), or spec_verify_run(ctx, VerifyArgs)."""
+    dbg_p_draft=None, dbg_probs=None, frequency_penalty=None, presence_penalty=None,
+    top_p=None, synthetic_rates=None (a host sequence), stream=None), or
+    spec_verify_run(ctx, VerifyArgs)."""
     a = args[0] if len(args) == 1 and isinstance(args[0], VerifyArgs) else make_verify_args(*args, **kwargs)
     st = lib().spec_verify_run(ctx, ctypes.byref(a), _stream_handle(stream))
     if st != SV_OK:
@@ -281,6 +304,15 @@ def spec_post_update(ctx, *args, stream=None) -> None:
     st = lib().spec_post_update(ctx, ctypes.byref(a), _stream_handle(stream))
     if st != SV_OK:
         raise SpecVerifyError(st, "spec_post_update")
+
+
+def spec_verify_synthetic_rates(mean_length: float, k: int) -> list:
+    """Minimum-variance unconditional acceptance rates for a mean acceptance length."""
+    buf = (ctypes.c_float * max(int(k), 1))()
+    st = lib().spec_verify_synthetic_rates(float(mean_length), int(k), ctypes.cast(buf, ctypes.c_void_p))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "spec_verify_synthetic_rates")
+    return [buf[i] for i in range(int(k))]
 
 
 def spec_verify_read_error(ctx, stream=None) -> int:

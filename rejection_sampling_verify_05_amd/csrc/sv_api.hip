@@ -87,9 +87,10 @@ extern "C" int spec_verify_create(sv_ctx **out, int32_t max_rows, int32_t max_re
   bool ok = dev_alloc(&c->chunk_tab, rows * ncs) && dev_alloc(&c->row_info, rows) &&
             dev_alloc(&c->res_req, reqs) &&
             dev_alloc(&c->res_tab, reqs * ncs) && dev_alloc(&c->res_list, reqs + 1) && dev_alloc(&c->err, 1);
+  // Row states and thresholds (top-k and top-p); candidate lists only for top-k.
+  if (ok) ok = dev_alloc(&c->cand_n, rows) && dev_alloc(&c->cand_tau, rows);
   if (ok && (flags & SV_CREATE_TOPK))
-    ok = dev_alloc(&c->cand_val, rows * sv::kCandCap) && dev_alloc(&c->cand_idx, rows * sv::kCandCap) &&
-         dev_alloc(&c->cand_n, rows) && dev_alloc(&c->cand_tau, rows);
+    ok = dev_alloc(&c->cand_val, rows * sv::kCandCap) && dev_alloc(&c->cand_idx, rows * sv::kCandCap);
   if (ok)
     ok = hipMemset(c->res_req, 0, reqs * sizeof(int4)) == hipSuccess &&
          hipMemset(c->res_list, 0, sizeof(int)) == hipSuccess &&
@@ -130,8 +131,19 @@ extern "C" int spec_verify_run(sv_ctx *ctx, const sv_verify_args *a, hipStream_t
   if (a->logits_row_stride < a->vocab_size) return SV_EINVAL;
   if (a->draft_probs && a->draft_row_stride < a->vocab_size) return SV_EINVAL;
   if (a->offset >> 32) return SV_EINVAL;
-  if (a->rep_penalty && (!a->idx_mapping || !a->output_bin_counts || a->num_slots < 1)) return SV_EINVAL;
+  const bool penalty = a->rep_penalty || a->frequency_penalty || a->presence_penalty;
+  if (penalty && (!a->idx_mapping || !a->output_bin_counts || a->num_slots < 1)) return SV_EINVAL;
   if (a->top_k && !(ctx->flags & SV_CREATE_TOPK)) return SV_ECAPACITY;
+  // Synthetic acceptance: unconditional rates of positions 1..out_stride-1, in
+  // [0, 1] and non-increasing (host array, checked here).
+  if (a->synthetic_rates) {
+    float prev = 1.0f;
+    for (int32_t i = 0; i + 1 < a->out_stride; ++i) {
+      const float v = a->synthetic_rates[i];
+      if (!(v >= 0.0f && v <= prev)) return SV_EINVAL;
+      prev = v;
+    }
+  }
 
   sv::Params p;
   memset(&p, 0, sizeof p);
@@ -144,6 +156,9 @@ extern "C" int spec_verify_run(sv_ctx *ctx, const sv_verify_args *a, hipStream_t
   p.rep_penalty = a->rep_penalty;
   p.idx_mapping = a->idx_mapping;
   p.counts = a->output_bin_counts;
+  p.freq_penalty = a->frequency_penalty;
+  p.pres_penalty = a->presence_penalty;
+  p.top_p = a->top_p;
   p.out_tokens = a->out_tokens;
   p.out_ns = a->out_num_sampled;
   p.out_nr = a->out_num_rejected;
@@ -181,7 +196,7 @@ extern "C" int spec_verify_run(sv_ctx *ctx, const sv_verify_args *a, hipStream_t
     // slice of the R * NC chunks spans at most kSliceRows rows.
     const int esize_ = a->logits_dtype == SV_BF16 ? 2 : 4;
     const bool aligned = ((uintptr_t)a->target_logits % 16 == 0) && ((a->logits_row_stride * esize_) % 16 == 0);
-    p.fast = aligned && a->vocab_size % (16 / esize_) == 0 && !a->rep_penalty && !a->top_k;
+    p.fast = aligned && a->vocab_size % (16 / esize_) == 0 && !penalty && !a->top_k;
     const int64_t chunks = (int64_t)a->num_rows * p.NC;
     if (chunks > 0x7FFFFFFF) return SV_ECAPACITY;
     const int64_t per = (int64_t)(sv::kSliceRows - 1) * p.NC + 1;  // longest slice allowed
@@ -191,10 +206,16 @@ extern "C" int spec_verify_run(sv_ctx *ctx, const sv_verify_args *a, hipStream_t
     p.stats_grid = (int32_t)grid;
   }
   p.out_stride = a->out_stride;
-  p.num_slots = a->rep_penalty ? a->num_slots : 0;
+  p.num_slots = penalty ? a->num_slots : 0;
   const int esize = a->logits_dtype == SV_BF16 ? 2 : 4;
   p.vec_ok = ((uintptr_t)a->target_logits % 16 == 0) && ((a->logits_row_stride * esize) % 16 == 0);
   p.has_topk = a->top_k ? 1 : 0;
+  p.has_topp = a->top_p ? 1 : 0;
+  p.cand_valid = p.has_topk;
+  if (a->synthetic_rates) {
+    p.synthetic = 1;
+    for (int32_t i = 0; i + 1 < a->out_stride; ++i) p.syn[i] = a->synthetic_rates[i];
+  }
   p.seed_lo = (uint32_t)(a->seed & 0xFFFFFFFFu);
   p.seed_hi = (uint32_t)(a->seed >> 32);
   p.offset = (uint32_t)a->offset;
@@ -211,12 +232,39 @@ extern "C" int spec_verify_run(sv_ctx *ctx, const sv_verify_args *a, hipStream_t
   if (p.has_topk && sv::launch_topk(p, stream) != hipSuccess) return SV_EHIP;
   ctx->res_dirty = p.draft_probs != nullptr;  // until the residual race has zeroed the count
   if (sv::launch_stats(p, stream, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr) != hipSuccess) return SV_EHIP;
+  if (p.has_topp) {
+    // Top-p on dense rows, then their statistics again under the threshold
+    // (general pass, only the marked rows).
+    if (sv::launch_topp(p, stream) != hipSuccess) return SV_EHIP;
+    p.cand_valid = 1;
+    sv::Params p2 = p;
+    p2.pass2 = 1;
+    p2.fast = 0;
+    const int64_t chunks = (int64_t)p.R * p.NC;
+    const int64_t per = (int64_t)(sv::kSliceRows - 1) * p.NC + 1;
+    int64_t grid = ctx->resident[a->logits_dtype][0];
+    if (grid * per < chunks) grid = (chunks + per - 1) / per;
+    if (grid > chunks) grid = chunks;
+    p2.stats_grid = (int32_t)grid;
+    if (sv::launch_stats(p2, stream, nullptr, nullptr) != hipSuccess) return SV_EHIP;
+  }
   if (sv::launch_epilogue(p, stream, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr) != hipSuccess) return SV_EHIP;
   if (p.draft_probs) {
     if (sv::launch_resid(p, stream) != hipSuccess) return SV_EHIP;
     ctx->res_dirty = false;
   }
   if (p.dbg_probs && sv::launch_dbg_probs(p, stream) != hipSuccess) return SV_EHIP;
+  return SV_OK;
+}
+
+extern "C" int spec_verify_synthetic_rates(float mean_length, int32_t k, float *rates) {
+  if (k < 0 || (k > 0 && !rates)) return SV_EINVAL;
+  const double L = (double)mean_length;
+  if (!(L >= 1.0) || !(L <= (double)k + 1.0)) return SV_EINVAL;
+  // The accepted count takes floor(L - 1) or that + 1: P(N >= i) is 1, then
+  // the fractional part, then 0.
+  const double n0 = __builtin_floor(L - 1.0), frac = (L - 1.0) - n0;
+  for (int32_t i = 1; i <= k; ++i) rates[i - 1] = (float)((double)i <= n0 ? 1.0 : ((double)i == n0 + 1.0 ? frac : 0.0));
   return SV_OK;
 }
 

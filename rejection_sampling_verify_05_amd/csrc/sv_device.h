@@ -248,12 +248,26 @@ __device__ __forceinline__ float load_logit(const Params &p, int64_t row, int x)
 // Per-request logit processing (penalty, then the top-k threshold).
 struct Proc {
   const int32_t *counts; // counts row or nullptr (no penalty)
-  float theta;
+  float theta;           // repetition penalty (1: none)
+  float freq, pres;      // frequency and presence penalties (0: none)
   float tau;             // -inf: no threshold
 };
 
+// Penalties of a token seen c > 0 times, in this order and each rounded to
+// fp32: repetition (z / theta for z > 0, z * theta otherwise), frequency
+// (z - freq * c), presence (z - pres).  With theta = 1 and zero penalties
+// every step is exact, so the identity settings need no test.
+__device__ __forceinline__ float penalize(float z, int c, const Proc &pr) {
+  z = z > 0.0f ? z / pr.theta : z * pr.theta;
+  z = z - pr.freq * (float)c;
+  return z - pr.pres;
+}
+
 __device__ __forceinline__ float apply_proc(float z, int x, const Proc &pr) {
-  if (pr.counts != nullptr && pr.counts[x] > 0) z = z > 0.0f ? z / pr.theta : z * pr.theta;
+  if (pr.counts != nullptr) {
+    const int c = pr.counts[x];
+    if (c > 0) z = penalize(z, c, pr);
+  }
   return z < pr.tau ? -__builtin_inff() : z;
 }
 

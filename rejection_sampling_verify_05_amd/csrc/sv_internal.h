@@ -20,6 +20,8 @@ constexpr int kResidCPS = 8;      // chunks per residual-pass workgroup
 // Per-row candidate state written by the top-k pass.
 constexpr int kRowDense = -2;     // no top-k on this row: dense stats
 constexpr int kRowThreshold = -1; // top-k kept too many tokens: dense stats with z < tau masked
+constexpr int kRowTopP = -3;      // top-p threshold found on a dense row: stats again with z < tau masked
+__host__ __device__ constexpr bool row_has_tau(int st) { return st == kRowThreshold || st == kRowTopP; }
 
 // Request-level modes.
 enum : int { kModeSample = 0, kModeGreedy = 1, kModeInvalid = 2 };
@@ -35,6 +37,9 @@ struct Params {
   const float *rep_penalty;
   const int32_t *idx_mapping;
   const int32_t *counts;
+  const float *freq_penalty;
+  const float *pres_penalty;
+  const float *top_p;
   // outputs
   int32_t *out_tokens;
   int32_t *out_ns;
@@ -68,8 +73,13 @@ struct Params {
   int32_t num_slots;
   int32_t vec_ok;    // rows and base 16-byte aligned: vector loads allowed
   int32_t has_topk;
+  int32_t has_topp;
+  int32_t cand_valid; // cand_n holds this call's row states (after the top-k or top-p pass)
+  int32_t pass2;      // stats pass over the rows the top-p pass marked (kRowTopP) only
   uint32_t seed_lo, seed_hi, offset;
   uint32_t epoch;
+  int32_t synthetic;  // synthetic acceptance with the rates below
+  float syn[kMaxDrafts]; // unconditional acceptance rates of draft positions 1..
 };
 
 struct PostParams {
@@ -81,6 +91,7 @@ struct PostParams {
 
 // Launchers (sv_kernels.hip).  Return the hipError_t of the last launch.
 hipError_t launch_topk(const Params &p, hipStream_t s);
+hipError_t launch_topp(const Params &p, hipStream_t s);
 // t0, t1: optional events stamped at the kernel's start and end (may be null).
 hipError_t launch_stats(const Params &p, hipStream_t s, hipEvent_t t0, hipEvent_t t1);
 hipError_t launch_epilogue(const Params &p, hipStream_t s, hipEvent_t t0, hipEvent_t t1);

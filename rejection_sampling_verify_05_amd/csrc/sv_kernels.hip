@@ -42,6 +42,7 @@ struct Req {
   float a;           // log2(e) / T
   unsigned errbits;  // device errors this request raises
   bool cu_ok;        // its own cu entries are consistent
+  float top_p;       // nucleus mass in [1e-6, 1]; 1: off
   Proc proc;         // penalty part (tau set per row)
 };
 
@@ -57,7 +58,10 @@ __device__ __forceinline__ Req make_req(const Params &p, int r, int c0, int c1, 
   q.errbits = 0;
   q.proc.counts = nullptr;
   q.proc.theta = 1.0f;
+  q.proc.freq = 0.0f;
+  q.proc.pres = 0.0f;
   q.proc.tau = kNegInf;
+  q.top_p = 1.0f;
   q.a = 0.0f;
   if (!(T >= 0.0f) || !__builtin_isfinite(T)) {
     q.mode = kModeInvalid;
@@ -68,20 +72,55 @@ __device__ __forceinline__ Req make_req(const Params &p, int r, int c0, int c1, 
     q.mode = kModeSample;
     q.a = kLog2e / T;
   }
+  // Penalties: a valid setting other than the identity needs the request's
+  // histogram slot.
+  bool need_counts = false;
   if (p.rep_penalty != nullptr) {
     const float th = p.rep_penalty[r];
     if (!(th > 0.0f) || !__builtin_isfinite(th)) {
       q.mode = kModeInvalid;
       q.errbits |= SV_ERR_PENALTY;
     } else if (th != 1.0f) {
-      const int slot = p.idx_mapping[r];
-      if (slot < 0 || slot >= p.num_slots) {
-        q.mode = kModeInvalid;
-        q.errbits |= SV_ERR_SLOT;
-      } else {
-        q.proc.counts = p.counts + (int64_t)slot * p.V;
-        q.proc.theta = th;
-      }
+      q.proc.theta = th;
+      need_counts = true;
+    }
+  }
+  if (p.freq_penalty != nullptr) {
+    const float f = p.freq_penalty[r];
+    if (!__builtin_isfinite(f)) {
+      q.mode = kModeInvalid;
+      q.errbits |= SV_ERR_PENALTY;
+    } else if (f != 0.0f) {
+      q.proc.freq = f;
+      need_counts = true;
+    }
+  }
+  if (p.pres_penalty != nullptr) {
+    const float f = p.pres_penalty[r];
+    if (!__builtin_isfinite(f)) {
+      q.mode = kModeInvalid;
+      q.errbits |= SV_ERR_PENALTY;
+    } else if (f != 0.0f) {
+      q.proc.pres = f;
+      need_counts = true;
+    }
+  }
+  if (need_counts) {
+    const int slot = p.idx_mapping[r];
+    if (slot < 0 || slot >= p.num_slots) {
+      q.mode = kModeInvalid;
+      q.errbits |= SV_ERR_SLOT;
+    } else {
+      q.proc.counts = p.counts + (int64_t)slot * p.V;
+    }
+  }
+  if (p.top_p != nullptr) {
+    const float tp = p.top_p[r];
+    if (tp != tp) {
+      q.mode = kModeInvalid;
+      q.errbits |= SV_ERR_TOP_P;
+    } else {
+      q.top_p = tp < 1e-6f ? 1e-6f : (tp > 1.0f ? 1.0f : tp);
     }
   }
   return q;
@@ -142,7 +181,7 @@ __device__ __forceinline__ Req lookup_req(const Params &p, int g) {
   }
 }
 
-__device__ __forceinline__ int row_state(const Params &p, int g) { return p.has_topk ? p.cand_n[g] : kRowDense; }
+__device__ __forceinline__ int row_state(const Params &p, int g) { return p.cand_valid ? p.cand_n[g] : kRowDense; }
 
 __device__ __forceinline__ float exp2_acc(float t) { return __builtin_amdgcn_exp2f(t); }
 
@@ -690,7 +729,16 @@ __device__ __forceinline__ void request_epilogue(const Params &p, const Req &q, 
     if (lane < K) {
       const int d = sh.d[lane];
       const int g = q.g0 + lane;
-      if (greedy) {
+      if (p.synthetic) {
+        // Synthetic acceptance: u * a_i <= a_{i+1} with a_0 = 1, exact in fp64.
+        const double u = u_accept(rng_block(p, 0, (uint32_t)g, kTagAccept).x);
+        const double prev = lane == 0 ? 1.0 : (double)p.syn[lane - 1];
+        rej = !(d >= 0 && d < p.V && u * prev <= (double)p.syn[lane]);
+        if (p.dbg_p_draft) {
+          const bool valid = d >= 0 && d < p.V;
+          p.dbg_p_draft[q.c0 + lane] = greedy ? -1.0f : (valid ? exp2_acc(q.a * (sh.zd[lane] - sh.m[lane])) / sh.s[lane] : 0.0f);
+        }
+      } else if (greedy) {
         rej = d != sh.amax[lane];
         if (p.dbg_p_draft) p.dbg_p_draft[q.c0 + lane] = -1.0f;
       } else {
@@ -814,9 +862,12 @@ __device__ __forceinline__ void request_epilogue(const Params &p, const Req &q, 
 // ---------------------------------------------------------------------------
 struct RowInfo {
   int g, r, i, c0, K, g0, mode, st;  // mode kModeInvalid: row skipped
-  float a, theta, tau;
+  float a, theta, freq, pres, tau;
   const int32_t *counts;
 };
+// Rows a stats pass streams: dense rows, or on the second pass of a top-p
+// call only the rows the top-p pass marked.
+__device__ __forceinline__ bool stream_state(const Params &p, int st) { return p.pass2 ? st == kRowTopP : st < 0; }
 constexpr int kRowCache = kSliceRows;  // rows of a slice looked up before streaming
 constexpr int kFastDepth = 3;  // chunks in flight per wave in the fast pass (2, 4, 5: slower)
 
@@ -833,8 +884,10 @@ __device__ __forceinline__ RowInfo row_info_of(const Params &p, const Req &q, in
   ri.st = ok ? row_state(p, g) : kRowDense;
   ri.a = q.a;
   ri.theta = q.proc.theta;
+  ri.freq = q.proc.freq;
+  ri.pres = q.proc.pres;
   ri.counts = q.proc.counts;
-  ri.tau = (ok && ri.st == kRowThreshold) ? p.cand_tau[g] : kNegInf;
+  ri.tau = (ok && row_has_tau(ri.st)) ? p.cand_tau[g] : kNegInf;
   return ri;
 }
 
@@ -862,6 +915,8 @@ __device__ __forceinline__ void chunk_stats(const Params &p, const RowInfo &ri, 
   Proc pr;
   pr.counts = ri.counts;
   pr.theta = ri.theta;
+  pr.freq = ri.freq;
+  pr.pres = ri.pres;
   pr.tau = ri.tau;
   float z[16];
   if (p.vec_ok && (c + 1) * kChunk <= p.V) {
@@ -903,7 +958,7 @@ __device__ __forceinline__ void process_chunk(const Params &p, int64_t ff, const
   const int g = (int)(ff / p.NC);
   const int c = (int)(ff - (int64_t)g * p.NC);
   if (g != cur.g) cur = (g - g_first < kRowCache) ? rows[g - g_first] : row_info_of(p, lookup_req(p, g), g);
-  if (cur.mode != kModeInvalid && cur.st < 0) chunk_stats<DT>(p, cur, c, v);
+  if (cur.mode != kModeInvalid && stream_state(p, cur.st)) chunk_stats<DT>(p, cur, c, v);
 }
 
 // Row state read back from LDS is the same in every lane: keep it in SGPRs.
@@ -921,6 +976,8 @@ __device__ __forceinline__ RowInfo uniform_row(const RowInfo &x) {
   y.st = uni(x.st);
   y.a = uni(x.a);
   y.theta = uni(x.theta);
+  y.freq = uni(x.freq);
+  y.pres = uni(x.pres);
   y.tau = uni(x.tau);
   const uintptr_t c = (uintptr_t)x.counts;
   y.counts = (const int32_t *)(((uintptr_t)(uint32_t)uni((int)(uint32_t)c)) | ((uintptr_t)(uint32_t)uni((int)(uint32_t)(c >> 32)) << 32));
@@ -956,11 +1013,11 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(Params p) {
   auto streamed = [&](int64_t ff) {
     if (ff >= end) return false;
     const int gi = (int)(ff / p.NC) - g_first;
-    return gi >= kRowCache || (sh.rows[gi].mode != kModeInvalid && sh.rows[gi].st < 0);
+    return gi >= kRowCache || (sh.rows[gi].mode != kModeInvalid && stream_state(p, sh.rows[gi].st));
   };
   {
     bool any = false;
-    for (int i = 0; i < min(nrows, kRowCache); ++i) any |= sh.rows[i].mode != kModeInvalid && sh.rows[i].st < 0;
+    for (int i = 0; i < min(nrows, kRowCache); ++i) any |= sh.rows[i].mode != kModeInvalid && stream_state(p, sh.rows[i].st);
     if (!any && nrows <= kRowCache) return;
   }
 
@@ -1160,7 +1217,7 @@ __global__ __launch_bounds__(kThreads) void resid_kernel(Params p) {
     const float4 ri = p.row_info[gs];
     const float m = ri.x, inv_s = 1.0f / ri.y, a = q.a;
     Proc pr = q.proc;
-    if (__float_as_int(ri.w) == kRowThreshold) pr.tau = p.cand_tau[gs];
+    if (row_has_tau(__float_as_int(ri.w))) pr.tau = p.cand_tau[gs];
     const float *qrow = p.draft_probs + (int64_t)(q.c0 + j) * p.dstride;
     float *rt = p.res_tab + (int64_t)r * p.nc_stride;
     for (int c = seg * p.cps + wave; c < min(p.NC, (seg + 1) * p.cps); c += kWaves) {
@@ -1195,7 +1252,7 @@ __global__ __launch_bounds__(kThreads) void resid_race_kernel(Params p) {
   const float4 ri = p.row_info[gs];
   const float m = ri.x, inv_s = 1.0f / ri.y, a = q.a;
   Proc pr = q.proc;
-  if (__float_as_int(ri.w) == kRowThreshold) pr.tau = p.cand_tau[gs];
+  if (row_has_tau(__float_as_int(ri.w))) pr.tau = p.cand_tau[gs];
   const float *qrow = p.draft_probs + (int64_t)(q.c0 + j) * p.dstride;
   const float *rt = p.res_tab + (int64_t)r * p.nc_stride;
   // An empty residual (rounding) falls back to racing over p_j.
@@ -1257,7 +1314,9 @@ struct TopkShared {
   int tile_n[2];  // passers of the current super-tile (by parity: one is reset while the other counts)
   int sel, want;
   float theta;
+  BlockScratch red;
 };
+static_assert(kBuf >= 2 * kCandCap, "the id-ordered kept list is staged in the upper half of the buffer");
 
 // Super-tile of the top-k filter: thread t holds kTopkPer tokens, as
 // kTopkPer / VW vectors of VW tokens (VW = 4 fp32, 8 bf16) at
@@ -1395,7 +1454,7 @@ __device__ __forceinline__ void penalize_tile(const Params &p, const Proc &pr, i
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int x = topk_tok<DT>(base, e0 + e);
-      if (x < p.V && c[e] > 0) z[e0 + e] = z[e0 + e] > 0.0f ? z[e0 + e] / pr.theta : z[e0 + e] * pr.theta;
+      if (x < p.V && c[e] > 0) z[e0 + e] = penalize(z[e0 + e], c[e], pr);
     }
   }
 }
@@ -1409,7 +1468,8 @@ __device__ __forceinline__ void resolve_buffer(TopkShared &sh, int n, const Proc
     if (xi & kUnresolved) {
       const int x = xi & 0x7FFFFFFF;
       float z = sh.bv[e];
-      if (pr.counts[x] > 0) z = z > 0.0f ? z / pr.theta : z * pr.theta;
+      const int c = pr.counts[x];
+      if (c > 0) z = penalize(z, c, pr);
       sh.bv[e] = z;
       sh.bi[e] = x;
     }
@@ -1493,13 +1553,14 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(Params p) {
   // Streaming filter in super-tiles of kTopkTile tokens, kTopkPer per thread
   // (vector loads, all in flight together).  A token passes when its processed
   // logit is >= the running threshold theta (a lower bound of tau_k: the k-th
-  // largest of a subset of the row).  With a penalty theta_r >= 1 the penalty
-  // never raises a logit, so later super-tiles test the raw logit and the counts
+  // largest of a subset of the row).  With a repetition penalty >= 1 and
+  // frequency and presence penalties >= 0 the penalties never raise a logit
+  // (each step rounds monotonically), so later super-tiles test the raw logit and the counts
   // of the few passers are read only when a selection needs them.  Two barriers
   // per super-tile: one to count the passers (compacting the candidate buffer
   // first if they would not fit), one after they are appended.
   const bool pen = pr.counts != nullptr;
-  const bool raw_first = !pen || pr.theta >= 1.0f;
+  const bool raw_first = !pen || (pr.theta >= 1.0f && pr.freq >= 0.0f && pr.pres >= 0.0f);
   bool overflow = k > kCandCap;
   constexpr int kFirstPer = kBuf / kThreads;  // the first kBuf tokens are all kept
   if (!overflow) {
@@ -1668,18 +1729,297 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(Params p) {
     return;
   }
 
-  // Write the kept tokens in increasing id order: each one's position is the
-  // number of kept tokens with a smaller id (ids are distinct).
+  // The kept tokens in increasing id order, staged in the upper half of the
+  // buffer: each one's position is the number of kept tokens with a smaller id
+  // (ids are distinct).
+  float *sv_ = sh.bv + kCandCap;
+  int *si_ = sh.bi + kCandCap;
   for (int e = threadIdx.x; e < ncand; e += kThreads) {
     const int id = sh.bi[e];
     int rank = 0;
     for (int t = 0; t < ncand; ++t) rank += sh.bi[t] < id ? 1 : 0;
-    p.cand_val[(int64_t)g * kCandCap + rank] = sh.bv[e];
-    p.cand_idx[(int64_t)g * kCandCap + rank] = id;
+    sv_[rank] = sh.bv[e];
+    si_[rank] = id;
+  }
+  __syncthreads();
+  int nout = ncand;
+  if (q.top_p < 1.0f) {
+    // Top-p over the candidates, which hold the whole top-k distribution:
+    // weights w = exp2(a (z - m)), S = sum w; token e stays iff the weight of
+    // the tokens with a larger logit is below top_p * S.  Sums run in id order
+    // (fixed, so the result replays bit for bit).  sh.bi[0..ncand) then holds
+    // the kept flags.
+    float lm = kNegInf;
+    for (int e = threadIdx.x; e < ncand; e += kThreads) lm = fmaxf(lm, sv_[e]);
+    const float m = block_max(lm, sh.red);
+    const float a = q.a;
+    float ls = 0.0f;
+    for (int e = threadIdx.x; e < ncand; e += kThreads) ls += exp2_acc(a * (sv_[e] - m));
+    const float bound = q.top_p * block_sum(ls, sh.red);
+    for (int e = threadIdx.x; e < ncand; e += kThreads) {
+      const float ze = sv_[e];
+      float above = 0.0f;
+      for (int t = 0; t < ncand; ++t)
+        if (sv_[t] > ze) above += exp2_acc(a * (sv_[t] - m));
+      sh.bi[e] = above < bound ? 1 : 0;
+    }
+    __syncthreads();
+    // The kept set is every token with z >= the smallest kept logit, which is
+    // also the row's new threshold for single-token lookups.
+    float lt = __builtin_inff();
+    for (int e = threadIdx.x; e < ncand; e += kThreads)
+      if (sh.bi[e]) lt = fminf(lt, sv_[e]);
+    tau = -block_max(-lt, sh.red);
+    int pos = 0;
+    for (int e = threadIdx.x; e < ncand; e += kThreads) {
+      if (sh.bi[e]) {
+        pos = 0;
+        for (int t = 0; t < e; ++t) pos += sh.bi[t];
+        p.cand_val[(int64_t)g * kCandCap + pos] = sv_[e];
+        p.cand_idx[(int64_t)g * kCandCap + pos] = si_[e];
+      }
+    }
+    int lk = 0;
+    for (int e = threadIdx.x; e < ncand; e += kThreads) lk += sh.bi[e];
+    nout = (int)block_sum((float)lk, sh.red);
+  } else {
+    for (int e = threadIdx.x; e < ncand; e += kThreads) {
+      p.cand_val[(int64_t)g * kCandCap + e] = sv_[e];
+      p.cand_idx[(int64_t)g * kCandCap + e] = si_[e];
+    }
   }
   if (threadIdx.x == 0) {
-    p.cand_n[g] = ncand;
+    p.cand_n[g] = nout;
     p.cand_tau[g] = tau;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Top-p pass for dense rows (rows without a candidate list), after the first
+// statistics pass.  One workgroup per row.  The kept set is every token whose
+// strictly larger logits hold less than top_p of the mass; it is all z >= z*
+// for a boundary logit z*, which becomes the row's threshold (cand_tau, state
+// kRowTopP) for a second statistics pass.
+//
+// Masses are fixed point, W(z) = p(z) 2^62 as an integer, so every sum is
+// exact and independent of order.  Pass A streams the row into 256 buckets of
+// t = a (m - z) (a quarter unit of log2 weight each, monotone in z: ties share
+// a bucket) and finds the bucket holding the boundary.  Pass B collects that
+// bucket's logits in LDS, where an MSD radix select on the order-preserving
+// keys, weighted by W, finds z*.  A boundary bucket larger than the LDS list
+// is selected the same way straight from the row (four more passes).
+// ---------------------------------------------------------------------------
+constexpr int kToppBuckets = 256;
+constexpr float kToppT0 = -20.0f;  // bucket 0 starts at t = -20 (weights up to 2^20 relative to m)
+constexpr float kToppPerUnit = 4.0f;
+constexpr int kToppList = 4096;
+
+struct ToppShared {
+  unsigned long long mass[kToppBuckets];
+  unsigned cnt[kToppBuckets];
+  float list[kToppList];
+  unsigned long long above;
+  int n, sel;
+  BlockScratch red;
+};
+
+// Calls fn(x, raw logit) for every token of row g (vector loads, two
+// super-tiles in flight, when the rows are aligned).  All threads call it.
+template <int DT, class F>
+__device__ __forceinline__ void stream_row(const Params &p, int g, F fn) {
+  if (p.vec_ok) {
+    constexpr int VW = TopkRaw<DT>::VW;
+    const int vfull = p.V - p.V % VW;
+    TopkRaw<DT> ra, rb;
+    int base = 0;
+    topk_issue<DT>(p, g, base, vfull, ra);
+    topk_issue<DT>(p, g, base + kTopkTile, vfull, rb);
+    while (base < vfull) {
+      float z[kTopkPer];
+      topk_decode<DT>(base, vfull, ra, z);
+      topk_issue<DT>(p, g, base + 2 * kTopkTile, vfull, ra);
+#pragma unroll
+      for (int e = 0; e < kTopkPer; ++e) {
+        const int x = topk_tok<DT>(base, e);
+        if (x < vfull) fn(x, z[e]);
+      }
+      base += kTopkTile;
+      if (base >= vfull) break;
+      topk_decode<DT>(base, vfull, rb, z);
+      topk_issue<DT>(p, g, base + 2 * kTopkTile, vfull, rb);
+#pragma unroll
+      for (int e = 0; e < kTopkPer; ++e) {
+        const int x = topk_tok<DT>(base, e);
+        if (x < vfull) fn(x, z[e]);
+      }
+      base += kTopkTile;
+    }
+    for (int x = vfull + (int)threadIdx.x; x < p.V; x += kThreads) fn(x, load_logit(p, g, x));
+  } else {
+    for (int x = threadIdx.x; x < p.V; x += kThreads) fn(x, load_logit(p, g, x));
+  }
+}
+
+// MSD radix select weighted by mass among the tokens `each` enumerates (each
+// thread calls its callback for its share): the largest key whose strictly
+// larger keys, together with `above`, hold less than `bound`.
+template <class EACH, class WF>
+__device__ __forceinline__ float topp_select(ToppShared &sh, EACH each, WF weight, unsigned long long above,
+                                             unsigned long long bound) {
+  uint32_t prefix = 0, mask = 0;
+  if (threadIdx.x == 0) sh.above = above;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    sh.mass[threadIdx.x] = 0;
+    __syncthreads();
+    each([&](float z) {
+      const uint32_t key = ukey(z);
+      if ((key & mask) == prefix) atomicAdd(&sh.mass[(key >> shift) & 0xFFu], weight(z));
+    });
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      unsigned long long acc = sh.above;
+      int sel = -1, low = 0;
+      for (int d = 255; d >= 0; --d) {
+        const unsigned long long h = sh.mass[d];
+        if (h == 0) continue;
+        low = d;
+        if (acc + h >= bound) {
+          sel = d;
+          break;
+        }
+        acc += h;
+      }
+      if (sel < 0) {  // not reached (the enumerated tokens hold the boundary): keep everything
+        sel = low;
+        acc -= sh.mass[low];
+      }
+      sh.sel = sel;
+      sh.above = acc;
+    }
+    __syncthreads();
+    prefix |= (uint32_t)sh.sel << shift;
+    mask |= 0xFFu << shift;
+    __syncthreads();
+  }
+  return ukey_val(prefix);
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void topp_kernel(Params p) {
+  __shared__ ToppShared sh;
+  const int tid = threadIdx.x;
+  const int g = blockIdx.x;
+  const int r = find_request(p.cu, p.B, g);
+  const Req q = load_req(p, r);
+  const int st = p.has_topk ? p.cand_n[g] : kRowDense;
+  const bool use = q.cu_ok && g >= q.g0 && g <= q.g0 + q.K && q.mode == kModeSample && q.top_p < 1.0f && st < 0;
+  if (!use) {
+    if (tid == 0 && !p.has_topk) p.cand_n[g] = kRowDense;  // later kernels read every row's state
+    return;
+  }
+  Proc pr = q.proc;
+  pr.tau = st == kRowThreshold ? p.cand_tau[g] : kNegInf;
+  const float a = q.a;
+
+  // Row scale from the first pass's chunk table.
+  const float2 *tab = p.chunk_tab + (int64_t)g * p.nc_stride;
+  float lm = kNegInf;
+  for (int c = tid; c < p.NC; c += kThreads) lm = fmaxf(lm, tab[c].x);
+  const float m = block_max(lm, sh.red);
+  float ls = 0.0f;
+  for (int c = tid; c < p.NC; c += kThreads) {
+    const float2 e = tab[c];
+    if (e.x > kNegInf) ls += e.y * exp2_acc(a * (e.x - m));
+  }
+  const float S = block_sum(ls, sh.red);
+  if (!(m > kNegInf) || !(S > 0.0f) || !__builtin_isfinite(S)) {  // no finite logit: the epilogue flags the row
+    if (tid == 0) p.cand_n[g] = st;
+    return;
+  }
+  // W(z) = exp2(fma(z, a, -hi)) * exp2(-lo) / S * 2^62, a m = hi + lo.
+  const float hi = a * m, lo = __builtin_fmaf(a, m, -hi);
+  const float c0 = exp2_acc(-lo) * (0x1p62f / S);
+  auto weight = [&](float z) -> unsigned long long {
+    return (unsigned long long)(exp2_acc(__builtin_fmaf(z, a, -hi)) * c0);
+  };
+  auto bucket = [&](float z) -> int {
+    const float t = (m - z) * a;
+    const float u = (t - kToppT0) * kToppPerUnit;
+    return u < 0.0f ? 0 : (u >= (float)(kToppBuckets - 1) ? kToppBuckets - 1 : (int)u);
+  };
+
+  // Pass A: mass and count per bucket.
+  sh.mass[tid] = 0;
+  sh.cnt[tid] = 0;
+  if (tid == 0) sh.n = 0;
+  __syncthreads();
+  stream_row<DT>(p, g, [&](int x, float raw) {
+    const float z = apply_proc(raw, x, pr);
+    if (!(z > kNegInf)) return;
+    const int j = bucket(z);
+    atomicAdd(&sh.mass[j], weight(z));
+    atomicAdd(&sh.cnt[j], 1u);
+  });
+  __syncthreads();
+  if (tid == 0) {
+    unsigned long long total = 0;
+    for (int j = 0; j < kToppBuckets; ++j) total += sh.mass[j];
+    const unsigned long long bound = (unsigned long long)((double)q.top_p * (double)total);
+    unsigned long long acc = 0;
+    int sel = -1, last = 0;
+    for (int j = 0; j < kToppBuckets; ++j) {
+      const unsigned long long h = sh.mass[j];
+      if (sh.cnt[j] == 0) continue;
+      last = j;
+      if (acc + h >= bound) {
+        sel = j;
+        break;
+      }
+      acc += h;
+    }
+    if (sel < 0) {
+      sel = last;
+      acc -= sh.mass[last];
+    }
+    sh.sel = sel;
+    sh.above = acc;
+    sh.mass[0] = bound;  // handed over (the histogram is rebuilt below)
+  }
+  __syncthreads();
+  const int jstar = sh.sel;
+  const unsigned long long above = sh.above, bound = sh.mass[0];
+  const unsigned nstar = sh.cnt[jstar];
+  __syncthreads();
+
+  float zstar;
+  if (nstar <= (unsigned)kToppList) {
+    // Pass B: the boundary bucket's logits into LDS, then the select there.
+    stream_row<DT>(p, g, [&](int x, float raw) {
+      const float z = apply_proc(raw, x, pr);
+      if (!(z > kNegInf) || bucket(z) != jstar) return;
+      const int pos = atomicAdd(&sh.n, 1);
+      if (pos < kToppList) sh.list[pos] = z;
+    });
+    __syncthreads();
+    const int n = sh.n < kToppList ? sh.n : kToppList;
+    zstar = topp_select(
+        sh, [&](auto fn) {
+          for (int e = tid; e < n; e += kThreads) fn(sh.list[e]);
+        },
+        weight, above, bound);
+  } else {
+    zstar = topp_select(
+        sh, [&](auto fn) {
+          stream_row<DT>(p, g, [&](int x, float raw) {
+            const float z = apply_proc(raw, x, pr);
+            if (z > kNegInf && bucket(z) == jstar) fn(z);
+          });
+        },
+        weight, above, bound);
+  }
+  if (tid == 0) {
+    p.cand_tau[g] = zstar;
+    p.cand_n[g] = kRowTopP;
   }
 }
 
@@ -1747,6 +2087,14 @@ hipError_t launch_topk(const Params &p, hipStream_t s) {
     topk_kernel<1><<<dim3(p.R), dim3(kThreads), 0, s>>>(p);
   else
     topk_kernel<0><<<dim3(p.R), dim3(kThreads), 0, s>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_topp(const Params &p, hipStream_t s) {
+  if (p.dtype == 1)
+    topp_kernel<1><<<dim3(p.R), dim3(kThreads), 0, s>>>(p);
+  else
+    topp_kernel<0><<<dim3(p.R), dim3(kThreads), 0, s>>>(p);
   return hipGetLastError();
 }
 

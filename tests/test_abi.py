@@ -31,7 +31,8 @@ def test_exports_every_declared_symbol():
     names = declared_functions()
     assert names == sorted(["spec_post_update", "spec_verify_create", "spec_verify_destroy",
                             "spec_verify_profile_read", "spec_verify_profile_start",
-                            "spec_verify_read_error", "spec_verify_run", "spec_verify_strerror"])
+                            "spec_verify_read_error", "spec_verify_run", "spec_verify_strerror",
+                            "spec_verify_synthetic_rates"])
     L = ctypes.CDLL(sv.library_path())
     for n in names:
         assert hasattr(L, n), n
@@ -53,7 +54,8 @@ int main(void) {
   printf("sv_post_update_args %zu\n", sizeof(sv_post_update_args));
   F(sv_verify_args, target_logits) F(sv_verify_args, dbg_probs) F(sv_verify_args, logits_row_stride)
   F(sv_verify_args, seed) F(sv_verify_args, offset) F(sv_verify_args, logits_dtype)
-  F(sv_verify_args, num_rows) F(sv_verify_args, num_slots)
+  F(sv_verify_args, num_rows) F(sv_verify_args, num_slots) F(sv_verify_args, frequency_penalty)
+  F(sv_verify_args, presence_penalty) F(sv_verify_args, top_p) F(sv_verify_args, synthetic_rates)
   F(sv_post_update_args, num_computed_tokens) F(sv_post_update_args, num_reqs)
   F(sv_post_update_args, num_slots)
   return 0;
@@ -123,3 +125,17 @@ def test_product_package_has_no_oracle_or_cpu_fallback():
                 text = open(os.path.join(dirpath, fn), encoding="utf-8").read()
                 assert "import oracle" not in text and "from oracle" not in text, fn
                 assert "oracle.h" not in text, fn
+
+
+def test_synthetic_rates_helper_matches_the_oracle():
+    import numpy as np
+    import oracle
+    for k in [0, 1, 3, 8]:
+        for L in np.linspace(1.0, k + 1.0, 13):
+            got = sv.spec_verify_synthetic_rates(float(np.float32(L)), k)
+            want = oracle.synthetic_rates(float(np.float32(L)), k)
+            assert got == want.tolist(), (k, L)
+    for L, k in [(0.5, 3), (4.5, 3), (float("nan"), 2), (float("inf"), 2)]:
+        with pytest.raises(sv.SpecVerifyError):
+            sv.spec_verify_synthetic_rates(L, k)
+    assert sv.lib().spec_verify_synthetic_rates(ctypes.c_float(2.0), 3, None) == sv.SV_EINVAL

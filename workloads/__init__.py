@@ -51,6 +51,10 @@ class Workload:
     history: int = 0             # tokens in each request's output history (counts)
     draft_mix: float = 1.0       # draft logits = mix * target + noise_scale * N(0,1)
     draft_noise: float = 1.0
+    freq: float = 0.0            # frequency penalty of most requests (every 5th: none)
+    pres: float = 0.0            # presence penalty of most requests (every 5th: none)
+    top_p: float = 1.0           # top-p of most requests (every 7th: none)
+    synthetic_rates: tuple = ()  # synthetic acceptance rates of positions 1.. (empty: off)
 
     def with_(self, **kw) -> "Workload":
         return replace(self, **kw)
@@ -123,6 +127,11 @@ def make_inputs(w: Workload, device="cpu", salt: int = 0, slots_extra: int = 64)
         counts.index_put_((rows.reshape(-1), hist.reshape(-1)),
                           torch.ones(B * w.history, dtype=torch.int32, device=dev), accumulate=True)
     rep = torch.full((B,), w.rep_penalty, dtype=torch.float32, device=dev) if w.rep_penalty != 1.0 else None
+    every = lambda n, v, off: torch.where(torch.arange(B, device=dev) % n == 0, torch.full((B,), off, device=dev),
+                                          torch.full((B,), v, device=dev)).to(torch.float32)
+    freq = every(5, w.freq, 0.0) if w.freq else None
+    pres = every(5, w.pres, 0.0) if w.pres else None
+    top_p = every(7, w.top_p, 1.0) if w.top_p < 1.0 else None
 
     # draft side: draft position i of request r sits on target row cu[r] + r + i
     req = torch.repeat_interleave(torch.arange(B, device=dev), K)
@@ -148,6 +157,8 @@ def make_inputs(w: Workload, device="cpu", salt: int = 0, slots_extra: int = 64)
     return dict(
         workload=w, logits=logits, cu=cu, draft_ids=draft_ids, draft_probs=draft_probs,
         temperature=T, top_k=top_k, rep_penalty=rep, idx_mapping=idx_mapping, counts=counts,
+        freq=freq, pres=pres, top_p=top_p,
+        synthetic_rates=list(w.synthetic_rates) if w.synthetic_rates else None,
         query_len=(K + 1).to(torch.int32), K=K.to(torch.int32), R=R, D=D, B=B, V=V,
         num_slots=S,
     )
@@ -163,7 +174,9 @@ def to_numpy(inp: dict, rows=None) -> dict:
     else:
         lg_np = lg.contiguous().cpu().numpy()
     out = {"logits": lg_np}
-    for k in ("cu", "draft_ids", "temperature", "top_k", "rep_penalty", "idx_mapping", "query_len", "K"):
+    for k in ("cu", "draft_ids", "temperature", "top_k", "rep_penalty", "idx_mapping", "query_len", "K",
+              "freq", "pres", "top_p"):
         v = inp.get(k)
         out[k] = None if v is None else v.cpu().numpy()
+    out["synthetic_rates"] = inp.get("synthetic_rates")
     return out
