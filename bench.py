@@ -61,7 +61,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="3", help="workload id (1, 2, 3, 3k3, 4, 5)")
+    ap.add_argument("--workload", default="3", help="workload id (1, 2, 3, 3k3, 4, 5; with optional "
+                    "settings: 3p top-p, 3f frequency/presence penalties, 3s synthetic acceptance, "
+                    "4f and 4p)")
     ap.add_argument("--copies", type=int, default=0, help="input copies to rotate (0: >= 1 GB)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
@@ -104,6 +106,7 @@ def main():
     ncomp = torch.zeros(S, dtype=torch.int32, device="cuda")
     counts = first["counts"].clone()
     outs = []
+    penalty = any(first[k] is not None for k in ("rep_penalty", "freq", "pres"))
     for c in copies:
         o = dict(tokens=torch.empty((w.B, out_stride), dtype=torch.int32, device="cuda"),
                  ns=torch.empty(w.B, dtype=torch.int32, device="cuda"),
@@ -111,8 +114,9 @@ def main():
         o["vargs"] = sv.make_verify_args(
             c["logits"], c["draft_ids"], c["cu"], c["temperature"], o["tokens"], o["ns"], o["nr"],
             draft_probs=c["draft_probs"], top_k=c["top_k"], rep_penalty=c["rep_penalty"],
-            idx_mapping=c["idx_mapping"], output_bin_counts=c["counts"] if c["rep_penalty"] is not None else None,
-            seed=1234, offset=0)
+            idx_mapping=c["idx_mapping"], output_bin_counts=c["counts"] if penalty else None,
+            seed=1234, offset=0, frequency_penalty=c["freq"], presence_penalty=c["pres"], top_p=c["top_p"],
+            synthetic_rates=c["synthetic_rates"])
         o["pargs"] = sv.make_post_update_args(c["idx_mapping"], c["query_len"], o["tokens"], o["ns"],
                                               o["nr"], last, counts, ncomp)
         outs.append(o)
@@ -206,8 +210,9 @@ def main():
         while True:
             oracle.verify_batch(h["logits"], h["cu"], h["draft_ids"], h["temperature"], draft_probs=dp,
                                 top_k=h["top_k"], rep_penalty=h["rep_penalty"], idx_mapping=h["idx_mapping"],
-                                counts=None if first["rep_penalty"] is None else first["counts"].cpu().numpy(),
-                                seed=1234, offset=n_calls)
+                                counts=first["counts"].cpu().numpy() if penalty else None,
+                                seed=1234, offset=n_calls, freq=h["freq"], pres=h["pres"], top_p=h["top_p"],
+                                synthetic_rates=h["synthetic_rates"])
             n_calls += 1
             cpu_rows += first["R"]
             if time.perf_counter() - t_start >= args.cpu_seconds:
