@@ -20,8 +20,11 @@ constexpr int kResidCPS = 8;      // chunks per residual-pass workgroup
 // Per-row candidate state written by the top-k pass.
 constexpr int kRowDense = -2;     // no top-k on this row: dense stats
 constexpr int kRowThreshold = -1; // top-k kept too many tokens: dense stats with z < tau masked
-constexpr int kRowTopP = -3;      // top-p threshold found on a dense row: stats again with z < tau masked
-__host__ __device__ constexpr bool row_has_tau(int st) { return st == kRowThreshold || st == kRowTopP; }
+constexpr int kRowTopP = -3;      // top-p threshold on a dense row, its chunk table rewritten under it
+constexpr int kRowTopPRedo = -4;  // top-p threshold on a dense row, chunk table from a second stats pass
+__host__ __device__ constexpr bool row_has_tau(int st) {
+  return st == kRowThreshold || st == kRowTopP || st == kRowTopPRedo;
+}
 
 // Request-level modes.
 enum : int { kModeSample = 0, kModeGreedy = 1, kModeInvalid = 2 };
@@ -75,7 +78,7 @@ struct Params {
   int32_t has_topk;
   int32_t has_topp;
   int32_t cand_valid; // cand_n holds this call's row states (after the top-k or top-p pass)
-  int32_t pass2;      // stats pass over the rows the top-p pass marked (kRowTopP) only
+  int32_t pass2;      // stats pass over the rows the top-p pass left to it (kRowTopPRedo) only
   uint32_t seed_lo, seed_hi, offset;
   uint32_t epoch;
   int32_t synthetic;  // synthetic acceptance with the rates below

@@ -866,8 +866,8 @@ struct RowInfo {
   const int32_t *counts;
 };
 // Rows a stats pass streams: dense rows, or on the second pass of a top-p
-// call only the rows the top-p pass marked.
-__device__ __forceinline__ bool stream_state(const Params &p, int st) { return p.pass2 ? st == kRowTopP : st < 0; }
+// call only the rows whose tables the top-p pass left to it.
+__device__ __forceinline__ bool stream_state(const Params &p, int st) { return p.pass2 ? st == kRowTopPRedo : st < 0; }
 constexpr int kRowCache = kSliceRows;  // rows of a slice looked up before streaming
 constexpr int kFastDepth = 3;  // chunks in flight per wave in the fast pass (2, 4, 5: slower)
 
@@ -1797,31 +1797,54 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(Params p) {
 // ---------------------------------------------------------------------------
 // Top-p pass for dense rows (rows without a candidate list), after the first
 // statistics pass.  One workgroup per row.  The kept set is every token whose
-// strictly larger logits hold less than top_p of the mass; it is all z >= z*
-// for a boundary logit z*, which becomes the row's threshold (cand_tau, state
-// kRowTopP) for a second statistics pass.
+// strictly larger logits hold less than top_p of the mass: all z >= z* for a
+// boundary logit z*, the row's threshold afterwards (cand_tau).
 //
-// Masses are fixed point, W(z) = p(z) 2^62 as an integer, so every sum is
-// exact and independent of order.  Pass A streams the row into 256 buckets of
-// t = a (m - z) (a quarter unit of log2 weight each, monotone in z: ties share
-// a bucket) and finds the bucket holding the boundary.  Pass B collects that
-// bucket's logits in LDS, where an MSD radix select on the order-preserving
-// keys, weighted by W, finds z*.  A boundary bucket larger than the LDS list
-// is selected the same way straight from the row (four more passes).
+// Weights relative to the row scale m: w = 2^-t, t = a (m - z).  A token
+// falls in sub-bucket j = floor(16 t) + 320 (clamped to [0, 1024)), of integer
+// part k = j / 16 - 20, and one exp2 gives W = 2^(31 - (t - k)), an
+// integer-valued float near 2^31: w = W 2^(-31-k) exactly, and sums of W
+// within one sub-bucket are exact 64-bit integers (independent of order).
+// Pass A: mass per sub-bucket; an fp64 scan in a fixed order finds the
+// sub-bucket j* holding the boundary and the mass above it.  Pass B: the
+// tokens of j* go to an LDS list, where a radix select on the order-preserving
+// keys, weighted by W, finds z*; tokens before j* are summed per chunk, and
+// the row's chunk table is rewritten as (m, kept mass): no further pass.  When
+// j* holds more tokens than the list, the rows are not 16-byte aligned or the
+// row has more chunks than the LDS tables, z* is selected straight from the
+// row and the row is left to a second statistics pass (kRowTopPRedo).
 // ---------------------------------------------------------------------------
-constexpr int kToppBuckets = 256;
-constexpr float kToppT0 = -20.0f;  // bucket 0 starts at t = -20 (weights up to 2^20 relative to m)
-constexpr float kToppPerUnit = 4.0f;
-constexpr int kToppList = 4096;
+constexpr int kToppSub = 1024;
+constexpr int kToppSubOff = 320;  // sub-bucket of t = 0: t >= -20 is covered (a (z - m) <= 20)
+constexpr int kToppList = 2048;
+constexpr int kToppMaxNC = 512;   // chunks per row whose sums live in LDS (V <= 524288)
 
 struct ToppShared {
-  unsigned long long mass[kToppBuckets];
-  unsigned cnt[kToppBuckets];
-  float list[kToppList];
-  unsigned long long above;
+  unsigned long long mass[kToppSub];
+  float lz[kToppList];
+  int lx[kToppList];
+  float part[kToppMaxNC * 4];            // per chunk, one slot per wave covering it
+  unsigned long long lsum[kToppMaxNC];   // kept list weights per chunk (integer W)
+  float tail[8];
+  unsigned long long need;
   int n, sel;
   BlockScratch red;
 };
+
+struct ToppW {
+  int j, k;
+  float W;  // 2^(31 - (t - k)): an integer-valued float below 2^32
+};
+
+// Sub-bucket and weight of logit z, branch-free: z = -inf (t = +inf) lands in
+// the last sub-bucket with W = 0.
+__device__ __forceinline__ ToppW topp_w(float z, float m, float a) {
+  const float t = (m - z) * a;
+  const float u = fminf(fmaxf(__builtin_floorf(t * 16.0f), -(float)kToppSubOff), (float)(kToppSub - 1 - kToppSubOff));
+  const int j = (int)u + kToppSubOff;
+  const int k = (j >> 4) - kToppSubOff / 16;
+  return ToppW{j, k, exp2_acc(31.0f - (t - (float)k))};
+}
 
 // Calls fn(x, raw logit) for every token of row g (vector loads, two
 // super-tiles in flight, when the rows are aligned).  All threads call it.
@@ -1860,46 +1883,94 @@ __device__ __forceinline__ void stream_row(const Params &p, int g, F fn) {
   }
 }
 
-// MSD radix select weighted by mass among the tokens `each` enumerates (each
-// thread calls its callback for its share): the largest key whose strictly
-// larger keys, together with `above`, hold less than `bound`.
-template <class EACH, class WF>
-__device__ __forceinline__ float topp_select(ToppShared &sh, EACH each, WF weight, unsigned long long above,
-                                             unsigned long long bound) {
+// Calls tile(base, z[kTopkPer]) for every super-tile of an aligned row (two in
+// flight); logits of tokens at or past vfull = V - V % VW read as -inf.
+template <int DT, class F>
+__device__ __forceinline__ void stream_tiles(const Params &p, int g, int vfull, F tile) {
+  TopkRaw<DT> ra, rb;
+  int base = 0;
+  topk_issue<DT>(p, g, base, vfull, ra);
+  topk_issue<DT>(p, g, base + kTopkTile, vfull, rb);
+  while (base < vfull) {
+    float z[kTopkPer];
+    topk_decode<DT>(base, vfull, ra, z);
+    topk_issue<DT>(p, g, base + 2 * kTopkTile, vfull, ra);
+    tile(base, z);
+    base += kTopkTile;
+    if (base >= vfull) break;
+    topk_decode<DT>(base, vfull, rb, z);
+    topk_issue<DT>(p, g, base + 2 * kTopkTile, vfull, rb);
+    tile(base, z);
+    base += kTopkTile;
+  }
+}
+
+// One MSD digit of the weighted select (wave 0 scans, all threads call):
+// bins hold integer weights of the candidates matching the prefix; the digit
+// is the largest whose bins above it hold less than `need` and whose own bin
+// reaches it.  None reaches it only through rounding of the bound: the lowest
+// non-empty digit (everything kept).  need is reduced by the bins above.
+__device__ __forceinline__ int topp_digit(ToppShared &sh, unsigned long long &need) {
+  if (threadIdx.x < 64) {
+    const int l = threadIdx.x;
+    unsigned long long h[4], own = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      h[i] = sh.mass[255 - 4 * l - i];
+      own += h[i];
+    }
+    unsigned long long incl = own;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const unsigned long long o = __shfl_up(incl, d, 64);
+      if (l >= d) incl += o;
+    }
+    const unsigned long long before = incl - own;
+    const bool here = before < need && incl >= need;
+    const unsigned long long any = __ballot(here);
+    const unsigned long long nonempty = __ballot(own != 0);
+    const int src = any ? __ffsll((long long)any) - 1 : 63 - __builtin_clzll(nonempty | 1ull);
+    if (l == src) {
+      unsigned long long acc = before;
+      int sel = -1, low = 255 - 4 * l;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (h[i] == 0) continue;
+        if (sel < 0 && acc + h[i] >= need) sel = 255 - 4 * l - i;
+        if (sel < 0) acc += h[i];
+        low = 255 - 4 * l - i;
+      }
+      if (sel < 0) {  // not reached: keep everything, descend into the lowest non-empty digit
+        sel = low;
+        acc -= h[255 - 4 * l - low];
+      }
+      sh.sel = sel;
+      sh.need = need - acc;
+    }
+  }
+  __syncthreads();
+  const int sel = sh.sel;
+  need = sh.need;
+  __syncthreads();
+  return sel;
+}
+
+// Weighted MSD radix select among the tokens `each` enumerates (each thread
+// calls its callback with (z, W) for its share): the largest key whose
+// strictly larger keys hold less than `need` integer weight units.
+template <class EACH>
+__device__ __forceinline__ float topp_select(ToppShared &sh, EACH each, unsigned long long need) {
   uint32_t prefix = 0, mask = 0;
-  if (threadIdx.x == 0) sh.above = above;
   for (int shift = 24; shift >= 0; shift -= 8) {
     sh.mass[threadIdx.x] = 0;
     __syncthreads();
-    each([&](float z) {
+    each([&](float z, float W) {
       const uint32_t key = ukey(z);
-      if ((key & mask) == prefix) atomicAdd(&sh.mass[(key >> shift) & 0xFFu], weight(z));
+      if ((key & mask) == prefix) atomicAdd(&sh.mass[(key >> shift) & 0xFFu], (unsigned long long)(uint32_t)W);
     });
     __syncthreads();
-    if (threadIdx.x == 0) {
-      unsigned long long acc = sh.above;
-      int sel = -1, low = 0;
-      for (int d = 255; d >= 0; --d) {
-        const unsigned long long h = sh.mass[d];
-        if (h == 0) continue;
-        low = d;
-        if (acc + h >= bound) {
-          sel = d;
-          break;
-        }
-        acc += h;
-      }
-      if (sel < 0) {  // not reached (the enumerated tokens hold the boundary): keep everything
-        sel = low;
-        acc -= sh.mass[low];
-      }
-      sh.sel = sel;
-      sh.above = acc;
-    }
-    __syncthreads();
-    prefix |= (uint32_t)sh.sel << shift;
+    prefix |= (uint32_t)topp_digit(sh, need) << shift;
     mask |= 0xFFu << shift;
-    __syncthreads();
   }
   return ukey_val(prefix);
 }
@@ -1907,7 +1978,7 @@ __device__ __forceinline__ float topp_select(ToppShared &sh, EACH each, WF weigh
 template <int DT>
 __global__ __launch_bounds__(kThreads) void topp_kernel(Params p) {
   __shared__ ToppShared sh;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = blockIdx.x;
   const int r = find_request(p.cu, p.B, g);
   const Req q = load_req(p, r);
@@ -1919,107 +1990,187 @@ __global__ __launch_bounds__(kThreads) void topp_kernel(Params p) {
   }
   Proc pr = q.proc;
   pr.tau = st == kRowThreshold ? p.cand_tau[g] : kNegInf;
-  const float a = q.a;
+  const float a = q.a, tau = pr.tau;
 
-  // Row scale from the first pass's chunk table.
-  const float2 *tab = p.chunk_tab + (int64_t)g * p.nc_stride;
+  // Row scale m from the first pass's chunk table.
+  float2 *tab = p.chunk_tab + (int64_t)g * p.nc_stride;
   float lm = kNegInf;
   for (int c = tid; c < p.NC; c += kThreads) lm = fmaxf(lm, tab[c].x);
   const float m = block_max(lm, sh.red);
-  float ls = 0.0f;
-  for (int c = tid; c < p.NC; c += kThreads) {
-    const float2 e = tab[c];
-    if (e.x > kNegInf) ls += e.y * exp2_acc(a * (e.x - m));
-  }
-  const float S = block_sum(ls, sh.red);
-  if (!(m > kNegInf) || !(S > 0.0f) || !__builtin_isfinite(S)) {  // no finite logit: the epilogue flags the row
+  if (!(m > kNegInf)) {  // no finite logit: the epilogue flags the row
     if (tid == 0) p.cand_n[g] = st;
     return;
   }
-  // W(z) = exp2(fma(z, a, -hi)) * exp2(-lo) / S * 2^62, a m = hi + lo.
-  const float hi = a * m, lo = __builtin_fmaf(a, m, -hi);
-  const float c0 = exp2_acc(-lo) * (0x1p62f / S);
-  auto weight = [&](float z) -> unsigned long long {
-    return (unsigned long long)(exp2_acc(__builtin_fmaf(z, a, -hi)) * c0);
-  };
-  auto bucket = [&](float z) -> int {
-    const float t = (m - z) * a;
-    const float u = (t - kToppT0) * kToppPerUnit;
-    return u < 0.0f ? 0 : (u >= (float)(kToppBuckets - 1) ? kToppBuckets - 1 : (int)u);
-  };
+  constexpr int VW = TopkRaw<DT>::VW;
+  const int vfull = p.V - p.V % VW;
+  // Aligned rows without a penalty take the branch-free tile loops.
+  const bool tiles = p.vec_ok && pr.counts == nullptr;
 
-  // Pass A: mass and count per bucket.
-  sh.mass[tid] = 0;
-  sh.cnt[tid] = 0;
-  if (tid == 0) sh.n = 0;
+  // Pass A: integer weight per sub-bucket.
+  for (int j = tid; j < kToppSub; j += kThreads) sh.mass[j] = 0;
   __syncthreads();
-  stream_row<DT>(p, g, [&](int x, float raw) {
-    const float z = apply_proc(raw, x, pr);
-    if (!(z > kNegInf)) return;
-    const int j = bucket(z);
-    atomicAdd(&sh.mass[j], weight(z));
-    atomicAdd(&sh.cnt[j], 1u);
-  });
+  if (tiles) {
+    stream_tiles<DT>(p, g, vfull, [&](int, float (&z)[kTopkPer]) {
+#pragma unroll
+      for (int e = 0; e < kTopkPer; ++e) {
+        const ToppW w = topp_w(z[e] < tau ? kNegInf : z[e], m, a);
+        atomicAdd(&sh.mass[w.j], (unsigned long long)(uint32_t)w.W);
+      }
+    });
+    if (vfull + tid < p.V) {
+      const ToppW w = topp_w(apply_proc(load_logit(p, g, vfull + tid), vfull + tid, pr), m, a);
+      atomicAdd(&sh.mass[w.j], (unsigned long long)(uint32_t)w.W);
+    }
+  } else {
+    stream_row<DT>(p, g, [&](int x, float raw) {
+      const ToppW w = topp_w(apply_proc(raw, x, pr), m, a);
+      atomicAdd(&sh.mass[w.j], (unsigned long long)(uint32_t)w.W);
+    });
+  }
   __syncthreads();
-  if (tid == 0) {
-    unsigned long long total = 0;
-    for (int j = 0; j < kToppBuckets; ++j) total += sh.mass[j];
-    const unsigned long long bound = (unsigned long long)((double)q.top_p * (double)total);
-    unsigned long long acc = 0;
-    int sel = -1, last = 0;
-    for (int j = 0; j < kToppBuckets; ++j) {
-      const unsigned long long h = sh.mass[j];
-      if (sh.cnt[j] == 0) continue;
-      last = j;
-      if (acc + h >= bound) {
-        sel = j;
+  // Scan (wave 0): lane l owns sub-buckets 16 l .. 16 l + 15, of integer part
+  // k = l - 20; fp64 in a fixed order.
+  if (wave == 0) {
+    const int kl = lane - kToppSubOff / 16;
+    double own = 0.0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) own += __builtin_ldexp((double)sh.mass[16 * lane + i], -31 - kl);
+    double incl = own;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const double o = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += o;
+    }
+    const double total = __shfl(incl, 63, 64);
+    const double bound = (double)q.top_p * total;
+    double acc = incl - own;
+    int hit = -1;
+    double hit_above = 0.0;
+    for (int i = 0; i < 16; ++i) {
+      const unsigned long long h = sh.mass[16 * lane + i];
+      if (h == 0) continue;
+      const double hm = __builtin_ldexp((double)h, -31 - kl);
+      if (acc + hm >= bound) {
+        hit = 16 * lane + i;
+        hit_above = acc;
         break;
       }
-      acc += h;
+      acc += hm;
     }
-    if (sel < 0) {
-      sel = last;
-      acc -= sh.mass[last];
+    const unsigned long long hits = __ballot(hit >= 0);
+    // the first crossing; none only through rounding with top_p near 1: the last non-empty sub-bucket
+    const unsigned long long nonempty = __ballot(own > 0.0);
+    const int src = hits ? __ffsll((long long)hits) - 1 : 63 - __builtin_clzll(nonempty | 1ull);
+    if (lane == src) {
+      if (hit < 0) {
+        for (int i = 15; i >= 0; --i)
+          if (sh.mass[16 * lane + i]) {
+            hit = 16 * lane + i;
+            hit_above = incl - __builtin_ldexp((double)sh.mass[hit], -31 - kl);
+            break;
+          }
+        if (hit < 0) hit = 16 * lane;
+      }
+      sh.sel = hit;
+      // integer weight units of sub-bucket hit still needed to reach the bound
+      const int kh = (hit >> 4) - kToppSubOff / 16;
+      const double rest = __builtin_ceil(__builtin_ldexp(bound - hit_above, 31 + kh));
+      sh.need = rest < 1.0 ? 1ull : (unsigned long long)rest;
+      sh.n = 0;
     }
-    sh.sel = sel;
-    sh.above = acc;
-    sh.mass[0] = bound;  // handed over (the histogram is rebuilt below)
   }
   __syncthreads();
   const int jstar = sh.sel;
-  const unsigned long long above = sh.above, bound = sh.mass[0];
-  const unsigned nstar = sh.cnt[jstar];
-  __syncthreads();
+  const int kstar = (jstar >> 4) - kToppSubOff / 16;
+  const unsigned long long need = sh.need;
+  const bool direct = p.vec_ok && p.NC <= kToppMaxNC;
+
+  // Pass B: the boundary sub-bucket into the list, the mass before it per chunk.
+  bool redo = !direct;
+  if (direct) {
+    for (int c = tid; c < p.NC * 4; c += kThreads) sh.part[c] = 0.0f;
+    for (int c = tid; c < p.NC; c += kThreads) sh.lsum[c] = 0;
+    if (tid < 8) sh.tail[tid] = 0.0f;
+    __syncthreads();
+    constexpr int WPC = kChunk / (64 * VW);  // waves covering one chunk in a super-tile
+    auto token = [&](int x, float z, float &acc) {
+      const ToppW w = topp_w(z, m, a);
+      acc += w.j < jstar ? __builtin_ldexpf(w.W, -31 - w.k) : 0.0f;
+      if (w.j == jstar && z > kNegInf) {
+        const int pos = atomicAdd(&sh.n, 1);
+        if (pos < kToppList) {
+          sh.lz[pos] = z;
+          sh.lx[pos] = x;
+        }
+      }
+    };
+    stream_tiles<DT>(p, g, vfull, [&](int base, float (&z)[kTopkPer]) {
+#pragma unroll
+      for (int v = 0; v < kTopkPer / VW; ++v) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int i = 0; i < VW; ++i) {
+          const int e = v * VW + i;
+          const int x = topk_tok<DT>(base, e);
+          float zz = z[e];
+          if (!tiles && x < vfull) zz = apply_proc(zz, x, pr);  // penalty rows
+          token(x, zz < tau ? kNegInf : zz, acc);
+        }
+        const float sum = wave_sum(acc);
+        const int c = (base + (v * kThreads + wave * 64) * VW) / kChunk;
+        if (lane == 0 && c < p.NC) sh.part[c * 4 + wave % WPC] = sum;
+      }
+    });
+    if (vfull + tid < p.V) {  // the last V % VW tokens (one chunk)
+      float acc = 0.0f;
+      token(vfull + tid, apply_proc(load_logit(p, g, vfull + tid), vfull + tid, pr), acc);
+      sh.tail[tid] = acc;
+    }
+    __syncthreads();
+    redo = sh.n > kToppList;
+  }
 
   float zstar;
-  if (nstar <= (unsigned)kToppList) {
-    // Pass B: the boundary bucket's logits into LDS, then the select there.
-    stream_row<DT>(p, g, [&](int x, float raw) {
-      const float z = apply_proc(raw, x, pr);
-      if (!(z > kNegInf) || bucket(z) != jstar) return;
-      const int pos = atomicAdd(&sh.n, 1);
-      if (pos < kToppList) sh.list[pos] = z;
-    });
-    __syncthreads();
-    const int n = sh.n < kToppList ? sh.n : kToppList;
+  if (!redo) {
+    const int n = sh.n;
     zstar = topp_select(
         sh, [&](auto fn) {
-          for (int e = tid; e < n; e += kThreads) fn(sh.list[e]);
+          for (int e = tid; e < n; e += kThreads) fn(sh.lz[e], topp_w(sh.lz[e], m, a).W);
         },
-        weight, above, bound);
+        need);
+    // Kept list tokens into their chunks (integer sums), then the new table.
+    for (int e = tid; e < n; e += kThreads)
+      if (sh.lz[e] >= zstar)
+        atomicAdd(&sh.lsum[sh.lx[e] / kChunk], (unsigned long long)(uint32_t)topp_w(sh.lz[e], m, a).W);
+    __syncthreads();
+    constexpr int WPC = kChunk / (64 * VW);
+    const int clast = (p.V - 1) / kChunk;
+    for (int c = tid; c < p.NC; c += kThreads) {
+      float sc = 0.0f;
+#pragma unroll
+      for (int w = 0; w < WPC; ++w) sc += sh.part[c * 4 + w];
+      if (c == clast) {
+        float t = 0.0f;
+        for (int i = 0; i < 8; ++i) t += sh.tail[i];
+        sc += t;
+      }
+      sc += (float)__builtin_ldexp((double)sh.lsum[c], -31 - kstar);
+      tab[c] = make_float2(m, sc);
+    }
   } else {
     zstar = topp_select(
         sh, [&](auto fn) {
           stream_row<DT>(p, g, [&](int x, float raw) {
             const float z = apply_proc(raw, x, pr);
-            if (z > kNegInf && bucket(z) == jstar) fn(z);
+            const ToppW w = topp_w(z, m, a);
+            if (w.j == jstar && z > kNegInf) fn(z, w.W);
           });
         },
-        weight, above, bound);
+        need);
   }
   if (tid == 0) {
     p.cand_tau[g] = zstar;
-    p.cand_n[g] = kRowTopP;
+    p.cand_n[g] = redo ? kRowTopPRedo : kRowTopP;
   }
 }
 
