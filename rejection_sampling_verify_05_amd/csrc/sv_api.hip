@@ -16,7 +16,7 @@ struct sv_ctx {
   uint32_t flags;
   int32_t nc_stride;
   uint32_t epoch;
-  int32_t resident[2][2];  // resident stats workgroups: [dtype][fast pass]
+  int32_t resident[2][3];  // resident stats workgroups: [dtype][general, fast, fast with penalties]
   int32_t ncu;             // compute units
   float2 *chunk_tab;
   float4 *row_info;
@@ -102,7 +102,7 @@ extern "C" int spec_verify_create(sv_ctx **out, int32_t max_rows, int32_t max_re
     return SV_EHIP;
   }
   for (int dt = 0; dt < 2; ++dt)
-    for (int f = 0; f < 2; ++f) c->resident[dt][f] = ncu * sv::stats_blocks_per_cu(dt, f != 0);
+    for (int f = 0; f < 3; ++f) c->resident[dt][f] = ncu * sv::stats_blocks_per_cu(dt, f);
   c->ncu = ncu > 0 ? ncu : 1;
   *out = c;
   return SV_OK;
@@ -191,16 +191,19 @@ extern "C" int spec_verify_run(sv_ctx *ctx, const sv_verify_args *a, hipStream_t
     p.resid_grid = (int32_t)(items < cap ? items : cap);
   }
   {
-    // Fast pass: aligned rows whose length is whole 16-byte vectors, no penalty,
-    // no top-k.  Grid: every resident workgroup, but enough workgroups that a
-    // slice of the R * NC chunks spans at most kSliceRows rows.
+    // Fast pass: aligned rows whose length is whole 16-byte vectors, no top-k.
+    // Grid: every resident workgroup, but enough workgroups that a slice of the
+    // R * NC chunks spans at most kSliceRows rows.
     const int esize_ = a->logits_dtype == SV_BF16 ? 2 : 4;
     const bool aligned = ((uintptr_t)a->target_logits % 16 == 0) && ((a->logits_row_stride * esize_) % 16 == 0);
-    p.fast = aligned && a->vocab_size % (16 / esize_) == 0 && !penalty && !a->top_k;
+    // With a penalty the counts rows are read as 16-byte vectors too.
+    const bool counts_ok = !penalty || ((uintptr_t)a->output_bin_counts % 16 == 0 && a->vocab_size % 4 == 0);
+    p.fast = aligned && a->vocab_size % (16 / esize_) == 0 && counts_ok && !a->top_k;
+    p.fast_pen = p.fast && penalty;
     const int64_t chunks = (int64_t)a->num_rows * p.NC;
     if (chunks > 0x7FFFFFFF) return SV_ECAPACITY;
     const int64_t per = (int64_t)(sv::kSliceRows - 1) * p.NC + 1;  // longest slice allowed
-    int64_t grid = ctx->resident[a->logits_dtype][p.fast ? 1 : 0];
+    int64_t grid = ctx->resident[a->logits_dtype][p.fast ? (p.fast_pen ? 2 : 1) : 0];
     if (grid * per < chunks) grid = (chunks + per - 1) / per;
     if (grid > chunks) grid = chunks;
     p.stats_grid = (int32_t)grid;

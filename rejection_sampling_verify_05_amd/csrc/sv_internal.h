@@ -72,6 +72,7 @@ struct Params {
   int32_t nseg;      // residual-pass workgroups per row
   int32_t stats_grid; // stats workgroups (persistent grid; slices span <= kRowCache rows)
   int32_t fast;       // use the fast streaming pass
+  int32_t fast_pen;   // ... its variant that applies penalties (counts loaded as vectors)
   int32_t out_stride;
   int32_t num_slots;
   int32_t vec_ok;    // rows and base 16-byte aligned: vector loads allowed
@@ -103,8 +104,9 @@ hipError_t launch_resid(const Params &p, hipStream_t s);
 hipError_t launch_zero_count(int *count, hipStream_t s);
 hipError_t launch_dbg_probs(const Params &p, hipStream_t s);
 hipError_t launch_post_update(const PostParams &p, hipStream_t s);
-// Resident stats workgroups per CU (occupancy query).
-int stats_blocks_per_cu(int dtype, bool fast);
+// Resident stats workgroups per CU (occupancy query); kind 0 general pass,
+// 1 fast pass, 2 fast pass with penalties.
+int stats_blocks_per_cu(int dtype, int kind);
 constexpr int kSliceRows = 4;  // rows a stats slice may span (kRowCache)
 
 }  // namespace sv

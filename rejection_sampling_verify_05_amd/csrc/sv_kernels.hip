@@ -1045,7 +1045,9 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(Params p) {
 
 // ---------------------------------------------------------------------------
 // Fast streaming pass: aligned rows, V a multiple of the vector width, no
-// penalty and no top-k (the common case, and the no-draft-probs workload).
+// top-k (the common case, and the no-draft-probs workload); the PEN variant
+// also loads each token's output count with the logits (16-byte vectors of
+// four counts) and applies the penalties.
 // Same slices and tables as stats_kernel, with a loop the compiler
 // can pipeline exactly: every wave issues one unconditional set of 16-byte
 // loads per chunk (lanes past the row end read the row's first vector and are
@@ -1066,6 +1068,20 @@ __device__ __forceinline__ void fast_load(const Params &p, int g, int c, u32x4 (
   }
 }
 
+// The counts of this lane's 16 tokens of chunk c (rows whose request has a
+// penalty): four 16-byte vectors; vectors past V read the row start (masked).
+template <int DT>
+__device__ __forceinline__ void fast_load_counts(const Params &p, const int32_t *crow, int c, int4 (&cv)[4]) {
+  using L = Layout<DT>;
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const int x = c * kChunk + L::local(4 * h, lane);  // tokens 4h .. 4h+3 of the lane are consecutive
+    const uint32_t off = x + 4 <= p.V ? (uint32_t)x * 4u : 0u;
+    cv[h] = *reinterpret_cast<const int4 *>(reinterpret_cast<const char *>(crow) + off);
+  }
+}
+
 __device__ __forceinline__ void advance_chunk(int &g, int &c, int by, int NC) {
   c += by;
   while (c >= NC) {
@@ -1083,14 +1099,32 @@ __device__ __forceinline__ void advance_chunk(int &g, int &c, int by, int NC) {
 // exponent of each term is rounded with an absolute error of at most
 // 20 * 2^-24.  Greedy rows (a = 0) always take the exact maximum: their
 // argmax search needs it.
-template <int DT>
+template <int DT, bool PEN>
 __device__ __forceinline__ void fast_chunk(const Params &p, const RowInfo &ri, int c,
-                                           const u32x4 (&v)[Layout<DT>::kVec], float &ref) {
+                                           const u32x4 (&v)[Layout<DT>::kVec], const int4 (&cv)[4], float &ref) {
   using L = Layout<DT>;
   const int lane = threadIdx.x & 63;
   float z[16];
 #pragma unroll
   for (int e = 0; e < 16; ++e) z[e] = L::elem(v, e);
+  if (PEN && ri.counts != nullptr) {
+    // Penalties of the tokens seen (count > 0), as apply_proc; the division
+    // only when the repetition penalty is not 1.
+    Proc pr;
+    pr.theta = ri.theta;
+    pr.freq = ri.freq;
+    pr.pres = ri.pres;
+    const bool rep = ri.theta != 1.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int4 q4 = cv[e >> 2];
+      const int cnt = (e & 3) == 0 ? q4.x : (e & 3) == 1 ? q4.y : (e & 3) == 2 ? q4.z : q4.w;
+      float zp = rep ? (z[e] > 0.0f ? z[e] / pr.theta : z[e] * pr.theta) : z[e];
+      zp = zp - pr.freq * (float)cnt;
+      zp = zp - pr.pres;
+      z[e] = cnt > 0 ? zp : z[e];
+    }
+  }
   if ((c + 1) * kChunk > p.V) {  // row tail: tokens past V do not exist
 #pragma unroll
     for (int e = 0; e < 16; ++e)
@@ -1124,7 +1158,7 @@ __device__ __forceinline__ void fast_chunk(const Params &p, const RowInfo &ri, i
   if (lane == 0 && ri.mode != kModeInvalid) p.chunk_tab[(int64_t)ri.g * p.nc_stride + c] = entry;
 }
 
-template <int DT>
+template <int DT, bool PEN>
 __global__ __launch_bounds__(kThreads) void stats_fast_kernel(Params p) {
   using L = Layout<DT>;
   constexpr int NV = L::kVec;
@@ -1144,6 +1178,7 @@ __global__ __launch_bounds__(kThreads) void stats_fast_kernel(Params p) {
   // slice's first chunk instead), so that every path into the loop has the
   // same loads in flight and the waits stay D chunks deep.
   u32x4 buf[D][NV];
+  int4 cb[D][4];
   int gs[D], cs[D];
   gs[0] = (start + wave) / p.NC;
   cs[0] = start + wave - gs[0] * p.NC;
@@ -1153,8 +1188,10 @@ __global__ __launch_bounds__(kThreads) void stats_fast_kernel(Params p) {
     cs[s] = cs[s - 1];
     advance_chunk(gs[s], cs[s], kWaves, p.NC);
   }
+  if (!PEN) {
 #pragma unroll
-  for (int s = 0; s < D; ++s) fast_load<DT>(p, n > s ? gs[s] : g_first, n > s ? cs[s] : 0, buf[s]);
+    for (int s = 0; s < D; ++s) fast_load<DT>(p, n > s ? gs[s] : g_first, n > s ? cs[s] : 0, buf[s]);
+  }
 
   // Request lookups for the slice's rows (overlapping the loads).
   if (wave < nrows) {
@@ -1164,6 +1201,30 @@ __global__ __launch_bounds__(kThreads) void stats_fast_kernel(Params p) {
   }
   __syncthreads();
 
+  // Counts rows of the slice's rows (a valid address for rows without one).
+  const int32_t *crow[kRowCache];
+  if (PEN) {
+#pragma unroll
+    for (int i = 0; i < kRowCache; ++i) {
+      const RowInfo x = uniform_row(sh.rows[i < nrows ? i : 0]);
+      crow[i] = x.counts != nullptr ? x.counts : p.counts;
+    }
+  }
+  auto load = [&](int s, int g, int c) {
+    fast_load<DT>(p, g, c, buf[s]);
+    if (PEN) {
+      const int gi = g - g_first;
+      const int32_t *cr = crow[0];
+#pragma unroll
+      for (int i = 1; i < kRowCache; ++i) cr = gi == i ? crow[i] : cr;
+      fast_load_counts<DT>(p, cr, c, cb[s]);
+    }
+  };
+  if (PEN) {
+#pragma unroll
+    for (int s = 0; s < D; ++s) load(s, n > s ? gs[s] : g_first, n > s ? cs[s] : 0);
+  }
+
   RowInfo cur = uniform_row(sh.rows[gs[0] - g_first]);
   float ref = kNegInf;  // this wave's reference for row cur.g (uniform)
   auto chunk = [&](int s) {
@@ -1171,7 +1232,7 @@ __global__ __launch_bounds__(kThreads) void stats_fast_kernel(Params p) {
       cur = uniform_row(sh.rows[gs[s] - g_first]);
       ref = kNegInf;
     }
-    fast_chunk<DT>(p, cur, cs[s], buf[s], ref);
+    fast_chunk<DT, PEN>(p, cur, cs[s], buf[s], cb[s], ref);
   };
   int k = 0;
   for (; k + 2 * D - 1 < n; k += D) {
@@ -1179,7 +1240,7 @@ __global__ __launch_bounds__(kThreads) void stats_fast_kernel(Params p) {
     for (int s = 0; s < D; ++s) {
       chunk(s);
       advance_chunk(gs[s], cs[s], D * kWaves, p.NC);
-      fast_load<DT>(p, gs[s], cs[s], buf[s]);
+      load(s, gs[s], cs[s]);
     }
   }
   // Drain: at most 2D - 1 chunks left, loads only while in range.
@@ -1190,7 +1251,7 @@ __global__ __launch_bounds__(kThreads) void stats_fast_kernel(Params p) {
     chunk(s);
     if (k + t + D < n) {
       advance_chunk(gs[s], cs[s], D * kWaves, p.NC);
-      fast_load<DT>(p, gs[s], cs[s], buf[s]);
+      load(s, gs[s], cs[s]);
     }
   }
 }
@@ -2259,19 +2320,24 @@ hipError_t launch_timed(const void *fn, dim3 grid, const Params &p, hipStream_t 
 
 hipError_t launch_stats(const Params &p, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
   const dim3 grid((unsigned)p.stats_grid);
-  const void *fn = p.fast ? (p.dtype == 1 ? reinterpret_cast<const void *>(&stats_fast_kernel<1>)
-                                          : reinterpret_cast<const void *>(&stats_fast_kernel<0>))
-                          : (p.dtype == 1 ? reinterpret_cast<const void *>(&stats_kernel<1>)
-                                          : reinterpret_cast<const void *>(&stats_kernel<0>));
+  const void *fn = !p.fast ? (p.dtype == 1 ? reinterpret_cast<const void *>(&stats_kernel<1>)
+                                           : reinterpret_cast<const void *>(&stats_kernel<0>))
+                   : p.fast_pen ? (p.dtype == 1 ? reinterpret_cast<const void *>(&stats_fast_kernel<1, true>)
+                                                : reinterpret_cast<const void *>(&stats_fast_kernel<0, true>))
+                                : (p.dtype == 1 ? reinterpret_cast<const void *>(&stats_fast_kernel<1, false>)
+                                                : reinterpret_cast<const void *>(&stats_fast_kernel<0, false>));
   return launch_timed(fn, grid, p, s, t0, t1);
 }
 
-int stats_blocks_per_cu(int dtype, bool fast) {
+int stats_blocks_per_cu(int dtype, int kind) {
   int n = 0;
   hipError_t e;
-  if (fast)
-    e = dtype == 1 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, stats_fast_kernel<1>, kThreads, 0)
-                   : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, stats_fast_kernel<0>, kThreads, 0);
+  if (kind == 1)
+    e = dtype == 1 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, stats_fast_kernel<1, false>, kThreads, 0)
+                   : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, stats_fast_kernel<0, false>, kThreads, 0);
+  else if (kind == 2)
+    e = dtype == 1 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, stats_fast_kernel<1, true>, kThreads, 0)
+                   : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, stats_fast_kernel<0, true>, kThreads, 0);
   else
     e = dtype == 1 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, stats_kernel<1>, kThreads, 0)
                    : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, stats_kernel<0>, kThreads, 0);
