@@ -24,7 +24,7 @@ _SRC = os.path.join(_HERE, "oracle.c")
 _SO = os.path.join(_HERE, "liborc.so")
 
 RACE_CHUNK = 1024
-TAG_ACCEPT, TAG_CHUNK, TAG_TOKEN = 0, 1, 2
+TAG_ACCEPT, TAG_CHUNK, TAG_TOKEN, TAG_DRAFT_CHUNK, TAG_DRAFT_TOKEN = 0, 1, 2, 3, 4
 F32, BF16 = 0, 1
 ERR_CU, ERR_TEMPERATURE, ERR_PENALTY, ERR_ROW, ERR_SLOT, ERR_OFFSET = 1, 2, 4, 8, 16, 32
 ERR_TOP_P = 64
@@ -108,6 +108,15 @@ def lib():
         L.orc_verify_batch_ex.argtypes = [P, ctypes.c_int, i64, i32, i32, P, i64, P, P, i32, i32,
                                           P, P, P, P, P, i32, u64, u64, i32, P, P, i32, P, P, P, P]
         L.orc_verify_batch_ex.restype = u32
+        L.orc_race_tags.argtypes = [P, i32, i32, u64, u32, u32, u32, u32, P]
+        L.orc_race_tags.restype = i32
+        L.orc_draft_sample.argtypes = [P, ctypes.c_int, i32, f32, u64, u32, u32, i32, P, P]
+        L.orc_draft_sample.restype = i32
+        L.orc_decide_request_q64.argtypes = [P, P, i32, i32, f32, P, P, u32, u64, u32, i32, P, P, P,
+                                             P, P]
+        L.orc_decide_request_q64.restype = f64
+        L.orc_draft_q_rows.argtypes = [P, ctypes.c_int, i64, i32, i32, f32, P]
+        L.orc_draft_q_rows.restype = ctypes.c_int
         L.orc_post_update.argtypes = [P, P, P, i32, P, P, i32, i32, i32, P, P, P]
         L.orc_post_update.restype = u32
         _lib = L
@@ -215,6 +224,37 @@ def race(w, C: int, seed: int, offset: int, g: int):
     return int(x), float(m.value)
 
 
+def race_tags(w, C: int, seed: int, offset: int, g: int, tag_chunk: int, tag_token: int):
+    ww = _c(w, np.float64)
+    m = ctypes.c_double(0.0)
+    x = lib().orc_race_tags(_ptr(ww), ww.size, C, seed, offset, g, tag_chunk, tag_token, ctypes.byref(m))
+    return int(x), float(m.value)
+
+
+# ---- draft side ------------------------------------------------------------
+def draft_sample(row, T: float, seed: int, offset: int, key: int, C: int = RACE_CHUNK):
+    """row: [V] float32 or uint16 (bf16 bits).  Returns (token, q(token), margin)."""
+    rr = np.ascontiguousarray(row).reshape(-1)
+    dtype = BF16 if rr.dtype == np.uint16 else F32
+    q = ctypes.c_double(0.0)
+    m = ctypes.c_double(0.0)
+    d = lib().orc_draft_sample(_ptr(rr), dtype, rr.size, float(T), seed, offset, key, C, ctypes.byref(q),
+                               ctypes.byref(m))
+    return int(d), float(q.value), float(m.value)
+
+
+def draft_q_rows(rows, T: float):
+    """fp64 draft distributions softmax(z / T) of [K, V] draft logits (float32 or bf16 bits)."""
+    rr = np.ascontiguousarray(rows)
+    K, V = rr.shape
+    Q = np.zeros((K, V), dtype=np.float64)
+    if K:
+        err = lib().orc_draft_q_rows(_ptr(rr), BF16 if rr.dtype == np.uint16 else F32, V, K, V, float(T), _ptr(Q))
+        if err:
+            raise ValueError("draft row has no finite maximum")
+    return Q
+
+
 # ---- one request -----------------------------------------------------------
 def prepare_request_ex(rows, T: float, top_k: int = 0, theta=None, counts=None, freq: float = 0.0,
                        pres: float = 0.0, top_p: float = 1.0, top_p_shift: float = 0.0):
@@ -243,8 +283,9 @@ def prepare_request(rows, T: float, top_k: int = 0, theta=None, counts=None, **k
 
 
 def decide_request(P, amax, T: float, draft_ids, draft_probs=None, g0: int = 0, seed: int = 0,
-                   offset: int = 0, C: int = RACE_CHUNK, synthetic_rates=None):
-    """Returns (tokens list, num_sampled, num_rejected, margin, p_draft)."""
+                   offset: int = 0, C: int = RACE_CHUNK, synthetic_rates=None, draft_q64=None):
+    """Returns (tokens list, num_sampled, num_rejected, margin, p_draft).  draft_q64:
+    fp64 draft distributions [K, V] (from draft logits) in place of draft_probs."""
     n, V = P.shape
     K = n - 1
     PP = np.ascontiguousarray(P, dtype=np.float64)
@@ -258,9 +299,15 @@ def decide_request(P, amax, T: float, draft_ids, draft_probs=None, g0: int = 0, 
     ns = ctypes.c_int32(0)
     nr = ctypes.c_int32(0)
     pd = np.zeros(max(K, 1), dtype=np.float32)
-    mg = lib().orc_decide_request_ex(_ptr(PP), _ptr(am), K, V, float(T), _ptr(d), _ptr(q),
-                                     V if q is None else q.shape[-1], g0, seed, offset, C, _ptr(sr),
-                                     _ptr(tokens), ctypes.byref(ns), ctypes.byref(nr), _ptr(pd))
+    if draft_q64 is not None:
+        Q = np.ascontiguousarray(draft_q64, dtype=np.float64)
+        mg = lib().orc_decide_request_q64(_ptr(PP), _ptr(am), K, V, float(T), _ptr(d), _ptr(Q), g0, seed,
+                                          offset, C, _ptr(sr), _ptr(tokens), ctypes.byref(ns),
+                                          ctypes.byref(nr), _ptr(pd))
+    else:
+        mg = lib().orc_decide_request_ex(_ptr(PP), _ptr(am), K, V, float(T), _ptr(d), _ptr(q),
+                                         V if q is None else q.shape[-1], g0, seed, offset, C, _ptr(sr),
+                                         _ptr(tokens), ctypes.byref(ns), ctypes.byref(nr), _ptr(pd))
     return tokens[: ns.value].tolist(), ns.value, nr.value, float(mg), pd[:K]
 
 

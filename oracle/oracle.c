@@ -249,8 +249,8 @@ static double level_margin(double b1, double b2, int have_second) {
   return 1.0 - b2 / b1;
 }
 
-int32_t orc_race(const double *w, int32_t V, int32_t C, uint64_t seed, uint32_t offset,
-                 uint32_t g, double *margin) {
+int32_t orc_race_tags(const double *w, int32_t V, int32_t C, uint64_t seed, uint32_t offset,
+                      uint32_t g, uint32_t tag_chunk, uint32_t tag_token, double *margin) {
   int32_t nchunks = (V + C - 1) / C;
   double b1 = 0.0, b2 = -1.0;
   int32_t c_best = -1, ncand = 0;
@@ -259,7 +259,7 @@ int32_t orc_race(const double *w, int32_t V, int32_t C, uint64_t seed, uint32_t 
     double M = 0.0;
     for (int32_t x = lo; x < hi; ++x) M += w[x];
     if (!(M > 0.0)) continue;
-    double score = M / orc_exp_noise(seed, offset, g, ORC_TAG_CHUNK, (uint32_t)c);
+    double score = M / orc_exp_noise(seed, offset, g, tag_chunk, (uint32_t)c);
     keep_top2(score, c, &b1, &c_best, &b2);
     ++ncand;
   }
@@ -274,13 +274,18 @@ int32_t orc_race(const double *w, int32_t V, int32_t C, uint64_t seed, uint32_t 
   int32_t lo = c_best * C, hi = lo + C < V ? lo + C : V;
   for (int32_t x = lo; x < hi; ++x) {
     if (!(w[x] > 0.0)) continue;
-    double score = w[x] / orc_exp_noise(seed, offset, g, ORC_TAG_TOKEN, (uint32_t)x);
+    double score = w[x] / orc_exp_noise(seed, offset, g, tag_token, (uint32_t)x);
     keep_top2(score, x, &t1, &x_best, &t2);
     ++tcand;
   }
   double m2 = level_margin(t1, t2, tcand > 1);
   if (margin) *margin = m1 < m2 ? m1 : m2;
   return x_best;
+}
+
+int32_t orc_race(const double *w, int32_t V, int32_t C, uint64_t seed, uint32_t offset,
+                 uint32_t g, double *margin) {
+  return orc_race_tags(w, V, C, seed, offset, g, ORC_TAG_CHUNK, ORC_TAG_TOKEN, margin);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -367,11 +372,19 @@ static int synthetic_accept(const float *a, int32_t i, double u) {
   return u * prev <= (double)a[i];
 }
 
-double orc_decide_request_ex(const double *P, const int32_t *amax, int32_t K, int32_t V, float T,
-                             const int32_t *draft_ids, const float *draft_probs, int64_t dstride,
-                             uint32_t g0, uint64_t seed, uint32_t offset, int32_t C,
-                             const float *syn_rates, int32_t *tokens, int32_t *num_sampled,
-                             int32_t *num_rejected, float *p_draft) {
+/* q_i(x) of draft row i: fp32 draft probabilities, fp64 rows, or none (NULL). */
+static double draft_q(const float *draft_probs, int64_t dstride, const double *Q, int32_t V, int32_t i,
+                      int32_t x) {
+  if (Q) return Q[(int64_t)i * V + x];
+  return (double)draft_probs[(int64_t)i * dstride + x];
+}
+
+static double decide(const double *P, const int32_t *amax, int32_t K, int32_t V, float T,
+                     const int32_t *draft_ids, const float *draft_probs, int64_t dstride,
+                     const double *Q, uint32_t g0, uint64_t seed, uint32_t offset, int32_t C,
+                     const float *syn_rates, int32_t *tokens, int32_t *num_sampled,
+                     int32_t *num_rejected, float *p_draft) {
+  const int has_q = draft_probs != NULL || Q != NULL;
   double margin = INFINITY;
 
   if (T == 0.0f) {
@@ -428,7 +441,7 @@ double orc_decide_request_ex(const double *P, const int32_t *amax, int32_t K, in
       continue;
     }
     double q = 1.0;
-    if (draft_probs) q = valid ? (double)draft_probs[(int64_t)i * dstride + d] : 0.0;
+    if (has_q) q = valid ? draft_q(draft_probs, dstride, Q, V, i, d) : 0.0;
     if (!valid || !(q > 0.0)) {
       j = i;
       break;
@@ -451,11 +464,10 @@ double orc_decide_request_ex(const double *P, const int32_t *amax, int32_t K, in
   if (j < K) {
     int32_t d = draft_ids[j];
     double total = 0.0;
-    if (draft_probs) {
+    if (has_q) {
       /* Residual max(0, p - q), unnormalised (page 2, residual Q&A; page 3, 7.0). */
-      const float *qj = draft_probs + (int64_t)j * dstride;
       for (int32_t x = 0; x < V; ++x) {
-        double r = pj[x] - (double)qj[x];
+        double r = pj[x] - draft_q(draft_probs, dstride, Q, V, j, x);
         w[x] = r > 0.0 ? r : 0.0;
         total += w[x];
       }
@@ -481,6 +493,23 @@ double orc_decide_request_ex(const double *P, const int32_t *amax, int32_t K, in
 }
 
 
+double orc_decide_request_ex(const double *P, const int32_t *amax, int32_t K, int32_t V, float T,
+                             const int32_t *draft_ids, const float *draft_probs, int64_t dstride,
+                             uint32_t g0, uint64_t seed, uint32_t offset, int32_t C,
+                             const float *syn_rates, int32_t *tokens, int32_t *num_sampled,
+                             int32_t *num_rejected, float *p_draft) {
+  return decide(P, amax, K, V, T, draft_ids, draft_probs, dstride, NULL, g0, seed, offset, C, syn_rates,
+                tokens, num_sampled, num_rejected, p_draft);
+}
+
+double orc_decide_request_q64(const double *P, const int32_t *amax, int32_t K, int32_t V, float T,
+                              const int32_t *draft_ids, const double *Q, uint32_t g0, uint64_t seed,
+                              uint32_t offset, int32_t C, const float *syn_rates, int32_t *tokens,
+                              int32_t *num_sampled, int32_t *num_rejected, float *p_draft) {
+  return decide(P, amax, K, V, T, draft_ids, NULL, 0, Q, g0, seed, offset, C, syn_rates, tokens,
+                num_sampled, num_rejected, p_draft);
+}
+
 double orc_decide_request(const double *P, const int32_t *amax, int32_t K, int32_t V, float T,
                           const int32_t *draft_ids, const float *draft_probs, int64_t dstride,
                           uint32_t g0, uint64_t seed, uint32_t offset, int32_t C,
@@ -488,6 +517,52 @@ double orc_decide_request(const double *P, const int32_t *amax, int32_t K, int32
                           float *p_draft) {
   return orc_decide_request_ex(P, amax, K, V, T, draft_ids, draft_probs, dstride, g0, seed, offset,
                                C, NULL, tokens, num_sampled, num_rejected, p_draft);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Draft side (row f4): the draft token of one draft row is sampled from     */
+/* q = softmax(z / T) with the same two-level race as the verifier, on noise  */
+/* of its own tags, so the verifier can take q from the draft logits and the  */
+/* row's softmax statistics instead of stored probabilities (page 3, 7.1:     */
+/* probabilistic drafting needs the full draft distribution at verification). */
+/* ------------------------------------------------------------------------ */
+int32_t orc_draft_sample(const void *row, int dtype, int32_t V, float T, uint64_t seed,
+                         uint32_t offset, uint32_t key, int32_t C, double *q_token, double *margin) {
+  float *z = (float *)malloc(sizeof(float) * (size_t)V);
+  load_row(row, dtype, (int64_t)V, 0, V, z);
+  int32_t d = orc_argmax(z, V);
+  if (!isfinite(z[d])) {
+    free(z);
+    return -1;
+  }
+  if (T == 0.0f) {
+    free(z);
+    if (q_token) *q_token = 1.0;
+    if (margin) *margin = INFINITY;
+    return d;
+  }
+  double *q = (double *)malloc(sizeof(double) * (size_t)V);
+  orc_softmax(z, V, (double)T, q);
+  double mg = 1.0;
+  d = orc_race_tags(q, V, C, seed, offset, key, ORC_TAG_DRAFT_CHUNK, ORC_TAG_DRAFT_TOKEN, &mg);
+  if (q_token) *q_token = d >= 0 ? q[d] : 0.0;
+  if (margin) *margin = mg;
+  free(q);
+  free(z);
+  return d;
+}
+
+/* fp64 draft distributions of K draft rows: softmax(z / T) (page 3, 7.1). */
+int orc_draft_q_rows(const void *rows, int dtype, int64_t stride, int32_t K, int32_t V, float T,
+                     double *Q) {
+  float *z = (float *)malloc(sizeof(float) * (size_t)V);
+  int err = 0;
+  for (int32_t i = 0; i < K; ++i) {
+    load_row(rows, dtype, stride, i, V, z);
+    err |= orc_softmax(z, V, (double)T, Q + (int64_t)i * V);
+  }
+  free(z);
+  return err;
 }
 
 /* ------------------------------------------------------------------------ */

@@ -32,6 +32,11 @@
  *      than top_p of the mass), and synthetic acceptance with per-position
  *      unconditional rates or a mean acceptance length ("speculative decoding
  *      in vLLM", 7.2);
+ *  - draft-side sampling ("speculative decoding in vLLM", 7.1: probabilistic
+ *      drafting needs the draft distribution at verification): each draft token
+ *      is drawn from q = softmax(z / T) by the same two-level race on noise of
+ *      its own tags, and verification may take q rows computed from the draft
+ *      logits instead of stored probabilities;
  *  - sampling by an exponential race argmax(w / E), E ~ Exp(1)
  *      (Q&A on NO_DRAFT_PROBS: the recovered-token kernel draws Exp(1) noise and
  *      takes argmax(prob / q)); here run as a two-level race (chunk, then token)
@@ -60,7 +65,7 @@ enum {
   ORC_ERR_TOP_P = 1u << 6,       /* top_p is NaN                                  */
 };
 
-enum { ORC_TAG_ACCEPT = 0, ORC_TAG_CHUNK = 1, ORC_TAG_TOKEN = 2 };
+enum { ORC_TAG_ACCEPT = 0, ORC_TAG_CHUNK = 1, ORC_TAG_TOKEN = 2, ORC_TAG_DRAFT_CHUNK = 3, ORC_TAG_DRAFT_TOKEN = 4 };
 enum { ORC_F32 = 0, ORC_BF16 = 1 };
 
 /* Optional per-request settings beyond temperature.  Processing order of the
@@ -121,6 +126,22 @@ int orc_softmax(const float *z, int32_t V, double T, double *p);
  * two levels (1 when a level has a single candidate). */
 int32_t orc_race(const double *w, int32_t V, int32_t C, uint64_t seed, uint32_t offset,
                  uint32_t g, double *margin);
+/* The same race with the noise of the given chunk and token tags. */
+int32_t orc_race_tags(const double *w, int32_t V, int32_t C, uint64_t seed, uint32_t offset,
+                      uint32_t g, uint32_t tag_chunk, uint32_t tag_token, double *margin);
+
+/* ---- draft side -------------------------------------------------------- */
+/* Draft-side sampling of one draft row: q = softmax(z / T) in fp64 (T = 0:
+ * the argmax, q(d) = 1), d from the two-level race over q with the draft tags
+ * (3 and 4) at counter row `key` (the draft's row in the verify call).  *q_token
+ * receives q(d); *margin the race margin (+inf for T = 0).  Returns d, or -1
+ * (no finite logit). */
+int32_t orc_draft_sample(const void *row, int dtype, int32_t V, float T, uint64_t seed,
+                         uint32_t offset, uint32_t key, int32_t C, double *q_token, double *margin);
+
+/* fp64 draft distributions softmax(z / T) of K draft rows (stride in elements). */
+int orc_draft_q_rows(const void *rows, int dtype, int64_t stride, int32_t K, int32_t V, float T,
+                     double *Q);
 
 /* ---- one request ------------------------------------------------------- */
 /* Process the K+1 target rows of one request (penalty, top-k, then softmax at T,
@@ -161,6 +182,12 @@ double orc_decide_request_ex(const double *P, const int32_t *amax, int32_t K, in
                              uint32_t g0, uint64_t seed, uint32_t offset, int32_t C,
                              const float *syn_rates, int32_t *tokens, int32_t *num_sampled,
                              int32_t *num_rejected, float *p_draft);
+/* orc_decide_request_ex with fp64 draft distributions Q [K, V] (rows computed
+ * from draft logits), used in place of draft_probs when Q is not NULL. */
+double orc_decide_request_q64(const double *P, const int32_t *amax, int32_t K, int32_t V, float T,
+                              const int32_t *draft_ids, const double *Q, uint32_t g0, uint64_t seed,
+                              uint32_t offset, int32_t C, const float *syn_rates, int32_t *tokens,
+                              int32_t *num_sampled, int32_t *num_rejected, float *p_draft);
 
 /* ---- whole call -------------------------------------------------------- */
 /* Mirrors the library's verify entry point with host arrays.  out_tokens is
