@@ -158,6 +158,13 @@ typedef struct sv_verify_args {
   const float *synthetic_rates;     /* HOST pointer [out_stride - 1] or NULL: synthetic      */
                                     /* acceptance with these unconditional rates of draft   */
                                     /* positions 1.., each in [0, 1], non-increasing        */
+  /* Draft-logits mode (instead of draft_probs; all three given or none):               */
+  const void *draft_logits;         /* [D, draft_logits_stride], dtype draft_logits_dtype   */
+  const float *draft_stats;         /* [2 D] (m, s) per draft row, from spec_draft_sample   */
+  const float *draft_temperature;   /* [num_reqs] temperature the drafts were drawn at; 0:  */
+                                    /* greedy drafts (then as draft ids only)               */
+  int64_t draft_logits_stride;      /* elements between draft-logit rows, >= vocab_size     */
+  int32_t draft_logits_dtype;       /* SV_F32 or SV_BF16                                    */
 } sv_verify_args;
 
 /*
@@ -199,6 +206,40 @@ typedef struct sv_post_update_args {
  * Errors: SV_EINVAL, SV_EHIP.
  */
 int spec_post_update(sv_ctx *ctx, const sv_post_update_args *args, hipStream_t stream);
+
+/*
+ * Draft-side sampling (NEXT row of the verify step; "speculative decoding in
+ * vLLM", 7.1: probabilistic drafting needs the draft distribution at
+ * verification).  For one draft step, request r's draft token is drawn from
+ * q = softmax(z_r / T_r) over its row of draft_logits by the same two-level
+ * race as the verifier, on Philox counter row cu[r] + step (its row in the
+ * verify call's draft arrays) with tags 3 (chunks) and 4 (tokens); T_r = 0
+ * takes the argmax (lowest index).  Outputs: out_tokens[r] (-1 when step >=
+ * K_r or the request is invalid), out_q[r] = q(d) (1 for greedy; may be NULL),
+ * and draft_stats[2 (cu[r] + step) + {0, 1}] = (m, s), the row's scale and
+ * mass: q(x) = 2^(log2(e) / T (z_x - m)) / s.  Keep the draft logits rows and
+ * pass them with draft_stats and the same temperatures to spec_verify_run
+ * (draft-logits mode): no probability rows are stored.  Reads each draft row
+ * once.  Errors: SV_EINVAL, SV_ECAPACITY (num_reqs beyond max_reqs or
+ * max_rows, vocab beyond max_vocab), SV_EDTYPE, SV_EHIP.
+ */
+typedef struct sv_draft_args {
+  const void *draft_logits;     /* [num_reqs, logits_row_stride] this step's draft logits */
+  const float *temperature;     /* [num_reqs] draft temperature, >= 0                      */
+  const int32_t *cu_num_draft;  /* [num_reqs + 1] prefix sums of the verify call          */
+  int32_t *out_tokens;          /* [num_reqs]                                             */
+  float *out_q;                 /* [num_reqs] or NULL                                     */
+  float *draft_stats;           /* [2 D] written at the drafted rows                      */
+  int64_t logits_row_stride;    /* elements between rows, >= vocab_size                   */
+  uint64_t seed;                /* Philox key                                             */
+  uint64_t offset;              /* per-call step, must be < 2^32                          */
+  int32_t logits_dtype;         /* SV_F32 or SV_BF16                                      */
+  int32_t num_reqs;
+  int32_t vocab_size;
+  int32_t step;                 /* draft position sampled by this call, >= 0              */
+} sv_draft_args;
+
+int spec_draft_sample(sv_ctx *ctx, const sv_draft_args *args, hipStream_t stream);
 
 /*
  * Host helper for synthetic acceptance ("speculative decoding in vLLM", 7.2):

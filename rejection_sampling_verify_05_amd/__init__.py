@@ -10,7 +10,8 @@ point raises.
 Entry points (same names as the C ABI):
     spec_verify_create, spec_verify_destroy, spec_verify_run,
     spec_post_update, spec_verify_strerror, spec_verify_read_error,
-    spec_verify_synthetic_rates, spec_verify_profile_start, spec_verify_profile_read
+    spec_verify_synthetic_rates, spec_verify_profile_start, spec_verify_profile_read,
+    spec_draft_sample
 """
 from __future__ import annotations
 
@@ -24,6 +25,7 @@ __all__ = [
     "SpecVerifyError", "VerifyArgs", "PostUpdateArgs", "lib", "library_path",
     "spec_verify_create", "spec_verify_destroy", "spec_verify_run", "spec_post_update",
     "spec_verify_strerror", "spec_verify_read_error", "spec_verify_synthetic_rates",
+    "DraftArgs", "spec_draft_sample",
 ]
 
 SV_OK, SV_EINVAL, SV_ECAPACITY, SV_EDTYPE, SV_EHIP, SV_EINPUT = 0, -1, -2, -3, -4, -5
@@ -80,6 +82,30 @@ class VerifyArgs(ctypes.Structure):
         ("presence_penalty", ctypes.c_void_p),
         ("top_p", ctypes.c_void_p),
         ("synthetic_rates", ctypes.c_void_p),  # host pointer
+        ("draft_logits", ctypes.c_void_p),
+        ("draft_stats", ctypes.c_void_p),
+        ("draft_temperature", ctypes.c_void_p),
+        ("draft_logits_stride", ctypes.c_int64),
+        ("draft_logits_dtype", ctypes.c_int32),
+    ]
+
+
+class DraftArgs(ctypes.Structure):
+    """Mirror of ``sv_draft_args``."""
+    _fields_ = [
+        ("draft_logits", ctypes.c_void_p),
+        ("temperature", ctypes.c_void_p),
+        ("cu_num_draft", ctypes.c_void_p),
+        ("out_tokens", ctypes.c_void_p),
+        ("out_q", ctypes.c_void_p),
+        ("draft_stats", ctypes.c_void_p),
+        ("logits_row_stride", ctypes.c_int64),
+        ("seed", ctypes.c_uint64),
+        ("offset", ctypes.c_uint64),
+        ("logits_dtype", ctypes.c_int32),
+        ("num_reqs", ctypes.c_int32),
+        ("vocab_size", ctypes.c_int32),
+        ("step", ctypes.c_int32),
     ]
 
 
@@ -126,6 +152,8 @@ def lib() -> ctypes.CDLL:
         L.spec_verify_strerror.restype = ctypes.c_char_p
         L.spec_verify_read_error.argtypes = [P, ctypes.POINTER(ctypes.c_uint32), P]
         L.spec_verify_read_error.restype = ctypes.c_int
+        L.spec_draft_sample.argtypes = [P, ctypes.POINTER(DraftArgs), P]
+        L.spec_draft_sample.restype = ctypes.c_int
         L.spec_verify_synthetic_rates.argtypes = [ctypes.c_float, ctypes.c_int32, P]
         L.spec_verify_synthetic_rates.restype = ctypes.c_int
         L.spec_verify_profile_start.argtypes = [P, ctypes.c_int32]
@@ -189,7 +217,8 @@ def make_verify_args(target_logits, draft_ids, cu_num_draft, temperature, out_to
                      out_num_sampled, out_num_rejected, *, draft_probs=None, top_k=None,
                      rep_penalty=None, idx_mapping=None, output_bin_counts=None, seed=0,
                      offset=0, dbg_p_draft=None, dbg_probs=None, frequency_penalty=None,
-                     presence_penalty=None, top_p=None, synthetic_rates=None) -> VerifyArgs:
+                     presence_penalty=None, top_p=None, synthetic_rates=None, draft_logits=None,
+                     draft_stats=None, draft_temperature=None) -> VerifyArgs:
     """Fill an sv_verify_args from torch tensors (no copies, no compute)."""
     import torch
     if target_logits.dim() != 2 or not target_logits.is_cuda or target_logits.stride(1) != 1:
@@ -216,6 +245,13 @@ def make_verify_args(target_logits, draft_ids, cu_num_draft, temperature, out_to
     _dev(frequency_penalty, torch.float32, "frequency_penalty", 1)
     _dev(presence_penalty, torch.float32, "presence_penalty", 1)
     _dev(top_p, torch.float32, "top_p", 1)
+    _dev(draft_stats, torch.float32, "draft_stats", 1)
+    _dev(draft_temperature, torch.float32, "draft_temperature", 1)
+    if draft_logits is not None:
+        if draft_logits.dim() != 2 or not draft_logits.is_cuda or draft_logits.stride(1) != 1:
+            raise ValueError("draft_logits must be a 2-D CUDA tensor with unit column stride")
+        if draft_logits.dtype not in (torch.float32, torch.bfloat16):
+            raise TypeError("draft_logits must be float32 or bfloat16")
     _dev(idx_mapping, torch.int32, "idx_mapping", 1)
     _dev(output_bin_counts, torch.int32, "output_bin_counts", 2)
     _dev(dbg_p_draft, torch.float32, "dbg_p_draft", 1)
@@ -249,6 +285,12 @@ def make_verify_args(target_logits, draft_ids, cu_num_draft, temperature, out_to
     a.frequency_penalty = None if frequency_penalty is None else frequency_penalty.data_ptr()
     a.presence_penalty = None if presence_penalty is None else presence_penalty.data_ptr()
     a.top_p = None if top_p is None else top_p.data_ptr()
+    if draft_logits is not None:
+        a.draft_logits = draft_logits.data_ptr()
+        a.draft_logits_stride = draft_logits.stride(0)
+        a.draft_logits_dtype = SV_BF16 if draft_logits.dtype == torch.bfloat16 else SV_F32
+    a.draft_stats = None if draft_stats is None else draft_stats.data_ptr()
+    a.draft_temperature = None if draft_temperature is None else draft_temperature.data_ptr()
     if synthetic_rates is not None:
         # host array: copied by the library during the call
         vals = [float(v) for v in synthetic_rates]
@@ -304,6 +346,50 @@ def spec_post_update(ctx, *args, stream=None) -> None:
     st = lib().spec_post_update(ctx, ctypes.byref(a), _stream_handle(stream))
     if st != SV_OK:
         raise SpecVerifyError(st, "spec_post_update")
+
+
+def make_draft_args(draft_logits, temperature, cu_num_draft, out_tokens, draft_stats, *, step: int,
+                    out_q=None, seed=0, offset=0) -> DraftArgs:
+    """Fill an sv_draft_args from torch tensors (no copies, no compute)."""
+    import torch
+    if draft_logits.dim() != 2 or not draft_logits.is_cuda or draft_logits.stride(1) != 1:
+        raise ValueError("draft_logits must be a 2-D CUDA tensor with unit column stride")
+    if draft_logits.dtype == torch.float32:
+        dt = SV_F32
+    elif draft_logits.dtype == torch.bfloat16:
+        dt = SV_BF16
+    else:
+        raise TypeError("draft_logits must be float32 or bfloat16")
+    _dev(temperature, torch.float32, "temperature", 1)
+    _dev(cu_num_draft, torch.int32, "cu_num_draft", 1)
+    _dev(out_tokens, torch.int32, "out_tokens", 1)
+    _dev(out_q, torch.float32, "out_q", 1)
+    _dev(draft_stats, torch.float32, "draft_stats", 1)
+    a = DraftArgs()
+    a.draft_logits = draft_logits.data_ptr()
+    a.temperature = temperature.data_ptr()
+    a.cu_num_draft = cu_num_draft.data_ptr()
+    a.out_tokens = out_tokens.data_ptr()
+    a.out_q = None if out_q is None else out_q.data_ptr()
+    a.draft_stats = draft_stats.data_ptr()
+    a.logits_row_stride = draft_logits.stride(0)
+    a.seed = int(seed)
+    a.offset = int(offset)
+    a.logits_dtype = dt
+    a.num_reqs = draft_logits.shape[0]
+    a.vocab_size = draft_logits.shape[1]
+    a.step = int(step)
+    return a
+
+
+def spec_draft_sample(ctx, *args, stream=None, **kwargs) -> None:
+    """spec_draft_sample(ctx, draft_logits [B, V], temperature [B], cu_num_draft [B+1],
+    out_tokens [B], draft_stats [2 D], step=i, out_q=None, seed=0, offset=0,
+    stream=None), or spec_draft_sample(ctx, DraftArgs)."""
+    a = args[0] if len(args) == 1 and isinstance(args[0], DraftArgs) else make_draft_args(*args, **kwargs)
+    st = lib().spec_draft_sample(ctx, ctypes.byref(a), _stream_handle(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "spec_draft_sample")
 
 
 def spec_verify_synthetic_rates(mean_length: float, k: int) -> list:

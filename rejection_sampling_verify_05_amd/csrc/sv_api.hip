@@ -28,6 +28,8 @@ struct sv_ctx {
   int32_t *cand_idx;
   int32_t *cand_n;
   float *cand_tau;
+  int32_t *zeros;    // [max_reqs + 1] zero prefix sums (draft-side sampling: one bonus-only row per request)
+  int32_t *scratch_ns, *scratch_nr;  // [max_reqs] (draft-side sampling)
   unsigned int *err;
   hipEvent_t *ev;   // measurement: 4 events per recorded call
   int32_t ev_cap, ev_n;
@@ -47,8 +49,8 @@ void free_events(sv_ctx *c) {
 
 void free_ctx(sv_ctx *c) {
   free_events(c);
-  void *ptrs[] = {c->chunk_tab, c->row_info, c->res_req,  c->res_tab, c->res_list,
-                  c->cand_val,  c->cand_idx, c->cand_n,   c->cand_tau, c->err};
+  void *ptrs[] = {c->chunk_tab, c->row_info, c->res_req, c->res_tab,    c->res_list,   c->cand_val,
+                  c->cand_idx,  c->cand_n,   c->cand_tau, c->zeros,      c->scratch_ns, c->scratch_nr, c->err};
   for (void *p : ptrs)
     if (p) (void)hipFree(p);
   delete c;
@@ -89,10 +91,12 @@ extern "C" int spec_verify_create(sv_ctx **out, int32_t max_rows, int32_t max_re
             dev_alloc(&c->res_tab, reqs * ncs) && dev_alloc(&c->res_list, reqs + 1) && dev_alloc(&c->err, 1);
   // Row states and thresholds (top-k and top-p); candidate lists only for top-k.
   if (ok) ok = dev_alloc(&c->cand_n, rows) && dev_alloc(&c->cand_tau, rows);
+  if (ok) ok = dev_alloc(&c->zeros, reqs + 1) && dev_alloc(&c->scratch_ns, reqs) && dev_alloc(&c->scratch_nr, reqs);
   if (ok && (flags & SV_CREATE_TOPK))
     ok = dev_alloc(&c->cand_val, rows * sv::kCandCap) && dev_alloc(&c->cand_idx, rows * sv::kCandCap);
   if (ok)
     ok = hipMemset(c->res_req, 0, reqs * sizeof(int4)) == hipSuccess &&
+         hipMemset(c->zeros, 0, (reqs + 1) * sizeof(int32_t)) == hipSuccess &&
          hipMemset(c->res_list, 0, sizeof(int)) == hipSuccess &&
          hipMemset(c->err, 0, sizeof(unsigned int)) == hipSuccess && hipDeviceSynchronize() == hipSuccess;
   int ncu = 0;
@@ -130,6 +134,11 @@ extern "C" int spec_verify_run(sv_ctx *ctx, const sv_verify_args *a, hipStream_t
   if (D > 0 && !a->draft_ids) return SV_EINVAL;
   if (a->logits_row_stride < a->vocab_size) return SV_EINVAL;
   if (a->draft_probs && a->draft_row_stride < a->vocab_size) return SV_EINVAL;
+  if (a->draft_logits || a->draft_stats || a->draft_temperature) {  // draft-logits mode: all three
+    if (!a->draft_logits || !a->draft_stats || !a->draft_temperature || a->draft_probs) return SV_EINVAL;
+    if (a->draft_logits_stride < a->vocab_size) return SV_EINVAL;
+    if (a->draft_logits_dtype != SV_F32 && a->draft_logits_dtype != SV_BF16) return SV_EDTYPE;
+  }
   if (a->offset >> 32) return SV_EINVAL;
   const bool penalty = a->rep_penalty || a->frequency_penalty || a->presence_penalty;
   if (penalty && (!a->idx_mapping || !a->output_bin_counts || a->num_slots < 1)) return SV_EINVAL;
@@ -156,6 +165,11 @@ extern "C" int spec_verify_run(sv_ctx *ctx, const sv_verify_args *a, hipStream_t
   p.rep_penalty = a->rep_penalty;
   p.idx_mapping = a->idx_mapping;
   p.counts = a->output_bin_counts;
+  p.draft_logits = a->draft_logits;
+  p.draft_stats = a->draft_stats;
+  p.draft_temp = a->draft_temperature;
+  p.dlstride = a->draft_logits ? a->draft_logits_stride : 0;
+  p.ddtype = a->draft_logits_dtype;
   p.freq_penalty = a->frequency_penalty;
   p.pres_penalty = a->presence_penalty;
   p.top_p = a->top_p;
@@ -233,7 +247,8 @@ extern "C" int spec_verify_run(sv_ctx *ctx, const sv_verify_args *a, hipStream_t
     ctx->res_dirty = false;
   }
   if (p.has_topk && sv::launch_topk(p, stream) != hipSuccess) return SV_EHIP;
-  ctx->res_dirty = p.draft_probs != nullptr;  // until the residual race has zeroed the count
+  const bool resid = p.draft_probs != nullptr || p.draft_logits != nullptr;
+  ctx->res_dirty = resid;  // until the residual race has zeroed the count
   if (sv::launch_stats(p, stream, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr) != hipSuccess) return SV_EHIP;
   if (p.has_topp) {
     // Top-p on dense rows, then their statistics again under the threshold
@@ -252,11 +267,91 @@ extern "C" int spec_verify_run(sv_ctx *ctx, const sv_verify_args *a, hipStream_t
     if (sv::launch_stats(p2, stream, nullptr, nullptr) != hipSuccess) return SV_EHIP;
   }
   if (sv::launch_epilogue(p, stream, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr) != hipSuccess) return SV_EHIP;
-  if (p.draft_probs) {
+  if (resid) {
     if (sv::launch_resid(p, stream) != hipSuccess) return SV_EHIP;
     ctx->res_dirty = false;
   }
   if (p.dbg_probs && sv::launch_dbg_probs(p, stream) != hipSuccess) return SV_EHIP;
+  return SV_OK;
+}
+
+extern "C" int spec_draft_sample(sv_ctx *ctx, const sv_draft_args *a, hipStream_t stream) {
+  if (!ctx || !a) return SV_EINVAL;
+  if (a->logits_dtype != SV_F32 && a->logits_dtype != SV_BF16) return SV_EDTYPE;
+  if (a->num_reqs < 0 || a->vocab_size <= 0 || a->step < 0) return SV_EINVAL;
+  if (a->num_reqs == 0) return SV_OK;
+  if (a->num_reqs > ctx->max_reqs || a->num_reqs > ctx->max_rows || a->vocab_size > ctx->max_vocab)
+    return SV_ECAPACITY;
+  if (!a->draft_logits || !a->temperature || !a->cu_num_draft || !a->out_tokens || !a->draft_stats)
+    return SV_EINVAL;
+  if (a->logits_row_stride < a->vocab_size || (a->offset >> 32)) return SV_EINVAL;
+
+  // The draft rows as a verify call of bonus-only requests (all cu zero), with
+  // the race keyed by each request's draft row and the draft tags.
+  sv::Params p;
+  memset(&p, 0, sizeof p);
+  p.logits = a->draft_logits;
+  p.cu = ctx->zeros;
+  p.temperature = a->temperature;
+  p.out_tokens = a->out_tokens;
+  p.out_ns = ctx->scratch_ns;
+  p.out_nr = ctx->scratch_nr;
+  p.chunk_tab = ctx->chunk_tab;
+  p.row_info = ctx->row_info;
+  p.res_req = ctx->res_req;
+  p.res_tab = ctx->res_tab;
+  p.res_list = ctx->res_list;
+  p.cand_val = ctx->cand_val;
+  p.cand_idx = ctx->cand_idx;
+  p.cand_n = ctx->cand_n;
+  p.cand_tau = ctx->cand_tau;
+  p.err = ctx->err;
+  p.lstride = a->logits_row_stride;
+  p.dtype = a->logits_dtype;
+  p.R = a->num_reqs;
+  p.B = a->num_reqs;
+  p.D = 0;
+  p.V = a->vocab_size;
+  p.NC = (a->vocab_size + sv::kChunk - 1) / sv::kChunk;
+  p.nc_stride = ctx->nc_stride;
+  p.cps = sv::kResidCPS;
+  p.nseg = (p.NC + p.cps - 1) / p.cps;
+  p.resid_grid = 1;
+  const int esize = a->logits_dtype == SV_BF16 ? 2 : 4;
+  p.vec_ok = ((uintptr_t)a->draft_logits % 16 == 0) && ((a->logits_row_stride * esize) % 16 == 0);
+  p.fast = p.vec_ok && a->vocab_size % (16 / esize) == 0;
+  {
+    const int64_t chunks = (int64_t)p.R * p.NC;
+    if (chunks > 0x7FFFFFFF) return SV_ECAPACITY;
+    const int64_t per = (int64_t)(sv::kSliceRows - 1) * p.NC + 1;
+    int64_t grid = ctx->resident[a->logits_dtype][p.fast ? 1 : 0];
+    if (grid * per < chunks) grid = (chunks + per - 1) / per;
+    if (grid > chunks) grid = chunks;
+    p.stats_grid = (int32_t)grid;
+  }
+  p.out_stride = 1;
+  p.seed_lo = (uint32_t)(a->seed & 0xFFFFFFFFu);
+  p.seed_hi = (uint32_t)(a->seed >> 32);
+  p.offset = (uint32_t)a->offset;
+  ctx->epoch = ctx->epoch == 0xFFFFFFFFu ? 1u : ctx->epoch + 1u;
+  p.epoch = ctx->epoch;
+  p.key_cu = a->cu_num_draft;
+  p.key_step = a->step;
+  p.tag_shift = 2;  // chunk tag 1 -> 3, token tag 2 -> 4
+
+  sv::DraftOut o;
+  o.cu = a->cu_num_draft;
+  o.step = a->step;
+  o.tokens = a->out_tokens;
+  o.q = a->out_q;
+  o.stats = a->draft_stats;
+  if (ctx->res_dirty) {
+    if (sv::launch_zero_count(ctx->res_list, stream) != hipSuccess) return SV_EHIP;
+    ctx->res_dirty = false;
+  }
+  if (sv::launch_stats(p, stream, nullptr, nullptr) != hipSuccess) return SV_EHIP;
+  if (sv::launch_epilogue(p, stream, nullptr, nullptr) != hipSuccess) return SV_EHIP;
+  if (sv::launch_draft_finish(p, o, stream) != hipSuccess) return SV_EHIP;
   return SV_OK;
 }
 

@@ -33,9 +33,11 @@ __device__ __forceinline__ uint4 philox10(uint4 ctr, uint32_t k0, uint32_t k1) {
 
 enum : uint32_t { kTagAccept = 0, kTagChunk = 1, kTagToken = 2 };
 
-// Four consecutive words idx = 4*blk .. 4*blk+3 of stream (g, tag).
+// Four consecutive words idx = 4*blk .. 4*blk+3 of stream (g, tag).  Draft-side
+// sampling keys row g by its draft row key_cu[g] + key_step and shifts the tags.
 __device__ __forceinline__ uint4 rng_block(const Params &p, uint32_t blk, uint32_t g, uint32_t tag) {
-  return philox10(make_uint4(blk, g, tag, p.offset), p.seed_lo, p.seed_hi);
+  const uint32_t row = p.key_cu != nullptr ? (uint32_t)(p.key_cu[g] + p.key_step) : g;
+  return philox10(make_uint4(blk, row, tag + p.tag_shift, p.offset), p.seed_lo, p.seed_hi);
 }
 
 __device__ __forceinline__ uint32_t pick(uint4 w, int k) {
@@ -243,6 +245,14 @@ __device__ __forceinline__ float load_logit(const Params &p, int64_t row, int x)
     return bf16_bits_to_f32(b[row * p.lstride + x]);
   }
   return static_cast<const float *>(p.logits)[row * p.lstride + x];
+}
+
+__device__ __forceinline__ float load_draft_logit(const Params &p, int64_t row, int x) {
+  if (p.ddtype == 1) {
+    const uint16_t *b = static_cast<const uint16_t *>(p.draft_logits);
+    return bf16_bits_to_f32(b[row * p.dlstride + x]);
+  }
+  return static_cast<const float *>(p.draft_logits)[row * p.dlstride + x];
 }
 
 // Per-request logit processing (penalty, then the top-k threshold).

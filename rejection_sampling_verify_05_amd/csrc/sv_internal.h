@@ -43,6 +43,11 @@ struct Params {
   const float *freq_penalty;
   const float *pres_penalty;
   const float *top_p;
+  // draft-logits mode: q_i(x) = exp2(aq (zq_x - m_q)) / s_q from the draft row
+  // and its (m_q, s_q) pair; aq = log2(e) / draft temperature
+  const void *draft_logits;
+  const float *draft_stats;   // [2 D]
+  const float *draft_temp;    // [B]
   // outputs
   int32_t *out_tokens;
   int32_t *out_ns;
@@ -64,6 +69,8 @@ struct Params {
   // sizes and scalars
   int64_t lstride;
   int64_t dstride;
+  int64_t dlstride;  // draft-logits row stride (elements)
+  int32_t ddtype;    // draft-logits dtype
   int32_t dtype;
   int32_t R, B, D, V;
   int32_t NC;        // ceil(V / kChunk)
@@ -84,6 +91,20 @@ struct Params {
   uint32_t epoch;
   int32_t synthetic;  // synthetic acceptance with the rates below
   float syn[kMaxDrafts]; // unconditional acceptance rates of draft positions 1..
+  // Random stream rows and tags: row key_cu[g] + key_step instead of g when
+  // key_cu is set (draft-side sampling), tags shifted by tag_shift.
+  const int32_t *key_cu;
+  int32_t key_step;
+  uint32_t tag_shift;
+};
+
+// Draft-side sampling: outputs of one spec_draft_sample call.
+struct DraftOut {
+  const int32_t *cu;     // [B + 1] prefix sums of the verify call
+  int32_t step;
+  int32_t *tokens;       // [B]
+  float *q;              // [B] or null
+  float *stats;          // [2 D]
 };
 
 struct PostParams {
@@ -103,6 +124,7 @@ hipError_t launch_resid(const Params &p, hipStream_t s);
 // Zeroes the residual-request count (after a call that stopped before the residual race).
 hipError_t launch_zero_count(int *count, hipStream_t s);
 hipError_t launch_dbg_probs(const Params &p, hipStream_t s);
+hipError_t launch_draft_finish(const Params &p, const DraftOut &o, hipStream_t s);
 hipError_t launch_post_update(const PostParams &p, hipStream_t s);
 // Resident stats workgroups per CU (occupancy query); kind 0 general pass,
 // 1 fast pass, 2 fast pass with penalties.

@@ -43,6 +43,8 @@ struct Req {
   unsigned errbits;  // device errors this request raises
   bool cu_ok;        // its own cu entries are consistent
   float top_p;       // nucleus mass in [1e-6, 1]; 1: off
+  bool has_q;        // the drafts carry a distribution q (probabilities, or draft logits at T_q > 0)
+  float aq;          // log2(e) / T_q (draft-logits mode)
   Proc proc;         // penalty part (tau set per row)
 };
 
@@ -112,6 +114,18 @@ __device__ __forceinline__ Req make_req(const Params &p, int r, int c0, int c1, 
       q.errbits |= SV_ERR_SLOT;
     } else {
       q.proc.counts = p.counts + (int64_t)slot * p.V;
+    }
+  }
+  q.has_q = p.draft_probs != nullptr;
+  q.aq = 0.0f;
+  if (p.draft_logits != nullptr) {  // draft-logits mode; greedy drafts (T_q = 0) act as draft ids only
+    const float tq = p.draft_temp[r];
+    if (!(tq >= 0.0f) || !__builtin_isfinite(tq)) {
+      q.mode = kModeInvalid;
+      q.errbits |= SV_ERR_TEMPERATURE;
+    } else if (tq > 0.0f) {
+      q.has_q = true;
+      q.aq = kLog2e / tq;
     }
   }
   if (p.top_p != nullptr) {
@@ -184,6 +198,16 @@ __device__ __forceinline__ Req lookup_req(const Params &p, int g) {
 __device__ __forceinline__ int row_state(const Params &p, int g) { return p.cand_valid ? p.cand_n[g] : kRowDense; }
 
 __device__ __forceinline__ float exp2_acc(float t) { return __builtin_amdgcn_exp2f(t); }
+
+// q_i(x) of request q's draft row i: stored probability, or from the draft
+// logits and the row's (m_q, s_q) (the draft-side sampler's formula).
+__device__ __forceinline__ float draft_q_of(const Params &p, const Req &q, int i, int x) {
+  const int64_t dr = q.c0 + i;
+  if (p.draft_probs != nullptr) return p.draft_probs[dr * p.dstride + x];
+  const float mq = p.draft_stats[2 * dr], sq = p.draft_stats[2 * dr + 1];
+  return exp2_acc(q.aq * (load_draft_logit(p, dr, x) - mq)) / sq;
+}
+
 
 // ---------------------------------------------------------------------------
 // Chunk decoding.  A wave reads one chunk of kChunk tokens with 16-byte loads:
@@ -515,7 +539,7 @@ template <class EF>
 __device__ __forceinline__ void spec_issue(const Params &p, const Req &q, int i, int d, float m, EF ent, RowSpec &rs,
                                            const ChunkNoise &cn) {
   const int g = q.g0 + i;
-  const bool excl = i < q.K && !p.draft_probs && d >= 0 && d < p.V;
+  const bool excl = i < q.K && !q.has_q && d >= 0 && d < p.V;
   rs.cd = excl ? d / kChunk : -1;
   rs.rcd = 0.0f;
   rs.w1 = wave_chunk_race(p, g, ent, q.a, m, rs.cd, cn, &rs.rcd);
@@ -691,14 +715,14 @@ __device__ __forceinline__ void request_epilogue(const Params &p, const Req &q, 
         load_chunk16(p, g, lc, rs.zc);
         am = wave_first_equal(p, lc, rs.zc, pr, m);
       }
-    } else if (st < 0 && spec && (!p.draft_probs || i == K)) {
+    } else if (st < 0 && spec && (!q.has_q || i == K)) {
       spec_issue(p, q, i, d, m, ent, rs, cn);
       if (rs.cd >= 0) spec_draft_record(p, q, d, pr, rs, ent(rs.cd).x, zd, sx);
       spec_publish(rs, wave, sh);
     } else if (valid_d) {
       // single loads: z_d (and q(d)) for the accept test
       zd = apply_proc(load_logit(p, g, d), d, pr);
-      if (p.draft_probs) qd = p.draft_probs[(int64_t)(q.c0 + i) * p.dstride + d];
+      if (q.has_q) qd = draft_q_of(p, q, i, d);
     }
     if (lane == 0) {
       sh.m[i] = m;
@@ -744,10 +768,10 @@ __device__ __forceinline__ void request_epilogue(const Params &p, const Req &q, 
       } else {
         const bool valid = d >= 0 && d < p.V;
         float pd = 0.0f;
-        double qd = p.draft_probs ? 0.0 : 1.0;
+        double qd = q.has_q ? 0.0 : 1.0;
         if (valid) {
           pd = exp2_acc(q.a * (sh.zd[lane] - sh.m[lane])) / sh.s[lane];
-          if (p.draft_probs) qd = (double)sh.qd[lane];
+          if (q.has_q) qd = (double)sh.qd[lane];
         }
         const double u = u_accept(rng_block(p, 0, (uint32_t)g, kTagAccept).x);
         rej = !(valid && qd > 0.0 && (double)pd >= u * qd);
@@ -795,15 +819,15 @@ __device__ __forceinline__ void request_epilogue(const Params &p, const Req &q, 
     __syncthreads();  // the LDS chunk-table cache is reused for the candidates
     const float *cv = p.cand_val + (int64_t)gs * kCandCap;
     const int32_t *cix = p.cand_idx + (int64_t)gs * kCandCap;
-    const float *qrow = (rejected && p.draft_probs) ? p.draft_probs + (int64_t)(q.c0 + j) * p.dstride : nullptr;
+    const bool qres = rejected && q.has_q;
     float part = 0.0f;
     for (int t = tid; t < st; t += kThreads) {
       const int x = cix[t];
       const float pxv = exp2_acc(a * (cv[t] - m)) / s;
       float w = pxv;
       if (rejected) {
-        if (qrow)
-          w = fmaxf(pxv - qrow[x], 0.0f);
+        if (qres)
+          w = fmaxf(pxv - draft_q_of(p, q, j, x), 0.0f);
         else if (x == dj)
           w = 0.0f;
       }
@@ -820,7 +844,7 @@ __device__ __forceinline__ void request_epilogue(const Params &p, const Req &q, 
     return;
   }
 
-  if (rejected && p.draft_probs) {
+  if (rejected && q.has_q) {
     // Dense residual: handed to resid_kernel (needs the full draft row).
     if (tid == 0) {
       p.res_req[r] = make_int4(gs, j, dj, (int)p.epoch);
@@ -1279,14 +1303,13 @@ __global__ __launch_bounds__(kThreads) void resid_kernel(Params p) {
     const float m = ri.x, inv_s = 1.0f / ri.y, a = q.a;
     Proc pr = q.proc;
     if (row_has_tau(__float_as_int(ri.w))) pr.tau = p.cand_tau[gs];
-    const float *qrow = p.draft_probs + (int64_t)(q.c0 + j) * p.dstride;
     float *rt = p.res_tab + (int64_t)r * p.nc_stride;
     for (int c = seg * p.cps + wave; c < min(p.NC, (seg + 1) * p.cps); c += kWaves) {
       // 16 tokens per lane, all loads issued before any use
       float z[16], qx[16];
       load_chunk16(p, gs, c, z);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) qx[e] = qrow[min(c16_tok(c, e, lane), p.V - 1)];
+      for (int e = 0; e < 16; ++e) qx[e] = draft_q_of(p, q, j, min(c16_tok(c, e, lane), p.V - 1));
       float acc = 0.0f;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
@@ -1314,7 +1337,6 @@ __global__ __launch_bounds__(kThreads) void resid_race_kernel(Params p) {
   const float m = ri.x, inv_s = 1.0f / ri.y, a = q.a;
   Proc pr = q.proc;
   if (row_has_tau(__float_as_int(ri.w))) pr.tau = p.cand_tau[gs];
-  const float *qrow = p.draft_probs + (int64_t)(q.c0 + j) * p.dstride;
   const float *rt = p.res_tab + (int64_t)r * p.nc_stride;
   // An empty residual (rounding) falls back to racing over p_j.
   float part = 0.0f;
@@ -1334,7 +1356,7 @@ __global__ __launch_bounds__(kThreads) void resid_race_kernel(Params p) {
     for (int k = 0; k < 4; ++k) {  // all loads first
       const int xc = min(x0 + k, p.V - 1);
       z[k] = load_logit(p, gs, xc);
-      qx[k] = qrow[xc];
+      qx[k] = draft_q_of(p, q, j, xc);
     }
     const uint4 w4 = rng_block(p, (uint32_t)x0 >> 2, (uint32_t)gs, kTagToken);
     ArgMax best{-1.0f, 0x7FFFFFFF};
@@ -2294,6 +2316,38 @@ __global__ __launch_bounds__(kThreads) void post_update_kernel(PostParams p) {
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
+// Draft-side sampling: after the streaming pass and the epilogue ran over the
+// draft rows as bonus-only requests (race rows keyed by the draft row, draft
+// tags), record q(d) and the row's (m, s) at its draft row cu[r] + step.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void draft_finish_kernel(Params p, DraftOut o) {
+  const int r = blockIdx.x * kThreads + threadIdx.x;
+  if (r >= p.B) return;
+  const int K = o.cu[r + 1] - o.cu[r];
+  if (o.step >= K) {  // no draft at this position for request r
+    o.tokens[r] = -1;
+    if (o.q) o.q[r] = 0.0f;
+    return;
+  }
+  const int d = o.tokens[r];
+  const float4 ri = p.row_info[r];
+  const int64_t dr = (int64_t)o.cu[r] + o.step;
+  o.stats[2 * dr] = ri.x;
+  o.stats[2 * dr + 1] = ri.y;
+  if (o.q) {
+    const float T = p.temperature[r];
+    float qd = d >= 0 ? 1.0f : 0.0f;
+    if (d >= 0 && T > 0.0f) qd = exp2_acc((kLog2e / T) * (load_logit(p, r, d) - ri.x)) / ri.y;
+    o.q[r] = qd;
+  }
+}
+
+hipError_t launch_draft_finish(const Params &p, const DraftOut &o, hipStream_t s) {
+  draft_finish_kernel<<<dim3((unsigned)((p.B + kThreads - 1) / kThreads)), dim3(kThreads), 0, s>>>(p, o);
+  return hipGetLastError();
+}
+
 hipError_t launch_topk(const Params &p, hipStream_t s) {
   if (p.dtype == 1)
     topk_kernel<1><<<dim3(p.R), dim3(kThreads), 0, s>>>(p);

@@ -74,6 +74,9 @@ def run_gpu(ctx: Ctx, inp: dict, seed=0, offset=0, dbg_probs=False, out_stride=N
                        seed=seed, offset=offset, dbg_p_draft=pd if D else None, dbg_probs=probs,
                        frequency_penalty=inp.get("freq"), presence_penalty=inp.get("pres"),
                        top_p=inp.get("top_p"), synthetic_rates=inp.get("synthetic_rates"),
+                       draft_logits=inp.get("draft_logits") if inp.get("draft_stats") is not None else None,
+                       draft_stats=inp.get("draft_stats"),
+                       draft_temperature=inp.get("draft_temp") if inp.get("draft_stats") is not None else None,
                        stream=stream)
     err = sv.spec_verify_read_error(ctx.h, stream)
     res = dict(tokens=out.cpu().numpy(), num_sampled=ns.cpu().numpy(),
@@ -81,6 +84,59 @@ def run_gpu(ctx: Ctx, inp: dict, seed=0, offset=0, dbg_probs=False, out_stride=N
     if probs is not None:
         res["probs"] = probs.cpu().numpy()
     return res
+
+
+def run_draft_steps(ctx: Ctx, inp: dict, seed=0, offset=0):
+    """Draw every draft token with spec_draft_sample, one call per draft
+    position, from the rows of inp["draft_logits"]; fills inp["draft_ids"] and
+    inp["draft_stats"] and returns the per-draft-row q(d) (host)."""
+    B, D, V = inp["B"], inp["D"], inp["V"]
+    dev = inp["logits"].device
+    cu = inp["cu"]
+    K = inp["K"]
+    kmax = int(K.max().item()) if B else 0
+    stats = torch.full((2 * max(D, 1),), -7.0, dtype=torch.float32, device=dev)
+    qd = torch.zeros(max(D, 1), dtype=torch.float32, device=dev)
+    ids = torch.full((max(D, 1),), -7, dtype=torch.int32, device=dev)
+    r_idx = torch.arange(B, device=dev)
+    for step in range(kmax):
+        rows = torch.clamp(cu[:-1].long() + step, max=max(D - 1, 0))  # requests without this step read any row
+        dl = inp["draft_logits"][rows].contiguous()
+        tok = torch.full((B,), -7, dtype=torch.int32, device=dev)
+        q = torch.full((B,), -7.0, dtype=torch.float32, device=dev)
+        sv.spec_draft_sample(ctx.h, dl, inp["draft_temp"], cu, tok, stats, step=step, out_q=q, seed=seed,
+                             offset=offset)
+        has = K > step
+        dst = cu[:-1].long()[has] + step
+        ids[dst] = tok[has]
+        qd[dst] = q[has]
+        assert bool((tok[~has] == -1).all())
+    inp["draft_ids"] = ids[:D]
+    inp["draft_stats"] = stats[: 2 * D]
+    return qd[:D].cpu().numpy()
+
+
+def check_draft_tokens(inp: dict, q_gpu, seed=0, offset=0, C=oracle.RACE_CHUNK, requests=None):
+    """Compare the GPU draft tokens and q(d) with the oracle's draft sampler;
+    returns (n_margin, mismatches)."""
+    cu = inp["cu"].cpu().numpy()
+    lg = inp["draft_logits"]
+    rows = lg.contiguous().view(torch.int16).cpu().numpy().view(np.uint16) if lg.dtype == torch.bfloat16 \
+        else lg.contiguous().cpu().numpy()
+    ids = inp["draft_ids"].cpu().numpy()
+    Tq = inp["draft_temp"].cpu().numpy()
+    bad, n_margin = [], 0
+    for r in (range(inp["B"]) if requests is None else requests):
+        for dr in range(int(cu[r]), int(cu[r + 1])):
+            d, q, mg = oracle.draft_sample(rows[dr], float(Tq[r]), seed, offset, dr, C)
+            if d != ids[dr]:
+                if mg < MARGIN:
+                    n_margin += 1
+                else:
+                    bad.append(f"draft row {dr}: gpu {ids[dr]} oracle {d} margin {mg:.3g}")
+            elif abs(float(q_gpu[dr]) - q) > PROB_ATOL:
+                bad.append(f"draft row {dr}: q(d) gpu {q_gpu[dr]} oracle {q}")
+    return n_margin, bad
 
 
 class OracleRequest:
@@ -117,6 +173,14 @@ class OracleRequest:
         self.q = None
         if inp["draft_probs"] is not None and self.K:
             self.q = inp["draft_probs"][self.c0:self.c1].float().cpu().numpy()
+        self.q64 = None
+        if inp.get("draft_stats") is not None and self.K:
+            tq = float(inp["draft_temp"][r].item())
+            if tq > 0:  # greedy drafts carry no distribution: the draft-ids-only rules
+                dl = inp["draft_logits"][self.c0:self.c1]
+                dl = dl.contiguous().view(torch.int16).cpu().numpy().view(np.uint16) if dl.dtype == torch.bfloat16 \
+                    else dl.contiguous().cpu().numpy()
+                self.q64 = oracle.draft_q_rows(dl, tq)
         self.P, self.amax, self.err, self.topp_margin = self.prepare(0.0)
 
     def prepare(self, shift):
@@ -130,11 +194,11 @@ class OracleRequest:
     def decide_shifted(self, shift, seed=0, offset=0, C=oracle.RACE_CHUNK):
         P, amax, err, _ = self.prepare(shift)
         return oracle.decide_request(P, amax, self.T, self.d, self.q, self.g0, seed, offset, C,
-                                     synthetic_rates=self.syn)
+                                     synthetic_rates=self.syn, draft_q64=self.q64)
 
     def decide(self, seed=0, offset=0, C=oracle.RACE_CHUNK):
         return oracle.decide_request(self.P, self.amax, self.T, self.d, self.q, self.g0, seed,
-                                     offset, C, synthetic_rates=self.syn)
+                                     offset, C, synthetic_rates=self.syn, draft_q64=self.q64)
 
 
 def compare_request(g: dict, r: int, o_tokens, o_ns, o_nr, o_margin, out_stride):

@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol():
     assert names == sorted(["spec_post_update", "spec_verify_create", "spec_verify_destroy",
                             "spec_verify_profile_read", "spec_verify_profile_start",
                             "spec_verify_read_error", "spec_verify_run", "spec_verify_strerror",
-                            "spec_verify_synthetic_rates"])
+                            "spec_verify_synthetic_rates", "spec_draft_sample"])
     L = ctypes.CDLL(sv.library_path())
     for n in names:
         assert hasattr(L, n), n
@@ -56,6 +56,12 @@ int main(void) {
   F(sv_verify_args, seed) F(sv_verify_args, offset) F(sv_verify_args, logits_dtype)
   F(sv_verify_args, num_rows) F(sv_verify_args, num_slots) F(sv_verify_args, frequency_penalty)
   F(sv_verify_args, presence_penalty) F(sv_verify_args, top_p) F(sv_verify_args, synthetic_rates)
+  F(sv_verify_args, draft_logits) F(sv_verify_args, draft_stats) F(sv_verify_args, draft_temperature)
+  F(sv_verify_args, draft_logits_stride) F(sv_verify_args, draft_logits_dtype)
+  printf("sv_draft_args %zu\n", sizeof(sv_draft_args));
+  F(sv_draft_args, draft_logits) F(sv_draft_args, out_q) F(sv_draft_args, draft_stats)
+  F(sv_draft_args, logits_row_stride) F(sv_draft_args, seed) F(sv_draft_args, offset)
+  F(sv_draft_args, logits_dtype) F(sv_draft_args, step)
   F(sv_post_update_args, num_computed_tokens) F(sv_post_update_args, num_reqs)
   F(sv_post_update_args, num_slots)
   return 0;
@@ -74,11 +80,12 @@ int main(void) {
         got[parts[0]] = tuple(int(x) for x in parts[1:])
     assert got["sv_verify_args"] == (ctypes.sizeof(sv.VerifyArgs),)
     assert got["sv_post_update_args"] == (ctypes.sizeof(sv.PostUpdateArgs),)
+    assert got["sv_draft_args"] == (ctypes.sizeof(sv.DraftArgs),)
     for key, val in got.items():
         if "." not in key:
             continue
         struct, field = key.split(".")
-        cls = sv.VerifyArgs if struct == "sv_verify_args" else sv.PostUpdateArgs
+        cls = {"sv_verify_args": sv.VerifyArgs, "sv_draft_args": sv.DraftArgs}.get(struct, sv.PostUpdateArgs)
         f = getattr(cls, field)
         assert (f.offset, f.size) == val, key
 
@@ -109,6 +116,14 @@ def test_strerror_and_host_checks_without_gpu():
     pa.tokens_stride = 0
     assert L.spec_post_update(fake, ctypes.byref(pa), None) == sv.SV_EINVAL
     assert L.spec_verify_read_error(None, None, None) == sv.SV_EINVAL
+    da = sv.DraftArgs()
+    assert L.spec_draft_sample(None, ctypes.byref(da), None) == sv.SV_EINVAL
+    da.logits_dtype = 9
+    assert L.spec_draft_sample(fake, ctypes.byref(da), None) == sv.SV_EDTYPE
+    da.logits_dtype = sv.SV_F32
+    da.step = -1
+    da.vocab_size = 4
+    assert L.spec_draft_sample(fake, ctypes.byref(da), None) == sv.SV_EINVAL
     assert L.spec_verify_profile_start(None, 4) == sv.SV_EINVAL
     assert L.spec_verify_profile_start(fake, 0) == sv.SV_EINVAL
     n = ctypes.c_int32(7)

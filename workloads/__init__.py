@@ -55,6 +55,7 @@ class Workload:
     pres: float = 0.0            # presence penalty of most requests (every 5th: none)
     top_p: float = 1.0           # top-p of most requests (every 7th: none)
     synthetic_rates: tuple = ()  # synthetic acceptance rates of positions 1.. (empty: off)
+    draft_logits: bool = False   # keep the draft logits (target dtype) for draft-side sampling
 
     def with_(self, **kw) -> "Workload":
         return replace(self, **kw)
@@ -148,10 +149,15 @@ def make_inputs(w: Workload, device="cpu", salt: int = 0, slots_extra: int = 64)
     drow = cu[:-1].long()[req] + req + pos
     draft_ids = torch.zeros(D, dtype=torch.int32, device=dev)
     draft_probs = None
+    draft_logits = None
+    draft_temp = None
     if D:
         dl = logits[drow].float() * w.draft_mix
         dl.add_(torch.randn(dl.shape, generator=gen, device=dev), alpha=w.draft_noise)
         greedy_req = (T == 0)[req]
+        if w.draft_logits:  # drafts are drawn later by the draft-side sampler
+            draft_logits = dl.to(w.dtype)
+            draft_temp = torch.where(T == 0, torch.zeros_like(T), torch.full_like(T, w.draft_T))
         if w.draft_probs:
             if w.draft_top_k:
                 kth = torch.topk(dl, w.draft_top_k, dim=1).values[:, -1:]
@@ -166,7 +172,7 @@ def make_inputs(w: Workload, device="cpu", salt: int = 0, slots_extra: int = 64)
     return dict(
         workload=w, logits=logits, cu=cu, draft_ids=draft_ids, draft_probs=draft_probs,
         temperature=T, top_k=top_k, rep_penalty=rep, idx_mapping=idx_mapping, counts=counts,
-        freq=freq, pres=pres, top_p=top_p,
+        freq=freq, pres=pres, top_p=top_p, draft_logits=draft_logits, draft_temp=draft_temp,
         synthetic_rates=list(w.synthetic_rates) if w.synthetic_rates else None,
         query_len=(K + 1).to(torch.int32), K=K.to(torch.int32), R=R, D=D, B=B, V=V,
         num_slots=S,
