@@ -28,8 +28,7 @@ struct sv_ctx {
   int32_t *cand_idx;
   int32_t *cand_n;
   float *cand_tau;
-  int32_t *zeros;    // [max_reqs + 1] zero prefix sums (draft-side sampling: one bonus-only row per request)
-  int32_t *scratch_ns, *scratch_nr;  // [max_reqs] (draft-side sampling)
+  int32_t *zeros;    // [max_reqs + 1] zero prefix sums (draft-side sampling: row r is request r)
   unsigned int *err;
   hipEvent_t *ev;   // measurement: 4 events per recorded call
   int32_t ev_cap, ev_n;
@@ -50,7 +49,7 @@ void free_events(sv_ctx *c) {
 void free_ctx(sv_ctx *c) {
   free_events(c);
   void *ptrs[] = {c->chunk_tab, c->row_info, c->res_req, c->res_tab,    c->res_list,   c->cand_val,
-                  c->cand_idx,  c->cand_n,   c->cand_tau, c->zeros,      c->scratch_ns, c->scratch_nr, c->err};
+                  c->cand_idx,  c->cand_n,   c->cand_tau, c->zeros,      c->err};
   for (void *p : ptrs)
     if (p) (void)hipFree(p);
   delete c;
@@ -91,7 +90,7 @@ extern "C" int spec_verify_create(sv_ctx **out, int32_t max_rows, int32_t max_re
             dev_alloc(&c->res_tab, reqs * ncs) && dev_alloc(&c->res_list, reqs + 1) && dev_alloc(&c->err, 1);
   // Row states and thresholds (top-k and top-p); candidate lists only for top-k.
   if (ok) ok = dev_alloc(&c->cand_n, rows) && dev_alloc(&c->cand_tau, rows);
-  if (ok) ok = dev_alloc(&c->zeros, reqs + 1) && dev_alloc(&c->scratch_ns, reqs) && dev_alloc(&c->scratch_nr, reqs);
+  if (ok) ok = dev_alloc(&c->zeros, reqs + 1);
   if (ok && (flags & SV_CREATE_TOPK))
     ok = dev_alloc(&c->cand_val, rows * sv::kCandCap) && dev_alloc(&c->cand_idx, rows * sv::kCandCap);
   if (ok)
@@ -286,16 +285,12 @@ extern "C" int spec_draft_sample(sv_ctx *ctx, const sv_draft_args *a, hipStream_
     return SV_EINVAL;
   if (a->logits_row_stride < a->vocab_size || (a->offset >> 32)) return SV_EINVAL;
 
-  // The draft rows as a verify call of bonus-only requests (all cu zero), with
-  // the race keyed by each request's draft row and the draft tags.
+  // A streaming pass over the draft rows (row r = request r), then the race.
   sv::Params p;
   memset(&p, 0, sizeof p);
   p.logits = a->draft_logits;
   p.cu = ctx->zeros;
   p.temperature = a->temperature;
-  p.out_tokens = a->out_tokens;
-  p.out_ns = ctx->scratch_ns;
-  p.out_nr = ctx->scratch_nr;
   p.chunk_tab = ctx->chunk_tab;
   p.row_info = ctx->row_info;
   p.res_req = ctx->res_req;
@@ -329,15 +324,10 @@ extern "C" int spec_draft_sample(sv_ctx *ctx, const sv_draft_args *a, hipStream_
     if (grid > chunks) grid = chunks;
     p.stats_grid = (int32_t)grid;
   }
-  p.out_stride = 1;
+  p.out_stride = 1;  // each row a request without drafts (its lookups take K = 0)
   p.seed_lo = (uint32_t)(a->seed & 0xFFFFFFFFu);
   p.seed_hi = (uint32_t)(a->seed >> 32);
   p.offset = (uint32_t)a->offset;
-  ctx->epoch = ctx->epoch == 0xFFFFFFFFu ? 1u : ctx->epoch + 1u;
-  p.epoch = ctx->epoch;
-  p.key_cu = a->cu_num_draft;
-  p.key_step = a->step;
-  p.tag_shift = 2;  // chunk tag 1 -> 3, token tag 2 -> 4
 
   sv::DraftOut o;
   o.cu = a->cu_num_draft;
@@ -345,13 +335,8 @@ extern "C" int spec_draft_sample(sv_ctx *ctx, const sv_draft_args *a, hipStream_
   o.tokens = a->out_tokens;
   o.q = a->out_q;
   o.stats = a->draft_stats;
-  if (ctx->res_dirty) {
-    if (sv::launch_zero_count(ctx->res_list, stream) != hipSuccess) return SV_EHIP;
-    ctx->res_dirty = false;
-  }
   if (sv::launch_stats(p, stream, nullptr, nullptr) != hipSuccess) return SV_EHIP;
-  if (sv::launch_epilogue(p, stream, nullptr, nullptr) != hipSuccess) return SV_EHIP;
-  if (sv::launch_draft_finish(p, o, stream) != hipSuccess) return SV_EHIP;
+  if (sv::launch_draft_race(p, o, stream) != hipSuccess) return SV_EHIP;
   return SV_OK;
 }
 

@@ -31,13 +31,11 @@ __device__ __forceinline__ uint4 philox10(uint4 ctr, uint32_t k0, uint32_t k1) {
   return ctr;
 }
 
-enum : uint32_t { kTagAccept = 0, kTagChunk = 1, kTagToken = 2 };
+enum : uint32_t { kTagAccept = 0, kTagChunk = 1, kTagToken = 2, kTagDraftChunk = 3, kTagDraftToken = 4 };
 
-// Four consecutive words idx = 4*blk .. 4*blk+3 of stream (g, tag).  Draft-side
-// sampling keys row g by its draft row key_cu[g] + key_step and shifts the tags.
+// Four consecutive words idx = 4*blk .. 4*blk+3 of stream (g, tag).
 __device__ __forceinline__ uint4 rng_block(const Params &p, uint32_t blk, uint32_t g, uint32_t tag) {
-  const uint32_t row = p.key_cu != nullptr ? (uint32_t)(p.key_cu[g] + p.key_step) : g;
-  return philox10(make_uint4(blk, row, tag + p.tag_shift, p.offset), p.seed_lo, p.seed_hi);
+  return philox10(make_uint4(blk, g, tag, p.offset), p.seed_lo, p.seed_hi);
 }
 
 __device__ __forceinline__ uint32_t pick(uint4 w, int k) {

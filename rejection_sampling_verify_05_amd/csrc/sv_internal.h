@@ -91,11 +91,6 @@ struct Params {
   uint32_t epoch;
   int32_t synthetic;  // synthetic acceptance with the rates below
   float syn[kMaxDrafts]; // unconditional acceptance rates of draft positions 1..
-  // Random stream rows and tags: row key_cu[g] + key_step instead of g when
-  // key_cu is set (draft-side sampling), tags shifted by tag_shift.
-  const int32_t *key_cu;
-  int32_t key_step;
-  uint32_t tag_shift;
 };
 
 // Draft-side sampling: outputs of one spec_draft_sample call.
@@ -124,7 +119,7 @@ hipError_t launch_resid(const Params &p, hipStream_t s);
 // Zeroes the residual-request count (after a call that stopped before the residual race).
 hipError_t launch_zero_count(int *count, hipStream_t s);
 hipError_t launch_dbg_probs(const Params &p, hipStream_t s);
-hipError_t launch_draft_finish(const Params &p, const DraftOut &o, hipStream_t s);
+hipError_t launch_draft_race(const Params &p, const DraftOut &o, hipStream_t s);
 hipError_t launch_post_update(const PostParams &p, hipStream_t s);
 // Resident stats workgroups per CU (occupancy query); kind 0 general pass,
 // 1 fast pass, 2 fast pass with penalties.

@@ -280,12 +280,13 @@ struct EpiShared {
 // Block-level chunk race (all threads call it); thread t takes chunks t,
 // t + 256, ...; W(c) >= 0.  Returns -1 if no chunk has positive weight.
 template <class WF>
-__device__ __forceinline__ int block_chunk_race(const Params &p, uint32_t g, int NC, WF W, BlockScratch &red) {
+__device__ __forceinline__ int block_chunk_race(const Params &p, uint32_t g, int NC, WF W, BlockScratch &red,
+                                                uint32_t tag = kTagChunk) {
   ArgMax best{-1.0f, 0x7FFFFFFF};
   for (int c = threadIdx.x; c < NC; c += kThreads) {
     const float Wc = W(c);
     if (Wc > 0.0f) {
-      const uint4 w4 = rng_block(p, (uint32_t)c >> 2, g, kTagChunk);
+      const uint4 w4 = rng_block(p, (uint32_t)c >> 2, g, tag);
       ArgMax o{race_score(Wc, pick(w4, c & 3)), c};
       if (better(o, best)) best = o;
     }
@@ -454,10 +455,11 @@ __device__ __forceinline__ ArgMax wave_chunk_race(const Params &p, int g, EF ent
 // tokens 4t..4t+3 (one Philox block).  All threads call it; -1 if no token has
 // weight.
 __device__ __forceinline__ int block_token_race(const Params &p, int g, int c, const float *zs, const Proc &pr,
-                                                float a, float hi, int skip, BlockScratch &red) {
+                                                float a, float hi, int skip, BlockScratch &red,
+                                                uint32_t tag = kTagToken) {
   const int t4 = 4 * threadIdx.x;
   const int x0 = c * kChunk + t4;
-  const uint4 w4 = rng_block(p, (uint32_t)x0 >> 2, (uint32_t)g, kTagToken);
+  const uint4 w4 = rng_block(p, (uint32_t)x0 >> 2, (uint32_t)g, tag);
   const float4 z4 = *reinterpret_cast<const float4 *>(zs + t4);
   const float zz[4] = {z4.x, z4.y, z4.z, z4.w};
   ArgMax best{-1.0f, 0x7FFFFFFF};
@@ -2317,34 +2319,96 @@ __global__ __launch_bounds__(kThreads) void post_update_kernel(PostParams p) {
 // Launchers
 // ---------------------------------------------------------------------------
 // ---------------------------------------------------------------------------
-// Draft-side sampling: after the streaming pass and the epilogue ran over the
-// draft rows as bonus-only requests (race rows keyed by the draft row, draft
-// tags), record q(d) and the row's (m, s) at its draft row cu[r] + step.
+// Draft-side sampling, after a streaming pass over this step's draft rows (row
+// r of the call = request r).  One workgroup per request: the row's scale m and
+// mass s from its chunk table, then the two-level race on counter row
+// cu[r] + step (the draft's row in the verify call) with the draft tags, or the
+// argmax (lowest index) when T = 0; q(d) and (m, s) are recorded for the
+// verifier.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) void draft_finish_kernel(Params p, DraftOut o) {
-  const int r = blockIdx.x * kThreads + threadIdx.x;
-  if (r >= p.B) return;
+struct DraftShared {
+  BlockScratch red;
+  float zs[kChunk];
+};
+
+__global__ __launch_bounds__(kThreads) void draft_race_kernel(Params p, DraftOut o) {
+  __shared__ DraftShared sh;
+  const int r = blockIdx.x, tid = threadIdx.x;
   const int K = o.cu[r + 1] - o.cu[r];
-  if (o.step >= K) {  // no draft at this position for request r
-    o.tokens[r] = -1;
-    if (o.q) o.q[r] = 0.0f;
+  const float T = p.temperature[r];
+  const bool bad_t = !(T >= 0.0f) || !__builtin_isfinite(T);
+  if (o.step >= K || bad_t) {  // no draft at this position, or an invalid temperature
+    if (tid == 0) {
+      if (bad_t && o.step < K) raise_err(p, SV_ERR_TEMPERATURE);
+      o.tokens[r] = -1;
+      if (o.q) o.q[r] = 0.0f;
+    }
     return;
   }
-  const int d = o.tokens[r];
-  const float4 ri = p.row_info[r];
-  const int64_t dr = (int64_t)o.cu[r] + o.step;
-  o.stats[2 * dr] = ri.x;
-  o.stats[2 * dr + 1] = ri.y;
-  if (o.q) {
-    const float T = p.temperature[r];
-    float qd = d >= 0 ? 1.0f : 0.0f;
-    if (d >= 0 && T > 0.0f) qd = exp2_acc((kLog2e / T) * (load_logit(p, r, d) - ri.x)) / ri.y;
-    o.q[r] = qd;
+  const uint32_t key = (uint32_t)(o.cu[r] + o.step);
+  const float a = T > 0.0f ? kLog2e / T : 0.0f;
+  const float2 *tab = p.chunk_tab + (int64_t)r * p.nc_stride;
+  float lm = kNegInf;
+  for (int c = tid; c < p.NC; c += kThreads) lm = fmaxf(lm, tab[c].x);
+  const float m = block_max(lm, sh.red);
+  if (!(m > kNegInf)) {
+    if (tid == 0) {
+      raise_err(p, SV_ERR_ROW);
+      o.tokens[r] = -1;
+      if (o.q) o.q[r] = 0.0f;
+    }
+    return;
+  }
+  float ls = 0.0f;
+  for (int c = tid; c < p.NC; c += kThreads) {
+    const float2 e = tab[c];
+    if (e.x > kNegInf) ls += e.y * exp2_acc(a * (e.x - m));
+  }
+  const float s = block_sum(ls, sh.red);
+  int cstar;
+  if (T == 0.0f) {  // the lowest chunk holding the maximum (greedy tables hold exact chunk maxima)
+    ArgMax best{-1.0f, 0x7FFFFFFF};
+    for (int c = tid; c < p.NC; c += kThreads)
+      if (tab[c].x == m && c < best.i) best = ArgMax{1.0f, c};
+    cstar = block_argmax(best, sh.red).i;
+  } else {
+    cstar = block_chunk_race(p, key, p.NC, [&](int c) -> float {
+      const float2 e = tab[c];
+      return e.x > kNegInf ? e.y * exp2_acc(a * (e.x - m)) : 0.0f;
+    }, sh.red, kTagDraftChunk);
+  }
+  int d = -1;
+  if (cstar >= 0) {
+    for (int t = tid; t < kChunk; t += kThreads) {
+      const int x = cstar * kChunk + t;
+      sh.zs[t] = x < p.V ? load_logit(p, r, x) : kNegInf;
+    }
+    __syncthreads();
+    if (T == 0.0f) {  // first token of the chunk equal to the maximum
+      ArgMax best{-1.0f, 0x7FFFFFFF};
+      for (int t = tid; t < kChunk; t += kThreads)
+        if (sh.zs[t] == m && t < best.i) best = ArgMax{1.0f, t};
+      const ArgMax b = block_argmax(best, sh.red);
+      d = b.s < 0.0f ? -1 : cstar * kChunk + b.i;
+    } else {
+      Proc pr;
+      pr.counts = nullptr;
+      pr.theta = 1.0f;
+      pr.freq = pr.pres = 0.0f;
+      pr.tau = kNegInf;
+      d = block_token_race(p, (int)key, cstar, sh.zs, pr, a, a * m, -1, sh.red, kTagDraftToken);
+    }
+  }
+  if (tid == 0) {
+    o.tokens[r] = d;
+    o.stats[2 * (int64_t)key] = m;
+    o.stats[2 * (int64_t)key + 1] = s;
+    if (o.q) o.q[r] = d < 0 ? 0.0f : (T == 0.0f ? 1.0f : exp2_acc(a * (sh.zs[d - cstar * kChunk] - m)) / s);
   }
 }
 
-hipError_t launch_draft_finish(const Params &p, const DraftOut &o, hipStream_t s) {
-  draft_finish_kernel<<<dim3((unsigned)((p.B + kThreads - 1) / kThreads)), dim3(kThreads), 0, s>>>(p, o);
+hipError_t launch_draft_race(const Params &p, const DraftOut &o, hipStream_t s) {
+  draft_race_kernel<<<dim3((unsigned)p.B), dim3(kThreads), 0, s>>>(p, o);
   return hipGetLastError();
 }
 
