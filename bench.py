@@ -63,7 +63,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="3", help="workload id (1, 2, 3, 3k3, 4, 5; with optional "
                     "settings: 3p top-p, 3f frequency/presence penalties, 3s synthetic acceptance, "
-                    "4f and 4p)")
+                    "3d draft-side sampling plus draft-logits verification, 4f and 4p)")
     ap.add_argument("--copies", type=int, default=0, help="input copies to rotate (0: >= 1 GB)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
@@ -117,12 +117,35 @@ def main():
             idx_mapping=c["idx_mapping"], output_bin_counts=c["counts"] if penalty else None,
             seed=1234, offset=0, frequency_penalty=c["freq"], presence_penalty=c["pres"], top_p=c["top_p"],
             synthetic_rates=c["synthetic_rates"])
+        if w.draft_logits:
+            # Draft-side sampling: one call per draft position over that position's
+            # draft-logit rows (gathered once, before timing), writing the draft ids
+            # and row statistics the verify call then reads in draft-logits mode.
+            D = c["D"]
+            stats = torch.zeros(2 * max(D, 1), dtype=torch.float32, device="cuda")
+            o["dargs"] = []
+            for step in range(w.K):
+                rows = torch.clamp(c["cu"][:-1].long() + step, max=max(D - 1, 0))
+                dl = c["draft_logits"][rows].contiguous()
+                o.setdefault("keep", []).append(dl)
+                o["dargs"].append(sv.make_draft_args(
+                    dl, c["draft_temp"], c["cu"], torch.empty(w.B, dtype=torch.int32, device="cuda"), stats,
+                    step=step, seed=1234, offset=0, draft_ids=c["draft_ids"]))
+                o["keep"].append(o["dargs"][-1])
+            o["keep"].append(stats)
+            o["vargs"] = sv.make_verify_args(
+                c["logits"], c["draft_ids"], c["cu"], c["temperature"], o["tokens"], o["ns"], o["nr"],
+                seed=1234, offset=0, draft_logits=c["draft_logits"], draft_stats=stats,
+                draft_temperature=c["draft_temp"])
         o["pargs"] = sv.make_post_update_args(c["idx_mapping"], c["query_len"], o["tokens"], o["ns"],
                                               o["nr"], last, counts, ncomp)
         outs.append(o)
 
     def step(i):
         o = outs[i % ncopies]
+        for da in o.get("dargs", ()):
+            da.offset = i
+            sv.spec_draft_sample(ctx, da, stream=stream)
         o["vargs"].offset = i
         sv.spec_verify_run(ctx, o["vargs"], stream=stream)
         sv.spec_post_update(ctx, o["pargs"], stream=stream)
@@ -238,7 +261,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{w.name}: B={w.B}, K_r {'~U{0..%d}' % w.K if w.ragged else '=%d' % w.K}, "
                                f"V={w.V}, {'bf16' if w.dtype == torch.bfloat16 else 'fp32'} logits, "
-                               f"{'draft probs' if w.draft_probs else 'draft ids only'}",
+                               f"{'draft probs' if w.draft_probs else ('draft logits, drafts sampled in the step' if w.draft_logits else 'draft ids only')}",
                    "global_batch": w.B, "rows_per_step": round(rows_per, 1), "input_copies": ncopies,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

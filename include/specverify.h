@@ -216,7 +216,8 @@ int spec_post_update(sv_ctx *ctx, const sv_post_update_args *args, hipStream_t s
  * verify call's draft arrays) with tags 3 (chunks) and 4 (tokens); T_r = 0
  * takes the argmax (lowest index).  Outputs: out_tokens[r] (-1 when step >=
  * K_r or the request is invalid), out_q[r] = q(d) (1 for greedy; may be NULL),
- * and draft_stats[2 (cu[r] + step) + {0, 1}] = (m, s), the row's scale and
+ * draft_ids[cu[r] + step] = d when draft_ids is given (the verify call's draft
+ * ids), and draft_stats[2 (cu[r] + step) + {0, 1}] = (m, s), the row's scale and
  * mass: q(x) = 2^(log2(e) / T (z_x - m)) / s.  Keep the draft logits rows and
  * pass them with draft_stats and the same temperatures to spec_verify_run
  * (draft-logits mode): no probability rows are stored.  Reads each draft row
@@ -230,6 +231,7 @@ typedef struct sv_draft_args {
   int32_t *out_tokens;          /* [num_reqs]                                             */
   float *out_q;                 /* [num_reqs] or NULL                                     */
   float *draft_stats;           /* [2 D] written at the drafted rows                      */
+  int32_t *draft_ids;           /* [D] or NULL: d also written at draft row cu[r] + step  */
   int64_t logits_row_stride;    /* elements between rows, >= vocab_size                   */
   uint64_t seed;                /* Philox key                                             */
   uint64_t offset;              /* per-call step, must be < 2^32                          */

@@ -99,6 +99,7 @@ class DraftArgs(ctypes.Structure):
         ("out_tokens", ctypes.c_void_p),
         ("out_q", ctypes.c_void_p),
         ("draft_stats", ctypes.c_void_p),
+        ("draft_ids", ctypes.c_void_p),
         ("logits_row_stride", ctypes.c_int64),
         ("seed", ctypes.c_uint64),
         ("offset", ctypes.c_uint64),
@@ -349,7 +350,7 @@ def spec_post_update(ctx, *args, stream=None) -> None:
 
 
 def make_draft_args(draft_logits, temperature, cu_num_draft, out_tokens, draft_stats, *, step: int,
-                    out_q=None, seed=0, offset=0) -> DraftArgs:
+                    out_q=None, seed=0, offset=0, draft_ids=None) -> DraftArgs:
     """Fill an sv_draft_args from torch tensors (no copies, no compute)."""
     import torch
     if draft_logits.dim() != 2 or not draft_logits.is_cuda or draft_logits.stride(1) != 1:
@@ -365,6 +366,7 @@ def make_draft_args(draft_logits, temperature, cu_num_draft, out_tokens, draft_s
     _dev(out_tokens, torch.int32, "out_tokens", 1)
     _dev(out_q, torch.float32, "out_q", 1)
     _dev(draft_stats, torch.float32, "draft_stats", 1)
+    _dev(draft_ids, torch.int32, "draft_ids", 1)
     a = DraftArgs()
     a.draft_logits = draft_logits.data_ptr()
     a.temperature = temperature.data_ptr()
@@ -372,6 +374,7 @@ def make_draft_args(draft_logits, temperature, cu_num_draft, out_tokens, draft_s
     a.out_tokens = out_tokens.data_ptr()
     a.out_q = None if out_q is None else out_q.data_ptr()
     a.draft_stats = draft_stats.data_ptr()
+    a.draft_ids = None if draft_ids is None else draft_ids.data_ptr()
     a.logits_row_stride = draft_logits.stride(0)
     a.seed = int(seed)
     a.offset = int(offset)
@@ -385,7 +388,7 @@ def make_draft_args(draft_logits, temperature, cu_num_draft, out_tokens, draft_s
 def spec_draft_sample(ctx, *args, stream=None, **kwargs) -> None:
     """spec_draft_sample(ctx, draft_logits [B, V], temperature [B], cu_num_draft [B+1],
     out_tokens [B], draft_stats [2 D], step=i, out_q=None, seed=0, offset=0,
-    stream=None), or spec_draft_sample(ctx, DraftArgs)."""
+    draft_ids=None, stream=None), or spec_draft_sample(ctx, DraftArgs)."""
     a = args[0] if len(args) == 1 and isinstance(args[0], DraftArgs) else make_draft_args(*args, **kwargs)
     st = lib().spec_draft_sample(ctx, ctypes.byref(a), _stream_handle(stream))
     if st != SV_OK:

@@ -169,6 +169,8 @@ extern "C" int spec_verify_run(sv_ctx *ctx, const sv_verify_args *a, hipStream_t
   p.draft_temp = a->draft_temperature;
   p.dlstride = a->draft_logits ? a->draft_logits_stride : 0;
   p.ddtype = a->draft_logits_dtype;
+  p.dvec_ok = a->draft_logits && ((uintptr_t)a->draft_logits % 16 == 0) &&
+              ((a->draft_logits_stride * (a->draft_logits_dtype == SV_BF16 ? 2 : 4)) % 16 == 0);
   p.freq_penalty = a->frequency_penalty;
   p.pres_penalty = a->presence_penalty;
   p.top_p = a->top_p;
@@ -335,6 +337,7 @@ extern "C" int spec_draft_sample(sv_ctx *ctx, const sv_draft_args *a, hipStream_
   o.tokens = a->out_tokens;
   o.q = a->out_q;
   o.stats = a->draft_stats;
+  o.ids = a->draft_ids;
   if (sv::launch_stats(p, stream, nullptr, nullptr) != hipSuccess) return SV_EHIP;
   if (sv::launch_draft_race(p, o, stream) != hipSuccess) return SV_EHIP;
   return SV_OK;

@@ -71,6 +71,7 @@ struct Params {
   int64_t dstride;
   int64_t dlstride;  // draft-logits row stride (elements)
   int32_t ddtype;    // draft-logits dtype
+  int32_t dvec_ok;   // draft-logit rows and base 16-byte aligned
   int32_t dtype;
   int32_t R, B, D, V;
   int32_t NC;        // ceil(V / kChunk)
@@ -100,6 +101,7 @@ struct DraftOut {
   int32_t *tokens;       // [B]
   float *q;              // [B] or null
   float *stats;          // [2 D]
+  int32_t *ids;          // [D] or null
 };
 
 struct PostParams {

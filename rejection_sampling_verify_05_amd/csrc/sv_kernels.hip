@@ -204,8 +204,8 @@ __device__ __forceinline__ float exp2_acc(float t) { return __builtin_amdgcn_exp
 __device__ __forceinline__ float draft_q_of(const Params &p, const Req &q, int i, int x) {
   const int64_t dr = q.c0 + i;
   if (p.draft_probs != nullptr) return p.draft_probs[dr * p.dstride + x];
-  const float mq = p.draft_stats[2 * dr], sq = p.draft_stats[2 * dr + 1];
-  return exp2_acc(q.aq * (load_draft_logit(p, dr, x) - mq)) / sq;
+  const float mq = p.draft_stats[2 * dr], inv_sq = 1.0f / p.draft_stats[2 * dr + 1];
+  return exp2_acc(q.aq * (load_draft_logit(p, dr, x) - mq)) * inv_sq;
 }
 
 
@@ -359,41 +359,46 @@ __device__ __forceinline__ int c16_tok(int c, int e, int lane) { return c * kChu
 // to back: with aligned rows and V a multiple of 4, one 8-byte (bf16) or
 // 16-byte (fp32) load per group of 4 tokens (a group at or past V reads group
 // 0 and is masked later); otherwise 16 scalar loads.
-__device__ __forceinline__ void load_chunk16(const Params &p, int g, int c, float (&z)[16]) {
+__device__ __forceinline__ void load_chunk16_at(const void *base, int dtype, int64_t stride, bool vec, int V, int64_t g,
+                                                int c, float (&z)[16]) {
   const int lane = threadIdx.x & 63;
-  if (p.vec_ok && (p.V & 3) == 0) {
-    if (p.dtype == 1) {
-      const uint2 *row = reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.logits) + (int64_t)g * p.lstride);
+  if (vec && (V & 3) == 0) {
+    if (dtype == 1) {
+      const uint2 *row = reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(base) + (int64_t)g * stride);
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int x0 = c16_tok(c, 4 * t, lane);
-        const uint2 w = row[x0 < p.V ? x0 >> 2 : 0];
+        const uint2 w = row[x0 < V ? x0 >> 2 : 0];
         z[4 * t] = __uint_as_float(w.x << 16);
         z[4 * t + 1] = __uint_as_float(w.x & 0xFFFF0000u);
         z[4 * t + 2] = __uint_as_float(w.y << 16);
         z[4 * t + 3] = __uint_as_float(w.y & 0xFFFF0000u);
       }
     } else {
-      const float4 *row = reinterpret_cast<const float4 *>(static_cast<const float *>(p.logits) + (int64_t)g * p.lstride);
+      const float4 *row = reinterpret_cast<const float4 *>(static_cast<const float *>(base) + (int64_t)g * stride);
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int x0 = c16_tok(c, 4 * t, lane);
-        const float4 w = row[x0 < p.V ? x0 >> 2 : 0];
+        const float4 w = row[x0 < V ? x0 >> 2 : 0];
         z[4 * t] = w.x;
         z[4 * t + 1] = w.y;
         z[4 * t + 2] = w.z;
         z[4 * t + 3] = w.w;
       }
     }
-  } else if (p.dtype == 1) {
-    const uint16_t *row = static_cast<const uint16_t *>(p.logits) + (int64_t)g * p.lstride;
+  } else if (dtype == 1) {
+    const uint16_t *row = static_cast<const uint16_t *>(base) + (int64_t)g * stride;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) z[e] = bf16_bits_to_f32(row[min(c16_tok(c, e, lane), p.V - 1)]);
+    for (int e = 0; e < 16; ++e) z[e] = bf16_bits_to_f32(row[min(c16_tok(c, e, lane), V - 1)]);
   } else {
-    const float *row = static_cast<const float *>(p.logits) + (int64_t)g * p.lstride;
+    const float *row = static_cast<const float *>(base) + (int64_t)g * stride;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) z[e] = row[min(c16_tok(c, e, lane), p.V - 1)];
+    for (int e = 0; e < 16; ++e) z[e] = row[min(c16_tok(c, e, lane), V - 1)];
   }
+}
+
+__device__ __forceinline__ void load_chunk16(const Params &p, int g, int c, float (&z)[16]) {
+  load_chunk16_at(p.logits, p.dtype, p.lstride, p.vec_ok, p.V, g, c, z);
 }
 
 // Wave-level chunk race of row g over its chunk table (W_c = s_c exp2(a (r_c - m))),
@@ -1310,8 +1315,16 @@ __global__ __launch_bounds__(kThreads) void resid_kernel(Params p) {
       // 16 tokens per lane, all loads issued before any use
       float z[16], qx[16];
       load_chunk16(p, gs, c, z);
+      if (p.draft_probs != nullptr) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) qx[e] = draft_q_of(p, q, j, min(c16_tok(c, e, lane), p.V - 1));
+        for (int e = 0; e < 16; ++e) qx[e] = draft_q_of(p, q, j, min(c16_tok(c, e, lane), p.V - 1));
+      } else {  // draft-logits mode: the draft row's chunk with vector loads
+        const int64_t dr = q.c0 + j;
+        load_chunk16_at(p.draft_logits, p.ddtype, p.dlstride, p.dvec_ok, p.V, dr, c, qx);
+        const float mq = p.draft_stats[2 * dr], inv_sq = 1.0f / p.draft_stats[2 * dr + 1];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) qx[e] = exp2_acc(q.aq * (qx[e] - mq)) * inv_sq;
+      }
       float acc = 0.0f;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
@@ -2401,6 +2414,7 @@ __global__ __launch_bounds__(kThreads) void draft_race_kernel(Params p, DraftOut
   }
   if (tid == 0) {
     o.tokens[r] = d;
+    if (o.ids) o.ids[key] = d;
     o.stats[2 * (int64_t)key] = m;
     o.stats[2 * (int64_t)key + 1] = s;
     if (o.q) o.q[r] = d < 0 ? 0.0f : (T == 0.0f ? 1.0f : exp2_acc(a * (sh.zs[d - cstar * kChunk] - m)) / s);

@@ -105,10 +105,10 @@ def run_draft_steps(ctx: Ctx, inp: dict, seed=0, offset=0):
         tok = torch.full((B,), -7, dtype=torch.int32, device=dev)
         q = torch.full((B,), -7.0, dtype=torch.float32, device=dev)
         sv.spec_draft_sample(ctx.h, dl, inp["draft_temp"], cu, tok, stats, step=step, out_q=q, seed=seed,
-                             offset=offset)
+                             offset=offset, draft_ids=ids)
         has = K > step
         dst = cu[:-1].long()[has] + step
-        ids[dst] = tok[has]
+        assert bool((ids[dst] == tok[has]).all())  # written at the draft rows by the library
         qd[dst] = q[has]
         assert bool((tok[~has] == -1).all())
     inp["draft_ids"] = ids[:D]

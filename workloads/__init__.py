@@ -84,13 +84,14 @@ CONFIGS.update({
     "3p": CONFIGS["3"].with_(cid="3p", name="no-draft top-p 0.9", top_p=0.9),
     "3f": CONFIGS["3"].with_(cid="3f", name="no-draft freq 0.5 pres 0.3", freq=0.5, pres=0.3, history=512),
     "3s": CONFIGS["3"].with_(cid="3s", name="no-draft synthetic (0.8, 0.6, 0.4)", synthetic_rates=(0.8, 0.6, 0.4)),
+    "3d": CONFIGS["3"].with_(cid="3d", name="draft-side sampling, draft logits bf16 at T 1", draft_logits=True),
     "4f": CONFIGS["4"].with_(cid="4f", name="topk-pen freq 0.5 pres 0.25", freq=0.5, pres=0.25),
     "4p": CONFIGS["4"].with_(cid="4p", name="topk-pen top-p 0.8", top_p=0.8),
 })
 
 
 def _seed_of(cid: str) -> int:
-    return 1000 + {"1": 1, "2": 2, "3": 3, "3k3": 3, "4": 4, "5": 5}.get(cid.rstrip("pfs"), 9)
+    return 1000 + {"1": 1, "2": 2, "3": 3, "3k3": 3, "4": 4, "5": 5}.get(cid.rstrip("pfsd"), 9)
 
 
 def make_inputs(w: Workload, device="cpu", salt: int = 0, slots_extra: int = 64) -> dict:
