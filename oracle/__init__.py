@@ -115,6 +115,11 @@ def lib():
         L.orc_decide_request_q64.argtypes = [P, P, i32, i32, f32, P, P, u32, u64, u32, i32, P, P, P,
                                              P, P]
         L.orc_decide_request_q64.restype = f64
+        L.orc_lm_head_logits.argtypes = [P, P, i64, i32, i32, i32, P]
+        L.orc_lm_head_logits.restype = None
+        L.orc_lm_head_verify.argtypes = [P, i64, P, i64, i32, i32, P, P, i32, P, u64, u64, P, i32, P, P,
+                                         P, P, P]
+        L.orc_lm_head_verify.restype = ctypes.c_uint32
         L.orc_draft_q_rows.argtypes = [P, ctypes.c_int, i64, i32, i32, f32, P]
         L.orc_draft_q_rows.restype = ctypes.c_int
         L.orc_post_update.argtypes = [P, P, P, i32, P, P, i32, i32, i32, P, P, P]
@@ -253,6 +258,50 @@ def draft_q_rows(rows, T: float):
         if err:
             raise ValueError("draft row has no finite maximum")
     return Q
+
+
+# ---- LM head ----------------------------------------------------------------
+def lm_head_logits(h_bits, W_bits, x0: int = 0, x1=None) -> np.ndarray:
+    """fp64 logits of one row: h [d] and W [V, d] as bf16 bit patterns (uint16)."""
+    h = np.ascontiguousarray(h_bits, dtype=np.uint16).reshape(-1)
+    W = np.ascontiguousarray(W_bits, dtype=np.uint16)
+    V, d = W.shape
+    assert h.size == d
+    x1 = V if x1 is None else x1
+    z = np.zeros(x1 - x0, dtype=np.float64)
+    lib().orc_lm_head_logits(_ptr(h), _ptr(W), d, d, x0, x1, _ptr(z))
+    return z
+
+
+def lm_head_verify(hidden_bits, W_bits, cu, draft_ids, temperature, seed: int = 0, offset: int = 0,
+                   out_stride=None):
+    """Verify step on LM-head logits (no-draft-probs mode, one-level race).
+    hidden_bits [R, d] and W_bits [V, d]: bf16 bit patterns (uint16).  Returns a
+    dict with tokens [B, out_stride], num_sampled, num_rejected, margin [B],
+    greedy_gap [B], p_draft [D] and the error mask."""
+    H = np.ascontiguousarray(hidden_bits, dtype=np.uint16)
+    W = np.ascontiguousarray(W_bits, dtype=np.uint16)
+    R, d = H.shape
+    V, d2 = W.shape
+    assert d == d2
+    cu = _c(cu, np.int32)
+    B = cu.size - 1
+    D = R - B
+    if out_stride is None:
+        out_stride = (int(np.max(np.diff(cu))) if B > 0 else 0) + 1
+    dd = _c(draft_ids, np.int32) if D > 0 else np.zeros(1, np.int32)
+    T = _c(temperature, np.float32)
+    tokens = np.full((B, out_stride), -1, dtype=np.int32)
+    ns = np.zeros(B, dtype=np.int32)
+    nr = np.zeros(B, dtype=np.int32)
+    mg = np.zeros(B, dtype=np.float64)
+    gg = np.zeros(B, dtype=np.float64)
+    pd = np.zeros(max(D, 1), dtype=np.float32)
+    err = lib().orc_lm_head_verify(_ptr(H), d, _ptr(W), d, d, V, _ptr(dd), _ptr(cu), B, _ptr(T), seed,
+                                   offset, _ptr(tokens), out_stride, _ptr(ns), _ptr(nr), _ptr(mg),
+                                   _ptr(gg), _ptr(pd))
+    return dict(tokens=tokens, num_sampled=ns, num_rejected=nr, margin=mg, greedy_gap=gg,
+                p_draft=pd[:D], err=int(err))
 
 
 # ---- one request -----------------------------------------------------------

@@ -566,6 +566,120 @@ int orc_draft_q_rows(const void *rows, int dtype, int64_t stride, int32_t K, int
 }
 
 /* ------------------------------------------------------------------------ */
+/* LM head (row f2): the logits the verifier streams are the product of the  */
+/* target rows' hidden states with the LM-head weight (page 3, 7.4: the       */
+/* stats kernel works on the target logits; page 1: the logits come from the  */
+/* LM head).  The plain definition, in fp64.                                 */
+/* ------------------------------------------------------------------------ */
+void orc_lm_head_logits(const uint16_t *h, const uint16_t *W, int64_t wstride, int32_t d, int32_t x0,
+                        int32_t x1, double *z) {
+  double *hd = (double *)malloc(sizeof(double) * (size_t)d);
+  for (int32_t k = 0; k < d; ++k) hd[k] = (double)orc_bf16_to_f32(h[k]);
+  for (int32_t x = x0; x < x1; ++x) {
+    const uint16_t *w = W + (int64_t)x * wstride;
+    double acc = 0.0;
+    for (int32_t k = 0; k < d; ++k) acc += hd[k] * (double)orc_bf16_to_f32(w[k]);
+    z[x - x0] = acc;
+  }
+  free(hd);
+}
+
+/* The verify step on LM-head logits (row f2): for each request the logits of
+ * its K+1 rows come from orc_lm_head_logits (fp64, never rounded to fp32),
+ * then the no-draft-probs rules of 8.3 of "vLLM 投机解码（Eagle / MTP）实现与运行
+ * 流程" with the one-level race (chunk width V, the NO_DRAFT_PROBS Q&A's
+ * argmax(w / E) over all tokens): greedy rows take the first fp64 argmax,
+ * sampled rows p = softmax(z / T) in fp64.  *gap receives, per request, the
+ * smallest fp64 logit gap between the best and second-best token of a greedy
+ * row it used (+inf for sampled requests or V = 1). */
+static int32_t argmax64(const double *z, int32_t V, double *gap) {
+  int32_t best = 0;
+  for (int32_t x = 1; x < V; ++x)
+    if (z[x] > z[best]) best = x;
+  double second = -INFINITY;
+  for (int32_t x = 0; x < V; ++x)
+    if (x != best && z[x] > second) second = z[x];
+  *gap = z[best] - second;
+  return best;
+}
+
+uint32_t orc_lm_head_verify(const uint16_t *hidden, int64_t hstride, const uint16_t *W,
+                            int64_t wstride, int32_t d, int32_t V, const int32_t *draft_ids,
+                            const int32_t *cu, int32_t B, const float *temperature, uint64_t seed,
+                            uint64_t offset, int32_t *out_tokens, int32_t out_stride,
+                            int32_t *num_sampled, int32_t *num_rejected, double *margin,
+                            double *greedy_gap, float *p_draft) {
+  uint32_t err = 0;
+  if ((offset >> 32) != 0) return ORC_ERR_OFFSET;
+  for (int32_t r = 0; r < B; ++r) {
+    for (int32_t t = 0; t < out_stride; ++t) out_tokens[(int64_t)r * out_stride + t] = -1;
+    num_sampled[r] = num_rejected[r] = 0;
+    if (margin) margin[r] = INFINITY;
+    if (greedy_gap) greedy_gap[r] = INFINITY;
+  }
+  for (int32_t r = 0; r <= B; ++r)
+    if (cu[r] < 0 || (r > 0 && cu[r] < cu[r - 1]) || (r > 0 && cu[r] - cu[r - 1] > out_stride - 1))
+      return ORC_ERR_CU;
+  if (cu[0] != 0) return ORC_ERR_CU;
+  for (int32_t r = 0; r < B; ++r) {
+    const int32_t K = cu[r + 1] - cu[r];
+    const int64_t g0 = (int64_t)cu[r] + r;
+    const float T = temperature[r];
+    if (!(T >= 0.0f) || !isfinite(T)) {
+      err |= ORC_ERR_TEMPERATURE;
+      continue;
+    }
+    double *Z = (double *)malloc(sizeof(double) * (size_t)(K + 1) * (size_t)V);
+    double *P = (double *)malloc(sizeof(double) * (size_t)(K + 1) * (size_t)V);
+    int32_t *amax = (int32_t *)malloc(sizeof(int32_t) * (size_t)(K + 1));
+    int bad = 0;
+    for (int32_t i = 0; i <= K; ++i) {
+      double *z = Z + (int64_t)i * V, *p = P + (int64_t)i * V;
+      orc_lm_head_logits(hidden + (g0 + i) * hstride, W, wstride, d, 0, V, z);
+      for (int32_t x = 0; x < V; ++x)
+        if (!isfinite(z[x])) bad = 1;
+      double gap;
+      amax[i] = argmax64(z, V, &gap);
+      if (T == 0.0f) {
+        for (int32_t x = 0; x < V; ++x) p[x] = x == amax[i] ? 1.0 : 0.0;
+      } else {
+        double m = z[amax[i]] / (double)T, s = 0.0;
+        for (int32_t x = 0; x < V; ++x) {
+          p[x] = exp(z[x] / (double)T - m);
+          s += p[x];
+        }
+        for (int32_t x = 0; x < V; ++x) p[x] /= s;
+      }
+    }
+    if (bad) {
+      err |= ORC_ERR_ROW;
+      free(Z), free(P), free(amax);
+      continue;
+    }
+    int32_t ns = 0, nr = 0;
+    float *pd = p_draft ? p_draft + cu[r] : NULL;
+    float pd_tmp[64];
+    const double mg = orc_decide_request(P, amax, K, V, T, draft_ids + cu[r], NULL, V, (uint32_t)g0,
+                                         seed, (uint32_t)offset, V, out_tokens + (int64_t)r * out_stride,
+                                         &ns, &nr, pd ? pd : pd_tmp);
+    num_sampled[r] = ns;
+    num_rejected[r] = nr;
+    if (margin) margin[r] = mg;
+    if (greedy_gap && T == 0.0f) {
+      /* the rows whose argmax decided something: 0 .. num_sampled - 1 */
+      double gmin = INFINITY, gap;
+      for (int32_t i = 0; i < ns; ++i) {
+        argmax64(Z + (int64_t)i * V, V, &gap);
+        if (gap < gmin) gmin = gap;
+      }
+      greedy_gap[r] = gmin;
+    }
+    free(Z), free(P), free(amax);
+  }
+  return err;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Whole call                                                                */
 /* ------------------------------------------------------------------------ */
 uint32_t orc_verify_batch_ex(const void *logits, int dtype, int64_t stride, int32_t num_rows,

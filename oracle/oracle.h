@@ -139,6 +139,26 @@ int32_t orc_race_tags(const double *w, int32_t V, int32_t C, uint64_t seed, uint
 int32_t orc_draft_sample(const void *row, int dtype, int32_t V, float T, uint64_t seed,
                          uint32_t offset, uint32_t key, int32_t C, double *q_token, double *margin);
 
+/* ---- LM head (row f2) ---------------------------------------------------- */
+/* Logits of one row from its hidden state and the LM-head weight: z_x =
+ * sum_k h_k W[x][k] over bf16 inputs (bit patterns), products and sums in fp64
+ * (the plain definition of the matrix product), for tokens x in [x0, x1). */
+void orc_lm_head_logits(const uint16_t *h, const uint16_t *W, int64_t wstride, int32_t d, int32_t x0,
+                        int32_t x1, double *z);
+/* The verify step on LM-head logits, no-draft-probs mode: hidden [R, d] with row
+ * stride hstride, W [V, d] with row stride wstride (bf16 bits); per request the
+ * logits of its rows by orc_lm_head_logits, then greedy (first fp64 argmax) or
+ * p = softmax(z / T) in fp64, and the decisions of orc_decide_request with the
+ * one-level race (chunk width V).  Outputs as orc_verify_batch; greedy_gap [B]
+ * (or NULL) receives each greedy request's smallest top-1 / top-2 logit gap over
+ * the rows it used (+inf otherwise).  Returns the ORC_ERR_* mask. */
+uint32_t orc_lm_head_verify(const uint16_t *hidden, int64_t hstride, const uint16_t *W,
+                            int64_t wstride, int32_t d, int32_t V, const int32_t *draft_ids,
+                            const int32_t *cu, int32_t B, const float *temperature, uint64_t seed,
+                            uint64_t offset, int32_t *out_tokens, int32_t out_stride,
+                            int32_t *num_sampled, int32_t *num_rejected, double *margin,
+                            double *greedy_gap, float *p_draft);
+
 /* fp64 draft distributions softmax(z / T) of K draft rows (stride in elements). */
 int orc_draft_q_rows(const void *rows, int dtype, int64_t stride, int32_t K, int32_t V, float T,
                      double *Q);
