@@ -106,7 +106,8 @@ enum {
 
 /* spec_verify_create flags. */
 enum {
-  SV_CREATE_TOPK = 1u << 0 /* reserve top-k candidate storage (needed for top_k != NULL) */
+  SV_CREATE_TOPK = 1u << 0,   /* reserve top-k candidate storage (needed for top_k != NULL)  */
+  SV_CREATE_LM_HEAD = 1u << 1 /* reserve the LM-head path's tile records (spec_verify_lm_head) */
 };
 
 /*
@@ -253,6 +254,58 @@ int spec_draft_sample(sv_ctx *ctx, const sv_draft_args *args, hipStream_t stream
  */
 int spec_verify_synthetic_rates(float mean_length, int32_t k, float *rates);
 
+/*
+ * Verify step on LM-head logits (NEXT row of the verify step).  The target
+ * logits are z = W h: the hidden states of the target rows times the LM-head
+ * weight ("【vllm】DeepSeekMTP、eagle", compute_logits: the LM head maps the
+ * hidden states of the logit positions to [num_logit_pos, vocab_size]).  The
+ * library computes them with bf16 inputs and fp32 accumulation on the matrix
+ * cores and reduces them in the same kernel to the verify step's statistics
+ * ("speculative decoding in vLLM", 7.4: max, argmax and sum of exp per target
+ * row), so the [num_rows, vocab_size] logits are never written to memory.
+ * Then, as spec_verify_run in no-draft-probs mode without penalties, top-k or
+ * top-p: greedy requests (T = 0) compare each draft with the row's argmax
+ * (lowest index on ties); sampled requests accept d_i iff it is a valid id and
+ * p_i(d_i) >= u_i, and the recovered token (p_j with d_j removed) or the bonus
+ * token is drawn by the exponential race argmax_x p_x / E_x over the whole
+ * vocabulary in one level (the race of the NO_DRAFT_PROBS Q&A of "vLLM
+ * 投机解码（Eagle / MTP）实现与运行流程"; E_x from tag 2 of the row's Philox
+ * stream, as in spec_verify_run; the law is exactly p).  Outputs as
+ * spec_verify_run.  The context must be created with SV_CREATE_LM_HEAD
+ * (records of ceil(max_vocab / 256) x 16 bytes per row).  Cost: one pass over W
+ * (V d bf16) per 128 target rows, shared through L2 by the workgroups of one
+ * token tile, and 2 R V d flops.
+ * Errors: SV_EINVAL (NULL pointer, hidden_size not a positive multiple of 64,
+ * strides below hidden_size or not multiples of 8, bases not 16-byte aligned,
+ * offset >= 2^32), SV_ECAPACITY (sizes beyond the context, or no
+ * SV_CREATE_LM_HEAD), SV_EHIP.  Device-side: SV_ERR_CU, SV_ERR_TEMPERATURE, and
+ * SV_ERR_ROW for a request with a non-finite logit.
+ */
+typedef struct sv_lm_head_args {
+  const void *hidden;           /* [num_rows, hidden_row_stride] bf16 hidden states of the  */
+                                /* target rows (rows ordered as target_logits)              */
+  const void *lm_head;          /* [vocab_size, lm_head_row_stride] bf16 LM-head weight     */
+  const int32_t *draft_ids;     /* [D], D = num_rows - num_reqs                             */
+  const int32_t *cu_num_draft;  /* [num_reqs + 1] as in spec_verify_run                     */
+  const float *temperature;     /* [num_reqs]; 0 = greedy                                   */
+  int32_t *out_tokens;          /* [num_reqs, out_stride], -1 padded                        */
+  int32_t *out_num_sampled;     /* [num_reqs]                                               */
+  int32_t *out_num_rejected;    /* [num_reqs]                                               */
+  float *dbg_p_draft;           /* [D] p_i(d_i) (-1 for greedy requests) or NULL            */
+  float *dbg_logits;            /* [num_rows, vocab_size] fp32 logits or NULL (parity only) */
+  int64_t hidden_row_stride;    /* elements, >= hidden_size, multiple of 8                  */
+  int64_t lm_head_row_stride;   /* elements, >= hidden_size, multiple of 8                  */
+  uint64_t seed;                /* Philox key                                               */
+  uint64_t offset;              /* per-call step, < 2^32                                    */
+  int32_t hidden_size;          /* d, a multiple of 64                                      */
+  int32_t num_rows;             /* R = cu[B] + B                                            */
+  int32_t num_reqs;             /* B                                                        */
+  int32_t vocab_size;           /* V <= max_vocab                                           */
+  int32_t out_stride;           /* row length of out_tokens, <= max_k + 1                   */
+} sv_lm_head_args;
+
+int spec_verify_lm_head(sv_ctx *ctx, const sv_lm_head_args *args, hipStream_t stream);
+
 /* Static string for a return code. */
 const char *spec_verify_strerror(int status);
 
@@ -267,7 +320,8 @@ int spec_verify_read_error(sv_ctx *ctx, uint32_t *host_flags, hipStream_t stream
 /*
  * Measurement.  spec_verify_profile_start makes the next `max_calls` calls of
  * spec_verify_run launch the streaming statistics kernel and the request
- * epilogue kernel with start/stop HIP events that the launch stamps at the
+ * epilogue kernel (of spec_verify_lm_head: the fused LM-head GEMM and its
+ * request kernel) with start/stop HIP events that the launch stamps at the
  * kernel's own start and end on the call's stream (hipExtLaunchKernel), so an
  * interval is that kernel's execution time.  The events are created here
  * (timing only: no system-scope fence, so they add no cache writeback to the

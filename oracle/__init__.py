@@ -118,7 +118,7 @@ def lib():
         L.orc_lm_head_logits.argtypes = [P, P, i64, i32, i32, i32, P]
         L.orc_lm_head_logits.restype = None
         L.orc_lm_head_verify.argtypes = [P, i64, P, i64, i32, i32, P, P, i32, P, u64, u64, P, i32, P, P,
-                                         P, P, P]
+                                         P, P, P, P]
         L.orc_lm_head_verify.restype = ctypes.c_uint32
         L.orc_draft_q_rows.argtypes = [P, ctypes.c_int, i64, i32, i32, f32, P]
         L.orc_draft_q_rows.restype = ctypes.c_int
@@ -274,11 +274,12 @@ def lm_head_logits(h_bits, W_bits, x0: int = 0, x1=None) -> np.ndarray:
 
 
 def lm_head_verify(hidden_bits, W_bits, cu, draft_ids, temperature, seed: int = 0, offset: int = 0,
-                   out_stride=None):
+                   out_stride=None, requests=None):
     """Verify step on LM-head logits (no-draft-probs mode, one-level race).
-    hidden_bits [R, d] and W_bits [V, d]: bf16 bit patterns (uint16).  Returns a
-    dict with tokens [B, out_stride], num_sampled, num_rejected, margin [B],
-    greedy_gap [B], p_draft [D] and the error mask."""
+    hidden_bits [R, d] and W_bits [V, d]: bf16 bit patterns (uint16).  requests:
+    optional iterable of the request ids to compute (others stay -1 / 0).
+    Returns a dict with tokens [B, out_stride], num_sampled, num_rejected,
+    margin [B], greedy_gap [B], p_draft [D] and the error mask."""
     H = np.ascontiguousarray(hidden_bits, dtype=np.uint16)
     W = np.ascontiguousarray(W_bits, dtype=np.uint16)
     R, d = H.shape
@@ -297,9 +298,13 @@ def lm_head_verify(hidden_bits, W_bits, cu, draft_ids, temperature, seed: int = 
     mg = np.zeros(B, dtype=np.float64)
     gg = np.zeros(B, dtype=np.float64)
     pd = np.zeros(max(D, 1), dtype=np.float32)
+    only = None
+    if requests is not None:
+        only = np.zeros(max(B, 1), dtype=np.uint8)
+        only[list(requests)] = 1
     err = lib().orc_lm_head_verify(_ptr(H), d, _ptr(W), d, d, V, _ptr(dd), _ptr(cu), B, _ptr(T), seed,
                                    offset, _ptr(tokens), out_stride, _ptr(ns), _ptr(nr), _ptr(mg),
-                                   _ptr(gg), _ptr(pd))
+                                   _ptr(gg), _ptr(pd), _ptr(only))
     return dict(tokens=tokens, num_sampled=ns, num_rejected=nr, margin=mg, greedy_gap=gg,
                 p_draft=pd[:D], err=int(err))
 

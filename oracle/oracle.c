@@ -608,7 +608,7 @@ uint32_t orc_lm_head_verify(const uint16_t *hidden, int64_t hstride, const uint1
                             const int32_t *cu, int32_t B, const float *temperature, uint64_t seed,
                             uint64_t offset, int32_t *out_tokens, int32_t out_stride,
                             int32_t *num_sampled, int32_t *num_rejected, double *margin,
-                            double *greedy_gap, float *p_draft) {
+                            double *greedy_gap, float *p_draft, const uint8_t *only) {
   uint32_t err = 0;
   if ((offset >> 32) != 0) return ORC_ERR_OFFSET;
   for (int32_t r = 0; r < B; ++r) {
@@ -622,6 +622,7 @@ uint32_t orc_lm_head_verify(const uint16_t *hidden, int64_t hstride, const uint1
       return ORC_ERR_CU;
   if (cu[0] != 0) return ORC_ERR_CU;
   for (int32_t r = 0; r < B; ++r) {
+    if (only && !only[r]) continue;
     const int32_t K = cu[r + 1] - cu[r];
     const int64_t g0 = (int64_t)cu[r] + r;
     const float T = temperature[r];

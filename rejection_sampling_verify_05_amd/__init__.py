@@ -11,7 +11,7 @@ Entry points (same names as the C ABI):
     spec_verify_create, spec_verify_destroy, spec_verify_run,
     spec_post_update, spec_verify_strerror, spec_verify_read_error,
     spec_verify_synthetic_rates, spec_verify_profile_start, spec_verify_profile_read,
-    spec_draft_sample
+    spec_draft_sample, spec_verify_lm_head
 """
 from __future__ import annotations
 
@@ -25,12 +25,14 @@ __all__ = [
     "SpecVerifyError", "VerifyArgs", "PostUpdateArgs", "lib", "library_path",
     "spec_verify_create", "spec_verify_destroy", "spec_verify_run", "spec_post_update",
     "spec_verify_strerror", "spec_verify_read_error", "spec_verify_synthetic_rates",
-    "DraftArgs", "spec_draft_sample",
+    "DraftArgs", "spec_draft_sample", "SV_CREATE_LM_HEAD", "LmHeadArgs", "spec_verify_lm_head",
 ]
 
 SV_OK, SV_EINVAL, SV_ECAPACITY, SV_EDTYPE, SV_EHIP, SV_EINPUT = 0, -1, -2, -3, -4, -5
 SV_F32, SV_BF16 = 0, 1
 SV_CREATE_TOPK = 1
+SV_CREATE_LM_HEAD = 2
+SV_LM_HEAD_TILE = 256
 SV_RACE_CHUNK = 1024
 SV_MAX_DRAFTS = 64
 SV_TOPK_CANDIDATES = 1024
@@ -110,6 +112,31 @@ class DraftArgs(ctypes.Structure):
     ]
 
 
+class LmHeadArgs(ctypes.Structure):
+    """Mirror of ``sv_lm_head_args``."""
+    _fields_ = [
+        ("hidden", ctypes.c_void_p),
+        ("lm_head", ctypes.c_void_p),
+        ("draft_ids", ctypes.c_void_p),
+        ("cu_num_draft", ctypes.c_void_p),
+        ("temperature", ctypes.c_void_p),
+        ("out_tokens", ctypes.c_void_p),
+        ("out_num_sampled", ctypes.c_void_p),
+        ("out_num_rejected", ctypes.c_void_p),
+        ("dbg_p_draft", ctypes.c_void_p),
+        ("dbg_logits", ctypes.c_void_p),
+        ("hidden_row_stride", ctypes.c_int64),
+        ("lm_head_row_stride", ctypes.c_int64),
+        ("seed", ctypes.c_uint64),
+        ("offset", ctypes.c_uint64),
+        ("hidden_size", ctypes.c_int32),
+        ("num_rows", ctypes.c_int32),
+        ("num_reqs", ctypes.c_int32),
+        ("vocab_size", ctypes.c_int32),
+        ("out_stride", ctypes.c_int32),
+    ]
+
+
 class PostUpdateArgs(ctypes.Structure):
     """Mirror of ``sv_post_update_args``."""
     _fields_ = [
@@ -155,6 +182,8 @@ def lib() -> ctypes.CDLL:
         L.spec_verify_read_error.restype = ctypes.c_int
         L.spec_draft_sample.argtypes = [P, ctypes.POINTER(DraftArgs), P]
         L.spec_draft_sample.restype = ctypes.c_int
+        L.spec_verify_lm_head.argtypes = [P, ctypes.POINTER(LmHeadArgs), P]
+        L.spec_verify_lm_head.restype = ctypes.c_int
         L.spec_verify_synthetic_rates.argtypes = [ctypes.c_float, ctypes.c_int32, P]
         L.spec_verify_synthetic_rates.restype = ctypes.c_int
         L.spec_verify_profile_start.argtypes = [P, ctypes.c_int32]
@@ -393,6 +422,59 @@ def spec_draft_sample(ctx, *args, stream=None, **kwargs) -> None:
     st = lib().spec_draft_sample(ctx, ctypes.byref(a), _stream_handle(stream))
     if st != SV_OK:
         raise SpecVerifyError(st, "spec_draft_sample")
+
+
+def make_lm_head_args(hidden, lm_head, draft_ids, cu_num_draft, temperature, out_tokens,
+                      out_num_sampled, out_num_rejected, *, seed=0, offset=0, dbg_p_draft=None,
+                      dbg_logits=None) -> LmHeadArgs:
+    """Fill an sv_lm_head_args from torch tensors (no copies, no compute).
+    hidden [R, d] and lm_head [V, d] are bfloat16 with unit column stride."""
+    import torch
+    for t, n in ((hidden, "hidden"), (lm_head, "lm_head")):
+        if t.dim() != 2 or not t.is_cuda or t.stride(1) != 1 or t.dtype != torch.bfloat16:
+            raise ValueError(f"{n} must be a 2-D bfloat16 CUDA tensor with unit column stride")
+    if hidden.shape[1] != lm_head.shape[1]:
+        raise ValueError("hidden and lm_head disagree on the hidden size")
+    _dev(draft_ids, torch.int32, "draft_ids", 1)
+    _dev(cu_num_draft, torch.int32, "cu_num_draft", 1)
+    _dev(temperature, torch.float32, "temperature", 1)
+    _dev(out_tokens, torch.int32, "out_tokens", 2)
+    _dev(out_num_sampled, torch.int32, "out_num_sampled", 1)
+    _dev(out_num_rejected, torch.int32, "out_num_rejected", 1)
+    _dev(dbg_p_draft, torch.float32, "dbg_p_draft", 1)
+    _dev(dbg_logits, torch.float32, "dbg_logits", 2)
+    a = LmHeadArgs()
+    a.hidden = hidden.data_ptr()
+    a.lm_head = lm_head.data_ptr()
+    a.draft_ids = None if draft_ids is None or draft_ids.numel() == 0 else draft_ids.data_ptr()
+    a.cu_num_draft = cu_num_draft.data_ptr()
+    a.temperature = temperature.data_ptr()
+    a.out_tokens = out_tokens.data_ptr()
+    a.out_num_sampled = out_num_sampled.data_ptr()
+    a.out_num_rejected = out_num_rejected.data_ptr()
+    a.dbg_p_draft = None if dbg_p_draft is None else dbg_p_draft.data_ptr()
+    a.dbg_logits = None if dbg_logits is None else dbg_logits.data_ptr()
+    a.hidden_row_stride = hidden.stride(0)
+    a.lm_head_row_stride = lm_head.stride(0)
+    a.seed = int(seed)
+    a.offset = int(offset)
+    a.hidden_size = hidden.shape[1]
+    a.num_rows = hidden.shape[0]
+    a.num_reqs = cu_num_draft.shape[0] - 1
+    a.vocab_size = lm_head.shape[0]
+    a.out_stride = out_tokens.shape[1]
+    return a
+
+
+def spec_verify_lm_head(ctx, *args, stream=None, **kwargs) -> None:
+    """spec_verify_lm_head(ctx, hidden [R, d], lm_head [V, d], draft_ids [D],
+    cu_num_draft [B+1], temperature [B], out_tokens [B, S], out_num_sampled [B],
+    out_num_rejected [B], seed=0, offset=0, dbg_p_draft=None, dbg_logits=None,
+    stream=None), or spec_verify_lm_head(ctx, LmHeadArgs)."""
+    a = args[0] if len(args) == 1 and isinstance(args[0], LmHeadArgs) else make_lm_head_args(*args, **kwargs)
+    st = lib().spec_verify_lm_head(ctx, ctypes.byref(a), _stream_handle(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "spec_verify_lm_head")
 
 
 def spec_verify_synthetic_rates(mean_length: float, k: int) -> list:

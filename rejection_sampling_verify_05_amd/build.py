@@ -6,7 +6,7 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = [os.path.join(HERE, "csrc", "sv_api.hip"), os.path.join(HERE, "csrc", "sv_kernels.hip")]
+SOURCES = [os.path.join(HERE, "csrc", n) for n in ("sv_api.hip", "sv_kernels.hip", "sv_lmhead.hip")]
 OUTPUT = os.path.join(HERE, "libspecverify.so")
 
 # -ffp-contract=off: every fp32 operation on logits rounds once (the penalty and

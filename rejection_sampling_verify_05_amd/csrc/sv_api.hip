@@ -29,6 +29,8 @@ struct sv_ctx {
   int32_t *cand_n;
   float *cand_tau;
   int32_t *zeros;    // [max_reqs + 1] zero prefix sums (draft-side sampling: row r is request r)
+  float4 *lm_rec;    // [max_rows, ceil(max_vocab / 256)] LM-head tile records (SV_CREATE_LM_HEAD)
+  float4 *lm_drec;   // [max_rows] LM-head draft-token records
   unsigned int *err;
   hipEvent_t *ev;   // measurement: 4 events per recorded call
   int32_t ev_cap, ev_n;
@@ -48,8 +50,8 @@ void free_events(sv_ctx *c) {
 
 void free_ctx(sv_ctx *c) {
   free_events(c);
-  void *ptrs[] = {c->chunk_tab, c->row_info, c->res_req, c->res_tab,    c->res_list,   c->cand_val,
-                  c->cand_idx,  c->cand_n,   c->cand_tau, c->zeros,      c->err};
+  void *ptrs[] = {c->chunk_tab, c->row_info, c->res_req, c->res_tab, c->res_list, c->cand_val, c->cand_idx,
+                  c->cand_n,    c->cand_tau, c->zeros,   c->lm_rec,  c->lm_drec,   c->err};
   for (void *p : ptrs)
     if (p) (void)hipFree(p);
   delete c;
@@ -70,7 +72,7 @@ extern "C" int spec_verify_create(sv_ctx **out, int32_t max_rows, int32_t max_re
   *out = nullptr;
   if (max_rows <= 0 || max_reqs <= 0 || max_k < 0 || max_vocab <= 0) return SV_EINVAL;
   if (max_k > SV_MAX_DRAFTS || max_rows > (1 << 30) / 2) return SV_ECAPACITY;
-  if ((flags & ~(uint32_t)SV_CREATE_TOPK) != 0) return SV_EINVAL;
+  if ((flags & ~(uint32_t)(SV_CREATE_TOPK | SV_CREATE_LM_HEAD)) != 0) return SV_EINVAL;
   sv_ctx *c = new (std::nothrow) sv_ctx();
   if (!c) return SV_EHIP;
   if (hipGetDevice(&c->device) != hipSuccess) {
@@ -93,6 +95,9 @@ extern "C" int spec_verify_create(sv_ctx **out, int32_t max_rows, int32_t max_re
   if (ok) ok = dev_alloc(&c->zeros, reqs + 1);
   if (ok && (flags & SV_CREATE_TOPK))
     ok = dev_alloc(&c->cand_val, rows * sv::kCandCap) && dev_alloc(&c->cand_idx, rows * sv::kCandCap);
+  if (ok && (flags & SV_CREATE_LM_HEAD))
+    ok = dev_alloc(&c->lm_rec, rows * (size_t)((max_vocab + sv::kLmTok - 1) / sv::kLmTok)) &&
+         dev_alloc(&c->lm_drec, rows);
   if (ok)
     ok = hipMemset(c->res_req, 0, reqs * sizeof(int4)) == hipSuccess &&
          hipMemset(c->zeros, 0, (reqs + 1) * sizeof(int32_t)) == hipSuccess &&
@@ -405,6 +410,61 @@ extern "C" int spec_verify_read_error(sv_ctx *ctx, uint32_t *host_flags, hipStre
   if (hipMemset(ctx->err, 0, sizeof h) != hipSuccess) return SV_EHIP;
   *host_flags = h;
   return h ? SV_EINPUT : SV_OK;
+}
+
+extern "C" int spec_verify_lm_head(sv_ctx *ctx, const sv_lm_head_args *a, hipStream_t stream) {
+  if (!ctx || !a) return SV_EINVAL;
+  if (a->num_reqs < 0 || a->vocab_size <= 0 || a->num_rows < a->num_reqs) return SV_EINVAL;
+  if (a->num_reqs == 0) return SV_OK;
+  if (!(ctx->flags & SV_CREATE_LM_HEAD)) return SV_ECAPACITY;
+  if (a->num_rows > ctx->max_rows || a->num_reqs > ctx->max_reqs || a->vocab_size > ctx->max_vocab)
+    return SV_ECAPACITY;
+  if (a->out_stride < 1) return SV_EINVAL;
+  if (a->out_stride > ctx->max_k + 1) return SV_ECAPACITY;
+  const int32_t D = a->num_rows - a->num_reqs;
+  if (!a->hidden || !a->lm_head || !a->cu_num_draft || !a->temperature || !a->out_tokens || !a->out_num_sampled ||
+      !a->out_num_rejected || (D > 0 && !a->draft_ids))
+    return SV_EINVAL;
+  // The main loop reads 16-byte fragments: aligned bases and strides, d a multiple of 64.
+  if (a->hidden_size <= 0 || a->hidden_size % sv::kLmK != 0) return SV_EINVAL;
+  if (a->hidden_row_stride < a->hidden_size || a->lm_head_row_stride < a->hidden_size) return SV_EINVAL;
+  if (a->hidden_row_stride % 8 != 0 || a->lm_head_row_stride % 8 != 0) return SV_EINVAL;
+  if ((uintptr_t)a->hidden % 16 != 0 || (uintptr_t)a->lm_head % 16 != 0) return SV_EINVAL;
+  if (a->offset >> 32) return SV_EINVAL;
+  const int32_t NT = (a->vocab_size + sv::kLmTok - 1) / sv::kLmTok;
+  const int32_t RB = (a->num_rows + sv::kLmRows - 1) / sv::kLmRows;
+  if ((int64_t)NT * RB > 0x7FFFFFFF) return SV_ECAPACITY;
+
+  sv::LmParams p;
+  memset(&p, 0, sizeof p);
+  p.H = static_cast<const uint16_t *>(a->hidden);
+  p.W = static_cast<const uint16_t *>(a->lm_head);
+  p.hstride = a->hidden_row_stride;
+  p.wstride = a->lm_head_row_stride;
+  p.d = a->hidden_size;
+  p.draft_ids = a->draft_ids;
+  p.cu = a->cu_num_draft;
+  p.temperature = a->temperature;
+  p.out_tokens = a->out_tokens;
+  p.out_ns = a->out_num_sampled;
+  p.out_nr = a->out_num_rejected;
+  p.dbg_p_draft = a->dbg_p_draft;
+  p.dbg_logits = a->dbg_logits;
+  p.rec = ctx->lm_rec;
+  p.drec = ctx->lm_drec;
+  p.err = ctx->err;
+  p.R = a->num_rows;
+  p.B = a->num_reqs;
+  p.D = D;
+  p.V = a->vocab_size;
+  p.NT = NT;
+  p.RB = RB;
+  p.out_stride = a->out_stride;
+  p.seed_lo = (uint32_t)(a->seed & 0xFFFFFFFFu);
+  p.seed_hi = (uint32_t)(a->seed >> 32);
+  p.offset = (uint32_t)a->offset;
+  hipEvent_t *ev = (ctx->ev && ctx->ev_n < ctx->ev_cap) ? ctx->ev + 4 * ctx->ev_n++ : nullptr;
+  return sv::launch_lm_head(p, stream, ev) == hipSuccess ? SV_OK : SV_EHIP;
 }
 
 extern "C" int spec_verify_profile_start(sv_ctx *ctx, int32_t max_calls) {

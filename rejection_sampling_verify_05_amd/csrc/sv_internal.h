@@ -104,6 +104,37 @@ struct DraftOut {
   int32_t *ids;          // [D] or null
 };
 
+// LM-head path: the logits of target row g are z = W h_g (W [V, d], h_g [d],
+// bf16), computed tile by tile and reduced in the tile's epilogue; they are
+// never stored (except to dbg_logits).
+constexpr int kLmTok = 256;   // tokens per workgroup tile (the unit of the per-tile records)
+constexpr int kLmRows = 128;  // target rows per workgroup tile
+constexpr int kLmK = 64;      // hidden elements per main-loop step (d must be a multiple)
+
+struct LmParams {
+  const uint16_t *H;          // [R, hstride] hidden states (bf16 bits)
+  const uint16_t *W;          // [V, wstride] LM-head weight (bf16 bits)
+  int64_t hstride, wstride;   // elements between rows
+  int32_t d;                  // hidden size
+  const int32_t *draft_ids;   // [D]
+  const int32_t *cu;          // [B + 1]
+  const float *temperature;   // [B]
+  int32_t *out_tokens, *out_ns, *out_nr;
+  float *dbg_p_draft;         // [D] or null
+  float *dbg_logits;          // [R, V] or null
+  float4 *rec;                // [R, NT]: per (row, tile) (max z, sum exp2(a (z - max)), best race key, token bits)
+  float4 *drec;               // [R]: the draft token's tile, (z_d, best key without d, its token bits, 0)
+  unsigned int *err;
+  int32_t R, B, D, V;
+  int32_t NT;                 // token tiles ceil(V / kLmTok)
+  int32_t RB;                 // row blocks ceil(R / kLmRows)
+  int32_t out_stride;
+  uint32_t seed_lo, seed_hi, offset;
+};
+
+// ev: null, or four events stamped around the GEMM and the request kernel.
+hipError_t launch_lm_head(const LmParams &p, hipStream_t s, const hipEvent_t *ev);
+
 struct PostParams {
   const int32_t *idx_mapping, *query_len, *tokens, *num_sampled, *num_rejected;
   int32_t *last_sampled, *counts, *num_computed;

@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol():
     assert names == sorted(["spec_post_update", "spec_verify_create", "spec_verify_destroy",
                             "spec_verify_profile_read", "spec_verify_profile_start",
                             "spec_verify_read_error", "spec_verify_run", "spec_verify_strerror",
-                            "spec_verify_synthetic_rates", "spec_draft_sample"])
+                            "spec_verify_synthetic_rates", "spec_draft_sample", "spec_verify_lm_head"])
     L = ctypes.CDLL(sv.library_path())
     for n in names:
         assert hasattr(L, n), n
@@ -62,6 +62,10 @@ int main(void) {
   F(sv_draft_args, draft_logits) F(sv_draft_args, out_q) F(sv_draft_args, draft_stats)
   F(sv_draft_args, logits_row_stride) F(sv_draft_args, seed) F(sv_draft_args, offset)
   F(sv_draft_args, logits_dtype) F(sv_draft_args, step)
+  printf("sv_lm_head_args %zu\n", sizeof(sv_lm_head_args));
+  F(sv_lm_head_args, hidden) F(sv_lm_head_args, dbg_logits) F(sv_lm_head_args, hidden_row_stride)
+  F(sv_lm_head_args, lm_head_row_stride) F(sv_lm_head_args, seed) F(sv_lm_head_args, offset)
+  F(sv_lm_head_args, hidden_size) F(sv_lm_head_args, vocab_size) F(sv_lm_head_args, out_stride)
   F(sv_post_update_args, num_computed_tokens) F(sv_post_update_args, num_reqs)
   F(sv_post_update_args, num_slots)
   return 0;
@@ -81,11 +85,13 @@ int main(void) {
     assert got["sv_verify_args"] == (ctypes.sizeof(sv.VerifyArgs),)
     assert got["sv_post_update_args"] == (ctypes.sizeof(sv.PostUpdateArgs),)
     assert got["sv_draft_args"] == (ctypes.sizeof(sv.DraftArgs),)
+    assert got["sv_lm_head_args"] == (ctypes.sizeof(sv.LmHeadArgs),)
     for key, val in got.items():
         if "." not in key:
             continue
         struct, field = key.split(".")
-        cls = {"sv_verify_args": sv.VerifyArgs, "sv_draft_args": sv.DraftArgs}.get(struct, sv.PostUpdateArgs)
+        cls = {"sv_verify_args": sv.VerifyArgs, "sv_draft_args": sv.DraftArgs,
+               "sv_lm_head_args": sv.LmHeadArgs}.get(struct, sv.PostUpdateArgs)
         f = getattr(cls, field)
         assert (f.offset, f.size) == val, key
 
@@ -124,6 +130,15 @@ def test_strerror_and_host_checks_without_gpu():
     da.step = -1
     da.vocab_size = 4
     assert L.spec_draft_sample(fake, ctypes.byref(da), None) == sv.SV_EINVAL
+    la = sv.LmHeadArgs()
+    assert L.spec_verify_lm_head(None, ctypes.byref(la), None) == sv.SV_EINVAL
+    assert L.spec_verify_lm_head(fake, None, None) == sv.SV_EINVAL
+    la.num_reqs = -1
+    la.vocab_size = 8
+    assert L.spec_verify_lm_head(fake, ctypes.byref(la), None) == sv.SV_EINVAL
+    la.num_reqs, la.num_rows = 2, 1  # fewer rows than requests
+    assert L.spec_verify_lm_head(fake, ctypes.byref(la), None) == sv.SV_EINVAL
+    assert L.spec_verify_create(ctypes.byref(ctx), 1, 1, 1, 1, 0x4) == sv.SV_EINVAL
     assert L.spec_verify_profile_start(None, 4) == sv.SV_EINVAL
     assert L.spec_verify_profile_start(fake, 0) == sv.SV_EINVAL
     n = ctypes.c_int32(7)

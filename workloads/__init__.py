@@ -16,6 +16,13 @@ Workloads (sizes and distributions of the five benchmark configurations):
                   T=0.7, repetition penalty 1.1 from a 512-token history per request
   5  stress       B=1024, K=5,        V=256000, bf16 3*t_3,     draft probs, T=1.0
 
+LM-head workloads (make_lm_head_inputs): hidden states N(0,1) and an LM-head
+weight N(0, (scale / sqrt(d))^2), both bf16, so the target logits W h are about
+N(0, scale^2) (scale 3 as config 3); config 3's request mix (B=256, K_r ~
+U{0..3}, V=128256) with d=4096, the hidden size of the models with that
+vocabulary.  Drafts: d = argmax(W h + N(0,1)) (the fp32 product here is only
+an input generator).
+
 Draft side: draft logits = target + N(0,1) (config 5: 0.9*target + N(0,0.5^2));
 in draft-probs mode q = softmax(draft logits / T_draft) (config 4: over the
 draft's own top 50) and d ~ q; in the no-draft mode (and for greedy requests)
@@ -178,6 +185,41 @@ def make_inputs(w: Workload, device="cpu", salt: int = 0, slots_extra: int = 64)
         query_len=(K + 1).to(torch.int32), K=K.to(torch.int32), R=R, D=D, B=B, V=V,
         num_slots=S,
     )
+
+
+def make_lm_head_inputs(B: int, K: int, V: int, d: int, ragged: bool = True, T: float = 1.0,
+                        greedy_every: int = 0, scale: float = 3.0, draft_noise: float = 1.0,
+                        device="cpu", seed: int = 1003) -> dict:
+    """Hidden states [R, d] and an LM-head weight [V, d] (bf16), request layout,
+    temperatures and draft ids for spec_verify_lm_head."""
+    dev = torch.device(device)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    if ragged:
+        Kr = torch.randint(0, K + 1, (B,), generator=gen, device=dev)
+    else:
+        Kr = torch.full((B,), K, device=dev)
+    cu = torch.zeros(B + 1, dtype=torch.int32, device=dev)
+    cu[1:] = torch.cumsum(Kr, 0).to(torch.int32)
+    D = int(cu[-1].item())
+    R = D + B
+    hidden = torch.randn((R, d), generator=gen, device=dev).to(torch.bfloat16)
+    W = (torch.randn((V, d), generator=gen, device=dev) * (scale / d ** 0.5)).to(torch.bfloat16)
+    Tt = torch.full((B,), T, dtype=torch.float32, device=dev)
+    if greedy_every:
+        Tt[::greedy_every] = 0.0
+    req = torch.repeat_interleave(torch.arange(B, device=dev), Kr)
+    pos = torch.arange(D, device=dev) - cu[:-1].long()[req]
+    drow = cu[:-1].long()[req] + req + pos
+    draft_ids = torch.zeros(D, dtype=torch.int32, device=dev)
+    for s0 in range(0, D, 256):  # drafts: argmax of a noisy copy of the target logits
+        rows = drow[s0:s0 + 256]
+        z = hidden[rows].float() @ W.float().t()
+        z.add_(torch.randn(z.shape, generator=gen, device=dev), alpha=draft_noise)
+        draft_ids[s0:s0 + 256] = z.argmax(1).to(torch.int32)
+        del z
+    return dict(hidden=hidden, W=W, cu=cu, draft_ids=draft_ids, temperature=Tt, K=Kr.to(torch.int32),
+                R=R, D=D, B=B, V=V, d=d)
 
 
 def to_numpy(inp: dict, rows=None) -> dict:
