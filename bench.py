@@ -26,34 +26,55 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 # FETCH_SIZE / WRITE_SIZE counter record of the streaming kernel on this workload
 COUNTERS = os.path.join(ROOT, "profiles", "stats_fast_kernel_bf16_B256_V128256_counters.md")
 KERNEL_SOURCES = ["rejection_sampling_verify_05_amd/csrc/sv_kernels.hip", "rejection_sampling_verify_05_amd/csrc/sv_device.h",
                   "rejection_sampling_verify_05_amd/csrc/sv_internal.h", "rejection_sampling_verify_05_amd/build.py"]
 
 
-def kernel_source_hash() -> str:
+# ... and of the LM-head GEMM on its workload
+COUNTERS_LM = os.path.join(ROOT, "profiles", "lm_gemm_kernel_B256_V128256_d4096_counters.md")
+KERNEL_SOURCES_LM = ["rejection_sampling_verify_05_amd/csrc/sv_lmhead.hip", "rejection_sampling_verify_05_amd/csrc/sv_device.h",
+                     "rejection_sampling_verify_05_amd/csrc/sv_internal.h", "rejection_sampling_verify_05_amd/build.py"]
+
+
+def kernel_source_hash(sources=None) -> str:
     import hashlib
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in sources or KERNEL_SOURCES:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def recorded_traffic_per_row():
+def recorded_traffic_per_row(path=None, sources=None):
     """HBM bytes per target row measured by the counter runs, or None when the
     record is missing or was taken on different kernel sources."""
-    if not os.path.exists(COUNTERS):
+    path = path or COUNTERS
+    if not os.path.exists(path):
         return None
     rec = {}
-    for line in open(COUNTERS):
+    for line in open(path):
         if line.startswith("- ") and ": " in line:
             k, v = line[2:].split(": ", 1)
             rec[k.strip("` ")] = v.strip().strip("`")
-    if rec.get("kernel_source_sha256") != kernel_source_hash():
+    if rec.get("kernel_source_sha256") != kernel_source_hash(sources):
         return None
     return float(rec["hbm_bytes_per_target_row"])
+
+
+def copy_calibration():
+    """torch's copy kernel on 256 MiB, three times: a known-size reference for
+    the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def parse():
@@ -63,7 +84,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="3", help="workload id (1, 2, 3, 3k3, 4, 5; with optional "
                     "settings: 3p top-p, 3f frequency/presence penalties, 3s synthetic acceptance, "
-                    "3d draft-side sampling plus draft-logits verification, 4f and 4p)")
+                    "3d draft-side sampling plus draft-logits verification, 4f and 4p; 3h: the "
+                    "LM-head path, logits computed from hidden states d=4096 in the step)")
     ap.add_argument("--copies", type=int, default=0, help="input copies to rotate (0: >= 1 GB)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
@@ -91,6 +113,8 @@ def main():
     import rejection_sampling_verify_05_amd as sv
 
     torch.cuda.set_device(0)
+    if args.workload == "3h":
+        return bench_lm_head(args)
     w = wl.CONFIGS[args.workload]
     first = wl.make_inputs(w, "cuda", salt=0)
     per_copy = first["logits"].numel() * first["logits"].element_size()
@@ -151,13 +175,7 @@ def main():
         sv.spec_post_update(ctx, o["pargs"], stream=stream)
 
     if args.copy_calibration:
-        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_calibration()
 
     for i in range(args.warmup):
         step(i)
@@ -271,6 +289,173 @@ def main():
                      "bytes_rule": f"R*V*{esize} (each target row read once)"},
         "verify_call_us": pct(verify_ms),
         "epilogue_kernel_us": pct(epi_ms),
+        "cpu_baseline": cpu,
+        "wall_s": round(wall, 3),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def pct(a):
+    import numpy as np
+    return {"mean": round(float(np.mean(a)) * 1e3, 2), "p10": round(float(np.percentile(a, 10)) * 1e3, 2),
+            "p50": round(float(np.median(a)) * 1e3, 2), "p90": round(float(np.percentile(a, 90)) * 1e3, 2)}
+
+
+def bench_lm_head(args):
+    """One step = spec_verify_lm_head (the LM-head GEMM with the verify
+    statistics in its epilogue, then the per-request decisions) + post_update,
+    on config 3's request mix with hidden size 4096.  The LM-head weight (1.05 GB)
+    is one resident tensor, as in serving; the hidden states rotate over copies.
+    Also times, as context, the same step with the logits materialised: torch's
+    bf16 matmul (hipBLASLt) then spec_verify_run on the logits."""
+    import numpy as np
+    import torch
+
+    import workloads as wl
+    import rejection_sampling_verify_05_amd as sv
+
+    B, K, V, d = 256, 3, 128256, 4096
+    ncopies = args.copies or 4
+    copies = [wl.make_lm_head_inputs(B=B, K=K, V=V, d=d, device="cuda", seed=1003 + i) for i in range(ncopies)]
+    W = copies[0]["W"]
+    for c in copies[1:]:
+        c["W"] = W  # one weight, several batches of hidden states
+    max_rows = max(c["R"] for c in copies)
+    ctx = sv.spec_verify_create(max_rows, B, K, V, sv.SV_CREATE_LM_HEAD)
+    stream = torch.cuda.current_stream()
+    S = B + 64
+    last = torch.zeros(S, dtype=torch.int32, device="cuda")
+    ncomp = torch.zeros(S, dtype=torch.int32, device="cuda")
+    counts = torch.zeros((S, V), dtype=torch.int32, device="cuda")
+    idx_mapping = torch.arange(B, dtype=torch.int32, device="cuda")
+    outs = []
+    for c in copies:
+        o = dict(tokens=torch.empty((B, K + 1), dtype=torch.int32, device="cuda"),
+                 ns=torch.empty(B, dtype=torch.int32, device="cuda"),
+                 nr=torch.empty(B, dtype=torch.int32, device="cuda"))
+        o["largs"] = sv.make_lm_head_args(c["hidden"], W, c["draft_ids"], c["cu"], c["temperature"], o["tokens"],
+                                          o["ns"], o["nr"], seed=1234, offset=0)
+        o["pargs"] = sv.make_post_update_args(idx_mapping, (c["K"] + 1).to(torch.int32), o["tokens"], o["ns"],
+                                              o["nr"], last, counts, ncomp)
+        outs.append(o)
+
+    def step(i):
+        o = outs[i % ncopies]
+        o["largs"].offset = i
+        sv.spec_verify_lm_head(ctx, o["largs"], stream=stream)
+        sv.spec_post_update(ctx, o["pargs"], stream=stream)
+
+    if args.copy_calibration:
+        copy_calibration()
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    assert sv.spec_verify_read_error(ctx) == 0
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    rows = 0
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for k in range(args.steps):
+        i = args.warmup + k
+        step(i)
+        rows += copies[i % ncopies]["R"]
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t0.elapsed_time(t1)
+    assert sv.spec_verify_read_error(ctx) == 0
+
+    # Instrumented pass: dispatch-stamped events around the GEMM and the request kernel.
+    sv.spec_verify_profile_start(ctx, args.steps)
+    torch.cuda.synchronize()
+    for k in range(args.steps):
+        step(args.warmup + k)
+    torch.cuda.synchronize()
+    gemm_ms, req_ms = sv.spec_verify_profile_read(ctx, args.steps)
+    gemm_ms, req_ms = np.array(gemm_ms), np.array(req_ms)
+    assert len(gemm_ms) == args.steps
+
+    # Context: logits materialised by torch's bf16 matmul, then the verify call.
+    vctx = sv.spec_verify_create(max_rows, B, K, V, 0)
+    logits = [torch.empty((c["R"], V), dtype=torch.bfloat16, device="cuda") for c in copies]
+    vargs = [sv.make_verify_args(logits[j], c["draft_ids"], c["cu"], c["temperature"], outs[j]["tokens"],
+                                 outs[j]["ns"], outs[j]["nr"], seed=1234, offset=0)
+             for j, c in enumerate(copies)]
+    nref = min(args.steps, 50)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(nref)]
+    for k in range(nref + 5):
+        j = k % ncopies
+        e = ev[k - 5] if k >= 5 else None
+        if e:
+            e[0].record(stream)
+        torch.mm(copies[j]["hidden"], W.t(), out=logits[j])
+        if e:
+            e[1].record(stream)
+        vargs[j].offset = k
+        sv.spec_verify_run(vctx, vargs[j], stream=stream)
+        if e:
+            e[2].record(stream)
+    torch.cuda.synchronize()
+    mm_ms = np.array([a.elapsed_time(b) for a, b, _ in ev])
+    vr_ms = np.array([b.elapsed_time(c) for _, b, c in ev])
+    sv.spec_verify_destroy(vctx)
+    del logits
+
+    R_mean = float(np.mean([copies[(args.warmup + k) % ncopies]["R"] for k in range(args.steps)]))
+    flops = 2.0 * R_mean * V * d
+    per_row = recorded_traffic_per_row(COUNTERS_LM, KERNEL_SOURCES_LM)
+    traffic = None if per_row is None else int(per_row * R_mean)
+    achieved = flops / (float(np.mean(gemm_ms)) * 1e-3) / 1e12
+
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        c = copies[0]
+        H = c["hidden"].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        Wb = W.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        cu, dids, T = c["cu"].cpu().numpy(), c["draft_ids"].cpu().numpy(), c["temperature"].cpu().numpy()
+        t_start = time.perf_counter()
+        n_req, cpu_rows = 0, 0
+        while True:
+            oracle.lm_head_verify(H, Wb, cu, dids, T, seed=1234, offset=0, out_stride=K + 1, requests=[n_req])
+            cpu_rows += int(cu[n_req + 1] - cu[n_req]) + 1
+            n_req += 1
+            if time.perf_counter() - t_start >= args.cpu_seconds or n_req == B:
+                break
+        cpu_s = time.perf_counter() - t_start
+        cpu = {"value": cpu_rows / cpu_s, "unit": "rows/s", "cores": 1, "kind": "oracle",
+               "sample": f"requests 0..{n_req - 1} of one batch ({cpu_rows} rows: fp64 LM-head logits and the "
+                         f"verify step), single-threaded C oracle, {cpu_s:.1f} s"}
+
+    sv.spec_verify_destroy(ctx)
+    line = {
+        "metric": "verified logit rows/sec + achieved HBM GB/s (B=256, K=3, V=128256)",
+        "value": round(rows / (total_ms * 1e-3), 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"LM-head path: B={B}, K_r ~U{{0..{K}}}, V={V}, hidden size {d}, bf16 hidden "
+                               "states and LM-head weight, logits computed in the step (never stored), "
+                               "draft ids only",
+                   "global_batch": B, "rows_per_step": round(rows / args.steps, 1), "input_copies": ncopies,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
+                     "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                     "kernel": "lm_gemm_kernel (LM-head GEMM with the verify statistics in its epilogue)",
+                     "kernel_us": pct(gemm_ms), "flops_per_launch": int(flops),
+                     "flops_rule": "2 R V d (the product W h of every target row)"},
+        "request_kernel_us": pct(req_ms),
+        "materialised_logits_context_us": {"torch_matmul_bf16": pct(mm_ms), "spec_verify_run": pct(vr_ms)},
         "cpu_baseline": cpu,
         "wall_s": round(wall, 3),
     }

@@ -275,7 +275,7 @@ int spec_verify_synthetic_rates(float mean_length, int32_t k, float *rates);
  * (records of ceil(max_vocab / 256) x 16 bytes per row).  Cost: one pass over W
  * (V d bf16) per 128 target rows, shared through L2 by the workgroups of one
  * token tile, and 2 R V d flops.
- * Errors: SV_EINVAL (NULL pointer, hidden_size not a positive multiple of 64,
+ * Errors: SV_EINVAL (NULL pointer, hidden_size not a positive multiple of 32,
  * strides below hidden_size or not multiples of 8, bases not 16-byte aligned,
  * offset >= 2^32), SV_ECAPACITY (sizes beyond the context, or no
  * SV_CREATE_LM_HEAD), SV_EHIP.  Device-side: SV_ERR_CU, SV_ERR_TEMPERATURE, and
@@ -297,7 +297,7 @@ typedef struct sv_lm_head_args {
   int64_t lm_head_row_stride;   /* elements, >= hidden_size, multiple of 8                  */
   uint64_t seed;                /* Philox key                                               */
   uint64_t offset;              /* per-call step, < 2^32                                    */
-  int32_t hidden_size;          /* d, a multiple of 64                                      */
+  int32_t hidden_size;          /* d, a multiple of 32                                      */
   int32_t num_rows;             /* R = cu[B] + B                                            */
   int32_t num_reqs;             /* B                                                        */
   int32_t vocab_size;           /* V <= max_vocab                                           */

@@ -18,13 +18,12 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // multiplies whose high halves are xored with the other counter words and the
 // round key; the key advances by the golden-ratio Weyl increments.
 // ---------------------------------------------------------------------------
+// Each 32x32 -> 64-bit product is one v_mad_u64_u32 (high and low halves at once).
 __device__ __forceinline__ uint4 philox10(uint4 ctr, uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int round = 0; round < 10; ++round) {
-    const uint32_t m0 = 0xD2511F53u, m1 = 0xCD9E8D57u;
-    uint32_t hi0 = __umulhi(m0, ctr.x), lo0 = m0 * ctr.x;
-    uint32_t hi1 = __umulhi(m1, ctr.z), lo1 = m1 * ctr.z;
-    ctr = make_uint4(hi1 ^ ctr.y ^ k0, lo1, hi0 ^ ctr.w ^ k1, lo0);
+    const uint64_t p0 = (uint64_t)0xD2511F53u * ctr.x, p1 = (uint64_t)0xCD9E8D57u * ctr.z;
+    ctr = make_uint4((uint32_t)(p1 >> 32) ^ ctr.y ^ k0, (uint32_t)p1, (uint32_t)(p0 >> 32) ^ ctr.w ^ k1, (uint32_t)p0);
     k0 += 0x9E3779B9u;
     k1 += 0xBB67AE85u;
   }

@@ -109,7 +109,7 @@ struct DraftOut {
 // never stored (except to dbg_logits).
 constexpr int kLmTok = 256;   // tokens per workgroup tile (the unit of the per-tile records)
 constexpr int kLmRows = 128;  // target rows per workgroup tile
-constexpr int kLmK = 64;      // hidden elements per main-loop step (d must be a multiple)
+constexpr int kLmK = 32;      // hidden elements per main-loop step (d must be a multiple)
 
 struct LmParams {
   const uint16_t *H;          // [R, hstride] hidden states (bf16 bits)

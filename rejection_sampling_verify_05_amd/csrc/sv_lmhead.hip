@@ -32,10 +32,27 @@ typedef __attribute__((ext_vector_type(16))) float f32x16;
 constexpr float kLog2eL = 1.4426950408889634f;
 constexpr float kNegInfL = -__builtin_inff();
 constexpr int kIntMax = 0x7FFFFFFF;
-// LDS pitch of one staged hidden row: 128 bytes of data + 16 of padding, so
-// the 16-byte fragment reads of 8 consecutive rows hit disjoint banks.
-constexpr int kHPitch = kLmK * 2 + 16;
-constexpr int kHStage = kLmRows * kHPitch;
+
+// Main loop: a workgroup (4 waves, one per SIMD; two workgroups per CU, so
+// that one's epilogue overlaps the other's matrix work) owns a tile of kLmTok
+// = 256 tokens x kLmRows = 128 target rows; wave w computes tokens 64 w .. + 64
+// of all 128 rows as 2 x 4 MFMA 32x32x16 tiles (128 fp32 accumulators per
+// lane).  The hidden dimension advances kLmK = 32 elements per step; each
+// step's W slice (256 rows x 64 bytes) and hidden slice (128 rows x 64 bytes)
+// are copied to LDS by the loads themselves (global_load_lds, no registers)
+// into a ring of kStages stages, kStages - 1 steps ahead of the MFMAs.
+constexpr int kStages = 3;
+constexpr int kRowBytes = kLmK * 2;                    // 64 bytes of one row per step
+constexpr int kWPart = kLmTok * kRowBytes;             // W part of a stage: 16 KB
+constexpr int kHPart = kLmRows * kRowBytes;            // hidden part: 8 KB
+constexpr int kStage = kWPart + kHPart;
+constexpr int kDmaW = kWPart / (kThreads * 16);        // 16-byte loads per thread per stage: W (4)
+constexpr int kDmaH = kHPart / (kThreads * 16);        // ... and hidden (2)
+
+// Rows are stored densely (64 bytes); the 16-byte chunk c of row r sits at
+// position c ^ ((r >> 2) & 3), so that the fragment reads of 16 consecutive
+// rows (one LDS cycle of 16-byte reads) hit 16 distinct bank groups.
+__device__ __forceinline__ int chunk_pos(int r, int c) { return c ^ ((r >> 2) & 3); }
 
 struct LmRed {  // per (wave, row) partial results of the epilogue
   float m[kWaves][kLmRows], s[kWaves][kLmRows], k1[kWaves][kLmRows], k2[kWaves][kLmRows], zd[kWaves][kLmRows];
@@ -44,78 +61,98 @@ struct LmRed {  // per (wave, row) partial results of the epilogue
 
 struct LmShared {
   union alignas(16) {
-    unsigned char h[2][kHStage];  // double-buffered hidden tile [128 rows][64 elements]
+    unsigned char ring[kStages][kStage];
     LmRed red;
   } u;
   float a[kLmRows];  // log2(e) / T of each row's request (0: greedy or invalid)
   int d[kLmRows];    // draft token of the row (-1: bonus row or no valid draft slot)
 };
-static_assert(sizeof(LmRed) <= 2 * kHStage, "epilogue partials reuse the hidden-tile buffers");
+static_assert(sizeof(LmRed) <= kStages * kStage, "epilogue partials reuse the ring");
 
 __device__ __forceinline__ bool key_better(float k, int x, float bk, int bx) { return k > bk || (k == bk && x < bx); }
 
-// Main-loop operands.  W fragment of lane l, subtile tm, step j: token
-// tok0 + 64 wave + 32 tm + (l & 31), hidden elements k0 + 32 (l >> 5) + 8 j ..
-// + 8 (the MFMA's k index 8 (l >> 5) + e maps to hidden element
-// 32 (l >> 5) + 8 j + e of the step; the hidden fragments use the same map).
-__device__ __forceinline__ void load_w(uint4 (&w)[2][4], const uint16_t *const (&wp)[2], int kb) {
-#pragma unroll
-  for (int tm = 0; tm < 2; ++tm) {
-    const uint4 *src = reinterpret_cast<const uint4 *>(wp[tm] + (int64_t)kb * kLmK);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) w[tm][j] = src[j];
-  }
+// One 16-byte load per lane from global memory straight into LDS: lane i
+// writes bytes lds + 16 i .. + 16 (lds is the wave's 1 KB destination).  The
+// waits for these loads are explicit (s_waitcnt vmcnt in the main loop).
+__device__ __forceinline__ void dma16(const void *g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(__builtin_amdgcn_readfirstlane(lds)),
+               "v"(g)
+               : "memory", "m0");
 }
 
-// Hidden tile: thread t stages row t >> 1, elements 32 (t & 1) .. + 32 of the step.
-__device__ __forceinline__ void load_h(uint4 (&h)[4], const uint16_t *hp, int kb) {
-  const uint4 *src = reinterpret_cast<const uint4 *>(hp + (int64_t)kb * kLmK);
+// Per-lane source rows of the stage copies: wave w's load i of a part fills
+// the part's bytes (n_w + i) KB .. + 1 KB, i.e. rows 16 (n_w + i) + (lane >> 2),
+// stored chunk lane & 3, which holds chunk chunk_pos(row, lane & 3) of the
+// row's 64 bytes (n_w = kDmaW w for W, kDmaH w for the hidden part).
+struct DmaSrc {
+  const uint16_t *w[kDmaW];  // W rows (+ chunk offset), step 0
+  const uint16_t *h[kDmaH];  // hidden rows (+ chunk offset), step 0
+};
+
+__device__ __forceinline__ void issue_stage(const DmaSrc &src, uint32_t stage_lds, int kb) {
+  const int wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) h[j] = src[j];
+  for (int i = 0; i < kDmaW; ++i) dma16(src.w[i] + (int64_t)kb * kLmK, stage_lds + (kDmaW * wave + i) * 1024);
+#pragma unroll
+  for (int i = 0; i < kDmaH; ++i)
+    dma16(src.h[i] + (int64_t)kb * kLmK, stage_lds + kWPart + (kDmaH * wave + i) * 1024);
 }
 
-__device__ __forceinline__ void store_h(unsigned char *stage, int hoff, const uint4 (&h)[4]) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4 *>(stage + hoff + 16 * j) = h[j];
+// Waits until at most `ahead` steps of this wave's stage copies are in flight.
+__device__ __forceinline__ void wait_stages(int ahead) {
+  static_assert(kDmaW + kDmaH == 6 && kStages == 3, "vmcnt immediates below assume 6 loads per step");
+  if (ahead >= 1)
+    asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-// One main-loop step on stage S: prefetch step kb + 1 (hidden tile first, so
-// waiting for it leaves the W loads in flight), 32 MFMAs, stage the prefetched
-// hidden tile in the other buffer.
-template <int S>
-__device__ __forceinline__ void gemm_step(LmShared &sh, f32x16 (&acc)[2][4], uint4 (&wa)[2][2][4], uint4 (&hs)[4],
-                                          const uint16_t *const (&wp)[2], const uint16_t *hp, int hoff, int boff,
-                                          int kb, int nk) {
-  const bool more = kb + 1 < nk;
-  if (more) {
-    load_h(hs, hp, kb + 1);
-    load_w(wa[S ^ 1], wp, kb + 1);
-  }
-  const unsigned char *stage = sh.u.h[S];
+// MFMAs of one step on stage S: MFMA k index 8 (l >> 5) + e of sub-step j is
+// hidden element 16 j + 8 (l >> 5) + e of the step, i.e. chunk 2 j + (l >> 5).
+__device__ __forceinline__ void compute_stage(const unsigned char *stage, f32x16 (&acc)[2][4]) {
+  const int lane = threadIdx.x & 63, l32 = lane & 31, half = lane >> 5, wave = threadIdx.x >> 6;
+  bf16x8 wf[2][2], hf[2][4];  // both sub-steps' fragments are read first
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    bf16x8 hb[4];
+  for (int j = 0; j < 2; ++j) {
+    const int c = 2 * j + half;
 #pragma unroll
-    for (int tn = 0; tn < 4; ++tn)
-      hb[tn] = *reinterpret_cast<const bf16x8 *>(stage + boff + tn * 32 * kHPitch + 16 * j);
+    for (int t = 0; t < 2; ++t) {
+      const int rw = 64 * wave + 32 * t + l32;
+      wf[j][t] = *reinterpret_cast<const bf16x8 *>(stage + rw * kRowBytes + 16 * chunk_pos(rw, c));
+    }
 #pragma unroll
-    for (int tm = 0; tm < 2; ++tm) {
-      const bf16x8 wf = __builtin_bit_cast(bf16x8, wa[S][tm][j]);
-#pragma unroll
-      for (int tn = 0; tn < 4; ++tn)
-        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf, hb[tn], acc[tm][tn], 0, 0, 0);
+    for (int t = 0; t < 4; ++t) {
+      const int rh = 32 * t + l32;
+      hf[j][t] = *reinterpret_cast<const bf16x8 *>(stage + kWPart + rh * kRowBytes + 16 * chunk_pos(rh, c));
     }
   }
-  if (more) store_h(sh.u.h[S ^ 1], hoff, hs);
-  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int tm = 0; tm < 2; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < 4; ++tn)
+        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j][tm], hf[j][tn], acc[tm][tn], 0, 0, 0);
+}
+
+// Step kb on ring slot S: wait for its copies (this wave's, then everybody's
+// through the barrier, which also retires every wave's reads of the slot the
+// next copy overwrites), start the copy of step kb + kStages - 1, compute.
+template <int S>
+__device__ __forceinline__ void main_step(LmShared &sh, const DmaSrc &src, uint32_t ring_lds, f32x16 (&acc)[2][4],
+                                          int kb, int nk) {
+  wait_stages(min(nk - 1 - kb, kStages - 2));
+  __builtin_amdgcn_s_barrier();
+  if (kb + kStages - 1 < nk) issue_stage(src, ring_lds + ((S + kStages - 1) % kStages) * kStage, kb + kStages - 1);
+  compute_stage(sh.u.ring[S], acc);
 }
 
 __device__ __forceinline__ float shfl32f(float v) { return __shfl_xor(v, 32); }
 __device__ __forceinline__ int shfl32i(int v) { return __shfl_xor(v, 32); }
 
 // Epilogue of row subtile TN: lane l holds the logits of row 32 TN + (l & 31)
-// for tokens tok0 + 64 wave + 32 tm + 8 (q >> 2) + 4 (l >> 5) + (q & 3), q < 16;
-// lanes l and l ^ 32 together hold the wave's 64 tokens.
+// for tokens tok0 + 64 wave + 32 tm + 8 (q >> 2) + 4 (l >> 5) + (q & 3),
+// tm < 2, q < 16; lanes l and l ^ 32 together hold the wave's 64 tokens.
 template <int TN>
 __device__ __forceinline__ void epilogue_rows(const LmParams &p, LmShared &sh, const f32x16 (&acc)[2][4], int tok0,
                                               int row0) {
@@ -257,17 +294,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     sh.d[tid] = d;
   }
 
-  const int half = lane >> 5, l32 = lane & 31;
-  const uint16_t *wp[2];
+  // Copy sources: tokens past V read row V - 1, rows past R read row R - 1
+  // (their results are masked in the epilogue).
+  DmaSrc src;
 #pragma unroll
-  for (int tm = 0; tm < 2; ++tm) {
-    const int t = min(tok0 + 64 * wave + 32 * tm + l32, p.V - 1);  // tokens past V read row V - 1 (masked later)
-    wp[tm] = p.W + (int64_t)t * p.wstride + 32 * half;
+  for (int i = 0; i < kDmaW; ++i) {
+    const int r = 16 * (kDmaW * wave + i) + (lane >> 2);
+    src.w[i] = p.W + (int64_t)min(tok0 + r, p.V - 1) * p.wstride + 8 * chunk_pos(r, lane & 3);
   }
-  const int hr = tid >> 1, hh = tid & 1;
-  const uint16_t *hp = p.H + (int64_t)min(row0 + hr, p.R - 1) * p.hstride + 32 * hh;  // rows past R: row R - 1
-  const int hoff = hr * kHPitch + 64 * hh;
-  const int boff = l32 * kHPitch + 64 * half;
+#pragma unroll
+  for (int i = 0; i < kDmaH; ++i) {
+    const int r = 16 * (kDmaH * wave + i) + (lane >> 2);
+    src.h[i] = p.H + (int64_t)min(row0 + r, p.R - 1) * p.hstride + 8 * chunk_pos(r, lane & 3);
+  }
+  // LDS byte address of the ring (an address-space-3 pointer is the offset itself).
+  const uint32_t ring_lds =
+      (uint32_t)(uintptr_t)((__attribute__((address_space(3))) unsigned char *)(&sh.u.ring[0][0]));
 
   f32x16 acc[2][4];
 #pragma unroll
@@ -276,18 +318,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     for (int tn = 0; tn < 4; ++tn)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[tm][tn][q] = 0.0f;
-  uint4 wa[2][2][4];
-  uint4 hs[4];
+
   const int nk = p.d / kLmK;
-  load_h(hs, hp, 0);
-  load_w(wa[0], wp, 0);
-  store_h(sh.u.h[0], hoff, hs);
-  __syncthreads();
-  for (int kb = 0; kb < nk; kb += 2) {
-    gemm_step<0>(sh, acc, wa, hs, wp, hp, hoff, boff, kb, nk);
-    if (kb + 1 < nk) gemm_step<1>(sh, acc, wa, hs, wp, hp, hoff, boff, kb + 1, nk);
+  __syncthreads();  // sh.a / sh.d written; nothing in flight
+#pragma unroll
+  for (int s = 0; s < kStages - 1; ++s)
+    if (s < nk) issue_stage(src, ring_lds + s * kStage, s);
+  for (int kb = 0; kb < nk; kb += kStages) {
+    main_step<0>(sh, src, ring_lds, acc, kb, nk);
+    if (kb + 1 < nk) main_step<1>(sh, src, ring_lds, acc, kb + 1, nk);
+    if (kb + 2 < nk) main_step<2>(sh, src, ring_lds, acc, kb + 2, nk);
   }
-  // (every gemm_step ends with a barrier: the hidden buffers are free)
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();  // every wave done with the ring: it now holds the epilogue partials
 
   epilogue_rows<0>(p, sh, acc, tok0, row0);
   epilogue_rows<1>(p, sh, acc, tok0, row0);

@@ -187,8 +187,8 @@ def test_lm_head_invalid_requests():
         assert g["err"] == sv.SV_ERR_ROW
         assert g["num_sampled"][5] == 0 and np.all(g["tokens"][5] == -1)
         assert np.all(g["num_sampled"][[0, 1, 2, 3, 4, 6, 7]] >= 1)
-        # host-side checks: hidden size not a multiple of 64, no LM-head storage
-        bad = wl.make_lm_head_inputs(B=2, K=1, V=100, d=96, device=DEV)
+        # host-side checks: hidden size not a multiple of 32, no LM-head storage
+        bad = wl.make_lm_head_inputs(B=2, K=1, V=100, d=80, device=DEV)
         with pytest.raises(sv.SpecVerifyError):
             lm_run(ctx, bad)
         plain = sv.spec_verify_create(inp["R"], inp["B"], 2, inp["V"], 0)
