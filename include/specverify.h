@@ -78,6 +78,7 @@ extern "C" {
 #define SV_RACE_CHUNK 1024        /* tokens per chunk of the two-level race        */
 #define SV_MAX_DRAFTS 64          /* largest max_k a context accepts               */
 #define SV_TOPK_CANDIDATES 1024   /* top-k rows with more kept tokens use the dense path */
+#define SV_LM_HEAD_CHUNK 64       /* tokens per race chunk of spec_verify_lm_head          */
 
 typedef struct sv_ctx sv_ctx; /* opaque; owns the device scratch */
 
@@ -267,14 +268,17 @@ int spec_verify_synthetic_rates(float mean_length, int32_t k, float *rates);
  * top-p: greedy requests (T = 0) compare each draft with the row's argmax
  * (lowest index on ties); sampled requests accept d_i iff it is a valid id and
  * p_i(d_i) >= u_i, and the recovered token (p_j with d_j removed) or the bonus
- * token is drawn by the exponential race argmax_x p_x / E_x over the whole
- * vocabulary in one level (the race of the NO_DRAFT_PROBS Q&A of "vLLM
- * 投机解码（Eagle / MTP）实现与运行流程"; E_x from tag 2 of the row's Philox
- * stream, as in spec_verify_run; the law is exactly p).  Outputs as
+ * token is drawn by the two-level exponential race of spec_verify_run with
+ * chunks of SV_LM_HEAD_CHUNK tokens (the race of the NO_DRAFT_PROBS Q&A of
+ * "vLLM 投机解码（Eagle / MTP）实现与运行流程"; tags 1 and 2 of the row's
+ * Philox stream; the law is exactly p): the GEMM leaves per (row, chunk) the
+ * maximum logit, the chunk's mass and its argmax, and the winning chunk's
+ * logits are recomputed from W and h for the token race.  Outputs as
  * spec_verify_run.  The context must be created with SV_CREATE_LM_HEAD
- * (records of ceil(max_vocab / 256) x 16 bytes per row).  Cost: one pass over W
- * (V d bf16) per 128 target rows, shared through L2 by the workgroups of one
- * token tile, and 2 R V d flops.
+ * (records of ceil(max_vocab / SV_LM_HEAD_CHUNK) x 16 bytes per row).  Cost:
+ * one pass over W (V d bf16) per 256 target rows, shared through L2 by the
+ * workgroups of one token tile, 2 R V d flops, and SV_LM_HEAD_CHUNK rows of W
+ * per sampled request.
  * Errors: SV_EINVAL (NULL pointer, hidden_size not a positive multiple of 32,
  * strides below hidden_size or not multiples of 8, bases not 16-byte aligned,
  * offset >= 2^32), SV_ECAPACITY (sizes beyond the context, or no

@@ -24,6 +24,7 @@ _SRC = os.path.join(_HERE, "oracle.c")
 _SO = os.path.join(_HERE, "liborc.so")
 
 RACE_CHUNK = 1024
+LM_HEAD_CHUNK = 64  # race chunk width of the LM-head path
 TAG_ACCEPT, TAG_CHUNK, TAG_TOKEN, TAG_DRAFT_CHUNK, TAG_DRAFT_TOKEN = 0, 1, 2, 3, 4
 F32, BF16 = 0, 1
 ERR_CU, ERR_TEMPERATURE, ERR_PENALTY, ERR_ROW, ERR_SLOT, ERR_OFFSET = 1, 2, 4, 8, 16, 32
@@ -117,8 +118,8 @@ def lib():
         L.orc_decide_request_q64.restype = f64
         L.orc_lm_head_logits.argtypes = [P, P, i64, i32, i32, i32, P]
         L.orc_lm_head_logits.restype = None
-        L.orc_lm_head_verify.argtypes = [P, i64, P, i64, i32, i32, P, P, i32, P, u64, u64, P, i32, P, P,
-                                         P, P, P, P]
+        L.orc_lm_head_verify.argtypes = [P, i64, P, i64, i32, i32, P, P, i32, P, u64, u64, i32, P, i32, P,
+                                         P, P, P, P, P]
         L.orc_lm_head_verify.restype = ctypes.c_uint32
         L.orc_draft_q_rows.argtypes = [P, ctypes.c_int, i64, i32, i32, f32, P]
         L.orc_draft_q_rows.restype = ctypes.c_int
@@ -274,8 +275,8 @@ def lm_head_logits(h_bits, W_bits, x0: int = 0, x1=None) -> np.ndarray:
 
 
 def lm_head_verify(hidden_bits, W_bits, cu, draft_ids, temperature, seed: int = 0, offset: int = 0,
-                   out_stride=None, requests=None):
-    """Verify step on LM-head logits (no-draft-probs mode, one-level race).
+                   out_stride=None, requests=None, C: int = LM_HEAD_CHUNK):
+    """Verify step on LM-head logits (no-draft-probs mode, two-level race of chunk width C).
     hidden_bits [R, d] and W_bits [V, d]: bf16 bit patterns (uint16).  requests:
     optional iterable of the request ids to compute (others stay -1 / 0).
     Returns a dict with tokens [B, out_stride], num_sampled, num_rejected,
@@ -303,7 +304,7 @@ def lm_head_verify(hidden_bits, W_bits, cu, draft_ids, temperature, seed: int = 
         only = np.zeros(max(B, 1), dtype=np.uint8)
         only[list(requests)] = 1
     err = lib().orc_lm_head_verify(_ptr(H), d, _ptr(W), d, d, V, _ptr(dd), _ptr(cu), B, _ptr(T), seed,
-                                   offset, _ptr(tokens), out_stride, _ptr(ns), _ptr(nr), _ptr(mg),
+                                   offset, int(C), _ptr(tokens), out_stride, _ptr(ns), _ptr(nr), _ptr(mg),
                                    _ptr(gg), _ptr(pd), _ptr(only))
     return dict(tokens=tokens, num_sampled=ns, num_rejected=nr, margin=mg, greedy_gap=gg,
                 p_draft=pd[:D], err=int(err))

@@ -587,11 +587,11 @@ void orc_lm_head_logits(const uint16_t *h, const uint16_t *W, int64_t wstride, i
 /* The verify step on LM-head logits (row f2): for each request the logits of
  * its K+1 rows come from orc_lm_head_logits (fp64, never rounded to fp32),
  * then the no-draft-probs rules of 8.3 of "vLLM 投机解码（Eagle / MTP）实现与运行
- * 流程" with the one-level race (chunk width V, the NO_DRAFT_PROBS Q&A's
- * argmax(w / E) over all tokens): greedy rows take the first fp64 argmax,
- * sampled rows p = softmax(z / T) in fp64.  *gap receives, per request, the
- * smallest fp64 logit gap between the best and second-best token of a greedy
- * row it used (+inf for sampled requests or V = 1). */
+ * 流程" with the two-level race of chunk width C (the NO_DRAFT_PROBS Q&A's
+ * argmax(w / E), run over chunks and then tokens): greedy rows take the first
+ * fp64 argmax, sampled rows p = softmax(z / T) in fp64.  *gap receives, per
+ * request, the smallest fp64 logit gap between the best and second-best token
+ * of a greedy row it used (+inf for sampled requests or V = 1). */
 static int32_t argmax64(const double *z, int32_t V, double *gap) {
   int32_t best = 0;
   for (int32_t x = 1; x < V; ++x)
@@ -606,7 +606,7 @@ static int32_t argmax64(const double *z, int32_t V, double *gap) {
 uint32_t orc_lm_head_verify(const uint16_t *hidden, int64_t hstride, const uint16_t *W,
                             int64_t wstride, int32_t d, int32_t V, const int32_t *draft_ids,
                             const int32_t *cu, int32_t B, const float *temperature, uint64_t seed,
-                            uint64_t offset, int32_t *out_tokens, int32_t out_stride,
+                            uint64_t offset, int32_t C, int32_t *out_tokens, int32_t out_stride,
                             int32_t *num_sampled, int32_t *num_rejected, double *margin,
                             double *greedy_gap, float *p_draft, const uint8_t *only) {
   uint32_t err = 0;
@@ -661,7 +661,7 @@ uint32_t orc_lm_head_verify(const uint16_t *hidden, int64_t hstride, const uint1
     float *pd = p_draft ? p_draft + cu[r] : NULL;
     float pd_tmp[64];
     const double mg = orc_decide_request(P, amax, K, V, T, draft_ids + cu[r], NULL, V, (uint32_t)g0,
-                                         seed, (uint32_t)offset, V, out_tokens + (int64_t)r * out_stride,
+                                         seed, (uint32_t)offset, C, out_tokens + (int64_t)r * out_stride,
                                          &ns, &nr, pd ? pd : pd_tmp);
     num_sampled[r] = ns;
     num_rejected[r] = nr;

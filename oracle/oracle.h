@@ -149,14 +149,14 @@ void orc_lm_head_logits(const uint16_t *h, const uint16_t *W, int64_t wstride, i
  * stride hstride, W [V, d] with row stride wstride (bf16 bits); per request the
  * logits of its rows by orc_lm_head_logits, then greedy (first fp64 argmax) or
  * p = softmax(z / T) in fp64, and the decisions of orc_decide_request with the
- * one-level race (chunk width V).  Outputs as orc_verify_batch; greedy_gap [B]
+ * two-level race of chunk width C.  Outputs as orc_verify_batch; greedy_gap [B]
  * (or NULL) receives each greedy request's smallest top-1 / top-2 logit gap over
  * the rows it used (+inf otherwise).  only [B] (or NULL): requests with only[r]
  * == 0 are skipped (outputs left at -1 / 0).  Returns the ORC_ERR_* mask. */
 uint32_t orc_lm_head_verify(const uint16_t *hidden, int64_t hstride, const uint16_t *W,
                             int64_t wstride, int32_t d, int32_t V, const int32_t *draft_ids,
                             const int32_t *cu, int32_t B, const float *temperature, uint64_t seed,
-                            uint64_t offset, int32_t *out_tokens, int32_t out_stride,
+                            uint64_t offset, int32_t C, int32_t *out_tokens, int32_t out_stride,
                             int32_t *num_sampled, int32_t *num_rejected, double *margin,
                             double *greedy_gap, float *p_draft, const uint8_t *only);
 

@@ -32,7 +32,7 @@ SV_OK, SV_EINVAL, SV_ECAPACITY, SV_EDTYPE, SV_EHIP, SV_EINPUT = 0, -1, -2, -3, -
 SV_F32, SV_BF16 = 0, 1
 SV_CREATE_TOPK = 1
 SV_CREATE_LM_HEAD = 2
-SV_LM_HEAD_TILE = 256
+SV_LM_HEAD_CHUNK = 64
 SV_RACE_CHUNK = 1024
 SV_MAX_DRAFTS = 64
 SV_TOPK_CANDIDATES = 1024

@@ -29,7 +29,7 @@ struct sv_ctx {
   int32_t *cand_n;
   float *cand_tau;
   int32_t *zeros;    // [max_reqs + 1] zero prefix sums (draft-side sampling: row r is request r)
-  float4 *lm_rec;    // [max_rows, ceil(max_vocab / 256)] LM-head tile records (SV_CREATE_LM_HEAD)
+  float4 *lm_rec;    // [max_rows, ceil(max_vocab / 64)] LM-head chunk records (SV_CREATE_LM_HEAD)
   float4 *lm_drec;   // [max_rows] LM-head draft-token records
   unsigned int *err;
   hipEvent_t *ev;   // measurement: 4 events per recorded call
@@ -96,7 +96,7 @@ extern "C" int spec_verify_create(sv_ctx **out, int32_t max_rows, int32_t max_re
   if (ok && (flags & SV_CREATE_TOPK))
     ok = dev_alloc(&c->cand_val, rows * sv::kCandCap) && dev_alloc(&c->cand_idx, rows * sv::kCandCap);
   if (ok && (flags & SV_CREATE_LM_HEAD))
-    ok = dev_alloc(&c->lm_rec, rows * (size_t)((max_vocab + sv::kLmTok - 1) / sv::kLmTok)) &&
+    ok = dev_alloc(&c->lm_rec, rows * (size_t)((max_vocab + sv::kLmChunk - 1) / sv::kLmChunk)) &&
          dev_alloc(&c->lm_drec, rows);
   if (ok)
     ok = hipMemset(c->res_req, 0, reqs * sizeof(int4)) == hipSuccess &&
@@ -458,6 +458,7 @@ extern "C" int spec_verify_lm_head(sv_ctx *ctx, const sv_lm_head_args *a, hipStr
   p.D = D;
   p.V = a->vocab_size;
   p.NT = NT;
+  p.NC = (a->vocab_size + sv::kLmChunk - 1) / sv::kLmChunk;
   p.RB = RB;
   p.out_stride = a->out_stride;
   p.seed_lo = (uint32_t)(a->seed & 0xFFFFFFFFu);

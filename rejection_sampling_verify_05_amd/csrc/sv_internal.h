@@ -107,9 +107,12 @@ struct DraftOut {
 // LM-head path: the logits of target row g are z = W h_g (W [V, d], h_g [d],
 // bf16), computed tile by tile and reduced in the tile's epilogue; they are
 // never stored (except to dbg_logits).
-constexpr int kLmTok = 256;   // tokens per workgroup tile (the unit of the per-tile records)
-constexpr int kLmRows = 128;  // target rows per workgroup tile
-constexpr int kLmK = 32;      // hidden elements per main-loop step (d must be a multiple)
+constexpr int kLmTok = 256;     // tokens per workgroup tile
+constexpr int kLmRows = 256;    // target rows per workgroup tile
+constexpr int kLmK = 32;        // hidden elements per main-loop step (d must be a multiple)
+constexpr int kLmChunk = 64;    // tokens per race chunk (SV_LM_HEAD_CHUNK; one record per row and chunk)
+constexpr int kLmThreads = 512; // threads of the GEMM workgroup (8 waves)
+static_assert(kLmChunk == SV_LM_HEAD_CHUNK, "the ABI names the LM-head race chunk");
 
 struct LmParams {
   const uint16_t *H;          // [R, hstride] hidden states (bf16 bits)
@@ -122,10 +125,11 @@ struct LmParams {
   int32_t *out_tokens, *out_ns, *out_nr;
   float *dbg_p_draft;         // [D] or null
   float *dbg_logits;          // [R, V] or null
-  float4 *rec;                // [R, NT]: per (row, tile) (max z, sum exp2(a (z - max)), best race key, token bits)
-  float4 *drec;               // [R]: the draft token's tile, (z_d, best key without d, its token bits, 0)
+  float4 *rec;                // [R, NC]: per (row, chunk) (max z, sum exp2(a (z - max)), lowest argmax bits, 0)
+  float4 *drec;               // [R]: the draft token's chunk, (z_d, its mass without d, 0, 0)
   unsigned int *err;
   int32_t R, B, D, V;
+  int32_t NC;                 // chunks ceil(V / kLmChunk)
   int32_t NT;                 // token tiles ceil(V / kLmTok)
   int32_t RB;                 // row blocks ceil(R / kLmRows)
   int32_t out_stride;

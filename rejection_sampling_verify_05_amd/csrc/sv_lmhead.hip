@@ -4,20 +4,19 @@
 // times the LM-head weight W [V, d], both bf16 ("【vllm】DeepSeekMTP、eagle":
 // compute_logits is the LM head applied to the hidden states of the logit
 // positions).  lm_gemm_kernel computes them on the bf16 matrix cores tile by
-// tile (256 tokens x 128 rows) and reduces each tile in its epilogue to what
-// the verify step needs ("speculative decoding in vLLM", 7.4: the statistics
-// pass takes max, argmax and sum of exp over the target logits): per (row,
-// tile) the maximum logit, sum exp2(a (z - max)), the sampling race's best
-// token with its key, and for a draft row the draft token's logit and the
-// race's best token without it.  The logits never reach memory.
-// lm_request_kernel then takes each request's decisions from those records:
-// the accept tests, the first reject, the recovered or bonus token (8.3 of
-// "vLLM 投机解码（Eagle / MTP）实现与运行流程", no-draft-probs mode).
+// tile (256 tokens x 256 rows) and reduces them in its epilogue to what the
+// verify step needs ("speculative decoding in vLLM", 7.4: the statistics pass
+// takes max, argmax and sum of exp over the target logits): per row and chunk
+// of kLmChunk = 64 tokens the maximum logit, sum exp2(a (z - max)) and the
+// lowest argmax, and for a draft row the draft token's logit and its chunk's
+// mass without it.  The logits never reach memory.
 //
-// Sampling is the one-level exponential race argmax_x w_x / E_x of the
-// NO_DRAFT_PROBS Q&A, compared as keys a (z_x - m) - log2(E_x) (a = log2(e) /
-// T): E_x is drawn for every token of every sampled row in the epilogue, so
-// whichever row a request samples, its winner is already known.
+// lm_request_kernel then takes each request's decisions from those records:
+// the accept tests, the first reject, and the recovered or bonus token (8.3 of
+// "vLLM 投机解码（Eagle / MTP）实现与运行流程", no-draft-probs mode) by the
+// two-level exponential race of the NO_DRAFT_PROBS Q&A: a chunk by its mass,
+// then a token of that chunk, whose 64 logits it recomputes from W and h (a
+// 512 KB read per sampled request at d = 4096, instead of keeping any logits).
 #include <stdint.h>
 
 #include "sv_device.h"
@@ -33,43 +32,34 @@ constexpr float kLog2eL = 1.4426950408889634f;
 constexpr float kNegInfL = -__builtin_inff();
 constexpr int kIntMax = 0x7FFFFFFF;
 
-// Main loop: a workgroup (4 waves, one per SIMD; two workgroups per CU, so
-// that one's epilogue overlaps the other's matrix work) owns a tile of kLmTok
-// = 256 tokens x kLmRows = 128 target rows; wave w computes tokens 64 w .. + 64
-// of all 128 rows as 2 x 4 MFMA 32x32x16 tiles (128 fp32 accumulators per
-// lane).  The hidden dimension advances kLmK = 32 elements per step; each
-// step's W slice (256 rows x 64 bytes) and hidden slice (128 rows x 64 bytes)
-// are copied to LDS by the loads themselves (global_load_lds, no registers)
-// into a ring of kStages stages, kStages - 1 steps ahead of the MFMAs.
-constexpr int kStages = 3;
+// Main loop: one workgroup per CU (8 waves, two per SIMD) owns a tile of
+// kLmTok = 256 tokens x kLmRows = 256 target rows; wave w computes the 64
+// tokens of chunk (w & 3) of the tile for rows 128 (w >> 2) .. + 128 as 2 x 4
+// MFMA 32x32x16 tiles (128 fp32 accumulators per lane).  The hidden dimension
+// advances kLmK = 32 elements per step; each step's W and hidden slices (256
+// rows x 64 bytes each) are copied to LDS by the loads themselves
+// (global_load_lds, no registers) into a ring of kStages stages, kStages - 1
+// steps ahead of the MFMAs.
+constexpr int kStages = 4;
 constexpr int kRowBytes = kLmK * 2;                    // 64 bytes of one row per step
 constexpr int kWPart = kLmTok * kRowBytes;             // W part of a stage: 16 KB
-constexpr int kHPart = kLmRows * kRowBytes;            // hidden part: 8 KB
+constexpr int kHPart = kLmRows * kRowBytes;            // hidden part: 16 KB
 constexpr int kStage = kWPart + kHPart;
-constexpr int kDmaW = kWPart / (kThreads * 16);        // 16-byte loads per thread per stage: W (4)
-constexpr int kDmaH = kHPart / (kThreads * 16);        // ... and hidden (2)
+constexpr int kDmaW = kWPart / (kLmThreads * 16);      // 16-byte loads per thread per stage: W (2)
+constexpr int kDmaH = kHPart / (kLmThreads * 16);      // ... and hidden (2)
+static_assert(kLmTok == 4 * kLmChunk, "four chunks per token tile, one per wave column");
+static_assert(kLmChunk % (8 * kWaves) == 0, "the recompute takes tokens in blocks of 8 per wave");
 
 // Rows are stored densely (64 bytes); the 16-byte chunk c of row r sits at
 // position c ^ ((r >> 2) & 3), so that the fragment reads of 16 consecutive
 // rows (one LDS cycle of 16-byte reads) hit 16 distinct bank groups.
 __device__ __forceinline__ int chunk_pos(int r, int c) { return c ^ ((r >> 2) & 3); }
 
-struct LmRed {  // per (wave, row) partial results of the epilogue
-  float m[kWaves][kLmRows], s[kWaves][kLmRows], k1[kWaves][kLmRows], k2[kWaves][kLmRows], zd[kWaves][kLmRows];
-  int x1[kWaves][kLmRows], x2[kWaves][kLmRows], xg[kWaves][kLmRows], hd[kWaves][kLmRows];
-};
-
 struct LmShared {
-  union alignas(16) {
-    unsigned char ring[kStages][kStage];
-    LmRed red;
-  } u;
+  alignas(16) unsigned char ring[kStages][kStage];
   float a[kLmRows];  // log2(e) / T of each row's request (0: greedy or invalid)
   int d[kLmRows];    // draft token of the row (-1: bonus row or no valid draft slot)
 };
-static_assert(sizeof(LmRed) <= kStages * kStage, "epilogue partials reuse the ring");
-
-__device__ __forceinline__ bool key_better(float k, int x, float bk, int bx) { return k > bk || (k == bk && x < bx); }
 
 // One 16-byte load per lane from global memory straight into LDS: lane i
 // writes bytes lds + 16 i .. + 16 (lds is the wave's 1 KB destination).  The
@@ -81,9 +71,9 @@ __device__ __forceinline__ void dma16(const void *g, uint32_t lds) {
 }
 
 // Per-lane source rows of the stage copies: wave w's load i of a part fills
-// the part's bytes (n_w + i) KB .. + 1 KB, i.e. rows 16 (n_w + i) + (lane >> 2),
+// the part's bytes (2 w + i) KB .. + 1 KB, i.e. rows 16 (2 w + i) + (lane >> 2),
 // stored chunk lane & 3, which holds chunk chunk_pos(row, lane & 3) of the
-// row's 64 bytes (n_w = kDmaW w for W, kDmaH w for the hidden part).
+// row's 64 bytes.
 struct DmaSrc {
   const uint16_t *w[kDmaW];  // W rows (+ chunk offset), step 0
   const uint16_t *h[kDmaH];  // hidden rows (+ chunk offset), step 0
@@ -100,29 +90,32 @@ __device__ __forceinline__ void issue_stage(const DmaSrc &src, uint32_t stage_ld
 
 // Waits until at most `ahead` steps of this wave's stage copies are in flight.
 __device__ __forceinline__ void wait_stages(int ahead) {
-  static_assert(kDmaW + kDmaH == 6 && kStages == 3, "vmcnt immediates below assume 6 loads per step");
-  if (ahead >= 1)
-    asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+  static_assert(kDmaW + kDmaH == 4 && kStages == 4, "vmcnt immediates below assume 4 loads per step");
+  if (ahead >= 2)
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else if (ahead == 1)
+    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
   else
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-// MFMAs of one step on stage S: MFMA k index 8 (l >> 5) + e of sub-step j is
-// hidden element 16 j + 8 (l >> 5) + e of the step, i.e. chunk 2 j + (l >> 5).
+// MFMAs of one step: MFMA k index 8 (l >> 5) + e of sub-step j is hidden
+// element 16 j + 8 (l >> 5) + e of the step, i.e. chunk 2 j + (l >> 5).
 __device__ __forceinline__ void compute_stage(const unsigned char *stage, f32x16 (&acc)[2][4]) {
   const int lane = threadIdx.x & 63, l32 = lane & 31, half = lane >> 5, wave = threadIdx.x >> 6;
+  const int tq = wave & 3, wr = wave >> 2;
   bf16x8 wf[2][2], hf[2][4];  // both sub-steps' fragments are read first
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int c = 2 * j + half;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const int rw = 64 * wave + 32 * t + l32;
+      const int rw = 64 * tq + 32 * t + l32;
       wf[j][t] = *reinterpret_cast<const bf16x8 *>(stage + rw * kRowBytes + 16 * chunk_pos(rw, c));
     }
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const int rh = 32 * t + l32;
+      const int rh = 128 * wr + 32 * t + l32;
       hf[j][t] = *reinterpret_cast<const bf16x8 *>(stage + kWPart + rh * kRowBytes + 16 * chunk_pos(rh, c));
     }
   }
@@ -144,24 +137,27 @@ __device__ __forceinline__ void main_step(LmShared &sh, const DmaSrc &src, uint3
   wait_stages(min(nk - 1 - kb, kStages - 2));
   __builtin_amdgcn_s_barrier();
   if (kb + kStages - 1 < nk) issue_stage(src, ring_lds + ((S + kStages - 1) % kStages) * kStage, kb + kStages - 1);
-  compute_stage(sh.u.ring[S], acc);
+  compute_stage(sh.ring[S], acc);
 }
 
 __device__ __forceinline__ float shfl32f(float v) { return __shfl_xor(v, 32); }
 __device__ __forceinline__ int shfl32i(int v) { return __shfl_xor(v, 32); }
 
-// Epilogue of row subtile TN: lane l holds the logits of row 32 TN + (l & 31)
-// for tokens tok0 + 64 wave + 32 tm + 8 (q >> 2) + 4 (l >> 5) + (q & 3),
-// tm < 2, q < 16; lanes l and l ^ 32 together hold the wave's 64 tokens.
+// Epilogue of row subtile TN: lane l holds the logits of row
+// 128 wr + 32 TN + (l & 31) for tokens tok0 + 64 tq + 32 tm + 8 (q >> 2) +
+// 4 (l >> 5) + (q & 3), tm < 2, q < 16; lanes l and l ^ 32 together hold the
+// wave's chunk of 64 tokens.  Lane l < 32 writes the (row, chunk) record.
 template <int TN>
-__device__ __forceinline__ void epilogue_rows(const LmParams &p, LmShared &sh, const f32x16 (&acc)[2][4], int tok0,
-                                              int row0) {
+__device__ __forceinline__ void epilogue_rows(const LmParams &p, const LmShared &sh, const f32x16 (&acc)[2][4],
+                                              int tok0, int row0) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int half = lane >> 5, rl = 32 * TN + (lane & 31);
+  const int tq = wave & 3, wr = wave >> 2;
+  const int half = lane >> 5, rl = 128 * wr + 32 * TN + (lane & 31);
   const int g = row0 + rl;
+  const int c = tok0 / kLmChunk + tq;
   const float a = sh.a[rl];
   const int dd = sh.d[rl];
-  const int xb = tok0 + 64 * wave + 4 * half;
+  const int xb = tok0 + kLmChunk * tq + 4 * half;
   auto tok = [&](int tm, int q) { return xb + 32 * tm + 8 * (q >> 2) + (q & 3); };
 
   float m = kNegInfL;
@@ -186,38 +182,22 @@ __device__ __forceinline__ void epilogue_rows(const LmParams &p, LmShared &sh, c
   m = fmaxf(m, shfl32f(m));
   bad |= shfl32i(bad);
 
-  float s = 0.0f, zd = 0.0f, k1 = kNegInfL, k2 = kNegInfL;
-  int x1 = kIntMax, x2 = kIntMax, xg = kIntMax, hd = 0;
+  float s = 0.0f, sx = 0.0f, zd = 0.0f;
+  int xg = kIntMax, hd = 0;
   if (a > 0.0f) {
-    // Tokens are visited in increasing order, so a strictly larger key is
-    // needed to replace the best (ties keep the lowest token).
 #pragma unroll
     for (int tm = 0; tm < 2; ++tm)
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const int x0 = tok(tm, 4 * qq);
-        const uint4 w4 = philox10(make_uint4((uint32_t)x0 >> 2, (uint32_t)g, kTagToken, p.offset), p.seed_lo, p.seed_hi);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int x = x0 + e;
-          const float z = acc[tm][TN][4 * qq + e];
-          if (x < p.V) {
-            const float t = a * (z - m);
-            s += __builtin_amdgcn_exp2f(t);
-            const float key = t - __builtin_amdgcn_logf(exp_noise(pick(w4, e)));
-            if (key > k1) {
-              k1 = key;
-              x1 = x;
-            }
-            if (x != dd && key > k2) {
-              k2 = key;
-              x2 = x;
-            }
-            if (x == dd) {
-              zd = z;
-              hd = 1;
-            }
-          }
+      for (int q = 0; q < 16; ++q) {
+        const int x = tok(tm, q);
+        const float z = acc[tm][TN][q];
+        const float w = x < p.V ? __builtin_amdgcn_exp2f(a * (z - m)) : 0.0f;
+        s += w;
+        if (x == dd) {
+          zd = z;
+          hd = 1;
+        } else {
+          sx += w;
         }
       }
   } else {
@@ -227,18 +207,8 @@ __device__ __forceinline__ void epilogue_rows(const LmParams &p, LmShared &sh, c
       for (int q = 0; q < 16; ++q)
         if (tok(tm, q) < p.V && acc[tm][TN][q] == m) xg = min(xg, tok(tm, q));
   }
-  // Combine with the partner lane (the other 32 tokens of the wave).
   s += shfl32f(s);
-  {
-    const float pk = shfl32f(k1);
-    const int px = shfl32i(x1);
-    if (key_better(pk, px, k1, x1)) k1 = pk, x1 = px;
-  }
-  {
-    const float pk = shfl32f(k2);
-    const int px = shfl32i(x2);
-    if (key_better(pk, px, k2, x2)) k2 = pk, x2 = px;
-  }
+  sx += shfl32f(sx);
   xg = min(xg, shfl32i(xg));
   {
     const float pz = shfl32f(zd);
@@ -246,21 +216,13 @@ __device__ __forceinline__ void epilogue_rows(const LmParams &p, LmShared &sh, c
     if (ph) zd = pz;
     hd |= ph;
   }
-  if (half == 0) {
-    LmRed &r = sh.u.red;
-    r.m[wave][rl] = bad ? __builtin_nanf("") : m;
-    r.s[wave][rl] = s;
-    r.k1[wave][rl] = k1;
-    r.x1[wave][rl] = x1;
-    r.k2[wave][rl] = k2;
-    r.x2[wave][rl] = x2;
-    r.xg[wave][rl] = xg;
-    r.zd[wave][rl] = zd;
-    r.hd[wave][rl] = hd;
+  if (half == 0 && g < p.R && c < p.NC) {
+    p.rec[(int64_t)g * p.NC + c] = make_float4(bad ? __builtin_nanf("") : m, s, __int_as_float(xg), 0.0f);
+    if (hd) p.drec[g] = make_float4(zd, sx, 0.0f, 0.0f);
   }
 }
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void lm_gemm_kernel(LmParams p) {
+__global__ __launch_bounds__(kLmThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void lm_gemm_kernel(LmParams p) {
   __shared__ LmShared sh;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
@@ -295,7 +257,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
 
   // Copy sources: tokens past V read row V - 1, rows past R read row R - 1
-  // (their results are masked in the epilogue).
+  // (their results are never written).
   DmaSrc src;
 #pragma unroll
   for (int i = 0; i < kDmaW; ++i) {
@@ -308,8 +270,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     src.h[i] = p.H + (int64_t)min(row0 + r, p.R - 1) * p.hstride + 8 * chunk_pos(r, lane & 3);
   }
   // LDS byte address of the ring (an address-space-3 pointer is the offset itself).
-  const uint32_t ring_lds =
-      (uint32_t)(uintptr_t)((__attribute__((address_space(3))) unsigned char *)(&sh.u.ring[0][0]));
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) unsigned char *)(&sh.ring[0][0]));
 
   f32x16 acc[2][4];
 #pragma unroll
@@ -328,73 +289,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     main_step<0>(sh, src, ring_lds, acc, kb, nk);
     if (kb + 1 < nk) main_step<1>(sh, src, ring_lds, acc, kb + 1, nk);
     if (kb + 2 < nk) main_step<2>(sh, src, ring_lds, acc, kb + 2, nk);
+    if (kb + 3 < nk) main_step<3>(sh, src, ring_lds, acc, kb + 3, nk);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();  // every wave done with the ring: it now holds the epilogue partials
 
   epilogue_rows<0>(p, sh, acc, tok0, row0);
   epilogue_rows<1>(p, sh, acc, tok0, row0);
   epilogue_rows<2>(p, sh, acc, tok0, row0);
   epilogue_rows<3>(p, sh, acc, tok0, row0);
-  __syncthreads();
-
-  // One thread per row merges the four waves (in token order) into the tile record.
-  if (tid < kLmRows) {
-    const int g = row0 + tid;
-    if (g < p.R) {
-      const LmRed &r = sh.u.red;
-      const float a = sh.a[tid];
-      const int dd = sh.d[tid];
-      float mc = kNegInfL;
-      int bad = 0;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float mw = r.m[w][tid];
-        if (mw != mw)
-          bad = 1;
-        else
-          mc = fmaxf(mc, mw);
-      }
-      float4 out;
-      if (a > 0.0f) {
-        float sc = 0.0f, kc = kNegInfL, k2c = kNegInfL, zdc = 0.0f;
-        int xc = kIntMax, x2c = kIntMax, hdc = 0;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-          const float mw = r.m[w][tid];
-          if (mw > kNegInfL) {  // the wave held valid tokens
-            const float sh_ = a * (mw - mc);
-            sc += r.s[w][tid] * __builtin_amdgcn_exp2f(sh_);
-            const float ka = r.k1[w][tid] + sh_, kb = r.k2[w][tid] + sh_;
-            if (key_better(ka, r.x1[w][tid], kc, xc)) kc = ka, xc = r.x1[w][tid];
-            if (key_better(kb, r.x2[w][tid], k2c, x2c)) k2c = kb, x2c = r.x2[w][tid];
-          }
-          if (r.hd[w][tid]) {
-            zdc = r.zd[w][tid];
-            hdc = 1;
-          }
-        }
-        out = make_float4(bad ? __builtin_nanf("") : mc, sc, kc, __int_as_float(xc));
-        if (hdc && dd >= 0) p.drec[g] = make_float4(zdc, k2c, __int_as_float(x2c), 0.0f);
-      } else {
-        int xg = kIntMax;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w)
-          if (r.m[w][tid] == mc) xg = min(xg, r.xg[w][tid]);
-        out = make_float4(bad ? __builtin_nanf("") : mc, 0.0f, 0.0f, __int_as_float(xg));
-      }
-      p.rec[(int64_t)g * p.NT + tt] = out;
-    }
-  }
 }
 
 // ---------------------------------------------------------------------------
-// Request kernel: one workgroup per request; wave w reduces rows w, w + 4, ...
+// Request kernel: one workgroup (256 threads) per request.
 // ---------------------------------------------------------------------------
 struct LmReqShared {
-  float m[kMaxDrafts + 1], s[kMaxDrafts + 1], zd[kMaxDrafts + 1];
-  int amax[kMaxDrafts + 1], xw[kMaxDrafts + 1], d[kMaxDrafts + 1], bad[kMaxDrafts + 1];
+  float m[kMaxDrafts + 1], s[kMaxDrafts + 1], zd[kMaxDrafts + 1], sxd[kMaxDrafts + 1];
+  int amax[kMaxDrafts + 1], d[kMaxDrafts + 1], bad[kMaxDrafts + 1];
   int j;
+  float z[kLmChunk];  // recomputed logits of the winning chunk
+  BlockScratch red;
 };
 
 __device__ __forceinline__ void lm_write_empty(const LmParams &p, int r) {
@@ -403,6 +316,12 @@ __device__ __forceinline__ void lm_write_empty(const LmParams &p, int r) {
     p.out_ns[r] = 0;
     p.out_nr[r] = 0;
   }
+}
+
+// Race noise 1/E of position idx of stream (g, tag) (one position).
+__device__ __forceinline__ float inv_noise(const LmParams &p, uint32_t idx, uint32_t g, uint32_t tag) {
+  const uint4 w4 = philox10(make_uint4(idx >> 2, g, tag, p.offset), p.seed_lo, p.seed_hi);
+  return __builtin_amdgcn_rcpf(exp_noise(pick(w4, (int)(idx & 3))));
 }
 
 __global__ __launch_bounds__(kThreads) void lm_request_kernel(LmParams p) {
@@ -425,57 +344,55 @@ __global__ __launch_bounds__(kThreads) void lm_request_kernel(LmParams p) {
   const float a = greedy ? 0.0f : kLog2eL / T;
   const int nrow = K + 1;
 
+  // Row statistics from the chunk records: wave w takes rows w, w + 4, ...
   for (int i = wave; i < nrow; i += kWaves) {
     const int g = g0 + i;
     const int d = i < K ? p.draft_ids[c0 + i] : -1;
     const bool vd = i < K && d >= 0 && d < p.V;
-    const float4 *rr = p.rec + (int64_t)g * p.NT;
-    float lm = kNegInfL;
-    int lbad = 0;
-    for (int c = lane; c < p.NT; c += 64) {
-      const float x = rr[c].x;
-      if (x != x)
-        lbad = 1;
-      else
-        lm = fmaxf(lm, x);
+    const float4 *rr = p.rec + (int64_t)g * p.NC;
+    // One pass over the records with 8 loads in flight per lane; a lane keeps
+    // (max, mass relative to it), rescaled when the max grows (greedy rows: the
+    // max and the first chunk holding it; chunks are visited in order).
+    float lm = kNegInfL, ls = 0.0f;
+    int lbad = 0, lc = kIntMax;
+    for (int cb = lane; cb < p.NC; cb += 64 * 8) {
+      float4 e[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int c = cb + 64 * u;
+        e[u] = c < p.NC ? rr[c] : make_float4(kNegInfL, 0.0f, 0.0f, 0.0f);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float x = e[u].x;
+        if (x != x) {
+          lbad = 1;
+        } else if (x > lm) {
+          ls = greedy ? 0.0f : ls * __builtin_amdgcn_exp2f(a * (lm - x)) + e[u].y;
+          lm = x;
+          lc = cb + 64 * u;
+        } else if (!greedy && x > kNegInfL) {
+          ls += e[u].y * __builtin_amdgcn_exp2f(a * (x - lm));
+        }
+      }
     }
     const float m = wave_max(lm);
     const int bad = wave_max_i(lbad);
-    float s = 0.0f, zd = 0.0f;
-    int am = -1, xw = -1;
+    float s = 0.0f;
+    int am = -1;
     if (greedy) {
-      int lc = kIntMax;
-      for (int c = lane; c < p.NT; c += 64)
-        if (rr[c].x == m) lc = min(lc, c);
-      lc = wave_min_i(lc);
-      if (lc < p.NT) am = __float_as_int(rr[lc].w);
+      lc = wave_min_i(lm == m ? lc : kIntMax);
+      if (lc < p.NC) am = __float_as_int(rr[lc].z);
     } else {
-      const int cd = vd ? d / kLmTok : -1;
-      const float4 dr = vd ? p.drec[g] : make_float4(0.0f, kNegInfL, __int_as_float(kIntMax), 0.0f);
-      float ls = 0.0f;
-      ArgMax bi{kNegInfL, kIntMax}, bx{kNegInfL, kIntMax};
-      for (int c = lane; c < p.NT; c += 64) {
-        const float4 e = rr[c];
-        const float sh_ = a * (e.x - m);
-        ls += e.y * __builtin_amdgcn_exp2f(sh_);
-        const ArgMax ci{e.z + sh_, __float_as_int(e.w)};
-        if (better(ci, bi)) bi = ci;
-        const ArgMax cx = c == cd ? ArgMax{dr.y + sh_, __float_as_int(dr.z)} : ci;
-        if (better(cx, bx)) bx = cx;
-      }
-      s = wave_sum(ls);
-      bi = wave_argmax(bi);
-      bx = wave_argmax(bx);
-      // Without d_j nothing may be left (a one-token vocabulary): race over p_j.
-      xw = (vd && bx.i < p.V) ? bx.i : bi.i;
-      if (vd) zd = dr.x;
+      s = wave_sum(lm > kNegInfL ? ls * __builtin_amdgcn_exp2f(a * (lm - m)) : 0.0f);
     }
     if (lane == 0) {
+      const float4 dr = vd && !greedy ? p.drec[g] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
       sh.m[i] = m;
       sh.s[i] = s;
-      sh.zd[i] = zd;
+      sh.zd[i] = dr.x;
+      sh.sxd[i] = dr.y;
       sh.amax[i] = am;
-      sh.xw[i] = xw;
       sh.d[i] = d;
       sh.bad[i] = bad;
     }
@@ -516,12 +433,109 @@ __global__ __launch_bounds__(kThreads) void lm_request_kernel(LmParams p) {
   for (int t = tid; t < p.out_stride; t += kThreads) {
     int v = -1;
     if (t < j) v = sh.d[t];
-    if (t == j) v = greedy ? sh.amax[j] : sh.xw[j];
-    p.out_tokens[(int64_t)r * p.out_stride + t] = v;
+    if (t == j && greedy) v = sh.amax[j];
+    if (t != j || greedy) p.out_tokens[(int64_t)r * p.out_stride + t] = v;
   }
   if (tid == 0) {
     p.out_ns[r] = j + 1;
     p.out_nr[r] = K - j;
+  }
+  if (greedy) return;
+
+  // Sampled row j: chunk race over the chunk masses (the draft token's chunk
+  // with its mass without d when j is a rejected draft), then the token race
+  // inside the winner on its recomputed logits.
+  const int gs = g0 + j;
+  const int dj = j < K ? sh.d[j] : -1;
+  const int cd = (dj >= 0 && dj < p.V) ? dj / kLmChunk : -1;
+  const float m = sh.m[j];
+  const float4 *rr = p.rec + (int64_t)gs * p.NC;
+  ArgMax best{-1.0f, kIntMax}, bestf{-1.0f, kIntMax};  // without d_j / over p_j
+  for (int c4 = 4 * tid; c4 < p.NC; c4 += 4 * kThreads) {  // one Philox block per 4 chunks
+    const uint4 w4 = philox10(make_uint4((uint32_t)c4 >> 2, (uint32_t)gs, kTagChunk, p.offset), p.seed_lo, p.seed_hi);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int c = c4 + k;
+      if (c < p.NC) {
+        const float4 e = rr[c];
+        const float sc = __builtin_amdgcn_exp2f(a * (e.x - m));
+        const float rn = __builtin_amdgcn_rcpf(exp_noise(pick(w4, k)));
+        const float wf = e.y * sc, wx = c == cd ? sh.sxd[j] * sc : wf;
+        if (wf > 0.0f && better(ArgMax{wf * rn, c}, bestf)) bestf = ArgMax{wf * rn, c};
+        if (wx > 0.0f && better(ArgMax{wx * rn, c}, best)) best = ArgMax{wx * rn, c};
+      }
+    }
+  }
+  best = block_argmax(best, sh.red);
+  bestf = block_argmax(bestf, sh.red);
+  const bool excl = cd >= 0 && best.s >= 0.0f;  // without d nothing left (rounding): race over p_j
+  const ArgMax win = excl ? best : bestf;
+  if (win.s < 0.0f) {
+    if (tid == 0) p.out_tokens[(int64_t)r * p.out_stride + j] = -1;
+    return;
+  }
+  const int cs = win.i;
+
+  // Logits of chunk cs of row gs: wave w takes tokens 16 w .. 16 w + 15 of the
+  // chunk, eight at a time; lane l reads the 16-byte pieces l, l + 64, ... of
+  // the W rows and of h (whole-wave 1 KB reads, 4 pieces of each row in flight),
+  // fp32 FMAs, then a wave sum per token.
+  {
+    constexpr int kTB = 8;  // tokens per block
+    const uint4 *hrow = reinterpret_cast<const uint4 *>(p.H + (int64_t)gs * p.hstride);
+    const int n8 = p.d / 8;
+    for (int tb = 0; tb < kLmChunk / kWaves; tb += kTB) {
+      const int tk0 = (kLmChunk / kWaves) * wave + tb;
+      const uint4 *wr[kTB];
+#pragma unroll
+      for (int t = 0; t < kTB; ++t)
+        wr[t] = reinterpret_cast<const uint4 *>(p.W + (int64_t)min(cs * kLmChunk + tk0 + t, p.V - 1) * p.wstride);
+      float acc[kTB];
+#pragma unroll
+      for (int t = 0; t < kTB; ++t) acc[t] = 0.0f;
+      for (int kb8 = lane; kb8 < n8; kb8 += 64 * 4) {
+        uint4 hv[4], wv[kTB][4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int k8 = min(kb8 + 64 * u, n8 - 1);
+          hv[u] = hrow[k8];
+#pragma unroll
+          for (int t = 0; t < kTB; ++t) wv[t][u] = wr[t][k8];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (kb8 + 64 * u >= n8) break;
+          const uint32_t hh[4] = {hv[u].x, hv[u].y, hv[u].z, hv[u].w};
+#pragma unroll
+          for (int t = 0; t < kTB; ++t) {
+            const uint32_t ww[4] = {wv[t][u].x, wv[t][u].y, wv[t][u].z, wv[t][u].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              acc[t] = __builtin_fmaf(__uint_as_float(ww[e] << 16), __uint_as_float(hh[e] << 16), acc[t]);
+              acc[t] = __builtin_fmaf(__uint_as_float(ww[e] & 0xFFFF0000u), __uint_as_float(hh[e] & 0xFFFF0000u),
+                                      acc[t]);
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < kTB; ++t) {
+        const float z = wave_sum(acc[t]);
+        if (lane == 0) sh.z[tk0 + t] = z;
+      }
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const int x = cs * kLmChunk + lane;
+    const bool ok = x < p.V && !(excl && x == dj);
+    const float zc = ok ? sh.z[lane] : kNegInfL;
+    const float hi = wave_max(zc);
+    const float w = ok ? __builtin_amdgcn_exp2f(a * (zc - hi)) : 0.0f;
+    ArgMax o{-1.0f, kIntMax};
+    if (w > 0.0f) o = ArgMax{w * inv_noise(p, (uint32_t)x, (uint32_t)gs, kTagToken), x};
+    o = wave_argmax(o);
+    if (lane == 0) p.out_tokens[(int64_t)r * p.out_stride + j] = o.s < 0.0f ? -1 : o.i;
   }
 }
 
@@ -531,8 +545,8 @@ hipError_t launch_lm_head(const LmParams &p, hipStream_t s, const hipEvent_t *ev
   LmParams arg = p;
   void *args[] = {&arg};
   const dim3 grid((unsigned)(p.NT * p.RB));
-  hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void *>(&lm_gemm_kernel), grid, dim3(kThreads), args, 0, s,
-                                    ev ? ev[0] : nullptr, ev ? ev[1] : nullptr, 0);
+  hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void *>(&lm_gemm_kernel), grid, dim3(kLmThreads), args, 0,
+                                    s, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr, 0);
   if (e != hipSuccess) return e;
   return hipExtLaunchKernel(reinterpret_cast<const void *>(&lm_request_kernel), dim3((unsigned)p.B), dim3(kThreads),
                             args, 0, s, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr, 0);

@@ -81,16 +81,16 @@ def one_hot_case(seed, B=6, V=40, d=16, kmax=3, greedy_every=3):
 
 def test_one_hot_head_matches_logit_path():
     for seed in range(5):
-        H, W, Z, cu, draft, T = one_hot_case(seed)
-        V = W.shape[0]
+        H, W, Z, cu, draft, T = one_hot_case(seed, V=200)
         for off in range(4):
-            a = oracle.lm_head_verify(H, W, cu, draft, T, seed=7, offset=off)
-            b = oracle.verify_batch(Z, cu, draft, T, seed=7, offset=off, C=V)
-            assert a["err"] == 0 and b["err"] == 0
-            np.testing.assert_array_equal(a["tokens"], b["tokens"])
-            np.testing.assert_array_equal(a["num_sampled"], b["num_sampled"])
-            np.testing.assert_array_equal(a["num_rejected"], b["num_rejected"])
-            np.testing.assert_array_equal(a["p_draft"], b["p_draft"])
+            for C in (oracle.LM_HEAD_CHUNK, 200):
+                a = oracle.lm_head_verify(H, W, cu, draft, T, seed=7, offset=off, C=C)
+                b = oracle.verify_batch(Z, cu, draft, T, seed=7, offset=off, C=C)
+                assert a["err"] == 0 and b["err"] == 0
+                np.testing.assert_array_equal(a["tokens"], b["tokens"])
+                np.testing.assert_array_equal(a["num_sampled"], b["num_sampled"])
+                np.testing.assert_array_equal(a["num_rejected"], b["num_rejected"])
+                np.testing.assert_array_equal(a["p_draft"], b["p_draft"])
 
 
 def test_bonus_token_law():
@@ -105,7 +105,7 @@ def test_bonus_token_law():
     cu = np.array([0, 0], np.int32)
     for off in range(N):
         out = oracle.lm_head_verify(H, W, cu, np.zeros(0, np.int32), np.array([T], np.float32), seed=3,
-                                    offset=off)
+                                    offset=off, C=4)
         counts[out["tokens"][0, 0]] += 1
     keep = p * N >= 5
     obs = np.append(counts[keep], counts[~keep].sum())
@@ -126,7 +126,7 @@ def test_rejected_draft_never_recovered_and_accept_rate():
     rec = np.zeros(V, np.int64)
     for off in range(N):
         out = oracle.lm_head_verify(H, W, cu, np.array([dtok], np.int32), np.array([T], np.float32), seed=1,
-                                    offset=off)
+                                    offset=off, C=4)
         if out["num_rejected"][0] == 0:
             acc += 1
             assert out["tokens"][0, 0] == dtok
