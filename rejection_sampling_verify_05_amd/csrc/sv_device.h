@@ -159,31 +159,6 @@ __device__ __forceinline__ ArgMax wave_argmax(ArgMax a) {
   return ArgMax{rd(a.s, 63), __builtin_amdgcn_readlane(a.i, 63)};
 }
 
-// ---------------------------------------------------------------------------
-// Publication between workgroups of one launch.  Entries are written with
-// agent-scope stores (written through to the device-coherent level, not held
-// in one XCD's L2), the writer waits for its stores to be acknowledged, and
-// only then bumps an agent-scope counter; the reader observes the counter and
-// then reads the entries with agent-scope loads.  No L2 write-back or
-// invalidate of unrelated lines is needed.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ void publish_f2(float2 *addr, float2 v) {
-  __hip_atomic_store(reinterpret_cast<unsigned long long *>(addr), __builtin_bit_cast(unsigned long long, v),
-                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float2 fetch_f2(const float2 *addr) {
-  return __builtin_bit_cast(float2, __hip_atomic_load(reinterpret_cast<const unsigned long long *>(addr),
-                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-}
-__device__ __forceinline__ void publish_f(float *addr, float v) {
-  __hip_atomic_store(addr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float fetch_f(const float *addr) {
-  return __hip_atomic_load(addr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// Wait until every memory operation this wave issued has completed.
-__device__ __forceinline__ void wait_memory() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
 // Block-wide (256 threads) reductions; every thread gets the result.
 struct BlockScratch {
   float s[kWaves];

@@ -170,6 +170,29 @@ def test_lm_head_parity(name):
         sv.spec_verify_destroy(ctx)
 
 
+def test_lm_head_strided_rows():
+    # hidden states and W as row slices of wider buffers (row strides > d), d = 96
+    inp = wl.make_lm_head_inputs(B=10, K=3, V=900, d=96, greedy_every=3, device=DEV)
+    ctx = lm_ctx(inp)
+    try:
+        Hw = torch.zeros((inp["R"], 96 + 40), dtype=torch.bfloat16, device=DEV)
+        Ww = torch.zeros((inp["V"], 96 + 8), dtype=torch.bfloat16, device=DEV)
+        Hw[:, 8:104] = inp["hidden"]
+        Ww[:, :96] = inp["W"]
+        strided = dict(inp, hidden=Hw[:, 8:104], W=Ww[:, :96])
+        assert strided["hidden"].stride(0) == 136 and strided["W"].stride(0) == 104
+        h = host(inp)
+        for seed, off in [(3, 0), (4, 5)]:
+            g = lm_run(ctx, strided, seed=seed, offset=off, dbg_logits=True)
+            ref = lm_run(ctx, inp, seed=seed, offset=off)
+            assert g["err"] == 0
+            np.testing.assert_array_equal(g["tokens"], ref["tokens"])
+            ex, bad = check(inp, h, g, seed, off, range(inp["B"]))
+            assert not bad and ex <= 1, "\n".join(bad[:10])
+    finally:
+        sv.spec_verify_destroy(ctx)
+
+
 def test_lm_head_invalid_requests():
     inp = wl.make_lm_head_inputs(B=8, K=2, V=700, d=64, device=DEV)
     ctx = lm_ctx(inp)
