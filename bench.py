@@ -1,7 +1,9 @@
 #!/usr/bin/env python3
 """Benchmark of the speculative-decoding verify step on one MI355X.
 
-One step = spec_verify_run + spec_post_update over one batch of the headline
+One step = spec_verify_run with post_update applied inside the call (or,
+with --separate-post-update, spec_verify_run then spec_post_update) over one
+batch of the headline
 workload (B=256 requests, K_r uniform in {0..3}, V=128256, bf16 target logits
 N(0, 3^2), no draft probabilities).  Inputs are resident in HBM before the
 timed region; the step rotates over several distinct input copies (more than
@@ -17,6 +19,7 @@ bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -89,6 +92,8 @@ def parse():
     ap.add_argument("--copies", type=int, default=0, help="input copies to rotate (0: >= 1 GB)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--separate-post-update", action="store_true",
+                    help="run post_update as its own call after spec_verify_run instead of inside it")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="before warmup, run torch's copy kernel on 256 MiB three times (a known-size "
                          "reference for the FETCH_SIZE / WRITE_SIZE counters)")
@@ -163,6 +168,9 @@ def main():
                 draft_temperature=c["draft_temp"])
         o["pargs"] = sv.make_post_update_args(c["idx_mapping"], c["query_len"], o["tokens"], o["ns"],
                                               o["nr"], last, counts, ncomp)
+        if not args.separate_post_update:  # the bookkeeping inside the verify call
+            o["vargs"].post_update = ctypes.addressof(o["pargs"])
+            o["vargs"]._post_update = o["pargs"]
         outs.append(o)
 
     def step(i):
@@ -172,7 +180,8 @@ def main():
             sv.spec_draft_sample(ctx, da, stream=stream)
         o["vargs"].offset = i
         sv.spec_verify_run(ctx, o["vargs"], stream=stream)
-        sv.spec_post_update(ctx, o["pargs"], stream=stream)
+        if args.separate_post_update:
+            sv.spec_post_update(ctx, o["pargs"], stream=stream)
 
     if args.copy_calibration:
         copy_calibration()
@@ -216,7 +225,8 @@ def main():
         ev[k][0].record(stream)
         sv.spec_verify_run(ctx, o["vargs"], stream=stream)
         ev[k][1].record(stream)
-        sv.spec_post_update(ctx, o["pargs"], stream=stream)
+        if args.separate_post_update:
+            sv.spec_post_update(ctx, o["pargs"], stream=stream)
     torch.cuda.synchronize()
     verify_ms = np.array([a.elapsed_time(b) for a, b in ev])
     stream_ms, epi_ms = sv.spec_verify_profile_read(ctx, args.steps)
@@ -281,6 +291,7 @@ def main():
                                f"V={w.V}, {'bf16' if w.dtype == torch.bfloat16 else 'fp32'} logits, "
                                f"{'draft probs' if w.draft_probs else ('draft logits, drafts sampled in the step' if w.draft_logits else 'draft ids only')}",
                    "global_batch": w.B, "rows_per_step": round(rows_per, 1), "input_copies": ncopies,
+                   "post_update": "separate call" if args.separate_post_update else "inside the verify call",
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,

@@ -81,6 +81,7 @@ extern "C" {
 #define SV_LM_HEAD_CHUNK 64       /* tokens per race chunk of spec_verify_lm_head          */
 
 typedef struct sv_ctx sv_ctx; /* opaque; owns the device scratch */
+struct sv_post_update_args;   /* defined with spec_post_update below */
 
 /* Return codes. */
 enum {
@@ -167,6 +168,13 @@ typedef struct sv_verify_args {
                                     /* greedy drafts (then as draft ids only)               */
   int64_t draft_logits_stride;      /* elements between draft-logit rows, >= vocab_size     */
   int32_t draft_logits_dtype;       /* SV_F32 or SV_BF16                                    */
+  /* HOST pointer or NULL: apply post_update (see spec_post_update) for this    */
+  /* step inside the call, from its own outputs, as soon as each request's      */
+  /* tokens are final; its idx_mapping, query_len, last_sampled,                */
+  /* output_bin_counts, num_computed_tokens and num_slots are used (num_reqs    */
+  /* and vocab_size must match; tokens, num_sampled, num_rejected and           */
+  /* tokens_stride are ignored).  Not with dbg_probs.                           */
+  const struct sv_post_update_args *post_update;
 } sv_verify_args;
 
 /*
@@ -177,12 +185,15 @@ typedef struct sv_verify_args {
  * four more passes find the nucleus threshold, and one more recomputes their
  * statistics under it.  A penalty array other than NULL needs idx_mapping,
  * output_bin_counts and num_slots >= 1.  Errors: SV_EINVAL (also synthetic
- * rates outside [0, 1], not finite or increasing), SV_ECAPACITY, SV_EDTYPE,
- * SV_EHIP (nothing enqueued on the first three).
+ * rates outside [0, 1], not finite or increasing; post_update with dbg_probs
+ * or with mismatched sizes), SV_ECAPACITY, SV_EDTYPE, SV_EHIP (nothing
+ * enqueued on the first three).  With post_update the bookkeeping of the step
+ * is done by the call's last kernels (one launch fewer than calling
+ * spec_post_update afterwards; the same results).
  */
 int spec_verify_run(sv_ctx *ctx, const sv_verify_args *args, hipStream_t stream);
 
-typedef struct sv_post_update_args {
+struct sv_post_update_args {
   const int32_t *idx_mapping;   /* [num_reqs] batch row -> state slot                     */
   const int32_t *query_len;     /* [num_reqs] tokens scheduled for the request this step  */
   const int32_t *tokens;        /* [num_reqs, tokens_stride] out_tokens of the verify step */
@@ -195,7 +206,8 @@ typedef struct sv_post_update_args {
   int32_t tokens_stride;
   int32_t vocab_size;
   int32_t num_slots;
-} sv_post_update_args;
+};
+typedef struct sv_post_update_args sv_post_update_args;
 
 /*
  * post_update ("【vllm】DeepSeekMTP、eagle", postprocess / _post_update_kernel):

@@ -89,6 +89,7 @@ class VerifyArgs(ctypes.Structure):
         ("draft_temperature", ctypes.c_void_p),
         ("draft_logits_stride", ctypes.c_int64),
         ("draft_logits_dtype", ctypes.c_int32),
+        ("post_update", ctypes.c_void_p),
     ]
 
 
@@ -248,8 +249,9 @@ def make_verify_args(target_logits, draft_ids, cu_num_draft, temperature, out_to
                      rep_penalty=None, idx_mapping=None, output_bin_counts=None, seed=0,
                      offset=0, dbg_p_draft=None, dbg_probs=None, frequency_penalty=None,
                      presence_penalty=None, top_p=None, synthetic_rates=None, draft_logits=None,
-                     draft_stats=None, draft_temperature=None) -> VerifyArgs:
-    """Fill an sv_verify_args from torch tensors (no copies, no compute)."""
+                     draft_stats=None, draft_temperature=None, post_update=None) -> VerifyArgs:
+    """Fill an sv_verify_args from torch tensors (no copies, no compute).
+    post_update: a PostUpdateArgs (make_post_update_args) applied inside the call."""
     import torch
     if target_logits.dim() != 2 or not target_logits.is_cuda or target_logits.stride(1) != 1:
         raise ValueError("target_logits must be a 2-D CUDA tensor with unit column stride")
@@ -327,6 +329,11 @@ def make_verify_args(target_logits, draft_ids, cu_num_draft, temperature, out_to
         buf = (ctypes.c_float * max(len(vals), 1))(*vals)
         a._synthetic_buf = buf
         a.synthetic_rates = ctypes.cast(buf, ctypes.c_void_p).value
+    if post_update is not None:
+        if not isinstance(post_update, PostUpdateArgs):
+            raise TypeError("post_update must be a PostUpdateArgs")
+        a._post_update = post_update  # keeps the host struct alive with the args
+        a.post_update = ctypes.addressof(post_update)
     return a
 
 

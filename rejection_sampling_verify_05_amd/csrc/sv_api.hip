@@ -184,6 +184,18 @@ extern "C" int spec_verify_run(sv_ctx *ctx, const sv_verify_args *a, hipStream_t
   p.out_nr = a->out_num_rejected;
   p.dbg_p_draft = a->dbg_p_draft;
   p.dbg_probs = a->dbg_probs;
+  if (a->post_update) {  // post_update inside the call
+    const sv_post_update_args *u = a->post_update;
+    if (a->dbg_probs || u->num_reqs != a->num_reqs || u->vocab_size != a->vocab_size || u->num_slots < 1 ||
+        !u->idx_mapping || !u->query_len || !u->last_sampled || !u->output_bin_counts || !u->num_computed_tokens)
+      return SV_EINVAL;
+    p.pu_idx_mapping = u->idx_mapping;
+    p.pu_query_len = u->query_len;
+    p.pu_last_sampled = u->last_sampled;
+    p.pu_counts = u->output_bin_counts;
+    p.pu_num_computed = u->num_computed_tokens;
+    p.pu_num_slots = u->num_slots;
+  }
   p.chunk_tab = ctx->chunk_tab;
   p.row_info = ctx->row_info;
   p.res_req = ctx->res_req;

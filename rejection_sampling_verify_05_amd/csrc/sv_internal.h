@@ -90,6 +90,10 @@ struct Params {
   int32_t pass2;      // stats pass over the rows the top-p pass left to it (kRowTopPRedo) only
   uint32_t seed_lo, seed_hi, offset;
   uint32_t epoch;
+  // post_update applied inside the call (pu_idx_mapping null: not requested)
+  const int32_t *pu_idx_mapping, *pu_query_len;
+  int32_t *pu_last_sampled, *pu_counts, *pu_num_computed;
+  int32_t pu_num_slots;
   int32_t synthetic;  // synthetic acceptance with the rates below
   float syn[kMaxDrafts]; // unconditional acceptance rates of draft positions 1..
 };

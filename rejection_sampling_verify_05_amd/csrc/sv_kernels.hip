@@ -330,6 +330,27 @@ __device__ __forceinline__ int compact_race(const Params &p, uint32_t g, int n, 
   return b.s < 0.0f ? -1 : b.i;
 }
 
+// post_update of request r inside the verify call, once its tokens are final:
+// the accepted drafts draft(0..j-1), then x (num_sampled = j + 1, num_rejected
+// = K - j); the same updates as post_update_kernel.  All threads call it.
+template <class DF>
+__device__ __forceinline__ void fused_post_update(const Params &p, int r, int K, int j, int x, DF draft) {
+  if (p.pu_idx_mapping == nullptr) return;
+  const int s = p.pu_idx_mapping[r];
+  if (s < 0 || s >= p.pu_num_slots) {
+    if (threadIdx.x == 0) atomicOr(p.err, SV_ERR_SLOT);
+    return;
+  }
+  for (int i = threadIdx.x; i <= j; i += kThreads) {
+    const int tok = i < j ? draft(i) : x;
+    if (tok >= 0 && tok < p.V) atomicAdd(&p.pu_counts[(int64_t)s * p.V + tok], 1);
+  }
+  if (threadIdx.x == 0) {
+    p.pu_last_sampled[s] = x;
+    atomicAdd(&p.pu_num_computed[s], p.pu_query_len[r] - (K - j));
+  }
+}
+
 __device__ __forceinline__ void write_empty(const Params &p, int r) {
   for (int t = threadIdx.x; t < p.out_stride; t += kThreads) p.out_tokens[(int64_t)r * p.out_stride + t] = -1;
   if (threadIdx.x == 0) {
@@ -807,8 +828,10 @@ __device__ __forceinline__ void request_epilogue(const Params &p, const Req &q, 
   }
   const int64_t out_j = (int64_t)r * p.out_stride + j;
 
+  auto accepted = [&](int i) { return sh.d[i]; };
   if (greedy) {
     if (tid == 0) p.out_tokens[out_j] = sh.amax[j];
+    fused_post_update(p, r, K, j, sh.amax[j], accepted);
     return;
   }
 
@@ -848,6 +871,7 @@ __device__ __forceinline__ void request_epilogue(const Params &p, const Req &q, 
     }
     const int x = compact_race(p, (uint32_t)gs, st, sh);
     if (tid == 0) p.out_tokens[out_j] = x;
+    fused_post_update(p, r, K, j, x, accepted);
     return;
   }
 
@@ -879,6 +903,7 @@ __device__ __forceinline__ void request_epilogue(const Params &p, const Req &q, 
   }
   const int x = spec_finish(p, q, j, dj, m, sxj, pr, entj, slot, sh);
   if (tid == 0) p.out_tokens[out_j] = x;
+  fused_post_update(p, r, K, j, x, accepted);
 }
 
 // ---------------------------------------------------------------------------
@@ -1391,6 +1416,7 @@ __global__ __launch_bounds__(kThreads) void resid_race_kernel(Params p) {
     x = bb.s < 0.0f ? -1 : bb.i;
   }
   if (threadIdx.x == 0) p.out_tokens[(int64_t)r * p.out_stride + j] = x;
+  fused_post_update(p, r, q.K, j, x, [&](int i) { return p.draft_ids[q.c0 + i]; });
 }
 
 // Request epilogue kernel: one workgroup per request, after the stats pass.

@@ -9,7 +9,7 @@ import torch
 import oracle
 import rejection_sampling_verify_05_amd as sv
 import workloads as wl
-from harness import ctx_for, run_gpu
+from harness import ctx_for, run_gpu, run_draft_steps
 
 pytestmark = pytest.mark.gpu
 
@@ -95,3 +95,67 @@ def test_post_update_edge_cases_and_repeats():
         assert g[3] == sv.SV_ERR_SLOT and o[3] != 0
         for a, b in zip(g[:3], o[:3]):
             assert np.array_equal(a, b)
+
+
+IN_CALL_CASES = {
+    "1_draft_probs": wl.CONFIGS["1"],
+    "2_greedy_mix": wl.CONFIGS["2"].with_(B=32, V=8000),
+    "3_no_draft": wl.CONFIGS["3"].with_(B=48, V=20000 + 3),
+    "4_topk_penalty": wl.CONFIGS["4"].with_(B=16, K=4, V=6000, history=64),
+    "3p_top_p": wl.CONFIGS["3"].with_(B=24, V=9000, top_p=0.8),
+    "3f_penalties": wl.CONFIGS["3"].with_(B=24, V=9000, freq=0.5, pres=0.25, history=64),
+    "3d_draft_logits": wl.CONFIGS["3"].with_(B=16, V=7000, draft_logits=True),
+}
+
+
+@pytest.mark.parametrize("name", sorted(IN_CALL_CASES))
+def test_post_update_inside_verify(name):
+    # spec_verify_run with post_update attached: the same tokens as without it,
+    # and the same state as spec_post_update applied afterwards (and as the
+    # oracle's post_update), including the penalty paths that read the counts
+    # the call updates and the residual paths that finish a request later.
+    w = IN_CALL_CASES[name]
+    say(f"case {name}: {w}")
+    inp = wl.make_inputs(w, DEV)
+    with ctx_for(inp) as ctx:
+        if w.draft_logits:  # draft ids and row statistics from the draft sampler
+            run_draft_steps(ctx, inp, seed=1, offset=2)
+        dl = inp.get("draft_stats") is not None
+        B, S, V = inp["B"], inp["num_slots"], inp["V"]
+        out_stride = int(inp["K"].max().item()) + 1
+        rng = np.random.default_rng(11)
+        last0 = rng.integers(-1, V, S).astype(np.int32)
+        ncomp0 = rng.integers(0, 1000, S).astype(np.int32)
+        counts0 = inp["counts"].cpu().numpy().copy()
+        penalty = any(inp.get(k) is not None for k in ("rep_penalty", "freq", "pres"))
+        for seed, off in [(3, 5), (8, 0)]:
+            # reference: verify, then spec_post_update (separate calls)
+            g = run_gpu(ctx, inp, seed=seed, offset=off)
+            assert g["err"] == 0
+            ref = gpu_post_update(ctx, inp["idx_mapping"].cpu().numpy(), inp["query_len"].cpu().numpy(), g["tokens"],
+                                  g["num_sampled"], g["num_rejected"], last0, counts0, ncomp0)
+            want = oracle_post_update(inp["idx_mapping"].cpu().numpy(), inp["query_len"].cpu().numpy(), g["tokens"],
+                                      g["num_sampled"], g["num_rejected"], last0, counts0, ncomp0)
+            # in-call: the counts the call reads for penalties are the state it updates
+            counts = torch.from_numpy(counts0.copy()).to(DEV)
+            last = torch.from_numpy(last0.copy()).to(DEV)
+            ncomp = torch.from_numpy(ncomp0.copy()).to(DEV)
+            toks = torch.full((B, out_stride), -7, dtype=torch.int32, device=DEV)
+            ns = torch.full((B,), -7, dtype=torch.int32, device=DEV)
+            nr = torch.full((B,), -7, dtype=torch.int32, device=DEV)
+            pu = sv.make_post_update_args(inp["idx_mapping"], inp["query_len"], toks, ns, nr, last, counts, ncomp)
+            sv.spec_verify_run(ctx.h, inp["logits"], inp["draft_ids"], inp["cu"], inp["temperature"], toks, ns, nr,
+                               draft_probs=inp["draft_probs"], top_k=inp["top_k"], rep_penalty=inp["rep_penalty"],
+                               idx_mapping=inp["idx_mapping"], output_bin_counts=counts if penalty else None,
+                               seed=seed, offset=off, frequency_penalty=inp.get("freq"),
+                               presence_penalty=inp.get("pres"), top_p=inp.get("top_p"),
+                               draft_logits=inp["draft_logits"] if dl else None,
+                               draft_stats=inp["draft_stats"] if dl else None,
+                               draft_temperature=inp["draft_temp"] if dl else None, post_update=pu)
+            assert sv.spec_verify_read_error(ctx.h) == 0
+            assert np.array_equal(toks.cpu().numpy(), g["tokens"])
+            assert np.array_equal(ns.cpu().numpy(), g["num_sampled"])
+            assert np.array_equal(nr.cpu().numpy(), g["num_rejected"])
+            for got_t, ref_t, want_t in zip((last, counts, ncomp), ref[:3], want[:3]):
+                assert np.array_equal(got_t.cpu().numpy(), ref_t)
+                assert np.array_equal(got_t.cpu().numpy(), want_t)
