@@ -314,7 +314,8 @@ def pct(a):
 
 def bench_lm_head(args):
     """One step = spec_verify_lm_head (the LM-head GEMM with the verify
-    statistics in its epilogue, then the per-request decisions) + post_update,
+    statistics in its epilogue, then the per-request decisions) with post_update
+    inside the call (or as its own call with --separate-post-update),
     on config 3's request mix with hidden size 4096.  The LM-head weight (1.05 GB)
     is one resident tensor, as in serving; the hidden states rotate over copies.
     Also times, as context, the same step with the logits materialised: torch's
@@ -348,13 +349,17 @@ def bench_lm_head(args):
                                           o["ns"], o["nr"], seed=1234, offset=0)
         o["pargs"] = sv.make_post_update_args(idx_mapping, (c["K"] + 1).to(torch.int32), o["tokens"], o["ns"],
                                               o["nr"], last, counts, ncomp)
+        if not args.separate_post_update:  # the bookkeeping inside the call
+            o["largs"].post_update = ctypes.addressof(o["pargs"])
+            o["largs"]._post_update = o["pargs"]
         outs.append(o)
 
     def step(i):
         o = outs[i % ncopies]
         o["largs"].offset = i
         sv.spec_verify_lm_head(ctx, o["largs"], stream=stream)
-        sv.spec_post_update(ctx, o["pargs"], stream=stream)
+        if args.separate_post_update:
+            sv.spec_post_update(ctx, o["pargs"], stream=stream)
 
     if args.copy_calibration:
         copy_calibration()

@@ -318,6 +318,8 @@ typedef struct sv_lm_head_args {
   int32_t num_reqs;             /* B                                                        */
   int32_t vocab_size;           /* V <= max_vocab                                           */
   int32_t out_stride;           /* row length of out_tokens, <= max_k + 1                   */
+  const struct sv_post_update_args *post_update; /* HOST pointer or NULL: post_update of   */
+                                /* this step inside the call, as in sv_verify_args          */
 } sv_lm_head_args;
 
 int spec_verify_lm_head(sv_ctx *ctx, const sv_lm_head_args *args, hipStream_t stream);

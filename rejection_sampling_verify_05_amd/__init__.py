@@ -135,6 +135,7 @@ class LmHeadArgs(ctypes.Structure):
         ("num_reqs", ctypes.c_int32),
         ("vocab_size", ctypes.c_int32),
         ("out_stride", ctypes.c_int32),
+        ("post_update", ctypes.c_void_p),
     ]
 
 
@@ -433,7 +434,7 @@ def spec_draft_sample(ctx, *args, stream=None, **kwargs) -> None:
 
 def make_lm_head_args(hidden, lm_head, draft_ids, cu_num_draft, temperature, out_tokens,
                       out_num_sampled, out_num_rejected, *, seed=0, offset=0, dbg_p_draft=None,
-                      dbg_logits=None) -> LmHeadArgs:
+                      dbg_logits=None, post_update=None) -> LmHeadArgs:
     """Fill an sv_lm_head_args from torch tensors (no copies, no compute).
     hidden [R, d] and lm_head [V, d] are bfloat16 with unit column stride."""
     import torch
@@ -470,6 +471,11 @@ def make_lm_head_args(hidden, lm_head, draft_ids, cu_num_draft, temperature, out
     a.num_reqs = cu_num_draft.shape[0] - 1
     a.vocab_size = lm_head.shape[0]
     a.out_stride = out_tokens.shape[1]
+    if post_update is not None:
+        if not isinstance(post_update, PostUpdateArgs):
+            raise TypeError("post_update must be a PostUpdateArgs")
+        a._post_update = post_update
+        a.post_update = ctypes.addressof(post_update)
     return a
 
 

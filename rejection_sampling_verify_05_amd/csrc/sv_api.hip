@@ -476,6 +476,18 @@ extern "C" int spec_verify_lm_head(sv_ctx *ctx, const sv_lm_head_args *a, hipStr
   p.seed_lo = (uint32_t)(a->seed & 0xFFFFFFFFu);
   p.seed_hi = (uint32_t)(a->seed >> 32);
   p.offset = (uint32_t)a->offset;
+  if (a->post_update) {  // post_update inside the call
+    const sv_post_update_args *u = a->post_update;
+    if (u->num_reqs != a->num_reqs || u->vocab_size != a->vocab_size || u->num_slots < 1 || !u->idx_mapping ||
+        !u->query_len || !u->last_sampled || !u->output_bin_counts || !u->num_computed_tokens)
+      return SV_EINVAL;
+    p.pu_idx_mapping = u->idx_mapping;
+    p.pu_query_len = u->query_len;
+    p.pu_last_sampled = u->last_sampled;
+    p.pu_counts = u->output_bin_counts;
+    p.pu_num_computed = u->num_computed_tokens;
+    p.pu_num_slots = u->num_slots;
+  }
   hipEvent_t *ev = (ctx->ev && ctx->ev_n < ctx->ev_cap) ? ctx->ev + 4 * ctx->ev_n++ : nullptr;
   return sv::launch_lm_head(p, stream, ev) == hipSuccess ? SV_OK : SV_EHIP;
 }

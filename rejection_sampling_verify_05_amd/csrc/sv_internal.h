@@ -138,6 +138,10 @@ struct LmParams {
   int32_t RB;                 // row blocks ceil(R / kLmRows)
   int32_t out_stride;
   uint32_t seed_lo, seed_hi, offset;
+  // post_update applied inside the call (pu_idx_mapping null: not requested)
+  const int32_t *pu_idx_mapping, *pu_query_len;
+  int32_t *pu_last_sampled, *pu_counts, *pu_num_computed;
+  int32_t pu_num_slots;
 };
 
 // ev: null, or four events stamped around the GEMM and the request kernel.

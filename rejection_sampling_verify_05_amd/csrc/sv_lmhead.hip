@@ -305,7 +305,7 @@ __global__ __launch_bounds__(kLmThreads) __attribute__((amdgpu_waves_per_eu(2, 2
 struct LmReqShared {
   float m[kMaxDrafts + 1], s[kMaxDrafts + 1], zd[kMaxDrafts + 1], sxd[kMaxDrafts + 1];
   int amax[kMaxDrafts + 1], d[kMaxDrafts + 1], bad[kMaxDrafts + 1];
-  int j;
+  int j, xw;          // first reject; the sampled token
   float z[kLmChunk];  // recomputed logits of the winning chunk
   BlockScratch red;
 };
@@ -315,6 +315,25 @@ __device__ __forceinline__ void lm_write_empty(const LmParams &p, int r) {
   if (threadIdx.x == 0) {
     p.out_ns[r] = 0;
     p.out_nr[r] = 0;
+  }
+}
+
+// post_update of request r once its tokens are final (the accepted drafts
+// sh.d[0..j-1], then x): the updates of spec_post_update.  All threads call it.
+__device__ __forceinline__ void lm_post_update(const LmParams &p, const LmReqShared &sh, int r, int K, int j, int x) {
+  if (p.pu_idx_mapping == nullptr) return;
+  const int s = p.pu_idx_mapping[r];
+  if (s < 0 || s >= p.pu_num_slots) {
+    if (threadIdx.x == 0) atomicOr(p.err, SV_ERR_SLOT);
+    return;
+  }
+  for (int i = threadIdx.x; i <= j; i += kThreads) {
+    const int tok = i < j ? sh.d[i] : x;
+    if (tok >= 0 && tok < p.V) atomicAdd(&p.pu_counts[(int64_t)s * p.V + tok], 1);
+  }
+  if (threadIdx.x == 0) {
+    p.pu_last_sampled[s] = x;
+    atomicAdd(&p.pu_num_computed[s], p.pu_query_len[r] - (K - j));
   }
 }
 
@@ -440,7 +459,10 @@ __global__ __launch_bounds__(kThreads) void lm_request_kernel(LmParams p) {
     p.out_ns[r] = j + 1;
     p.out_nr[r] = K - j;
   }
-  if (greedy) return;
+  if (greedy) {
+    lm_post_update(p, sh, r, K, j, sh.amax[j]);
+    return;
+  }
 
   // Sampled row j: chunk race over the chunk masses (the draft token's chunk
   // with its mass without d when j is a rejected draft), then the token race
@@ -472,6 +494,7 @@ __global__ __launch_bounds__(kThreads) void lm_request_kernel(LmParams p) {
   const ArgMax win = excl ? best : bestf;
   if (win.s < 0.0f) {
     if (tid == 0) p.out_tokens[(int64_t)r * p.out_stride + j] = -1;
+    lm_post_update(p, sh, r, K, j, -1);
     return;
   }
   const int cs = win.i;
@@ -535,8 +558,14 @@ __global__ __launch_bounds__(kThreads) void lm_request_kernel(LmParams p) {
     ArgMax o{-1.0f, kIntMax};
     if (w > 0.0f) o = ArgMax{w * inv_noise(p, (uint32_t)x, (uint32_t)gs, kTagToken), x};
     o = wave_argmax(o);
-    if (lane == 0) p.out_tokens[(int64_t)r * p.out_stride + j] = o.s < 0.0f ? -1 : o.i;
+    if (lane == 0) {
+      const int x = o.s < 0.0f ? -1 : o.i;
+      p.out_tokens[(int64_t)r * p.out_stride + j] = x;
+      sh.xw = x;
+    }
   }
+  __syncthreads();
+  lm_post_update(p, sh, r, K, j, sh.xw);
 }
 
 }  // namespace

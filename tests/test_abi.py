@@ -66,6 +66,7 @@ int main(void) {
   F(sv_lm_head_args, hidden) F(sv_lm_head_args, dbg_logits) F(sv_lm_head_args, hidden_row_stride)
   F(sv_lm_head_args, lm_head_row_stride) F(sv_lm_head_args, seed) F(sv_lm_head_args, offset)
   F(sv_lm_head_args, hidden_size) F(sv_lm_head_args, vocab_size) F(sv_lm_head_args, out_stride)
+  F(sv_lm_head_args, post_update)
   F(sv_post_update_args, num_computed_tokens) F(sv_post_update_args, num_reqs)
   F(sv_post_update_args, num_slots)
   return 0;

@@ -247,3 +247,39 @@ def test_lm_head_full_size_sampled(greedy_every):
         assert ex <= 1
     finally:
         sv.spec_verify_destroy(ctx)
+
+
+def test_lm_head_post_update_inside_call():
+    # post_update attached to spec_verify_lm_head: the same tokens, and the same
+    # state as spec_post_update applied afterwards and as the oracle's post_update.
+    inp = wl.make_lm_head_inputs(B=20, K=3, V=1500, d=64, greedy_every=4, device=DEV)
+    B, V = inp["B"], inp["V"]
+    S = B + 5
+    rng = np.random.default_rng(3)
+    idx = torch.from_numpy(rng.permutation(S)[:B].astype(np.int32)).to(DEV)
+    ql = (inp["K"] + 1).to(torch.int32)
+    last0 = rng.integers(-1, V, S).astype(np.int32)
+    ncomp0 = rng.integers(0, 100, S).astype(np.int32)
+    counts0 = rng.integers(0, 3, (S, V)).astype(np.int32)
+    ctx = lm_ctx(inp)
+    try:
+        g = lm_run(ctx, inp, seed=9, offset=4)
+        assert g["err"] == 0
+        want = [last0.copy(), counts0.copy(), ncomp0.copy()]
+        assert oracle.post_update(idx.cpu().numpy(), ql.cpu().numpy(), g["tokens"], g["num_sampled"],
+                                  g["num_rejected"], *want) == 0
+        st = [torch.from_numpy(x.copy()).to(DEV) for x in (last0, counts0, ncomp0)]
+        S_ = int(inp["K"].max().item()) + 1
+        out = torch.full((B, S_), -7, dtype=torch.int32, device=DEV)
+        ns = torch.full((B,), -7, dtype=torch.int32, device=DEV)
+        nr = torch.full((B,), -7, dtype=torch.int32, device=DEV)
+        pu = sv.make_post_update_args(idx, ql, out, ns, nr, st[0], st[1], st[2])
+        sv.spec_verify_lm_head(ctx, inp["hidden"], inp["W"], inp["draft_ids"], inp["cu"], inp["temperature"],
+                               out, ns, nr, seed=9, offset=4, post_update=pu)
+        assert sv.spec_verify_read_error(ctx) == 0
+        assert np.array_equal(out.cpu().numpy(), g["tokens"])
+        assert np.array_equal(ns.cpu().numpy(), g["num_sampled"])
+        for got, w in zip(st, want):
+            assert np.array_equal(got.cpu().numpy(), w)
+    finally:
+        sv.spec_verify_destroy(ctx)

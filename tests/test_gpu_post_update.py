@@ -159,3 +159,19 @@ def test_post_update_inside_verify(name):
             for got_t, ref_t, want_t in zip((last, counts, ncomp), ref[:3], want[:3]):
                 assert np.array_equal(got_t.cpu().numpy(), ref_t)
                 assert np.array_equal(got_t.cpu().numpy(), want_t)
+
+
+def test_post_update_inside_verify_refuses_dbg_probs():
+    inp = wl.make_inputs(wl.CONFIGS["1"], DEV)
+    with ctx_for(inp) as ctx:
+        B, S, V = inp["B"], inp["num_slots"], inp["V"]
+        toks = torch.empty((B, 4), dtype=torch.int32, device=DEV)
+        ns = torch.empty(B, dtype=torch.int32, device=DEV)
+        nr = torch.empty(B, dtype=torch.int32, device=DEV)
+        st = [torch.zeros(S, dtype=torch.int32, device=DEV), inp["counts"].clone(),
+              torch.zeros(S, dtype=torch.int32, device=DEV)]
+        pu = sv.make_post_update_args(inp["idx_mapping"], inp["query_len"], toks, ns, nr, *st)
+        probs = torch.empty((inp["R"], V), dtype=torch.float32, device=DEV)
+        with pytest.raises(sv.SpecVerifyError):
+            sv.spec_verify_run(ctx.h, inp["logits"], inp["draft_ids"], inp["cu"], inp["temperature"], toks, ns, nr,
+                               draft_probs=inp["draft_probs"], dbg_probs=probs, post_update=pu)
