@@ -291,7 +291,7 @@ int spec_verify_synthetic_rates(float mean_length, int32_t k, float *rates);
  * one pass over W (V d bf16) per 256 target rows, shared through L2 by the
  * workgroups of one token tile, 2 R V d flops, and SV_LM_HEAD_CHUNK rows of W
  * per sampled request.
- * Errors: SV_EINVAL (NULL pointer, hidden_size not a positive multiple of 32,
+ * Errors: SV_EINVAL (NULL pointer, hidden_size not a positive multiple of 64,
  * strides below hidden_size or not multiples of 8, bases not 16-byte aligned,
  * offset >= 2^32), SV_ECAPACITY (sizes beyond the context, or no
  * SV_CREATE_LM_HEAD), SV_EHIP.  Device-side: SV_ERR_CU, SV_ERR_TEMPERATURE, and
@@ -313,7 +313,7 @@ typedef struct sv_lm_head_args {
   int64_t lm_head_row_stride;   /* elements, >= hidden_size, multiple of 8                  */
   uint64_t seed;                /* Philox key                                               */
   uint64_t offset;              /* per-call step, < 2^32                                    */
-  int32_t hidden_size;          /* d, a multiple of 32                                      */
+  int32_t hidden_size;          /* d, a multiple of 64                                      */
   int32_t num_rows;             /* R = cu[B] + B                                            */
   int32_t num_reqs;             /* B                                                        */
   int32_t vocab_size;           /* V <= max_vocab                                           */

@@ -437,7 +437,7 @@ extern "C" int spec_verify_lm_head(sv_ctx *ctx, const sv_lm_head_args *a, hipStr
   if (!a->hidden || !a->lm_head || !a->cu_num_draft || !a->temperature || !a->out_tokens || !a->out_num_sampled ||
       !a->out_num_rejected || (D > 0 && !a->draft_ids))
     return SV_EINVAL;
-  // The main loop copies 16-byte pieces: aligned bases and strides, d a multiple of 32.
+  // The main loop copies 16-byte pieces: aligned bases and strides, d a multiple of 64.
   if (a->hidden_size <= 0 || a->hidden_size % sv::kLmK != 0) return SV_EINVAL;
   if (a->hidden_row_stride < a->hidden_size || a->lm_head_row_stride < a->hidden_size) return SV_EINVAL;
   if (a->hidden_row_stride % 8 != 0 || a->lm_head_row_stride % 8 != 0) return SV_EINVAL;

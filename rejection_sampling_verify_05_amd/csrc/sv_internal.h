@@ -113,7 +113,7 @@ struct DraftOut {
 // never stored (except to dbg_logits).
 constexpr int kLmTok = 256;     // tokens per workgroup tile
 constexpr int kLmRows = 256;    // target rows per workgroup tile
-constexpr int kLmK = 32;        // hidden elements per main-loop step (d must be a multiple)
+constexpr int kLmK = 64;        // hidden elements per main-loop step (d must be a multiple)
 constexpr int kLmChunk = 64;    // tokens per race chunk (SV_LM_HEAD_CHUNK; one record per row and chunk)
 constexpr int kLmThreads = 512; // threads of the GEMM workgroup (8 waves)
 static_assert(kLmChunk == SV_LM_HEAD_CHUNK, "the ABI names the LM-head race chunk");

@@ -36,29 +36,36 @@ constexpr int kIntMax = 0x7FFFFFFF;
 // kLmTok = 256 tokens x kLmRows = 256 target rows; wave w computes the 64
 // tokens of chunk (w & 3) of the tile for rows 128 (w >> 2) .. + 128 as 2 x 4
 // MFMA 32x32x16 tiles (128 fp32 accumulators per lane).  The hidden dimension
-// advances kLmK = 32 elements per step; each step's W and hidden slices (256
-// rows x 64 bytes each) are copied to LDS by the loads themselves
-// (global_load_lds, no registers) into a ring of kStages stages, kStages - 1
-// steps ahead of the MFMAs.
-constexpr int kStages = 4;
-constexpr int kRowBytes = kLmK * 2;                    // 64 bytes of one row per step
-constexpr int kWPart = kLmTok * kRowBytes;             // W part of a stage: 16 KB
-constexpr int kHPart = kLmRows * kRowBytes;            // hidden part: 16 KB
-constexpr int kStage = kWPart + kHPart;
-constexpr int kDmaW = kWPart / (kLmThreads * 16);      // 16-byte loads per thread per stage: W (2)
-constexpr int kDmaH = kHPart / (kLmThreads * 16);      // ... and hidden (2)
+// advances kLmK = 64 elements per step, so that each row's slice of a step is
+// one whole 128-byte line: with half lines per step every line was requested
+// twice (the second half a step later, after the L1 had dropped it) and the
+// loop ran about 6 % slower.  A step's W and hidden slices (256 rows x 128
+// bytes each, the step's two parts) are copied to LDS by the loads themselves
+// (global_load_lds, no registers) into a ring of kSlots = 5 part slots: while
+// step k computes from its two parts, the three parts after them are in flight
+// (96 KB; the ring is the whole 160 KB of LDS).
+constexpr int kSlots = 5;
+constexpr int kRowBytes = kLmK * 2;                    // 128 bytes of one row per step
+constexpr int kPart = kLmTok * kRowBytes;              // one part (W or hidden) of a step: 32 KB
+constexpr int kDmaPart = kPart / (kLmThreads * 16);    // 16-byte loads per thread per part (4)
+static_assert(kLmTok == kLmRows, "W and hidden parts have the same size");
 static_assert(kLmTok == 4 * kLmChunk, "four chunks per token tile, one per wave column");
 static_assert(kLmChunk % (8 * kWaves) == 0, "the recompute takes tokens in blocks of 8 per wave");
+static_assert(kDmaPart == 4, "vmcnt immediates below assume 4 loads per part");
 
-// Rows are stored densely (64 bytes); the 16-byte chunk c of row r sits at
-// position c ^ ((r >> 2) & 3), so that the fragment reads of 16 consecutive
-// rows (one LDS cycle of 16-byte reads) hit 16 distinct bank groups.
-__device__ __forceinline__ int chunk_pos(int r, int c) { return c ^ ((r >> 2) & 3); }
+// Rows are stored densely (128 bytes); the 16-byte chunk c of row r sits at
+// position c ^ ((r >> 1) & 7), so that the fragment reads of 16 consecutive
+// rows (one LDS cycle of 16-byte reads over 64 banks) hit 16 distinct bank
+// groups: rows of one parity take 8 distinct positions, and the two parities
+// fall in the two halves of the banks.
+__device__ __forceinline__ int chunk_pos(int r, int c) { return c ^ ((r >> 1) & 7); }
 
-struct LmShared {
-  alignas(16) unsigned char ring[kStages][kStage];
-  float a[kLmRows];  // log2(e) / T of each row's request (0: greedy or invalid)
-  int d[kLmRows];    // draft token of the row (-1: bonus row or no valid draft slot)
+union LmShared {
+  alignas(16) unsigned char ring[kSlots][kPart];
+  struct {
+    float a[kLmRows];  // log2(e) / T of each row's request (0: greedy or invalid)
+    int d[kLmRows];    // draft token of the row (-1: bonus row or no valid draft slot)
+  } rq;                // written once the ring is no longer read
 };
 
 // One 16-byte load per lane from global memory straight into LDS: lane i
@@ -70,74 +77,91 @@ __device__ __forceinline__ void dma16(const void *g, uint32_t lds) {
                : "memory", "m0");
 }
 
-// Per-lane source rows of the stage copies: wave w's load i of a part fills
-// the part's bytes (2 w + i) KB .. + 1 KB, i.e. rows 16 (2 w + i) + (lane >> 2),
-// stored chunk lane & 3, which holds chunk chunk_pos(row, lane & 3) of the
-// row's 64 bytes.
+// Per-lane source rows of the part copies: wave w's load i of a part fills the
+// part's bytes (4 w + i) KB .. + 1 KB, i.e. rows 8 (4 w + i) + (lane >> 3),
+// stored chunk lane & 7, which holds chunk chunk_pos(row, lane & 7) of the
+// row's 128 bytes (the XOR is its own inverse).
 struct DmaSrc {
-  const uint16_t *w[kDmaW];  // W rows (+ chunk offset), step 0
-  const uint16_t *h[kDmaH];  // hidden rows (+ chunk offset), step 0
+  const uint16_t *w[kDmaPart];  // W rows (+ chunk offset), step 0
+  const uint16_t *h[kDmaPart];  // hidden rows (+ chunk offset), step 0
 };
 
-__device__ __forceinline__ void issue_stage(const DmaSrc &src, uint32_t stage_lds, int kb) {
+// Part 2 k + e of the copy sequence: e = 0 the W part of step k, e = 1 its hidden part.
+__device__ __forceinline__ void issue_part(const DmaSrc &src, uint32_t slot_lds, int k, int e) {
   const int wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int i = 0; i < kDmaW; ++i) dma16(src.w[i] + (int64_t)kb * kLmK, stage_lds + (kDmaW * wave + i) * 1024);
-#pragma unroll
-  for (int i = 0; i < kDmaH; ++i)
-    dma16(src.h[i] + (int64_t)kb * kLmK, stage_lds + kWPart + (kDmaH * wave + i) * 1024);
+  for (int i = 0; i < kDmaPart; ++i)
+    dma16((e == 0 ? src.w[i] : src.h[i]) + (int64_t)k * kLmK, slot_lds + (kDmaPart * wave + i) * 1024);
 }
 
-// Waits until at most `ahead` steps of this wave's stage copies are in flight.
-__device__ __forceinline__ void wait_stages(int ahead) {
-  static_assert(kDmaW + kDmaH == 4 && kStages == 4, "vmcnt immediates below assume 4 loads per step");
-  if (ahead >= 2)
-    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-  else if (ahead == 1)
+// MFMAs of one step from its W and hidden parts: MFMA k index 8 (l >> 5) + e
+// of sub-step j is hidden element 16 j + 8 (l >> 5) + e of the step, i.e.
+// chunk 2 j + (l >> 5).  Only the wave's first NTN row subtiles hold target
+// rows (the others lie past R in the last row block) and only those are read
+// and multiplied.  The fragments are read two sub-steps at a time.
+template <int NTN>
+__device__ __forceinline__ void compute_step(const unsigned char *wpart, const unsigned char *hpart,
+                                             f32x16 (&acc)[2][4]) {
+  const int lane = threadIdx.x & 63, l32 = lane & 31, half = lane >> 5, wave = threadIdx.x >> 6;
+  const int tq = wave & 3, wr = wave >> 2;
+#pragma unroll
+  for (int jj = 0; jj < 4; jj += 2) {
+    bf16x8 wf[2][2], hf[2][4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int c = 2 * (jj + j) + half;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int rw = 64 * tq + 32 * t + l32;
+        wf[j][t] = *reinterpret_cast<const bf16x8 *>(wpart + rw * kRowBytes + 16 * chunk_pos(rw, c));
+      }
+#pragma unroll
+      for (int t = 0; t < NTN; ++t) {
+        const int rh = 128 * wr + 32 * t + l32;
+        hf[j][t] = *reinterpret_cast<const bf16x8 *>(hpart + rh * kRowBytes + 16 * chunk_pos(rh, c));
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int tm = 0; tm < 2; ++tm)
+#pragma unroll
+        for (int tn = 0; tn < NTN; ++tn)
+          acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j][tm], hf[j][tn], acc[tm][tn], 0, 0, 0);
+  }
+}
+
+// Step k, with S = k mod 5: its parts 2 k and 2 k + 1 sit in slots 2 S mod 5
+// and (2 S + 1) mod 5.  Wait for them (this wave's copies: everything but part
+// 2 k + 2, the last one issued; then everybody's through the barrier, which
+// also retires every wave's reads of step k - 1), copy parts 2 k + 3 and
+// 2 k + 4 into step k - 1's slots, compute.
+template <int S, int NTN>
+__device__ __forceinline__ void main_step(LmShared &sh, const DmaSrc &src, uint32_t ring_lds, f32x16 (&acc)[2][4],
+                                          int k, int nk) {
+  if (k + 1 < nk)
     asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
   else
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-}
-
-// MFMAs of one step: MFMA k index 8 (l >> 5) + e of sub-step j is hidden
-// element 16 j + 8 (l >> 5) + e of the step, i.e. chunk 2 j + (l >> 5).
-__device__ __forceinline__ void compute_stage(const unsigned char *stage, f32x16 (&acc)[2][4]) {
-  const int lane = threadIdx.x & 63, l32 = lane & 31, half = lane >> 5, wave = threadIdx.x >> 6;
-  const int tq = wave & 3, wr = wave >> 2;
-  bf16x8 wf[2][2], hf[2][4];  // both sub-steps' fragments are read first
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int c = 2 * j + half;
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int rw = 64 * tq + 32 * t + l32;
-      wf[j][t] = *reinterpret_cast<const bf16x8 *>(stage + rw * kRowBytes + 16 * chunk_pos(rw, c));
-    }
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int rh = 128 * wr + 32 * t + l32;
-      hf[j][t] = *reinterpret_cast<const bf16x8 *>(stage + kWPart + rh * kRowBytes + 16 * chunk_pos(rh, c));
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int tm = 0; tm < 2; ++tm)
-#pragma unroll
-      for (int tn = 0; tn < 4; ++tn)
-        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j][tm], hf[j][tn], acc[tm][tn], 0, 0, 0);
-}
-
-// Step kb on ring slot S: wait for its copies (this wave's, then everybody's
-// through the barrier, which also retires every wave's reads of the slot the
-// next copy overwrites), start the copy of step kb + kStages - 1, compute.
-template <int S>
-__device__ __forceinline__ void main_step(LmShared &sh, const DmaSrc &src, uint32_t ring_lds, f32x16 (&acc)[2][4],
-                                          int kb, int nk) {
-  wait_stages(min(nk - 1 - kb, kStages - 2));
   __builtin_amdgcn_s_barrier();
-  if (kb + kStages - 1 < nk) issue_stage(src, ring_lds + ((S + kStages - 1) % kStages) * kStage, kb + kStages - 1);
-  compute_stage(sh.ring[S], acc);
+  constexpr int s3 = (2 * S + 3) % kSlots, s4 = (2 * S + 4) % kSlots;
+  if (k + 1 < nk) issue_part(src, ring_lds + s3 * kPart, k + 1, 1);
+  if (k + 2 < nk) issue_part(src, ring_lds + s4 * kPart, k + 2, 0);
+  if (NTN > 0) compute_step<NTN>(sh.ring[(2 * S) % kSlots], sh.ring[(2 * S + 1) % kSlots], acc);
+}
+
+// The whole hidden dimension for a wave with NTN row subtiles (every wave of
+// the workgroup runs the same copies and barriers).
+template <int NTN>
+__device__ __forceinline__ void main_loop(LmShared &sh, const DmaSrc &src, uint32_t ring_lds, f32x16 (&acc)[2][4],
+                                          int nk) {
+  for (int k = 0; k < nk; k += kSlots) {
+    main_step<0, NTN>(sh, src, ring_lds, acc, k, nk);
+    if (k + 1 < nk) main_step<1, NTN>(sh, src, ring_lds, acc, k + 1, nk);
+    if (k + 2 < nk) main_step<2, NTN>(sh, src, ring_lds, acc, k + 2, nk);
+    if (k + 3 < nk) main_step<3, NTN>(sh, src, ring_lds, acc, k + 3, nk);
+    if (k + 4 < nk) main_step<4, NTN>(sh, src, ring_lds, acc, k + 4, nk);
+  }
 }
 
 __device__ __forceinline__ float shfl32f(float v) { return __shfl_xor(v, 32); }
@@ -155,8 +179,8 @@ __device__ __forceinline__ void epilogue_rows(const LmParams &p, const LmShared 
   const int half = lane >> 5, rl = 128 * wr + 32 * TN + (lane & 31);
   const int g = row0 + rl;
   const int c = tok0 / kLmChunk + tq;
-  const float a = sh.a[rl];
-  const int dd = sh.d[rl];
+  const float a = sh.rq.a[rl];
+  const int dd = sh.rq.d[rl];
   const int xb = tok0 + kLmChunk * tq + 4 * half;
   auto tok = [&](int tm, int q) { return xb + 32 * tm + 8 * (q >> 2) + (q & 3); };
 
@@ -236,38 +260,32 @@ __global__ __launch_bounds__(kLmThreads) __attribute__((amdgpu_waves_per_eu(2, 2
   const int tt = idx / p.RB, rb = idx - tt * p.RB;
   const int tok0 = tt * kLmTok, row0 = rb * kLmRows;
 
-  // Request settings of the tile's rows.
+  // Request settings of the tile's rows (kept in registers until the ring is free).
+  float row_a = 0.0f;
+  int row_d = -1;
   if (tid < kLmRows) {
     const int g = row0 + tid;
-    float a = 0.0f;
-    int d = -1;
     if (g < p.R) {
       const int r = find_request(p.cu, p.B, g);
       const int c0 = p.cu[r], c1 = p.cu[r + 1];
       const int i = g - (c0 + r);
       const float T = p.temperature[r];
-      if (T > 0.0f && __builtin_isfinite(T)) a = kLog2eL / T;
+      if (T > 0.0f && __builtin_isfinite(T)) row_a = kLog2eL / T;
       if (i >= 0 && i < c1 - c0) {
         const int di = c0 + i;
-        if (di >= 0 && di < p.D) d = p.draft_ids[di];
+        if (di >= 0 && di < p.D) row_d = p.draft_ids[di];
       }
     }
-    sh.a[tid] = a;
-    sh.d[tid] = d;
   }
 
   // Copy sources: tokens past V read row V - 1, rows past R read row R - 1
   // (their results are never written).
   DmaSrc src;
 #pragma unroll
-  for (int i = 0; i < kDmaW; ++i) {
-    const int r = 16 * (kDmaW * wave + i) + (lane >> 2);
-    src.w[i] = p.W + (int64_t)min(tok0 + r, p.V - 1) * p.wstride + 8 * chunk_pos(r, lane & 3);
-  }
-#pragma unroll
-  for (int i = 0; i < kDmaH; ++i) {
-    const int r = 16 * (kDmaH * wave + i) + (lane >> 2);
-    src.h[i] = p.H + (int64_t)min(row0 + r, p.R - 1) * p.hstride + 8 * chunk_pos(r, lane & 3);
+  for (int i = 0; i < kDmaPart; ++i) {
+    const int r = 8 * (kDmaPart * wave + i) + (lane >> 3);
+    src.w[i] = p.W + (int64_t)min(tok0 + r, p.V - 1) * p.wstride + 8 * chunk_pos(r, lane & 7);
+    src.h[i] = p.H + (int64_t)min(row0 + r, p.R - 1) * p.hstride + 8 * chunk_pos(r, lane & 7);
   }
   // LDS byte address of the ring (an address-space-3 pointer is the offset itself).
   const uint32_t ring_lds = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) unsigned char *)(&sh.ring[0][0]));
@@ -280,23 +298,34 @@ __global__ __launch_bounds__(kLmThreads) __attribute__((amdgpu_waves_per_eu(2, 2
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[tm][tn][q] = 0.0f;
 
+  // Parts 0, 1 and 2 (step 0, W of step 1) into slots 0, 1, 2.
   const int nk = p.d / kLmK;
-  __syncthreads();  // sh.a / sh.d written; nothing in flight
-#pragma unroll
-  for (int s = 0; s < kStages - 1; ++s)
-    if (s < nk) issue_stage(src, ring_lds + s * kStage, s);
-  for (int kb = 0; kb < nk; kb += kStages) {
-    main_step<0>(sh, src, ring_lds, acc, kb, nk);
-    if (kb + 1 < nk) main_step<1>(sh, src, ring_lds, acc, kb + 1, nk);
-    if (kb + 2 < nk) main_step<2>(sh, src, ring_lds, acc, kb + 2, nk);
-    if (kb + 3 < nk) main_step<3>(sh, src, ring_lds, acc, kb + 3, nk);
+  issue_part(src, ring_lds, 0, 0);
+  issue_part(src, ring_lds + kPart, 0, 1);
+  if (nk > 1) issue_part(src, ring_lds + 2 * kPart, 1, 0);
+  // Row subtiles of this wave that hold target rows (4 except in the last row block).
+  const int ntn = __builtin_amdgcn_readfirstlane(max(0, min(4, (p.R - row0 - 128 * (wave >> 2) + 31) / 32)));
+  if (ntn == 4)
+    main_loop<4>(sh, src, ring_lds, acc, nk);
+  else if (ntn == 3)
+    main_loop<3>(sh, src, ring_lds, acc, nk);
+  else if (ntn == 2)
+    main_loop<2>(sh, src, ring_lds, acc, nk);
+  else if (ntn == 1)
+    main_loop<1>(sh, src, ring_lds, acc, nk);
+  else
+    main_loop<0>(sh, src, ring_lds, acc, nk);
+  __syncthreads();  // every wave is done with the ring (its last step waited for all its copies)
+  if (tid < kLmRows) {
+    sh.rq.a[tid] = row_a;
+    sh.rq.d[tid] = row_d;
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
 
-  epilogue_rows<0>(p, sh, acc, tok0, row0);
-  epilogue_rows<1>(p, sh, acc, tok0, row0);
-  epilogue_rows<2>(p, sh, acc, tok0, row0);
-  epilogue_rows<3>(p, sh, acc, tok0, row0);
+  if (ntn > 0) epilogue_rows<0>(p, sh, acc, tok0, row0);
+  if (ntn > 1) epilogue_rows<1>(p, sh, acc, tok0, row0);
+  if (ntn > 2) epilogue_rows<2>(p, sh, acc, tok0, row0);
+  if (ntn > 3) epilogue_rows<3>(p, sh, acc, tok0, row0);
 }
 
 // ---------------------------------------------------------------------------

@@ -171,16 +171,16 @@ def test_lm_head_parity(name):
 
 
 def test_lm_head_strided_rows():
-    # hidden states and W as row slices of wider buffers (row strides > d), d = 96
-    inp = wl.make_lm_head_inputs(B=10, K=3, V=900, d=96, greedy_every=3, device=DEV)
+    # hidden states and W as row slices of wider buffers (row strides > d), d = 192
+    inp = wl.make_lm_head_inputs(B=10, K=3, V=900, d=192, greedy_every=3, device=DEV)
     ctx = lm_ctx(inp)
     try:
-        Hw = torch.zeros((inp["R"], 96 + 40), dtype=torch.bfloat16, device=DEV)
-        Ww = torch.zeros((inp["V"], 96 + 8), dtype=torch.bfloat16, device=DEV)
-        Hw[:, 8:104] = inp["hidden"]
-        Ww[:, :96] = inp["W"]
-        strided = dict(inp, hidden=Hw[:, 8:104], W=Ww[:, :96])
-        assert strided["hidden"].stride(0) == 136 and strided["W"].stride(0) == 104
+        Hw = torch.zeros((inp["R"], 192 + 40), dtype=torch.bfloat16, device=DEV)
+        Ww = torch.zeros((inp["V"], 192 + 8), dtype=torch.bfloat16, device=DEV)
+        Hw[:, 8:200] = inp["hidden"]
+        Ww[:, :192] = inp["W"]
+        strided = dict(inp, hidden=Hw[:, 8:200], W=Ww[:, :192])
+        assert strided["hidden"].stride(0) == 232 and strided["W"].stride(0) == 200
         h = host(inp)
         for seed, off in [(3, 0), (4, 5)]:
             g = lm_run(ctx, strided, seed=seed, offset=off, dbg_logits=True)
@@ -210,10 +210,11 @@ def test_lm_head_invalid_requests():
         assert g["err"] == sv.SV_ERR_ROW
         assert g["num_sampled"][5] == 0 and np.all(g["tokens"][5] == -1)
         assert np.all(g["num_sampled"][[0, 1, 2, 3, 4, 6, 7]] >= 1)
-        # host-side checks: hidden size not a multiple of 32, no LM-head storage
-        bad = wl.make_lm_head_inputs(B=2, K=1, V=100, d=80, device=DEV)
-        with pytest.raises(sv.SpecVerifyError):
-            lm_run(ctx, bad)
+        # host-side checks: hidden size not a multiple of 64, no LM-head storage
+        for d_bad in (80, 96):
+            bad = wl.make_lm_head_inputs(B=2, K=1, V=100, d=d_bad, device=DEV)
+            with pytest.raises(sv.SpecVerifyError):
+                lm_run(ctx, bad)
         plain = sv.spec_verify_create(inp["R"], inp["B"], 2, inp["V"], 0)
         try:
             with pytest.raises(sv.SpecVerifyError):
