@@ -925,12 +925,22 @@ struct RowInfo {
 // call only the rows whose tables the top-p pass left to it.
 __device__ __forceinline__ bool stream_state(const Params &p, int st) { return p.pass2 ? st == kRowTopPRedo : st < 0; }
 constexpr int kRowCache = kSliceRows;  // rows of a slice looked up before streaming
-constexpr int kFastDepth = 3;  // chunks in flight per wave in the fast pass (2, 4, 5: slower)
-// Waves per workgroup of the fast pass: eight (two per SIMD) halves the number of
-// workgroups against four and measured about 4 % faster on the streaming pass.
-constexpr int kFastWaves = 8;
-constexpr int kFastThreads = 64 * kFastWaves;
-static_assert(kRowCache <= kFastWaves, "one wave looks up each row of a slice");
+// Chunks in flight per wave in the fast pass: bf16 rows 4 (with eight-wave
+// workgroups, 2, 3, 5 and 6 measured 30.4, 28.5, 29.3 and 29.5 us against
+// 28.0 on the 164 MB headline batch; 6 no longer fits 8 waves per SIMD),
+// fp32 rows 3 (16 registers per chunk in flight instead of 8); 3 with penalties
+// (at 4 the counts' registers leave one workgroup per CU instead of two).
+template <int DT>
+constexpr int kFastDepth = DT == 1 ? 4 : 3;
+// Waves per workgroup of the fast pass: eight (two per SIMD) for bf16 rows
+// without penalties, where halving the number of workgroups against four
+// measured about 4 % faster; four otherwise (fp32 rows and the penalty variant
+// measured about 1 % slower with eight).
+template <int DT, bool PEN>
+constexpr int kFastWaves = (DT == 1 && !PEN) ? 8 : 4;
+template <int DT, bool PEN>
+constexpr int kFastThreads = 64 * kFastWaves<DT, PEN>;
+static_assert(kRowCache <= 4, "one wave looks up each row of a slice");
 
 __device__ __forceinline__ RowInfo row_info_of(const Params &p, const Req &q, int g) {
   RowInfo ri;
@@ -1220,10 +1230,11 @@ __device__ __forceinline__ void fast_chunk(const Params &p, const RowInfo &ri, i
 }
 
 template <int DT, bool PEN>
-__global__ __launch_bounds__(kFastThreads) void stats_fast_kernel(Params p) {
+__global__ __launch_bounds__((kFastThreads<DT, PEN>)) void stats_fast_kernel(Params p) {
+  constexpr int NW = kFastWaves<DT, PEN>;
   using L = Layout<DT>;
   constexpr int NV = L::kVec;
-  constexpr int D = kFastDepth;  // chunks in flight per wave
+  constexpr int D = PEN ? 3 : kFastDepth<DT>;  // chunks in flight per wave (the counts take registers too)
   __shared__ StatsShared sh;
   const int wave = uni((int)(threadIdx.x >> 6));
   const int N = p.R * p.NC;
@@ -1233,7 +1244,7 @@ __global__ __launch_bounds__(kFastThreads) void stats_fast_kernel(Params p) {
   const int g_first = start / p.NC, g_last = (end - 1) / p.NC;
   const int nrows = g_last - g_first + 1;
   const int len = end - start;
-  const int n = wave < len ? (len - wave + kFastWaves - 1) / kFastWaves : 0;
+  const int n = wave < len ? (len - wave + NW - 1) / NW : 0;
 
   // The first D loads are unconditional (a wave with fewer chunks reads the
   // slice's first chunk instead), so that every path into the loop has the
@@ -1247,7 +1258,7 @@ __global__ __launch_bounds__(kFastThreads) void stats_fast_kernel(Params p) {
   for (int s = 1; s < D; ++s) {
     gs[s] = gs[s - 1];
     cs[s] = cs[s - 1];
-    advance_chunk(gs[s], cs[s], kFastWaves, p.NC);
+    advance_chunk(gs[s], cs[s], NW, p.NC);
   }
   if (!PEN) {
 #pragma unroll
@@ -1300,7 +1311,7 @@ __global__ __launch_bounds__(kFastThreads) void stats_fast_kernel(Params p) {
 #pragma unroll
     for (int s = 0; s < D; ++s) {
       chunk(s);
-      advance_chunk(gs[s], cs[s], D * kFastWaves, p.NC);
+      advance_chunk(gs[s], cs[s], D * NW, p.NC);
       load(s, gs[s], cs[s]);
     }
   }
@@ -1311,7 +1322,7 @@ __global__ __launch_bounds__(kFastThreads) void stats_fast_kernel(Params p) {
     const int s = t % D;
     chunk(s);
     if (k + t + D < n) {
-      advance_chunk(gs[s], cs[s], D * kFastWaves, p.NC);
+      advance_chunk(gs[s], cs[s], D * NW, p.NC);
       load(s, gs[s], cs[s]);
     }
   }
@@ -2490,18 +2501,21 @@ hipError_t launch_stats(const Params &p, hipStream_t s, hipEvent_t t0, hipEvent_
                                                 : reinterpret_cast<const void *>(&stats_fast_kernel<0, true>))
                                 : (p.dtype == 1 ? reinterpret_cast<const void *>(&stats_fast_kernel<1, false>)
                                                 : reinterpret_cast<const void *>(&stats_fast_kernel<0, false>));
-  return launch_timed(fn, grid, p, s, t0, t1, p.fast ? kFastThreads : kThreads);
+  const int threads = !p.fast ? kThreads
+                      : p.fast_pen ? (p.dtype == 1 ? kFastThreads<1, true> : kFastThreads<0, true>)
+                                   : (p.dtype == 1 ? kFastThreads<1, false> : kFastThreads<0, false>);
+  return launch_timed(fn, grid, p, s, t0, t1, threads);
 }
 
 int stats_blocks_per_cu(int dtype, int kind) {
   int n = 0;
   hipError_t e;
   if (kind == 1)
-    e = dtype == 1 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, stats_fast_kernel<1, false>, kFastThreads, 0)
-                   : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, stats_fast_kernel<0, false>, kFastThreads, 0);
+    e = dtype == 1 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, stats_fast_kernel<1, false>, kFastThreads<1, false>, 0)
+                   : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, stats_fast_kernel<0, false>, kFastThreads<0, false>, 0);
   else if (kind == 2)
-    e = dtype == 1 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, stats_fast_kernel<1, true>, kFastThreads, 0)
-                   : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, stats_fast_kernel<0, true>, kFastThreads, 0);
+    e = dtype == 1 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, stats_fast_kernel<1, true>, kFastThreads<1, true>, 0)
+                   : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, stats_fast_kernel<0, true>, kFastThreads<0, true>, 0);
   else
     e = dtype == 1 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, stats_kernel<1>, kThreads, 0)
                    : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, stats_kernel<0>, kThreads, 0);
