@@ -1463,10 +1463,10 @@ static_assert(kBuf >= 2 * kCandCap, "the id-ordered kept list is staged in the u
 // base + (v kThreads + t) VW + w.
 constexpr int kTopkPer = 16;
 constexpr int kTopkTile = kTopkPer * kThreads;
-template <int DT>
+template <int DT, int NT = kThreads>
 __device__ __forceinline__ int topk_tok(int base, int e) {
   constexpr int VW = DT == 1 ? 8 : 4;
-  return base + ((e / VW) * kThreads + (int)threadIdx.x) * VW + (e % VW);
+  return base + ((e / VW) * NT + (int)threadIdx.x) * VW + (e % VW);
 }
 template <int DT, int NPER = kTopkPer>
 __device__ __forceinline__ void load_topk_tile(const Params &p, int g, int base, float (&z)[NPER]) {
@@ -1555,23 +1555,23 @@ struct TopkRaw {
   static constexpr int VW = DT == 1 ? 8 : 4;
   u32x4 v[kTopkPer / VW];
 };
-template <int DT>
+template <int DT, int NT = kThreads>
 __device__ __forceinline__ void topk_issue(const Params &p, int g, int base, int vfull, TopkRaw<DT> &r) {
   constexpr int VW = TopkRaw<DT>::VW;
   const char *row = static_cast<const char *>(p.logits) + (int64_t)g * p.lstride * (DT == 1 ? 2 : 4);
 #pragma unroll
   for (int v = 0; v < kTopkPer / VW; ++v) {
-    const int x0 = topk_tok<DT>(base, v * VW);
+    const int x0 = topk_tok<DT, NT>(base, v * VW);
     const uint32_t off = x0 + VW <= vfull ? (uint32_t)x0 * (DT == 1 ? 2u : 4u) : 0u;
     r.v[v] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(row + off));
   }
 }
-template <int DT>
+template <int DT, int NT = kThreads>
 __device__ __forceinline__ void topk_decode(int base, int vfull, const TopkRaw<DT> &r, float (&z)[kTopkPer]) {
   constexpr int VW = TopkRaw<DT>::VW;
 #pragma unroll
   for (int v = 0; v < kTopkPer / VW; ++v) {
-    const int x0 = topk_tok<DT>(base, v * VW);
+    const int x0 = topk_tok<DT, NT>(base, v * VW);
     const uint32_t ww[4] = {r.v[v].x, r.v[v].y, r.v[v].z, r.v[v].w};
 #pragma unroll
     for (int i = 0; i < VW; ++i) {
@@ -1958,6 +1958,12 @@ constexpr int kToppSub = 1024;
 constexpr int kToppSubOff = 320;  // sub-bucket of t = 0: t >= -20 is covered (a (z - m) <= 20)
 constexpr int kToppList = 2048;
 constexpr int kToppMaxNC = 512;   // chunks per row whose sums live in LDS (V <= 524288)
+// Threads per row: eight waves when most rows are dense (one row per
+// workgroup leaves few waves per CU, and the pass is bound by each
+// workgroup's own arithmetic: eight waves measured 11 % faster per step on
+// 640 dense bf16 rows); four with top-k on, where most rows have candidate
+// lists and their workgroups return at once (eight measured 1 % slower there).
+constexpr int kTpMaxWaves = 8;
 
 struct ToppShared {
   unsigned long long mass[kToppSub];
@@ -1966,9 +1972,9 @@ struct ToppShared {
   float part[kToppMaxNC * 4];            // per chunk, one slot per wave covering it
   unsigned long long lsum[kToppMaxNC];   // kept list weights per chunk (integer W)
   float tail[8];
+  float wmax[kTpMaxWaves];
   unsigned long long need;
   int n, sel;
-  BlockScratch red;
 };
 
 struct ToppW {
@@ -1977,71 +1983,75 @@ struct ToppW {
 };
 
 // Sub-bucket and weight of logit z, branch-free: z = -inf (t = +inf) lands in
-// the last sub-bucket with W = 0.
+// the last sub-bucket with W = 0.  topp_j is the sub-bucket alone (the same
+// operations), for tests that need no weight.
+__device__ __forceinline__ int topp_j(float t) {
+  const float u = fminf(fmaxf(__builtin_floorf(t * 16.0f), -(float)kToppSubOff), (float)(kToppSub - 1 - kToppSubOff));
+  return (int)u + kToppSubOff;
+}
 __device__ __forceinline__ ToppW topp_w(float z, float m, float a) {
   const float t = (m - z) * a;
-  const float u = fminf(fmaxf(__builtin_floorf(t * 16.0f), -(float)kToppSubOff), (float)(kToppSub - 1 - kToppSubOff));
-  const int j = (int)u + kToppSubOff;
+  const int j = topp_j(t);
   const int k = (j >> 4) - kToppSubOff / 16;
   return ToppW{j, k, exp2_acc(31.0f - (t - (float)k))};
 }
 
 // Calls fn(x, raw logit) for every token of row g (vector loads, two
 // super-tiles in flight, when the rows are aligned).  All threads call it.
-template <int DT, class F>
+template <int DT, int NT, class F>
 __device__ __forceinline__ void stream_row(const Params &p, int g, F fn) {
   if (p.vec_ok) {
     constexpr int VW = TopkRaw<DT>::VW;
     const int vfull = p.V - p.V % VW;
     TopkRaw<DT> ra, rb;
     int base = 0;
-    topk_issue<DT>(p, g, base, vfull, ra);
-    topk_issue<DT>(p, g, base + kTopkTile, vfull, rb);
+    topk_issue<DT, NT>(p, g, base, vfull, ra);
+    topk_issue<DT, NT>(p, g, base + (kTopkPer * NT), vfull, rb);
     while (base < vfull) {
       float z[kTopkPer];
-      topk_decode<DT>(base, vfull, ra, z);
-      topk_issue<DT>(p, g, base + 2 * kTopkTile, vfull, ra);
+      topk_decode<DT, NT>(base, vfull, ra, z);
+      topk_issue<DT, NT>(p, g, base + 2 * (kTopkPer * NT), vfull, ra);
 #pragma unroll
       for (int e = 0; e < kTopkPer; ++e) {
-        const int x = topk_tok<DT>(base, e);
+        const int x = topk_tok<DT, NT>(base, e);
         if (x < vfull) fn(x, z[e]);
       }
-      base += kTopkTile;
+      base += (kTopkPer * NT);
       if (base >= vfull) break;
-      topk_decode<DT>(base, vfull, rb, z);
-      topk_issue<DT>(p, g, base + 2 * kTopkTile, vfull, rb);
+      topk_decode<DT, NT>(base, vfull, rb, z);
+      topk_issue<DT, NT>(p, g, base + 2 * (kTopkPer * NT), vfull, rb);
 #pragma unroll
       for (int e = 0; e < kTopkPer; ++e) {
-        const int x = topk_tok<DT>(base, e);
+        const int x = topk_tok<DT, NT>(base, e);
         if (x < vfull) fn(x, z[e]);
       }
-      base += kTopkTile;
+      base += (kTopkPer * NT);
     }
-    for (int x = vfull + (int)threadIdx.x; x < p.V; x += kThreads) fn(x, load_logit(p, g, x));
+    for (int x = vfull + (int)threadIdx.x; x < p.V; x += NT) fn(x, load_logit(p, g, x));
   } else {
-    for (int x = threadIdx.x; x < p.V; x += kThreads) fn(x, load_logit(p, g, x));
+    for (int x = threadIdx.x; x < p.V; x += NT) fn(x, load_logit(p, g, x));
   }
 }
 
 // Calls tile(base, z[kTopkPer]) for every super-tile of an aligned row (two in
 // flight); logits of tokens at or past vfull = V - V % VW read as -inf.
-template <int DT, class F>
+template <int DT, int NT, class F>
 __device__ __forceinline__ void stream_tiles(const Params &p, int g, int vfull, F tile) {
   TopkRaw<DT> ra, rb;
   int base = 0;
-  topk_issue<DT>(p, g, base, vfull, ra);
-  topk_issue<DT>(p, g, base + kTopkTile, vfull, rb);
+  topk_issue<DT, NT>(p, g, base, vfull, ra);
+  topk_issue<DT, NT>(p, g, base + (kTopkPer * NT), vfull, rb);
   while (base < vfull) {
     float z[kTopkPer];
-    topk_decode<DT>(base, vfull, ra, z);
-    topk_issue<DT>(p, g, base + 2 * kTopkTile, vfull, ra);
+    topk_decode<DT, NT>(base, vfull, ra, z);
+    topk_issue<DT, NT>(p, g, base + 2 * (kTopkPer * NT), vfull, ra);
     tile(base, z);
-    base += kTopkTile;
+    base += (kTopkPer * NT);
     if (base >= vfull) break;
-    topk_decode<DT>(base, vfull, rb, z);
-    topk_issue<DT>(p, g, base + 2 * kTopkTile, vfull, rb);
+    topk_decode<DT, NT>(base, vfull, rb, z);
+    topk_issue<DT, NT>(p, g, base + 2 * (kTopkPer * NT), vfull, rb);
     tile(base, z);
-    base += kTopkTile;
+    base += (kTopkPer * NT);
   }
 }
 
@@ -2102,7 +2112,7 @@ template <class EACH>
 __device__ __forceinline__ float topp_select(ToppShared &sh, EACH each, unsigned long long need) {
   uint32_t prefix = 0, mask = 0;
   for (int shift = 24; shift >= 0; shift -= 8) {
-    sh.mass[threadIdx.x] = 0;
+    if (threadIdx.x < 256) sh.mass[threadIdx.x] = 0;
     __syncthreads();
     each([&](float z, float W) {
       const uint32_t key = ukey(z);
@@ -2115,8 +2125,9 @@ __device__ __forceinline__ float topp_select(ToppShared &sh, EACH each, unsigned
   return ukey_val(prefix);
 }
 
-template <int DT>
-__global__ __launch_bounds__(kThreads) void topp_kernel(Params p) {
+template <int DT, int NT>
+__global__ __launch_bounds__(NT) void topp_kernel(Params p) {
+  static_assert(NT % 256 == 0 && NT / 64 <= kTpMaxWaves, "the selects' 256-bin histograms and the wave maxima");
   __shared__ ToppShared sh;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = blockIdx.x;
@@ -2135,8 +2146,13 @@ __global__ __launch_bounds__(kThreads) void topp_kernel(Params p) {
   // Row scale m from the first pass's chunk table.
   float2 *tab = p.chunk_tab + (int64_t)g * p.nc_stride;
   float lm = kNegInf;
-  for (int c = tid; c < p.NC; c += kThreads) lm = fmaxf(lm, tab[c].x);
-  const float m = block_max(lm, sh.red);
+  for (int c = tid; c < p.NC; c += NT) lm = fmaxf(lm, tab[c].x);
+  lm = wave_max(lm);
+  if (lane == 0) sh.wmax[wave] = lm;
+  __syncthreads();
+  float m = sh.wmax[0];
+#pragma unroll
+  for (int w = 1; w < (NT / 64); ++w) m = fmaxf(m, sh.wmax[w]);
   if (!(m > kNegInf)) {  // no finite logit: the epilogue flags the row
     if (tid == 0) p.cand_n[g] = st;
     return;
@@ -2147,10 +2163,10 @@ __global__ __launch_bounds__(kThreads) void topp_kernel(Params p) {
   const bool tiles = p.vec_ok && pr.counts == nullptr;
 
   // Pass A: integer weight per sub-bucket.
-  for (int j = tid; j < kToppSub; j += kThreads) sh.mass[j] = 0;
+  for (int j = tid; j < kToppSub; j += NT) sh.mass[j] = 0;
   __syncthreads();
   if (tiles) {
-    stream_tiles<DT>(p, g, vfull, [&](int, float (&z)[kTopkPer]) {
+    stream_tiles<DT, NT>(p, g, vfull, [&](int, float (&z)[kTopkPer]) {
 #pragma unroll
       for (int e = 0; e < kTopkPer; ++e) {
         const ToppW w = topp_w(z[e] < tau ? kNegInf : z[e], m, a);
@@ -2162,7 +2178,7 @@ __global__ __launch_bounds__(kThreads) void topp_kernel(Params p) {
       atomicAdd(&sh.mass[w.j], (unsigned long long)(uint32_t)w.W);
     }
   } else {
-    stream_row<DT>(p, g, [&](int x, float raw) {
+    stream_row<DT, NT>(p, g, [&](int x, float raw) {
       const ToppW w = topp_w(apply_proc(raw, x, pr), m, a);
       atomicAdd(&sh.mass[w.j], (unsigned long long)(uint32_t)w.W);
     });
@@ -2228,12 +2244,15 @@ __global__ __launch_bounds__(kThreads) void topp_kernel(Params p) {
   // Pass B: the boundary sub-bucket into the list, the mass before it per chunk.
   bool redo = !direct;
   if (direct) {
-    for (int c = tid; c < p.NC * 4; c += kThreads) sh.part[c] = 0.0f;
-    for (int c = tid; c < p.NC; c += kThreads) sh.lsum[c] = 0;
+    for (int c = tid; c < p.NC * 4; c += NT) sh.part[c] = 0.0f;
+    for (int c = tid; c < p.NC; c += NT) sh.lsum[c] = 0;
     if (tid < 8) sh.tail[tid] = 0.0f;
     __syncthreads();
     constexpr int WPC = kChunk / (64 * VW);  // waves covering one chunk in a super-tile
+    // Most tokens lie below the boundary sub-bucket: their weight is not
+    // needed, and a wave whose tokens all do skips the rest.
     auto token = [&](int x, float z, float &acc) {
+      if (topp_j((m - z) * a) > jstar) return;
       const ToppW w = topp_w(z, m, a);
       acc += w.j < jstar ? __builtin_ldexpf(w.W, -31 - w.k) : 0.0f;
       if (w.j == jstar && z > kNegInf) {
@@ -2244,20 +2263,20 @@ __global__ __launch_bounds__(kThreads) void topp_kernel(Params p) {
         }
       }
     };
-    stream_tiles<DT>(p, g, vfull, [&](int base, float (&z)[kTopkPer]) {
+    stream_tiles<DT, NT>(p, g, vfull, [&](int base, float (&z)[kTopkPer]) {
 #pragma unroll
       for (int v = 0; v < kTopkPer / VW; ++v) {
         float acc = 0.0f;
 #pragma unroll
         for (int i = 0; i < VW; ++i) {
           const int e = v * VW + i;
-          const int x = topk_tok<DT>(base, e);
+          const int x = topk_tok<DT, NT>(base, e);
           float zz = z[e];
           if (!tiles && x < vfull) zz = apply_proc(zz, x, pr);  // penalty rows
           token(x, zz < tau ? kNegInf : zz, acc);
         }
         const float sum = wave_sum(acc);
-        const int c = (base + (v * kThreads + wave * 64) * VW) / kChunk;
+        const int c = (base + (v * NT + wave * 64) * VW) / kChunk;
         if (lane == 0 && c < p.NC) sh.part[c * 4 + wave % WPC] = sum;
       }
     });
@@ -2275,17 +2294,17 @@ __global__ __launch_bounds__(kThreads) void topp_kernel(Params p) {
     const int n = sh.n;
     zstar = topp_select(
         sh, [&](auto fn) {
-          for (int e = tid; e < n; e += kThreads) fn(sh.lz[e], topp_w(sh.lz[e], m, a).W);
+          for (int e = tid; e < n; e += NT) fn(sh.lz[e], topp_w(sh.lz[e], m, a).W);
         },
         need);
     // Kept list tokens into their chunks (integer sums), then the new table.
-    for (int e = tid; e < n; e += kThreads)
+    for (int e = tid; e < n; e += NT)
       if (sh.lz[e] >= zstar)
         atomicAdd(&sh.lsum[sh.lx[e] / kChunk], (unsigned long long)(uint32_t)topp_w(sh.lz[e], m, a).W);
     __syncthreads();
     constexpr int WPC = kChunk / (64 * VW);
     const int clast = (p.V - 1) / kChunk;
-    for (int c = tid; c < p.NC; c += kThreads) {
+    for (int c = tid; c < p.NC; c += NT) {
       float sc = 0.0f;
 #pragma unroll
       for (int w = 0; w < WPC; ++w) sc += sh.part[c * 4 + w];
@@ -2300,7 +2319,7 @@ __global__ __launch_bounds__(kThreads) void topp_kernel(Params p) {
   } else {
     zstar = topp_select(
         sh, [&](auto fn) {
-          stream_row<DT>(p, g, [&](int x, float raw) {
+          stream_row<DT, NT>(p, g, [&](int x, float raw) {
             const float z = apply_proc(raw, x, pr);
             const ToppW w = topp_w(z, m, a);
             if (w.j == jstar && z > kNegInf) fn(z, w.W);
@@ -2477,10 +2496,17 @@ hipError_t launch_topk(const Params &p, hipStream_t s) {
 }
 
 hipError_t launch_topp(const Params &p, hipStream_t s) {
-  if (p.dtype == 1)
-    topp_kernel<1><<<dim3(p.R), dim3(kThreads), 0, s>>>(p);
-  else
-    topp_kernel<0><<<dim3(p.R), dim3(kThreads), 0, s>>>(p);
+  if (p.has_topk) {
+    if (p.dtype == 1)
+      topp_kernel<1, 256><<<dim3(p.R), dim3(256), 0, s>>>(p);
+    else
+      topp_kernel<0, 256><<<dim3(p.R), dim3(256), 0, s>>>(p);
+  } else {
+    if (p.dtype == 1)
+      topp_kernel<1, 512><<<dim3(p.R), dim3(512), 0, s>>>(p);
+    else
+      topp_kernel<0, 512><<<dim3(p.R), dim3(512), 0, s>>>(p);
+  }
   return hipGetLastError();
 }
 

@@ -70,7 +70,12 @@ union LmShared {
 
 // One 16-byte load per lane from global memory straight into LDS: lane i
 // writes bytes lds + 16 i .. + 16 (lds is the wave's 1 KB destination).  The
-// waits for these loads are explicit (s_waitcnt vmcnt in the main loop).
+// waits for these loads are explicit (s_waitcnt vmcnt in the main loop); the
+// compiler's own form of this load makes it wait for every copy before any
+// LDS read, which serialises the ring.  hipcc warns that m0 is a reserved
+// register in the clobber list: nothing else in this file's kernels uses m0
+// (the generated code sets it only in these statements), so no value of the
+// compiler's lives in it across them.
 __device__ __forceinline__ void dma16(const void *g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(__builtin_amdgcn_readfirstlane(lds)),
                "v"(g)
