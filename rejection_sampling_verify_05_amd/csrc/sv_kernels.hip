@@ -1232,6 +1232,9 @@ __device__ __forceinline__ void fast_chunk(const Params &p, const RowInfo &ri, i
 template <int DT, bool PEN>
 __global__ __launch_bounds__((kFastThreads<DT, PEN>)) void stats_fast_kernel(Params p) {
   constexpr int NW = kFastWaves<DT, PEN>;
+  // Items in (request, chunk, row) order: the bf16 penalty variant (for fp32
+  // rows its registers would cost a wave per SIMD).
+  constexpr bool RQ = PEN && DT == 1;
   using L = Layout<DT>;
   constexpr int NV = L::kVec;
   constexpr int D = PEN ? 3 : kFastDepth<DT>;  // chunks in flight per wave (the counts take registers too)
@@ -1252,17 +1255,20 @@ __global__ __launch_bounds__((kFastThreads<DT, PEN>)) void stats_fast_kernel(Par
   u32x4 buf[D][NV];
   int4 cb[D][4];
   int gs[D], cs[D];
-  gs[0] = (start + wave) / p.NC;
-  cs[0] = start + wave - gs[0] * p.NC;
+  int xs[D], js[D];  // penalty variant: item index, and the slice row whose request holds it
+  if (!RQ) {
+    gs[0] = (start + wave) / p.NC;
+    cs[0] = start + wave - gs[0] * p.NC;
 #pragma unroll
-  for (int s = 1; s < D; ++s) {
-    gs[s] = gs[s - 1];
-    cs[s] = cs[s - 1];
-    advance_chunk(gs[s], cs[s], NW, p.NC);
-  }
-  if (!PEN) {
+    for (int s = 1; s < D; ++s) {
+      gs[s] = gs[s - 1];
+      cs[s] = cs[s - 1];
+      advance_chunk(gs[s], cs[s], NW, p.NC);
+    }
+    if (!PEN) {
 #pragma unroll
-    for (int s = 0; s < D; ++s) fast_load<DT>(p, n > s ? gs[s] : g_first, n > s ? cs[s] : 0, buf[s]);
+      for (int s = 0; s < D; ++s) fast_load<DT>(p, n > s ? gs[s] : g_first, n > s ? cs[s] : 0, buf[s]);
+    }
   }
 
   // Request lookups for the slice's rows (overlapping the loads).
@@ -1273,45 +1279,120 @@ __global__ __launch_bounds__((kFastThreads<DT, PEN>)) void stats_fast_kernel(Par
   }
   __syncthreads();
 
-  // Counts rows of the slice's rows (a valid address for rows without one).
+  // Penalty variant: the counts rows of the slice's requests (a valid address
+  // for rows without one), and the items in (request, chunk, row) order.  The
+  // R NC items keep their ranges per request (request r owns [g0 NC,
+  // (g0 + K + 1) NC) either way), but inside a request its rows' chunk c are
+  // consecutive items: the waves of a workgroup stream chunk c of the
+  // request's rows together, and the request's counts chunk c, the same for
+  // each row, is fetched from memory once and found in L2 by the others.
   const int32_t *crow[kRowCache];
+  int g0s[kRowCache], k1s[kRowCache];
+  bool oks[kRowCache];
   if (PEN) {
 #pragma unroll
     for (int i = 0; i < kRowCache; ++i) {
       const RowInfo x = uniform_row(sh.rows[i < nrows ? i : 0]);
       crow[i] = x.counts != nullptr ? x.counts : p.counts;
+      g0s[i] = x.g0;
+      k1s[i] = x.K + 1;
+      oks[i] = x.mode != kModeInvalid;
     }
   }
+  // Item x: row g, chunk c, and the slice row j whose request holds it (rows
+  // of an invalid request keep the row order).
+  auto place = [&](int x, int &g, int &c, int &j) {
+    const int gr = uni(x / p.NC);
+    j = gr - g_first;
+    int g0 = g0s[0], k1 = k1s[0];
+    bool ok = oks[0];  // (all uniform)
+#pragma unroll
+    for (int i = 1; i < kRowCache; ++i)
+      if (j == i) {
+        g0 = g0s[i];
+        k1 = k1s[i];
+        ok = oks[i];
+      }
+    if (!ok) {
+      g = gr;
+      c = x - gr * p.NC;
+      return;
+    }
+    const int l = x - g0 * p.NC;
+    c = uni(l / k1);
+    g = uni(g0 + (l - c * k1));
+  };
   auto load = [&](int s, int g, int c) {
     fast_load<DT>(p, g, c, buf[s]);
     if (PEN) {
-      const int gi = g - g_first;
       const int32_t *cr = crow[0];
 #pragma unroll
-      for (int i = 1; i < kRowCache; ++i) cr = gi == i ? crow[i] : cr;
+      for (int i = 1; i < kRowCache; ++i) cr = (RQ ? js[s] : g - g_first) == i ? crow[i] : cr;
       fast_load_counts<DT>(p, cr, c, cb[s]);
     }
   };
-  if (PEN) {
+  if (RQ) {
+#pragma unroll
+    for (int s = 0; s < D; ++s) {
+      xs[s] = uni(start + wave + s * NW);
+      if (n > s) {
+        place(xs[s], gs[s], cs[s], js[s]);
+      } else {
+        gs[s] = g_first;
+        cs[s] = 0;
+        js[s] = 0;
+      }
+      load(s, gs[s], cs[s]);
+    }
+  } else if (PEN) {
 #pragma unroll
     for (int s = 0; s < D; ++s) load(s, n > s ? gs[s] : g_first, n > s ? cs[s] : 0);
   }
 
-  RowInfo cur = uniform_row(sh.rows[n > 0 ? gs[0] - g_first : 0]);  // a wave without chunks may start past the slice
+  RowInfo cur = uniform_row(sh.rows[RQ ? js[0] : (n > 0 ? gs[0] - g_first : 0)]);  // a wave without chunks may start past the slice
   float ref = kNegInf;  // this wave's reference for row cur.g (uniform)
+  // Penalty variant: a wave's references for up to four rows (its items move
+  // between the rows of a request), slot g & 3.
+  int rg[4] = {-1, -1, -1, -1};
+  float rv[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
   auto chunk = [&](int s) {
+    if (RQ) {
+      cur = uniform_row(sh.rows[js[s]]);
+      cur.g = gs[s];
+      const int q = gs[s] & 3;
+      ref = kNegInf;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (q == i && rg[i] == gs[s]) ref = rv[i];
+      fast_chunk<DT, PEN>(p, cur, cs[s], buf[s], cb[s], ref);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (q == i) {
+          rg[i] = gs[s];
+          rv[i] = uni(ref);
+        }
+      return;
+    }
     if (gs[s] != cur.g) {
       cur = uniform_row(sh.rows[gs[s] - g_first]);
       ref = kNegInf;
     }
     fast_chunk<DT, PEN>(p, cur, cs[s], buf[s], cb[s], ref);
   };
+  auto advance = [&](int s) {
+    if (RQ) {
+      xs[s] = uni(xs[s] + D * NW);
+      place(xs[s], gs[s], cs[s], js[s]);
+    } else {
+      advance_chunk(gs[s], cs[s], D * NW, p.NC);
+    }
+  };
   int k = 0;
   for (; k + 2 * D - 1 < n; k += D) {
 #pragma unroll
     for (int s = 0; s < D; ++s) {
       chunk(s);
-      advance_chunk(gs[s], cs[s], D * NW, p.NC);
+      advance(s);
       load(s, gs[s], cs[s]);
     }
   }
@@ -1322,7 +1403,7 @@ __global__ __launch_bounds__((kFastThreads<DT, PEN>)) void stats_fast_kernel(Par
     const int s = t % D;
     chunk(s);
     if (k + t + D < n) {
-      advance_chunk(gs[s], cs[s], D * NW, p.NC);
+      advance(s);
       load(s, gs[s], cs[s]);
     }
   }
