@@ -103,7 +103,7 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: measures one GPU only (asked for --gpus {args.gpus}); "
               "the verify step shards by request with no exchange, so run one process per GPU.",
               file=sys.stderr)
         sys.exit(2)
