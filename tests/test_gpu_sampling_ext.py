@@ -26,6 +26,8 @@ CASES = {
     # ... the vectorised penalty pass with slices over several rows (about ten
     # 1024-token chunks per workgroup, eight chunks per row; items in column order)
     "freq_pres_fast_multirow": C3.with_(B=500, V=8192, history=100, freq=0.5, pres=0.3),
+    # ... with up to nine rows per request (the pass's items go request by request)
+    "freq_pres_fast_k8": C3.with_(B=200, K=8, V=8192, history=64, freq=0.4, pres=0.2),
     # penalties with top-k: lazy penalty (>= 0) and eager (negative penalty)
     "topk_freq_pres": C4.with_(B=6, K=3, V=4000, history=60, freq=0.5, pres=0.25),
     "topk_negative_freq": C4.with_(B=5, K=2, V=3000, history=60, freq=-0.5, pres=0.1, rep_penalty=1.0),
