@@ -422,6 +422,31 @@ __device__ __forceinline__ void load_chunk16(const Params &p, int g, int c, floa
   load_chunk16_at(p.logits, p.dtype, p.lstride, p.vec_ok, p.V, g, c, z);
 }
 
+// load_chunk16 with the row's penalties applied (those of apply_proc; the
+// top-k threshold is left to the consumers): the counts of the chunk's tokens
+// are loaded together with the logits, so penalties cost no extra round trip.
+__device__ __forceinline__ void load_chunk16_pen(const Params &p, int g, int c, const Proc &pr, float (&z)[16]) {
+  if (pr.counts == nullptr) {
+    load_chunk16(p, g, c, z);
+    return;
+  }
+  const int lane = threadIdx.x & 63;
+  int cnt[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) cnt[e] = pr.counts[min(c16_tok(c, e, lane), p.V - 1)];
+  load_chunk16(p, g, c, z);
+#pragma unroll
+  for (int e = 0; e < 16; ++e)
+    if (cnt[e] > 0) z[e] = penalize(z[e], cnt[e], pr);
+}
+
+// The processing left for logits whose penalties are applied: the threshold.
+__device__ __forceinline__ Proc proc_after_pen(const Proc &pr) {
+  Proc id = pr;
+  id.counts = nullptr;
+  return id;
+}
+
 // Wave-level chunk race of row g over its chunk table (W_c = s_c exp2(a (r_c - m))),
 // chunk `skip` left out.  Lane l draws the words of chunks 4l..4l+3.
 // 1/E of the chunk race for a wave's first 256 chunks of row g: lane l holds
@@ -562,23 +587,24 @@ __device__ __forceinline__ void row_stats(const Params &p, const Req &q, int g, 
 
 // Speculative part for dense stochastic row i (no-draft-probs rows and bonus
 // rows): the chunk race without the draft token's chunk, then the loads of
-// the winning chunk and of the draft token's chunk.
+// the winning chunk and of the draft token's chunk (penalties applied).
 template <class EF>
 __device__ __forceinline__ void spec_issue(const Params &p, const Req &q, int i, int d, float m, EF ent, RowSpec &rs,
-                                           const ChunkNoise &cn) {
+                                           const ChunkNoise &cn, const Proc &pr) {
   const int g = q.g0 + i;
   const bool excl = i < q.K && !q.has_q && d >= 0 && d < p.V;
   rs.cd = excl ? d / kChunk : -1;
   rs.rcd = 0.0f;
   rs.w1 = wave_chunk_race(p, g, ent, q.a, m, rs.cd, cn, &rs.rcd);
   const int c1 = rs.w1.s < 0.0f ? -1 : rs.w1.i;
-  if (c1 >= 0) load_chunk16(p, g, c1, rs.zc);
-  if (excl) load_chunk16(p, g, rs.cd, rs.zx);
+  if (c1 >= 0) load_chunk16_pen(p, g, c1, pr, rs.zc);
+  if (excl) load_chunk16_pen(p, g, rs.cd, pr, rs.zx);
 }
 
 // After the loads of spec_issue: z_d and the mass of d's chunk without d, in
 // the scale of that chunk's table entry r = ent(c_d).x:
-// exp2(fma(z, a, -hi)) exp2(-lo) with a r = hi + lo.
+// exp2(fma(z, a, -hi)) exp2(-lo) with a r = hi + lo (pr: the processing left
+// after the penalties).
 __device__ __forceinline__ void spec_draft_record(const Params &p, const Req &q, int d, const Proc &pr,
                                                   const RowSpec &rs, float ref, float &zd, float &sx) {
   const int lane = threadIdx.x & 63;
@@ -643,8 +669,8 @@ __device__ __forceinline__ int spec_finish(const Params &p, const Req &q, int j,
   if (win.s < 0.0f) return -1;
   const int cstar = win.i;
   const float hi = a * ent(cstar).x;
-  const float *zs = cstar == cd ? sh.zx[slot] : sh.zc[slot];
-  return block_token_race(p, gs, cstar, zs, pr, a, hi, (excl && cstar == cd) ? dj : -1, sh.red);
+  const float *zs = cstar == cd ? sh.zx[slot] : sh.zc[slot];  // penalties applied
+  return block_token_race(p, gs, cstar, zs, proc_after_pen(pr), a, hi, (excl && cstar == cd) ? dj : -1, sh.red);
 }
 
 // Speculative rows: with at most four rows, row w for wave w; with more, rows
@@ -740,12 +766,12 @@ __device__ __forceinline__ void request_epilogue(const Params &p, const Req &q, 
     const bool valid_d = i < K && d >= 0 && d < p.V;
     if (st < 0 && greedy) {
       if (lc < p.NC) {
-        load_chunk16(p, g, lc, rs.zc);
-        am = wave_first_equal(p, lc, rs.zc, pr, m);
+        load_chunk16_pen(p, g, lc, pr, rs.zc);
+        am = wave_first_equal(p, lc, rs.zc, proc_after_pen(pr), m);
       }
     } else if (st < 0 && spec && (!q.has_q || i == K)) {
-      spec_issue(p, q, i, d, m, ent, rs, cn);
-      if (rs.cd >= 0) spec_draft_record(p, q, d, pr, rs, ent(rs.cd).x, zd, sx);
+      spec_issue(p, q, i, d, m, ent, rs, cn, pr);
+      if (rs.cd >= 0) spec_draft_record(p, q, d, proc_after_pen(pr), rs, ent(rs.cd).x, zd, sx);
       spec_publish(rs, wave, sh);
     } else if (valid_d) {
       // single loads: z_d (and q(d)) for the accept test
@@ -890,10 +916,10 @@ __device__ __forceinline__ void request_epilogue(const Params &p, const Req &q, 
   float sxj = sh.sx[j];
   if (slot < 0) {  // no speculative state for this row: same steps, loads now
     if (wave == 0) {
-      spec_issue(p, q, j, dj, m, entj, rs, chunk_noise(p, q.g0 + j));
+      spec_issue(p, q, j, dj, m, entj, rs, chunk_noise(p, q.g0 + j), pr);
       float zd = kNegInf;
       sxj = 0.0f;
-      if (rs.cd >= 0) spec_draft_record(p, q, dj, pr, rs, entj(rs.cd).x, zd, sxj);
+      if (rs.cd >= 0) spec_draft_record(p, q, dj, proc_after_pen(pr), rs, entj(rs.cd).x, zd, sxj);
       spec_publish(rs, 0, sh);
       if (lane == 0) sh.sx[j] = sxj;
     }
