@@ -682,7 +682,19 @@ __device__ __forceinline__ int spec_slot(int i, int nrow) {
   return i < kWaves - 1 ? i : (i == nrow - 1 ? kWaves - 1 : -1);
 }
 
-__device__ __forceinline__ void request_epilogue(const Params &p, const Req &q, EpiShared &sh) {
+// PLAIN: the call has no top-k, top-p, penalties or draft distributions; the
+// settings they would read are then constants, and their paths compile away.
+template <bool PLAIN>
+__device__ __forceinline__ void request_epilogue(const Params &p, const Req &q_in, EpiShared &sh) {
+  Req q = q_in;
+  if (PLAIN) {
+    q.proc.counts = nullptr;
+    q.proc.theta = 1.0f;
+    q.proc.freq = 0.0f;
+    q.proc.pres = 0.0f;
+    q.proc.tau = kNegInf;
+    q.has_q = false;
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K = q.K, r = q.r, nrow = K + 1;
 
@@ -701,7 +713,7 @@ __device__ __forceinline__ void request_epilogue(const Params &p, const Req &q, 
   // Row states (top-k pass results), draft ids and the chunk tables.
   for (int i = tid; i < nrow; i += kThreads) {
     const int g = q.g0 + i;
-    const int st = row_state(p, g);
+    const int st = PLAIN ? kRowDense : row_state(p, g);
     sh.state[i] = st;
     sh.tau[i] = (st == kRowDense) ? kNegInf : p.cand_tau[g];
     sh.d[i] = i < K ? p.draft_ids[q.c0 + i] : -1;
@@ -753,14 +765,14 @@ __device__ __forceinline__ void request_epilogue(const Params &p, const Req &q, 
       if (i >= nrow) break;
     }
     const int g = q.g0 + i;
-    const int st = sh.state[i];
+    const int st = PLAIN ? kRowDense : sh.state[i];
     const int d = sh.d[i];
     auto ent = [&](int c) { return entry(i, c); };
     float m, s;
     int lc;
     row_stats(p, q, g, st, greedy, ent, m, s, lc);
     Proc pr = q.proc;
-    pr.tau = sh.tau[i];
+    pr.tau = PLAIN ? kNegInf : sh.tau[i];
     int am = 0x7FFFFFFF;
     float zd = kNegInf, qd = 1.0f, sx = 0.0f;
     const bool valid_d = i < K && d >= 0 && d < p.V;
@@ -866,8 +878,8 @@ __device__ __forceinline__ void request_epilogue(const Params &p, const Req &q, 
   const int dj = rejected ? sh.d[j] : -1;
   const float m = sh.m[j], s = sh.s[j];
   Proc pr = q.proc;
-  pr.tau = sh.tau[j];
-  const int st = sh.state[j];
+  pr.tau = PLAIN ? kNegInf : sh.tau[j];
+  const int st = PLAIN ? kRowDense : sh.state[j];
   const float a = q.a;
 
   if (st >= 0) {
@@ -1543,9 +1555,10 @@ __global__ __launch_bounds__(kThreads) void resid_race_kernel(Params p) {
 }
 
 // Request epilogue kernel: one workgroup per request, after the stats pass.
+template <bool PLAIN>
 __global__ __launch_bounds__(kThreads) void epilogue_kernel(Params p) {
   __shared__ EpiShared sh;
-  request_epilogue(p, load_req(p, blockIdx.x), sh);
+  request_epilogue<PLAIN>(p, load_req(p, blockIdx.x), sh);
 }
 
 // ---------------------------------------------------------------------------
@@ -2656,7 +2669,12 @@ int stats_blocks_per_cu(int dtype, int kind) {
 }
 
 hipError_t launch_epilogue(const Params &p, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
-  return launch_timed(reinterpret_cast<const void *>(&epilogue_kernel), dim3((unsigned)p.B), p, s, t0, t1);
+  // Without top-k, top-p, penalties or draft distributions: the plain variant.
+  const bool plain = !p.has_topk && !p.has_topp && p.rep_penalty == nullptr && p.freq_penalty == nullptr &&
+                     p.pres_penalty == nullptr && p.draft_probs == nullptr && p.draft_logits == nullptr;
+  const void *fn = plain ? reinterpret_cast<const void *>(&epilogue_kernel<true>)
+                         : reinterpret_cast<const void *>(&epilogue_kernel<false>);
+  return launch_timed(fn, dim3((unsigned)p.B), p, s, t0, t1);
 }
 
 __global__ void zero_count_kernel(int *count) { *count = 0; }
