@@ -682,8 +682,9 @@ __device__ __forceinline__ int spec_slot(int i, int nrow) {
   return i < kWaves - 1 ? i : (i == nrow - 1 ? kWaves - 1 : -1);
 }
 
-// PLAIN: the call has no top-k, top-p, penalties or draft distributions; the
-// settings they would read are then constants, and their paths compile away.
+// PLAIN: the call has no top-k, top-p, penalties or draft distributions and
+// at most four rows per request; the settings they would read are then
+// constants, and their paths compile away.
 template <bool PLAIN>
 __device__ __forceinline__ void request_epilogue(const Params &p, const Req &q_in, EpiShared &sh) {
   Req q = q_in;
@@ -703,6 +704,9 @@ __device__ __forceinline__ void request_epilogue(const Params &p, const Req &q_i
     write_empty(p, r);
     return;
   }
+  // The plain variant also runs only with at most four rows per request
+  // (cu_ok bounds K by out_stride - 1): every row has a wave of its own.
+  if (PLAIN) __builtin_assume(nrow <= kWaves);
   if (q.mode == kModeInvalid) {
     if (tid == 0) raise_err(p, q.errbits);
     write_empty(p, r);
@@ -2669,9 +2673,10 @@ int stats_blocks_per_cu(int dtype, int kind) {
 }
 
 hipError_t launch_epilogue(const Params &p, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
-  // Without top-k, top-p, penalties or draft distributions: the plain variant.
+  // Without top-k, top-p, penalties or draft distributions, K <= 3: the plain variant.
   const bool plain = !p.has_topk && !p.has_topp && p.rep_penalty == nullptr && p.freq_penalty == nullptr &&
-                     p.pres_penalty == nullptr && p.draft_probs == nullptr && p.draft_logits == nullptr;
+                     p.pres_penalty == nullptr && p.draft_probs == nullptr && p.draft_logits == nullptr &&
+                     p.out_stride <= kWaves;
   const void *fn = plain ? reinterpret_cast<const void *>(&epilogue_kernel<true>)
                          : reinterpret_cast<const void *>(&epilogue_kernel<false>);
   return launch_timed(fn, dim3((unsigned)p.B), p, s, t0, t1);
