@@ -21,7 +21,10 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
-_SO = os.path.join(_HERE, "liborc.so")
+# SV_ORACLE_LIB names another build of oracle.c to load (the mutation check
+# loads deliberately broken copies this way); default: the in-tree build.
+_DEFAULT_SO = os.path.join(_HERE, "liborc.so")
+_SO = os.environ.get("SV_ORACLE_LIB") or _DEFAULT_SO
 
 RACE_CHUNK = 1024
 LM_HEAD_CHUNK = 64  # race chunk width of the LM-head path
@@ -43,15 +46,24 @@ class _BatchOpts(ctypes.Structure):
                 ("synthetic_rates", ctypes.c_void_p)]
 
 
+GCC_FLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra"]
+
+
+def compile_to(src: str, out: str, extra=()) -> str:
+    """Compile a copy of oracle.c (src) into the shared library `out`."""
+    tmp = out + ".tmp"
+    r = subprocess.run(["gcc", *GCC_FLAGS, *extra, "-o", tmp, src, "-lm"], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"gcc failed on {src}:\n{r.stderr}")
+    os.replace(tmp, out)
+    return out
+
+
 def build(force: bool = True) -> str:
     """Compile oracle.c into liborc.so with gcc (no FMA contraction)."""
-    if force or not os.path.exists(_SO):
-        tmp = _SO + ".tmp"
-        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
-               "-fno-fast-math", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
-        subprocess.run(cmd, check=True)
-        os.replace(tmp, _SO)
-    return _SO
+    if force or not os.path.exists(_DEFAULT_SO):
+        compile_to(_SRC, _DEFAULT_SO)
+    return _DEFAULT_SO
 
 
 def lib():

@@ -60,6 +60,14 @@ def test_draft_noise_is_not_the_verifiers():
         b, _ = oracle.race_tags(w, 16, 5, 0, key, oracle.TAG_DRAFT_CHUNK, oracle.TAG_DRAFT_TOKEN)
         same += a == b
     assert stats.binomtest(same, N, float(q @ q)).pvalue > P_MIN
+    # The draft sampler itself: its token for draft row `key` against the
+    # verifier's race of target row `key` over the same q.
+    z = np.log(w).astype(np.float32)
+    qz = oracle.softmax(z, 1.0)
+    N2 = 4000
+    same = sum(oracle.draft_sample(z, 1.0, 5, 0, key, C=16)[0] == oracle.race(qz, 16, 5, 0, key)[0]
+               for key in range(N2))
+    assert stats.binomtest(int(same), N2, float(qz @ qz)).pvalue > P_MIN
 
 
 def test_drafting_then_verifying_keeps_the_target_law():
