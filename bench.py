@@ -10,11 +10,15 @@ timed region; the step rotates over several distinct input copies (more than
 1 GB in total) so that the 256 MB Infinity Cache cannot serve the logits.
 
 Prints one JSON line: verified logit rows/s over the timed steps; the
-streaming statistics kernel's achieved algorithmic HBM bandwidth against the
+first pass over the rows (the streaming statistics kernel, or the top-k pass
+when top-k is on) with its achieved algorithmic HBM bandwidth against the
 8 TB/s peak (its duration from dispatch-stamped HIP events on the launch
-stream, over a second, instrumented pass of the same steps); the whole verify
-call's and the epilogue kernel's durations; and the CPU oracle's rate on a
-bounded sample of the same workload.
+stream, over a second, instrumented pass of the same steps), next to the
+same kernel's figure from the committed rocprofv3 trace of this workload;
+the whole verify call's and the epilogue kernel's durations; the acceptance
+measured on the outputs; and the CPU oracle's rate on a bounded sample of the
+same workload, single-threaded and over a process pool on the host's cores
+(timed before the GPU is touched).
 """
 from __future__ import annotations
 
@@ -30,8 +34,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
-# FETCH_SIZE / WRITE_SIZE counter record of the streaming kernel on this workload
-COUNTERS = os.path.join(ROOT, "profiles", "stats_fast_kernel_bf16_B256_V128256_counters.md")
+PROFILES = os.path.join(ROOT, "profiles")
+# FETCH_SIZE / WRITE_SIZE counter record of the streaming kernel on the headline workload
+COUNTERS = os.path.join(PROFILES, "stats_fast_kernel_bf16_B256_V128256_counters.md")
 KERNEL_SOURCES = ["rejection_sampling_verify_05_amd/csrc/sv_kernels.hip", "rejection_sampling_verify_05_amd/csrc/sv_device.h",
                   "rejection_sampling_verify_05_amd/csrc/sv_internal.h", "rejection_sampling_verify_05_amd/build.py"]
 
@@ -51,11 +56,10 @@ def kernel_source_hash(sources=None) -> str:
     return h.hexdigest()
 
 
-def recorded_traffic_per_row(path=None, sources=None):
-    """HBM bytes per target row measured by the counter runs, or None when the
-    record is missing or was taken on different kernel sources."""
-    path = path or COUNTERS
-    if not os.path.exists(path):
+def read_record(path, sources=None):
+    """The `- key: value` record of a profiles/ summary, or None when the file is
+    missing or was taken on different kernel sources."""
+    if not path or not os.path.exists(path):
         return None
     rec = {}
     for line in open(path):
@@ -64,7 +68,128 @@ def recorded_traffic_per_row(path=None, sources=None):
             rec[k.strip("` ")] = v.strip().strip("`")
     if rec.get("kernel_source_sha256") != kernel_source_hash(sources):
         return None
-    return float(rec["hbm_bytes_per_target_row"])
+    return rec
+
+
+def recorded_traffic_per_row(path=None, sources=None):
+    """HBM bytes per target row measured by the counter runs, or None when the
+    record is missing or was taken on different kernel sources."""
+    rec = read_record(path or COUNTERS, sources)
+    return None if rec is None else float(rec["hbm_bytes_per_target_row"])
+
+
+# Per-workload profiles/ summaries: the first pass over the rows, named for the
+# kernel and the workload.
+WORKLOAD_PROFILE = {
+    "2": "stats_fast_kernel_bf16_B64_K4_V32000",
+    "3": "stats_fast_kernel_bf16_B256_V128256",
+    "3k3": "stats_fast_kernel_bf16_B256_K3_V128256",
+    "4": "topk_kernel_f32_B512_K8_V151936",
+    "5": "stats_fast_kernel_bf16_B1024_K5_V256000",
+}
+
+
+def profile_paths(cid):
+    base = WORKLOAD_PROFILE.get(cid)
+    if base is None:
+        return None, None
+    return os.path.join(PROFILES, base + "_counters.md"), os.path.join(PROFILES, base + "_trace.md")
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_workers():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))  # the GPU machine gives one GPU's process 16 cores
+
+
+_POOL_INPUT = None
+
+
+def _oracle_slice(task):
+    """Oracle verify call on requests [a, b) of the pool's input batch (run in a
+    forked worker; the batch is inherited, not sent)."""
+    import oracle
+    a, b, offset = task
+    h = _POOL_INPUT
+    cu = h["cu"]
+    g0, g1 = int(cu[a]) + a, int(cu[b]) + b
+    d0, d1 = int(cu[a]), int(cu[b])
+    sl = lambda v, lo, hi: None if v is None else v[lo:hi]
+    oracle.verify_batch(h["logits"][g0:g1], cu[a:b + 1] - cu[a], h["draft_ids"][d0:d1],
+                        h["temperature"][a:b], draft_probs=sl(h["draft_probs"], d0, d1),
+                        top_k=sl(h["top_k"], a, b), rep_penalty=sl(h["rep_penalty"], a, b),
+                        idx_mapping=sl(h["idx_mapping"], a, b), counts=h["counts"], seed=1234, offset=offset,
+                        freq=sl(h["freq"], a, b), pres=sl(h["pres"], a, b), top_p=sl(h["top_p"], a, b),
+                        synthetic_rates=h["synthetic_rates"], max_k=h["max_k"])
+    return g1 - g0
+
+
+def cpu_baseline_leg(w, seconds):
+    """The oracle on a bounded sample of workload w, made on the host with the
+    same generator recipe (the GPU is not touched yet): whole batches in one
+    process for half the budget, then request slices over a fork pool of the
+    host's cores for the other half."""
+    import multiprocessing as mp
+    import time as _t
+    import numpy as np
+    import oracle
+    import workloads as wl
+    global _POOL_INPUT
+    inp = wl.make_inputs(w, "cpu", salt=0)
+    h = wl.to_numpy(inp)
+    penalty = any(inp[k] is not None for k in ("rep_penalty", "freq", "pres"))
+    h["counts"] = inp["counts"].numpy() if penalty else None
+    h["draft_probs"] = None if inp["draft_probs"] is None else inp["draft_probs"].numpy()
+    h["max_k"] = w.K
+    B, R = inp["B"], inp["R"]
+    _POOL_INPUT = h
+    t0 = _t.perf_counter()
+    n1 = rows1 = 0
+    while True:
+        _oracle_slice((0, B, n1))
+        n1 += 1
+        rows1 += R
+        if _t.perf_counter() - t0 >= seconds / 2:
+            break
+    s1 = _t.perf_counter() - t0
+    workers = host_workers()
+    per = max(1, -(-B // (4 * workers)))
+    tasks = [(a, min(B, a + per), k) for k in range(64) for a in range(0, B, per)]
+    ctx = mp.get_context("fork")
+    rows_n, batches = 0, 0
+    with ctx.Pool(workers) as pool:
+        pool.map(_oracle_slice, tasks[:workers])  # workers started and warm
+        t1 = _t.perf_counter()
+        k = 0
+        per_batch = -(-B // per)
+        while True:
+            rows_n += sum(pool.map(_oracle_slice, tasks[k * per_batch:(k + 1) * per_batch]))
+            batches += 1
+            k = (k + 1) % 64
+            if _t.perf_counter() - t1 >= seconds / 2:
+                break
+        sn = _t.perf_counter() - t1
+    _POOL_INPUT = None
+    return {"value": rows_n / sn, "unit": "rows/s", "cores": workers, "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "single_process": {"value": rows1 / s1, "unit": "rows/s", "cores": 1,
+                               "sample": f"{n1} whole batch(es) ({R} rows each), {s1:.1f} s"},
+            "sample": f"{batches} whole batch(es) of workload {w.cid} ({R} rows each; B={B} requests in slices "
+                      f"of {per}) over a fork pool of {workers} processes, {sn:.1f} s; inputs made on the host "
+                      "with the same generator recipe as the GPU copies (same distribution, other draws); "
+                      "C oracle, fp64"}
 
 
 def copy_calibration():
@@ -112,6 +237,12 @@ def main():
     import torch
 
     import workloads as wl
+
+    # CPU baseline first: its process pool forks before anything touches the GPU.
+    cpu = None
+    if not args.no_cpu and args.workload != "3h":
+        cpu = cpu_baseline_leg(wl.CONFIGS[args.workload], args.cpu_seconds)
+
     from rejection_sampling_verify_05_amd import build as libbuild
     if not os.path.exists(libbuild.OUTPUT):
         libbuild.build_library()
@@ -234,44 +365,59 @@ def main():
     assert len(stream_ms) == args.steps
     assert sv.spec_verify_read_error(ctx) == 0
 
-    # Dominant kernel: the streaming statistics pass.  Its algorithmic bytes
-    # are one read of every target row, R V s (s = 2 for bf16, 4 for fp32).
+    # Dominant kernel: the first pass over the rows (the streaming statistics
+    # pass, or the top-k pass).  Its algorithmic bytes are one read of every
+    # target row, R V s (s = 2 for bf16, 4 for fp32), plus, for the statistics
+    # pass with penalties, the counts row of each penalised request (V 4).
     esize = first["logits"].element_size()
-    bytes_per = float(np.mean([copies[(args.warmup + k) % ncopies]["R"] * w.V * esize
-                               for k in range(args.steps)]))
+    kernel = "topk_kernel (top-k pass: every row read once)" if w.top_k else \
+        "stats_fast_kernel (streaming softmax statistics)"
+
+    def launch_bytes(c):
+        b = c["R"] * w.V * esize
+        if penalty and not w.top_k:
+            pen = torch.zeros(w.B, dtype=torch.bool)
+            for k in ("rep_penalty", "freq", "pres"):
+                if c[k] is not None:
+                    pen |= (c[k].cpu() != (1.0 if k == "rep_penalty" else 0.0))
+            b += int(pen.sum()) * w.V * 4
+        return b
+
+    per_copy_bytes = [launch_bytes(c) for c in copies]
+    bytes_per = float(np.mean([per_copy_bytes[(args.warmup + k) % ncopies] for k in range(args.steps)]))
     rows_per = rows / args.steps
+    R_mean = float(np.mean([copies[(args.warmup + k) % ncopies]["R"] for k in range(args.steps)]))
     achieved = bytes_per / (float(np.mean(stream_ms)) * 1e-3) / 1e9
-    per_row = recorded_traffic_per_row() if w.cid == "3" else None
-    traffic = None if per_row is None else int(per_row * float(np.mean(
-        [copies[(args.warmup + k) % ncopies]["R"] for k in range(args.steps)])))
+    cpath, tpath = profile_paths(w.cid)
+    per_row = recorded_traffic_per_row(cpath) if cpath else None
+    traffic = None if per_row is None else int(per_row * R_mean)
+    trace = read_record(tpath)
+    prof = None
+    if trace is not None:
+        avg_ns = float(trace["kernel_avg_ns"])
+        rb = float(trace["bytes_per_launch"])
+        prof = {"avg_us": round(avg_ns / 1e3, 3), "achieved": round(rb / avg_ns, 1),
+                "frac": round(rb / avg_ns / HBM_PEAK_GBS, 4), "dispatches": int(trace["dispatches"]),
+                "source": os.path.relpath(tpath, ROOT)}
     value = rows / (total_ms * 1e-3)
+
+    # Acceptance measured on the outputs of the instrumented pass's last step
+    # of each input copy: accepted drafts per draft position.
+    acc_n = np.zeros(w.K + 1)
+    acc_d = np.zeros(w.K + 1)
+    for c, o in zip(copies, outs):
+        Kr = c["K"].cpu().numpy()
+        ns = o["ns"].cpu().numpy()
+        T = c["temperature"].cpu().numpy()
+        for i in range(w.K):
+            has = Kr > i
+            acc_d[i] += has.sum()
+            acc_n[i] += (has & (ns - 1 > i)).sum()
+    per_pos = [round(float(a / d), 4) if d else None for a, d in zip(acc_n[:w.K], acc_d[:w.K])]
 
     def pct(a):
         return {"mean": round(float(np.mean(a)) * 1e3, 2), "p10": round(float(np.percentile(a, 10)) * 1e3, 2),
                 "p50": round(float(np.median(a)) * 1e3, 2), "p90": round(float(np.percentile(a, 90)) * 1e3, 2)}
-
-    # CPU baseline: the oracle on a bounded sample of the same workload
-    cpu = None
-    if not args.no_cpu:
-        import oracle
-        h = wl.to_numpy(first)
-        dp = None if first["draft_probs"] is None else first["draft_probs"].cpu().numpy()
-        t_start = time.perf_counter()
-        n_calls, cpu_rows = 0, 0
-        while True:
-            oracle.verify_batch(h["logits"], h["cu"], h["draft_ids"], h["temperature"], draft_probs=dp,
-                                top_k=h["top_k"], rep_penalty=h["rep_penalty"], idx_mapping=h["idx_mapping"],
-                                counts=first["counts"].cpu().numpy() if penalty else None,
-                                seed=1234, offset=n_calls, freq=h["freq"], pres=h["pres"], top_p=h["top_p"],
-                                synthetic_rates=h["synthetic_rates"])
-            n_calls += 1
-            cpu_rows += first["R"]
-            if time.perf_counter() - t_start >= args.cpu_seconds:
-                break
-        cpu_s = time.perf_counter() - t_start
-        cpu = {"value": cpu_rows / cpu_s, "unit": "rows/s", "cores": 1, "kind": "oracle",
-               "sample": f"{n_calls} full batch(es) of workload {w.cid} ({first['R']} rows each, "
-                         f"offsets 0..{n_calls - 1}), single-threaded C oracle, {cpu_s:.1f} s"}
 
     sv.spec_verify_destroy(ctx)
     line = {
@@ -295,11 +441,15 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "stats_fast_kernel (streaming softmax statistics)",
+                     "kernel": kernel,
                      "kernel_us": pct(stream_ms), "bytes_per_launch": int(bytes_per),
-                     "bytes_rule": f"R*V*{esize} (each target row read once)"},
+                     "bytes_rule": f"R*V*{esize} (each target row read once)" +
+                                   (" + V*4 per penalised request (its counts row)" if penalty and not w.top_k else ""),
+                     "rocprof": prof},
+        "step_achieved_GBs": round(bytes_per / (total_ms / args.steps * 1e-3) / 1e9, 1),
         "verify_call_us": pct(verify_ms),
         "epilogue_kernel_us": pct(epi_ms),
+        "acceptance_per_position": per_pos,
         "cpu_baseline": cpu,
         "wall_s": round(wall, 3),
     }

@@ -75,6 +75,14 @@
 extern "C" {
 #endif
 
+/* The library exports only the entry points below (it is built with hidden
+ * default visibility). */
+#if defined(__GNUC__)
+#define SV_API __attribute__((visibility("default")))
+#else
+#define SV_API
+#endif
+
 #define SV_RACE_CHUNK 1024        /* tokens per chunk of the two-level race        */
 #define SV_MAX_DRAFTS 64          /* largest max_k a context accepts               */
 #define SV_TOPK_CANDIDATES 1024   /* top-k rows with more kept tokens use the dense path */
@@ -108,10 +116,9 @@ enum {
 
 /* spec_verify_create flags. */
 enum {
-  SV_CREATE_TOPK = 1u << 0,   /* reserve top-k candidate storage (needed for top_k != NULL)  */
+  SV_CREATE_TOPK = 1u << 0,    /* reserve top-k candidate storage (needed for top_k != NULL)  */
   SV_CREATE_LM_HEAD = 1u << 1 /* reserve the LM-head path's tile records (spec_verify_lm_head) */
 };
-
 /*
  * Create a context sized for calls with at most max_rows target rows,
  * max_reqs requests, max_k drafts per request (<= SV_MAX_DRAFTS) and a
@@ -121,11 +128,11 @@ enum {
  * candidates per row).  *out receives the context.  Errors: SV_EINVAL (NULL
  * out, non-positive size), SV_ECAPACITY (max_k > SV_MAX_DRAFTS), SV_EHIP.
  */
-int spec_verify_create(sv_ctx **out, int32_t max_rows, int32_t max_reqs, int32_t max_k,
+SV_API int spec_verify_create(sv_ctx **out, int32_t max_rows, int32_t max_reqs, int32_t max_k,
                        int32_t max_vocab, uint32_t flags);
 
 /* Free a context (synchronises the device first).  NULL is ignored. */
-void spec_verify_destroy(sv_ctx *ctx);
+SV_API void spec_verify_destroy(sv_ctx *ctx);
 
 typedef struct sv_verify_args {
   const void *target_logits;        /* [num_rows, logits_row_stride], dtype logits_dtype    */
@@ -191,7 +198,7 @@ typedef struct sv_verify_args {
  * is done by the call's last kernels (one launch fewer than calling
  * spec_post_update afterwards; the same results).
  */
-int spec_verify_run(sv_ctx *ctx, const sv_verify_args *args, hipStream_t stream);
+SV_API int spec_verify_run(sv_ctx *ctx, const sv_verify_args *args, hipStream_t stream);
 
 struct sv_post_update_args {
   const int32_t *idx_mapping;   /* [num_reqs] batch row -> state slot                     */
@@ -219,7 +226,7 @@ typedef struct sv_post_update_args sv_post_update_args;
  * must not share a slot (counts stay exact, last_sampled is then either one).
  * Errors: SV_EINVAL, SV_EHIP.
  */
-int spec_post_update(sv_ctx *ctx, const sv_post_update_args *args, hipStream_t stream);
+SV_API int spec_post_update(sv_ctx *ctx, const sv_post_update_args *args, hipStream_t stream);
 
 /*
  * Draft-side sampling (NEXT row of the verify step; "speculative decoding in
@@ -255,7 +262,7 @@ typedef struct sv_draft_args {
   int32_t step;                 /* draft position sampled by this call, >= 0              */
 } sv_draft_args;
 
-int spec_draft_sample(sv_ctx *ctx, const sv_draft_args *args, hipStream_t stream);
+SV_API int spec_draft_sample(sv_ctx *ctx, const sv_draft_args *args, hipStream_t stream);
 
 /*
  * Host helper for synthetic acceptance ("speculative decoding in vLLM", 7.2):
@@ -265,7 +272,7 @@ int spec_draft_sample(sv_ctx *ctx, const sv_draft_args *args, hipStream_t stream
  * then the fractional part, then 0.  rates is a HOST array of k floats.
  * Returns SV_OK, or SV_EINVAL (L out of range or not finite, k < 0, NULL).
  */
-int spec_verify_synthetic_rates(float mean_length, int32_t k, float *rates);
+SV_API int spec_verify_synthetic_rates(float mean_length, int32_t k, float *rates);
 
 /*
  * Verify step on LM-head logits (NEXT row of the verify step).  The target
@@ -322,10 +329,10 @@ typedef struct sv_lm_head_args {
                                 /* this step inside the call, as in sv_verify_args          */
 } sv_lm_head_args;
 
-int spec_verify_lm_head(sv_ctx *ctx, const sv_lm_head_args *args, hipStream_t stream);
+SV_API int spec_verify_lm_head(sv_ctx *ctx, const sv_lm_head_args *args, hipStream_t stream);
 
 /* Static string for a return code. */
-const char *spec_verify_strerror(int status);
+SV_API const char *spec_verify_strerror(int status);
 
 /*
  * Synchronise `stream`, copy the device error word into *host_flags (a host
@@ -333,11 +340,12 @@ const char *spec_verify_strerror(int status);
  * some were, SV_EINVAL / SV_EHIP on failure.  For tests and debugging: it
  * blocks the host.
  */
-int spec_verify_read_error(sv_ctx *ctx, uint32_t *host_flags, hipStream_t stream);
+SV_API int spec_verify_read_error(sv_ctx *ctx, uint32_t *host_flags, hipStream_t stream);
 
 /*
  * Measurement.  spec_verify_profile_start makes the next `max_calls` calls of
- * spec_verify_run launch the streaming statistics kernel and the request
+ * spec_verify_run launch their first pass over the target rows (the top-k
+ * pass when top-k is on, else the streaming statistics kernel) and the request
  * epilogue kernel (of spec_verify_lm_head: the fused LM-head GEMM and its
  * request kernel) with start/stop HIP events that the launch stamps at the
  * kernel's own start and end on the call's stream (hipExtLaunchKernel), so an
@@ -352,8 +360,28 @@ int spec_verify_read_error(sv_ctx *ctx, uint32_t *host_flags, hipStream_t stream
  * SV_EINVAL (null context, max_calls < 1 or > 65536, nothing started) or
  * SV_EHIP.
  */
-int spec_verify_profile_start(sv_ctx *ctx, int32_t max_calls);
-int spec_verify_profile_read(sv_ctx *ctx, float *stream_ms, float *epilogue_ms, int32_t *n_calls);
+SV_API int spec_verify_profile_start(sv_ctx *ctx, int32_t max_calls);
+SV_API int spec_verify_profile_read(sv_ctx *ctx, float *stream_ms, float *epilogue_ms, int32_t *n_calls);
+
+/*
+ * Debug and test entry points: the library's own random stream and race noise,
+ * value for value, so that tests can compare them directly with the published
+ * Philox4x32-10 known-answer vectors (Salmon et al., SC'11) and with an
+ * independent implementation.  Neither needs a context.
+ *
+ * spec_verify_debug_philox: out[i] = Philox4x32-10(counters[i], key) for i < n,
+ * where counters and out are DEVICE arrays of n blocks of four uint32 words
+ * (word 0 first), both 16-byte aligned, and key is split as (key lo, key hi)
+ * like the seed of sv_verify_args.
+ * spec_verify_debug_exp_noise: out[i] = the fp32 Exp(1) noise E = -ln U that
+ * the races use for the Philox word words[i], U = (words[i] >> 8) * 2^-24
+ * (+inf for U = 0); words and out are DEVICE arrays of n elements.
+ * Both are stream-ordered.  Returns SV_OK, SV_EINVAL (n < 0, a null or
+ * misaligned pointer with n > 0) or SV_EHIP.
+ */
+SV_API int spec_verify_debug_philox(const uint32_t *counters, int64_t n, uint64_t key, uint32_t *out,
+                             hipStream_t stream);
+SV_API int spec_verify_debug_exp_noise(const uint32_t *words, int64_t n, float *out, hipStream_t stream);
 
 #ifdef __cplusplus
 }

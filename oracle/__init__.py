@@ -77,6 +77,8 @@ def lib():
         f32, f64 = ctypes.c_float, ctypes.c_double
         L.orc_philox4x32_10.argtypes = [P, P, P]
         L.orc_philox4x32_10.restype = None
+        L.orc_philox4x32_10_n.argtypes = [P, i64, P, P]
+        L.orc_philox4x32_10_n.restype = None
         L.orc_word.argtypes = [u64, u32, u32, u32, u32]
         L.orc_word.restype = u32
         L.orc_uniform_accept.argtypes = [u32]
@@ -155,6 +157,15 @@ def philox4x32_10(ctr, key) -> np.ndarray:
     k = np.asarray(key, dtype=np.uint32)
     out = np.zeros(4, dtype=np.uint32)
     lib().orc_philox4x32_10(_ptr(c), _ptr(k), _ptr(out))
+    return out
+
+
+def philox4x32_10_n(ctr, key) -> np.ndarray:
+    """Philox blocks of counters [n, 4] (uint32) under one key [2]; returns [n, 4] uint32."""
+    c = np.ascontiguousarray(ctr, dtype=np.uint32).reshape(-1, 4)
+    k = np.asarray(key, dtype=np.uint32)
+    out = np.zeros_like(c)
+    lib().orc_philox4x32_10_n(_ptr(c), c.shape[0], _ptr(k), _ptr(out))
     return out
 
 

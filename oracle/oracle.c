@@ -55,6 +55,11 @@ void orc_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t ou
   out[3] = x3;
 }
 
+/* n blocks at once (counters and outputs [n][4]), same key: a loop over the above. */
+void orc_philox4x32_10_n(const uint32_t *ctr, int64_t n, const uint32_t key[2], uint32_t *out) {
+  for (int64_t i = 0; i < n; ++i) orc_philox4x32_10(ctr + 4 * i, key, out + 4 * i);
+}
+
 /* Counter layout: (idx >> 2, target row g, tag, call offset); word idx & 3.
  * Key: the two 32-bit halves of the 64-bit seed. */
 uint32_t orc_word(uint64_t seed, uint32_t offset, uint32_t g, uint32_t tag, uint32_t idx) {
@@ -155,7 +160,7 @@ void orc_frequency_presence_penalty(float *z, const int32_t *counts, int32_t V, 
   }
 }
 
-static const double *g_sort_p; /* qsort context: probabilities, descending */
+static _Thread_local const double *g_sort_p; /* qsort context: probabilities, descending (per thread) */
 static int cmp_idx_p_desc(const void *a, const void *b) {
   int32_t ia = *(const int32_t *)a, ib = *(const int32_t *)b;
   double pa = g_sort_p[ia], pb = g_sort_p[ib];

@@ -92,6 +92,8 @@ typedef struct orc_batch_opts {
 
 /* ---- random stream ----------------------------------------------------- */
 void orc_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]);
+/* n blocks, counters and outputs [n][4], one key. */
+void orc_philox4x32_10_n(const uint32_t *ctr, int64_t n, const uint32_t key[2], uint32_t *out);
 /* Word idx&3 of Philox(counter = (idx>>2, g, tag, offset), key = (seed lo, seed hi)). */
 uint32_t orc_word(uint64_t seed, uint32_t offset, uint32_t g, uint32_t tag, uint32_t idx);
 double orc_uniform_accept(uint32_t w); /* ((w>>8)+1) * 2^-24, in (0, 1] */

@@ -11,7 +11,8 @@ Entry points (same names as the C ABI):
     spec_verify_create, spec_verify_destroy, spec_verify_run,
     spec_post_update, spec_verify_strerror, spec_verify_read_error,
     spec_verify_synthetic_rates, spec_verify_profile_start, spec_verify_profile_read,
-    spec_draft_sample, spec_verify_lm_head
+    spec_draft_sample, spec_verify_lm_head, spec_verify_debug_philox,
+    spec_verify_debug_exp_noise
 """
 from __future__ import annotations
 
@@ -26,6 +27,7 @@ __all__ = [
     "spec_verify_create", "spec_verify_destroy", "spec_verify_run", "spec_post_update",
     "spec_verify_strerror", "spec_verify_read_error", "spec_verify_synthetic_rates",
     "DraftArgs", "spec_draft_sample", "SV_CREATE_LM_HEAD", "LmHeadArgs", "spec_verify_lm_head",
+    "spec_verify_debug_philox", "spec_verify_debug_exp_noise",
 ]
 
 SV_OK, SV_EINVAL, SV_ECAPACITY, SV_EDTYPE, SV_EHIP, SV_EINPUT = 0, -1, -2, -3, -4, -5
@@ -192,6 +194,10 @@ def lib() -> ctypes.CDLL:
         L.spec_verify_profile_start.restype = ctypes.c_int
         L.spec_verify_profile_read.argtypes = [P, P, P, ctypes.POINTER(ctypes.c_int32)]
         L.spec_verify_profile_read.restype = ctypes.c_int
+        L.spec_verify_debug_philox.argtypes = [P, ctypes.c_int64, ctypes.c_uint64, P, P]
+        L.spec_verify_debug_philox.restype = ctypes.c_int
+        L.spec_verify_debug_exp_noise.argtypes = [P, ctypes.c_int64, P, P]
+        L.spec_verify_debug_exp_noise.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -527,3 +533,37 @@ def spec_verify_profile_read(ctx, max_calls: int):
     if st != SV_OK:
         raise SpecVerifyError(st, "spec_verify_profile_read")
     return list(a[:n.value]), list(b[:n.value])
+
+
+def spec_verify_debug_philox(counters, key: int, out=None, stream=None):
+    """Philox4x32-10 blocks of the library for int32/uint32 device counters [n, 4]
+    under a 64-bit key; returns (or fills) an int32 [n, 4] tensor of the words."""
+    import torch
+    if counters.dim() != 2 or counters.shape[1] != 4:
+        raise ValueError("counters must be [n, 4]")
+    _dev(counters, counters.dtype, "counters")
+    if counters.element_size() != 4:
+        raise TypeError("counters must hold 32-bit words")
+    if out is None:
+        out = torch.empty((counters.shape[0], 4), dtype=torch.int32, device=counters.device)
+    _dev(out, torch.int32, "out", 2)
+    st = lib().spec_verify_debug_philox(_ptr(counters), counters.shape[0], key & 0xFFFFFFFFFFFFFFFF, _ptr(out),
+                                        _stream_handle(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "spec_verify_debug_philox")
+    return out
+
+
+def spec_verify_debug_exp_noise(words, out=None, stream=None):
+    """The library's fp32 Exp(1) noise for 32-bit device words [n]; returns a float32 [n] tensor."""
+    import torch
+    _dev(words, words.dtype, "words", 1)
+    if words.element_size() != 4:
+        raise TypeError("words must be 32-bit")
+    if out is None:
+        out = torch.empty(words.shape[0], dtype=torch.float32, device=words.device)
+    _dev(out, torch.float32, "out", 1)
+    st = lib().spec_verify_debug_exp_noise(_ptr(words), words.shape[0], _ptr(out), _stream_handle(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "spec_verify_debug_exp_noise")
+    return out

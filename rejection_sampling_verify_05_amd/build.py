@@ -12,10 +12,11 @@ OUTPUT = os.path.join(HERE, "libspecverify.so")
 # -ffp-contract=off: every fp32 operation on logits rounds once (the penalty and
 # the greedy/top-k comparisons must match IEEE arithmetic bit for bit).
 # -packed-fp32-ops: no v_pk_*_f32 instructions.
+# -fvisibility=hidden: only the C ABI (SV_API in include/specverify.h) is exported.
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-Wall", "-Wno-unused-function",
+    "-Wall", "-Wno-unused-function", "-fvisibility=hidden",
 ]
 
 

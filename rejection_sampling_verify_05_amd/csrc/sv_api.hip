@@ -102,7 +102,8 @@ extern "C" int spec_verify_create(sv_ctx **out, int32_t max_rows, int32_t max_re
     ok = hipMemset(c->res_req, 0, reqs * sizeof(int4)) == hipSuccess &&
          hipMemset(c->zeros, 0, (reqs + 1) * sizeof(int32_t)) == hipSuccess &&
          hipMemset(c->res_list, 0, sizeof(int)) == hipSuccess &&
-         hipMemset(c->err, 0, sizeof(unsigned int)) == hipSuccess && hipDeviceSynchronize() == hipSuccess;
+         hipMemset(c->err, 0, sizeof(unsigned int)) == hipSuccess &&
+         hipDeviceSynchronize() == hipSuccess;
   int ncu = 0;
   if (ok) ok = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, c->device) == hipSuccess;
   if (!ok) {
@@ -264,10 +265,15 @@ extern "C" int spec_verify_run(sv_ctx *ctx, const sv_verify_args *a, hipStream_t
     if (sv::launch_zero_count(ctx->res_list, stream) != hipSuccess) return SV_EHIP;
     ctx->res_dirty = false;
   }
-  if (p.has_topk && sv::launch_topk(p, stream) != hipSuccess) return SV_EHIP;
+  // Measurement: the first pass over the rows carries the first two events --
+  // the top-k pass when top-k is on (the statistics pass then skips the rows
+  // it reduced to candidate lists), else the statistics pass.
+  hipEvent_t e0 = ev ? ev[0] : nullptr, e1 = ev ? ev[1] : nullptr;
+  if (p.has_topk && sv::launch_topk(p, stream, e0, e1) != hipSuccess) return SV_EHIP;
+  if (p.has_topk) e0 = e1 = nullptr;
   const bool resid = p.draft_probs != nullptr || p.draft_logits != nullptr;
   ctx->res_dirty = resid;  // until the residual race has zeroed the count
-  if (sv::launch_stats(p, stream, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr) != hipSuccess) return SV_EHIP;
+  if (sv::launch_stats(p, stream, e0, e1) != hipSuccess) return SV_EHIP;
   if (p.has_topp) {
     // Top-p on dense rows, then their statistics again under the threshold
     // (general pass, only the marked rows).
@@ -527,4 +533,19 @@ extern "C" int spec_verify_profile_read(sv_ctx *ctx, float *stream_ms, float *ep
   *n_calls = st == SV_OK ? n : 0;
   free_events(ctx);
   return st;
+}
+
+extern "C" int spec_verify_debug_philox(const uint32_t *counters, int64_t n, uint64_t key, uint32_t *out,
+                                        hipStream_t stream) {
+  if (n < 0) return SV_EINVAL;
+  if (n == 0) return SV_OK;
+  if (!counters || !out || (uintptr_t)counters % 16 != 0 || (uintptr_t)out % 16 != 0) return SV_EINVAL;
+  return sv::launch_dbg_philox(counters, n, key, out, stream) == hipSuccess ? SV_OK : SV_EHIP;
+}
+
+extern "C" int spec_verify_debug_exp_noise(const uint32_t *words, int64_t n, float *out, hipStream_t stream) {
+  if (n < 0) return SV_EINVAL;
+  if (n == 0) return SV_OK;
+  if (!words || !out) return SV_EINVAL;
+  return sv::launch_dbg_noise(words, n, out, stream) == hipSuccess ? SV_OK : SV_EHIP;
 }

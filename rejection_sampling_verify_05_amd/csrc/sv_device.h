@@ -159,12 +159,15 @@ __device__ __forceinline__ ArgMax wave_argmax(ArgMax a) {
   return ArgMax{rd(a.s, 63), __builtin_amdgcn_readlane(a.i, 63)};
 }
 
-// Block-wide (256 threads) reductions; every thread gets the result.
+// Block-wide reductions over every wave of the workgroup (up to kMaxBlockWaves);
+// every thread gets the result.
+constexpr int kMaxBlockWaves = 16;
 struct BlockScratch {
-  float s[kWaves];
-  int i[kWaves];
-  float f[kWaves];
+  float s[kMaxBlockWaves];
+  int i[kMaxBlockWaves];
+  float f[kMaxBlockWaves];
 };
+__device__ __forceinline__ int block_waves() { return (int)(blockDim.x >> 6); }
 
 __device__ __forceinline__ ArgMax block_argmax(ArgMax a, BlockScratch &sh) {
   a = wave_argmax(a);
@@ -176,8 +179,7 @@ __device__ __forceinline__ ArgMax block_argmax(ArgMax a, BlockScratch &sh) {
   }
   __syncthreads();
   ArgMax b{sh.s[0], sh.i[0]};
-#pragma unroll
-  for (int k = 1; k < kWaves; ++k) {
+  for (int k = 1; k < block_waves(); ++k) {
     ArgMax o{sh.s[k], sh.i[k]};
     if (better(o, b)) b = o;
   }
@@ -190,8 +192,7 @@ __device__ __forceinline__ float block_sum(float v, BlockScratch &sh) {
   if ((threadIdx.x & 63) == 0) sh.f[threadIdx.x >> 6] = v;
   __syncthreads();
   float t = 0.f;
-#pragma unroll
-  for (int k = 0; k < kWaves; ++k) t += sh.f[k];
+  for (int k = 0; k < block_waves(); ++k) t += sh.f[k];
   return t;
 }
 
@@ -201,8 +202,7 @@ __device__ __forceinline__ float block_max(float v, BlockScratch &sh) {
   if ((threadIdx.x & 63) == 0) sh.f[threadIdx.x >> 6] = v;
   __syncthreads();
   float t = sh.f[0];
-#pragma unroll
-  for (int k = 1; k < kWaves; ++k) t = fmaxf(t, sh.f[k]);
+  for (int k = 1; k < block_waves(); ++k) t = fmaxf(t, sh.f[k]);
   return t;
 }
 

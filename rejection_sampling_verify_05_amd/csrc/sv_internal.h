@@ -155,7 +155,7 @@ struct PostParams {
 };
 
 // Launchers (sv_kernels.hip).  Return the hipError_t of the last launch.
-hipError_t launch_topk(const Params &p, hipStream_t s);
+hipError_t launch_topk(const Params &p, hipStream_t s, hipEvent_t t0, hipEvent_t t1);
 hipError_t launch_topp(const Params &p, hipStream_t s);
 // t0, t1: optional events stamped at the kernel's start and end (may be null).
 hipError_t launch_stats(const Params &p, hipStream_t s, hipEvent_t t0, hipEvent_t t1);
@@ -166,9 +166,18 @@ hipError_t launch_zero_count(int *count, hipStream_t s);
 hipError_t launch_dbg_probs(const Params &p, hipStream_t s);
 hipError_t launch_draft_race(const Params &p, const DraftOut &o, hipStream_t s);
 hipError_t launch_post_update(const PostParams &p, hipStream_t s);
+// Debug: Philox blocks of n counters (uint4 each) under one key; Exp(1) noise of n words.
+hipError_t launch_dbg_philox(const uint32_t *ctr, int64_t n, uint64_t key, uint32_t *out, hipStream_t s);
+hipError_t launch_dbg_noise(const uint32_t *words, int64_t n, float *out, hipStream_t s);
 // Resident stats workgroups per CU (occupancy query); kind 0 general pass,
 // 1 fast pass, 2 fast pass with penalties.
 int stats_blocks_per_cu(int dtype, int kind);
+// The call needs no top-k, top-p, penalties or draft distributions and has at
+// most four rows per request (the plain epilogue).
+inline bool plain_call(const Params &p) {
+  return !p.has_topk && !p.has_topp && p.rep_penalty == nullptr && p.freq_penalty == nullptr &&
+         p.pres_penalty == nullptr && p.draft_probs == nullptr && p.draft_logits == nullptr && p.out_stride <= kWaves;
+}
 constexpr int kSliceRows = 4;  // rows a stats slice may span (kRowCache)
 
 }  // namespace sv

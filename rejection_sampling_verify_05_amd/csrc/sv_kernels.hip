@@ -246,9 +246,22 @@ struct Layout<0> {
 // M_c > 0, then token x* = argmax_{x in c*} w_x / E(g, 2, x) over w_x > 0.
 // Scores are fp32 (race_score); ties go to the lowest index.
 // ---------------------------------------------------------------------------
-constexpr int kTabCache = 2048;  // chunk-table entries the epilogue keeps in LDS
+constexpr int kTabCache = 2048;  // chunk-table entries the epilogue kernel keeps in LDS
 
-struct EpiShared {
+// Candidate lists of compact (top-k) rows, staged in LDS by the epilogue.
+template <bool CAND>
+struct CandBuf {
+  float cw[kCandCap];  // candidate weights
+  int ci[kCandCap];    // candidate token ids
+};
+template <>
+struct CandBuf<false> {};
+
+// LDS of the request epilogue: TC chunk-table entries cached; CAND: room for
+// the candidate lists of compact rows (not needed by the plain variant).
+template <int TC, bool CAND>
+struct EpiSharedT {
+  static constexpr int kCache = TC;
   BlockScratch red;
   float m[kMaxDrafts + 1];
   float s[kMaxDrafts + 1];
@@ -269,13 +282,11 @@ struct EpiShared {
   int cd[kWaves];            // the draft token's chunk when excluded, else -1
   float rcd[kWaves];         // 1/E of that chunk in the chunk race
   union {
-    float2 tab[kTabCache];  // dense rows: chunk tables of the request's rows
-    struct {
-      float cw[kCandCap];   // compact rows: candidate weights
-      int ci[kCandCap];     // compact rows: candidate token ids
-    } cand;
+    float2 tab[TC];  // dense rows: chunk tables of the request's rows
+    CandBuf<CAND> cand;
   } u;
 };
+using EpiShared = EpiSharedT<kTabCache, true>;
 
 // Block-level chunk race (all threads call it); thread t takes chunks t,
 // t + 256, ...; W(c) >= 0.  Returns -1 if no chunk has positive weight.
@@ -341,7 +352,7 @@ __device__ __forceinline__ void fused_post_update(const Params &p, int r, int K,
     if (threadIdx.x == 0) atomicOr(p.err, SV_ERR_SLOT);
     return;
   }
-  for (int i = threadIdx.x; i <= j; i += kThreads) {
+  for (int i = threadIdx.x; i <= j; i += blockDim.x) {  // each output counted once
     const int tok = i < j ? draft(i) : x;
     if (tok >= 0 && tok < p.V) atomicAdd(&p.pu_counts[(int64_t)s * p.V + tok], 1);
   }
@@ -502,25 +513,28 @@ __device__ __forceinline__ ArgMax wave_chunk_race(const Params &p, int g, EF ent
 
 // Token race over chunk c of row g whose raw logits are in LDS (zs, token
 // order): weights exp2(fma(z', a, -hi)) on the processed z' (hi = a r_c; a
-// factor common to the chunk cancels), token `skip` left out.  Thread t takes
-// tokens 4t..4t+3 (one Philox block).  All threads call it; -1 if no token has
+// factor common to the chunk cancels), token `skip` left out.  Thread t < 256
+// takes tokens 4t..4t+3 (one Philox block); further threads of a larger
+// workgroup only join the reduction.  All threads call it; -1 if no token has
 // weight.
 __device__ __forceinline__ int block_token_race(const Params &p, int g, int c, const float *zs, const Proc &pr,
                                                 float a, float hi, int skip, BlockScratch &red,
                                                 uint32_t tag = kTagToken) {
-  const int t4 = 4 * threadIdx.x;
-  const int x0 = c * kChunk + t4;
-  const uint4 w4 = rng_block(p, (uint32_t)x0 >> 2, (uint32_t)g, tag);
-  const float4 z4 = *reinterpret_cast<const float4 *>(zs + t4);
-  const float zz[4] = {z4.x, z4.y, z4.z, z4.w};
   ArgMax best{-1.0f, 0x7FFFFFFF};
+  if (threadIdx.x < kThreads) {
+    const int t4 = 4 * threadIdx.x;
+    const int x0 = c * kChunk + t4;
+    const uint4 w4 = rng_block(p, (uint32_t)x0 >> 2, (uint32_t)g, tag);
+    const float4 z4 = *reinterpret_cast<const float4 *>(zs + t4);
+    const float zz[4] = {z4.x, z4.y, z4.z, z4.w};
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int x = x0 + k;
-    const bool ok = x < p.V && x != skip;
-    const float wx = ok ? exp2_acc(__builtin_fmaf(apply_proc(zz[k], min(x, p.V - 1), pr), a, -hi)) : 0.0f;
-    const ArgMax o{race_score(wx, pick(w4, k)), x};
-    if (wx > 0.0f && better(o, best)) best = o;
+    for (int k = 0; k < 4; ++k) {
+      const int x = x0 + k;
+      const bool ok = x < p.V && x != skip;
+      const float wx = ok ? exp2_acc(__builtin_fmaf(apply_proc(zz[k], min(x, p.V - 1), pr), a, -hi)) : 0.0f;
+      const ArgMax o{race_score(wx, pick(w4, k)), x};
+      if (wx > 0.0f && better(o, best)) best = o;
+    }
   }
   const ArgMax b = block_argmax(best, red);
   return b.s < 0.0f ? -1 : b.i;
@@ -624,7 +638,8 @@ __device__ __forceinline__ void spec_draft_record(const Params &p, const Req &q,
 }
 
 // Moves a wave's speculative chunks and race state for row i to LDS slot `slot`.
-__device__ __forceinline__ void spec_publish(const RowSpec &rs, int slot, EpiShared &sh) {
+template <class SH>
+__device__ __forceinline__ void spec_publish(const RowSpec &rs, int slot, SH &sh) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
@@ -644,9 +659,9 @@ __device__ __forceinline__ void spec_publish(const RowSpec &rs, int slot, EpiSha
 // Final race of row j from LDS slot `slot` (all threads): the chunk of d
 // competes with its mass without d (sx); if nothing is left without d, the race
 // is over p_j.
-template <class EF>
+template <class EF, class SH>
 __device__ __forceinline__ int spec_finish(const Params &p, const Req &q, int j, int dj, float m, float sx,
-                                           const Proc &pr, EF ent, int slot, EpiShared &sh) {
+                                           const Proc &pr, EF ent, int slot, SH &sh) {
   const int gs = q.g0 + j;
   const float a = q.a;
   ArgMax win{sh.w1s[slot], sh.w1c[slot]};
@@ -685,8 +700,9 @@ __device__ __forceinline__ int spec_slot(int i, int nrow) {
 // PLAIN: the call has no top-k, top-p, penalties or draft distributions and
 // at most four rows per request; the settings they would read are then
 // constants, and their paths compile away.
-template <bool PLAIN>
-__device__ __forceinline__ void request_epilogue(const Params &p, const Req &q_in, EpiShared &sh) {
+template <bool PLAIN, class SH>
+__device__ __forceinline__ void request_epilogue(const Params &p, const Req &q_in, SH &sh) {
+  constexpr int TC = SH::kCache;
   Req q = q_in;
   if (PLAIN) {
     q.proc.counts = nullptr;
@@ -722,11 +738,11 @@ __device__ __forceinline__ void request_epilogue(const Params &p, const Req &q_i
     sh.tau[i] = (st == kRowDense) ? kNegInf : p.cand_tau[g];
     sh.d[i] = i < K ? p.draft_ids[q.c0 + i] : -1;
   }
-  const bool cached = nrow * p.NC <= kTabCache;
-  float2 tv[kTabCache / kThreads];
+  const bool cached = nrow * p.NC <= TC;
+  float2 tv[TC / kThreads];
   if (cached) {  // all table loads issued first
 #pragma unroll
-    for (int m = 0; m < kTabCache / kThreads; ++m) {
+    for (int m = 0; m < TC / kThreads; ++m) {
       const int t = tid + m * kThreads;
       const int i = t / p.NC, c = t - i * p.NC;
       tv[m] = t < nrow * p.NC ? p.chunk_tab[(int64_t)(q.g0 + i) * p.nc_stride + c] : make_float2(0.0f, 0.0f);
@@ -738,7 +754,7 @@ __device__ __forceinline__ void request_epilogue(const Params &p, const Req &q_i
   const ChunkNoise cn = chunk_noise(p, q.g0 + min(srow, nrow - 1));
   if (cached) {
 #pragma unroll
-    for (int m = 0; m < kTabCache / kThreads; ++m) {
+    for (int m = 0; m < TC / kThreads; ++m) {
       const int t = tid + m * kThreads;
       if (t < nrow * p.NC) sh.u.tab[t] = tv[m];
     }
@@ -886,6 +902,7 @@ __device__ __forceinline__ void request_epilogue(const Params &p, const Req &q_i
   const int st = PLAIN ? kRowDense : sh.state[j];
   const float a = q.a;
 
+  if constexpr (!PLAIN) {
   if (st >= 0) {
     // Compact top-k row: the race runs over the kept tokens only.
     __syncthreads();  // the LDS chunk-table cache is reused for the candidates
@@ -915,6 +932,7 @@ __device__ __forceinline__ void request_epilogue(const Params &p, const Req &q_i
     if (tid == 0) p.out_tokens[out_j] = x;
     fused_post_update(p, r, K, j, x, accepted);
     return;
+  }
   }
 
   if (rejected && q.has_q) {
@@ -1449,6 +1467,7 @@ __global__ __launch_bounds__((kFastThreads<DT, PEN>)) void stats_fast_kernel(Par
       load(s, gs[s], cs[s]);
     }
   }
+
 }
 
 // ---------------------------------------------------------------------------
@@ -2511,6 +2530,21 @@ __global__ __launch_bounds__(kThreads) void post_update_kernel(PostParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Debug: the library's own random stream and Exp(1) noise, value for value
+// (tests compare them with the published known-answer vectors and the oracle).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void dbg_philox_kernel(const uint4 *ctr, int64_t n, uint32_t k0, uint32_t k1,
+                                                             uint4 *out) {
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads)
+    out[i] = philox10(ctr[i], k0, k1);
+}
+
+__global__ __launch_bounds__(kThreads) void dbg_noise_kernel(const uint32_t *words, int64_t n, float *out) {
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads)
+    out[i] = exp_noise(words[i]);
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -2611,13 +2645,6 @@ hipError_t launch_draft_race(const Params &p, const DraftOut &o, hipStream_t s) 
   return hipGetLastError();
 }
 
-hipError_t launch_topk(const Params &p, hipStream_t s) {
-  if (p.dtype == 1)
-    topk_kernel<1><<<dim3(p.R), dim3(kThreads), 0, s>>>(p);
-  else
-    topk_kernel<0><<<dim3(p.R), dim3(kThreads), 0, s>>>(p);
-  return hipGetLastError();
-}
 
 hipError_t launch_topp(const Params &p, hipStream_t s) {
   if (p.has_topk) {
@@ -2641,6 +2668,12 @@ hipError_t launch_timed(const void *fn, dim3 grid, const Params &p, hipStream_t 
   Params arg = p;
   void *args[] = {&arg};
   return hipExtLaunchKernel(fn, grid, dim3(threads), args, 0, s, t0, t1, 0);
+}
+
+hipError_t launch_topk(const Params &p, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+  const void *fn = p.dtype == 1 ? reinterpret_cast<const void *>(&topk_kernel<1>)
+                                : reinterpret_cast<const void *>(&topk_kernel<0>);
+  return launch_timed(fn, dim3((unsigned)p.R), p, s, t0, t1);
 }
 
 hipError_t launch_stats(const Params &p, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
@@ -2673,10 +2706,7 @@ int stats_blocks_per_cu(int dtype, int kind) {
 }
 
 hipError_t launch_epilogue(const Params &p, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
-  // Without top-k, top-p, penalties or draft distributions, K <= 3: the plain variant.
-  const bool plain = !p.has_topk && !p.has_topp && p.rep_penalty == nullptr && p.freq_penalty == nullptr &&
-                     p.pres_penalty == nullptr && p.draft_probs == nullptr && p.draft_logits == nullptr &&
-                     p.out_stride <= kWaves;
+  const bool plain = plain_call(p);
   const void *fn = plain ? reinterpret_cast<const void *>(&epilogue_kernel<true>)
                          : reinterpret_cast<const void *>(&epilogue_kernel<false>);
   return launch_timed(fn, dim3((unsigned)p.B), p, s, t0, t1);
@@ -2709,6 +2739,20 @@ hipError_t launch_dbg_probs(const Params &p, hipStream_t s) {
 hipError_t launch_post_update(const PostParams &p, hipStream_t s) {
   const int64_t total = (int64_t)p.B * p.tokens_stride;
   post_update_kernel<<<dim3((unsigned)((total + kThreads - 1) / kThreads)), dim3(kThreads), 0, s>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_dbg_philox(const uint32_t *ctr, int64_t n, uint64_t key, uint32_t *out, hipStream_t s) {
+  const int64_t blocks = (n + kThreads - 1) / kThreads;
+  dbg_philox_kernel<<<dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(kThreads), 0, s>>>(
+      reinterpret_cast<const uint4 *>(ctr), n, (uint32_t)(key & 0xFFFFFFFFu), (uint32_t)(key >> 32),
+      reinterpret_cast<uint4 *>(out));
+  return hipGetLastError();
+}
+
+hipError_t launch_dbg_noise(const uint32_t *words, int64_t n, float *out, hipStream_t s) {
+  const int64_t blocks = (n + kThreads - 1) / kThreads;
+  dbg_noise_kernel<<<dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(kThreads), 0, s>>>(words, n, out);
   return hipGetLastError();
 }
 

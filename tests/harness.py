@@ -57,7 +57,9 @@ def ctx_for(inp, extra_rows=0):
 
 def run_gpu(ctx: Ctx, inp: dict, seed=0, offset=0, dbg_probs=False, out_stride=None,
             stream=None):
-    """One spec_verify_run; returns host numpy outputs."""
+    """One spec_verify_run; returns host numpy outputs.  dbg_probs: True (every
+    row's probabilities come back as "probs"), or a list of target rows (only
+    those come back, as "probs_rows")."""
     B, D, V = inp["B"], inp["D"], inp["V"]
     dev = inp["logits"].device
     if out_stride is None:
@@ -66,7 +68,8 @@ def run_gpu(ctx: Ctx, inp: dict, seed=0, offset=0, dbg_probs=False, out_stride=N
     ns = torch.full((B,), -7, dtype=torch.int32, device=dev)
     nr = torch.full((B,), -7, dtype=torch.int32, device=dev)
     pd = torch.full((max(D, 1),), -7.0, dtype=torch.float32, device=dev)
-    probs = torch.full((inp["R"], V), -7.0, dtype=torch.float32, device=dev) if dbg_probs else None
+    probs = torch.full((inp["R"], V), -7.0, dtype=torch.float32, device=dev) if dbg_probs is not None and \
+        dbg_probs is not False else None
     sv.spec_verify_run(ctx.h, inp["logits"], inp["draft_ids"], inp["cu"], inp["temperature"],
                        out, ns, nr, draft_probs=inp["draft_probs"], top_k=inp["top_k"],
                        rep_penalty=inp["rep_penalty"], idx_mapping=inp["idx_mapping"],
@@ -82,7 +85,10 @@ def run_gpu(ctx: Ctx, inp: dict, seed=0, offset=0, dbg_probs=False, out_stride=N
     res = dict(tokens=out.cpu().numpy(), num_sampled=ns.cpu().numpy(),
                num_rejected=nr.cpu().numpy(), p_draft=pd[:D].cpu().numpy(), err=err)
     if probs is not None:
-        res["probs"] = probs.cpu().numpy()
+        if dbg_probs is True:
+            res["probs"] = probs.cpu().numpy()
+        else:  # only these target rows come back to the host
+            res["probs_rows"] = {int(r): probs[int(r)].cpu().numpy() for r in dbg_probs}
     return res
 
 
@@ -139,11 +145,34 @@ def check_draft_tokens(inp: dict, q_gpu, seed=0, offset=0, C=oracle.RACE_CHUNK, 
     return n_margin, bad
 
 
+class HostInputs:
+    """Host copies of one verify call's inputs, taken once (bf16 logits as their
+    bit patterns), so that the oracle can run over many requests in threads."""
+
+    def __init__(self, inp: dict):
+        lg = inp["logits"]
+        self.logits = (lg.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+                       if lg.dtype == torch.bfloat16 else lg.contiguous().cpu().numpy())
+        self.cu = inp["cu"].cpu().numpy()
+        self.draft_ids = inp["draft_ids"].cpu().numpy()
+        self.temperature = inp["temperature"].cpu().numpy()
+        self.draft_probs = None if inp["draft_probs"] is None else inp["draft_probs"].float().cpu().numpy()
+        tens = lambda k: None if inp.get(k) is None else inp[k].cpu().numpy()
+        self.top_k, self.rep_penalty = tens("top_k"), tens("rep_penalty")
+        self.freq, self.pres, self.top_p = tens("freq"), tens("pres"), tens("top_p")
+        self.idx_mapping = inp["idx_mapping"].cpu().numpy()
+        self.counts = inp["counts"].cpu().numpy() if has_penalty(inp) else None
+
+
 class OracleRequest:
     """Oracle state of one request: processed probabilities are computed once,
-    decisions can then be replayed for many (seed, offset)."""
+    decisions can then be replayed for many (seed, offset).  host: optional
+    HostInputs of the same call (no device reads then)."""
 
-    def __init__(self, inp: dict, r: int, host: dict | None = None):
+    def __init__(self, inp: dict, r: int, host=None):
+        if isinstance(host, HostInputs):
+            self._from_host(inp, r, host)
+            return
         cu = inp["cu"].cpu().numpy() if host is None else host["cu"]
         self.r = r
         self.c0, self.c1 = int(cu[r]), int(cu[r + 1])
@@ -181,6 +210,26 @@ class OracleRequest:
                 dl = dl.contiguous().view(torch.int16).cpu().numpy().view(np.uint16) if dl.dtype == torch.bfloat16 \
                     else dl.contiguous().cpu().numpy()
                 self.q64 = oracle.draft_q_rows(dl, tq)
+        self.P, self.amax, self.err, self.topp_margin = self.prepare(0.0)
+
+    def _from_host(self, inp: dict, r: int, h: HostInputs):
+        self.r = r
+        self.c0, self.c1 = int(h.cu[r]), int(h.cu[r + 1])
+        self.K = self.c1 - self.c0
+        self.g0 = self.c0 + r
+        self.rows = h.logits[self.g0:self.g0 + self.K + 1]
+        self.T = float(h.temperature[r])
+        self.top_k = int(h.top_k[r]) if h.top_k is not None else 0
+        self.theta = float(h.rep_penalty[r]) if h.rep_penalty is not None else None
+        self.freq = float(h.freq[r]) if h.freq is not None else 0.0
+        self.pres = float(h.pres[r]) if h.pres is not None else 0.0
+        self.top_p = float(h.top_p[r]) if h.top_p is not None else 1.0
+        self.counts = h.counts[int(h.idx_mapping[r])] if h.counts is not None else None
+        self.syn = inp.get("synthetic_rates")
+        self.d = h.draft_ids[self.c0:self.c1]
+        self.q = h.draft_probs[self.c0:self.c1] if (h.draft_probs is not None and self.K) else None
+        self.q64 = None
+        assert inp.get("draft_stats") is None, "draft-logits mode: use the device constructor"
         self.P, self.amax, self.err, self.topp_margin = self.prepare(0.0)
 
     def prepare(self, shift):
@@ -259,3 +308,49 @@ def check_requests(g: dict, inp: dict, requests, seed=0, offset=0, probs=False):
             if err > PROB_ATOL:
                 bad.append(f"request {r}: probability error {err:.3g}")
     return n_margin, bad
+
+
+def check_one(g: dict, inp: dict, r: int, host: HostInputs, seed=0, offset=0, probs_rows=None):
+    """check_requests for one request, from host copies; returns (is_margin, mismatch list)."""
+    out_stride = g["tokens"].shape[1]
+    bad = []
+    o = OracleRequest(inp, r, host)
+    if o.err != 0:
+        return False, [f"oracle rejected request {r}: {o.err}"]
+    toks, ns, nr, mg, pd = o.decide(seed, offset)
+    res = compare_request(g, r, toks, ns, nr, mg, out_stride)
+    if res not in ("ok", "margin") and o.near_topp_boundary():
+        for shift in (-TOPP_TOL, TOPP_TOL):
+            t2, ns2, nr2, mg2, _ = o.decide_shifted(shift, seed, offset)
+            if compare_request(g, r, t2, ns2, nr2, mg2, out_stride) in ("ok", "margin"):
+                res = "margin"
+                break
+    if res not in ("ok", "margin"):
+        bad.append(res)
+    if o.K and o.T > 0:
+        gp = g["p_draft"][o.c0:o.c1].astype(np.float64)
+        exact = np.array([o.P[i, d] if 0 <= d < o.P.shape[1] else 0.0 for i, d in enumerate(o.d)])
+        err = float(np.max(np.abs(gp - exact)))
+        if err > PROB_ATOL and o.near_topp_boundary():
+            err = min(err, *(_p_draft_err(gp.astype(np.float32), o, s) for s in (-TOPP_TOL, TOPP_TOL)))
+        if err > PROB_ATOL:
+            bad.append(f"request {r}: p(d) error {err:.3g}")
+    if probs_rows is not None:
+        for i in range(o.K + 1):
+            row = probs_rows.get(o.g0 + i)
+            if row is not None:
+                err = float(np.max(np.abs(row.astype(np.float64) - o.P[i])))
+                if err > PROB_ATOL:
+                    bad.append(f"request {r} row {o.g0 + i}: probability error {err:.3g}")
+    return res == "margin", bad
+
+
+def check_all(g: dict, inp: dict, requests, seed=0, offset=0, probs_rows=None, workers=16, host=None):
+    """check_requests over many requests with the oracle in a thread pool (its C
+    calls release the GIL).  probs_rows: {target row: device probabilities} to
+    compare with the oracle's fp64 ones.  Returns (n_margin, mismatches)."""
+    from concurrent.futures import ThreadPoolExecutor
+    host = host or HostInputs(inp)
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        res = list(ex.map(lambda r: check_one(g, inp, r, host, seed, offset, probs_rows), requests))
+    return sum(m for m, _ in res), [b for _, bl in res for b in bl]

@@ -32,14 +32,17 @@ def test_exports_every_declared_symbol():
     assert names == sorted(["spec_post_update", "spec_verify_create", "spec_verify_destroy",
                             "spec_verify_profile_read", "spec_verify_profile_start",
                             "spec_verify_read_error", "spec_verify_run", "spec_verify_strerror",
-                            "spec_verify_synthetic_rates", "spec_draft_sample", "spec_verify_lm_head"])
+                            "spec_verify_synthetic_rates", "spec_draft_sample", "spec_verify_lm_head",
+                            "spec_verify_debug_philox", "spec_verify_debug_exp_noise"])
     L = ctypes.CDLL(sv.library_path())
     for n in names:
         assert hasattr(L, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", sv.library_path()], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (spec_\w+)", out))
-    assert set(names) <= exported
+    assert set(names) == exported
+    # nothing else: the internal C++ symbols stay hidden
+    assert set(re.findall(r"\bT (\S+)", out)) == exported
 
 
 def test_struct_layout_matches_header(tmp_path):
@@ -139,12 +142,18 @@ def test_strerror_and_host_checks_without_gpu():
     assert L.spec_verify_lm_head(fake, ctypes.byref(la), None) == sv.SV_EINVAL
     la.num_reqs, la.num_rows = 2, 1  # fewer rows than requests
     assert L.spec_verify_lm_head(fake, ctypes.byref(la), None) == sv.SV_EINVAL
-    assert L.spec_verify_create(ctypes.byref(ctx), 1, 1, 1, 1, 0x4) == sv.SV_EINVAL
+    assert L.spec_verify_create(ctypes.byref(ctx), 1, 1, 1, 1, 0x8) == sv.SV_EINVAL
     assert L.spec_verify_profile_start(None, 4) == sv.SV_EINVAL
     assert L.spec_verify_profile_start(fake, 0) == sv.SV_EINVAL
     n = ctypes.c_int32(7)
     assert L.spec_verify_profile_read(None, None, None, ctypes.byref(n)) == sv.SV_EINVAL
     L.spec_verify_destroy(None)
+    assert L.spec_verify_debug_philox(None, -1, 0, None, None) == sv.SV_EINVAL
+    assert L.spec_verify_debug_philox(None, 0, 0, None, None) == sv.SV_OK
+    assert L.spec_verify_debug_philox(None, 4, 0, None, None) == sv.SV_EINVAL
+    assert L.spec_verify_debug_philox(ctypes.c_void_p(8), 4, 0, ctypes.c_void_p(16), None) == sv.SV_EINVAL
+    assert L.spec_verify_debug_exp_noise(None, 3, None, None) == sv.SV_EINVAL
+    assert L.spec_verify_debug_exp_noise(None, -2, None, None) == sv.SV_EINVAL
 
 
 def test_product_package_has_no_oracle_or_cpu_fallback():

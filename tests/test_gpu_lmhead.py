@@ -165,7 +165,7 @@ def test_lm_head_parity(name):
             g2 = lm_run(ctx, inp, seed=seed, offset=off)
             assert np.array_equal(g2["tokens"], g["tokens"])
         say(f"case {name}: margin-excused requests {total} of {3 * inp['B']}")
-        assert total <= max(1, inp["B"] // 20)
+        assert total <= int(1e-4 * 3 * inp["R"])  # 0.01 % of the rows checked
     finally:
         sv.spec_verify_destroy(ctx)
 
@@ -188,7 +188,7 @@ def test_lm_head_strided_rows():
             assert g["err"] == 0
             np.testing.assert_array_equal(g["tokens"], ref["tokens"])
             ex, bad = check(inp, h, g, seed, off, range(inp["B"]))
-            assert not bad and ex <= 1, "\n".join(bad[:10])
+            assert not bad and ex <= int(1e-4 * inp["R"]), "\n".join(bad[:10])
     finally:
         sv.spec_verify_destroy(ctx)
 
@@ -245,7 +245,7 @@ def test_lm_head_full_size_sampled(greedy_every):
         ex, bad = check(inp, h, g, 5, 3, pick)
         say(f"full size: margin-excused {ex} of {len(pick)}")
         assert not bad, "\n".join(bad[:10])
-        assert ex <= 1
+        assert ex <= int(1e-4 * inp["R"])
     finally:
         sv.spec_verify_destroy(ctx)
 
@@ -282,5 +282,30 @@ def test_lm_head_post_update_inside_call():
         assert np.array_equal(ns.cpu().numpy(), g["num_sampled"])
         for got, w in zip(st, want):
             assert np.array_equal(got.cpu().numpy(), w)
+    finally:
+        sv.spec_verify_destroy(ctx)
+
+
+def test_lm_head_margin_aggregate():
+    # The margin rule aggregated over enough runs that 0.01 % of the rows
+    # checked is at least one: B=128 requests, K_r ~ U{0..3}, V=777, d=128,
+    # every 5th request greedy; every request checked in every run.
+    inp = wl.make_lm_head_inputs(B=128, K=3, V=777, d=128, T=0.9, greedy_every=5, device=DEV)
+    h = host(inp)
+    R = inp["R"]
+    runs = max(40, -(-10_000 // R))
+    bound = int(1e-4 * R * runs)
+    ctx = lm_ctx(inp)
+    try:
+        excused = 0
+        for run in range(runs):
+            seed, off = 0xC0FFEE + 31 * run, 7 * run
+            g = lm_run(ctx, inp, seed=seed, offset=off)
+            assert g["err"] == 0
+            ex, bad = check(inp, h, g, seed, off, range(inp["B"]), check_logits=False)
+            assert not bad, f"run {run}: " + "\n".join(bad[:10])
+            excused += ex
+        say(f"LM-head aggregate: {runs} runs x {R} rows, margin-excused requests {excused}, bound {bound}")
+        assert bound >= 1 and excused <= bound
     finally:
         sv.spec_verify_destroy(ctx)

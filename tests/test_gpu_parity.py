@@ -17,43 +17,19 @@ def say(*a):
     print(*a, flush=True)
 
 
-def sample_requests(B, n, seed=0):
-    if B <= n:
-        return list(range(B))
-    rng = np.random.default_rng(seed)
-    pick = set(rng.choice(B, n - 2, replace=False).tolist()) | {0, B - 1}
-    return sorted(pick)
-
-
-@pytest.mark.parametrize("cid,nreq,probs", [("1", None, True), ("2", None, True), ("3", 48, True)])
-def test_small_configs_full_parity(cid, nreq, probs):
+@pytest.mark.parametrize("cid", ["1", "2"])
+def test_small_configs_full_parity(cid):
     w = wl.CONFIGS[cid]
     say(f"config {cid}: {w}")
     inp = wl.make_inputs(w, DEV)
     with ctx_for(inp) as ctx:
-        g = run_gpu(ctx, inp, seed=0, offset=0, dbg_probs=probs)
+        g = run_gpu(ctx, inp, seed=0, offset=0, dbg_probs=True)
     assert g["err"] == 0
-    reqs = range(inp["B"]) if nreq is None else sample_requests(inp["B"], nreq)
-    n_margin, bad = check_requests(g, inp, reqs, probs=probs)
+    n_margin, bad = check_requests(g, inp, range(inp["B"]), probs=True)
     say(f"config {cid}: margin requests {n_margin}, mismatches {len(bad)}")
     assert not bad, "\n".join(bad[:10])
     K = inp["K"].cpu().numpy()
     assert np.all(g["num_sampled"] >= 1) and np.all(g["num_sampled"] <= K + 1)
-    assert np.all(g["num_rejected"] == K + 1 - g["num_sampled"])
-
-
-@pytest.mark.parametrize("cid,nreq", [("3k3", 32), ("4", 24), ("5", 24)])
-def test_large_configs_sampled_parity(cid, nreq):
-    w = wl.CONFIGS[cid]
-    say(f"config {cid}: {w}")
-    inp = wl.make_inputs(w, DEV)
-    with ctx_for(inp) as ctx:
-        g = run_gpu(ctx, inp, seed=0, offset=0)
-    assert g["err"] == 0
-    n_margin, bad = check_requests(g, inp, sample_requests(inp["B"], nreq))
-    say(f"config {cid}: margin requests {n_margin}, mismatches {len(bad)}")
-    assert not bad, "\n".join(bad[:10])
-    K = inp["K"].cpu().numpy()
     assert np.all(g["num_rejected"] == K + 1 - g["num_sampled"])
 
 
