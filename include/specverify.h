@@ -200,6 +200,39 @@ typedef struct sv_verify_args {
  */
 SV_API int spec_verify_run(sv_ctx *ctx, const sv_verify_args *args, hipStream_t stream);
 
+/*
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, serving loops that must not allocate, harnesses that forbid it.
+ * The same verify step as spec_verify_run, with the same kernels and the
+ * same results, without a context.  Its scratch (chunk tables, row
+ * statistics, residual tables, row states) is one fixed device array of the
+ * library, of about 21 MB, which each GPU the library runs on holds until the
+ * process ends.  The first call on a device looks up that device's copy of
+ * the array.  The call allocates nothing, on the device or the host.
+ *
+ * Limits (SV_ECAPACITY beyond them, nothing enqueued):
+ * - at most SV_NOALLOC_MAX_ROWS target rows and SV_NOALLOC_MAX_REQS requests;
+ * - rows x ceil(V / SV_RACE_CHUNK) <= SV_NOALLOC_MAX_CHUNKS;
+ * - requests x ceil(V / SV_RACE_CHUNK) <= SV_NOALLOC_MAX_RESID;
+ * - no top_k (its candidate lists need SV_TOPK_CANDIDATES entries per row).
+ * Other settings are as for spec_verify_run, except that profiling is not
+ * available.
+ *
+ * device_errors: a DEVICE uint32 word that the call's kernels OR their
+ * SV_ERR_* bits into.  The caller zeroes it and reads it.
+ *
+ * Every call on one GPU shares that GPU's array, and the array keeps the
+ * last call's contents.  Calls whose work overlaps on one GPU (on different
+ * streams, or from different host threads without ordering) race and give
+ * unspecified results.  Calls ordered on one stream are safe.
+ * Errors: as spec_verify_run, plus SV_EINVAL for a NULL device_errors.
+ */
+#define SV_NOALLOC_MAX_ROWS 16384
+#define SV_NOALLOC_MAX_REQS 4096
+#define SV_NOALLOC_MAX_CHUNKS (1 << 21)
+#define SV_NOALLOC_MAX_RESID (1 << 20)
+SV_API int spec_verify_run_noalloc(const sv_verify_args *args, uint32_t *device_errors, hipStream_t stream);
+
 struct sv_post_update_args {
   const int32_t *idx_mapping;   /* [num_reqs] batch row -> state slot                     */
   const int32_t *query_len;     /* [num_reqs] tokens scheduled for the request this step  */

@@ -12,7 +12,7 @@ Entry points (same names as the C ABI):
     spec_post_update, spec_verify_strerror, spec_verify_read_error,
     spec_verify_synthetic_rates, spec_verify_profile_start, spec_verify_profile_read,
     spec_draft_sample, spec_verify_lm_head, spec_verify_debug_philox,
-    spec_verify_debug_exp_noise
+    spec_verify_debug_exp_noise, spec_verify_run_noalloc
 """
 from __future__ import annotations
 
@@ -27,7 +27,7 @@ __all__ = [
     "spec_verify_create", "spec_verify_destroy", "spec_verify_run", "spec_post_update",
     "spec_verify_strerror", "spec_verify_read_error", "spec_verify_synthetic_rates",
     "DraftArgs", "spec_draft_sample", "SV_CREATE_LM_HEAD", "LmHeadArgs", "spec_verify_lm_head",
-    "spec_verify_debug_philox", "spec_verify_debug_exp_noise",
+    "spec_verify_debug_philox", "spec_verify_debug_exp_noise", "spec_verify_run_noalloc",
 ]
 
 SV_OK, SV_EINVAL, SV_ECAPACITY, SV_EDTYPE, SV_EHIP, SV_EINPUT = 0, -1, -2, -3, -4, -5
@@ -38,6 +38,8 @@ SV_LM_HEAD_CHUNK = 64
 SV_RACE_CHUNK = 1024
 SV_MAX_DRAFTS = 64
 SV_TOPK_CANDIDATES = 1024
+SV_NOALLOC_MAX_ROWS, SV_NOALLOC_MAX_REQS = 16384, 4096
+SV_NOALLOC_MAX_CHUNKS, SV_NOALLOC_MAX_RESID = 1 << 21, 1 << 20
 SV_ERR_CU, SV_ERR_TEMPERATURE, SV_ERR_PENALTY, SV_ERR_ROW, SV_ERR_SLOT = 1, 2, 4, 8, 16
 SV_ERR_TOP_P = 64
 
@@ -194,6 +196,8 @@ def lib() -> ctypes.CDLL:
         L.spec_verify_profile_start.restype = ctypes.c_int
         L.spec_verify_profile_read.argtypes = [P, P, P, ctypes.POINTER(ctypes.c_int32)]
         L.spec_verify_profile_read.restype = ctypes.c_int
+        L.spec_verify_run_noalloc.argtypes = [ctypes.POINTER(VerifyArgs), P, P]
+        L.spec_verify_run_noalloc.restype = ctypes.c_int
         L.spec_verify_debug_philox.argtypes = [P, ctypes.c_int64, ctypes.c_uint64, P, P]
         L.spec_verify_debug_philox.restype = ctypes.c_int
         L.spec_verify_debug_exp_noise.argtypes = [P, ctypes.c_int64, P, P]
@@ -355,6 +359,21 @@ def spec_verify_run(ctx, *args, stream=None, **kwargs) -> None:
     st = lib().spec_verify_run(ctx, ctypes.byref(a), _stream_handle(stream))
     if st != SV_OK:
         raise SpecVerifyError(st, "spec_verify_run")
+
+
+def spec_verify_run_noalloc(*args, device_errors, stream=None, **kwargs) -> None:
+    """spec_verify_run without a context (the library's fixed scratch array);
+    device_errors: an int32 device tensor of one element that the kernels OR
+    their SV_ERR_* bits into (the caller zeroes and reads it).  Arguments as
+    spec_verify_run, passed as make_verify_args' (or one VerifyArgs)."""
+    import torch
+    _dev(device_errors, torch.int32, "device_errors")
+    if device_errors.numel() < 1:
+        raise ValueError("device_errors needs one element")
+    a = args[0] if len(args) == 1 and isinstance(args[0], VerifyArgs) else make_verify_args(*args, **kwargs)
+    st = lib().spec_verify_run_noalloc(ctypes.byref(a), _ptr(device_errors), _stream_handle(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "spec_verify_run_noalloc")
 
 
 def make_post_update_args(idx_mapping, query_len, tokens, num_sampled, num_rejected,

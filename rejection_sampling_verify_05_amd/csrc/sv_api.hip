@@ -3,6 +3,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
 #include <new>
 
 #include <hip/hip_runtime.h>
@@ -123,7 +125,19 @@ extern "C" void spec_verify_destroy(sv_ctx *ctx) {
   free_ctx(ctx);
 }
 
+namespace {
+int verify_on(sv_ctx *ctx, const sv_verify_args *a, hipStream_t stream);
+}  // namespace
+
 extern "C" int spec_verify_run(sv_ctx *ctx, const sv_verify_args *a, hipStream_t stream) {
+  if (!ctx || !a) return SV_EINVAL;
+  return verify_on(ctx, a, stream);
+}
+
+namespace {
+// The verify step on ctx's scratch (a context, or the fixed array of
+// spec_verify_run_noalloc described as one).
+int verify_on(sv_ctx *ctx, const sv_verify_args *a, hipStream_t stream) {
   if (!ctx || !a) return SV_EINVAL;
   if (a->logits_dtype != SV_F32 && a->logits_dtype != SV_BF16) return SV_EDTYPE;
   if (a->num_reqs < 0 || a->vocab_size <= 0 || a->num_rows < a->num_reqs) return SV_EINVAL;
@@ -298,6 +312,7 @@ extern "C" int spec_verify_run(sv_ctx *ctx, const sv_verify_args *a, hipStream_t
   if (p.dbg_probs && sv::launch_dbg_probs(p, stream) != hipSuccess) return SV_EHIP;
   return SV_OK;
 }
+}  // namespace
 
 extern "C" int spec_draft_sample(sv_ctx *ctx, const sv_draft_args *a, hipStream_t stream) {
   if (!ctx || !a) return SV_EINVAL;
@@ -548,4 +563,98 @@ extern "C" int spec_verify_debug_exp_noise(const uint32_t *words, int64_t n, flo
   if (n == 0) return SV_OK;
   if (!words || !out) return SV_EINVAL;
   return sv::launch_dbg_noise(words, n, out, stream) == hipSuccess ? SV_OK : SV_EHIP;
+}
+
+// ---------------------------------------------------------------------------
+// spec_verify_run without a context: the scratch of a context carved from one
+// fixed device array, looked up once per device.
+// ---------------------------------------------------------------------------
+namespace {
+constexpr size_t kNoallocTab = (size_t)SV_NOALLOC_MAX_CHUNKS * sizeof(float2);
+constexpr size_t kNoallocRowInfo = (size_t)SV_NOALLOC_MAX_ROWS * sizeof(float4);
+constexpr size_t kNoallocResReq = (size_t)SV_NOALLOC_MAX_REQS * sizeof(int4);
+constexpr size_t kNoallocResTab = (size_t)SV_NOALLOC_MAX_RESID * sizeof(float);
+constexpr size_t kNoallocResList = ((size_t)SV_NOALLOC_MAX_REQS + 1) * sizeof(int) + 252;  // kept 256-aligned
+constexpr size_t kNoallocCandN = (size_t)SV_NOALLOC_MAX_ROWS * sizeof(int32_t);
+constexpr size_t kNoallocCandTau = (size_t)SV_NOALLOC_MAX_ROWS * sizeof(float);
+constexpr size_t kNoallocBytes =
+    kNoallocTab + kNoallocRowInfo + kNoallocResReq + kNoallocResTab + kNoallocResList + kNoallocCandN + kNoallocCandTau;
+static_assert(kNoallocResList % 256 == 0, "regions stay 256-byte aligned");
+
+// Zero-initialised at load, which every region relies on only for the
+// residual-request count (res_list[0]) and the residual descriptors' epoch tags
+// (res_req[].w); everything else is written before it is read within a call.
+static __device__ __align__(256) unsigned char scratch[kNoallocBytes];
+
+constexpr int kMaxDevices = 64;
+struct NoallocDevice {
+  std::mutex mu;
+  bool ready = false;
+  unsigned char *base = nullptr;  // this device's copy of `scratch` (never the host-side name)
+  int32_t resident[2][3] = {};
+  int32_t ncu = 1;
+  uint32_t epoch = 0;
+  bool res_dirty = false;
+};
+NoallocDevice g_noalloc[kMaxDevices];
+
+int noalloc_setup(int dev, NoallocDevice &nd) {
+  if (nd.ready) return SV_OK;
+  void *ptr = nullptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return SV_EHIP;
+  int ncu = 0;
+  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return SV_EHIP;
+  nd.ncu = ncu > 0 ? ncu : 1;
+  for (int dt = 0; dt < 2; ++dt)
+    for (int f = 0; f < 3; ++f) nd.resident[dt][f] = nd.ncu * sv::stats_blocks_per_cu(dt, f);
+  nd.base = static_cast<unsigned char *>(ptr);
+  nd.ready = true;
+  return SV_OK;
+}
+}  // namespace
+
+extern "C" int spec_verify_run_noalloc(const sv_verify_args *a, uint32_t *device_errors, hipStream_t stream) {
+  if (!a || !device_errors) return SV_EINVAL;
+  if (a->top_k) return SV_ECAPACITY;
+  if (a->vocab_size <= 0 || a->num_reqs < 0) return SV_EINVAL;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SV_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return SV_ECAPACITY;
+  NoallocDevice &nd = g_noalloc[dev];
+  std::lock_guard<std::mutex> lock(nd.mu);
+  const int st = noalloc_setup(dev, nd);
+  if (st != SV_OK) return st;
+  const int32_t nc = (a->vocab_size + sv::kChunk - 1) / sv::kChunk;
+  sv_ctx c{};  // a context over the fixed array: capacities from its sizes for this vocabulary
+  c.device = dev;
+  c.max_vocab = a->vocab_size;
+  c.nc_stride = nc;
+  c.max_rows = (int32_t)(SV_NOALLOC_MAX_ROWS < SV_NOALLOC_MAX_CHUNKS / nc ? SV_NOALLOC_MAX_ROWS : SV_NOALLOC_MAX_CHUNKS / nc);
+  c.max_reqs = (int32_t)(SV_NOALLOC_MAX_REQS < SV_NOALLOC_MAX_RESID / nc ? SV_NOALLOC_MAX_REQS : SV_NOALLOC_MAX_RESID / nc);
+  c.max_k = SV_MAX_DRAFTS;
+  c.flags = 0;
+  c.epoch = nd.epoch;
+  c.res_dirty = nd.res_dirty;
+  for (int dt = 0; dt < 2; ++dt)
+    for (int f = 0; f < 3; ++f) c.resident[dt][f] = nd.resident[dt][f];
+  c.ncu = nd.ncu;
+  unsigned char *q = nd.base;
+  c.chunk_tab = reinterpret_cast<float2 *>(q);
+  q += kNoallocTab;
+  c.row_info = reinterpret_cast<float4 *>(q);
+  q += kNoallocRowInfo;
+  c.res_req = reinterpret_cast<int4 *>(q);
+  q += kNoallocResReq;
+  c.res_tab = reinterpret_cast<float *>(q);
+  q += kNoallocResTab;
+  c.res_list = reinterpret_cast<int *>(q);
+  q += kNoallocResList;
+  c.cand_n = reinterpret_cast<int32_t *>(q);
+  q += kNoallocCandN;
+  c.cand_tau = reinterpret_cast<float *>(q);
+  c.err = device_errors;
+  const int rc = verify_on(&c, a, stream);
+  nd.epoch = c.epoch;
+  nd.res_dirty = c.res_dirty;
+  return rc;
 }

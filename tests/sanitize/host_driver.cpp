@@ -241,6 +241,12 @@ int main() {
   CHECK(spec_verify_debug_philox((const uint32_t *)g_fake, 4, 1, (uint32_t *)(g_fake + 8), nullptr) == SV_EINVAL);
   CHECK(spec_verify_debug_philox((const uint32_t *)g_fake, 4, 1, (uint32_t *)(g_fake + 16), nullptr) == SV_OK);
   CHECK(spec_verify_debug_exp_noise((const uint32_t *)g_fake, 8, (float *)g_fake, nullptr) == SV_OK);
+  // The entry point without a context: argument checks before any HIP call.
+  uint32_t *dev_err = (uint32_t *)g_fake;
+  CHECK(spec_verify_run_noalloc(nullptr, dev_err, nullptr) == SV_EINVAL);
+  CHECK(spec_verify_run_noalloc(&a, nullptr, nullptr) == SV_EINVAL);
+  CHECK(spec_verify_run_noalloc(&ak, dev_err, nullptr) == SV_ECAPACITY);
+  CHECK(spec_verify_run_noalloc(&a, dev_err, nullptr) == SV_EHIP);  // no device here
   float r3[3];
   CHECK(spec_verify_synthetic_rates(2.5f, 3, r3) == SV_OK && r3[0] == 1.0f && r3[1] == 0.5f && r3[2] == 0.0f);
   CHECK(spec_verify_synthetic_rates(5.0f, 3, r3) == SV_EINVAL);

@@ -33,7 +33,8 @@ def test_exports_every_declared_symbol():
                             "spec_verify_profile_read", "spec_verify_profile_start",
                             "spec_verify_read_error", "spec_verify_run", "spec_verify_strerror",
                             "spec_verify_synthetic_rates", "spec_draft_sample", "spec_verify_lm_head",
-                            "spec_verify_debug_philox", "spec_verify_debug_exp_noise"])
+                            "spec_verify_debug_philox", "spec_verify_debug_exp_noise",
+                            "spec_verify_run_noalloc"])
     L = ctypes.CDLL(sv.library_path())
     for n in names:
         assert hasattr(L, n), n
@@ -154,6 +155,11 @@ def test_strerror_and_host_checks_without_gpu():
     assert L.spec_verify_debug_philox(ctypes.c_void_p(8), 4, 0, ctypes.c_void_p(16), None) == sv.SV_EINVAL
     assert L.spec_verify_debug_exp_noise(None, 3, None, None) == sv.SV_EINVAL
     assert L.spec_verify_debug_exp_noise(None, -2, None, None) == sv.SV_EINVAL
+    assert L.spec_verify_run_noalloc(None, None, None) == sv.SV_EINVAL
+    na = sv.VerifyArgs()
+    assert L.spec_verify_run_noalloc(ctypes.byref(na), None, None) == sv.SV_EINVAL  # no error word
+    na.top_k = 8
+    assert L.spec_verify_run_noalloc(ctypes.byref(na), ctypes.c_void_p(16), None) == sv.SV_ECAPACITY
 
 
 def test_product_package_has_no_oracle_or_cpu_fallback():

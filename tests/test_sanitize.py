@@ -4,9 +4,10 @@
   by tests/sanitize/oracle_driver.c (gcc, with the leak checker).
 - The C ABI's host side (csrc/sv_api.hip: argument checks, capacity checks,
   the choice of passes, grid sizing, post_update, draft-side, LM-head and
-  debug entry points), compiled for the host only with its kernel launchers
-  stubbed, driven by tests/sanitize/host_driver.cpp.  No GPU is involved:
-  the stubs record what would have been launched.
+  debug entry points, the allocation-free entry point's checks), with the
+  sanitizers on the host pass only and the kernel launchers stubbed, driven by
+  tests/sanitize/host_driver.cpp.  No GPU is involved: the stubs record what
+  would have been launched.
 
 CPU only; each build takes a few seconds."""
 import os
@@ -39,8 +40,9 @@ def test_oracle_under_asan_and_ubsan(tmp_path):
 def test_host_api_under_asan_and_ubsan(tmp_path):
     obj = str(tmp_path / "host_driver.o")
     exe = str(tmp_path / "host_driver")
-    # host-only compile; every sanitizer flag applies to the host pass only
-    compile_cmd = [os.path.join(ROCM, "bin", "hipcc"), "-x", "hip", "--offload-host-only", "-std=c++17", "-O1",
+    # every sanitizer flag applies to the host pass only (the device pass
+    # compiles the library's device-side data and nothing of the driver)
+    compile_cmd = [os.path.join(ROCM, "bin", "hipcc"), "-x", "hip", "--offload-arch=gfx950", "-std=c++17", "-O1",
                    "-g", "-fno-omit-frame-pointer"]
     for flag in ("address", "undefined"):
         compile_cmd += ["-Xarch_host", "-fsanitize=" + flag]
