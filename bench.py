@@ -37,8 +37,12 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 PROFILES = os.path.join(ROOT, "profiles")
 # FETCH_SIZE / WRITE_SIZE counter record of the streaming kernel on the headline workload
 COUNTERS = os.path.join(PROFILES, "stats_fast_kernel_bf16_B256_V128256_counters.md")
-KERNEL_SOURCES = ["rejection_sampling_verify_05_amd/csrc/sv_kernels.hip", "rejection_sampling_verify_05_amd/csrc/sv_device.h",
-                  "rejection_sampling_verify_05_amd/csrc/sv_internal.h", "rejection_sampling_verify_05_amd/build.py"]
+CSRC = "rejection_sampling_verify_05_amd/csrc/"
+_COMMON = [CSRC + "sv_common.h", CSRC + "sv_device.h", CSRC + "sv_internal.h", "rejection_sampling_verify_05_amd/build.py"]
+# The sources a profile record was taken on, per kernel: a record stays valid
+# while these files are unchanged.
+KERNEL_SOURCES = [CSRC + "sv_stats.hip"] + _COMMON
+KERNEL_SOURCES_TOPK = [CSRC + "sv_topk.hip", CSRC + "sv_tiles.h"] + _COMMON
 
 
 # ... and of the LM-head GEMM on its workload
@@ -81,19 +85,20 @@ def recorded_traffic_per_row(path=None, sources=None):
 # Per-workload profiles/ summaries: the first pass over the rows, named for the
 # kernel and the workload.
 WORKLOAD_PROFILE = {
-    "2": "stats_fast_kernel_bf16_B64_K4_V32000",
-    "3": "stats_fast_kernel_bf16_B256_V128256",
-    "3k3": "stats_fast_kernel_bf16_B256_K3_V128256",
-    "4": "topk_kernel_f32_B512_K8_V151936",
-    "5": "stats_fast_kernel_bf16_B1024_K5_V256000",
+    "2": ("stats_fast_kernel_bf16_B64_K4_V32000", KERNEL_SOURCES),
+    "3": ("stats_fast_kernel_bf16_B256_V128256", KERNEL_SOURCES),
+    "3k3": ("stats_fast_kernel_bf16_B256_K3_V128256", KERNEL_SOURCES),
+    "4": ("topk_kernel_f32_B512_K8_V151936", KERNEL_SOURCES_TOPK),
+    "5": ("stats_fast_kernel_bf16_B1024_K5_V256000", KERNEL_SOURCES),
 }
 
 
 def profile_paths(cid):
-    base = WORKLOAD_PROFILE.get(cid)
-    if base is None:
-        return None, None
-    return os.path.join(PROFILES, base + "_counters.md"), os.path.join(PROFILES, base + "_trace.md")
+    """(counter record, trace record, the sources both were taken on) of a workload."""
+    if cid not in WORKLOAD_PROFILE:
+        return None, None, None
+    base, sources = WORKLOAD_PROFILE[cid]
+    return os.path.join(PROFILES, base + "_counters.md"), os.path.join(PROFILES, base + "_trace.md"), sources
 
 
 def cpu_model():
@@ -219,6 +224,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--separate-post-update", action="store_true",
                     help="run post_update as its own call after spec_verify_run instead of inside it")
+    ap.add_argument("--cpu-leg", action="store_true",
+                    help="only the oracle baseline (run by the benchmark itself in a child process that "
+                         "never touches the GPU, so its process pool can fork); prints its JSON and exits")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="before warmup, run torch's copy kernel on 256 MiB three times (a known-size "
                          "reference for the FETCH_SIZE / WRITE_SIZE counters)")
@@ -238,10 +246,9 @@ def main():
 
     import workloads as wl
 
-    # CPU baseline first: its process pool forks before anything touches the GPU.
-    cpu = None
-    if not args.no_cpu and args.workload != "3h":
-        cpu = cpu_baseline_leg(wl.CONFIGS[args.workload], args.cpu_seconds)
+    if args.cpu_leg:
+        print(json.dumps(cpu_baseline_leg(wl.CONFIGS[args.workload], args.cpu_seconds)), flush=True)
+        return
 
     from rejection_sampling_verify_05_amd import build as libbuild
     if not os.path.exists(libbuild.OUTPUT):
@@ -387,11 +394,17 @@ def main():
     bytes_per = float(np.mean([per_copy_bytes[(args.warmup + k) % ncopies] for k in range(args.steps)]))
     rows_per = rows / args.steps
     R_mean = float(np.mean([copies[(args.warmup + k) % ncopies]["R"] for k in range(args.steps)]))
+    # Every verify call of this process (warmup, timed pass, instrumented pass):
+    # what a profiler run of the whole process averages over.
+    every = list(range(args.warmup)) + [args.warmup + k for k in range(args.steps)] * 2
+    launches = {"count": len(every),
+                "rows_mean": round(float(np.mean([copies[i % ncopies]["R"] for i in every])), 2),
+                "bytes_mean": round(float(np.mean([per_copy_bytes[i % ncopies] for i in every])), 1)}
     achieved = bytes_per / (float(np.mean(stream_ms)) * 1e-3) / 1e9
-    cpath, tpath = profile_paths(w.cid)
-    per_row = recorded_traffic_per_row(cpath) if cpath else None
+    cpath, tpath, srcs = profile_paths(w.cid)
+    per_row = recorded_traffic_per_row(cpath, srcs) if cpath else None
     traffic = None if per_row is None else int(per_row * R_mean)
-    trace = read_record(tpath)
+    trace = read_record(tpath, srcs)
     prof = None
     if trace is not None:
         avg_ns = float(trace["kernel_avg_ns"])
@@ -420,6 +433,20 @@ def main():
                 "p50": round(float(np.median(a)) * 1e3, 2), "p90": round(float(np.percentile(a, 90)) * 1e3, 2)}
 
     sv.spec_verify_destroy(ctx)
+
+    # CPU baseline after the GPU part (which then runs on a GPU that is not
+    # coming out of idle), in a child process that never touches the GPU: its
+    # process pool forks from there.
+    cpu = None
+    if not args.no_cpu:
+        import subprocess
+        r = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-leg", "--workload", args.workload,
+                            "--cpu-seconds", str(args.cpu_seconds)], capture_output=True, text=True,
+                           timeout=args.cpu_seconds * 10 + 300)
+        if r.returncode != 0:
+            raise RuntimeError(f"oracle baseline leg failed:\n{r.stderr[-2000:]}")
+        cpu = json.loads(r.stdout.strip().splitlines()[-1])
+
     line = {
         "metric": "verified logit rows/sec + achieved HBM GB/s (B=256, K=3, V=128256)",
         "value": round(value, 1),
@@ -451,6 +478,7 @@ def main():
         "epilogue_kernel_us": pct(epi_ms),
         "acceptance_per_position": per_pos,
         "cpu_baseline": cpu,
+        "launches_all_passes": launches,
         "wall_s": round(wall, 3),
     }
     print(json.dumps(line), flush=True)

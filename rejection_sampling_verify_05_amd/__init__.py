@@ -252,7 +252,12 @@ def spec_verify_create(max_rows: int, max_reqs: int, max_k: int, max_vocab: int,
 
 
 def spec_verify_destroy(ctx) -> None:
+    """Frees the context and clears the handle, so a second call is a no-op."""
+    if ctx is None or not getattr(ctx, "value", ctx):
+        return
     lib().spec_verify_destroy(ctx)
+    if isinstance(ctx, ctypes.c_void_p):
+        ctx.value = None
 
 
 def make_verify_args(target_logits, draft_ids, cu_num_draft, temperature, out_tokens,

@@ -6,7 +6,8 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = [os.path.join(HERE, "csrc", n) for n in ("sv_api.hip", "sv_kernels.hip", "sv_lmhead.hip")]
+SOURCES = [os.path.join(HERE, "csrc", n) for n in ("sv_api.hip", "sv_stats.hip", "sv_topk.hip", "sv_topp.hip",
+                                                    "sv_epilogue.hip", "sv_draft.hip", "sv_lmhead.hip")]
 OUTPUT = os.path.join(HERE, "libspecverify.so")
 
 # -ffp-contract=off: every fp32 operation on logits rounds once (the penalty and

@@ -1,0 +1,773 @@
+// sv_epilogue.hip -- request epilogue, residual pass, post_update and the debug kernels.
+//
+// Data flow of one spec_verify_run (all on one stream):
+//   topk_kernel   (only with top_k)      one workgroup per target row: exact
+//                 k-th largest processed logit tau and, when at most
+//                 kCandCap tokens reach tau, the kept tokens sorted by id.
+//   stats_kernel  the streaming pass.  A persistent grid reads every chunk of
+//   (or the       kChunk logits once, each workgroup a balanced contiguous
+//   fast variant) slice, and stores per chunk (max, sum exp2(a (z - max))) --
+//                 or (max, argmax) for greedy rows -- in the chunk table.
+//   epilogue_kernel  one workgroup per request: row softmax statistics from
+//                 the chunk table, the accept tests, the first reject, and
+//                 the bonus / recovered race.
+//   resid_kernel, resid_race_kernel  (draft-probs mode) residual
+//                 max(0, p - q) chunk masses of each rejected request's row,
+//                 then the race.
+//   dbg_kernel    (optional) writes the processed probabilities.
+//
+// The method follows "vLLM 投机解码（Eagle / MTP）实现与运行流程" section 八
+// (8.2 order of processing, 8.3 greedy and stochastic rules), its Q&A on the
+// residual distribution, the bonus token and NO_DRAFT_PROBS, and
+// "【vllm】DeepSeekMTP、eagle" for post_update.  The sampling race is the
+// exponential-race argmax(w / E) of the NO_DRAFT_PROBS Q&A, run over chunks
+// and then tokens.
+#include <stdint.h>
+
+#include "sv_common.h"
+
+namespace sv {
+
+namespace {
+
+constexpr int kTabCache = 2048;  // chunk-table entries the epilogue kernel keeps in LDS
+
+// Candidate lists of compact (top-k) rows, staged in LDS by the epilogue.
+template <bool CAND>
+struct CandBuf {
+  float cw[kCandCap];  // candidate weights
+  int ci[kCandCap];    // candidate token ids
+};
+template <>
+struct CandBuf<false> {};
+
+// LDS of the request epilogue: TC chunk-table entries cached; CAND: room for
+// the candidate lists of compact rows (not needed by the plain variant).
+template <int TC, bool CAND>
+struct EpiSharedT {
+  static constexpr int kCache = TC;
+  BlockScratch red;
+  float m[kMaxDrafts + 1];
+  float s[kMaxDrafts + 1];
+  float tau[kMaxDrafts + 1];
+  float zd[kMaxDrafts + 1];
+  float qd[kMaxDrafts + 1];
+  float sx[kMaxDrafts + 1];
+  int amax[kMaxDrafts + 1];
+  int state[kMaxDrafts + 1];
+  int d[kMaxDrafts + 1];
+  int j;
+  int bad;
+  int flag;
+  float zc[kWaves][kChunk];  // speculative chunks of rows 0..3 (raw logits, token order)
+  float zx[kWaves][kChunk];  // the draft tokens' chunks of rows 0..3
+  float w1s[kWaves];         // best chunk other than the draft token's: score
+  int w1c[kWaves];           //   and index (-1: none)
+  int cd[kWaves];            // the draft token's chunk when excluded, else -1
+  float rcd[kWaves];         // 1/E of that chunk in the chunk race
+  union {
+    float2 tab[TC];  // dense rows: chunk tables of the request's rows
+    CandBuf<CAND> cand;
+  } u;
+};
+using EpiShared = EpiSharedT<kTabCache, true>;
+
+// Race over a compact candidate list (token ids ascending in sh.u.cand.ci,
+// weights in sh.u.cand.cw, n entries); all threads call it.  Same law and
+// random words as the dense race: chunk masses are the sums over the
+// candidates of each chunk.
+__device__ __forceinline__ int compact_race(const Params &p, uint32_t g, int n, EpiShared &sh) {
+  __syncthreads();
+  const float *cw = sh.u.cand.cw;
+  const int *ci = sh.u.cand.ci;
+  ArgMax best{-1.0f, 0x7FFFFFFF};
+  for (int i = threadIdx.x; i < n; i += kThreads) {
+    const int c = ci[i] / kChunk;
+    if (i > 0 && ci[i - 1] / kChunk == c) continue;  // not the first candidate of its chunk
+    float M = 0.0f;
+    for (int t = i; t < n && ci[t] / kChunk == c; ++t) M += cw[t];
+    if (M > 0.0f) {
+      const uint4 w4 = rng_block(p, (uint32_t)c >> 2, g, kTagChunk);
+      ArgMax o{race_score(M, pick(w4, c & 3)), c};
+      if (better(o, best)) best = o;
+    }
+  }
+  const ArgMax cb = block_argmax(best, sh.red);
+  if (cb.s < 0.0f) return -1;
+  const int cstar = cb.i;
+  ArgMax tb{-1.0f, 0x7FFFFFFF};
+  for (int i = threadIdx.x; i < n; i += kThreads) {
+    const int x = ci[i];
+    if (x / kChunk != cstar || !(cw[i] > 0.0f)) continue;
+    const uint4 w4 = rng_block(p, (uint32_t)x >> 2, g, kTagToken);
+    ArgMax o{race_score(cw[i], pick(w4, x & 3)), x};
+    if (better(o, tb)) tb = o;
+  }
+  const ArgMax b = block_argmax(tb, sh.red);
+  return b.s < 0.0f ? -1 : b.i;
+}
+
+// ---------------------------------------------------------------------------
+// Request epilogue: one workgroup per request, after the streaming pass.
+//
+// Round trips: (1) the request's cu entries and temperature; (2) the chunk
+// tables and the draft ids; (3) for each of the first four rows, speculatively,
+// the logits of the chunks its race could need: the chunk that wins the race
+// among the chunks without the draft token, and the draft token's own chunk
+// (z_d, and the chunk mass without d), plus single loads of z_d and q(d) for the
+// other rows.  The speculative chunks go to LDS; the accept tests then pick
+// the row j to sample and the whole workgroup finishes its race from LDS.  A
+// rejected row past the fourth, or a bonus row past the fourth, takes one more
+// round trip; compact (top-k) rows race over their candidate lists.
+// ---------------------------------------------------------------------------
+
+// Speculative state of one row while its wave waits for the loads.
+struct RowSpec {
+  float zc[16];   // logits of chunk c1 (stochastic) or of the lowest max chunk (greedy)
+  float zx[16];   // logits of the draft token's chunk cd
+  ArgMax w1;      // best chunk other than cd: (score, c1); c1 = -1 if none
+  int cd;         // draft token's chunk when it is excluded, else -1
+  float rcd;      // 1/E of chunk cd in the chunk race
+};
+
+// Row statistics of row i from its chunk table (dense) or candidates (compact):
+// scale m (the largest chunk reference r_c; the row maximum for greedy rows and
+// compact rows) and Σ exp2(a (z - m)); greedy dense rows also get the lowest
+// chunk holding the maximum.  One wave; results uniform.
+template <class EF>
+__device__ __forceinline__ void row_stats(const Params &p, const Req &q, int g, int st, bool greedy, EF ent,
+                                          float &m, float &s, int &lc) {
+  const int lane = threadIdx.x & 63;
+  s = 0.0f;
+  lc = 0x7FFFFFFF;
+  if (st >= 0) {
+    const float *cv = p.cand_val + (int64_t)g * kCandCap;
+    float lm = kNegInf;
+    for (int t = lane; t < st; t += 64) lm = fmaxf(lm, cv[t]);
+    m = wave_max(lm);
+    float ls = 0.0f;
+    for (int t = lane; t < st; t += 64) ls += exp2_acc(q.a * (cv[t] - m));
+    s = wave_sum(ls);
+    return;
+  }
+  float lm = kNegInf;
+  for (int c = lane; c < p.NC; c += 64) lm = fmaxf(lm, ent(c).x);
+  m = wave_max(lm);
+  if (greedy) {
+    int l = 0x7FFFFFFF;
+    for (int c = lane; c < p.NC; c += 64)
+      if (ent(c).x == m) l = min(l, c);
+    lc = wave_min_i(l);
+  } else if (m > kNegInf) {
+    float ls = 0.0f;
+    for (int c = lane; c < p.NC; c += 64) {
+      const float2 e = ent(c);
+      if (e.x > kNegInf) ls += e.y * exp2_acc(q.a * (e.x - m));
+    }
+    s = wave_sum(ls);
+  }
+}
+
+// Speculative part for dense stochastic row i (no-draft-probs rows and bonus
+// rows): the chunk race without the draft token's chunk, then the loads of
+// the winning chunk and of the draft token's chunk (penalties applied).
+template <class EF>
+__device__ __forceinline__ void spec_issue(const Params &p, const Req &q, int i, int d, float m, EF ent, RowSpec &rs,
+                                           const ChunkNoise &cn, const Proc &pr) {
+  const int g = q.g0 + i;
+  const bool excl = i < q.K && !q.has_q && d >= 0 && d < p.V;
+  rs.cd = excl ? d / kChunk : -1;
+  rs.rcd = 0.0f;
+  rs.w1 = wave_chunk_race(p, g, ent, q.a, m, rs.cd, cn, &rs.rcd);
+  const int c1 = rs.w1.s < 0.0f ? -1 : rs.w1.i;
+  if (c1 >= 0 || excl) load_chunk16_pen_pair(p, g, c1, rs.cd, pr, rs.zc, rs.zx);
+}
+
+// After the loads of spec_issue: z_d and the mass of d's chunk without d, in
+// the scale of that chunk's table entry r = ent(c_d).x:
+// exp2(fma(z, a, -hi)) exp2(-lo) with a r = hi + lo (pr: the processing left
+// after the penalties).
+__device__ __forceinline__ void spec_draft_record(const Params &p, const Req &q, int d, const Proc &pr,
+                                                  const RowSpec &rs, float ref, float &zd, float &sx) {
+  const int lane = threadIdx.x & 63;
+  const float a = q.a, hi = a * ref, lo = __builtin_fmaf(a, ref, -hi);
+  float acc = 0.0f, zl = kNegInf;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int x = c16_tok(rs.cd, e, lane);
+    const float z = x < p.V ? apply_proc(rs.zx[e], x, pr) : kNegInf;
+    if (x == d)
+      zl = z;
+    else
+      acc += exp2_acc(__builtin_fmaf(z, a, -hi));
+  }
+  sx = ref > kNegInf ? wave_sum(acc) * exp2_acc(-lo) : 0.0f;
+  zd = wave_max(zl);
+}
+
+// Moves a wave's speculative chunks and race state for row i to LDS slot `slot`.
+template <class SH>
+__device__ __forceinline__ void spec_publish(const RowSpec &rs, int slot, SH &sh) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    *reinterpret_cast<float4 *>(&sh.zc[slot][t * 256 + 4 * lane]) =
+        make_float4(rs.zc[4 * t], rs.zc[4 * t + 1], rs.zc[4 * t + 2], rs.zc[4 * t + 3]);
+    *reinterpret_cast<float4 *>(&sh.zx[slot][t * 256 + 4 * lane]) =
+        make_float4(rs.zx[4 * t], rs.zx[4 * t + 1], rs.zx[4 * t + 2], rs.zx[4 * t + 3]);
+  }
+  if (lane == 0) {
+    sh.w1s[slot] = rs.w1.s;
+    sh.w1c[slot] = rs.w1.i;
+    sh.cd[slot] = rs.cd;
+    sh.rcd[slot] = rs.rcd;
+  }
+}
+
+// Final race of row j from LDS slot `slot` (all threads): the chunk of d
+// competes with its mass without d (sx); if nothing is left without d, the race
+// is over p_j.
+template <class EF, class SH>
+__device__ __forceinline__ int spec_finish(const Params &p, const Req &q, int j, int dj, float m, float sx,
+                                           const Proc &pr, EF ent, int slot, SH &sh) {
+  const int gs = q.g0 + j;
+  const float a = q.a;
+  ArgMax win{sh.w1s[slot], sh.w1c[slot]};
+  const int cd = sh.cd[slot];
+  bool excl = cd >= 0;
+  if (excl) {
+    const float2 e = ent(cd);
+    const float rd = sh.rcd[slot];  // 1/E of chunk cd, drawn by the chunk race
+    const float Wd = e.x > kNegInf ? sx * exp2_acc(a * (e.x - m)) : 0.0f;
+    if (Wd > 0.0f) {
+      ArgMax o{Wd * rd, cd};
+      if (better(o, win)) win = o;
+    }
+    if (win.s < 0.0f) {  // nothing left once d_j is removed (rounding): race over p_j
+      excl = false;
+      const float Wf = e.x > kNegInf ? e.y * exp2_acc(a * (e.x - m)) : 0.0f;
+      if (Wf > 0.0f) win = ArgMax{Wf * rd, cd};
+    }
+  }
+  if (win.s < 0.0f) return -1;
+  const int cstar = win.i;
+  const float hi = a * ent(cstar).x;
+  const float *zs = cstar == cd ? sh.zx[slot] : sh.zc[slot];  // penalties applied
+  return block_token_race(p, gs, cstar, zs, proc_after_pen(pr), a, hi, (excl && cstar == cd) ? dj : -1, sh.red);
+}
+
+// Speculative rows: with at most four rows, row w for wave w; with more, rows
+// 0, 1, 2 and the bonus row (the likeliest to be sampled after row 0 when the
+// acceptance rate is high).  spec_slot: the wave (LDS slot) of row i, or -1.
+__device__ __forceinline__ int spec_row(int w, int nrow) { return nrow <= kWaves || w < kWaves - 1 ? w : nrow - 1; }
+__device__ __forceinline__ int spec_slot(int i, int nrow) {
+  if (nrow <= kWaves) return i;
+  return i < kWaves - 1 ? i : (i == nrow - 1 ? kWaves - 1 : -1);
+}
+
+// PLAIN: the call has no top-k, top-p, penalties or draft distributions and
+// at most four rows per request; the settings they would read are then
+// constants, and their paths compile away.
+template <bool PLAIN, class SH>
+__device__ __forceinline__ void request_epilogue(const Params &p, const Req &q_in, SH &sh) {
+  constexpr int TC = SH::kCache;
+  Req q = q_in;
+  if (PLAIN) {
+    q.proc.counts = nullptr;
+    q.proc.theta = 1.0f;
+    q.proc.freq = 0.0f;
+    q.proc.pres = 0.0f;
+    q.proc.tau = kNegInf;
+    q.has_q = false;
+  }
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int K = q.K, r = q.r, nrow = K + 1;
+
+  if (!q.cu_ok || p.cu[0] != 0 || p.cu[p.B] != p.D) {
+    if (tid == 0) raise_err(p, SV_ERR_CU);
+    write_empty(p, r);
+    return;
+  }
+  // The plain variant also runs only with at most four rows per request
+  // (cu_ok bounds K by out_stride - 1): every row has a wave of its own.
+  if (PLAIN) __builtin_assume(nrow <= kWaves);
+  if (q.mode == kModeInvalid) {
+    if (tid == 0) raise_err(p, q.errbits);
+    write_empty(p, r);
+    return;
+  }
+  const bool greedy = q.mode == kModeGreedy;
+
+  // Row states (top-k pass results), draft ids and the chunk tables.
+  for (int i = tid; i < nrow; i += kThreads) {
+    const int g = q.g0 + i;
+    const int st = PLAIN ? kRowDense : row_state(p, g);
+    sh.state[i] = st;
+    sh.tau[i] = (st == kRowDense) ? kNegInf : p.cand_tau[g];
+    sh.d[i] = i < K ? p.draft_ids[q.c0 + i] : -1;
+  }
+  const bool cached = nrow * p.NC <= TC;
+  float2 tv[TC / kThreads];
+  if (cached) {  // all table loads issued first
+#pragma unroll
+    for (int m = 0; m < TC / kThreads; ++m) {
+      const int t = tid + m * kThreads;
+      const int i = t / p.NC, c = t - i * p.NC;
+      tv[m] = t < nrow * p.NC ? p.chunk_tab[(int64_t)(q.g0 + i) * p.nc_stride + c] : make_float2(0.0f, 0.0f);
+    }
+  }
+  // While the tables are in flight: the chunk-race noise of this wave's
+  // speculative row (it depends only on the row).
+  const int srow = spec_row(wave, nrow);
+  const ChunkNoise cn = chunk_noise(p, q.g0 + min(srow, nrow - 1));
+  if (cached) {
+#pragma unroll
+    for (int m = 0; m < TC / kThreads; ++m) {
+      const int t = tid + m * kThreads;
+      if (t < nrow * p.NC) sh.u.tab[t] = tv[m];
+    }
+  }
+  __syncthreads();
+  auto entry = [&](int i, int c) -> float2 {
+    return cached ? sh.u.tab[i * p.NC + c] : p.chunk_tab[(int64_t)(q.g0 + i) * p.nc_stride + c];
+  };
+
+  // Wave w first takes its speculative row spec_row(w) -- rows 0..3, or with
+  // more than four rows 0, 1, 2 and the bonus row K -- with the speculative
+  // loads; then, round robin, the rows nobody speculates on, with only what
+  // the accept tests need.
+  RowSpec rs;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) rs.zc[e] = rs.zx[e] = 0.0f;
+  rs.cd = -1;
+  rs.w1 = ArgMax{-1.0f, 0x7FFFFFFF};
+  for (int i = srow, phase = 0;;) {
+    bool spec = phase == 0;
+    if (spec && i >= nrow) {  // no speculative row for this wave
+      phase = 1;
+      i = wave;
+      continue;
+    }
+    if (!spec) {
+      while (i < nrow && spec_slot(i, nrow) >= 0) i += kWaves;
+      if (i >= nrow) break;
+    }
+    const int g = q.g0 + i;
+    const int st = PLAIN ? kRowDense : sh.state[i];
+    const int d = sh.d[i];
+    auto ent = [&](int c) { return entry(i, c); };
+    float m, s;
+    int lc;
+    row_stats(p, q, g, st, greedy, ent, m, s, lc);
+    Proc pr = q.proc;
+    pr.tau = PLAIN ? kNegInf : sh.tau[i];
+    int am = 0x7FFFFFFF;
+    float zd = kNegInf, qd = 1.0f, sx = 0.0f;
+    const bool valid_d = i < K && d >= 0 && d < p.V;
+    if (st < 0 && greedy) {
+      if (lc < p.NC) {
+        load_chunk16_pen(p, g, lc, pr, rs.zc);
+        am = wave_first_equal(p, lc, rs.zc, proc_after_pen(pr), m);
+      }
+    } else if (st < 0 && spec && (!q.has_q || i == K)) {
+      spec_issue(p, q, i, d, m, ent, rs, cn, pr);
+      if (rs.cd >= 0) spec_draft_record(p, q, d, proc_after_pen(pr), rs, ent(rs.cd).x, zd, sx);
+      spec_publish(rs, wave, sh);
+    } else if (valid_d) {
+      // single loads: z_d (and q(d)) for the accept test
+      zd = apply_proc(load_logit(p, g, d), d, pr);
+      if (q.has_q) qd = draft_q_of(p, q, i, d);
+    }
+    if (lane == 0) {
+      sh.m[i] = m;
+      sh.s[i] = s;
+      sh.amax[i] = am;
+      sh.zd[i] = zd;
+      sh.qd[i] = qd;
+      sh.sx[i] = sx;
+      p.row_info[g] = make_float4(m, s, __int_as_float(am), __int_as_float(st));
+    }
+    if (spec) {
+      phase = 1;
+      i = wave;
+    } else {
+      i += kWaves;
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int bad = 0;
+    for (int i = 0; i < nrow; ++i) bad |= !__builtin_isfinite(sh.m[i]);
+    sh.bad = bad;
+  }
+
+  // Accept tests: lane i of wave 0 takes draft position i.
+  if (wave == 0) {
+    bool rej = false;
+    if (lane < K) {
+      const int d = sh.d[lane];
+      const int g = q.g0 + lane;
+      if (p.synthetic) {
+        // Synthetic acceptance: u * a_i <= a_{i+1} with a_0 = 1, exact in fp64.
+        const double u = u_accept(rng_block(p, 0, (uint32_t)g, kTagAccept).x);
+        const double prev = lane == 0 ? 1.0 : (double)p.syn[lane - 1];
+        rej = !(d >= 0 && d < p.V && u * prev <= (double)p.syn[lane]);
+        if (p.dbg_p_draft) {
+          const bool valid = d >= 0 && d < p.V;
+          p.dbg_p_draft[q.c0 + lane] = greedy ? -1.0f : (valid ? exp2_acc(q.a * (sh.zd[lane] - sh.m[lane])) / sh.s[lane] : 0.0f);
+        }
+      } else if (greedy) {
+        rej = d != sh.amax[lane];
+        if (p.dbg_p_draft) p.dbg_p_draft[q.c0 + lane] = -1.0f;
+      } else {
+        const bool valid = d >= 0 && d < p.V;
+        float pd = 0.0f;
+        double qd = q.has_q ? 0.0 : 1.0;
+        if (valid) {
+          pd = exp2_acc(q.a * (sh.zd[lane] - sh.m[lane])) / sh.s[lane];
+          if (q.has_q) qd = (double)sh.qd[lane];
+        }
+        const double u = u_accept(rng_block(p, 0, (uint32_t)g, kTagAccept).x);
+        rej = !(valid && qd > 0.0 && (double)pd >= u * qd);
+        if (p.dbg_p_draft) p.dbg_p_draft[q.c0 + lane] = pd;
+      }
+    }
+    const unsigned long long mask = __ballot(rej);
+    if (lane == 0) sh.j = mask ? (__ffsll((long long)mask) - 1) : K;
+  }
+  __syncthreads();
+  if (sh.bad) {
+    if (tid == 0) raise_err(p, SV_ERR_ROW);
+    write_empty(p, r);
+    return;
+  }
+  const int j = sh.j;
+
+  // Accepted prefix, padding and counts.
+  for (int t = tid; t < p.out_stride; t += kThreads) {
+    const int v = t < j ? sh.d[t] : -1;
+    if (t != j) p.out_tokens[(int64_t)r * p.out_stride + t] = v;
+  }
+  if (tid == 0) {
+    p.out_ns[r] = j + 1;
+    p.out_nr[r] = K - j;
+  }
+  const int64_t out_j = (int64_t)r * p.out_stride + j;
+
+  auto accepted = [&](int i) { return sh.d[i]; };
+  if (greedy) {
+    if (tid == 0) p.out_tokens[out_j] = sh.amax[j];
+    fused_post_update(p, r, K, j, sh.amax[j], accepted);
+    return;
+  }
+
+  const int gs = q.g0 + j;
+  const bool rejected = j < K;
+  const int dj = rejected ? sh.d[j] : -1;
+  const float m = sh.m[j], s = sh.s[j];
+  Proc pr = q.proc;
+  pr.tau = PLAIN ? kNegInf : sh.tau[j];
+  const int st = PLAIN ? kRowDense : sh.state[j];
+  const float a = q.a;
+
+  if constexpr (!PLAIN) {
+  if (st >= 0) {
+    // Compact top-k row: the race runs over the kept tokens only.
+    __syncthreads();  // the LDS chunk-table cache is reused for the candidates
+    const float *cv = p.cand_val + (int64_t)gs * kCandCap;
+    const int32_t *cix = p.cand_idx + (int64_t)gs * kCandCap;
+    const bool qres = rejected && q.has_q;
+    float part = 0.0f;
+    for (int t = tid; t < st; t += kThreads) {
+      const int x = cix[t];
+      const float pxv = exp2_acc(a * (cv[t] - m)) / s;
+      float w = pxv;
+      if (rejected) {
+        if (qres)
+          w = fmaxf(pxv - draft_q_of(p, q, j, x), 0.0f);
+        else if (x == dj)
+          w = 0.0f;
+      }
+      sh.u.cand.ci[t] = x;
+      sh.u.cand.cw[t] = w;
+      part += w;
+    }
+    const float total = block_sum(part, sh.red);
+    if (!(total > 0.0f)) {  // residual empty by rounding: race over p
+      for (int t = tid; t < st; t += kThreads) sh.u.cand.cw[t] = exp2_acc(a * (cv[t] - m)) / s;
+    }
+    const int x = compact_race(p, (uint32_t)gs, st, sh);
+    if (tid == 0) p.out_tokens[out_j] = x;
+    fused_post_update(p, r, K, j, x, accepted);
+    return;
+  }
+  }
+
+  if (rejected && q.has_q) {
+    // Dense residual: handed to resid_kernel (needs the full draft row).
+    if (tid == 0) {
+      p.res_req[r] = make_int4(gs, j, dj, (int)p.epoch);
+      p.res_list[1 + atomicAdd(p.res_list, 1)] = r;  // at most one entry per request: fits in max_reqs
+    }
+    return;
+  }
+
+  // Dense race over p_j (bonus row, or the rejected row with d_j removed).
+  auto entj = [&](int c) { return entry(j, c); };
+  int slot = spec_slot(j, nrow);
+  float sxj = sh.sx[j];
+  if (slot < 0) {  // no speculative state for this row: same steps, loads now
+    if (wave == 0) {
+      spec_issue(p, q, j, dj, m, entj, rs, chunk_noise(p, q.g0 + j), pr);
+      float zd = kNegInf;
+      sxj = 0.0f;
+      if (rs.cd >= 0) spec_draft_record(p, q, dj, proc_after_pen(pr), rs, entj(rs.cd).x, zd, sxj);
+      spec_publish(rs, 0, sh);
+      if (lane == 0) sh.sx[j] = sxj;
+    }
+    __syncthreads();
+    slot = 0;
+    sxj = sh.sx[j];
+  }
+  const int x = spec_finish(p, q, j, dj, m, sxj, pr, entj, slot, sh);
+  if (tid == 0) p.out_tokens[out_j] = x;
+  fused_post_update(p, r, K, j, x, accepted);
+}
+
+// ---------------------------------------------------------------------------
+// Residual pass (draft-probs mode, dense rows).  The epilogue lists each
+// rejected request (res_list: a count, then request ids) and records its row in
+// res_req with this call's epoch.  resid_kernel: chunk masses of
+// w = max(0, p_j - q_j), persistent over (listed request, segment of cps chunks)
+// items; resid_race_kernel: the race over them (one workgroup per request,
+// active when its res_req entry carries this call's epoch).
+// ---------------------------------------------------------------------------
+template <int DT>
+__global__ __launch_bounds__(kThreads) void resid_kernel(Params p) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nact = p.res_list[0];
+  // persistent: work item w = (active request w / nseg, segment w % nseg)
+  for (int w = blockIdx.x; w < nact * p.nseg; w += gridDim.x) {
+    const int r = p.res_list[1 + w / p.nseg];
+    const int seg = w % p.nseg;
+    const int4 rq = p.res_req[r];
+    const Req q = load_req(p, r);
+    const int gs = rq.x, j = rq.y;
+    const float4 ri = p.row_info[gs];
+    const float m = ri.x, inv_s = 1.0f / ri.y, a = q.a;
+    Proc pr = q.proc;
+    if (row_has_tau(__float_as_int(ri.w))) pr.tau = p.cand_tau[gs];
+    float *rt = p.res_tab + (int64_t)r * p.nc_stride;
+    for (int c = seg * p.cps + wave; c < min(p.NC, (seg + 1) * p.cps); c += kWaves) {
+      // 16 tokens per lane, all loads issued before any use
+      float z[16], qx[16];
+      load_chunk16(p, gs, c, z);
+      if (p.draft_probs != nullptr) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) qx[e] = draft_q_of(p, q, j, min(c16_tok(c, e, lane), p.V - 1));
+      } else {  // draft-logits mode: the draft row's chunk with vector loads
+        const int64_t dr = q.c0 + j;
+        load_chunk16_at(p.draft_logits, p.ddtype, p.dlstride, p.dvec_ok, p.V, dr, c, qx);
+        const float mq = p.draft_stats[2 * dr], inv_sq = 1.0f / p.draft_stats[2 * dr + 1];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) qx[e] = exp2_acc(q.aq * (qx[e] - mq)) * inv_sq;
+      }
+      float acc = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int x = c16_tok(c, e, lane);
+        if (x < p.V) {
+          const float px = exp2_acc(a * (apply_proc(z[e], x, pr) - m)) * inv_s;
+          acc += fmaxf(px - qx[e], 0.0f);
+        }
+      }
+      const float Wc = wave_sum(acc);
+      if (lane == 0) rt[c] = Wc;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void resid_race_kernel(Params p) {
+  __shared__ BlockScratch red;
+  const int r = blockIdx.x;
+  if (r == 0 && threadIdx.x == 0) p.res_list[0] = 0;  // the residual pass has read it: zero for the next call
+  const int4 rq = p.res_req[r];
+  if (rq.w != (int)p.epoch) return;
+  const Req q = load_req(p, r);
+  const int gs = rq.x, j = rq.y;
+  const float4 ri = p.row_info[gs];
+  const float m = ri.x, inv_s = 1.0f / ri.y, a = q.a;
+  Proc pr = q.proc;
+  if (row_has_tau(__float_as_int(ri.w))) pr.tau = p.cand_tau[gs];
+  const float *rt = p.res_tab + (int64_t)r * p.nc_stride;
+  // An empty residual (rounding) falls back to racing over p_j.
+  float part = 0.0f;
+  for (int c = threadIdx.x; c < p.NC; c += kThreads) part += rt[c];
+  const bool fallback = !(block_sum(part, red) > 0.0f);
+  const float2 *tab = p.chunk_tab + (int64_t)gs * p.nc_stride;
+  const int cstar = block_chunk_race(p, (uint32_t)gs, p.NC, [&](int c) -> float {
+    if (!fallback) return rt[c];
+    const float2 e = tab[c];
+    return e.x > kNegInf ? e.y * exp2_acc(a * (e.x - m)) : 0.0f;
+  }, red);
+  int x = -1;
+  if (cstar >= 0) {
+    const int x0 = cstar * kChunk + 4 * (int)threadIdx.x;
+    float z[4], qx[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {  // all loads first
+      const int xc = min(x0 + k, p.V - 1);
+      z[k] = load_logit(p, gs, xc);
+      qx[k] = draft_q_of(p, q, j, xc);
+    }
+    const uint4 w4 = rng_block(p, (uint32_t)x0 >> 2, (uint32_t)gs, kTagToken);
+    ArgMax best{-1.0f, 0x7FFFFFFF};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int xx = x0 + k;
+      if (xx < p.V) {
+        const float px = exp2_acc(a * (apply_proc(z[k], xx, pr) - m)) * inv_s;
+        const float wx = fallback ? px : fmaxf(px - qx[k], 0.0f);
+        if (wx > 0.0f) {
+          ArgMax o{race_score(wx, pick(w4, k)), xx};
+          if (better(o, best)) best = o;
+        }
+      }
+    }
+    const ArgMax bb = block_argmax(best, red);
+    x = bb.s < 0.0f ? -1 : bb.i;
+  }
+  if (threadIdx.x == 0) p.out_tokens[(int64_t)r * p.out_stride + j] = x;
+  fused_post_update(p, r, q.K, j, x, [&](int i) { return p.draft_ids[q.c0 + i]; });
+}
+
+// Request epilogue kernel: one workgroup per request, after the stats pass.
+template <bool PLAIN>
+__global__ __launch_bounds__(kThreads) void epilogue_kernel(Params p) {
+  __shared__ EpiShared sh;
+  request_epilogue<PLAIN>(p, load_req(p, blockIdx.x), sh);
+}
+
+// ---------------------------------------------------------------------------
+// Debug probabilities (parity checks): p of every processed token.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void dbg_kernel(Params p) {
+  const int g = blockIdx.y;
+  const int x = blockIdx.x * kThreads + threadIdx.x;
+  if (x >= p.V) return;
+  const int r = find_request(p.cu, p.B, g);
+  const Req q = load_req(p, r);
+  float v = 0.0f;
+  if (q.cu_ok && q.mode != kModeInvalid) {
+    const float4 ri = p.row_info[g];
+    const int st = __float_as_int(ri.w);
+    if (q.mode == kModeGreedy) {
+      v = (x == __float_as_int(ri.z)) ? 1.0f : 0.0f;
+    } else {
+      Proc pr = q.proc;
+      if (st != kRowDense) pr.tau = p.cand_tau[g];
+      v = exp2_acc(q.a * (apply_proc(load_logit(p, g, x), x, pr) - ri.x)) / ri.y;
+    }
+  }
+  p.dbg_probs[(int64_t)g * p.V + x] = v;
+}
+
+// ---------------------------------------------------------------------------
+// post_update ("【vllm】DeepSeekMTP、eagle", _post_update_kernel walk-through).
+// ---------------------------------------------------------------------------
+// One thread per (request, output slot): every load is issued at once (indices
+// clamped into range), the histogram updates are fire-and-forget atomics, and
+// the thread holding the last sampled token also writes last_sampled and
+// advances num_computed.
+__global__ __launch_bounds__(kThreads) void post_update_kernel(PostParams p) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t total = (int64_t)p.B * p.tokens_stride;
+  if (i >= total) return;
+  const int r = (int)(i / p.tokens_stride), t = (int)(i - (int64_t)r * p.tokens_stride);
+  const int n = p.num_sampled[r];
+  const int s = p.idx_mapping[r];
+  const int tok = p.tokens[i];
+  const int ql = p.query_len[r];
+  const int nr = p.num_rejected[r];
+  const int nn = min(n, p.tokens_stride);
+  if (nn <= 0 || t >= nn) return;
+  if (s < 0 || s >= p.num_slots) {
+    if (t == 0) atomicOr(p.err, SV_ERR_SLOT);
+    return;
+  }
+  if (tok >= 0 && tok < p.V) atomicAdd(&p.counts[(int64_t)s * p.V + tok], 1);
+  if (t == nn - 1) {
+    p.last_sampled[s] = tok;
+    atomicAdd(&p.num_computed[s], ql - nr);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Debug: the library's own random stream and Exp(1) noise, value for value
+// (tests compare them with the published known-answer vectors and the oracle).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void dbg_philox_kernel(const uint4 *ctr, int64_t n, uint32_t k0, uint32_t k1,
+                                                             uint4 *out) {
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads)
+    out[i] = philox10(ctr[i], k0, k1);
+}
+
+__global__ __launch_bounds__(kThreads) void dbg_noise_kernel(const uint32_t *words, int64_t n, float *out) {
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads)
+    out[i] = exp_noise(words[i]);
+}
+
+}  // namespace
+
+hipError_t launch_epilogue(const Params &p, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+  const bool plain = plain_call(p);
+  const void *fn = plain ? reinterpret_cast<const void *>(&epilogue_kernel<true>)
+                         : reinterpret_cast<const void *>(&epilogue_kernel<false>);
+  return launch_timed(fn, dim3((unsigned)p.B), p, s, t0, t1);
+}
+
+__global__ void zero_count_kernel(int *count) { *count = 0; }
+
+hipError_t launch_zero_count(int *count, hipStream_t s) {
+  zero_count_kernel<<<dim3(1), dim3(1), 0, s>>>(count);
+  return hipGetLastError();
+}
+
+hipError_t launch_resid(const Params &p, hipStream_t s) {
+  const dim3 grid((unsigned)p.resid_grid);
+  if (p.dtype == 1)
+    resid_kernel<1><<<grid, dim3(kThreads), 0, s>>>(p);
+  else
+    resid_kernel<0><<<grid, dim3(kThreads), 0, s>>>(p);
+  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  resid_race_kernel<<<dim3((unsigned)p.B), dim3(kThreads), 0, s>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_dbg_probs(const Params &p, hipStream_t s) {
+  const dim3 grid((unsigned)((p.V + kThreads - 1) / kThreads), (unsigned)p.R);
+  dbg_kernel<<<grid, dim3(kThreads), 0, s>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_post_update(const PostParams &p, hipStream_t s) {
+  const int64_t total = (int64_t)p.B * p.tokens_stride;
+  post_update_kernel<<<dim3((unsigned)((total + kThreads - 1) / kThreads)), dim3(kThreads), 0, s>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_dbg_philox(const uint32_t *ctr, int64_t n, uint64_t key, uint32_t *out, hipStream_t s) {
+  const int64_t blocks = (n + kThreads - 1) / kThreads;
+  dbg_philox_kernel<<<dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(kThreads), 0, s>>>(
+      reinterpret_cast<const uint4 *>(ctr), n, (uint32_t)(key & 0xFFFFFFFFu), (uint32_t)(key >> 32),
+      reinterpret_cast<uint4 *>(out));
+  return hipGetLastError();
+}
+
+hipError_t launch_dbg_noise(const uint32_t *words, int64_t n, float *out, hipStream_t s) {
+  const int64_t blocks = (n + kThreads - 1) / kThreads;
+  dbg_noise_kernel<<<dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(kThreads), 0, s>>>(words, n, out);
+  return hipGetLastError();
+}
+
+}  // namespace sv

@@ -154,7 +154,8 @@ struct PostParams {
   unsigned int *err;
 };
 
-// Launchers (sv_kernels.hip).  Return the hipError_t of the last launch.
+// Launchers (sv_stats.hip, sv_topk.hip, sv_topp.hip, sv_epilogue.hip,
+// sv_draft.hip).  Return the hipError_t of the last launch.
 hipError_t launch_topk(const Params &p, hipStream_t s, hipEvent_t t0, hipEvent_t t1);
 hipError_t launch_topp(const Params &p, hipStream_t s);
 // t0, t1: optional events stamped at the kernel's start and end (may be null).

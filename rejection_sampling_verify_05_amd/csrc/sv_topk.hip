@@ -1,0 +1,412 @@
+// sv_topk.hip -- the top-k pass: per target row, the exact k-th largest processed logit and the kept tokens.
+#include <stdint.h>
+
+#include "sv_common.h"
+#include "sv_tiles.h"
+
+namespace sv {
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// Top-k pass: one workgroup per row.
+// ---------------------------------------------------------------------------
+constexpr int kBuf = 2048;   // LDS candidate buffer
+
+struct TopkShared {
+  float bv[kBuf];
+  int bi[kBuf];
+  unsigned hist[256];
+  int n;
+  int tile_n[2];  // passers of the current super-tile (by parity: one is reset while the other counts)
+  int sel, want;
+  float theta;
+  BlockScratch red;
+};
+static_assert(kBuf >= 2 * kCandCap, "the id-ordered kept list is staged in the upper half of the buffer");
+
+
+// One MSD radix digit: among keys matching (prefix, mask), find the digit at
+// `shift` holding the want-th largest; updates prefix/mask/want (uniform).
+__device__ __forceinline__ void radix_digit(TopkShared &sh, int shift, uint32_t &prefix, uint32_t &mask, int &want) {
+  // Wave 0 finds the digit: lane l holds bins 255-4l .. 252-4l (descending),
+  // an inclusive prefix sum over lanes gives the count of larger digits.
+  if (threadIdx.x < 64) {
+    const int l = threadIdx.x;
+    const int h0 = (int)sh.hist[255 - 4 * l], h1 = (int)sh.hist[254 - 4 * l];
+    const int h2 = (int)sh.hist[253 - 4 * l], h3 = (int)sh.hist[252 - 4 * l];
+    const int own = h0 + h1 + h2 + h3;
+    int incl = own;  // inclusive scan over lanes (Hillis-Steele with shuffles)
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(incl, d, 64);
+      if (l >= d) incl += o;
+    }
+    const int before = incl - own;  // count in bins above this lane's four
+    const bool here = before < want && incl >= want;
+    if (here) {
+      int acc = before, b = 255 - 4 * l;
+      const int hh[4] = {h0, h1, h2, h3};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (acc + hh[i] >= want) {
+          b = 255 - 4 * l - i;
+          break;
+        }
+        acc += hh[i];
+      }
+      sh.sel = b;
+      sh.want = want - acc;
+    }
+  }
+  __syncthreads();
+  prefix |= (uint32_t)sh.sel << shift;
+  mask |= 0xFFu << shift;
+  want = sh.want;
+  __syncthreads();
+}
+
+// Candidates appended with their raw logit (penalty still to apply) carry
+// index | kUnresolved.  Applies the penalty to every such entry.
+constexpr int kUnresolved = (int)0x80000000;
+__device__ __forceinline__ void resolve_buffer(TopkShared &sh, int n, const Proc &pr) {
+  for (int e = threadIdx.x; e < n; e += kThreads) {
+    const int xi = sh.bi[e];
+    if (xi & kUnresolved) {
+      const int x = xi & 0x7FFFFFFF;
+      float z = sh.bv[e];
+      const int c = pr.counts[x];
+      if (c > 0) z = penalize(z, c, pr);
+      sh.bv[e] = z;
+      sh.bi[e] = x;
+    }
+  }
+  __syncthreads();
+}
+
+// k-th largest value among sh.bv[0..n) (1 <= k <= n).
+__device__ __forceinline__ float buffer_kth(TopkShared &sh, int n, int k) {
+  uint32_t prefix = 0, mask = 0;
+  int want = k;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    sh.hist[threadIdx.x] = 0;
+    __syncthreads();
+    for (int e = threadIdx.x; e < n; e += kThreads) {
+      const uint32_t key = ukey(sh.bv[e]);
+      if ((key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & 0xFFu], 1u);
+    }
+    __syncthreads();
+    radix_digit(sh, shift, prefix, mask, want);
+  }
+  return ukey_val(prefix);
+}
+
+// In-place compaction of the candidate buffer: keeps entry e < n when
+// keep(value, index) holds, and sets sh.n.  Each thread reads its entries into
+// registers (fixed slots, no dynamic indexing), then appends the kept ones.
+template <class KEEP>
+__device__ __forceinline__ void buffer_compact(TopkShared &sh, int n, KEEP keep) {
+  float kv[kBuf / kThreads];
+  int ki[kBuf / kThreads];
+  bool kk[kBuf / kThreads];
+#pragma unroll
+  for (int m = 0; m < kBuf / kThreads; ++m) {
+    const int e = threadIdx.x + m * kThreads;
+    kv[m] = e < n ? sh.bv[e] : 0.0f;
+    ki[m] = e < n ? sh.bi[e] : -1;
+    kk[m] = e < n && keep(kv[m], ki[m]);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) sh.n = 0;
+  __syncthreads();
+#pragma unroll
+  for (int m = 0; m < kBuf / kThreads; ++m) {
+    if (kk[m]) {
+      const int pos = atomicAdd(&sh.n, 1);
+      sh.bv[pos] = kv[m];
+      sh.bi[pos] = ki[m];
+    }
+  }
+  __syncthreads();
+}
+// Keep the buffer entries >= t (order not preserved).
+__device__ __forceinline__ void buffer_keep(TopkShared &sh, int n, float t) {
+  buffer_compact(sh, n, [t](float v, int) { return v >= t; });
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void topk_kernel(Params p) {
+  __shared__ TopkShared sh;
+  const int g = blockIdx.x;
+  const int r = find_request(p.cu, p.B, g);
+  const Req q = load_req(p, r);
+  const int k = p.top_k[r];
+  const bool use = q.cu_ok && g >= q.g0 && g <= q.g0 + q.K && q.mode == kModeSample && k >= 1 && k < p.V;
+  if (!use) {
+    if (threadIdx.x == 0) {
+      p.cand_n[g] = kRowDense;
+      p.cand_tau[g] = kNegInf;
+    }
+    return;
+  }
+  const Proc pr = q.proc;  // penalty only
+
+  if (threadIdx.x == 0) {
+    sh.n = 0;
+    sh.theta = kNegInf;
+    sh.tile_n[0] = sh.tile_n[1] = 0;
+  }
+  __syncthreads();
+  // Streaming filter in super-tiles of kTopkTile tokens, kTopkPer per thread
+  // (vector loads, all in flight together).  A token passes when its processed
+  // logit is >= the running threshold theta (a lower bound of tau_k: the k-th
+  // largest of a subset of the row).  With a repetition penalty >= 1 and
+  // frequency and presence penalties >= 0 the penalties never raise a logit
+  // (each step rounds monotonically), so later super-tiles test the raw logit and the counts
+  // of the few passers are read only when a selection needs them.  Two barriers
+  // per super-tile: one to count the passers (compacting the candidate buffer
+  // first if they would not fit), one after they are appended.
+  const bool pen = pr.counts != nullptr;
+  const bool raw_first = !pen || (pr.theta >= 1.0f && pr.freq >= 0.0f && pr.pres >= 0.0f);
+  bool overflow = k > kCandCap;
+  constexpr int kFirstPer = kBuf / kThreads;  // the first kBuf tokens are all kept
+  if (!overflow) {
+    float z[kFirstPer];
+    load_topk_tile<DT, kFirstPer>(p, g, 0, z);
+    if (pen) penalize_tile<DT, kFirstPer>(p, pr, 0, z);
+#pragma unroll
+    for (int e = 0; e < kFirstPer; ++e) {
+      const int x = topk_tok<DT>(0, e);
+      sh.bv[threadIdx.x * kFirstPer + e] = z[e];
+      sh.bi[threadIdx.x * kFirstPer + e] = x < p.V && z[e] > kNegInf ? x : -1;
+    }
+    __syncthreads();
+    // compact the finite entries, then theta = their k-th largest
+    buffer_compact(sh, kBuf, [](float, int x) { return x >= 0; });
+    const int n = sh.n;
+    if (n >= k) {
+      const float t = buffer_kth(sh, n, k);
+      buffer_keep(sh, n, t);
+      if (threadIdx.x == 0) sh.theta = t;
+    }
+    __syncthreads();
+  }
+  // One super-tile: filter z (raw logits) against theta, count the passers,
+  // make room if needed, append them.  All threads call it (barriers inside).
+  auto tile_step = [&](int base, int par, float (&z)[kTopkPer]) {
+    // sh.n and sh.theta last changed before the previous super-tile's final
+    // barrier: every thread reads the same values here.
+    const int n0 = sh.n;
+    const float th = sh.theta;
+    if (!raw_first) penalize_tile<DT>(p, pr, base, z);  // a penalty < 1 can raise logits: test processed ones
+    int npass = 0;
+#pragma unroll
+    for (int e = 0; e < kTopkPer; ++e) {
+      const int x = topk_tok<DT>(base, e);
+      z[e] = (x < p.V && z[e] >= th && z[e] > kNegInf) ? z[e] : kNegInf;
+      npass += z[e] > kNegInf ? 1 : 0;
+    }
+    if (npass) atomicAdd(&sh.tile_n[par], npass);
+    __syncthreads();
+    if (threadIdx.x == 0) sh.tile_n[par ^ 1] = 0;  // read last in the previous super-tile
+    if (n0 + sh.tile_n[par] > kBuf) {
+      // Not enough room: theta becomes the k-th largest kept candidate
+      // (penalties applied first); this super-tile's passers are re-tested.
+      if (n0 < k) {
+        overflow = true;  // fewer than k finite logits so far and a full tile: exact radix select below
+      } else {
+        if (pen) resolve_buffer(sh, n0, pr);
+        const float t = buffer_kth(sh, n0, k);
+        buffer_keep(sh, n0, t);
+        if (threadIdx.x == 0) {
+          sh.theta = t;
+          sh.tile_n[par] = 0;
+        }
+        __syncthreads();
+        npass = 0;
+#pragma unroll
+        for (int e = 0; e < kTopkPer; ++e) {
+          if (!(z[e] >= t)) z[e] = kNegInf;
+          npass += z[e] > kNegInf ? 1 : 0;
+        }
+        if (npass) atomicAdd(&sh.tile_n[par], npass);
+        __syncthreads();
+        const bool full = sh.n + sh.tile_n[par] > kBuf;  // ties at theta: exact radix select below
+        __syncthreads();  // every thread has read the counts before anyone appends
+        overflow = full;
+      }
+    }
+    if (overflow) return;
+    const int flag = raw_first && pen ? kUnresolved : 0;  // raw logits: penalty applied at the next selection
+#pragma unroll
+    for (int e = 0; e < kTopkPer; ++e) {
+      if (z[e] > kNegInf) {
+        const int pos = atomicAdd(&sh.n, 1);
+        sh.bv[pos] = z[e];
+        sh.bi[pos] = topk_tok<DT>(base, e) | flag;
+      }
+    }
+    __syncthreads();
+  };
+  if (p.vec_ok) {
+    // Two super-tiles in flight: the next one's loads are issued before this
+    // one is filtered.
+    constexpr int VW = TopkRaw<DT>::VW;
+    const int vfull = p.V - p.V % VW;
+    TopkRaw<DT> ra, rb;
+    int base = kBuf, par = 0;
+    topk_issue<DT>(p, g, base, vfull, ra);
+    topk_issue<DT>(p, g, base + kTopkTile, vfull, rb);
+    while (base < vfull && !overflow) {
+      float z[kTopkPer];
+      topk_decode<DT>(base, vfull, ra, z);
+      topk_issue<DT>(p, g, base + 2 * kTopkTile, vfull, ra);
+      tile_step(base, par, z);
+      base += kTopkTile;
+      par ^= 1;
+      if (base >= vfull || overflow) break;
+      topk_decode<DT>(base, vfull, rb, z);
+      topk_issue<DT>(p, g, base + 2 * kTopkTile, vfull, rb);
+      tile_step(base, par, z);
+      base += kTopkTile;
+      par ^= 1;
+    }
+    if (!overflow && vfull < p.V) {  // the last V % VW tokens, penalty applied at once
+      if (sh.n > kBuf - VW) {  // make room (n >= k here: k <= kCandCap < kBuf - VW)
+        const int n = sh.n;
+        if (pen) resolve_buffer(sh, n, pr);
+        const float t = buffer_kth(sh, n, k);
+        buffer_keep(sh, n, t);
+        if (threadIdx.x == 0) sh.theta = t;
+        __syncthreads();
+      }
+      const int x = vfull + (int)threadIdx.x;
+      if (x < p.V) {
+        const float z = apply_proc(load_logit(p, g, x), x, pr);
+        if (z >= sh.theta && z > kNegInf) {
+          const int pos = atomicAdd(&sh.n, 1);
+          sh.bv[pos] = z;
+          sh.bi[pos] = x;
+        }
+      }
+      __syncthreads();
+    }
+  } else {
+    for (int base = kBuf, par = 0; base < p.V && !overflow; base += kTopkTile, par ^= 1) {
+      float z[kTopkPer];
+      load_topk_tile<DT>(p, g, base, z);
+      tile_step(base, par, z);
+    }
+  }
+  if (pen && !overflow) resolve_buffer(sh, sh.n, pr);
+
+  float tau;
+  int ncand = -1;
+  if (!overflow) {
+    const int n = sh.n;
+    if (n < k) {
+      tau = kNegInf;  // fewer than k finite logits: nothing is removed
+    } else {
+      tau = buffer_kth(sh, n, k);
+      buffer_keep(sh, n, tau);
+      ncand = sh.n;
+    }
+  } else {
+    // Exact tau by MSD radix select over the whole row (many ties).
+    uint32_t prefix = 0, mask = 0;
+    int want = k;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      sh.hist[threadIdx.x] = 0;
+      __syncthreads();
+      for (int x = threadIdx.x; x < p.V; x += kThreads) {
+        const uint32_t key = ukey(apply_proc(load_logit(p, g, x), x, pr));
+        if ((key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & 0xFFu], 1u);
+      }
+      __syncthreads();
+      radix_digit(sh, shift, prefix, mask, want);
+    }
+    tau = ukey_val(prefix);
+  }
+
+  if (ncand < 0 || ncand > kCandCap) {
+    if (threadIdx.x == 0) {
+      p.cand_n[g] = (tau > kNegInf) ? kRowThreshold : kRowDense;
+      p.cand_tau[g] = tau;
+    }
+    return;
+  }
+
+  // The kept tokens in increasing id order, staged in the upper half of the
+  // buffer: each one's position is the number of kept tokens with a smaller id
+  // (ids are distinct).
+  float *sv_ = sh.bv + kCandCap;
+  int *si_ = sh.bi + kCandCap;
+  for (int e = threadIdx.x; e < ncand; e += kThreads) {
+    const int id = sh.bi[e];
+    int rank = 0;
+    for (int t = 0; t < ncand; ++t) rank += sh.bi[t] < id ? 1 : 0;
+    sv_[rank] = sh.bv[e];
+    si_[rank] = id;
+  }
+  __syncthreads();
+  int nout = ncand;
+  if (q.top_p < 1.0f) {
+    // Top-p over the candidates, which hold the whole top-k distribution:
+    // weights w = exp2(a (z - m)), S = sum w; token e stays iff the weight of
+    // the tokens with a larger logit is below top_p * S.  Sums run in id order
+    // (fixed, so the result replays bit for bit).  sh.bi[0..ncand) then holds
+    // the kept flags.
+    float lm = kNegInf;
+    for (int e = threadIdx.x; e < ncand; e += kThreads) lm = fmaxf(lm, sv_[e]);
+    const float m = block_max(lm, sh.red);
+    const float a = q.a;
+    float ls = 0.0f;
+    for (int e = threadIdx.x; e < ncand; e += kThreads) ls += exp2_acc(a * (sv_[e] - m));
+    const float bound = q.top_p * block_sum(ls, sh.red);
+    for (int e = threadIdx.x; e < ncand; e += kThreads) {
+      const float ze = sv_[e];
+      float above = 0.0f;
+      for (int t = 0; t < ncand; ++t)
+        if (sv_[t] > ze) above += exp2_acc(a * (sv_[t] - m));
+      sh.bi[e] = above < bound ? 1 : 0;
+    }
+    __syncthreads();
+    // The kept set is every token with z >= the smallest kept logit, which is
+    // also the row's new threshold for single-token lookups.
+    float lt = __builtin_inff();
+    for (int e = threadIdx.x; e < ncand; e += kThreads)
+      if (sh.bi[e]) lt = fminf(lt, sv_[e]);
+    tau = -block_max(-lt, sh.red);
+    int pos = 0;
+    for (int e = threadIdx.x; e < ncand; e += kThreads) {
+      if (sh.bi[e]) {
+        pos = 0;
+        for (int t = 0; t < e; ++t) pos += sh.bi[t];
+        p.cand_val[(int64_t)g * kCandCap + pos] = sv_[e];
+        p.cand_idx[(int64_t)g * kCandCap + pos] = si_[e];
+      }
+    }
+    int lk = 0;
+    for (int e = threadIdx.x; e < ncand; e += kThreads) lk += sh.bi[e];
+    nout = (int)block_sum((float)lk, sh.red);
+  } else {
+    for (int e = threadIdx.x; e < ncand; e += kThreads) {
+      p.cand_val[(int64_t)g * kCandCap + e] = sv_[e];
+      p.cand_idx[(int64_t)g * kCandCap + e] = si_[e];
+    }
+  }
+  if (threadIdx.x == 0) {
+    p.cand_n[g] = nout;
+    p.cand_tau[g] = tau;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_topk(const Params &p, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+  const void *fn = p.dtype == 1 ? reinterpret_cast<const void *>(&topk_kernel<1>)
+                                : reinterpret_cast<const void *>(&topk_kernel<0>);
+  return launch_timed(fn, dim3((unsigned)p.R), p, s, t0, t1);
+}
+
+}  // namespace sv

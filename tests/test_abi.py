@@ -149,6 +149,7 @@ def test_strerror_and_host_checks_without_gpu():
     n = ctypes.c_int32(7)
     assert L.spec_verify_profile_read(None, None, None, ctypes.byref(n)) == sv.SV_EINVAL
     L.spec_verify_destroy(None)
+    sv.spec_verify_destroy(ctypes.c_void_p())  # an empty handle: nothing to free
     assert L.spec_verify_debug_philox(None, -1, 0, None, None) == sv.SV_EINVAL
     assert L.spec_verify_debug_philox(None, 0, 0, None, None) == sv.SV_OK
     assert L.spec_verify_debug_philox(None, 4, 0, None, None) == sv.SV_EINVAL
