@@ -52,27 +52,27 @@ __device__ __forceinline__ void load_topk_tile(const Params &p, int g, int base,
 // vectors are issued unconditionally (a vector not wholly inside [0, vfull)
 // reads the row start) and decoded later; tokens in [vfull, V) are handled
 // apart, after the loop.
-template <int DT>
+template <int DT, int NPER = kTopkPer>
 struct TopkRaw {
   static constexpr int VW = DT == 1 ? 8 : 4;
-  u32x4 v[kTopkPer / VW];
+  u32x4 v[NPER / VW];
 };
-template <int DT, int NT = kThreads>
-__device__ __forceinline__ void topk_issue(const Params &p, int g, int base, int vfull, TopkRaw<DT> &r) {
-  constexpr int VW = TopkRaw<DT>::VW;
+template <int DT, int NT = kThreads, int NPER = kTopkPer>
+__device__ __forceinline__ void topk_issue(const Params &p, int g, int base, int vfull, TopkRaw<DT, NPER> &r) {
+  constexpr int VW = TopkRaw<DT, NPER>::VW;
   const char *row = static_cast<const char *>(p.logits) + (int64_t)g * p.lstride * (DT == 1 ? 2 : 4);
 #pragma unroll
-  for (int v = 0; v < kTopkPer / VW; ++v) {
+  for (int v = 0; v < NPER / VW; ++v) {
     const int x0 = topk_tok<DT, NT>(base, v * VW);
     const uint32_t off = x0 + VW <= vfull ? (uint32_t)x0 * (DT == 1 ? 2u : 4u) : 0u;
     r.v[v] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(row + off));
   }
 }
-template <int DT, int NT = kThreads>
-__device__ __forceinline__ void topk_decode(int base, int vfull, const TopkRaw<DT> &r, float (&z)[kTopkPer]) {
-  constexpr int VW = TopkRaw<DT>::VW;
+template <int DT, int NT = kThreads, int NPER = kTopkPer>
+__device__ __forceinline__ void topk_decode(int base, int vfull, const TopkRaw<DT, NPER> &r, float (&z)[NPER]) {
+  constexpr int VW = TopkRaw<DT, NPER>::VW;
 #pragma unroll
-  for (int v = 0; v < kTopkPer / VW; ++v) {
+  for (int v = 0; v < NPER / VW; ++v) {
     const int x0 = topk_tok<DT, NT>(base, v * VW);
     const uint32_t ww[4] = {r.v[v].x, r.v[v].y, r.v[v].z, r.v[v].w};
 #pragma unroll

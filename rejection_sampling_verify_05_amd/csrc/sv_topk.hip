@@ -67,22 +67,8 @@ __device__ __forceinline__ void radix_digit(TopkShared &sh, int shift, uint32_t 
 }
 
 // Candidates appended with their raw logit (penalty still to apply) carry
-// index | kUnresolved.  Applies the penalty to every such entry.
+// index | kUnresolved.
 constexpr int kUnresolved = (int)0x80000000;
-__device__ __forceinline__ void resolve_buffer(TopkShared &sh, int n, const Proc &pr) {
-  for (int e = threadIdx.x; e < n; e += kThreads) {
-    const int xi = sh.bi[e];
-    if (xi & kUnresolved) {
-      const int x = xi & 0x7FFFFFFF;
-      float z = sh.bv[e];
-      const int c = pr.counts[x];
-      if (c > 0) z = penalize(z, c, pr);
-      sh.bv[e] = z;
-      sh.bi[e] = x;
-    }
-  }
-  __syncthreads();
-}
 
 // k-th largest value among sh.bv[0..n) (1 <= k <= n).
 __device__ __forceinline__ float buffer_kth(TopkShared &sh, int n, int k) {
@@ -99,6 +85,54 @@ __device__ __forceinline__ float buffer_kth(TopkShared &sh, int n, int k) {
     radix_digit(sh, shift, prefix, mask, want);
   }
   return ukey_val(prefix);
+}
+
+// Resolves (applies the penalty to) the unresolved entries whose value is >=
+// t; returns, the same in every thread, whether any value changed.  The
+// counts of a thread's entries are loaded four at a time.
+__device__ __forceinline__ bool resolve_at_least(TopkShared &sh, int n, float t, const Proc &pr) {
+  constexpr int M = 4;  // entries per batch (two batches: the registers of the tiles in flight stay free)
+  bool changed = false;
+#pragma unroll
+  for (int h = 0; h < kBuf / kThreads; h += M) {
+    int xs[M], c[M];
+    float vs[M];
+    bool need[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const int e = threadIdx.x + (h + m) * kThreads;
+      xs[m] = e < n ? sh.bi[e] : 0;
+      vs[m] = e < n ? sh.bv[e] : kNegInf;
+      need[m] = e < n && (xs[m] & kUnresolved) && vs[m] >= t;
+    }
+#pragma unroll
+    for (int m = 0; m < M; ++m) c[m] = need[m] ? pr.counts[xs[m] & 0x7FFFFFFF] : 0;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      if (need[m]) {
+        const int e = threadIdx.x + (h + m) * kThreads;
+        const float z = c[m] > 0 ? penalize(vs[m], c[m], pr) : vs[m];
+        changed |= z != vs[m];
+        sh.bv[e] = z;
+        sh.bi[e] = xs[m] & 0x7FFFFFFF;
+      }
+    }
+  }
+  return __syncthreads_or(changed) != 0;
+}
+
+// The k-th largest processed value among the n buffer entries (k <= n), where
+// unresolved entries hold raw logits that are never below their processed
+// value (penalties that cannot raise a logit).  Only entries that can reach
+// the k-th largest are resolved: take t = the k-th largest current value,
+// resolve the unresolved entries >= t, and repeat while that changed a value.
+// At the end every entry >= t holds its processed value and every other entry
+// is below t, so t is exact.
+__device__ __forceinline__ float select_tau(TopkShared &sh, int n, int k, const Proc &pr) {
+  for (;;) {
+    const float t = buffer_kth(sh, n, k);
+    if (pr.counts == nullptr || !resolve_at_least(sh, n, t, pr)) return t;
+  }
 }
 
 // In-place compaction of the candidate buffer: keeps entry e < n when
@@ -134,12 +168,43 @@ __device__ __forceinline__ void buffer_keep(TopkShared &sh, int n, float t) {
   buffer_compact(sh, n, [t](float v, int) { return v >= t; });
 }
 
+// Offsets of this thread's passers within a super-tile: an exclusive prefix
+// over the wave, and one LDS atomic per wave (on tile_n[par]) for the wave's
+// base.  Returns the wave's base; excl receives the thread's offset in the wave.
+__device__ __forceinline__ int wave_offsets(TopkShared &sh, int npass, int par, int &excl) {
+  const int lane = threadIdx.x & 63;
+  int incl = npass;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += o;
+  }
+  excl = incl - npass;
+  const int wtot = __shfl(incl, 63, 64);
+  int wb = 0;
+  if (lane == 63 && wtot > 0) wb = atomicAdd(&sh.tile_n[par], wtot);
+  return __shfl(wb, 63, 64);
+}
+
 template <int DT>
-__global__ __launch_bounds__(kThreads) void topk_kernel(Params p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void topk_kernel(Params p) {
   __shared__ TopkShared sh;
   const int g = blockIdx.x;
-  const int r = find_request(p.cu, p.B, g);
-  const Req q = load_req(p, r);
+  constexpr int kFirstPer = kBuf / kThreads;  // the first kBuf tokens: kFirstPer per thread
+  constexpr int VW = TopkRaw<DT>::VW;
+  const int vfull = p.V - p.V % VW;
+  // Aligned rows: the row's first loads (its first kBuf tokens and the first
+  // two streaming super-tiles) do not depend on its request and are issued
+  // before the lookup; the last V % VW tokens are taken apart at the end.
+  TopkRaw<DT, kFirstPer> r0;
+  TopkRaw<DT> ra, rb;
+  if (p.vec_ok) {
+    topk_issue<DT, kThreads, kFirstPer>(p, g, 0, vfull, r0);
+    topk_issue<DT>(p, g, kBuf, vfull, ra);
+    topk_issue<DT>(p, g, kBuf + kTopkTile, vfull, rb);
+  }
+  const Req q = lookup_req(p, g);  // one wide load in the common case
+  const int r = q.r;
   const int k = p.top_k[r];
   const bool use = q.cu_ok && g >= q.g0 && g <= q.g0 + q.K && q.mode == kModeSample && k >= 1 && k < p.V;
   if (!use) {
@@ -164,15 +229,90 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(Params p) {
   // frequency and presence penalties >= 0 the penalties never raise a logit
   // (each step rounds monotonically), so later super-tiles test the raw logit and the counts
   // of the few passers are read only when a selection needs them.  Two barriers
-  // per super-tile: one to count the passers (compacting the candidate buffer
-  // first if they would not fit), one after they are appended.
+  // per super-tile: one to count the passers (one LDS atomic per wave; the
+  // candidate buffer is compacted first if they would not fit), one after they
+  // are appended.
   const bool pen = pr.counts != nullptr;
   const bool raw_first = !pen || (pr.theta >= 1.0f && pr.freq >= 0.0f && pr.pres >= 0.0f);
   bool overflow = k > kCandCap;
-  constexpr int kFirstPer = kBuf / kThreads;  // the first kBuf tokens are all kept
-  if (!overflow) {
+  if (!overflow && k <= kThreads) {
+    // First threshold: the k-th largest of the threads' maxima over the first
+    // kBuf tokens (k distinct tokens reach it, so it is a lower bound of
+    // tau_k), found by wave 0 alone; then the first tokens that reach it are
+    // appended.  Values and counts are loaded together.
     float z[kFirstPer];
-    load_topk_tile<DT, kFirstPer>(p, g, 0, z);
+    int cnt[kFirstPer];
+    if (pen) {
+#pragma unroll
+      for (int e = 0; e < kFirstPer; ++e) cnt[e] = pr.counts[min(topk_tok<DT>(0, e), p.V - 1)];
+    }
+    if (p.vec_ok)
+      topk_decode<DT, kThreads, kFirstPer>(0, vfull, r0, z);
+    else
+      load_topk_tile<DT, kFirstPer>(p, g, 0, z);
+    float tmax = kNegInf;
+#pragma unroll
+    for (int e = 0; e < kFirstPer; ++e) {
+      if (pen && topk_tok<DT>(0, e) < p.V && cnt[e] > 0) z[e] = penalize(z[e], cnt[e], pr);
+      if (z[e] > kNegInf) tmax = fmaxf(tmax, z[e]);
+    }
+    sh.bv[threadIdx.x] = tmax;
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      // MSD bitwise select of the k-th largest of 256 keys, four per lane.
+      const int lane = threadIdx.x;
+      uint32_t key[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) key[i] = ukey(sh.bv[4 * lane + i]);
+      uint32_t prefix = 0;
+      int want = k;
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t hi = bit == 31 ? 0u : ~0u << (bit + 1);
+        int ones = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ones += __popcll(__ballot((key[i] & hi) == prefix && ((key[i] >> bit) & 1u)));
+        if (ones >= want)
+          prefix |= 1u << bit;
+        else
+          want -= ones;
+      }
+      if (lane == 0) sh.theta = ukey_val(prefix);
+    }
+    __syncthreads();
+    const float th = sh.theta;
+    int npass = 0;
+#pragma unroll
+    for (int e = 0; e < kFirstPer; ++e) {
+      if (!(z[e] >= th && z[e] > kNegInf)) z[e] = kNegInf;
+      npass += z[e] > kNegInf ? 1 : 0;
+    }
+    int excl;
+    const int wb = wave_offsets(sh, npass, 0, excl);
+    __syncthreads();
+    const int n = sh.tile_n[0];
+    int pos = wb + excl;
+#pragma unroll
+    for (int e = 0; e < kFirstPer; ++e) {
+      if (z[e] > kNegInf) {
+        sh.bv[pos] = z[e];
+        sh.bi[pos] = topk_tok<DT>(0, e);
+        ++pos;
+      }
+    }
+    __syncthreads();  // every thread has read tile_n[0]
+    if (threadIdx.x == 0) {
+      sh.n = n;
+      sh.tile_n[0] = 0;
+    }
+    __syncthreads();
+  } else if (!overflow) {
+    // k above the thread count: theta = the exact k-th largest of the first
+    // kBuf tokens.
+    float z[kFirstPer];
+    if (p.vec_ok)
+      topk_decode<DT, kThreads, kFirstPer>(0, vfull, r0, z);
+    else
+      load_topk_tile<DT, kFirstPer>(p, g, 0, z);
     if (pen) penalize_tile<DT, kFirstPer>(p, pr, 0, z);
 #pragma unroll
     for (int e = 0; e < kFirstPer; ++e) {
@@ -196,7 +336,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(Params p) {
   auto tile_step = [&](int base, int par, float (&z)[kTopkPer]) {
     // sh.n and sh.theta last changed before the previous super-tile's final
     // barrier: every thread reads the same values here.
-    const int n0 = sh.n;
+    int n0 = sh.n;
     const float th = sh.theta;
     if (!raw_first) penalize_tile<DT>(p, pr, base, z);  // a penalty < 1 can raise logits: test processed ones
     int npass = 0;
@@ -206,17 +346,18 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(Params p) {
       z[e] = (x < p.V && z[e] >= th && z[e] > kNegInf) ? z[e] : kNegInf;
       npass += z[e] > kNegInf ? 1 : 0;
     }
-    if (npass) atomicAdd(&sh.tile_n[par], npass);
+    int excl;
+    int wb = wave_offsets(sh, npass, par, excl);
     __syncthreads();
     if (threadIdx.x == 0) sh.tile_n[par ^ 1] = 0;  // read last in the previous super-tile
-    if (n0 + sh.tile_n[par] > kBuf) {
+    int tot = sh.tile_n[par];
+    if (n0 + tot > kBuf) {
       // Not enough room: theta becomes the k-th largest kept candidate
       // (penalties applied first); this super-tile's passers are re-tested.
       if (n0 < k) {
         overflow = true;  // fewer than k finite logits so far and a full tile: exact radix select below
       } else {
-        if (pen) resolve_buffer(sh, n0, pr);
-        const float t = buffer_kth(sh, n0, k);
+        const float t = select_tau(sh, n0, k, pr);
         buffer_keep(sh, n0, t);
         if (threadIdx.x == 0) {
           sh.theta = t;
@@ -229,34 +370,33 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(Params p) {
           if (!(z[e] >= t)) z[e] = kNegInf;
           npass += z[e] > kNegInf ? 1 : 0;
         }
-        if (npass) atomicAdd(&sh.tile_n[par], npass);
+        wb = wave_offsets(sh, npass, par, excl);
         __syncthreads();
-        const bool full = sh.n + sh.tile_n[par] > kBuf;  // ties at theta: exact radix select below
-        __syncthreads();  // every thread has read the counts before anyone appends
-        overflow = full;
+        n0 = sh.n;
+        tot = sh.tile_n[par];
+        overflow = n0 + tot > kBuf;  // ties at theta: exact radix select below
+        __syncthreads();  // every thread has read the counts before sh.n changes
       }
     }
     if (overflow) return;
+    // Every thread has read n0 (before the barrier above): sh.n can move on.
+    if (threadIdx.x == 0) sh.n = n0 + tot;
     const int flag = raw_first && pen ? kUnresolved : 0;  // raw logits: penalty applied at the next selection
+    int pos = n0 + wb + excl;
 #pragma unroll
     for (int e = 0; e < kTopkPer; ++e) {
       if (z[e] > kNegInf) {
-        const int pos = atomicAdd(&sh.n, 1);
         sh.bv[pos] = z[e];
         sh.bi[pos] = topk_tok<DT>(base, e) | flag;
+        ++pos;
       }
     }
     __syncthreads();
   };
   if (p.vec_ok) {
     // Two super-tiles in flight: the next one's loads are issued before this
-    // one is filtered.
-    constexpr int VW = TopkRaw<DT>::VW;
-    const int vfull = p.V - p.V % VW;
-    TopkRaw<DT> ra, rb;
+    // one is filtered (the first two at the start, above).
     int base = kBuf, par = 0;
-    topk_issue<DT>(p, g, base, vfull, ra);
-    topk_issue<DT>(p, g, base + kTopkTile, vfull, rb);
     while (base < vfull && !overflow) {
       float z[kTopkPer];
       topk_decode<DT>(base, vfull, ra, z);
@@ -274,8 +414,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(Params p) {
     if (!overflow && vfull < p.V) {  // the last V % VW tokens, penalty applied at once
       if (sh.n > kBuf - VW) {  // make room (n >= k here: k <= kCandCap < kBuf - VW)
         const int n = sh.n;
-        if (pen) resolve_buffer(sh, n, pr);
-        const float t = buffer_kth(sh, n, k);
+        const float t = select_tau(sh, n, k, pr);
         buffer_keep(sh, n, t);
         if (threadIdx.x == 0) sh.theta = t;
         __syncthreads();
@@ -298,8 +437,6 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(Params p) {
       tile_step(base, par, z);
     }
   }
-  if (pen && !overflow) resolve_buffer(sh, sh.n, pr);
-
   float tau;
   int ncand = -1;
   if (!overflow) {
@@ -307,7 +444,8 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(Params p) {
     if (n < k) {
       tau = kNegInf;  // fewer than k finite logits: nothing is removed
     } else {
-      tau = buffer_kth(sh, n, k);
+      // exact tau; the kept entries (>= tau) all hold processed values
+      tau = select_tau(sh, n, k, pr);
       buffer_keep(sh, n, tau);
       ncand = sh.n;
     }

@@ -55,6 +55,12 @@ EDGE = {
     "penalty_dense": wl.CONFIGS["4"].with_(B=5, K=3, V=4100, top_k=0, draft_top_k=0, history=300),
     # no-draft mode with top-k
     "topk_no_draft": wl.CONFIGS["3"].with_(B=8, V=3000, top_k=20, rep_penalty=1.3, history=50),
+    # the top-k pass's first threshold: k = 256 (the largest k taken from the
+    # threads' maxima), k = 300 (exact selection over the first 2048 tokens),
+    # and a row shorter than the first 2048 tokens
+    "topk_k256": wl.CONFIGS["4"].with_(B=4, K=2, V=9000, top_k=256, draft_top_k=0, history=60),
+    "topk_k300": wl.CONFIGS["4"].with_(B=4, K=2, V=9000, top_k=300, draft_top_k=0, history=60),
+    "topk_short_row": wl.CONFIGS["4"].with_(B=5, K=2, V=1500, top_k=30, history=40),
 }
 
 
@@ -161,6 +167,25 @@ def test_strided_logits_rows():
         g = run_gpu(ctx, inp)
     n_margin, bad = check_requests(g, inp, range(8))
     assert not bad, "\n".join(bad)
+
+
+@pytest.mark.parametrize("dtype,V", [(torch.bfloat16, 1001), (torch.bfloat16, 2053), (torch.float32, 2047),
+                                     (torch.bfloat16, 9003)])
+def test_topk_aligned_rows_ragged_tail(dtype, V):
+    # Aligned rows (the row stride padded to whole 16-byte vectors) whose
+    # length is not: the top-k pass streams whole vectors and takes the last
+    # V % (16 / element size) tokens apart, also when they fall in its first
+    # 2048 tokens.
+    w = wl.CONFIGS["4"].with_(B=4, K=2, V=V, dtype=dtype, top_k=20, draft_top_k=0, history=30)
+    inp = wl.make_inputs(w, DEV)
+    wide = torch.zeros((inp["R"], (V + 7) // 8 * 8 + 8), dtype=dtype, device=DEV)
+    wide[:, :V] = inp["logits"]
+    inp["logits"] = wide[:, :V]
+    with ctx_for(inp) as ctx:
+        g = run_gpu(ctx, inp, seed=5, offset=3, dbg_probs=True)
+    assert g["err"] == 0
+    n_margin, bad = check_requests(g, inp, range(inp["B"]), 5, 3, probs=True)
+    assert not bad, "\n".join(bad[:10])
 
 
 @pytest.mark.parametrize("draft_probs", [False, True])
