@@ -14,61 +14,62 @@ namespace {
 // strictly larger logits hold less than top_p of the mass: all z >= z* for a
 // boundary logit z*, the row's threshold afterwards (cand_tau).
 //
-// Weights relative to the row scale m: w = 2^-t, t = a (m - z).  A token
-// falls in sub-bucket j = floor(16 t) + 320 (clamped to [0, 1024)), of integer
-// part k = j / 16 - 20, and one exp2 gives W = 2^(31 - (t - k)), an
-// integer-valued float near 2^31: w = W 2^(-31-k) exactly, and sums of W
-// within one sub-bucket are exact 64-bit integers (independent of order).
-// Pass A: mass per sub-bucket; an fp64 scan in a fixed order finds the
-// sub-bucket j* holding the boundary and the mass above it.  Pass B: the
-// tokens of j* go to an LDS list, where a radix select on the order-preserving
-// keys, weighted by W, finds z*; tokens before j* are summed per chunk, and
-// the row's chunk table is rewritten as (m, kept mass): no further pass.  When
-// j* holds more tokens than the list, the rows are not 16-byte aligned or the
-// row has more chunks than the LDS tables, z* is selected straight from the
-// row and the row is left to a second statistics pass (kRowTopPRedo).
+// Weights relative to the row scale m: E = 2^(a (z - m)), below 2^21.  The
+// bucket of a weight is its float exponent and top four mantissa bits
+// (monotone in E); its units are its 24-bit significand, so the weights of one
+// bucket are integer multiples of one power of two and sum exactly, in any
+// order.  The row mass S comes from the chunk tables.  Tokens lighter than
+// E_skip = (1 - top_p) S / (2 V) weigh less than (1 - top_p) S / 2 together,
+// so the boundary lies among the heavier ones: both passes below test most
+// tokens with one comparison against a logit bound.
+// Pass A: units per bucket of the tokens not below E_skip; an fp64 scan from
+// the heaviest bucket finds the bucket b* where the mass above reaches
+// top_p S.  Pass B: the tokens of b* go to an LDS list, where a radix select
+// on the order-preserving keys, weighted by the units, finds z*; heavier
+// tokens are summed per chunk, and the row's chunk table is rewritten as
+// (m, kept mass): no further pass.  When b* holds more tokens than the list,
+// the rows are not 16-byte aligned or the row has more chunks than the LDS
+// tables, z* is selected straight from the row and the row is left to a
+// second statistics pass (kRowTopPRedo).
 // ---------------------------------------------------------------------------
-constexpr int kToppSub = 1024;
-constexpr int kToppSubOff = 320;  // sub-bucket of t = 0: t >= -20 is covered (a (z - m) <= 20)
+// The statistics pass's chunk references leave a (z - m) <= 20 (its maxima
+// are exact only where a chunk's sum reaches 2^20), so weights reach 2^20:
+// the buckets start at 2^21 and run down to 2^-43, below which a token's
+// weight is dropped (at most V 2^-43 of a row whose heaviest token weighs 1).
+constexpr int kToppBuckets = 1024;                  // buckets kept, the heaviest first
+constexpr int kToppTop = ((127 + 21) << 23) >> 19;  // bucket of E = 2^21
 constexpr int kToppList = 2048;
 constexpr int kToppMaxNC = 512;   // chunks per row whose sums live in LDS (V <= 524288)
 // Threads per row: eight waves when most rows are dense (one row per
-// workgroup leaves few waves per CU, and the pass is bound by each
-// workgroup's own arithmetic: eight waves measured 11 % faster per step on
-// 640 dense bf16 rows); four with top-k on, where most rows have candidate
-// lists and their workgroups return at once (eight measured 1 % slower there).
+// workgroup leaves few waves per CU); four with top-k on, where most rows have
+// candidate lists and their workgroups return at once.
 constexpr int kTpMaxWaves = 8;
 
 struct ToppShared {
-  unsigned long long mass[kToppSub];
+  unsigned long long mass[kToppBuckets];  // units per bucket, index kToppTop - bucket
   float lz[kToppList];
   int lx[kToppList];
-  float part[kToppMaxNC * 4];            // per chunk, one slot per wave covering it
-  unsigned long long lsum[kToppMaxNC];   // kept list weights per chunk (integer W)
+  float part[kToppMaxNC * 4];            // kept weight per chunk, one slot per wave covering it
+  unsigned long long lsum[kToppMaxNC];   // kept list units per chunk
   float tail[8];
   float wmax[kTpMaxWaves];
+  double wsum[kTpMaxWaves];
   unsigned long long need;
   int n, sel;
 };
 
-struct ToppW {
-  int j, k;
-  float W;  // 2^(31 - (t - k)): an integer-valued float below 2^32
-};
-
-// Sub-bucket and weight of logit z, branch-free: z = -inf (t = +inf) lands in
-// the last sub-bucket with W = 0.  topp_j is the sub-bucket alone (the same
-// operations), for tests that need no weight.
-__device__ __forceinline__ int topp_j(float t) {
-  const float u = fminf(fmaxf(__builtin_floorf(t * 16.0f), -(float)kToppSubOff), (float)(kToppSub - 1 - kToppSubOff));
-  return (int)u + kToppSubOff;
-}
-__device__ __forceinline__ ToppW topp_w(float z, float m, float a) {
-  const float t = (m - z) * a;
-  const int j = topp_j(t);
-  const int k = (j >> 4) - kToppSubOff / 16;
-  return ToppW{j, k, exp2_acc(31.0f - (t - (float)k))};
-}
+// Weight, bucket and units of a (processed) logit; z = -inf weighs 0, whose
+// bucket lies below every kept one.  The weight is the epilogue's
+// 2^(a (z - m)), with the same roundings, so the kept masses written to the
+// chunk table normalise exactly the probabilities it computes.
+__device__ __forceinline__ float tp_weight(float z, float a, float m) { return exp2_acc(a * (z - m)); }
+__device__ __forceinline__ int tp_bucket(float E) { return (int)(__float_as_uint(E) >> 19); }
+__device__ __forceinline__ unsigned long long tp_units(float E) { return (__float_as_uint(E) & 0x7FFFFFu) | 0x800000u; }
+// Binary exponent of one unit of bucket b.
+__device__ __forceinline__ int tp_unit_exp(int b) { return (b >> 4) - 150; }
+// Smallest logit whose weight can reach E (a conservative bound: 0.01 below in
+// log2 units, far beyond the rounding of the weight).
+__device__ __forceinline__ float tp_logit_bound(float E, float m, float a) { return m + (__log2f(E) - 0.01f) / a; }
 
 // Calls fn(x, raw logit) for every token of row g (vector loads, two
 // super-tiles in flight, when the rows are aligned).  All threads call it.
@@ -107,25 +108,30 @@ __device__ __forceinline__ void stream_row(const Params &p, int g, F fn) {
   }
 }
 
-// Calls tile(base, z[kTopkPer]) for every super-tile of an aligned row (two in
-// flight); logits of tokens at or past vfull = V - V % VW read as -inf.
+// Super-tiles in flight per workgroup in the top-p passes.
+template <int DT>
+constexpr int kToppDepth = 2;
+
+// Calls tile(base, z[kTopkPer]) for every super-tile of an aligned row
+// (kToppDepth in flight); logits of tokens at or past vfull = V - V % VW read
+// as -inf.
 template <int DT, int NT, class F>
 __device__ __forceinline__ void stream_tiles(const Params &p, int g, int vfull, F tile) {
-  TopkRaw<DT> ra, rb;
-  int base = 0;
-  topk_issue<DT, NT>(p, g, base, vfull, ra);
-  topk_issue<DT, NT>(p, g, base + (kTopkPer * NT), vfull, rb);
-  while (base < vfull) {
-    float z[kTopkPer];
-    topk_decode<DT, NT>(base, vfull, ra, z);
-    topk_issue<DT, NT>(p, g, base + 2 * (kTopkPer * NT), vfull, ra);
-    tile(base, z);
-    base += (kTopkPer * NT);
-    if (base >= vfull) break;
-    topk_decode<DT, NT>(base, vfull, rb, z);
-    topk_issue<DT, NT>(p, g, base + 2 * (kTopkPer * NT), vfull, rb);
-    tile(base, z);
-    base += (kTopkPer * NT);
+  constexpr int D = kToppDepth<DT>;
+  constexpr int T = kTopkPer * NT;
+  TopkRaw<DT> r[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i) topk_issue<DT, NT>(p, g, i * T, vfull, r[i]);
+  for (int base = 0; base < vfull; base += D * T) {
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      const int b = base + i * T;
+      if (b >= vfull) break;
+      float z[kTopkPer];
+      topk_decode<DT, NT>(b, vfull, r[i], z);
+      topk_issue<DT, NT>(p, g, b + D * T, vfull, r[i]);
+      tile(b, z);
+    }
   }
 }
 
@@ -180,17 +186,17 @@ __device__ __forceinline__ int topp_digit(ToppShared &sh, unsigned long long &ne
 }
 
 // Weighted MSD radix select among the tokens `each` enumerates (each thread
-// calls its callback with (z, W) for its share): the largest key whose
-// strictly larger keys hold less than `need` integer weight units.
+// calls its callback with (z, units) for its share): the largest key whose
+// strictly larger keys hold less than `need` units.
 template <class EACH>
 __device__ __forceinline__ float topp_select(ToppShared &sh, EACH each, unsigned long long need) {
   uint32_t prefix = 0, mask = 0;
   for (int shift = 24; shift >= 0; shift -= 8) {
     if (threadIdx.x < 256) sh.mass[threadIdx.x] = 0;
     __syncthreads();
-    each([&](float z, float W) {
+    each([&](float z, unsigned long long w) {
       const uint32_t key = ukey(z);
-      if ((key & mask) == prefix) atomicAdd(&sh.mass[(key >> shift) & 0xFFu], (unsigned long long)(uint32_t)W);
+      if ((key & mask) == prefix) atomicAdd(&sh.mass[(key >> shift) & 0xFFu], w);
     });
     __syncthreads();
     prefix |= (uint32_t)topp_digit(sh, need) << shift;
@@ -205,8 +211,7 @@ __global__ __launch_bounds__(NT) void topp_kernel(Params p) {
   __shared__ ToppShared sh;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = blockIdx.x;
-  const int r = find_request(p.cu, p.B, g);
-  const Req q = load_req(p, r);
+  const Req q = lookup_req(p, g);
   const int st = p.has_topk ? p.cand_n[g] : kRowDense;
   const bool use = q.cu_ok && g >= q.g0 && g <= q.g0 + q.K && q.mode == kModeSample && q.top_p < 1.0f && st < 0;
   if (!use) {
@@ -217,7 +222,7 @@ __global__ __launch_bounds__(NT) void topp_kernel(Params p) {
   pr.tau = st == kRowThreshold ? p.cand_tau[g] : kNegInf;
   const float a = q.a, tau = pr.tau;
 
-  // Row scale m from the first pass's chunk table.
+  // Row scale m and mass S (relative to 2^(a m)) from the first pass's chunk table.
   float2 *tab = p.chunk_tab + (int64_t)g * p.nc_stride;
   float lm = kNegInf;
   for (int c = tid; c < p.NC; c += NT) lm = fmaxf(lm, tab[c].x);
@@ -231,55 +236,78 @@ __global__ __launch_bounds__(NT) void topp_kernel(Params p) {
     if (tid == 0) p.cand_n[g] = st;
     return;
   }
+  double ls = 0.0;
+  for (int c = tid; c < p.NC; c += NT) {
+    const float2 e = tab[c];
+    if (e.x > kNegInf) ls += (double)(e.y * exp2_acc(a * (e.x - m)));
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) ls += __shfl_xor(ls, d, 64);
+  if (lane == 0) sh.wsum[wave] = ls;
+  __syncthreads();
+  double S = 0.0;
+#pragma unroll
+  for (int w = 0; w < (NT / 64); ++w) S += sh.wsum[w];
+  const double bound = (double)q.top_p * S;
+  const float zskip = tp_logit_bound((float)((1.0 - (double)q.top_p) * S / (2.0 * p.V)), m, a);
+
   constexpr int VW = TopkRaw<DT>::VW;
   const int vfull = p.V - p.V % VW;
   // Aligned rows without a penalty take the branch-free tile loops.
   const bool tiles = p.vec_ok && pr.counts == nullptr;
 
-  // Pass A: integer weight per sub-bucket.
-  for (int j = tid; j < kToppSub; j += NT) sh.mass[j] = 0;
+  // Pass A: units per bucket of the tokens not below E_skip.
+  for (int j = tid; j < kToppBuckets; j += NT) sh.mass[j] = 0;
   __syncthreads();
-  if (tiles) {
-    stream_tiles<DT, NT>(p, g, vfull, [&](int, float (&z)[kTopkPer]) {
+  auto count = [&](float z) {
+    const float E = tp_weight(z, a, m);
+    const int i = max(kToppTop - tp_bucket(E), 0);  // never clamped: E < 2^21
+    if (i < kToppBuckets) atomicAdd(&sh.mass[i], tp_units(E));
+  };
+  // Aligned rows: whole super-tiles (penalties applied per token); the last
+  // V % VW tokens, and unaligned rows, one token per thread.
+  if (p.vec_ok) {
+    stream_tiles<DT, NT>(p, g, vfull, [&](int base, float (&z)[kTopkPer]) {
 #pragma unroll
       for (int e = 0; e < kTopkPer; ++e) {
-        const ToppW w = topp_w(z[e] < tau ? kNegInf : z[e], m, a);
-        atomicAdd(&sh.mass[w.j], (unsigned long long)(uint32_t)w.W);
+        const int x = topk_tok<DT, NT>(base, e);
+        float zz = z[e];
+        if (!tiles && x < vfull) zz = apply_proc(zz, x, pr);  // penalty rows
+        zz = zz < tau ? kNegInf : zz;
+        if (zz >= zskip) count(zz);
       }
     });
     if (vfull + tid < p.V) {
-      const ToppW w = topp_w(apply_proc(load_logit(p, g, vfull + tid), vfull + tid, pr), m, a);
-      atomicAdd(&sh.mass[w.j], (unsigned long long)(uint32_t)w.W);
+      const float z = apply_proc(load_logit(p, g, vfull + tid), vfull + tid, pr);
+      if (z >= zskip) count(z);
     }
   } else {
     stream_row<DT, NT>(p, g, [&](int x, float raw) {
-      const ToppW w = topp_w(apply_proc(raw, x, pr), m, a);
-      atomicAdd(&sh.mass[w.j], (unsigned long long)(uint32_t)w.W);
+      const float z = apply_proc(raw, x, pr);
+      if (z >= zskip) count(z);
     });
   }
   __syncthreads();
-  // Scan (wave 0): lane l owns sub-buckets 16 l .. 16 l + 15, of integer part
-  // k = l - 20; fp64 in a fixed order.
+  // Scan (wave 0): lane l owns buckets 16 l .. 16 l + 15 (heaviest first); fp64
+  // in a fixed order.
   if (wave == 0) {
-    const int kl = lane - kToppSubOff / 16;
     double own = 0.0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) own += __builtin_ldexp((double)sh.mass[16 * lane + i], -31 - kl);
+    for (int i = 0; i < 16; ++i)
+      own += __builtin_ldexp((double)sh.mass[16 * lane + i], tp_unit_exp(kToppTop - (16 * lane + i)));
     double incl = own;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
       const double o = __shfl_up(incl, d, 64);
       if (lane >= d) incl += o;
     }
-    const double total = __shfl(incl, 63, 64);
-    const double bound = (double)q.top_p * total;
     double acc = incl - own;
     int hit = -1;
     double hit_above = 0.0;
     for (int i = 0; i < 16; ++i) {
       const unsigned long long h = sh.mass[16 * lane + i];
       if (h == 0) continue;
-      const double hm = __builtin_ldexp((double)h, -31 - kl);
+      const double hm = __builtin_ldexp((double)h, tp_unit_exp(kToppTop - (16 * lane + i)));
       if (acc + hm >= bound) {
         hit = 16 * lane + i;
         hit_above = acc;
@@ -288,7 +316,8 @@ __global__ __launch_bounds__(NT) void topp_kernel(Params p) {
       acc += hm;
     }
     const unsigned long long hits = __ballot(hit >= 0);
-    // the first crossing; none only through rounding with top_p near 1: the last non-empty sub-bucket
+    // the first crossing; none only through rounding (S from the tables, top_p
+    // near 1): the lightest non-empty bucket
     const unsigned long long nonempty = __ballot(own > 0.0);
     const int src = hits ? __ffsll((long long)hits) - 1 : 63 - __builtin_clzll(nonempty | 1ull);
     if (lane == src) {
@@ -296,26 +325,28 @@ __global__ __launch_bounds__(NT) void topp_kernel(Params p) {
         for (int i = 15; i >= 0; --i)
           if (sh.mass[16 * lane + i]) {
             hit = 16 * lane + i;
-            hit_above = incl - __builtin_ldexp((double)sh.mass[hit], -31 - kl);
+            hit_above = incl - __builtin_ldexp((double)sh.mass[hit], tp_unit_exp(kToppTop - hit));
             break;
           }
         if (hit < 0) hit = 16 * lane;
       }
-      sh.sel = hit;
-      // integer weight units of sub-bucket hit still needed to reach the bound
-      const int kh = (hit >> 4) - kToppSubOff / 16;
-      const double rest = __builtin_ceil(__builtin_ldexp(bound - hit_above, 31 + kh));
+      sh.sel = kToppTop - hit;
+      // units of bucket b* still needed to reach the bound
+      const double rest = __builtin_ceil(__builtin_ldexp(bound - hit_above, -tp_unit_exp(kToppTop - hit)));
       sh.need = rest < 1.0 ? 1ull : (unsigned long long)rest;
       sh.n = 0;
     }
   }
   __syncthreads();
-  const int jstar = sh.sel;
-  const int kstar = (jstar >> 4) - kToppSubOff / 16;
+  const int bstar = sh.sel;
+  const int ustar = tp_unit_exp(bstar);
   const unsigned long long need = sh.need;
+  // every token of bucket b* or heavier is at or above this logit
+  const float zb = tp_logit_bound(__uint_as_float((uint32_t)bstar << 19), m, a);
   const bool direct = p.vec_ok && p.NC <= kToppMaxNC;
 
-  // Pass B: the boundary sub-bucket into the list, the mass before it per chunk.
+  // Pass B: bucket b* into the list, the heavier tokens' weight per chunk
+  // (per vector, one wave sum into a slot of its own: a fixed order).
   bool redo = !direct;
   if (direct) {
     for (int c = tid; c < p.NC * 4; c += NT) sh.part[c] = 0.0f;
@@ -323,13 +354,12 @@ __global__ __launch_bounds__(NT) void topp_kernel(Params p) {
     if (tid < 8) sh.tail[tid] = 0.0f;
     __syncthreads();
     constexpr int WPC = kChunk / (64 * VW);  // waves covering one chunk in a super-tile
-    // Most tokens lie below the boundary sub-bucket: their weight is not
-    // needed, and a wave whose tokens all do skips the rest.
     auto token = [&](int x, float z, float &acc) {
-      if (topp_j((m - z) * a) > jstar) return;
-      const ToppW w = topp_w(z, m, a);
-      acc += w.j < jstar ? __builtin_ldexpf(w.W, -31 - w.k) : 0.0f;
-      if (w.j == jstar && z > kNegInf) {
+      if (!(z >= zb)) return;  // most tokens: lighter than bucket b*
+      const float E = tp_weight(z, a, m);
+      const int b = tp_bucket(E);
+      if (b > bstar) acc += E;
+      if (b == bstar) {
         const int pos = atomicAdd(&sh.n, 1);
         if (pos < kToppList) {
           sh.lz[pos] = z;
@@ -349,7 +379,7 @@ __global__ __launch_bounds__(NT) void topp_kernel(Params p) {
           if (!tiles && x < vfull) zz = apply_proc(zz, x, pr);  // penalty rows
           token(x, zz < tau ? kNegInf : zz, acc);
         }
-        const float sum = wave_sum(acc);
+        const float sum = __ballot(acc != 0.0f) ? wave_sum(acc) : 0.0f;
         const int c = (base + (v * NT + wave * 64) * VW) / kChunk;
         if (lane == 0 && c < p.NC) sh.part[c * 4 + wave % WPC] = sum;
       }
@@ -368,13 +398,12 @@ __global__ __launch_bounds__(NT) void topp_kernel(Params p) {
     const int n = sh.n;
     zstar = topp_select(
         sh, [&](auto fn) {
-          for (int e = tid; e < n; e += NT) fn(sh.lz[e], topp_w(sh.lz[e], m, a).W);
+          for (int e = tid; e < n; e += NT) fn(sh.lz[e], tp_units(tp_weight(sh.lz[e], a, m)));
         },
         need);
-    // Kept list tokens into their chunks (integer sums), then the new table.
+    // Kept list tokens into their chunks (units), then the new table.
     for (int e = tid; e < n; e += NT)
-      if (sh.lz[e] >= zstar)
-        atomicAdd(&sh.lsum[sh.lx[e] / kChunk], (unsigned long long)(uint32_t)topp_w(sh.lz[e], m, a).W);
+      if (sh.lz[e] >= zstar) atomicAdd(&sh.lsum[sh.lx[e] / kChunk], tp_units(tp_weight(sh.lz[e], a, m)));
     __syncthreads();
     constexpr int WPC = kChunk / (64 * VW);
     const int clast = (p.V - 1) / kChunk;
@@ -387,7 +416,7 @@ __global__ __launch_bounds__(NT) void topp_kernel(Params p) {
         for (int i = 0; i < 8; ++i) t += sh.tail[i];
         sc += t;
       }
-      sc += (float)__builtin_ldexp((double)sh.lsum[c], -31 - kstar);
+      sc += (float)__builtin_ldexp((double)sh.lsum[c], ustar);
       tab[c] = make_float2(m, sc);
     }
   } else {
@@ -395,8 +424,10 @@ __global__ __launch_bounds__(NT) void topp_kernel(Params p) {
         sh, [&](auto fn) {
           stream_row<DT, NT>(p, g, [&](int x, float raw) {
             const float z = apply_proc(raw, x, pr);
-            const ToppW w = topp_w(z, m, a);
-            if (w.j == jstar && z > kNegInf) fn(z, w.W);
+            if (z >= zb) {
+              const float E = tp_weight(z, a, m);
+              if (tp_bucket(E) == bstar) fn(z, tp_units(E));
+            }
           });
         },
         need);
