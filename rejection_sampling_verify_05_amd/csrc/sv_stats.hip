@@ -286,15 +286,23 @@ __device__ __forceinline__ void fast_chunk(const Params &p, const RowInfo &ri, i
     pr.theta = ri.theta;
     pr.freq = ri.freq;
     pr.pres = ri.pres;
+    // Counts are sparse (a request's output so far): a group of four
+    // tokens per lane whose counts are zero in every lane of the wave is
+    // skipped (a uniform branch).
     const bool rep = ri.theta != 1.0f;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int4 q4 = cv[e >> 2];
-      const int cnt = (e & 3) == 0 ? q4.x : (e & 3) == 1 ? q4.y : (e & 3) == 2 ? q4.z : q4.w;
-      float zp = rep ? (z[e] > 0.0f ? z[e] / pr.theta : z[e] * pr.theta) : z[e];
-      zp = zp - pr.freq * (float)cnt;
-      zp = zp - pr.pres;
-      z[e] = cnt > 0 ? zp : z[e];
+    for (int h = 0; h < 4; ++h) {
+      const int4 q4 = cv[h];
+      if (!__ballot((q4.x | q4.y | q4.z | q4.w) != 0)) continue;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int e = 4 * h + k;
+        const int cnt = k == 0 ? q4.x : k == 1 ? q4.y : k == 2 ? q4.z : q4.w;
+        float zp = rep ? (z[e] > 0.0f ? z[e] / pr.theta : z[e] * pr.theta) : z[e];
+        zp = zp - pr.freq * (float)cnt;
+        zp = zp - pr.pres;
+        z[e] = cnt > 0 ? zp : z[e];
+      }
     }
   }
   if ((c + 1) * kChunk > p.V) {  // row tail: tokens past V do not exist
