@@ -90,6 +90,7 @@ WORKLOAD_PROFILE = {
     "3k3": ("stats_fast_kernel_bf16_B256_K3_V128256", KERNEL_SOURCES),
     "4": ("topk_kernel_f32_B512_K8_V151936", KERNEL_SOURCES_TOPK),
     "5": ("stats_fast_kernel_bf16_B1024_K5_V256000", KERNEL_SOURCES),
+    "3f": ("stats_fast_kernel_pen_bf16_B256_V128256", KERNEL_SOURCES),
 }
 
 
@@ -143,46 +144,40 @@ def _oracle_slice(task):
 
 def cpu_baseline_leg(w, seconds):
     """The oracle on a bounded sample of workload w, made on the host with the
-    same generator recipe (the GPU is not touched yet): whole batches in one
-    process for half the budget, then request slices over a fork pool of the
-    host's cores for the other half."""
+    same generator recipe (the GPU is not touched): request slices in one
+    process for half the budget, then the same slices over a fork pool of the
+    host's cores for the other half (at least one slice, resp. one slice per
+    worker, so that the largest workloads stay bounded)."""
     import multiprocessing as mp
     import time as _t
-    import numpy as np
-    import oracle
-    import workloads as wl
     global _POOL_INPUT
-    inp = wl.make_inputs(w, "cpu", salt=0)
-    h = wl.to_numpy(inp)
-    penalty = any(inp[k] is not None for k in ("rep_penalty", "freq", "pres"))
-    h["counts"] = inp["counts"].numpy() if penalty else None
-    h["draft_probs"] = None if inp["draft_probs"] is None else inp["draft_probs"].numpy()
-    h["max_k"] = w.K
-    B, R = inp["B"], inp["R"]
+    inp = wl_make_host_inputs(w)
+    h = inp["host"]
+    B = inp["B"]
     _POOL_INPUT = h
+    workers = host_workers()
+    per = max(1, -(-B // (4 * workers)))  # requests per slice
+    slices = [(a, min(B, a + per)) for a in range(0, B, per)]
     t0 = _t.perf_counter()
     n1 = rows1 = 0
     while True:
-        _oracle_slice((0, B, n1))
+        a, b = slices[n1 % len(slices)]
+        rows1 += _oracle_slice((a, b, n1 // len(slices)))
         n1 += 1
-        rows1 += R
         if _t.perf_counter() - t0 >= seconds / 2:
             break
     s1 = _t.perf_counter() - t0
-    workers = host_workers()
-    per = max(1, -(-B // (4 * workers)))
-    tasks = [(a, min(B, a + per), k) for k in range(64) for a in range(0, B, per)]
     ctx = mp.get_context("fork")
-    rows_n, batches = 0, 0
+    rows_n = n_tasks = 0
     with ctx.Pool(workers) as pool:
-        pool.map(_oracle_slice, tasks[:workers])  # workers started and warm
+        pool.map(_oracle_slice, [(a, b, 63) for a, b in slices[:workers]])  # workers started and warm
         t1 = _t.perf_counter()
         k = 0
-        per_batch = -(-B // per)
         while True:
-            rows_n += sum(pool.map(_oracle_slice, tasks[k * per_batch:(k + 1) * per_batch]))
-            batches += 1
-            k = (k + 1) % 64
+            tasks = [(*slices[(k + i) % len(slices)], (k + i) // len(slices)) for i in range(workers)]
+            rows_n += sum(pool.map(_oracle_slice, tasks))
+            n_tasks += workers
+            k += workers
             if _t.perf_counter() - t1 >= seconds / 2:
                 break
         sn = _t.perf_counter() - t1
@@ -190,11 +185,22 @@ def cpu_baseline_leg(w, seconds):
     return {"value": rows_n / sn, "unit": "rows/s", "cores": workers, "kind": "oracle",
             "cpu_model": cpu_model(),
             "single_process": {"value": rows1 / s1, "unit": "rows/s", "cores": 1,
-                               "sample": f"{n1} whole batch(es) ({R} rows each), {s1:.1f} s"},
-            "sample": f"{batches} whole batch(es) of workload {w.cid} ({R} rows each; B={B} requests in slices "
-                      f"of {per}) over a fork pool of {workers} processes, {sn:.1f} s; inputs made on the host "
-                      "with the same generator recipe as the GPU copies (same distribution, other draws); "
-                      "C oracle, fp64"}
+                               "sample": f"{n1} slice(s) of {per} requests ({rows1} rows), {s1:.1f} s"},
+            "sample": f"{n_tasks} slices of {per} requests of workload {w.cid} ({rows_n} rows; B={B}) over a fork "
+                      f"pool of {workers} processes, {sn:.1f} s; inputs made on the host with the same generator "
+                      "recipe as the GPU copies (same distribution, other draws); C oracle, fp64"}
+
+
+def wl_make_host_inputs(w):
+    """Host copy of workload w for the oracle leg (numpy views, as the oracle takes them)."""
+    import workloads as wl
+    inp = wl.make_inputs(w, "cpu", salt=0)
+    h = wl.to_numpy(inp)
+    penalty = any(inp[k] is not None for k in ("rep_penalty", "freq", "pres"))
+    h["counts"] = inp["counts"].numpy() if penalty else None
+    h["draft_probs"] = None if inp["draft_probs"] is None else inp["draft_probs"].numpy()
+    h["max_k"] = w.K
+    return {"host": h, "B": inp["B"], "R": inp["R"]}
 
 
 def copy_calibration():
