@@ -379,11 +379,17 @@ def main():
     assert sv.spec_verify_read_error(ctx) == 0
 
     # Dominant kernel: the first pass over the rows (the streaming statistics
-    # pass, or the top-k pass).  Its algorithmic bytes are one read of every
+    # pass, the top-k pass, or the register-resident top-p pass).  Its algorithmic bytes are one read of every
     # target row, R V s (s = 2 for bf16, 4 for fp32), plus, for the statistics
     # pass with penalties, the counts row of each penalised request (V 4).
     esize = first["logits"].element_size()
+    # With top-p on aligned bf16 rows of at most 128 chunks and no top-k or
+    # penalty, the library's first (and only) pass over the rows is the
+    # register-resident top-p pass.
+    resident = (w.top_p < 1.0 and not w.top_k and not penalty and esize == 2 and w.V % 8 == 0
+                and -(-w.V // 1024) <= 128)
     kernel = "topk_kernel (top-k pass: every row read once)" if w.top_k else \
+        "topp_resident_kernel (top-p call: every row held in registers, read once)" if resident else \
         "stats_fast_kernel (streaming softmax statistics)"
 
     def launch_bytes(c):

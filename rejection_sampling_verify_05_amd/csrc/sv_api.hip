@@ -287,8 +287,18 @@ int verify_on(sv_ctx *ctx, const sv_verify_args *a, hipStream_t stream) {
   if (p.has_topk) e0 = e1 = nullptr;
   const bool resid = p.draft_probs != nullptr || p.draft_logits != nullptr;
   ctx->res_dirty = resid;  // until the residual race has zeroed the count
-  if (sv::launch_stats(p, stream, e0, e1) != hipSuccess) return SV_EHIP;
-  if (p.has_topp) {
+  // Top-p on aligned bf16 rows that fit the registers of one workgroup, with
+  // no top-k or penalty: a single pass that holds each row and does the
+  // statistics and the nucleus from it.
+  const bool resident = p.has_topp && !p.has_topk && !penalty && p.dtype == SV_BF16 && p.fast &&
+                        p.NC <= sv::kResidentMaxChunks;
+  if (resident) {
+    if (sv::launch_topp_resident(p, stream, e0, e1) != hipSuccess) return SV_EHIP;
+    p.cand_valid = 1;
+  } else if (sv::launch_stats(p, stream, e0, e1) != hipSuccess) {
+    return SV_EHIP;
+  }
+  if (p.has_topp && !resident) {
     // Top-p on dense rows, then their statistics again under the threshold
     // (general pass, only the marked rows).
     if (sv::launch_topp(p, stream) != hipSuccess) return SV_EHIP;

@@ -223,6 +223,81 @@ struct Layout<0> {
 };
 
 // ---------------------------------------------------------------------------
+// A target row as the statistics passes see it, and one chunk's statistics.
+// ---------------------------------------------------------------------------
+struct RowInfo {
+  int g, r, i, c0, K, g0, mode, st;  // mode kModeInvalid: row skipped
+  float a, theta, freq, pres, tau;
+  const int32_t *counts;
+};
+
+__device__ __forceinline__ RowInfo row_info_of(const Params &p, const Req &q, int g) {
+  RowInfo ri;
+  ri.g = g;
+  ri.r = q.r;
+  ri.i = g - q.g0;
+  ri.c0 = q.c0;
+  ri.K = q.K;
+  ri.g0 = q.g0;
+  const bool ok = q.cu_ok && ri.i >= 0 && ri.i <= q.K && q.mode != kModeInvalid;
+  ri.mode = ok ? q.mode : kModeInvalid;
+  ri.st = ok ? row_state(p, g) : kRowDense;
+  ri.a = q.a;
+  ri.theta = q.proc.theta;
+  ri.freq = q.proc.freq;
+  ri.pres = q.proc.pres;
+  ri.counts = q.proc.counts;
+  ri.tau = (ok && row_has_tau(ri.st)) ? p.cand_tau[g] : kNegInf;
+  return ri;
+}
+
+// Statistics of chunk c of row ri.g into the chunk table: (max, sum of
+// exp2(a (z - max))).  Greedy rows carry a = 0 and only their maxima are used.
+template <int DT>
+__device__ __forceinline__ void chunk_stats(const Params &p, const RowInfo &ri, int c, const u32x4 (&v)[Layout<DT>::kVec]) {
+  using L = Layout<DT>;
+  const int lane = threadIdx.x & 63;
+  const int g = ri.g;
+  Proc pr;
+  pr.counts = ri.counts;
+  pr.theta = ri.theta;
+  pr.freq = ri.freq;
+  pr.pres = ri.pres;
+  pr.tau = ri.tau;
+  float z[16];
+  if (p.vec_ok && (c + 1) * kChunk <= p.V) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) z[e] = L::elem(v, e);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int x = c * kChunk + L::local(e, lane);
+      z[e] = x < p.V ? load_logit(p, g, x) : kNegInf;
+    }
+  }
+  if (pr.counts != nullptr || pr.tau > kNegInf) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int x = c * kChunk + L::local(e, lane);
+      if (x < p.V) z[e] = apply_proc(z[e], x, pr);
+    }
+  }
+  float mx = z[0];
+#pragma unroll
+  for (int e = 1; e < 16; ++e) mx = fmaxf(mx, z[e]);
+  const float mc = wave_max(mx);
+  // exp2(a (z - mc)) = exp2(fma(z, a, -hi)) * exp2(-lo), a * mc = hi + lo exactly.
+  const float a = ri.a;
+  const float hi = a * mc;
+  const float lo = __builtin_fmaf(a, mc, -hi);
+  float sa = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) sa += exp2_acc(__builtin_fmaf(z[e], a, -hi));
+  const float2 entry = make_float2(mc, mc > kNegInf ? wave_sum(sa) * exp2_acc(-lo) : 0.0f);
+  if (lane == 0) p.chunk_tab[(int64_t)g * p.nc_stride + c] = entry;
+}
+
+// ---------------------------------------------------------------------------
 // Races.  RACE(w, g): chunk c* = argmax_c M_c / E(g, 1, c) over chunks with
 // M_c > 0, then token x* = argmax_{x in c*} w_x / E(g, 2, x) over w_x > 0.
 // Scores are fp32 (race_score); ties go to the lowest index.

@@ -158,6 +158,12 @@ struct PostParams {
 // sv_draft.hip).  Return the hipError_t of the last launch.
 hipError_t launch_topk(const Params &p, hipStream_t s, hipEvent_t t0, hipEvent_t t1);
 hipError_t launch_topp(const Params &p, hipStream_t s);
+// Top-p call with every row held in registers (aligned bf16 rows of at most
+// kResidentMaxChunks chunks, no top-k, no penalties): replaces the streaming
+// pass and the two-pass top-p kernel; the first two events bracket it.
+constexpr int kResidentThreads = 1024;
+constexpr int kResidentMaxChunks = 128;
+hipError_t launch_topp_resident(const Params &p, hipStream_t s, hipEvent_t t0, hipEvent_t t1);
 // t0, t1: optional events stamped at the kernel's start and end (may be null).
 hipError_t launch_stats(const Params &p, hipStream_t s, hipEvent_t t0, hipEvent_t t1);
 hipError_t launch_epilogue(const Params &p, hipStream_t s, hipEvent_t t0, hipEvent_t t1);

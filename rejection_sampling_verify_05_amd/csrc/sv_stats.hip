@@ -17,11 +17,7 @@ namespace {
 // the chunk table.  Nothing here depends on the draft tokens: the request
 // epilogue kernel, launched next on the same stream, reads the tables.
 // ---------------------------------------------------------------------------
-struct RowInfo {
-  int g, r, i, c0, K, g0, mode, st;  // mode kModeInvalid: row skipped
-  float a, theta, freq, pres, tau;
-  const int32_t *counts;
-};
+
 // Rows a stats pass streams: dense rows, or on the second pass of a top-p
 // call only the rows whose tables the top-p pass left to it.
 __device__ __forceinline__ bool stream_state(const Params &p, int st) { return p.pass2 ? st == kRowTopPRedo : st < 0; }
@@ -43,26 +39,6 @@ template <int DT, bool PEN>
 constexpr int kFastThreads = 64 * kFastWaves<DT, PEN>;
 static_assert(kRowCache <= 4, "one wave looks up each row of a slice");
 
-__device__ __forceinline__ RowInfo row_info_of(const Params &p, const Req &q, int g) {
-  RowInfo ri;
-  ri.g = g;
-  ri.r = q.r;
-  ri.i = g - q.g0;
-  ri.c0 = q.c0;
-  ri.K = q.K;
-  ri.g0 = q.g0;
-  const bool ok = q.cu_ok && ri.i >= 0 && ri.i <= q.K && q.mode != kModeInvalid;
-  ri.mode = ok ? q.mode : kModeInvalid;
-  ri.st = ok ? row_state(p, g) : kRowDense;
-  ri.a = q.a;
-  ri.theta = q.proc.theta;
-  ri.freq = q.proc.freq;
-  ri.pres = q.proc.pres;
-  ri.counts = q.proc.counts;
-  ri.tau = (ok && row_has_tau(ri.st)) ? p.cand_tau[g] : kNegInf;
-  return ri;
-}
-
 template <int DT>
 __device__ __forceinline__ void issue_chunk(const Params &p, int64_t f, int64_t end, u32x4 (&v)[Layout<DT>::kVec]) {
   using L = Layout<DT>;
@@ -75,52 +51,6 @@ __device__ __forceinline__ void issue_chunk(const Params &p, int64_t f, int64_t 
                                                     (g * p.lstride + (int64_t)c * kChunk) * L::kBytes);
 #pragma unroll
   for (int h = 0; h < L::kVec; ++h) v[h] = __builtin_nontemporal_load(&src[h * 64 + lane]);
-}
-
-// Statistics of chunk c of row ri.g into the chunk table: (max, sum of
-// exp2(a (z - max))).  Greedy rows carry a = 0 and only their maxima are used.
-template <int DT>
-__device__ __forceinline__ void chunk_stats(const Params &p, const RowInfo &ri, int c, const u32x4 (&v)[Layout<DT>::kVec]) {
-  using L = Layout<DT>;
-  const int lane = threadIdx.x & 63;
-  const int g = ri.g;
-  Proc pr;
-  pr.counts = ri.counts;
-  pr.theta = ri.theta;
-  pr.freq = ri.freq;
-  pr.pres = ri.pres;
-  pr.tau = ri.tau;
-  float z[16];
-  if (p.vec_ok && (c + 1) * kChunk <= p.V) {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) z[e] = L::elem(v, e);
-  } else {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int x = c * kChunk + L::local(e, lane);
-      z[e] = x < p.V ? load_logit(p, g, x) : kNegInf;
-    }
-  }
-  if (pr.counts != nullptr || pr.tau > kNegInf) {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int x = c * kChunk + L::local(e, lane);
-      if (x < p.V) z[e] = apply_proc(z[e], x, pr);
-    }
-  }
-  float mx = z[0];
-#pragma unroll
-  for (int e = 1; e < 16; ++e) mx = fmaxf(mx, z[e]);
-  const float mc = wave_max(mx);
-  // exp2(a (z - mc)) = exp2(fma(z, a, -hi)) * exp2(-lo), a * mc = hi + lo exactly.
-  const float a = ri.a;
-  const float hi = a * mc;
-  const float lo = __builtin_fmaf(a, mc, -hi);
-  float sa = 0.0f;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) sa += exp2_acc(__builtin_fmaf(z[e], a, -hi));
-  const float2 entry = make_float2(mc, mc > kNegInf ? wave_sum(sa) * exp2_acc(-lo) : 0.0f);
-  if (lane == 0) p.chunk_tab[(int64_t)g * p.nc_stride + c] = entry;
 }
 
 // Flattened chunk ff of a slice: row lookup (cached) and statistics.

@@ -40,10 +40,11 @@ constexpr int kToppBuckets = 1024;                  // buckets kept, the heavies
 constexpr int kToppTop = ((127 + 21) << 23) >> 19;  // bucket of E = 2^21
 constexpr int kToppList = 2048;
 constexpr int kToppMaxNC = 512;   // chunks per row whose sums live in LDS (V <= 524288)
-// Threads per row: eight waves when most rows are dense (one row per
-// workgroup leaves few waves per CU); four with top-k on, where most rows have
+// Waves per row: up to sixteen (the register-resident pass below); the
+// two-pass kernel takes eight when most rows are dense (one row per workgroup
+// leaves few waves per CU), four with top-k on, where most rows have
 // candidate lists and their workgroups return at once.
-constexpr int kTpMaxWaves = 8;
+constexpr int kTpMaxWaves = 16;
 
 struct ToppShared {
   unsigned long long mass[kToppBuckets];  // units per bucket, index kToppTop - bucket
@@ -205,6 +206,67 @@ __device__ __forceinline__ float topp_select(ToppShared &sh, EACH each, unsigned
   return ukey_val(prefix);
 }
 
+// Boundary bucket (wave 0 scans, all threads call; a barrier follows): with
+// sh.mass holding each bucket's units, lane l owns buckets 16 l .. 16 l + 15
+// (heaviest first) and an fp64 scan in a fixed order finds the first bucket
+// b* where the mass above reaches `bound`.  Sets sh.sel = b*, sh.need = the
+// units of b* still needed to reach the bound, sh.n = 0.  It runs once per
+// row on one wave; its loops stay rolled so that it needs few registers
+// beside a row held in them.
+__device__ __forceinline__ void topp_scan(ToppShared &sh, double bound) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    double own = 0.0;
+#pragma unroll 1
+    for (int i = 0; i < 16; ++i)
+      own += __builtin_ldexp((double)sh.mass[16 * lane + i], tp_unit_exp(kToppTop - (16 * lane + i)));
+    double incl = own;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const double o = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += o;
+    }
+    double acc = incl - own;
+    int hit = -1;
+    double hit_above = 0.0;
+#pragma unroll 1
+    for (int i = 0; i < 16; ++i) {
+      const unsigned long long h = sh.mass[16 * lane + i];
+      if (h == 0) continue;
+      const double hm = __builtin_ldexp((double)h, tp_unit_exp(kToppTop - (16 * lane + i)));
+      if (acc + hm >= bound) {
+        hit = 16 * lane + i;
+        hit_above = acc;
+        break;
+      }
+      acc += hm;
+    }
+    const unsigned long long hits = __ballot(hit >= 0);
+    // the first crossing; none only through the rounding of S against the
+    // bucket sums (top_p near 1): the lightest non-empty bucket
+    const unsigned long long nonempty = __ballot(own > 0.0);
+    const int src = hits ? __ffsll((long long)hits) - 1 : 63 - __builtin_clzll(nonempty | 1ull);
+    if (lane == src) {
+      if (hit < 0) {
+#pragma unroll 1
+        for (int i = 15; i >= 0; --i)
+          if (sh.mass[16 * lane + i]) {
+            hit = 16 * lane + i;
+            hit_above = incl - __builtin_ldexp((double)sh.mass[hit], tp_unit_exp(kToppTop - hit));
+            break;
+          }
+        if (hit < 0) hit = 16 * lane;
+      }
+      sh.sel = kToppTop - hit;
+      // units of bucket b* still needed to reach the bound
+      const double rest = __builtin_ceil(__builtin_ldexp(bound - hit_above, -tp_unit_exp(kToppTop - hit)));
+      sh.need = rest < 1.0 ? 1ull : (unsigned long long)rest;
+      sh.n = 0;
+    }
+  }
+  __syncthreads();
+}
+
 template <int DT, int NT>
 __global__ __launch_bounds__(NT) void topp_kernel(Params p) {
   static_assert(NT % 256 == 0 && NT / 64 <= kTpMaxWaves, "the selects' 256-bin histograms and the wave maxima");
@@ -288,56 +350,7 @@ __global__ __launch_bounds__(NT) void topp_kernel(Params p) {
     });
   }
   __syncthreads();
-  // Scan (wave 0): lane l owns buckets 16 l .. 16 l + 15 (heaviest first); fp64
-  // in a fixed order.
-  if (wave == 0) {
-    double own = 0.0;
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      own += __builtin_ldexp((double)sh.mass[16 * lane + i], tp_unit_exp(kToppTop - (16 * lane + i)));
-    double incl = own;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const double o = __shfl_up(incl, d, 64);
-      if (lane >= d) incl += o;
-    }
-    double acc = incl - own;
-    int hit = -1;
-    double hit_above = 0.0;
-    for (int i = 0; i < 16; ++i) {
-      const unsigned long long h = sh.mass[16 * lane + i];
-      if (h == 0) continue;
-      const double hm = __builtin_ldexp((double)h, tp_unit_exp(kToppTop - (16 * lane + i)));
-      if (acc + hm >= bound) {
-        hit = 16 * lane + i;
-        hit_above = acc;
-        break;
-      }
-      acc += hm;
-    }
-    const unsigned long long hits = __ballot(hit >= 0);
-    // the first crossing; none only through rounding (S from the tables, top_p
-    // near 1): the lightest non-empty bucket
-    const unsigned long long nonempty = __ballot(own > 0.0);
-    const int src = hits ? __ffsll((long long)hits) - 1 : 63 - __builtin_clzll(nonempty | 1ull);
-    if (lane == src) {
-      if (hit < 0) {
-        for (int i = 15; i >= 0; --i)
-          if (sh.mass[16 * lane + i]) {
-            hit = 16 * lane + i;
-            hit_above = incl - __builtin_ldexp((double)sh.mass[hit], tp_unit_exp(kToppTop - hit));
-            break;
-          }
-        if (hit < 0) hit = 16 * lane;
-      }
-      sh.sel = kToppTop - hit;
-      // units of bucket b* still needed to reach the bound
-      const double rest = __builtin_ceil(__builtin_ldexp(bound - hit_above, -tp_unit_exp(kToppTop - hit)));
-      sh.need = rest < 1.0 ? 1ull : (unsigned long long)rest;
-      sh.n = 0;
-    }
-  }
-  __syncthreads();
+  topp_scan(sh, bound);
   const int bstar = sh.sel;
   const int ustar = tp_unit_exp(bstar);
   const unsigned long long need = sh.need;
@@ -438,6 +451,339 @@ __global__ __launch_bounds__(NT) void topp_kernel(Params p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Top-p call over rows held in registers.  For aligned bf16 rows of at most
+// kResidentMaxChunks chunks, without top-k or penalties, one workgroup of
+// kResidentThreads threads takes one target row: wave w loads chunks w,
+// w + 16, ... once, in the streaming pass's layout (two 16-byte vectors per
+// lane and chunk; 64 registers hold the row), and every step runs from those
+// registers, so the call reads each row once and needs no streaming pass.
+// Rows without a nucleus (greedy requests, top_p = 1) get the streaming
+// pass's chunk statistics.  Nucleus rows: the row scale m, the row mass S as
+// a sum of the weights 2^(a (z - m)) (fp32 over each lane's 16 tokens of a
+// chunk, fp64 beyond), then the boundary.  Without penalties all tokens of
+// one bf16 value weigh the same, so counting the tokens of each value near
+// the top (one LDS increment per token, no weight) gives exact masses, and a
+// scan over the values finds z* itself; the kept mass per chunk then takes one
+// more pass.  When the nucleus reaches below that window of values, the
+// bucket steps of the two-pass kernel above run on the registers instead
+// (histogram of units, boundary bucket, list and weighted select).
+// The pass is bound by the VALU and LDS work per token rather than by HBM:
+// while a workgroup computes, its CU has no loads in flight.
+// ---------------------------------------------------------------------------
+constexpr int kResWaves = kResidentThreads / 64;
+constexpr int kResSlots = kResidentMaxChunks / kResWaves;  // chunks per wave
+static_assert(kResidentThreads == kToppBuckets && kResWaves <= kTpMaxWaves, "one bucket per thread to clear");
+static_assert(kResidentMaxChunks <= kToppMaxNC, "chunk sums in LDS");
+
+// An empty asm statement that "rewrites" one chunk's registers: placed before
+// each use of a chunk in each pass, so that the compiler decodes the logits
+// and computes the weights there (a few instructions each) instead of keeping
+// those of many chunks live at once, which would not fit the 128 registers a
+// lane has.
+__device__ __forceinline__ void res_fence(u32x4 (&w)[2]) { asm volatile("" : "+v"(w[0]), "+v"(w[1])); }
+
+// Order-preserving 16-bit key of a bf16 bit pattern (larger value, larger key)
+// and back.
+__device__ __forceinline__ uint32_t res_key(uint32_t b) { return b ^ ((b & 0x8000u) ? 0xFFFFu : 0x8000u); }
+__device__ __forceinline__ float res_val(uint32_t k) { return __uint_as_float((k ^ ((k & 0x8000u) ? 0x8000u : 0xFFFFu)) << 16); }
+// bf16 bit pattern of element e of a chunk in the layout of Layout<1>.
+__device__ __forceinline__ uint32_t res_bits(const u32x4 (&w)[2], int e) {
+  const u32x4 x = w[e >> 3];
+  const int k = e & 7;
+  const uint32_t u = (k >> 1) == 0 ? x.x : (k >> 1) == 1 ? x.y : (k >> 1) == 2 ? x.z : x.w;
+  return (k & 1) ? (u >> 16) : (u & 0xFFFFu);
+}
+
+constexpr int kResValueBins = 4096;  // bf16 values below the row maximum counted one by one
+struct ResShared {
+  ToppShared t;
+  unsigned cnt[kResValueBins];
+  int wmin[kResWaves];
+};
+
+__global__ __launch_bounds__(kResidentThreads) void topp_resident_kernel(Params p) {
+  using L = Layout<1>;
+  __shared__ ResShared rs;
+  ToppShared &sh = rs.t;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = blockIdx.x;
+  // The row first.  Vector h of chunk c = wave + 16 j holds tokens
+  // c C + 512 h + 8 lane .. + 7; vectors at or past V (a multiple of 8) and
+  // chunks past the row read as -inf.
+  u32x4 v[kResSlots][2];
+  {
+    const u32x4 *row = reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(p.logits) + (int64_t)g * p.lstride);
+    const u32x4 ninf = {0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u};
+#pragma unroll
+    for (int j = 0; j < kResSlots; ++j)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int x0 = (wave + kResWaves * j) * kChunk + 512 * h + 8 * lane;
+        v[j][h] = x0 < p.V ? __builtin_nontemporal_load(&row[x0 >> 3]) : ninf;
+      }
+  }
+  const Req q = lookup_req(p, g);
+  const RowInfo ri = row_info_of(p, q, g);
+  if (ri.mode == kModeInvalid) {  // no table; the epilogue flags the request
+    if (tid == 0) p.cand_n[g] = kRowDense;
+    return;
+  }
+  if (ri.mode != kModeSample || !(q.top_p < 1.0f)) {
+#pragma unroll
+    for (int j = 0; j < kResSlots; ++j) {
+      res_fence(v[j]);
+      const int c = wave + kResWaves * j;
+      if (c < p.NC) chunk_stats<1>(p, ri, c, v[j]);
+    }
+    if (tid == 0) p.cand_n[g] = kRowDense;
+    return;
+  }
+
+  const float a = q.a;
+  float2 *tab = p.chunk_tab + (int64_t)g * p.nc_stride;
+  sh.mass[tid] = 0;
+  if (tid < kResidentMaxChunks) sh.lsum[tid] = 0;
+#pragma unroll
+  for (int i = 0; i < kResValueBins / kResidentThreads; ++i) rs.cnt[tid + i * kResidentThreads] = 0;
+  // Row scale m.
+  float lm = kNegInf;
+#pragma unroll
+  for (int j = 0; j < kResSlots; ++j) {
+    res_fence(v[j]);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) lm = fmaxf(lm, L::elem(v[j], e));
+  }
+  lm = wave_max(lm);
+  if (lane == 0) sh.wmax[wave] = lm;
+  __syncthreads();
+  float m = sh.wmax[0];
+#pragma unroll
+  for (int w = 1; w < kResWaves; ++w) m = fmaxf(m, sh.wmax[w]);
+  if (!(m > kNegInf)) {  // no finite logit: the streaming pass's entries; the epilogue flags the row
+    for (int c = tid; c < p.NC; c += kResidentThreads) tab[c] = make_float2(kNegInf, 0.0f);
+    if (tid == 0) p.cand_n[g] = kRowDense;
+    return;
+  }
+  // Row mass S.
+  double ls = 0.0;
+#pragma unroll
+  for (int j = 0; j < kResSlots; ++j) {
+    res_fence(v[j]);
+    float cs = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) cs += tp_weight(L::elem(v[j], e), a, m);
+    ls += (double)cs;
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) ls += __shfl_xor(ls, d, 64);
+  if (lane == 0) sh.wsum[wave] = ls;
+  __syncthreads();
+  double S = 0.0;
+#pragma unroll
+  for (int w = 0; w < kResWaves; ++w) S += sh.wsum[w];
+  const double bound = (double)q.top_p * S;
+  const float zskip = tp_logit_bound((float)((1.0 - (double)q.top_p) * S / (2.0 * p.V)), m, a);
+
+  // Exact boundary from counts of bf16 values.  Without penalties all tokens
+  // of one bf16 value weigh the same, so a value's mass is its count times one
+  // weight.  The tokens whose keys lie in the kResValueBins keys up to the row
+  // maximum's (and not below E_skip's) are counted; a block scan over those
+  // values from the top finds z*, the smallest value whose strictly larger
+  // values hold less than top_p S.  When the whole window holds less than
+  // top_p S the boundary lies below it and the bucket path takes over.
+  {
+    const uint32_t khi = res_key(__float_as_uint(m) >> 16);
+    const uint32_t k0 = khi >= (uint32_t)(kResValueBins - 1) ? khi - (uint32_t)(kResValueBins - 1) : 0u;
+    const uint32_t kcut = max(k0, res_key(__float_as_uint(zskip) >> 16));
+#pragma unroll
+    for (int j = 0; j < kResSlots; ++j) {
+      res_fence(v[j]);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const uint32_t key = res_key(res_bits(v[j], e));
+        if (key >= kcut) atomicAdd(&rs.cnt[key - k0], 1u);
+      }
+    }
+    __syncthreads();
+    // Thread t holds keys khi - 4 t .. khi - 4 t - 3 (the heaviest first); an
+    // fp64 scan in a fixed order gives each key the mass strictly above it.
+    constexpr int PER = kResValueBins / kResidentThreads;
+    auto mass_of = [&](int i) {  // mass of this thread's i-th key (recomputed where needed)
+      const int kk = (int)khi - (PER * tid + i);
+      const unsigned c = kk >= (int)kcut ? rs.cnt[kk - (int)k0] : 0u;
+      return c ? (double)c * (double)tp_weight(res_val((uint32_t)kk), a, m) : 0.0;
+    };
+    double own = 0.0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) own += mass_of(i);
+    double incl = own;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const double o = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += o;
+    }
+    if (lane == 63) sh.wsum[wave] = incl;
+    __syncthreads();
+    double before = incl - own, total = 0.0;
+#pragma unroll
+    for (int w = 0; w < kResWaves; ++w) {
+      const double sw = sh.wsum[w];
+      if (w < wave) before += sw;
+      total += sw;
+    }
+    if (total >= bound) {  // uniform: the boundary is inside the window
+      int kmin = 0x7FFFFFFF;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int kk = (int)khi - (PER * tid + i);
+        if (kk >= (int)kcut && before < bound) kmin = kk;
+        before += mass_of(i);
+      }
+      kmin = wave_min_i(kmin);
+      if (lane == 0) rs.wmin[wave] = kmin;
+      __syncthreads();
+      int ks = rs.wmin[0];
+#pragma unroll
+      for (int w = 1; w < kResWaves; ++w) ks = min(ks, rs.wmin[w]);
+      const float zstar = res_val((uint32_t)ks);
+      // Kept mass per chunk: one wave sum, written by the chunk's wave.
+#pragma unroll
+      for (int j = 0; j < kResSlots; ++j) {
+        res_fence(v[j]);
+        float acc = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float z = L::elem(v[j], e);
+          if (z >= zstar) acc += tp_weight(z, a, m);
+        }
+        const int c = wave + kResWaves * j;
+        const float sum = wave_sum(acc);
+        if (lane == 0 && c < p.NC) tab[c] = make_float2(m, sum);
+      }
+      if (tid == 0) {
+        p.cand_tau[g] = zstar;
+        p.cand_n[g] = kRowTopP;
+      }
+      return;
+    }
+  }
+
+  // Pass A: units per bucket of the tokens not below E_skip.
+#pragma unroll
+  for (int j = 0; j < kResSlots; ++j) {
+    res_fence(v[j]);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float z = L::elem(v[j], e);
+      if (z >= zskip) {
+        const float E = tp_weight(z, a, m);
+        const int i = max(kToppTop - tp_bucket(E), 0);  // never clamped: E <= 1
+        if (i < kToppBuckets) atomicAdd(&sh.mass[i], tp_units(E));
+      }
+    }
+  }
+  __syncthreads();
+  topp_scan(sh, bound);
+  const int bstar = sh.sel;
+  const int ustar = tp_unit_exp(bstar);
+  const unsigned long long need = sh.need;
+  const float zb = tp_logit_bound(__uint_as_float((uint32_t)bstar << 19), m, a);
+
+  // Every token of bucket b* lies in [zb, zt]: the logit bounds of b* and of
+  // the next bucket, each 0.01 log2 units beyond the weight's rounding.
+  const float zt = m + (__log2f(__uint_as_float((uint32_t)(bstar + 1) << 19)) + 0.01f) / a;
+  // Pass B: per chunk the weight of the tokens heavier than bucket b* (one
+  // wave sum: a fixed order).
+#pragma unroll
+  for (int j = 0; j < kResSlots; ++j) {
+    res_fence(v[j]);
+    float acc = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float z = L::elem(v[j], e);
+      if (z >= zb) {
+        const float E = tp_weight(z, a, m);
+        if (tp_bucket(E) > bstar) acc += E;
+      }
+    }
+    const int c = wave + kResWaves * j;
+    const float sum = __ballot(acc != 0.0f) ? wave_sum(acc) : 0.0f;
+    if (lane == 0 && c < p.NC) sh.part[c] = sum;
+  }
+  // Bucket b*'s tokens into the list (few: one atomic per wave and hit).
+#pragma unroll
+  for (int j = 0; j < kResSlots; ++j) {
+    res_fence(v[j]);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float z = L::elem(v[j], e);
+      bool in = z >= zb && z <= zt;
+      if (__ballot(in) == 0) continue;
+      in = in && tp_bucket(tp_weight(z, a, m)) == bstar;
+      const unsigned long long hit = __ballot(in);
+      if (hit == 0) continue;
+      int base = 0;
+      if (lane == 0) base = atomicAdd(&sh.n, __popcll(hit));
+      base = __shfl(base, 0, 64);
+      const int pos =
+          base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(hit >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)hit, 0u));
+      if (in && pos < kToppList) {
+        sh.lz[pos] = z;
+        sh.lx[pos] = (wave + kResWaves * j) * kChunk + L::local(e, lane);
+      }
+    }
+  }
+  __syncthreads();
+  const int n = sh.n;
+  float zstar;
+  if (n <= kToppList) {
+    zstar = topp_select(
+        sh, [&](auto fn) {
+          for (int e = tid; e < n; e += kResidentThreads) fn(sh.lz[e], tp_units(tp_weight(sh.lz[e], a, m)));
+        },
+        need);
+    for (int e = tid; e < n; e += kResidentThreads)
+      if (sh.lz[e] >= zstar) atomicAdd(&sh.lsum[sh.lx[e] / kChunk], tp_units(tp_weight(sh.lz[e], a, m)));
+  } else {  // b* holds more tokens than the list: from the registers again
+    zstar = topp_select(
+        sh, [&](auto fn) {
+#pragma unroll
+          for (int j = 0; j < kResSlots; ++j) {
+            res_fence(v[j]);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const float z = L::elem(v[j], e);
+              if (z >= zb && z <= zt) {
+                const float E = tp_weight(z, a, m);
+                if (tp_bucket(E) == bstar) fn(z, tp_units(E));
+              }
+            }
+          }
+        },
+        need);
+#pragma unroll
+    for (int j = 0; j < kResSlots; ++j) {
+      res_fence(v[j]);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float z = L::elem(v[j], e);
+        if (z >= zb && z <= zt && z >= zstar) {
+          const float E = tp_weight(z, a, m);
+          if (tp_bucket(E) == bstar) atomicAdd(&sh.lsum[wave + kResWaves * j], tp_units(E));
+        }
+      }
+    }
+  }
+  __syncthreads();
+  for (int c = tid; c < p.NC; c += kResidentThreads)
+    tab[c] = make_float2(m, sh.part[c] + (float)__builtin_ldexp((double)sh.lsum[c], ustar));
+  if (tid == 0) {
+    p.cand_tau[g] = zstar;
+    p.cand_n[g] = kRowTopP;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_topp(const Params &p, hipStream_t s) {
@@ -453,6 +799,11 @@ hipError_t launch_topp(const Params &p, hipStream_t s) {
       topp_kernel<0, 512><<<dim3(p.R), dim3(512), 0, s>>>(p);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_topp_resident(const Params &p, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+  return launch_timed(reinterpret_cast<const void *>(&topp_resident_kernel), dim3((unsigned)p.R), p, s, t0, t1,
+                      kResidentThreads);
 }
 
 }  // namespace sv

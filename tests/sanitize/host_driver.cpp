@@ -17,11 +17,12 @@ namespace {
 Params g_last;
 LmParams g_lm;
 PostParams g_post;
-int g_n[12];
+int g_n[13];
 }  // namespace
-enum { kTopk, kTopp, kStats, kEpi, kResid, kZero, kDbg, kDraft, kPost, kPhilox, kNoise, kLm };
+enum { kTopk, kTopp, kStats, kEpi, kResid, kZero, kDbg, kDraft, kPost, kPhilox, kNoise, kLm, kRes };
 hipError_t launch_topk(const Params &p, hipStream_t, hipEvent_t, hipEvent_t) { g_last = p; ++g_n[kTopk]; return hipSuccess; }
 hipError_t launch_topp(const Params &p, hipStream_t) { g_last = p; ++g_n[kTopp]; return hipSuccess; }
+hipError_t launch_topp_resident(const Params &p, hipStream_t, hipEvent_t, hipEvent_t) { g_last = p; ++g_n[kRes]; return hipSuccess; }
 hipError_t launch_stats(const Params &p, hipStream_t, hipEvent_t, hipEvent_t) { g_last = p; ++g_n[kStats]; return hipSuccess; }
 hipError_t launch_epilogue(const Params &p, hipStream_t, hipEvent_t, hipEvent_t) { g_last = p; ++g_n[kEpi]; return hipSuccess; }
 hipError_t launch_resid(const Params &p, hipStream_t) { g_last = p; ++g_n[kResid]; return hipSuccess; }
@@ -137,8 +138,22 @@ int main() {
   CHECK(spec_verify_run(&ct, &ak, nullptr) == SV_OK && g_n[kTopk] == nt + 1 && g_last.fast == 0);
   sv_verify_args aq = a;
   aq.top_p = (const float *)g_fake;
-  const int np = g_n[kTopp], ns_ = g_n[kStats];
-  CHECK(spec_verify_run(&c, &aq, nullptr) == SV_OK && g_n[kTopp] == np + 1 && g_n[kStats] == ns_ + 2);
+  // Aligned bf16 rows of at most 128 chunks: the register-resident pass alone.
+  int np = g_n[kTopp], ns_ = g_n[kStats], nres = g_n[kRes];
+  CHECK(spec_verify_run(&c, &aq, nullptr) == SV_OK && g_n[kRes] == nres + 1 && g_n[kTopp] == np &&
+        g_n[kStats] == ns_ && g_last.cand_valid == 1);
+  // Larger vocabularies, fp32 rows or penalties: the two-pass kernel between two statistics passes.
+  sv_verify_args aq2 = aq;
+  aq2.logits_dtype = SV_F32;
+  np = g_n[kTopp], ns_ = g_n[kStats], nres = g_n[kRes];
+  CHECK(spec_verify_run(&c, &aq2, nullptr) == SV_OK && g_n[kTopp] == np + 1 && g_n[kStats] == ns_ + 2 && g_n[kRes] == nres);
+  aq2 = aq;
+  aq2.frequency_penalty = (const float *)g_fake;
+  aq2.idx_mapping = (const int32_t *)g_fake;
+  aq2.output_bin_counts = (const int32_t *)g_fake;
+  aq2.num_slots = 300;
+  np = g_n[kTopp], ns_ = g_n[kStats], nres = g_n[kRes];
+  CHECK(spec_verify_run(&c, &aq2, nullptr) == SV_OK && g_n[kTopp] == np + 1 && g_n[kStats] == ns_ + 2 && g_n[kRes] == nres);
   sv_verify_args ad = a;
   ad.draft_probs = (const float *)g_fake;
   ad.draft_row_stride = a.vocab_size;

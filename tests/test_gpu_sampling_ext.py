@@ -38,6 +38,15 @@ CASES = {
     "topp_penalty": C3.with_(B=8, V=6000, history=300, rep_penalty=1.2, freq=0.3, top_p=0.85),
     "topp_greedy_mix": C2.with_(B=12, V=4000, top_p=0.7),
     "topp_student_t": C5.with_(B=6, V=8000, top_p=0.95),
+    # bf16 rows held in registers: at most 128 chunks; one chunk more takes the two-pass kernel
+    "topp_resident_max_chunks": C3.with_(B=6, V=131072, top_p=0.9),
+    "topp_past_resident_limit": C3.with_(B=6, V=131072 + 8, top_p=0.9),
+    "topp_one_partial_chunk": C3.with_(B=10, V=1000, top_p=0.8),
+    # logits near 0: the nucleus reaches past the value window (negative logits),
+    # so the bucket path finds the boundary; at scale 0.01 its boundary bucket
+    # holds more tokens than the LDS list
+    "topp_bucket_fallback": C3.with_(B=6, V=9008, top_p=0.9, scale=0.3),
+    "topp_bucket_list_overflow": C3.with_(B=4, V=9008, top_p=0.9, scale=0.01),
     # top-p on top-k candidate lists, and on top-k threshold rows (k > candidates)
     "topk_topp": C4.with_(B=6, K=3, V=4000, history=40, top_p=0.8),
     "topk_big_topp": C4.with_(B=4, K=2, V=9000, top_k=2000, draft_top_k=0, history=30, top_p=0.9),
@@ -78,6 +87,25 @@ def test_topp_uniform_rows_take_the_row_select():
     n_margin, bad = check_requests(g, inp, range(3), probs=True)
     assert not bad, "\n".join(bad)
     assert np.allclose(g["probs"], 1.0 / 6000, atol=1e-9)
+
+
+def test_topp_masked_vocabulary_tail():
+    # Logits past a cut are -inf (a masked vocabulary); one row is all -inf and
+    # its request is flagged, the others keep their nucleus among the rest.
+    import rejection_sampling_verify_05_amd as sv
+    w = C3.with_(B=8, V=9008, top_p=0.85)
+    inp = wl.make_inputs(w, DEV)
+    inp["logits"][:, 5000:] = float("-inf")
+    g0 = int(inp["cu"][3].item()) + 3  # first target row of request 3
+    inp["logits"][g0] = float("-inf")
+    with ctx_for(inp) as ctx:
+        g = run_gpu(ctx, inp, seed=3, offset=7, dbg_probs=True)
+    assert g["err"] == sv.SV_ERR_ROW
+    assert g["num_sampled"][3] == 0 and np.all(g["tokens"][3] == -1)
+    ok = [r for r in range(8) if r != 3]
+    n_margin, bad = check_requests(g, inp, ok, 3, 7, probs=True)
+    assert not bad, "\n".join(bad)
+    assert np.all(g["tokens"][ok][g["tokens"][ok] >= 0] < 5000)
 
 
 def test_topp_at_large_vocab_sampled_rows():
