@@ -43,6 +43,7 @@ _COMMON = [CSRC + "sv_common.h", CSRC + "sv_device.h", CSRC + "sv_internal.h", "
 # while these files are unchanged.
 KERNEL_SOURCES = [CSRC + "sv_stats.hip"] + _COMMON
 KERNEL_SOURCES_TOPK = [CSRC + "sv_topk.hip", CSRC + "sv_tiles.h"] + _COMMON
+KERNEL_SOURCES_TOPP = [CSRC + "sv_topp.hip", CSRC + "sv_tiles.h"] + _COMMON
 
 
 # ... and of the LM-head GEMM on its workload
@@ -91,6 +92,7 @@ WORKLOAD_PROFILE = {
     "4": ("topk_kernel_f32_B512_K8_V151936", KERNEL_SOURCES_TOPK),
     "5": ("stats_fast_kernel_bf16_B1024_K5_V256000", KERNEL_SOURCES),
     "3f": ("stats_fast_kernel_pen_bf16_B256_V128256", KERNEL_SOURCES),
+    "3p": ("topp_resident_kernel_bf16_B256_V128256", KERNEL_SOURCES_TOPP),
 }
 
 

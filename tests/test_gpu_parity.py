@@ -60,6 +60,10 @@ EDGE = {
     # and a row shorter than the first 2048 tokens
     "topk_k256": wl.CONFIGS["4"].with_(B=4, K=2, V=9000, top_k=256, draft_top_k=0, history=60),
     "topk_k300": wl.CONFIGS["4"].with_(B=4, K=2, V=9000, top_k=300, draft_top_k=0, history=60),
+    # k above the 256 threads of a row: the first threshold is the exact k-th
+    # largest of the first tokens (fp32 and bf16 rows)
+    "topk_k700": wl.CONFIGS["4"].with_(B=4, K=2, V=9000, top_k=700, draft_top_k=0, history=60),
+    "topk_bf16_k300": wl.CONFIGS["3"].with_(B=4, V=9000, top_k=300, rep_penalty=1.2, history=50),
     "topk_short_row": wl.CONFIGS["4"].with_(B=5, K=2, V=1500, top_k=30, history=40),
 }
 
