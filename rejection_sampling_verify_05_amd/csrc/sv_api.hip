@@ -285,7 +285,9 @@ int verify_on(sv_ctx *ctx, const sv_verify_args *a, hipStream_t stream) {
   hipEvent_t e0 = ev ? ev[0] : nullptr, e1 = ev ? ev[1] : nullptr;
   if (p.has_topk && sv::launch_topk(p, stream, e0, e1) != hipSuccess) return SV_EHIP;
   if (p.has_topk) e0 = e1 = nullptr;
-  const bool resid = p.draft_probs != nullptr || p.draft_logits != nullptr;
+  // Residual kernels: draft distributions given and rows of more chunks than
+  // the epilogue takes on itself.
+  const bool resid = (p.draft_probs != nullptr || p.draft_logits != nullptr) && p.NC > sv::kInlineResidNC;
   ctx->res_dirty = resid;  // until the residual race has zeroed the count
   // Top-p on aligned bf16 rows that fit the registers of one workgroup, with
   // no top-k or penalty: a single pass that holds each row and does the

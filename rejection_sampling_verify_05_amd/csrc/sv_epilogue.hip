@@ -59,6 +59,7 @@ struct EpiSharedT {
   int j;
   int bad;
   int flag;
+  float rt[kInlineResidNC];  // residual chunk masses (vocabularies of at most kInlineResidNC chunks)
   float zc[kWaves][kChunk];  // speculative chunks of rows 0..3 (raw logits, token order)
   float zx[kWaves][kChunk];  // the draft tokens' chunks of rows 0..3
   float w1s[kWaves];         // best chunk other than the draft token's: score
@@ -263,6 +264,86 @@ __device__ __forceinline__ int spec_row(int w, int nrow) { return nrow <= kWaves
 __device__ __forceinline__ int spec_slot(int i, int nrow) {
   if (nrow <= kWaves) return i;
   return i < kWaves - 1 ? i : (i == nrow - 1 ? kWaves - 1 : -1);
+}
+
+// The residual of rejected row j of request q in this workgroup (rows of at
+// most kInlineResidNC chunks, draft distributions given): chunk masses of
+// w = max(0, p_j - q_j), wave w taking chunks w, w + 4, ... two at a time
+// with all their loads issued first, then the chunk race and the token race
+// over w; an empty residual (rounding) races over p_j.  The arithmetic and
+// random words are those of resid_kernel and resid_race_kernel.
+template <class EF, class SH>
+__device__ __forceinline__ void inline_residual(const Params &p, const Req &q, int j, int gs, float m, float s,
+                                                const Proc &pr, int64_t out_j, EF entry, SH &sh) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float inv_s = 1.0f / s, a = q.a;
+  const int64_t dr = q.c0 + j;  // the draft row of position j
+  const bool probs = p.draft_probs != nullptr;
+  const bool qvec = probs ? ((uintptr_t)p.draft_probs % 16 == 0 && p.dstride % 4 == 0) : p.dvec_ok;
+  const float mq = probs ? 0.0f : p.draft_stats[2 * dr], inv_sq = probs ? 1.0f : 1.0f / p.draft_stats[2 * dr + 1];
+  auto draft_chunk = [&](int c, float (&qx)[16]) {
+    if (probs)
+      load_chunk16_at(p.draft_probs, SV_F32, p.dstride, qvec, p.V, dr, c, qx);
+    else
+      load_chunk16_at(p.draft_logits, p.ddtype, p.dlstride, qvec, p.V, dr, c, qx);
+  };
+  for (int c0 = wave; c0 < p.NC; c0 += 2 * kWaves) {
+    const int c1 = c0 + kWaves;  // may be past the row: its values are not used
+    float za[16], zb[16], qa[16], qb[16];
+    load_chunk16_pair(p, gs, c0, c1 < p.NC ? c1 : c0, za, zb);
+    draft_chunk(c0, qa);
+    draft_chunk(c1 < p.NC ? c1 : c0, qb);
+    float acc0 = 0.0f, acc1 = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int x0 = c16_tok(c0, e, lane), x1 = c16_tok(c1, e, lane);
+      const float q0 = probs ? qa[e] : exp2_acc(q.aq * (qa[e] - mq)) * inv_sq;
+      const float q1 = probs ? qb[e] : exp2_acc(q.aq * (qb[e] - mq)) * inv_sq;
+      if (x0 < p.V) acc0 += fmaxf(exp2_acc(a * (apply_proc(za[e], x0, pr) - m)) * inv_s - q0, 0.0f);
+      if (x1 < p.V) acc1 += fmaxf(exp2_acc(a * (apply_proc(zb[e], x1, pr) - m)) * inv_s - q1, 0.0f);
+    }
+    const float w0 = wave_sum(acc0), w1 = wave_sum(acc1);
+    if (lane == 0) {
+      sh.rt[c0] = w0;
+      if (c1 < p.NC) sh.rt[c1] = w1;
+    }
+  }
+  __syncthreads();
+  const bool fallback = !(block_sum(tid < p.NC ? sh.rt[tid] : 0.0f, sh.red) > 0.0f);
+  const int cstar = block_chunk_race(p, (uint32_t)gs, p.NC, [&](int c) -> float {
+    if (!fallback) return sh.rt[c];
+    const float2 e = entry(j, c);
+    return e.x > kNegInf ? e.y * exp2_acc(a * (e.x - m)) : 0.0f;
+  }, sh.red);
+  int x = -1;
+  if (cstar >= 0) {
+    const int x0 = cstar * kChunk + 4 * tid;
+    float z[4], qx[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {  // all loads first
+      const int xc = min(x0 + k, p.V - 1);
+      z[k] = load_logit(p, gs, xc);
+      qx[k] = draft_q_of(p, q, j, xc);
+    }
+    const uint4 w4 = rng_block(p, (uint32_t)x0 >> 2, (uint32_t)gs, kTagToken);
+    ArgMax best{-1.0f, 0x7FFFFFFF};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int xx = x0 + k;
+      if (xx < p.V) {
+        const float px = exp2_acc(a * (apply_proc(z[k], xx, pr) - m)) * inv_s;
+        const float wx = fallback ? px : fmaxf(px - qx[k], 0.0f);
+        if (wx > 0.0f) {
+          const ArgMax o{race_score(wx, pick(w4, k)), xx};
+          if (better(o, best)) best = o;
+        }
+      }
+    }
+    const ArgMax bb = block_argmax(best, sh.red);
+    x = bb.s < 0.0f ? -1 : bb.i;
+  }
+  if (tid == 0) p.out_tokens[out_j] = x;
+  fused_post_update(p, q.r, q.K, j, x, [&](int i) { return sh.d[i]; });
 }
 
 // PLAIN: the call has no top-k, top-p, penalties or draft distributions and
@@ -503,6 +584,10 @@ __device__ __forceinline__ void request_epilogue(const Params &p, const Req &q_i
   }
   }
 
+  if (rejected && q.has_q && p.NC <= kInlineResidNC) {
+    inline_residual(p, q, j, gs, m, s, pr, out_j, entry, sh);
+    return;
+  }
   if (rejected && q.has_q) {
     // Dense residual: handed to resid_kernel (needs the full draft row).
     if (tid == 0) {

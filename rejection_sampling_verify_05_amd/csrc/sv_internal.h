@@ -167,6 +167,13 @@ hipError_t launch_topp_resident(const Params &p, hipStream_t s, hipEvent_t t0, h
 // t0, t1: optional events stamped at the kernel's start and end (may be null).
 hipError_t launch_stats(const Params &p, hipStream_t s, hipEvent_t t0, hipEvent_t t1);
 hipError_t launch_epilogue(const Params &p, hipStream_t s, hipEvent_t t0, hipEvent_t t1);
+// Rows of at most kInlineResidNC chunks: a rejected request's residual
+// max(0, p - q) and its race are taken in the epilogue's own workgroup (its
+// four waves load two chunks each at once: one round trip), and the residual
+// kernels are not launched.  Past that the workgroup needs one more round trip
+// per eight chunks: at 32 chunks (V = 32000) it was slower than the residual
+// kernels.
+constexpr int kInlineResidNC = 8;
 hipError_t launch_resid(const Params &p, hipStream_t s);
 // Zeroes the residual-request count (after a call that stopped before the residual race).
 hipError_t launch_zero_count(int *count, hipStream_t s);

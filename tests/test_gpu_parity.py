@@ -115,6 +115,23 @@ def test_invalid_draft_ids_are_rejected():
         assert not bad, "\n".join(bad)
 
 
+@pytest.mark.parametrize("V", [3000, 8192, 8200, 70000])
+def test_empty_residual_races_over_p(V):
+    # Every draft probability 1: max(0, p - q) is 0 everywhere, so a rejected
+    # row races over p itself.  Up to 8 chunks (V <= 8192) the residual is
+    # taken inside the epilogue, beyond that by the residual kernels.
+    w = wl.CONFIGS["1"].with_(B=16, K=3, V=V)
+    inp = wl.make_inputs(w, DEV)
+    inp["draft_probs"][:] = 1.0
+    with ctx_for(inp) as ctx:
+        for seed, off in [(0, 0), (11, 5)]:
+            g = run_gpu(ctx, inp, seed=seed, offset=off)
+            assert g["err"] == 0
+            n_margin, bad = check_requests(g, inp, range(inp["B"]), seed, off)
+            assert not bad, "\n".join(bad)
+            assert (g["num_sampled"] < inp["K"].cpu().numpy() + 1).any()  # some rows rejected
+
+
 def test_request_errors_are_flagged_and_isolated():
     import rejection_sampling_verify_05_amd as sv
     w = wl.CONFIGS["4"].with_(B=6, K=2, V=1500, history=20)
