@@ -29,12 +29,12 @@ constexpr int kRowCache = kSliceRows;  // rows of a slice looked up before strea
 // (at 4 the counts' registers leave one workgroup per CU instead of two).
 template <int DT>
 constexpr int kFastDepth = DT == 1 ? 4 : 3;
-// Waves per workgroup of the fast pass: eight (two per SIMD) for bf16 rows
-// without penalties, where halving the number of workgroups against four
-// measured about 4 % faster; four otherwise (fp32 rows and the penalty variant
-// measured about 1 % slower with eight).
+// Waves per workgroup of the fast pass: eight for bf16 rows, where halving
+// the number of workgroups against four measured about 4 % faster without
+// penalties and, with two chunks in flight, 3 % with them; four for fp32
+// rows (about 1 % slower with eight).
 template <int DT, bool PEN>
-constexpr int kFastWaves = (DT == 1 && !PEN) ? 8 : 4;
+constexpr int kFastWaves = DT == 1 ? 8 : 4;
 template <int DT, bool PEN>
 constexpr int kFastThreads = 64 * kFastWaves<DT, PEN>;
 static_assert(kRowCache <= 4, "one wave looks up each row of a slice");
@@ -276,7 +276,10 @@ __global__ __launch_bounds__((kFastThreads<DT, PEN>)) void stats_fast_kernel(Par
   constexpr bool RQ = PEN && DT == 1;
   using L = Layout<DT>;
   constexpr int NV = L::kVec;
-  constexpr int D = PEN ? 3 : kFastDepth<DT>;  // chunks in flight per wave (the counts take registers too)
+  // Chunks in flight per wave (the counts take registers too): with penalties
+  // two for bf16 rows (78 VGPRs, eight-wave workgroups; three with four-wave
+  // workgroups measured 3 % slower), three for fp32 rows.
+  constexpr int D = PEN ? (DT == 1 ? 2 : 3) : kFastDepth<DT>;
   __shared__ StatsShared sh;
   const int wave = uni((int)(threadIdx.x >> 6));
   const int N = p.R * p.NC;
