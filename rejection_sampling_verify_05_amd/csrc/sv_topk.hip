@@ -22,6 +22,11 @@ struct TopkShared {
   int sel, want;
   float theta;
   BlockScratch red;
+  // barrier-free path: each wave's histogram, count, threshold; overflow flag
+  unsigned whist[kWaves][256];
+  int wn[kWaves];
+  float wth[kWaves];
+  int wflag;
 };
 static_assert(kBuf >= 2 * kCandCap, "the id-ordered kept list is staged in the upper half of the buffer");
 
@@ -186,6 +191,159 @@ __device__ __forceinline__ int wave_offsets(TopkShared &sh, int npass, int par, 
   return __shfl(wb, 63, 64);
 }
 
+// ---------------------------------------------------------------------------
+// Barrier-free filter, for k <= kWaveTopk on aligned rows.  Each wave keeps
+// its own candidates, in its own kSeg-entry segment of the buffer, with its own
+// threshold, and selects within the segment (wave-level steps, no workgroup
+// barrier) when it fills.  A wave's k-th largest never exceeds the row's, so
+// the union of the segments holds every token of the row's top k; they are
+// merged once at the end, where the exact selection of the two-barrier path
+// takes over.  (Two barriers per super-tile cost that path about a quarter of
+// its time on 608 KB rows.)
+// ---------------------------------------------------------------------------
+constexpr int kSeg = kBuf / kWaves;
+constexpr int kWaveTopk = 128;
+
+// Exclusive prefix of npass over the wave, and the wave's total (uniform).
+__device__ __forceinline__ void wave_scan(int npass, int &excl, int &wtot) {
+  const int lane = threadIdx.x & 63;
+  int incl = npass;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += o;
+  }
+  excl = incl - npass;
+  wtot = __builtin_amdgcn_readfirstlane(__shfl(incl, 63, 64));
+}
+
+// k-th largest value among the n entries of segment s (1 <= k <= n): MSD radix
+// select over order-preserving keys with the wave's own 256-bin histogram.
+__device__ __forceinline__ float wave_kth(TopkShared &sh, int s, int n, int k) {
+  const int lane = threadIdx.x & 63;
+  unsigned *h = sh.whist[s];
+  const float *bv = sh.bv + s * kSeg;
+  uint32_t prefix = 0, mask = 0;
+  int want = k;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) h[lane + 64 * i] = 0;
+    for (int e = lane; e < n; e += 64) {
+      const uint32_t key = ukey(bv[e]);
+      if ((key & mask) == prefix) atomicAdd(&h[(key >> shift) & 0xFFu], 1u);
+    }
+    // lane l holds bins 255 - 4l .. 252 - 4l (descending): the lane whose
+    // bins the want-th largest falls in picks the digit
+    int hh[4], own = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      hh[i] = (int)h[255 - 4 * lane - i];
+      own += hh[i];
+    }
+    int incl = own;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += o;
+    }
+    const int before = incl - own;
+    const unsigned long long here = __ballot(before < want && incl >= want);
+    const int src = __ffsll((long long)here) - 1;  // one lane: the matching keys number at least want
+    int sel = 0, nwant = want;
+    if (lane == src) {
+      int acc = before;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (acc + hh[i] >= want) {
+          sel = 255 - 4 * lane - i;
+          nwant = want - acc;
+          break;
+        }
+        acc += hh[i];
+      }
+    }
+    sel = __builtin_amdgcn_readlane(sel, src);
+    want = __builtin_amdgcn_readlane(nwant, src);
+    prefix |= (uint32_t)sel << shift;
+    mask |= 0xFFu << shift;
+  }
+  return ukey_val(prefix);
+}
+
+// Applies the penalty to the unresolved entries of segment s that are >= t;
+// whether any value changed (uniform).
+__device__ __forceinline__ bool wave_resolve(TopkShared &sh, int s, int n, float t, const Proc &pr) {
+  const int lane = threadIdx.x & 63;
+  float *bv = sh.bv + s * kSeg;
+  int *bi = sh.bi + s * kSeg;
+  bool changed = false;
+#pragma unroll
+  for (int h = 0; h < kSeg / 64; h += 4) {
+    int xs[4], c[4];
+    float vs[4];
+    bool need[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int e = lane + 64 * (h + m);
+      xs[m] = e < n ? bi[e] : 0;
+      vs[m] = e < n ? bv[e] : kNegInf;
+      need[m] = e < n && (xs[m] & kUnresolved) && vs[m] >= t;
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) c[m] = need[m] ? pr.counts[xs[m] & 0x7FFFFFFF] : 0;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      if (need[m]) {
+        const int e = lane + 64 * (h + m);
+        const float z = c[m] > 0 ? penalize(vs[m], c[m], pr) : vs[m];
+        changed |= z != vs[m];
+        bv[e] = z;
+        bi[e] = xs[m] & 0x7FFFFFFF;
+      }
+    }
+  }
+  return __ballot(changed) != 0;
+}
+
+// select_tau within segment s.
+__device__ __forceinline__ float wave_select_tau(TopkShared &sh, int s, int n, int k, const Proc &pr) {
+  for (;;) {
+    const float t = wave_kth(sh, s, n, k);
+    if (pr.counts == nullptr || !wave_resolve(sh, s, n, t, pr)) return t;
+  }
+}
+
+// Keeps the entries of segment s that are >= t, compacted in order (every
+// entry is read before any is written); the new count (uniform).
+__device__ __forceinline__ int wave_keep(TopkShared &sh, int s, int n, float t) {
+  const int lane = threadIdx.x & 63;
+  constexpr int M = kSeg / 64;
+  float *bv = sh.bv + s * kSeg;
+  int *bi = sh.bi + s * kSeg;
+  float v[M];
+  int x[M];
+  bool keep[M];
+#pragma unroll
+  for (int i = 0; i < M; ++i) {
+    const int e = lane + 64 * i;
+    v[i] = e < n ? bv[e] : kNegInf;
+    x[i] = e < n ? bi[e] : 0;
+    keep[i] = e < n && v[i] >= t;
+  }
+  int cnt = 0;
+#pragma unroll
+  for (int i = 0; i < M; ++i) {
+    const unsigned long long b = __ballot(keep[i]);
+    if (keep[i]) {
+      const int pos = cnt + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+      bv[pos] = v[i];
+      bi[pos] = x[i];
+    }
+    cnt += __popcll(b);
+  }
+  return cnt;
+}
+
 template <int DT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void topk_kernel(Params p) {
   __shared__ TopkShared sh;
@@ -220,6 +378,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     sh.n = 0;
     sh.theta = kNegInf;
     sh.tile_n[0] = sh.tile_n[1] = 0;
+    sh.wflag = 0;
   }
   __syncthreads();
   // Streaming filter in super-tiles of kTopkTile tokens, kTopkPer per thread
@@ -235,6 +394,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   const bool pen = pr.counts != nullptr;
   const bool raw_first = !pen || (pr.theta >= 1.0f && pr.freq >= 0.0f && pr.pres >= 0.0f);
   bool overflow = k > kCandCap;
+  const bool wpath = p.vec_ok && k <= kWaveTopk;  // the barrier-free filter
+  int wn0 = 0;  // its first passers in this wave's segment
   if (!overflow && k <= kThreads) {
     // First threshold: the k-th largest of the threads' maxima over the first
     // kBuf tokens (k distinct tokens reach it, so it is a lower bound of
@@ -287,24 +448,39 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
       npass += z[e] > kNegInf ? 1 : 0;
     }
     int excl;
-    const int wb = wave_offsets(sh, npass, 0, excl);
-    __syncthreads();
-    const int n = sh.tile_n[0];
-    int pos = wb + excl;
+    if (wpath) {  // into this wave's segment (kFirstPer per lane: it fits)
+      int wtot;
+      wave_scan(npass, excl, wtot);
+      int pos = (int)(threadIdx.x >> 6) * kSeg + excl;
 #pragma unroll
-    for (int e = 0; e < kFirstPer; ++e) {
-      if (z[e] > kNegInf) {
-        sh.bv[pos] = z[e];
-        sh.bi[pos] = topk_tok<DT>(0, e);
-        ++pos;
+      for (int e = 0; e < kFirstPer; ++e) {
+        if (z[e] > kNegInf) {
+          sh.bv[pos] = z[e];
+          sh.bi[pos] = topk_tok<DT>(0, e);
+          ++pos;
+        }
       }
+      wn0 = wtot;
+    } else {
+      const int wb = wave_offsets(sh, npass, 0, excl);
+      __syncthreads();
+      const int n = sh.tile_n[0];
+      int pos = wb + excl;
+#pragma unroll
+      for (int e = 0; e < kFirstPer; ++e) {
+        if (z[e] > kNegInf) {
+          sh.bv[pos] = z[e];
+          sh.bi[pos] = topk_tok<DT>(0, e);
+          ++pos;
+        }
+      }
+      __syncthreads();  // every thread has read tile_n[0]
+      if (threadIdx.x == 0) {
+        sh.n = n;
+        sh.tile_n[0] = 0;
+      }
+      __syncthreads();
     }
-    __syncthreads();  // every thread has read tile_n[0]
-    if (threadIdx.x == 0) {
-      sh.n = n;
-      sh.tile_n[0] = 0;
-    }
-    __syncthreads();
   } else if (!overflow) {
     // k above the thread count: theta = the exact k-th largest of the first
     // kBuf tokens.
@@ -393,11 +569,124 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     }
     __syncthreads();
   };
+  if (p.vec_ok && wpath) {
+    // Barrier-free: each wave filters its own tokens into its own segment,
+    // two super-tiles in flight as below.
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    int wn = wn0;
+    float wth = sh.theta;
+    bool wover = false;
+    const int flag = raw_first && pen ? kUnresolved : 0;
+    auto wave_tile = [&](int base, float (&z)[kTopkPer]) {
+      if (!raw_first) penalize_tile<DT>(p, pr, base, z);  // a penalty < 1 can raise logits: test processed ones
+      // One comparison per token (-inf never passes; tokens past the row
+      // decode as -inf), and nothing more when no token of the wave passes:
+      // the common case once the threshold has risen.
+      const float th = fmaxf(wth, -__FLT_MAX__);
+      int npass = 0;
+#pragma unroll
+      for (int e = 0; e < kTopkPer; ++e) npass += z[e] >= th ? 1 : 0;
+      if (__ballot(npass != 0) == 0) return;
+#pragma unroll
+      for (int e = 0; e < kTopkPer; ++e)
+        if (!(z[e] >= th)) z[e] = kNegInf;
+      int excl, wtot;
+      wave_scan(npass, excl, wtot);
+      if (wn + wtot > kSeg) {
+        // Full: the wave's threshold becomes the k-th largest of its
+        // candidates (penalties applied first), then this super-tile's passers
+        // are tested again.  Fewer than k candidates or still no room: the
+        // exact radix select below.
+        if (wn < k) {
+          wover = true;
+          return;
+        }
+        const float t = wave_select_tau(sh, wv, wn, k, pr);
+        wn = wave_keep(sh, wv, wn, t);
+        wth = t;
+        npass = 0;
+#pragma unroll
+        for (int e = 0; e < kTopkPer; ++e) {
+          if (!(z[e] >= t)) z[e] = kNegInf;
+          npass += z[e] > kNegInf ? 1 : 0;
+        }
+        wave_scan(npass, excl, wtot);
+        if (wn + wtot > kSeg) {
+          wover = true;
+          return;
+        }
+      }
+      int pos = wv * kSeg + wn + excl;
+#pragma unroll
+      for (int e = 0; e < kTopkPer; ++e) {
+        if (z[e] > kNegInf) {
+          sh.bv[pos] = z[e];
+          sh.bi[pos] = topk_tok<DT>(base, e) | flag;
+          ++pos;
+        }
+      }
+      wn += wtot;
+    };
+    int base = kBuf;
+    while (base < vfull && !wover) {
+      float z[kTopkPer];
+      topk_decode<DT>(base, vfull, ra, z);
+      topk_issue<DT>(p, g, base + 2 * kTopkTile, vfull, ra);
+      wave_tile(base, z);
+      base += kTopkTile;
+      if (base >= vfull || wover) break;
+      topk_decode<DT>(base, vfull, rb, z);
+      topk_issue<DT>(p, g, base + 2 * kTopkTile, vfull, rb);
+      wave_tile(base, z);
+      base += kTopkTile;
+    }
+    if (lane == 0) {
+      sh.wn[wv] = wn;
+      sh.wth[wv] = wth;
+      if (wover) atomicOr(&sh.wflag, 1);
+    }
+    __syncthreads();
+    overflow = sh.wflag != 0;
+    if (!overflow) {
+      // Merge the segments into buffer[0, n): every entry read, then written.
+      constexpr int M = kSeg / 64;
+      float mv[M];
+      int mi[M];
+#pragma unroll
+      for (int i = 0; i < M; ++i) {
+        const int e = lane + 64 * i;
+        mv[i] = e < wn ? sh.bv[wv * kSeg + e] : 0.0f;
+        mi[i] = e < wn ? sh.bi[wv * kSeg + e] : 0;
+      }
+      int off = 0, tot = 0;
+      float th = kNegInf;  // each wave's threshold is a lower bound of tau_k: the largest one
+#pragma unroll
+      for (int v = 0; v < kWaves; ++v) {
+        if (v < wv) off += sh.wn[v];
+        tot += sh.wn[v];
+        th = fmaxf(th, sh.wth[v]);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < M; ++i) {
+        const int e = lane + 64 * i;
+        if (e < wn) {
+          sh.bv[off + e] = mv[i];
+          sh.bi[off + e] = mi[i];
+        }
+      }
+      if (threadIdx.x == 0) {
+        sh.n = tot;
+        sh.theta = th;
+      }
+      __syncthreads();
+    }
+  }
   if (p.vec_ok) {
     // Two super-tiles in flight: the next one's loads are issued before this
     // one is filtered (the first two at the start, above).
     int base = kBuf, par = 0;
-    while (base < vfull && !overflow) {
+    while (!wpath && base < vfull && !overflow) {
       float z[kTopkPer];
       topk_decode<DT>(base, vfull, ra, z);
       topk_issue<DT>(p, g, base + 2 * kTopkTile, vfull, ra);
