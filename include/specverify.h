@@ -182,18 +182,31 @@ typedef struct sv_verify_args {
   /* and vocab_size must match; tokens, num_sampled, num_rejected and           */
   /* tokens_stride are ignored).  Not with dbg_probs.                           */
   const struct sv_post_update_args *post_update;
+  /* [num_rows] or NULL: per target row, the smallest relative margin of the  */
+  /* random decisions taken on it, in the library's own fp32 quantities (slow; */
+  /* parity checks only; not with post_update).  Accept test of draft i:      */
+  /* |p - u q| / max(p, u q) ("vLLM 投机解码（Eagle / MTP）实现与运行流程",      */
+  /* section 8.3); the race of the sampled row: 1 - s2 / s1 of the best and     */
+  /* second-best race scores at the chunk level and at the token level (1     */
+  /* with a single candidate), each race recomputed over the whole row; 0     */
+  /* when that recomputation picks another token than the one written.        */
+  /* INFINITY: no random decision (greedy requests, rows after the sampled    */
+  /* one, requests written empty); synthetic acceptance has no accept margin. */
+  float *dbg_margin;
 } sv_verify_args;
 
 /*
  * Enqueue one verify step on `stream` (see the top of this file).  Reads the
  * target logits once per row in a streaming pass; in draft-probs mode it also
- * reads the full draft row of each rejected request.  With top_p, rows that
- * have no top-k candidate list are read again: two (bf16 without penalties) or
- * four more passes find the nucleus threshold, and one more recomputes their
+ * reads the full draft row of each rejected request.  With top_p and neither
+ * top_k nor a penalty, 16-byte aligned bf16 rows of at most 131072 tokens are
+ * held on chip and read once in all; otherwise rows that have no top-k
+ * candidate list are read again: two (bf16 without penalties) or four more
+ * passes find the nucleus threshold, and one more recomputes their
  * statistics under it.  A penalty array other than NULL needs idx_mapping,
  * output_bin_counts and num_slots >= 1.  Errors: SV_EINVAL (also synthetic
- * rates outside [0, 1], not finite or increasing; post_update with dbg_probs
- * or with mismatched sizes), SV_ECAPACITY, SV_EDTYPE, SV_EHIP (nothing
+ * rates outside [0, 1], not finite or increasing; post_update with dbg_probs,
+ * dbg_margin or mismatched sizes), SV_ECAPACITY, SV_EDTYPE, SV_EHIP (nothing
  * enqueued on the first three).  With post_update the bookkeeping of the step
  * is done by the call's last kernels (one launch fewer than calling
  * spec_post_update afterwards; the same results).

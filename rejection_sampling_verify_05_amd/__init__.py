@@ -94,6 +94,7 @@ class VerifyArgs(ctypes.Structure):
         ("draft_logits_stride", ctypes.c_int64),
         ("draft_logits_dtype", ctypes.c_int32),
         ("post_update", ctypes.c_void_p),
+        ("dbg_margin", ctypes.c_void_p),
     ]
 
 
@@ -265,7 +266,8 @@ def make_verify_args(target_logits, draft_ids, cu_num_draft, temperature, out_to
                      rep_penalty=None, idx_mapping=None, output_bin_counts=None, seed=0,
                      offset=0, dbg_p_draft=None, dbg_probs=None, frequency_penalty=None,
                      presence_penalty=None, top_p=None, synthetic_rates=None, draft_logits=None,
-                     draft_stats=None, draft_temperature=None, post_update=None) -> VerifyArgs:
+                     draft_stats=None, draft_temperature=None, post_update=None,
+                     dbg_margin=None) -> VerifyArgs:
     """Fill an sv_verify_args from torch tensors (no copies, no compute).
     post_update: a PostUpdateArgs (make_post_update_args) applied inside the call."""
     import torch
@@ -304,6 +306,7 @@ def make_verify_args(target_logits, draft_ids, cu_num_draft, temperature, out_to
     _dev(output_bin_counts, torch.int32, "output_bin_counts", 2)
     _dev(dbg_p_draft, torch.float32, "dbg_p_draft", 1)
     _dev(dbg_probs, torch.float32, "dbg_probs", 2)
+    _dev(dbg_margin, torch.float32, "dbg_margin", 1)
     B = cu_num_draft.numel() - 1
     a = VerifyArgs()
     a.target_logits = target_logits.data_ptr()
@@ -320,6 +323,7 @@ def make_verify_args(target_logits, draft_ids, cu_num_draft, temperature, out_to
     a.out_num_rejected = out_num_rejected.data_ptr()
     a.dbg_p_draft = None if dbg_p_draft is None else dbg_p_draft.data_ptr()
     a.dbg_probs = None if dbg_probs is None else dbg_probs.data_ptr()
+    a.dbg_margin = None if dbg_margin is None else dbg_margin.data_ptr()
     a.logits_row_stride = target_logits.stride(0)
     a.draft_row_stride = 0 if draft_probs is None else draft_probs.stride(0)
     a.seed = int(seed)
@@ -358,8 +362,9 @@ def spec_verify_run(ctx, *args, stream=None, **kwargs) -> None:
     out_tokens, out_num_sampled, out_num_rejected, *, draft_probs=None, top_k=None,
     rep_penalty=None, idx_mapping=None, output_bin_counts=None, seed=0, offset=0,
     dbg_p_draft=None, dbg_probs=None, frequency_penalty=None, presence_penalty=None,
-    top_p=None, synthetic_rates=None (a host sequence), stream=None), or
-    spec_verify_run(ctx, VerifyArgs)."""
+    top_p=None, synthetic_rates=None (a host sequence), draft_logits=None,
+    draft_stats=None, draft_temperature=None, post_update=None, dbg_margin=None,
+    stream=None), or spec_verify_run(ctx, VerifyArgs)."""
     a = args[0] if len(args) == 1 and isinstance(args[0], VerifyArgs) else make_verify_args(*args, **kwargs)
     st = lib().spec_verify_run(ctx, ctypes.byref(a), _stream_handle(stream))
     if st != SV_OK:

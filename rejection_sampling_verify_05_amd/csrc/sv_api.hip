@@ -199,9 +199,10 @@ int verify_on(sv_ctx *ctx, const sv_verify_args *a, hipStream_t stream) {
   p.out_nr = a->out_num_rejected;
   p.dbg_p_draft = a->dbg_p_draft;
   p.dbg_probs = a->dbg_probs;
+  p.dbg_margin = a->dbg_margin;
   if (a->post_update) {  // post_update inside the call
     const sv_post_update_args *u = a->post_update;
-    if (a->dbg_probs || u->num_reqs != a->num_reqs || u->vocab_size != a->vocab_size || u->num_slots < 1 ||
+    if (a->dbg_probs || a->dbg_margin || u->num_reqs != a->num_reqs || u->vocab_size != a->vocab_size || u->num_slots < 1 ||
         !u->idx_mapping || !u->query_len || !u->last_sampled || !u->output_bin_counts || !u->num_computed_tokens)
       return SV_EINVAL;
     p.pu_idx_mapping = u->idx_mapping;
@@ -322,6 +323,7 @@ int verify_on(sv_ctx *ctx, const sv_verify_args *a, hipStream_t stream) {
     ctx->res_dirty = false;
   }
   if (p.dbg_probs && sv::launch_dbg_probs(p, stream) != hipSuccess) return SV_EHIP;
+  if (p.dbg_margin && p.R > 0 && sv::launch_dbg_margin(p, stream) != hipSuccess) return SV_EHIP;
   return SV_OK;
 }
 }  // namespace

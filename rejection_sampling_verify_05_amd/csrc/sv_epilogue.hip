@@ -758,6 +758,128 @@ __global__ __launch_bounds__(kThreads) void dbg_kernel(Params p) {
 }
 
 // ---------------------------------------------------------------------------
+// Debug decision margins (parity checks): one workgroup per target row, after
+// every other kernel of the call.  Row i of a sampled request gets the
+// smallest relative margin of the random decisions taken on it: its accept
+// test when i < K_r and i <= j (|p - u q| / max(p, u q), from the row
+// statistics the epilogue stored and the same p(d), q(d) and u), and, on the
+// sampled row j, the race: its weights (p_j, the residual max(0, p_j - q_j),
+// or p_j without d_j) recomputed token by token over the whole row, the chunk
+// and token races run again with their best and second-best scores, margin
+// 1 - s2 / s1 per level (1 with a single candidate).  If that recomputation
+// picks another token than the one written, the margin is 0.
+// ---------------------------------------------------------------------------
+struct Top2 {
+  float s1, s2;  // best and second-best score (-1: none)
+  int i1;        // index of the best (lowest index among equal scores)
+  int n;         // candidates
+};
+
+__device__ __forceinline__ void top2_add(Top2 &t, float s, int i) {
+  ++t.n;
+  if (t.i1 < 0 || s > t.s1 || (s == t.s1 && i < t.i1)) {
+    if (t.i1 >= 0) t.s2 = t.s1;
+    t.s1 = s;
+    t.i1 = i;
+  } else if (s > t.s2) {
+    t.s2 = s;
+  }
+}
+
+__device__ __forceinline__ double top2_margin(const Top2 &t) {
+  if (t.n < 2) return 1.0;
+  if (!(t.s1 > 0.0f)) return 0.0;
+  return 1.0 - (double)t.s2 / (double)t.s1;
+}
+
+__global__ __launch_bounds__(kThreads) void margin_kernel(Params p) {
+  __shared__ BlockScratch red;
+  __shared__ float ts[kChunk];
+  __shared__ Top2 wt[kWaves];
+  const int g = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = find_request(p.cu, p.B, g);
+  const Req q = load_req(p, r);
+  const int i = g - q.g0;
+  const int j = p.out_ns[r] - 1;  // the sampled row (-1: request written empty)
+  double mg = __builtin_inf();
+  if (q.cu_ok && q.mode == kModeSample && i >= 0 && i <= q.K && i <= j && j <= q.K) {
+    const float4 ri = p.row_info[g];
+    const float m = ri.x, s = ri.y;
+    Proc pr = q.proc;
+    if (__float_as_int(ri.w) != kRowDense) pr.tau = p.cand_tau[g];
+    const float a = q.a;
+    const int d = i < q.K ? p.draft_ids[q.c0 + i] : -1;
+    const bool valid_d = d >= 0 && d < p.V;
+    // Accept test of draft i, in the epilogue's arithmetic.
+    if (i < q.K && !p.synthetic && valid_d) {
+      const double qd = q.has_q ? (double)draft_q_of(p, q, i, d) : 1.0;
+      if (qd > 0.0) {
+        const float pd = exp2_acc(a * (apply_proc(load_logit(p, g, d), d, pr) - m)) / s;
+        const double uq = u_accept(rng_block(p, 0, (uint32_t)g, kTagAccept).x) * qd;
+        mg = __builtin_fabs((double)pd - uq) / __builtin_fmax((double)pd, uq);
+      }
+    }
+    if (i == j) {
+      const bool rej = j < q.K;
+      const float inv_s = 1.0f / s;
+      auto weight = [&](int x, bool resid) -> float {
+        const float px = exp2_acc(a * (apply_proc(load_logit(p, g, x), x, pr) - m)) * inv_s;
+        if (!resid) return px;
+        if (q.has_q) return fmaxf(px - draft_q_of(p, q, j, x), 0.0f);
+        return x == d ? 0.0f : px;
+      };
+      // An empty residual (rounding) races over p_j, as in the epilogue.
+      float part = 0.0f;
+      if (rej)
+        for (int x = tid; x < p.V; x += kThreads) part += weight(x, true);
+      const bool resid = rej && block_sum(part, red) > 0.0f;
+      // Chunk level: wave w takes chunks w, w + kWaves, ...
+      Top2 ct{-1.0f, -1.0f, -1, 0};
+      for (int c = wave; c < p.NC; c += kWaves) {
+        float acc = 0.0f;
+        for (int e = 0; e < kChunk / 64; ++e) {
+          const int x = c * kChunk + e * 64 + lane;
+          if (x < p.V) acc += weight(x, resid);
+        }
+        const float W = wave_sum(acc);
+        if (W > 0.0f) top2_add(ct, race_score(W, pick(rng_block(p, (uint32_t)c >> 2, (uint32_t)g, kTagChunk), c & 3)), c);
+      }
+      if (lane == 0) wt[wave] = ct;
+      __syncthreads();
+      Top2 cb{-1.0f, -1.0f, -1, 0};
+      for (int w = 0; w < kWaves; ++w) {  // merge (every thread, same order)
+        const Top2 o = wt[w];
+        if (o.n == 0) continue;
+        const int n = cb.n + o.n;
+        top2_add(cb, o.s1, o.i1);
+        if (o.s2 > cb.s2) cb.s2 = o.s2;
+        cb.n = n;
+      }
+      double mr = top2_margin(cb);
+      int xs = -1;
+      if (cb.i1 >= 0) {
+        // Token level in the winning chunk.
+        for (int t = tid; t < kChunk; t += kThreads) {
+          const int x = cb.i1 * kChunk + t;
+          const float w = x < p.V ? weight(x, resid) : 0.0f;
+          ts[t] = w > 0.0f ? race_score(w, pick(rng_block(p, (uint32_t)x >> 2, (uint32_t)g, kTagToken), x & 3)) : -1.0f;
+        }
+        __syncthreads();
+        Top2 tb{-1.0f, -1.0f, -1, 0};
+        for (int t = 0; t < kChunk; ++t)
+          if (ts[t] >= 0.0f) top2_add(tb, ts[t], t);
+        mr = __builtin_fmin(mr, top2_margin(tb));
+        xs = tb.i1 < 0 ? -1 : cb.i1 * kChunk + tb.i1;
+      }
+      if (xs != p.out_tokens[(int64_t)r * p.out_stride + j]) mr = 0.0;
+      mg = __builtin_fmin(mg, mr);
+    }
+  }
+  if (tid == 0) p.dbg_margin[g] = (float)mg;
+}
+
+// ---------------------------------------------------------------------------
 // post_update ("【vllm】DeepSeekMTP、eagle", _post_update_kernel walk-through).
 // ---------------------------------------------------------------------------
 // One thread per (request, output slot): every load is issued at once (indices
@@ -832,6 +954,11 @@ hipError_t launch_resid(const Params &p, hipStream_t s) {
 hipError_t launch_dbg_probs(const Params &p, hipStream_t s) {
   const dim3 grid((unsigned)((p.V + kThreads - 1) / kThreads), (unsigned)p.R);
   dbg_kernel<<<grid, dim3(kThreads), 0, s>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_dbg_margin(const Params &p, hipStream_t s) {
+  margin_kernel<<<dim3((unsigned)p.R), dim3(kThreads), 0, s>>>(p);
   return hipGetLastError();
 }
 

@@ -54,6 +54,7 @@ struct Params {
   int32_t *out_nr;
   float *dbg_p_draft;
   float *dbg_probs;
+  float *dbg_margin;
   // scratch
   float2 *chunk_tab;           // [max_rows, nc_stride]: (r_c, s_c)
   float4 *row_info;            // [max_rows]: (m, s, argmax bits, state bits)
@@ -178,6 +179,7 @@ hipError_t launch_resid(const Params &p, hipStream_t s);
 // Zeroes the residual-request count (after a call that stopped before the residual race).
 hipError_t launch_zero_count(int *count, hipStream_t s);
 hipError_t launch_dbg_probs(const Params &p, hipStream_t s);
+hipError_t launch_dbg_margin(const Params &p, hipStream_t s);
 hipError_t launch_draft_race(const Params &p, const DraftOut &o, hipStream_t s);
 hipError_t launch_post_update(const PostParams &p, hipStream_t s);
 // Debug: Philox blocks of n counters (uint4 each) under one key; Exp(1) noise of n words.

@@ -24,6 +24,7 @@ import rejection_sampling_verify_05_amd as sv
 MARGIN = 1e-5
 PROB_ATOL = 1e-6
 TOPP_TOL = 4e-6
+MARGIN_ATOL = 2e-5  # library margins are fp32 quantities, the oracle's fp64
 
 
 class Ctx:
@@ -56,10 +57,11 @@ def ctx_for(inp, extra_rows=0):
 
 
 def run_gpu(ctx: Ctx, inp: dict, seed=0, offset=0, dbg_probs=False, out_stride=None,
-            stream=None):
+            stream=None, dbg_margin=False):
     """One spec_verify_run; returns host numpy outputs.  dbg_probs: True (every
     row's probabilities come back as "probs"), or a list of target rows (only
-    those come back, as "probs_rows")."""
+    those come back, as "probs_rows").  dbg_margin: the library's per-row
+    decision margins come back as "margin_rows"."""
     B, D, V = inp["B"], inp["D"], inp["V"]
     dev = inp["logits"].device
     if out_stride is None:
@@ -70,6 +72,7 @@ def run_gpu(ctx: Ctx, inp: dict, seed=0, offset=0, dbg_probs=False, out_stride=N
     pd = torch.full((max(D, 1),), -7.0, dtype=torch.float32, device=dev)
     probs = torch.full((inp["R"], V), -7.0, dtype=torch.float32, device=dev) if dbg_probs is not None and \
         dbg_probs is not False else None
+    mrows = torch.full((inp["R"],), -7.0, dtype=torch.float32, device=dev) if dbg_margin else None
     sv.spec_verify_run(ctx.h, inp["logits"], inp["draft_ids"], inp["cu"], inp["temperature"],
                        out, ns, nr, draft_probs=inp["draft_probs"], top_k=inp["top_k"],
                        rep_penalty=inp["rep_penalty"], idx_mapping=inp["idx_mapping"],
@@ -80,10 +83,12 @@ def run_gpu(ctx: Ctx, inp: dict, seed=0, offset=0, dbg_probs=False, out_stride=N
                        draft_logits=inp.get("draft_logits") if inp.get("draft_stats") is not None else None,
                        draft_stats=inp.get("draft_stats"),
                        draft_temperature=inp.get("draft_temp") if inp.get("draft_stats") is not None else None,
-                       stream=stream)
+                       dbg_margin=mrows, stream=stream)
     err = sv.spec_verify_read_error(ctx.h, stream)
     res = dict(tokens=out.cpu().numpy(), num_sampled=ns.cpu().numpy(),
                num_rejected=nr.cpu().numpy(), p_draft=pd[:D].cpu().numpy(), err=err)
+    if mrows is not None:
+        res["margin_rows"] = mrows.cpu().numpy()
     if probs is not None:
         if dbg_probs is True:
             res["probs"] = probs.cpu().numpy()
@@ -308,6 +313,35 @@ def check_requests(g: dict, inp: dict, requests, seed=0, offset=0, probs=False):
             if err > PROB_ATOL:
                 bad.append(f"request {r}: probability error {err:.3g}")
     return n_margin, bad
+
+
+def check_margins(g: dict, inp: dict, requests, seed=0, offset=0, atol=MARGIN_ATOL):
+    """Compare the library's per-row decision margins (run_gpu with
+    dbg_margin) with the oracle's request margins: the smallest over a
+    request's rows must match the oracle's within atol; rows after the sampled
+    one carry no decision (+inf), and neither do greedy requests.  Requests
+    whose tokens differ from the oracle's by a margin (or top-p boundary)
+    excuse are skipped.  Returns (number compared, mismatch list)."""
+    mr = g["margin_rows"]
+    out_stride = g["tokens"].shape[1]
+    bad, n = [], 0
+    for r in requests:
+        o = OracleRequest(inp, r)
+        toks, ns, nr, mg, _ = o.decide(seed, offset)
+        if compare_request(g, r, toks, ns, nr, mg, out_stride) != "ok" or o.near_topp_boundary():
+            continue
+        rows = mr[o.g0:o.g0 + o.K + 1].astype(np.float64)
+        j = int(g["num_sampled"][r]) - 1
+        if not np.all(np.isinf(rows[j + 1:])):
+            bad.append(f"request {r}: rows after the sampled row {j} carry margins {rows[j + 1:]}")
+        dev = float(rows.min())
+        if np.isinf(mg) or np.isinf(dev):
+            if not (np.isinf(mg) and np.isinf(dev)):
+                bad.append(f"request {r}: margin gpu {dev} oracle {mg}")
+        elif abs(dev - mg) > atol:
+            bad.append(f"request {r}: margin gpu {dev:.9g} oracle {mg:.9g} (rows {rows})")
+        n += 1
+    return n, bad
 
 
 def check_one(g: dict, inp: dict, r: int, host: HostInputs, seed=0, offset=0, probs_rows=None):

@@ -17,9 +17,9 @@ namespace {
 Params g_last;
 LmParams g_lm;
 PostParams g_post;
-int g_n[13];
+int g_n[14];
 }  // namespace
-enum { kTopk, kTopp, kStats, kEpi, kResid, kZero, kDbg, kDraft, kPost, kPhilox, kNoise, kLm, kRes };
+enum { kTopk, kTopp, kStats, kEpi, kResid, kZero, kDbg, kDraft, kPost, kPhilox, kNoise, kLm, kRes, kMargin };
 hipError_t launch_topk(const Params &p, hipStream_t, hipEvent_t, hipEvent_t) { g_last = p; ++g_n[kTopk]; return hipSuccess; }
 hipError_t launch_topp(const Params &p, hipStream_t) { g_last = p; ++g_n[kTopp]; return hipSuccess; }
 hipError_t launch_topp_resident(const Params &p, hipStream_t, hipEvent_t, hipEvent_t) { g_last = p; ++g_n[kRes]; return hipSuccess; }
@@ -28,6 +28,7 @@ hipError_t launch_epilogue(const Params &p, hipStream_t, hipEvent_t, hipEvent_t)
 hipError_t launch_resid(const Params &p, hipStream_t) { g_last = p; ++g_n[kResid]; return hipSuccess; }
 hipError_t launch_zero_count(int *, hipStream_t) { ++g_n[kZero]; return hipSuccess; }
 hipError_t launch_dbg_probs(const Params &p, hipStream_t) { g_last = p; ++g_n[kDbg]; return hipSuccess; }
+hipError_t launch_dbg_margin(const Params &p, hipStream_t) { g_last = p; ++g_n[kMargin]; return hipSuccess; }
 hipError_t launch_draft_race(const Params &p, const DraftOut &, hipStream_t) { g_last = p; ++g_n[kDraft]; return hipSuccess; }
 hipError_t launch_post_update(const PostParams &p, hipStream_t) { g_post = p; ++g_n[kPost]; return hipSuccess; }
 hipError_t launch_dbg_philox(const uint32_t *, int64_t, uint64_t, uint32_t *, hipStream_t) { ++g_n[kPhilox]; return hipSuccess; }
@@ -161,6 +162,12 @@ int main() {
   CHECK(spec_verify_run(&c, &ad, nullptr) == SV_OK && g_n[kResid] == nr + 1 && !sv::plain_call(g_last));
   ad.draft_row_stride = a.vocab_size - 1;
   CHECK(spec_verify_run(&c, &ad, nullptr) == SV_EINVAL);
+  // Debug margins: one more launch, after the epilogue's.
+  sv_verify_args am = a;
+  am.dbg_margin = (float *)g_fake;
+  const int nm = g_n[kMargin];
+  CHECK(spec_verify_run(&c, &am, nullptr) == SV_OK && g_n[kMargin] == nm + 1 && g_last.dbg_margin == am.dbg_margin);
+  CHECK(spec_verify_run(&c, &a, nullptr) == SV_OK && g_n[kMargin] == nm + 1);
 
   // Scalar and capacity checks (nothing launched).
   const int before = g_n[kStats];
@@ -213,6 +220,9 @@ int main() {
   e = a;
   e.post_update = &pu;
   CHECK(spec_verify_run(&c, &e, nullptr) == SV_OK && g_last.pu_idx_mapping != nullptr);
+  e.dbg_margin = (float *)g_fake;  // debug margins read the penalties' counts: not with post_update
+  CHECK(spec_verify_run(&c, &e, nullptr) == SV_EINVAL);
+  e.dbg_margin = nullptr;
   pu.num_reqs = 255;
   CHECK(spec_verify_run(&c, &e, nullptr) == SV_EINVAL);
   // Epochs advance per call and skip 0 on wrap.

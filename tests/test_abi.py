@@ -62,6 +62,7 @@ int main(void) {
   F(sv_verify_args, presence_penalty) F(sv_verify_args, top_p) F(sv_verify_args, synthetic_rates)
   F(sv_verify_args, draft_logits) F(sv_verify_args, draft_stats) F(sv_verify_args, draft_temperature)
   F(sv_verify_args, draft_logits_stride) F(sv_verify_args, draft_logits_dtype) F(sv_verify_args, post_update)
+  F(sv_verify_args, dbg_margin)
   printf("sv_draft_args %zu\n", sizeof(sv_draft_args));
   F(sv_draft_args, draft_logits) F(sv_draft_args, out_q) F(sv_draft_args, draft_stats)
   F(sv_draft_args, logits_row_stride) F(sv_draft_args, seed) F(sv_draft_args, offset)
