@@ -546,16 +546,32 @@ __global__ __launch_bounds__(kResidentThreads) void topp_resident_kernel(Params 
   if (tid < kResidentMaxChunks) sh.lsum[tid] = 0;
 #pragma unroll
   for (int i = 0; i < kResValueBins / kResidentThreads; ++i) rs.cnt[tid + i * kResidentThreads] = 0;
-  // Row scale m.
-  float lm = kNegInf;
+  // Row scale m and row mass S in one pass: each lane keeps its own
+  // reference lr (the largest of its tokens so far) and the sum of its
+  // weights 2^(a (z - lr)) (fp32 over a chunk's 16 tokens, fp64 beyond),
+  // rescaled when lr rises; then m is the largest reference and S the sum of
+  // the lane sums scaled to m.
+  float lr = kNegInf;
+  double ls = 0.0;
 #pragma unroll
   for (int j = 0; j < kResSlots; ++j) {
     res_fence(v[j]);
+    float cm = kNegInf;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) lm = fmaxf(lm, L::elem(v[j], e));
+    for (int e = 0; e < 16; ++e) cm = fmaxf(cm, L::elem(v[j], e));
+    const float nr = fmaxf(lr, cm);
+    if (nr > kNegInf) {  // lanes whose tokens so far are all padding keep (-inf, 0)
+      if (nr != lr) ls *= (double)tp_weight(lr, a, nr);
+      lr = nr;
+      res_fence(v[j]);  // decode again rather than hold 16 decoded values across the maximum
+      float cs = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) cs += tp_weight(L::elem(v[j], e), a, lr);
+      ls += (double)cs;
+    }
   }
-  lm = wave_max(lm);
-  if (lane == 0) sh.wmax[wave] = lm;
+  const float wm = wave_max(lr);
+  if (lane == 0) sh.wmax[wave] = wm;
   __syncthreads();
   float m = sh.wmax[0];
 #pragma unroll
@@ -565,16 +581,7 @@ __global__ __launch_bounds__(kResidentThreads) void topp_resident_kernel(Params 
     if (tid == 0) p.cand_n[g] = kRowDense;
     return;
   }
-  // Row mass S.
-  double ls = 0.0;
-#pragma unroll
-  for (int j = 0; j < kResSlots; ++j) {
-    res_fence(v[j]);
-    float cs = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) cs += tp_weight(L::elem(v[j], e), a, m);
-    ls += (double)cs;
-  }
+  if (lr > kNegInf) ls *= (double)tp_weight(lr, a, m);
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) ls += __shfl_xor(ls, d, 64);
   if (lane == 0) sh.wsum[wave] = ls;
@@ -602,7 +609,8 @@ __global__ __launch_bounds__(kResidentThreads) void topp_resident_kernel(Params 
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const uint32_t key = res_key(res_bits(v[j], e));
-        if (key >= kcut) atomicAdd(&rs.cnt[key - k0], 1u);
+        // (a NaN's key lies above the window: clamped, so the index stays in it)
+        if (key >= kcut) atomicAdd(&rs.cnt[min(key - k0, (uint32_t)(kResValueBins - 1))], 1u);
       }
     }
     __syncthreads();
