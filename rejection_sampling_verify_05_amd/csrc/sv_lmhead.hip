@@ -103,44 +103,42 @@ __device__ __forceinline__ void issue_part(const DmaSrc &src, uint32_t slot_lds,
 // of sub-step j is hidden element 16 j + 8 (l >> 5) + e of the step, i.e.
 // chunk 2 j + (l >> 5).  Only the wave's first NTN row subtiles hold target
 // rows (the others lie past R in the last row block) and only those are read
-// and multiplied.  The fragments are read two sub-steps at a time.
+// and multiplied.
 template <int NTN>
-__device__ __forceinline__ void compute_step(const unsigned char *wpart, const unsigned char *hpart,
-                                             f32x16 (&acc)[2][4]) {
+struct StepFrags {
+  bf16x8 wf[4][2], hf[4][NTN > 0 ? NTN : 1];
+};
+
+// Fragment reads of sub-steps j0, j0 + 1.
+template <int NTN>
+__device__ __forceinline__ void read_frags(const unsigned char *wpart, const unsigned char *hpart, StepFrags<NTN> &f,
+                                           int j0) {
   const int lane = threadIdx.x & 63, l32 = lane & 31, half = lane >> 5, wave = threadIdx.x >> 6;
   const int tq = wave & 3, wr = wave >> 2;
 #pragma unroll
-  for (int jj = 0; jj < 4; jj += 2) {
-    bf16x8 wf[2][2], hf[2][4];
+  for (int j = j0; j < j0 + 2; ++j) {
+    const int c = 2 * j + half;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int c = 2 * (jj + j) + half;
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int rw = 64 * tq + 32 * t + l32;
-        wf[j][t] = *reinterpret_cast<const bf16x8 *>(wpart + rw * kRowBytes + 16 * chunk_pos(rw, c));
-      }
-#pragma unroll
-      for (int t = 0; t < NTN; ++t) {
-        const int rh = 128 * wr + 32 * t + l32;
-        hf[j][t] = *reinterpret_cast<const bf16x8 *>(hpart + rh * kRowBytes + 16 * chunk_pos(rh, c));
-      }
+    for (int t = 0; t < 2; ++t) {
+      const int rw = 64 * tq + 32 * t + l32;
+      f.wf[j][t] = *reinterpret_cast<const bf16x8 *>(wpart + rw * kRowBytes + 16 * chunk_pos(rw, c));
     }
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int tm = 0; tm < 2; ++tm)
-#pragma unroll
-        for (int tn = 0; tn < NTN; ++tn)
-          acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j][tm], hf[j][tn], acc[tm][tn], 0, 0, 0);
+    for (int t = 0; t < NTN; ++t) {
+      const int rh = 128 * wr + 32 * t + l32;
+      f.hf[j][t] = *reinterpret_cast<const bf16x8 *>(hpart + rh * kRowBytes + 16 * chunk_pos(rh, c));
+    }
   }
 }
 
 // Step k, with S = k mod 5: its parts 2 k and 2 k + 1 sit in slots 2 S mod 5
 // and (2 S + 1) mod 5.  Wait for them (this wave's copies: everything but part
 // 2 k + 2, the last one issued; then everybody's through the barrier, which
-// also retires every wave's reads of step k - 1), copy parts 2 k + 3 and
-// 2 k + 4 into step k - 1's slots, compute.
+// also retires every wave's reads of step k - 1), read the fragments of
+// sub-steps 0 and 1, copy parts 2 k + 3 and 2 k + 4 into step k - 1's slots,
+// then the MFMAs of sub-steps 0 and 1 with the reads of sub-steps 2 and 3
+// between them (one after each MFMA: their LDS latency is hidden by matrix
+// work), then the MFMAs of 2 and 3.
 template <int S, int NTN>
 __device__ __forceinline__ void main_step(LmShared &sh, const DmaSrc &src, uint32_t ring_lds, f32x16 (&acc)[2][4],
                                           int k, int nk) {
@@ -150,9 +148,29 @@ __device__ __forceinline__ void main_step(LmShared &sh, const DmaSrc &src, uint3
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
   constexpr int s3 = (2 * S + 3) % kSlots, s4 = (2 * S + 4) % kSlots;
+  const unsigned char *wpart = sh.ring[(2 * S) % kSlots], *hpart = sh.ring[(2 * S + 1) % kSlots];
+  StepFrags<NTN> f;
+  if (NTN > 0) read_frags<NTN>(wpart, hpart, f, 0);
   if (k + 1 < nk) issue_part(src, ring_lds + s3 * kPart, k + 1, 1);
   if (k + 2 < nk) issue_part(src, ring_lds + s4 * kPart, k + 2, 0);
-  if (NTN > 0) compute_step<NTN>(sh.ring[(2 * S) % kSlots], sh.ring[(2 * S + 1) % kSlots], acc);
+  if (NTN > 0) {
+    read_frags<NTN>(wpart, hpart, f, 2);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int tm = 0; tm < 2; ++tm)
+#pragma unroll
+        for (int tn = 0; tn < NTN; ++tn)
+          acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.wf[j][tm], f.hf[j][tn], acc[tm][tn], 0, 0, 0);
+    constexpr int kReads2 = 2 * (2 + NTN);  // reads of two sub-steps
+    constexpr int kMfma2 = 2 * 2 * NTN;     // MFMAs of two sub-steps
+#pragma unroll
+    for (int i = 0; i < kReads2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * kMfma2 - kReads2, 0);
+  }
 }
 
 // The whole hidden dimension for a wave with NTN row subtiles (every wave of
