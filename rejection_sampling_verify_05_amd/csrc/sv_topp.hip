@@ -564,10 +564,13 @@ __global__ __launch_bounds__(kResidentThreads) void topp_resident_kernel(Params 
       if (nr != lr) ls *= (double)tp_weight(lr, a, nr);
       lr = nr;
       res_fence(v[j]);  // decode again rather than hold 16 decoded values across the maximum
+      // 2^(a (z - lr)) as 2^(fma(z, a, -hi)) 2^(-lo) with a lr = hi + lo exactly:
+      // one instruction per token for the exponent.
+      const float hi = a * lr, lo = __builtin_fmaf(a, lr, -hi);
       float cs = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) cs += tp_weight(L::elem(v[j], e), a, lr);
-      ls += (double)cs;
+      for (int e = 0; e < 16; ++e) cs += exp2_acc(__builtin_fmaf(L::elem(v[j], e), a, -hi));
+      ls += (double)cs * (double)exp2_acc(-lo);
     }
   }
   const float wm = wave_max(lr);
@@ -655,7 +658,9 @@ __global__ __launch_bounds__(kResidentThreads) void topp_resident_kernel(Params 
 #pragma unroll
       for (int w = 1; w < kResWaves; ++w) ks = min(ks, rs.wmin[w]);
       const float zstar = res_val((uint32_t)ks);
-      // Kept mass per chunk: one wave sum, written by the chunk's wave.
+      // Kept mass per chunk: one wave sum, written by the chunk's wave (the
+      // weights in the same hi / lo form as above).
+      const float hm = a * m, lm = __builtin_fmaf(a, m, -hm), sm = exp2_acc(-lm);
 #pragma unroll
       for (int j = 0; j < kResSlots; ++j) {
         res_fence(v[j]);
@@ -663,10 +668,10 @@ __global__ __launch_bounds__(kResidentThreads) void topp_resident_kernel(Params 
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const float z = L::elem(v[j], e);
-          if (z >= zstar) acc += tp_weight(z, a, m);
+          if (z >= zstar) acc += exp2_acc(__builtin_fmaf(z, a, -hm));
         }
         const int c = wave + kResWaves * j;
-        const float sum = wave_sum(acc);
+        const float sum = wave_sum(acc) * sm;
         if (lane == 0 && c < p.NC) tab[c] = make_float2(m, sum);
       }
       if (tid == 0) {
