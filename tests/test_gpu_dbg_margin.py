@@ -98,3 +98,27 @@ def test_dbg_margin_refused_with_post_update():
         with pytest.raises(sv.SpecVerifyError):
             sv.spec_verify_run(ctx.h, inp["logits"], inp["draft_ids"], inp["cu"], inp["temperature"], toks, ns, nr,
                                draft_probs=inp["draft_probs"], dbg_margin=mrows, post_update=pu)
+
+
+def test_dbg_margin_of_flagged_requests_is_infinite():
+    # requests written empty (bad temperature, bad penalty, slot out of range,
+    # a row with no finite logit) took no decision: +inf on every row of
+    # theirs; the valid requests keep their margins, matched to the oracle
+    w = C4.with_(B=6, K=2, V=1500, history=20)
+    inp = wl.make_inputs(w, DEV)
+    inp["temperature"][1] = -1.0
+    inp["rep_penalty"][2] = 0.0
+    inp["idx_mapping"][3] = 10 ** 6
+    g0 = int(inp["cu"][4].item()) + 4
+    inp["logits"][g0 + 1] = float("-inf")
+    with ctx_for(inp) as ctx:
+        g = run_gpu(ctx, inp, dbg_margin=True)
+    assert g["err"] != 0
+    cu = inp["cu"].cpu().numpy()
+    mr = g["margin_rows"]
+    for r in (1, 2, 3, 4):
+        rows = mr[cu[r] + r:cu[r + 1] + r + 1]
+        assert np.all(np.isinf(rows) & (rows > 0)), (r, rows)
+    n, bad = check_margins(g, inp, [0, 5])
+    assert not bad, "\n".join(bad)
+    assert n == 2
