@@ -546,34 +546,57 @@ __global__ __launch_bounds__(kResidentThreads) void topp_resident_kernel(Params 
   if (tid < kResidentMaxChunks) sh.lsum[tid] = 0;
 #pragma unroll
   for (int i = 0; i < kResValueBins / kResidentThreads; ++i) rs.cnt[tid + i * kResidentThreads] = 0;
-  // Row scale m and row mass S in one pass: each lane keeps its own
-  // reference lr (the largest of its tokens so far) and the sum of its
-  // weights 2^(a (z - lr)) (fp32 over a chunk's 16 tokens, fp64 beyond),
-  // rescaled when lr rises; then m is the largest reference and S the sum of
-  // the lane sums scaled to m.
-  float lr = kNegInf;
+  // Row scale m and row mass S in one pass.  Each lane takes as its
+  // reference r the largest of its tokens in its first chunk and sums the
+  // weights 2^(a (z - r)) of every later chunk in the same sweep that takes
+  // their maximum (fp32 over a chunk's 16 tokens, fp64 beyond; each weight
+  // 2^(fma(z, a, -hi)) 2^(-lo) with a r = hi + lo exactly).  Weights above 1
+  // are fine up to 2^64; a chunk whose maximum lies further above r moves r
+  // up to it, rescales the sum and sums that chunk again (rare).  Then m is the
+  // largest token and S the sum of the lane sums scaled to m.
+  float lr, lmax;  // the lane's reference and its largest token so far
   double ls = 0.0;
-#pragma unroll
-  for (int j = 0; j < kResSlots; ++j) {
-    res_fence(v[j]);
+  float hi = 0.0f, sl = 1.0f;  // a lr = hi + lo, sl = 2^(-lo); hi = 0 while lr = -inf
+  {
+    res_fence(v[0]);
     float cm = kNegInf;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) cm = fmaxf(cm, L::elem(v[j], e));
-    const float nr = fmaxf(lr, cm);
-    if (nr > kNegInf) {  // lanes whose tokens so far are all padding keep (-inf, 0)
-      if (nr != lr) ls *= (double)tp_weight(lr, a, nr);
-      lr = nr;
-      res_fence(v[j]);  // decode again rather than hold 16 decoded values across the maximum
-      // 2^(a (z - lr)) as 2^(fma(z, a, -hi)) 2^(-lo) with a lr = hi + lo exactly:
-      // one instruction per token for the exponent.
-      const float hi = a * lr, lo = __builtin_fmaf(a, lr, -hi);
-      float cs = 0.0f;
+    for (int e = 0; e < 16; ++e) cm = fmaxf(cm, L::elem(v[0], e));
+    lr = lmax = cm;
+    if (lr > kNegInf) {
+      hi = a * lr;
+      sl = exp2_acc(-__builtin_fmaf(a, lr, -hi));
+    }
+    res_fence(v[0]);  // decode again rather than hold 16 decoded values across the maximum
+    float cs = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) cs += exp2_acc(__builtin_fmaf(L::elem(v[0], e), a, -hi));
+    ls = (double)cs * (double)sl;  // 0 for a lane of padding only (its z are -inf)
+  }
+#pragma unroll
+  for (int j = 1; j < kResSlots; ++j) {
+    res_fence(v[j]);
+    float cm = kNegInf, cs = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float z = L::elem(v[j], e);
+      cm = fmaxf(cm, z);
+      cs += exp2_acc(__builtin_fmaf(z, a, -hi));
+    }
+    lmax = fmaxf(lmax, cm);
+    if (cm > lr && (lr == kNegInf || a * (cm - lr) > 64.0f)) {
+      ls *= lr > kNegInf ? (double)tp_weight(lr, a, cm) : 0.0;
+      lr = cm;
+      hi = a * lr;
+      sl = exp2_acc(-__builtin_fmaf(a, lr, -hi));
+      res_fence(v[j]);
+      cs = 0.0f;
 #pragma unroll
       for (int e = 0; e < 16; ++e) cs += exp2_acc(__builtin_fmaf(L::elem(v[j], e), a, -hi));
-      ls += (double)cs * (double)exp2_acc(-lo);
     }
+    ls += (double)cs * (double)sl;
   }
-  const float wm = wave_max(lr);
+  const float wm = wave_max(lmax);
   if (lane == 0) sh.wmax[wave] = wm;
   __syncthreads();
   float m = sh.wmax[0];

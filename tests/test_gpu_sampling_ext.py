@@ -42,6 +42,9 @@ CASES = {
     "topp_resident_max_chunks": C3.with_(B=6, V=131072, top_p=0.9),
     "topp_past_resident_limit": C3.with_(B=6, V=131072 + 8, top_p=0.9),
     "topp_one_partial_chunk": C3.with_(B=10, V=1000, top_p=0.8),
+    # a = log2(e) / 0.05: later chunks far above a lane's first chunk move its
+    # reference up and are summed again
+    "topp_low_temperature": C3.with_(B=8, V=9000 + 8, top_p=0.9, T=0.05),
     # logits near 0: the nucleus reaches past the value window (negative logits),
     # so the bucket path finds the boundary; at scale 0.01 its boundary bucket
     # holds more tokens than the LDS list
