@@ -588,6 +588,47 @@ __device__ __forceinline__ ArgMax wave_chunk_race(const Params &p, int g, EF ent
   return wave_argmax(best);
 }
 
+// Row statistics and chunk race of a dense stochastic row of at most 256
+// chunks in one go: lane l holds the table entries of chunks 4l .. 4l + 3 in
+// registers; m = the largest r_c, then W_c = s_c exp2(a (r_c - m)) once per
+// chunk for both S = sum of W_c and the race (chunk `skip` left out, its 1/E
+// to *rskip), the two wave reductions side by side.  Same results as the
+// separate statistics and wave_chunk_race up to the summation order of S.
+template <class EF>
+__device__ __forceinline__ void row_stats_race(const Params &p, EF ent, float a, int skip, const ChunkNoise &cn,
+                                               float &m, float &s, ArgMax &w1, float *rskip) {
+  const int lane = threadIdx.x & 63;
+  float2 e[4];
+  float lm = kNegInf;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int c = 4 * lane + k;
+    e[k] = c < p.NC ? ent(c) : make_float2(kNegInf, 0.0f);
+    lm = fmaxf(lm, e[k].x);
+  }
+  m = wave_max(lm);
+  float ls = 0.0f, rs = 0.0f;
+  ArgMax best{-1.0f, 0x7FFFFFFF};
+  if (m > kNegInf) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int c = 4 * lane + k;
+      if (c == skip) rs = cn.r[k];
+      if (e[k].x > kNegInf) {
+        const float Wc = e[k].y * exp2_acc(a * (e[k].x - m));
+        ls += Wc;
+        if (c != skip && Wc > 0.0f) {
+          const ArgMax o{Wc * cn.r[k], c};
+          if (better(o, best)) best = o;
+        }
+      }
+    }
+  }
+  s = wave_sum(ls);
+  w1 = wave_argmax(best);
+  if (skip >= 0) *rskip = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rs), (skip >> 2) & 63));
+}
+
 // Token race over chunk c of row g whose raw logits are in LDS (zs, token
 // order): weights exp2(fma(z', a, -hi)) on the processed z' (hi = a r_c; a
 // factor common to the chunk cancels), token `skip` left out.  Thread t < 256

@@ -438,14 +438,29 @@ __device__ __forceinline__ void request_epilogue(const Params &p, const Req &q_i
     const int d = sh.d[i];
     auto ent = [&](int c) { return entry(i, c); };
     float m, s;
-    int lc;
-    row_stats(p, q, g, st, greedy, ent, m, s, lc);
+    int lc = 0x7FFFFFFF;
     Proc pr = q.proc;
     pr.tau = PLAIN ? kNegInf : sh.tau[i];
     int am = 0x7FFFFFFF;
     float zd = kNegInf, qd = 1.0f, sx = 0.0f;
     const bool valid_d = i < K && d >= 0 && d < p.V;
-    if (st < 0 && greedy) {
+    // Speculative dense stochastic rows of at most 256 chunks: statistics and
+    // chunk race from one read of the table (spec_issue's race is then done).
+    const bool fused = st < 0 && !greedy && spec && (!q.has_q || i == K) && p.NC <= 256;
+    if (fused) {
+      const bool excl = i < q.K && !q.has_q && valid_d;
+      rs.cd = excl ? d / kChunk : -1;
+      rs.rcd = 0.0f;
+      row_stats_race(p, ent, q.a, rs.cd, cn, m, s, rs.w1, &rs.rcd);
+    } else {
+      row_stats(p, q, g, st, greedy, ent, m, s, lc);
+    }
+    if (fused) {
+      const int c1 = rs.w1.s < 0.0f ? -1 : rs.w1.i;
+      if (c1 >= 0 || rs.cd >= 0) load_chunk16_pen_pair(p, g, c1, rs.cd, pr, rs.zc, rs.zx);
+      if (rs.cd >= 0) spec_draft_record(p, q, d, proc_after_pen(pr), rs, ent(rs.cd).x, zd, sx);
+      spec_publish(rs, wave, sh);
+    } else if (st < 0 && greedy) {
       if (lc < p.NC) {
         load_chunk16_pen(p, g, lc, pr, rs.zc);
         am = wave_first_equal(p, lc, rs.zc, proc_after_pen(pr), m);
