@@ -457,8 +457,29 @@ __device__ __forceinline__ void request_epilogue(const Params &p, const Req &q_i
     }
     if (fused) {
       const int c1 = rs.w1.s < 0.0f ? -1 : rs.w1.i;
-      if (c1 >= 0 || rs.cd >= 0) load_chunk16_pen_pair(p, g, c1, rs.cd, pr, rs.zc, rs.zx);
-      if (rs.cd >= 0) spec_draft_record(p, q, d, proc_after_pen(pr), rs, ent(rs.cd).x, zd, sx);
+      // The draft token's chunk (left out of the race above) can win only if
+      // its whole mass beats c1's score; else its mass without d is not
+      // needed, d stays out of the race, and only z_d is loaded.
+      bool need_cd = rs.cd >= 0;
+      if (need_cd && c1 >= 0) {
+        const float2 ec = ent(rs.cd);
+        const float Wcd = ec.x > kNegInf ? ec.y * exp2_acc(q.a * (ec.x - m)) : 0.0f;
+        need_cd = Wcd * rs.rcd >= rs.w1.s * (1.0f - 1e-5f);  // (a margin for the rounding of the two masses)
+      }
+      if (need_cd) {
+        load_chunk16_pen_pair(p, g, c1, rs.cd, pr, rs.zc, rs.zx);
+        spec_draft_record(p, q, d, proc_after_pen(pr), rs, ent(rs.cd).x, zd, sx);
+      } else {
+        // z_d (and its count) issued before the chunk, so that both arrive in one round trip
+        const float zr = valid_d ? load_logit(p, g, d) : 0.0f;
+        const int nd = (valid_d && pr.counts != nullptr) ? pr.counts[d] : 0;
+        if (c1 >= 0) load_chunk16_pen(p, g, c1, pr, rs.zc);
+        if (valid_d) {
+          const float z = nd > 0 ? penalize(zr, nd, pr) : zr;
+          zd = z < pr.tau ? kNegInf : z;
+        }
+        rs.cd = -1;
+      }
       spec_publish(rs, wave, sh);
     } else if (st < 0 && greedy) {
       if (lc < p.NC) {
