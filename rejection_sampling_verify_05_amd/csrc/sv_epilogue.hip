@@ -50,15 +50,11 @@ struct EpiSharedT {
   float m[kMaxDrafts + 1];
   float s[kMaxDrafts + 1];
   float tau[kMaxDrafts + 1];
-  float zd[kMaxDrafts + 1];
-  float qd[kMaxDrafts + 1];
   float sx[kMaxDrafts + 1];
   int amax[kMaxDrafts + 1];
   int state[kMaxDrafts + 1];
   int d[kMaxDrafts + 1];
-  int j;
-  int bad;
-  int flag;
+  int rj[kMaxDrafts + 1];  // accept test of draft i failed (1) or passed (0)
   float rt[kInlineResidNC];  // residual chunk masses (vocabularies of at most kInlineResidNC chunks)
   float zc[kWaves][kChunk];  // speculative chunks of rows 0..3 (raw logits, token order)
   float zx[kWaves][kChunk];  // the draft tokens' chunks of rows 0..3
@@ -401,6 +397,8 @@ __device__ __forceinline__ void request_epilogue(const Params &p, const Req &q_i
   // speculative row (it depends only on the row).
   const int srow = spec_row(wave, nrow);
   const ChunkNoise cn = chunk_noise(p, q.g0 + min(srow, nrow - 1));
+  // ... and its accept uniform (rows taken later draw theirs when they come)
+  const double u_srow = srow < K ? u_accept(rng_block(p, 0, (uint32_t)(q.g0 + srow), kTagAccept).x) : 1.0;
   if (cached) {
 #pragma unroll
     for (int m = 0; m < TC / kThreads; ++m) {
@@ -495,13 +493,38 @@ __device__ __forceinline__ void request_epilogue(const Params &p, const Req &q_i
       zd = apply_proc(load_logit(p, g, d), d, pr);
       if (q.has_q) qd = draft_q_of(p, q, i, d);
     }
+    // The accept test of draft i by the wave that has its row ("vLLM 投机解码
+    // （Eagle / MTP）实现与运行流程", 8.3): greedy, the draft equals the argmax;
+    // stochastic, a valid draft with q > 0 and p(d) >= u q (q = 1 without
+    // draft distributions); synthetic, u a_i <= a_{i+1} (a_0 = 1), exact in fp64.
+    bool rej = false;
+    float pdv = -1.0f;  // p(d) for dbg_p_draft (-1: greedy)
+    if (i < K) {
+      const double u = (greedy && !p.synthetic) ? 1.0 : (i == srow ? u_srow : u_accept(rng_block(p, 0, (uint32_t)g, kTagAccept).x));
+      if (p.synthetic) {
+        const double prev = i == 0 ? 1.0 : (double)p.syn[i - 1];
+        rej = !(valid_d && u * prev <= (double)p.syn[i]);
+        if (!greedy) pdv = valid_d ? exp2_acc(q.a * (zd - m)) / s : 0.0f;
+      } else if (greedy) {
+        rej = d != am;
+      } else {
+        float pd = 0.0f;
+        double qv = q.has_q ? 0.0 : 1.0;
+        if (valid_d) {
+          pd = exp2_acc(q.a * (zd - m)) / s;
+          if (q.has_q) qv = (double)qd;
+        }
+        rej = !(valid_d && qv > 0.0 && (double)pd >= u * qv);
+        pdv = pd;
+      }
+    }
     if (lane == 0) {
       sh.m[i] = m;
       sh.s[i] = s;
       sh.amax[i] = am;
-      sh.zd[i] = zd;
-      sh.qd[i] = qd;
       sh.sx[i] = sx;
+      sh.rj[i] = rej ? 1 : 0;
+      if (i < K && p.dbg_p_draft) p.dbg_p_draft[q.c0 + i] = pdv;
       p.row_info[g] = make_float4(m, s, __int_as_float(am), __int_as_float(st));
     }
     if (spec) {
@@ -512,53 +535,17 @@ __device__ __forceinline__ void request_epilogue(const Params &p, const Req &q_i
     }
   }
   __syncthreads();
-  if (tid == 0) {
-    int bad = 0;
-    for (int i = 0; i < nrow; ++i) bad |= !__builtin_isfinite(sh.m[i]);
-    sh.bad = bad;
-  }
-
-  // Accept tests: lane i of wave 0 takes draft position i.
-  if (wave == 0) {
-    bool rej = false;
-    if (lane < K) {
-      const int d = sh.d[lane];
-      const int g = q.g0 + lane;
-      if (p.synthetic) {
-        // Synthetic acceptance: u * a_i <= a_{i+1} with a_0 = 1, exact in fp64.
-        const double u = u_accept(rng_block(p, 0, (uint32_t)g, kTagAccept).x);
-        const double prev = lane == 0 ? 1.0 : (double)p.syn[lane - 1];
-        rej = !(d >= 0 && d < p.V && u * prev <= (double)p.syn[lane]);
-        if (p.dbg_p_draft) {
-          const bool valid = d >= 0 && d < p.V;
-          p.dbg_p_draft[q.c0 + lane] = greedy ? -1.0f : (valid ? exp2_acc(q.a * (sh.zd[lane] - sh.m[lane])) / sh.s[lane] : 0.0f);
-        }
-      } else if (greedy) {
-        rej = d != sh.amax[lane];
-        if (p.dbg_p_draft) p.dbg_p_draft[q.c0 + lane] = -1.0f;
-      } else {
-        const bool valid = d >= 0 && d < p.V;
-        float pd = 0.0f;
-        double qd = q.has_q ? 0.0 : 1.0;
-        if (valid) {
-          pd = exp2_acc(q.a * (sh.zd[lane] - sh.m[lane])) / sh.s[lane];
-          if (q.has_q) qd = (double)sh.qd[lane];
-        }
-        const double u = u_accept(rng_block(p, 0, (uint32_t)g, kTagAccept).x);
-        rej = !(valid && qd > 0.0 && (double)pd >= u * qd);
-        if (p.dbg_p_draft) p.dbg_p_draft[q.c0 + lane] = pd;
-      }
-    }
-    const unsigned long long mask = __ballot(rej);
-    if (lane == 0) sh.j = mask ? (__ffsll((long long)mask) - 1) : K;
-  }
-  __syncthreads();
-  if (sh.bad) {
+  // The row checks and the sampled row j (the first rejected draft, else the
+  // bonus row), in every wave from the rows' records: no further barrier.
+  bool bad = __ballot(lane < nrow && !__builtin_isfinite(sh.m[lane])) != 0;
+  if (nrow > 64) bad = bad || !__builtin_isfinite(sh.m[64]);
+  if (bad) {
     if (tid == 0) raise_err(p, SV_ERR_ROW);
     write_empty(p, r);
     return;
   }
-  const int j = sh.j;
+  const unsigned long long rmask = __ballot(lane < K && sh.rj[lane] != 0);
+  const int j = rmask ? (__ffsll((long long)rmask) - 1) : K;
 
   // Accepted prefix, padding and counts.
   for (int t = tid; t < p.out_stride; t += kThreads) {
