@@ -238,3 +238,26 @@ def test_chunk_scale_ramps(draft_probs):
             n_margin, bad = check_requests(g, inp, range(inp["B"]), seed, off, probs=True)
             say(f"ramps draft_probs={draft_probs} seed {seed}: margin {n_margin}, mismatches {len(bad)}")
             assert not bad, "\n".join(bad[:10])
+
+
+@pytest.mark.parametrize("scale", [0.3, 3.0])
+def test_nodraft_drafts_at_heavy_tokens(scale):
+    # Without draft probabilities, the rejected draft is removed from the race:
+    # with drafts at each row's heaviest token, the draft's chunk holds much of
+    # the row's mass, so the race must weigh that chunk without the draft (the
+    # epilogue loads it only when it could win) -- at scale 0.3 nearly every
+    # chunk competes, at 3.0 the heavy chunk usually wins.
+    w = wl.CONFIGS["3"].with_(B=48, V=9000 + 8, scale=scale)
+    inp = wl.make_inputs(w, DEV)
+    cu = inp["cu"].cpu().numpy()
+    lg = inp["logits"].float()
+    for r in range(inp["B"]):
+        for i in range(int(cu[r + 1] - cu[r])):
+            g = int(cu[r]) + r + i
+            inp["draft_ids"][int(cu[r]) + i] = int(torch.argmax(lg[g]).item())
+    with ctx_for(inp) as ctx:
+        for seed, off in [(0, 0), (3, 1), (77, 9)]:
+            g = run_gpu(ctx, inp, seed=seed, offset=off)
+            assert g["err"] == 0
+            n_margin, bad = check_requests(g, inp, range(inp["B"]), seed, off)
+            assert not bad, "\n".join(bad[:10])
