@@ -342,10 +342,12 @@ __device__ __forceinline__ void inline_residual(const Params &p, const Req &q, i
   fused_post_update(p, q.r, q.K, j, x, [&](int i) { return sh.d[i]; });
 }
 
-// PLAIN: the call has no top-k, top-p, penalties or draft distributions and
-// at most four rows per request; the settings they would read are then
-// constants, and their paths compile away.
-template <bool PLAIN, class SH>
+// PLAIN: the call has no top-k, penalties or draft distributions and at most
+// four rows per request; the settings they would read are then constants, and
+// their paths compile away.  TP (with PLAIN): the call has top-p, so each row
+// carries the top-p pass's threshold tau (tokens below it are out of the
+// race; the row's chunk table already holds the kept masses).
+template <bool PLAIN, bool TP, class SH>
 __device__ __forceinline__ void request_epilogue(const Params &p, const Req &q_in, SH &sh) {
   constexpr int TC = SH::kCache;
   Req q = q_in;
@@ -378,7 +380,7 @@ __device__ __forceinline__ void request_epilogue(const Params &p, const Req &q_i
   // Row states (top-k pass results), draft ids and the chunk tables.
   for (int i = tid; i < nrow; i += kThreads) {
     const int g = q.g0 + i;
-    const int st = PLAIN ? kRowDense : row_state(p, g);
+    const int st = (PLAIN && !TP) ? kRowDense : row_state(p, g);
     sh.state[i] = st;
     sh.tau[i] = (st == kRowDense) ? kNegInf : p.cand_tau[g];
     sh.d[i] = i < K ? p.draft_ids[q.c0 + i] : -1;
@@ -432,13 +434,13 @@ __device__ __forceinline__ void request_epilogue(const Params &p, const Req &q_i
       if (i >= nrow) break;
     }
     const int g = q.g0 + i;
-    const int st = PLAIN ? kRowDense : sh.state[i];
+    const int st = (PLAIN && !TP) ? kRowDense : sh.state[i];
     const int d = sh.d[i];
     auto ent = [&](int c) { return entry(i, c); };
     float m, s;
     int lc = 0x7FFFFFFF;
     Proc pr = q.proc;
-    pr.tau = PLAIN ? kNegInf : sh.tau[i];
+    pr.tau = (PLAIN && !TP) ? kNegInf : sh.tau[i];
     int am = 0x7FFFFFFF;
     float zd = kNegInf, qd = 1.0f, sx = 0.0f;
     const bool valid_d = i < K && d >= 0 && d < p.V;
@@ -570,8 +572,8 @@ __device__ __forceinline__ void request_epilogue(const Params &p, const Req &q_i
   const int dj = rejected ? sh.d[j] : -1;
   const float m = sh.m[j], s = sh.s[j];
   Proc pr = q.proc;
-  pr.tau = PLAIN ? kNegInf : sh.tau[j];
-  const int st = PLAIN ? kRowDense : sh.state[j];
+  pr.tau = (PLAIN && !TP) ? kNegInf : sh.tau[j];
+  const int st = (PLAIN && !TP) ? kRowDense : sh.state[j];
   const float a = q.a;
 
   if constexpr (!PLAIN) {
@@ -750,10 +752,10 @@ __global__ __launch_bounds__(kThreads) void resid_race_kernel(Params p) {
 }
 
 // Request epilogue kernel: one workgroup per request, after the stats pass.
-template <bool PLAIN>
+template <bool PLAIN, bool TP>
 __global__ __launch_bounds__(kThreads) void epilogue_kernel(Params p) {
   __shared__ EpiShared sh;
-  request_epilogue<PLAIN>(p, load_req(p, blockIdx.x), sh);
+  request_epilogue<PLAIN, TP>(p, load_req(p, blockIdx.x), sh);
 }
 
 // ---------------------------------------------------------------------------
@@ -950,9 +952,9 @@ __global__ __launch_bounds__(kThreads) void dbg_noise_kernel(const uint32_t *wor
 }  // namespace
 
 hipError_t launch_epilogue(const Params &p, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
-  const bool plain = plain_call(p);
-  const void *fn = plain ? reinterpret_cast<const void *>(&epilogue_kernel<true>)
-                         : reinterpret_cast<const void *>(&epilogue_kernel<false>);
+  const void *fn = plain_call(p)        ? reinterpret_cast<const void *>(&epilogue_kernel<true, false>)
+                   : plain_call(p, true) ? reinterpret_cast<const void *>(&epilogue_kernel<true, true>)
+                                         : reinterpret_cast<const void *>(&epilogue_kernel<false, false>);
   return launch_timed(fn, dim3((unsigned)p.B), p, s, t0, t1);
 }
 
