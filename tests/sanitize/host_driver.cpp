@@ -103,7 +103,7 @@ int main() {
   sv_ctx c = make_ctx(1100, 256, 3, 128256, 0);
   sv_verify_args a = plain_args(256, 650, 128256, SV_BF16, 4);
   CHECK(spec_verify_run(&c, &a, nullptr) == SV_OK);
-  CHECK(g_n[kStats] == 1 && g_n[kEpi] == 1 && g_last.fast == 1 && sv::plain_call(g_last));
+  CHECK(g_n[kStats] == 1 && g_n[kEpi] == 1 && g_last.fast == 1 && sv::plain_call(g_last) && !sv::pen_call(g_last));
   CHECK(g_last.NC == 126 && g_last.D == 394 && g_last.epoch == 1);
   {
     const int64_t chunks = (int64_t)650 * 126, per = 3 * 126 + 1;
@@ -128,7 +128,8 @@ int main() {
   ap.idx_mapping = (const int32_t *)g_fake;
   ap.output_bin_counts = (const int32_t *)g_fake;
   ap.num_slots = 300;
-  CHECK(spec_verify_run(&c, &ap, nullptr) == SV_OK && g_last.fast_pen == 1 && !sv::plain_call(g_last));
+  // (penalties alone keep the lean epilogue, in its penalty instantiation)
+  CHECK(spec_verify_run(&c, &ap, nullptr) == SV_OK && g_last.fast_pen == 1 && sv::plain_call(g_last) && sv::pen_call(g_last));
   sv_verify_args ak = a;
   ak.top_k = (const int32_t *)g_fake;
   CHECK(spec_verify_run(&c, &ak, nullptr) == SV_ECAPACITY);  // context without top-k storage
