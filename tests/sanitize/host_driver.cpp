@@ -144,6 +144,7 @@ int main() {
   int np = g_n[kTopp], ns_ = g_n[kStats], nres = g_n[kRes];
   CHECK(spec_verify_run(&c, &aq, nullptr) == SV_OK && g_n[kRes] == nres + 1 && g_n[kTopp] == np &&
         g_n[kStats] == ns_ && g_last.cand_valid == 1);
+  CHECK(sv::plain_call(g_last) && g_last.has_topp == 1 && !sv::pen_call(g_last));  // the lean epilogue with thresholds
   // Larger vocabularies, fp32 rows or penalties: the two-pass kernel between two statistics passes.
   sv_verify_args aq2 = aq;
   aq2.logits_dtype = SV_F32;
