@@ -342,13 +342,14 @@ __device__ __forceinline__ void inline_residual(const Params &p, const Req &q, i
   fused_post_update(p, q.r, q.K, j, x, [&](int i) { return sh.d[i]; });
 }
 
-// PLAIN: the call has no top-k or draft distributions and at most four rows
-// per request; the settings they would read are then constants, and their
-// paths compile away.  With PLAIN, TP: the call has top-p, so each row carries
-// the top-p pass's threshold tau (tokens below it are out of the race; the
-// row's chunk table already holds the kept masses); PEN: the call has
-// penalties, which the request's settings keep (else they are the identity).
-template <bool PLAIN, bool TP, bool PEN, class SH>
+// PLAIN: the call has no top-k and at most four rows per request; the
+// settings it does not use are then constants, and their paths compile away.
+// With PLAIN, TP: the call has top-p, so each row carries the top-p pass's
+// threshold tau (tokens below it are out of the race; the row's chunk table
+// already holds the kept masses); PEN: the call has penalties, which the
+// request's settings keep (else they are the identity); QD: the call has
+// draft distributions (else q = 1).
+template <bool PLAIN, bool TP, bool PEN, bool QD, class SH>
 __device__ __forceinline__ void request_epilogue(const Params &p, const Req &q_in, SH &sh) {
   constexpr int TC = SH::kCache;
   Req q = q_in;
@@ -360,7 +361,7 @@ __device__ __forceinline__ void request_epilogue(const Params &p, const Req &q_i
       q.proc.pres = 0.0f;
     }
     q.proc.tau = kNegInf;
-    q.has_q = false;
+    if (!QD) q.has_q = false;
   }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K = q.K, r = q.r, nrow = K + 1;
@@ -755,10 +756,10 @@ __global__ __launch_bounds__(kThreads) void resid_race_kernel(Params p) {
 }
 
 // Request epilogue kernel: one workgroup per request, after the stats pass.
-template <bool PLAIN, bool TP, bool PEN>
+template <bool PLAIN, bool TP, bool PEN, bool QD>
 __global__ __launch_bounds__(kThreads) void epilogue_kernel(Params p) {
   __shared__ EpiShared sh;
-  request_epilogue<PLAIN, TP, PEN>(p, load_req(p, blockIdx.x), sh);
+  request_epilogue<PLAIN, TP, PEN, QD>(p, load_req(p, blockIdx.x), sh);
 }
 
 // ---------------------------------------------------------------------------
@@ -955,11 +956,18 @@ __global__ __launch_bounds__(kThreads) void dbg_noise_kernel(const uint32_t *wor
 }  // namespace
 
 hipError_t launch_epilogue(const Params &p, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
-  const void *fn = !plain_call(p) ? reinterpret_cast<const void *>(&epilogue_kernel<false, false, false>)
-                   : p.has_topp   ? (pen_call(p) ? reinterpret_cast<const void *>(&epilogue_kernel<true, true, true>)
-                                                 : reinterpret_cast<const void *>(&epilogue_kernel<true, true, false>))
-                                  : (pen_call(p) ? reinterpret_cast<const void *>(&epilogue_kernel<true, false, true>)
-                                                 : reinterpret_cast<const void *>(&epilogue_kernel<true, false, false>));
+  const bool qd = p.draft_probs != nullptr || p.draft_logits != nullptr;
+  const void *fn;
+  if (!plain_call(p))
+    fn = reinterpret_cast<const void *>(&epilogue_kernel<false, false, false, false>);
+  else if (qd)  // (draft distributions with top-p or penalties: not a plain call)
+    fn = reinterpret_cast<const void *>(&epilogue_kernel<true, false, false, true>);
+  else if (p.has_topp)
+    fn = pen_call(p) ? reinterpret_cast<const void *>(&epilogue_kernel<true, true, true, false>)
+                     : reinterpret_cast<const void *>(&epilogue_kernel<true, true, false, false>);
+  else
+    fn = pen_call(p) ? reinterpret_cast<const void *>(&epilogue_kernel<true, false, true, false>)
+                     : reinterpret_cast<const void *>(&epilogue_kernel<true, false, false, false>);
   return launch_timed(fn, dim3((unsigned)p.B), p, s, t0, t1);
 }
 

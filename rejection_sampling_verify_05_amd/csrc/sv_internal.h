@@ -188,13 +188,15 @@ hipError_t launch_dbg_noise(const uint32_t *words, int64_t n, float *out, hipStr
 // Resident stats workgroups per CU (occupancy query); kind 0 general pass,
 // 1 fast pass, 2 fast pass with penalties.
 int stats_blocks_per_cu(int dtype, int kind);
-// Calls the lean request epilogue serves: no top-k or draft distributions, at
-// most four rows per request (top-p and penalties in instantiations of their own).
-inline bool plain_call(const Params &p) {
-  return !p.has_topk && p.draft_probs == nullptr && p.draft_logits == nullptr && p.out_stride <= kWaves;
-}
 inline bool pen_call(const Params &p) {
   return p.rep_penalty != nullptr || p.freq_penalty != nullptr || p.pres_penalty != nullptr;
+}
+// Calls the lean request epilogue serves: no top-k, at most four rows per
+// request; top-p and penalties, or draft distributions without either, in
+// instantiations of their own.
+inline bool plain_call(const Params &p) {
+  const bool qd = p.draft_probs != nullptr || p.draft_logits != nullptr;
+  return !p.has_topk && p.out_stride <= kWaves && !(qd && (p.has_topp || pen_call(p)));
 }
 constexpr int kSliceRows = 4;  // rows a stats slice may span (kRowCache)
 

@@ -161,7 +161,13 @@ int main() {
   ad.draft_probs = (const float *)g_fake;
   ad.draft_row_stride = a.vocab_size;
   const int nr = g_n[kResid];
-  CHECK(spec_verify_run(&c, &ad, nullptr) == SV_OK && g_n[kResid] == nr + 1 && !sv::plain_call(g_last));
+  // (draft distributions alone keep the lean epilogue; with top-p or penalties, the general one)
+  CHECK(spec_verify_run(&c, &ad, nullptr) == SV_OK && g_n[kResid] == nr + 1 && sv::plain_call(g_last));
+  {
+    sv_verify_args adq = ad;
+    adq.top_p = (const float *)g_fake;
+    CHECK(spec_verify_run(&c, &adq, nullptr) == SV_OK && !sv::plain_call(g_last));
+  }
   ad.draft_row_stride = a.vocab_size - 1;
   CHECK(spec_verify_run(&c, &ad, nullptr) == SV_EINVAL);
   // Debug margins: one more launch, after the epilogue's.
