@@ -348,8 +348,9 @@ __device__ __forceinline__ void inline_residual(const Params &p, const Req &q, i
 // threshold tau (tokens below it are out of the race; the row's chunk table
 // already holds the kept masses); PEN: the call has penalties, which the
 // request's settings keep (else they are the identity); QD: the call has
-// draft distributions (else q = 1).
-template <bool PLAIN, bool TP, bool PEN, bool QD, class SH>
+// draft distributions (else q = 1).  FEW: at most four rows per request (with
+// QD alone, more rows are allowed).
+template <bool PLAIN, bool TP, bool PEN, bool QD, bool FEW, class SH>
 __device__ __forceinline__ void request_epilogue(const Params &p, const Req &q_in, SH &sh) {
   constexpr int TC = SH::kCache;
   Req q = q_in;
@@ -371,9 +372,9 @@ __device__ __forceinline__ void request_epilogue(const Params &p, const Req &q_i
     write_empty(p, r);
     return;
   }
-  // The plain variant also runs only with at most four rows per request
-  // (cu_ok bounds K by out_stride - 1): every row has a wave of its own.
-  if (PLAIN) __builtin_assume(nrow <= kWaves);
+  // FEW: at most four rows per request (cu_ok bounds K by out_stride - 1):
+  // every row has a wave of its own.
+  if (PLAIN && FEW) __builtin_assume(nrow <= kWaves);
   if (q.mode == kModeInvalid) {
     if (tid == 0) raise_err(p, q.errbits);
     write_empty(p, r);
@@ -756,10 +757,10 @@ __global__ __launch_bounds__(kThreads) void resid_race_kernel(Params p) {
 }
 
 // Request epilogue kernel: one workgroup per request, after the stats pass.
-template <bool PLAIN, bool TP, bool PEN, bool QD>
+template <bool PLAIN, bool TP, bool PEN, bool QD, bool FEW = true>
 __global__ __launch_bounds__(kThreads) void epilogue_kernel(Params p) {
   __shared__ EpiShared sh;
-  request_epilogue<PLAIN, TP, PEN, QD>(p, load_req(p, blockIdx.x), sh);
+  request_epilogue<PLAIN, TP, PEN, QD, FEW>(p, load_req(p, blockIdx.x), sh);
 }
 
 // ---------------------------------------------------------------------------
@@ -961,7 +962,8 @@ hipError_t launch_epilogue(const Params &p, hipStream_t s, hipEvent_t t0, hipEve
   if (!plain_call(p))
     fn = reinterpret_cast<const void *>(&epilogue_kernel<false, false, false, false>);
   else if (qd)  // (draft distributions with top-p or penalties: not a plain call)
-    fn = reinterpret_cast<const void *>(&epilogue_kernel<true, false, false, true>);
+    fn = p.out_stride <= kWaves ? reinterpret_cast<const void *>(&epilogue_kernel<true, false, false, true>)
+                                : reinterpret_cast<const void *>(&epilogue_kernel<true, false, false, true, false>);
   else if (p.has_topp)
     fn = pen_call(p) ? reinterpret_cast<const void *>(&epilogue_kernel<true, true, true, false>)
                      : reinterpret_cast<const void *>(&epilogue_kernel<true, true, false, false>);

@@ -191,12 +191,12 @@ int stats_blocks_per_cu(int dtype, int kind);
 inline bool pen_call(const Params &p) {
   return p.rep_penalty != nullptr || p.freq_penalty != nullptr || p.pres_penalty != nullptr;
 }
-// Calls the lean request epilogue serves: no top-k, at most four rows per
-// request; top-p and penalties, or draft distributions without either, in
-// instantiations of their own.
+// Calls the lean request epilogue serves: no top-k; top-p and penalties
+// (at most four rows per request), or draft distributions without either (any
+// number of rows), in instantiations of their own.
 inline bool plain_call(const Params &p) {
   const bool qd = p.draft_probs != nullptr || p.draft_logits != nullptr;
-  return !p.has_topk && p.out_stride <= kWaves && !(qd && (p.has_topp || pen_call(p)));
+  return !p.has_topk && (qd ? !(p.has_topp || pen_call(p)) : p.out_stride <= kWaves);
 }
 constexpr int kSliceRows = 4;  // rows a stats slice may span (kRowCache)
 
